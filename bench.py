@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lynx hot path on one MI355X.
+
+One step = encode of the whole K and V cache of the workload (page/chunk
+statistics, alpha-law codes, anchor/residual planes), then anchor-only and
+full fused-dequant single-query decode attention.  Inputs are seeded
+synthetic Laplacian KV with outlier channels (long_context_serving_amd/synth.py),
+resident in HBM before timing starts.  To keep the 256 MB Infinity Cache from
+serving the data, every step works on one of several distinct buffer sets
+(>= 1.5 GB in total): step i encodes set i % S and runs attention over the
+planes of set (i + S/2) % S, which were encoded S/2 steps earlier.
+
+Prints ONE JSON line.  Throughput counts algorithmic bytes: encode
+3.28125 B per K/V element (2 read, 0.5 + 0.5 + 0.03125 + 0.25 written),
+full decode 1.28125 B and anchor-only decode 0.78125 B per element (plus
+query and output).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encode GB/s + fused-dequant decode-attn GB/s (% of HBM peak), 1×MI355X"
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(w):
+    """Per-launch algorithmic bytes of each kernel for workload w (one layer)."""
+    per_tensor = w.batch * w.tokens * w.kv_heads * w.head_dim
+    qo = w.batch * w.q_heads * w.head_dim * (2 + 4)
+    return {
+        "encode": per_tensor * 3.28125,                 # one tensor (K or V) per launch
+        "decode_full": 2 * per_tensor * 1.28125 + qo,
+        "decode_anchor": 2 * per_tensor * 0.78125 + qo,
+        "elements_per_tensor": per_tensor,
+    }
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, xk, xv, qb, pages, sm):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    nt = oracle.max_threads()
+    xk, xv = xk[:pages], xv[:pages]
+    t0 = time.perf_counter()
+    ek, ev = oracle.encode(xk), oracle.encode(xv)
+    t1 = time.perf_counter()
+    q = oracle.bf16_bits_to_float(qb).astype(np.float64)
+    ak, rk = oracle.split(ek["codes"])
+    av, rv = oracle.split(ev["codes"])
+    for full in (False, True):
+        kh = oracle.dequant(ak, rk if full else None, ek).reshape(1, -1, w.kv_heads, w.head_dim)
+        vh = oracle.dequant(av, rv if full else None, ev).reshape(1, -1, w.kv_heads, w.head_dim)
+        oracle.attention(q[:1], kh, vh, sm)
+    t2 = time.perf_counter()
+    elems = pages * 256 * w.kv_heads * w.head_dim
+    qo = w.q_heads * w.head_dim * 6
+    nbytes = 2 * elems * 3.28125 + 2 * elems * (1.28125 + 0.78125) + 2 * qo
+    return {
+        "value": nbytes / (t2 - t0) / 1e9, "unit": "GB/s", "cores": nt, "kind": "oracle",
+        "sample": "%d of %d pages of one request (K and V): encode, then anchor and full "
+                  "dequant + brute-force attention for all %d query heads; encode %.2f s, "
+                  "decode %.2f s" % (pages, w.pages, w.q_heads, t1 - t0, t2 - t1),
+        "seconds": t2 - t0,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="ctx32k")
+    ap.add_argument("--sets", type=int, default=8, help="distinct buffer sets cycled per step")
+    ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
+    ap.add_argument("--cpu-pages", type=int, default=128, help="pages in the CPU-baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run one 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not "
+              "supported. The multi-GPU sharding is a design note only." % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_serving_amd import lynx, synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.layers != 1 or w.batch < 1 or not w.q_heads:
+        raise SystemExit("bench workload must be a single-layer decode workload")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    S = max(2, args.sets)
+    sm = float(np.float32(1.0 / math.sqrt(w.head_dim)))
+    ab = algorithmic_bytes(w)
+
+    log("bench: generating %d buffer sets of workload %s" % (S, w.name))
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    sets = []
+    xk0 = xv0 = None
+    for s in range(S):
+        xk = synth.kv_pages(w, 0, 0, s)
+        xv = synth.kv_pages(w, 0, 1, s)
+        if s == 0:
+            xk0, xv0 = xk, xv
+        sets.append({
+            "k": to_dev(xk), "v": to_dev(xv),
+            "pk": lynx.alloc_planes(w.pages, w.kv_heads, lynx.ROLE_KEY, dev),
+            "pv": lynx.alloc_planes(w.pages, w.kv_heads, lynx.ROLE_VALUE, dev),
+        })
+    qb = synth.queries(w)
+    q = to_dev(qb)
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, lynx.workspace_size(w.batch, w.kv_heads, w.q_heads, w.pages)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        e = sets[i % S]
+        a = sets[(i + S // 2) % S]
+        if ev is not None:
+            ev[0].record(stream)
+        lynx.quantize_pages(e["k"], lynx.ROLE_KEY, out=e["pk"])
+        if ev is not None:
+            ev[1].record(stream)
+        lynx.quantize_pages(e["v"], lynx.ROLE_VALUE, out=e["pv"])
+        if ev is not None:
+            ev[2].record(stream)
+        lynx.decode_attention(q, a["pk"], a["pv"], w.pages, full=False, sm_scale=sm, out=out,
+                              workspace=ws)
+        if ev is not None:
+            ev[3].record(stream)
+        lynx.decode_attention(q, a["pk"], a["pv"], w.pages, full=True, sm_scale=sm, out=out,
+                              workspace=ws)
+        if ev is not None:
+            ev[4].record(stream)
+
+    # every set encoded at least once before its planes are read
+    for i in range(max(args.warmup, S)):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    enc_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]
+    enc_v_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(K)]
+    anc_ms = [evs[i][2].elapsed_time(evs[i][3]) for i in range(K)]
+    full_ms = [evs[i][3].elapsed_time(evs[i][4]) for i in range(K)]
+    step_ms = evs[0][0].elapsed_time(evs[K - 1][4]) / K
+
+    if args.copy_probe:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    enc_avg = float(np.mean(enc_ms + enc_v_ms))
+    anc_avg = float(np.mean(anc_ms))
+    full_avg = float(np.mean(full_ms))
+    gbps = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    step_bytes = 2 * ab["encode"] + ab["decode_full"] + ab["decode_anchor"]
+    kernels = {
+        "encode": {"us_per_launch": enc_avg * 1e3, "GBps": gbps(ab["encode"], enc_avg)},
+        "decode_anchor": {"us_per_call": anc_avg * 1e3, "GBps": gbps(ab["decode_anchor"], anc_avg)},
+        "decode_full": {"us_per_call": full_avg * 1e3, "GBps": gbps(ab["decode_full"], full_avg)},
+    }
+    for k in kernels.values():
+        k["pct_of_hbm_peak"] = 100.0 * k["GBps"] / HBM_PEAK_GBPS
+
+    result = {
+        "metric": METRIC,
+        "value": gbps(step_bytes, step_ms),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads,
+                   "head_dim": w.head_dim, "tokens": w.tokens, "batch": w.batch,
+                   "q_heads": w.q_heads, "buffer_sets": S},
+        "pct_of_hbm_peak": 100.0 * gbps(step_bytes, step_ms) / HBM_PEAK_GBPS,
+        "kernels": kernels,
+        "tokens_per_s": {"encode_kv_tokens": w.tokens * w.batch / (2 * enc_avg * 1e-3),
+                         "decode_full_kv_tokens": w.tokens * w.batch / (full_avg * 1e-3),
+                         "decode_anchor_kv_tokens": w.tokens * w.batch / (anc_avg * 1e-3)},
+        "roofline": {"bound": "hbm", "kernel": "encode_kernel",
+                     "achieved": gbps(ab["encode"], enc_avg), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": gbps(ab["encode"], enc_avg) / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "wall_s_timed": wall,
+    }
+    if args.cpu:
+        log("bench: CPU baseline (oracle) on %d pages" % args.cpu_pages)
+        result["cpu_baseline"] = cpu_baseline(w, xk0, xv0, qb, min(args.cpu_pages, w.pages), sm)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * lynx.h -- C ABI of liblynx, the MI355X (gfx950) implementation of Lynx
+ * progressive KV-cache quantization.
+ *
+ * What is computed (page "Lynx: the KV cache does not have to arrive whole",
+ * section 3 "The quantizer", and section 4 "Speculation at the communication
+ * boundary"):
+ *
+ *   encode, per page of 256 tokens, per KV head h, per channel d:
+ *     mn = min_t x, rg = fl32(max_t x - mn), inv_rg = fl32(1/rg) (0 if rg = 0)
+ *     x'_t = fl32(fl32(x_t - mn) * inv_rg)                    (map to [0,1])
+ *     per chunk c of C = 32 tokens:
+ *       mu = fl32(exact_sum(x'_t) / 32), d_t = fl32(x'_t - mu)
+ *       s  = max_t |d_t|,  inv_s = fl32(1/s) (0 if s = 0)
+ *       u_t = min(1, fl32(|d_t| * inv_s))                     (y = sign(d) u)
+ *     m_t = round_half_up(127 * ln(1 + 255 u_t) / ln 256)      (0..127)
+ *     q_t = d_t < 0 ? -m_t - 1 : m_t                           (int8, sign-aware)
+ *     anchor a_t = q_t >> 4 (int4, -8..7), residual r_t = q_t & 15 (uint4)
+ *   decode:
+ *     draft code 16 a + 7, full code 16 a + r;  m = code >= 0 ? code : ~code
+ *     yhat = sign * (256^(m/127) - 1) / 255
+ *     xhat = mn + rg * (mu + s * yhat)
+ *   decode attention (page "LLM KV cache quantization", sections "The
+ *   architecture" and "End-to-end flow"): one query token per request,
+ *   scores = sm_scale * q . khat_t, softmax over all cached tokens, output =
+ *   softmax-weighted sum of vhat_t; query head j reads KV head j / (Hq / H).
+ *   The compact planes are expanded only in registers.
+ *
+ * fl32() is one IEEE binary32 operation rounded to nearest even (no fused
+ * multiply-add); the chunk sum is exact.  alpha = 255, 127 levels, C = 32 and
+ * the +7 draft point are the readings documented with the repository.
+ *
+ * Conventions for every entry point:
+ *   - all pointers are DEVICE pointers unless stated otherwise; buffers are
+ *     owned and allocated by the caller; the library never allocates device
+ *     memory and never synchronizes;
+ *   - every call is asynchronous on `stream` (a hipStream_t; NULL = default);
+ *   - inputs must be finite; the output for NaN/Inf input is unspecified;
+ *   - calls return LYNX_OK (0) or a negative lynx_status; argument errors are
+ *     detected on the host before any launch; no exception crosses the ABI;
+ *   - calls are reentrant; the library holds no mutable state after its
+ *     one-time host-side table set-up.
+ */
+#ifndef LYNX_H
+#define LYNX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LYNX_PAGE_TOKENS 256 /* tokens per page (section 3) */
+#define LYNX_CHUNK_TOKENS 32 /* C, tokens per chunk (section 3) */
+#define LYNX_CHUNKS_PER_PAGE 8
+#define LYNX_HEAD_DIM 128    /* the only head_dim this build supports */
+#define LYNX_MAX_GROUP 16    /* largest supported Hq / H */
+
+typedef enum lynx_status {
+    LYNX_OK = 0,
+    LYNX_ERR_NULL_ARG = -1,      /* a required pointer is NULL */
+    LYNX_ERR_BAD_SHAPE = -2,     /* head_dim != 128, H < 1, P < 0, Hq % H,
+                                    Hq / H > 16, batch < 0, ... */
+    LYNX_ERR_MISALIGNED = -3,    /* a pointer is not 16-byte aligned */
+    LYNX_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than required */
+    LYNX_ERR_HIP = -5,           /* a HIP runtime call or launch failed */
+    LYNX_ERR_DEVICE = -6,        /* current device is not gfx950 */
+    LYNX_ERR_BAD_ARG = -7        /* unknown role or other invalid value */
+} lynx_status;
+
+/*
+ * Plane roles.  Keys and values are quantized identically (the pages make no
+ * distinction); only the byte layout of the two nibble planes differs, each
+ * chosen so that decode attention reads its operand tiles with contiguous
+ * 16-byte loads.
+ *
+ * LYNX_ROLE_KEY   anchor/residual: uint8 [P][H][256 tokens][64]
+ *                 byte j of token row t holds channel 2j (low nibble) and
+ *                 channel 2j+1 (high nibble).
+ * LYNX_ROLE_VALUE anchor/residual: uint8 [P][H][8 chunks][128 channels][16]
+ *                 the 16 bytes of (chunk c, channel d) hold that channel's 32
+ *                 tokens of chunk c as 4 little-endian 32-bit words; word w
+ *                 holds, in nibbles 0..7 (least significant first), the
+ *                 tokens 4w, 4w+1, 4w+2, 4w+3, 16+4w, 16+4w+1, 16+4w+2,
+ *                 16+4w+3 of the chunk.
+ * Anchor nibbles are two's complement int4 (a & 15); residual nibbles are
+ * uint4.  Both roles share the scale layout below.
+ */
+typedef enum lynx_role { LYNX_ROLE_KEY = 0, LYNX_ROLE_VALUE = 1 } lynx_role;
+
+/* One encoded K or V tensor of one layer: P pages x H heads x 128 channels. */
+typedef struct lynx_planes {
+    uint8_t *anchor;     /* 0.5 B/element, layout by role (see above) */
+    uint8_t *residual;   /* 0.5 B/element; may be NULL for anchor-only reads */
+    float *page_min;     /* [P][H][128]    fp32 page minimum mn */
+    float *page_range;   /* [P][H][128]    fp32 page range rg */
+    float *chunk_mean;   /* [P][H][8][128] fp32 chunk mean mu (normalised) */
+    float *chunk_maxabs; /* [P][H][8][128] fp32 chunk max-abs s (normalised) */
+} lynx_planes;
+
+/* Byte sizes of one plane and of the scale arrays for P pages, H heads. */
+size_t lynx_plane_bytes(int64_t num_pages, int32_t num_kv_heads);
+size_t lynx_page_scale_bytes(int64_t num_pages, int32_t num_kv_heads);
+size_t lynx_chunk_scale_bytes(int64_t num_pages, int32_t num_kv_heads);
+
+/*
+ * Encoder (section 3, all four stages) and plane packer.
+ *   kv    bf16 bit patterns [P][256][H][128] (a page is 256 tokens x KV heads
+ *         x head_dim, in paged order), 16-byte aligned
+ *   role  LYNX_ROLE_KEY or LYNX_ROLE_VALUE: plane layout to write
+ *   out   every member non-NULL and 16-byte aligned; written completely
+ * P = 0 is a no-op (no pointer is inspected).  Errors: NULL_ARG, BAD_SHAPE,
+ * MISALIGNED, BAD_ARG, DEVICE, HIP.
+ */
+int lynx_quantize_pages(const uint16_t *kv, int64_t num_pages,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t role,
+                        const lynx_planes *out, void *stream);
+
+/*
+ * Standalone dequantizers (section 4: the draft reads the anchor stream
+ * alone; the refined cache reads anchor and residual).  `in` as written by
+ * lynx_quantize_pages with the same role; the anchor variant never reads
+ * in->residual (it may be NULL).  out: fp32 [P][256][H][128] (the input
+ * layout of the encoder).  P = 0 is a no-op.  Errors as for the encoder.
+ */
+int lynx_dequantize_anchor(const lynx_planes *in, int64_t num_pages,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t role, float *out, void *stream);
+int lynx_dequantize_full(const lynx_planes *in, int64_t num_pages,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t role,
+                         float *out, void *stream);
+
+/*
+ * Fused-dequant single-query GQA decode attention (anchor-only = draft, or
+ * anchor + residual = Q_full).  K planes must have been written with
+ * LYNX_ROLE_KEY and V planes with LYNX_ROLE_VALUE.
+ *   q            bf16 bits [B][Hq][128]
+ *   k, v         encoded pools of pages (any number of pages)
+ *   block_table  int32 [B][max_pages_per_seq]: pool page index of each
+ *                logical page of each request; NULL = request b owns pool
+ *                pages b*max_pages_per_seq .. + n_b - 1 (then
+ *                batch*max_pages_per_seq must not exceed pool_pages)
+ *   pool_pages   number of pages in the k and v pools; a block-table entry
+ *                outside [0, pool_pages) is skipped (its page contributes
+ *                nothing), so no out-of-bounds read can happen
+ *   seq_lens     int32 [B] tokens per request, a multiple of 256 in
+ *                [256, 256*max_pages_per_seq]; NULL = every request is
+ *                max_pages_per_seq pages long.  Device memory, read on device:
+ *                values outside the range make the output unspecified (no
+ *                out-of-bounds access happens: lengths are clamped).
+ *   sm_scale     softmax scale applied to q . k (e.g. 1/sqrt(128))
+ *   out          fp32 [B][Hq][128]
+ *   scores       optional fp32 [B][Hq][256*max_pages_per_seq]: the scaled
+ *                logits, for ranking comparisons; NULL = not written
+ *   workspace    device scratch of at least
+ *                lynx_decode_attention_workspace_size(...) bytes, 16-byte
+ *                aligned; contents need not be initialised
+ * The anchor variant never reads k->residual or v->residual.  batch = 0 is
+ * a no-op once the shape arguments are valid (no pointer is inspected).
+ * Errors: NULL_ARG, BAD_SHAPE, MISALIGNED, WORKSPACE, DEVICE, HIP.
+ */
+size_t lynx_decode_attention_workspace_size(int32_t batch,
+                                            int32_t num_kv_heads,
+                                            int32_t num_q_heads,
+                                            int32_t head_dim,
+                                            int32_t max_pages_per_seq);
+int lynx_decode_attention_anchor(const uint16_t *q, const lynx_planes *k,
+                                 const lynx_planes *v,
+                                 const int32_t *block_table,
+                                 const int32_t *seq_lens, int32_t batch,
+                                 int32_t num_kv_heads, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_pages_per_seq,
+                                 int64_t pool_pages, float sm_scale,
+                                 float *out, float *scores,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+int lynx_decode_attention_full(const uint16_t *q, const lynx_planes *k,
+                               const lynx_planes *v,
+                               const int32_t *block_table,
+                               const int32_t *seq_lens, int32_t batch,
+                               int32_t num_kv_heads, int32_t num_q_heads,
+                               int32_t head_dim, int32_t max_pages_per_seq,
+                               int64_t pool_pages, float sm_scale,
+                               float *out, float *scores,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Static string for a status code (never NULL). */
+const char *lynx_status_string(int status);
+
+/*
+ * Host-side introspection, for tests (no GPU needed):
+ * lynx_code_thresholds writes the 128 fp32 thresholds T[0..127] the encoder
+ * uses: T[0] = 0 and, for k >= 1, T[k] is the smallest fp32 u with
+ * 127 ln(1 + 255 u)/ln 256 >= k - 1/2, so that m(u) = #{k >= 1 : u >= T[k]}.
+ * lynx_decode_table writes the 256 fp32 values yhat(code) indexed by
+ * code + 128, as used by the dequantizers.
+ */
+void lynx_code_thresholds(float *out128);
+
+/*
+ * Device self-test of the encoder's level computation: for every fp32 bit
+ * pattern b in [begin_bits, end_bits) (end_bits <= 0x3F800001, i.e. values
+ * in [0, 1]), compares the encoder's fast level path with the exact
+ * threshold count and adds the number of disagreements to *mismatches (a
+ * device uint64 the caller zeroes).  Errors: NULL_ARG, BAD_ARG, DEVICE, HIP.
+ */
+int lynx_selftest_code_map(uint32_t begin_bits, uint32_t end_bits,
+                           unsigned long long *mismatches, void *stream);
+void lynx_decode_table(float *out256);
+const char *lynx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LYNX_H */

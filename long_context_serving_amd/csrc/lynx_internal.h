@@ -1,0 +1,91 @@
+// Internal declarations shared by the liblynx translation units.
+//
+// Everything here is product code: host-side constant tables, kernel
+// argument structs and launcher prototypes.  The CPU oracle under oracle/
+// shares nothing with it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lynx.h"
+
+namespace lynx {
+
+constexpr int kPage = LYNX_PAGE_TOKENS;      // 256 tokens per page
+constexpr int kChunk = LYNX_CHUNK_TOKENS;    // C = 32
+constexpr int kChunks = LYNX_CHUNKS_PER_PAGE;
+constexpr int kDim = LYNX_HEAD_DIM;          // 128 channels per head
+constexpr int kLevels = 127;                 // magnitude levels 0..127
+constexpr double kAlpha = 255.0;             // alpha-law constant (a reading)
+
+// Plane bytes per (page, head): 256 tokens x 128 channels x 4 bits.
+constexpr int kPlaneTileBytes = kPage * kDim / 2;  // 16 KiB
+
+// Code-map thresholds: T[0] = 0, T[k] = smallest fp32 u whose level
+// 127 ln(1 + 255u)/ln 256 reaches k - 1/2 (k = 1..127).
+struct CodeTable {
+  float t[128];
+};
+
+// Decode table: yhat for every 8-bit code (index code + 128), fp32.
+struct DecodeTable {
+  float y[256];
+};
+
+const CodeTable &code_table();
+const DecodeTable &decode_table();
+
+// Draft (anchor-only) values for the 16 anchor nibbles (index = nibble,
+// i.e. a & 15): yhat(16a + 7).
+struct DraftTable {
+  float y[16];
+};
+const DraftTable &draft_table();
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipError_t of the launch; argument checking happens in
+// the API layer).
+// ---------------------------------------------------------------------------
+struct PlanesArg {
+  uint8_t *anchor;
+  uint8_t *residual;
+  float *page_min;
+  float *page_range;
+  float *chunk_mean;
+  float *chunk_maxabs;
+};
+
+hipError_t launch_encode(const uint16_t *kv, int64_t num_pages, int heads,
+                         int role, const PlanesArg &out, hipStream_t stream);
+
+hipError_t launch_code_map_check(uint32_t begin, uint32_t end,
+                                 unsigned long long *mismatches, hipStream_t stream);
+
+hipError_t launch_dequant(const PlanesArg &in, int64_t num_pages, int heads,
+                          int role, bool full, float *out,
+                          hipStream_t stream);
+
+struct AttnShape {
+  int batch;
+  int heads;         // KV heads H
+  int q_heads;       // Hq
+  int group;         // Hq / H
+  int max_pages;     // per request
+  int pages_per_split;
+  int splits;
+  long long pool_pages;  // pages in the k / v pools (block-table bound)
+};
+
+AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages);
+size_t attention_workspace_bytes(const AttnShape &s);
+
+hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
+                            const PlanesArg &v, const int32_t *block_table,
+                            const int32_t *seq_lens, const AttnShape &s,
+                            float sm_scale, bool full, float *out,
+                            float *scores, void *workspace,
+                            hipStream_t stream);
+
+}  // namespace lynx

@@ -1,0 +1,103 @@
+// Host-side constant tables of liblynx, built once per process.
+//
+// Code map (page "Lynx: the KV cache does not have to arrive whole",
+// section 3, non-linear transform): the magnitude level of u = |y| in [0,1]
+// is m = round-half-up(127 ln(1 + alpha u) / ln(1 + alpha)), alpha = 255.
+// The encoder takes m exactly as the number of thresholds T[k] <= u, where
+// T[k] is found by bisection over fp32 bit patterns with the level evaluated
+// in double precision.
+//
+// Decode (same section, the cut; section 4 for draft vs full): the 8-bit
+// code q gives m = q >= 0 ? q : ~q and yhat = sign ((1 + alpha)^(m/127) - 1)
+// / alpha, tabulated for all 256 codes; the draft of anchor a is the code
+// 16 a + 7.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "lynx_internal.h"
+
+namespace lynx {
+namespace {
+
+double level_of(float u) {
+  return static_cast<double>(kLevels) * std::log1p(kAlpha * static_cast<double>(u)) /
+         std::log1p(kAlpha);
+}
+
+float float_from_bits(uint32_t b) {
+  float f;
+  std::memcpy(&f, &b, sizeof f);
+  return f;
+}
+
+CodeTable build_code_table() {
+  CodeTable t;
+  t.t[0] = 0.0f;
+  const uint32_t one = 0x3F800000u;  // bits of 1.0f
+  for (int k = 1; k <= kLevels; ++k) {
+    const double target = k - 0.5;
+    // smallest bit pattern b in [0, one] with level(b) >= target
+    uint32_t lo = 0, hi = one;
+    while (lo < hi) {
+      const uint32_t mid = lo + (hi - lo) / 2;
+      if (level_of(float_from_bits(mid)) >= target)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    t.t[k] = float_from_bits(lo);
+  }
+  return t;
+}
+
+double yhat_of_code(int q) {
+  const int m = q >= 0 ? q : -q - 1;
+  const double g = (std::pow(1.0 + kAlpha, static_cast<double>(m) / kLevels) - 1.0) / kAlpha;
+  return q >= 0 ? g : -g;
+}
+
+DecodeTable build_decode_table() {
+  DecodeTable d;
+  for (int q = -128; q < 128; ++q) d.y[q + 128] = static_cast<float>(yhat_of_code(q));
+  return d;
+}
+
+DraftTable build_draft_table() {
+  DraftTable d;
+  for (int nib = 0; nib < 16; ++nib) {
+    const int a = nib >= 8 ? nib - 16 : nib;  // two's complement int4
+    d.y[nib] = static_cast<float>(yhat_of_code(16 * a + 7));
+  }
+  return d;
+}
+
+std::once_flag g_once;
+CodeTable g_code;
+DecodeTable g_decode;
+DraftTable g_draft;
+
+void init_tables() {
+  g_code = build_code_table();
+  g_decode = build_decode_table();
+  g_draft = build_draft_table();
+}
+
+}  // namespace
+
+const CodeTable &code_table() {
+  std::call_once(g_once, init_tables);
+  return g_code;
+}
+
+const DecodeTable &decode_table() {
+  std::call_once(g_once, init_tables);
+  return g_decode;
+}
+
+const DraftTable &draft_table() {
+  std::call_once(g_once, init_tables);
+  return g_draft;
+}
+
+}  // namespace lynx

@@ -1,0 +1,233 @@
+"""Thin Python binding of liblynx (include/lynx.h).
+
+Argument marshalling only: every step of the method runs in the HIP
+library.  PyTorch supplies device memory and streams.  If the library has
+not been built this module raises on import -- there is no fallback path.
+"""
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "liblynx.so")
+
+PAGE = 256
+CHUNK = 32
+CHUNKS = 8
+HEAD_DIM = 128
+MAX_GROUP = 16
+ROLE_KEY = 0
+ROLE_VALUE = 1
+
+LYNX_OK = 0
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("liblynx.so is not built (%s); run `python -m long_context_serving_amd.build` "
+                      "or __graft_entry__.build()" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class _CPlanes(ctypes.Structure):
+    _fields_ = [("anchor", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("page_min", ctypes.c_void_p), ("page_range", ctypes.c_void_p),
+                ("chunk_mean", ctypes.c_void_p), ("chunk_maxabs", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_i32, _i64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_lib.lynx_plane_bytes.argtypes = [_i64, _i32]
+_lib.lynx_plane_bytes.restype = _sz
+_lib.lynx_page_scale_bytes.argtypes = [_i64, _i32]
+_lib.lynx_page_scale_bytes.restype = _sz
+_lib.lynx_chunk_scale_bytes.argtypes = [_i64, _i32]
+_lib.lynx_chunk_scale_bytes.restype = _sz
+_lib.lynx_quantize_pages.argtypes = [_P, _i64, _i32, _i32, _i32, ctypes.POINTER(_CPlanes), _P]
+_lib.lynx_quantize_pages.restype = ctypes.c_int
+for _name in ("lynx_dequantize_anchor", "lynx_dequantize_full"):
+    getattr(_lib, _name).argtypes = [ctypes.POINTER(_CPlanes), _i64, _i32, _i32, _i32, _P, _P]
+    getattr(_lib, _name).restype = ctypes.c_int
+_lib.lynx_decode_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+_lib.lynx_decode_attention_workspace_size.restype = _sz
+for _name in ("lynx_decode_attention_anchor", "lynx_decode_attention_full"):
+    getattr(_lib, _name).argtypes = [_P, ctypes.POINTER(_CPlanes), ctypes.POINTER(_CPlanes), _P, _P,
+                                     _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _P, _P, _P,
+                                     _sz, _P]
+    getattr(_lib, _name).restype = ctypes.c_int
+_lib.lynx_status_string.argtypes = [ctypes.c_int]
+_lib.lynx_status_string.restype = ctypes.c_char_p
+_lib.lynx_code_thresholds.argtypes = [_P]
+_lib.lynx_code_thresholds.restype = None
+_lib.lynx_decode_table.argtypes = [_P]
+_lib.lynx_decode_table.restype = None
+_lib.lynx_selftest_code_map.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _P, _P]
+_lib.lynx_selftest_code_map.restype = ctypes.c_int
+_lib.lynx_version.argtypes = []
+_lib.lynx_version.restype = ctypes.c_char_p
+
+
+class LynxError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (%d)" % (what, _lib.lynx_status_string(status).decode(), status))
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status != LYNX_OK:
+        raise LynxError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def version() -> str:
+    return _lib.lynx_version().decode()
+
+
+def code_thresholds() -> "list[float]":
+    buf = (ctypes.c_float * 128)()
+    _lib.lynx_code_thresholds(ctypes.cast(buf, _P))
+    return list(buf)
+
+
+def decode_table() -> "list[float]":
+    buf = (ctypes.c_float * 256)()
+    _lib.lynx_decode_table(ctypes.cast(buf, _P))
+    return list(buf)
+
+
+def selftest_code_map(begin_bits: int = 0, end_bits: int = 0x3F800001, stream=None) -> int:
+    """Number of fp32 u in [begin, end) bit patterns where the encoder's fast
+    level path disagrees with the exact threshold count (runs on the GPU)."""
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    _check(_lib.lynx_selftest_code_map(begin_bits, end_bits, _ptr(cnt), _stream(stream)),
+           "lynx_selftest_code_map")
+    return int(cnt.item())
+
+
+@dataclass
+class Planes:
+    """One encoded K (role 0) or V (role 1) tensor of one layer.
+
+    anchor / residual: uint8, 16 KiB per (page, head) each, layout by role
+    (see include/lynx.h); scales: fp32 [P][H][128] and [P][H][8][128].
+    """
+    anchor: torch.Tensor
+    residual: Optional[torch.Tensor]
+    page_min: torch.Tensor
+    page_range: torch.Tensor
+    chunk_mean: torch.Tensor
+    chunk_maxabs: torch.Tensor
+    num_pages: int
+    heads: int
+    role: int
+
+    def c(self) -> _CPlanes:
+        return _CPlanes(*(None if t is None else t.data_ptr() for t in
+                          (self.anchor, self.residual, self.page_min, self.page_range,
+                           self.chunk_mean, self.chunk_maxabs)))
+
+    def without_residual(self) -> "Planes":
+        return Planes(self.anchor, None, self.page_min, self.page_range, self.chunk_mean,
+                      self.chunk_maxabs, self.num_pages, self.heads, self.role)
+
+    def nbytes(self, with_residual: bool = True) -> int:
+        n = self.anchor.numel() + self.page_min.numel() * 4 * 2 + self.chunk_mean.numel() * 4 * 2
+        if with_residual and self.residual is not None:
+            n += self.residual.numel()
+        return n
+
+
+def alloc_planes(num_pages: int, heads: int, role: int, device="cuda") -> Planes:
+    pb = _lib.lynx_plane_bytes(num_pages, heads)
+    return Planes(
+        anchor=torch.empty(pb, dtype=torch.uint8, device=device),
+        residual=torch.empty(pb, dtype=torch.uint8, device=device),
+        page_min=torch.empty((num_pages, heads, HEAD_DIM), dtype=torch.float32, device=device),
+        page_range=torch.empty((num_pages, heads, HEAD_DIM), dtype=torch.float32, device=device),
+        chunk_mean=torch.empty((num_pages, heads, CHUNKS, HEAD_DIM), dtype=torch.float32, device=device),
+        chunk_maxabs=torch.empty((num_pages, heads, CHUNKS, HEAD_DIM), dtype=torch.float32, device=device),
+        num_pages=num_pages, heads=heads, role=role)
+
+
+def _bf16_bits(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype == torch.bfloat16:
+        return x
+    if x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError("expected bf16 (or its 16-bit patterns), got %s" % x.dtype)
+
+
+def quantize_pages(kv: torch.Tensor, role: int, out: Optional[Planes] = None, stream=None) -> Planes:
+    """Encode bf16 pages [P][256][H][128] into anchor/residual planes + scales."""
+    kv = _bf16_bits(kv)
+    if kv.dim() != 4 or kv.shape[1] != PAGE or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous [P][256][H][128] bf16 tensor")
+    P, _, H, D = kv.shape
+    if out is None:
+        out = alloc_planes(P, H, role, kv.device)
+    cp = out.c()
+    _check(_lib.lynx_quantize_pages(_ptr(kv), P, H, D, role, ctypes.byref(cp), _stream(stream)),
+           "lynx_quantize_pages")
+    return out
+
+
+def dequantize(planes: Planes, full: bool = True, out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """fp32 reconstruction [P][256][H][128]; full=False is the anchor-only draft."""
+    P, H = planes.num_pages, planes.heads
+    if out is None:
+        out = torch.empty((P, PAGE, H, HEAD_DIM), dtype=torch.float32, device=planes.anchor.device)
+    cp = planes.c()
+    fn = _lib.lynx_dequantize_full if full else _lib.lynx_dequantize_anchor
+    _check(fn(ctypes.byref(cp), P, H, HEAD_DIM, planes.role, _ptr(out), _stream(stream)),
+           "lynx_dequantize_%s" % ("full" if full else "anchor"))
+    return out
+
+
+def workspace_size(batch: int, heads: int, q_heads: int, max_pages: int) -> int:
+    return int(_lib.lynx_decode_attention_workspace_size(batch, heads, q_heads, HEAD_DIM, max_pages))
+
+
+def decode_attention(q: torch.Tensor, k: Planes, v: Planes, max_pages: int, full: bool = True,
+                     block_table: Optional[torch.Tensor] = None,
+                     seq_lens: Optional[torch.Tensor] = None,
+                     sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     scores: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Single-query GQA decode attention over the compact planes.
+
+    q: bf16 [B][Hq][128].  k (role 0) and v (role 1) are page pools; request b
+    reads pool pages block_table[b] (or b*max_pages + i when block_table is
+    None).  Returns fp32 [B][Hq][128].
+    """
+    q = _bf16_bits(q)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][Hq][128] bf16 tensor")
+    B, Hq, D = q.shape
+    H = k.heads
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    need = workspace_size(B, H, Hq, max_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    fn = _lib.lynx_decode_attention_full if full else _lib.lynx_decode_attention_anchor
+    kc, vc = k.c(), v.c()
+    _check(fn(_ptr(q), ctypes.byref(kc), ctypes.byref(vc), _ptr(block_table), _ptr(seq_lens),
+              B, H, Hq, D, max_pages, min(k.num_pages, v.num_pages), float(sm_scale), _ptr(out),
+              _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "lynx_decode_attention_%s" % ("full" if full else "anchor"))
+    return out

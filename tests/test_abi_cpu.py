@@ -1,0 +1,144 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol that
+include/lynx.h declares, rejects bad arguments before touching a GPU, and
+its host-side constant tables agree with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lynx.h")
+LIB = os.path.join(ROOT, "long_context_serving_amd", "_lib", "liblynx.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from long_context_serving_amd import build
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lynx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("lynx_quantize_pages", "lynx_dequantize_anchor", "lynx_dequantize_full",
+                     "lynx_decode_attention_anchor", "lynx_decode_attention_full",
+                     "lynx_decode_attention_workspace_size", "lynx_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+class CPlanes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("anchor", "residual", "page_min", "page_range", "chunk_mean", "chunk_maxabs")]
+
+
+def _fake_planes(base=0x10000):
+    return CPlanes(*(base + 0x1000 * i for i in range(6)))
+
+
+def test_argument_errors_are_reported_before_any_launch(lib):
+    P = ctypes.c_void_p
+    lib.lynx_quantize_pages.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.POINTER(CPlanes), P]
+    pl = _fake_planes()
+    kv = P(0x20000)
+    assert lib.lynx_quantize_pages(None, 4, 8, 128, 0, ctypes.byref(pl), None) == -1
+    assert lib.lynx_quantize_pages(kv, 4, 8, 64, 0, ctypes.byref(pl), None) == -2
+    assert lib.lynx_quantize_pages(kv, -1, 8, 128, 0, ctypes.byref(pl), None) == -2
+    assert lib.lynx_quantize_pages(kv, 4, 0, 128, 0, ctypes.byref(pl), None) == -2
+    assert lib.lynx_quantize_pages(kv, 4, 8, 128, 3, ctypes.byref(pl), None) == -7
+    assert lib.lynx_quantize_pages(P(0x20001), 4, 8, 128, 0, ctypes.byref(pl), None) == -3
+    bad = _fake_planes()
+    bad.residual = None
+    assert lib.lynx_quantize_pages(kv, 4, 8, 128, 0, ctypes.byref(bad), None) == -1
+    bad = _fake_planes()
+    bad.chunk_mean = 0x30004
+    assert lib.lynx_quantize_pages(kv, 4, 8, 128, 1, ctypes.byref(bad), None) == -3
+    # zero pages is a no-op that needs no device
+    assert lib.lynx_quantize_pages(kv, 0, 8, 128, 0, ctypes.byref(pl), None) == 0
+
+    for name in ("lynx_dequantize_anchor", "lynx_dequantize_full"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.POINTER(CPlanes), ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_int32, P, P]
+        assert fn(ctypes.byref(pl), 4, 8, 128, 0, None, None) == -1
+        assert fn(ctypes.byref(pl), 4, 8, 100, 0, P(0x40000), None) == -2
+        assert fn(ctypes.byref(pl), 0, 8, 128, 1, P(0x40000), None) == 0
+    # the anchor dequantizer never needs the residual plane
+    nores = _fake_planes()
+    nores.residual = None
+    assert lib.lynx_dequantize_full(ctypes.byref(nores), 4, 8, 128, 0, P(0x40000), None) == -1
+    assert lib.lynx_dequantize_anchor(ctypes.byref(nores), 0, 8, 128, 0, P(0x40000), None) == 0
+
+    lib.lynx_decode_attention_workspace_size.restype = ctypes.c_size_t
+    lib.lynx_decode_attention_workspace_size.argtypes = [ctypes.c_int32] * 5
+    need = lib.lynx_decode_attention_workspace_size(2, 8, 64, 128, 16)
+    assert need > 0
+    assert lib.lynx_decode_attention_workspace_size(2, 8, 60, 128, 16) == 0   # Hq % H != 0
+    assert lib.lynx_decode_attention_workspace_size(2, 2, 64, 128, 16) == 0   # group 32 > 16
+    for name in ("lynx_decode_attention_anchor", "lynx_decode_attention_full"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, ctypes.POINTER(CPlanes), ctypes.POINTER(CPlanes), P, P,
+                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_int32, ctypes.c_int64, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+        q, out, ws = P(0x50000), P(0x60000), P(0x70000)
+        args = lambda **kw: dict(dict(q=q, bt=None, sl=None, B=2, H=8, Hq=64, D=128, mp=16, pool=32,
+                                      ws=ws, wsb=need), **kw)
+
+        def call(a):
+            return fn(a["q"], ctypes.byref(pl), ctypes.byref(pl), a["bt"], a["sl"], a["B"], a["H"],
+                      a["Hq"], a["D"], a["mp"], a["pool"], 0.088, out, None, a["ws"], a["wsb"], None)
+        assert call(args(q=None)) == -1
+        assert call(args(D=96)) == -2
+        assert call(args(Hq=60)) == -2
+        assert call(args(pool=31)) == -2            # contiguous pools too small for B*max_pages
+        assert call(args(wsb=need - 1)) == -4
+        assert call(args(ws=None)) == -4
+        assert call(args(q=P(0x50002))) == -3
+        assert call(args(B=0)) == 0                 # empty batch: no-op
+
+
+def test_status_strings(lib):
+    lib.lynx_status_string.restype = ctypes.c_char_p
+    for code in range(-7, 1):
+        assert lib.lynx_status_string(code)
+    assert lib.lynx_status_string(-99) == b"unknown status"
+
+
+def test_code_thresholds_agree_with_the_oracle(lib):
+    """T[k] is the first fp32 u the oracle puts on level >= k (away from the
+    oracle's 2^-20 boundary window)."""
+    buf = (ctypes.c_float * 128)()
+    lib.lynx_code_thresholds(buf)
+    T = np.array(buf[:], np.float32)
+    assert T[0] == 0.0 and np.all(np.diff(T) > 0) and T[-1] < 1.0
+    below = np.nextafter(T[1:], np.float32(0.0)).astype(np.float32)
+    q_at, f_at = oracle.codes(T[1:])
+    q_below, f_below = oracle.codes(below)
+    k = np.arange(1, 128)
+    ok_at = (q_at == k) | (f_at != 0)
+    ok_below = (q_below == k - 1) | (f_below != 0)
+    assert ok_at.all() and ok_below.all()
+
+
+def test_decode_table_agrees_with_the_oracle(lib):
+    buf = (ctypes.c_float * 256)()
+    lib.lynx_decode_table(buf)
+    y = np.array(buf[:], np.float32)
+    ref = oracle.yhat(np.arange(-128, 128))
+    assert np.array_equal(y, ref.astype(np.float32))     # correctly rounded fp32 of the fp64 value

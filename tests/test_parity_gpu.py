@@ -1,0 +1,311 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar (element by element, same seeded inputs):
+  codes       bit-exact, except +-1 on elements the oracle flags as lying
+              within 2^-20 of a rounding boundary;
+  scales      bit-exact (page min/range, chunk mean/max-abs);
+  dequant     |gpu - oracle| <= 1e-3 |oracle|, or <= 1e-6 * page range where
+              the reconstruction cancels to ~0;
+  attention   max |gpu - oracle| <= 2e-3 (oracle in fp64 over its own
+              dequantized K and V).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_serving_amd import synth
+from planes_layout import unpack_codes
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATOL_ATTN = 2e-3
+RTOL_DQ = 1e-3
+FLOOR_DQ = 1e-6
+SM = float(np.float32(1.0 / math.sqrt(128.0)))
+
+
+@pytest.fixture(scope="module")
+def lynx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_serving_amd import lynx as mod
+    return mod
+
+
+def to_dev(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def gpu_codes(pl, P, H, role):
+    a = pl.anchor.cpu().numpy()
+    r = pl.residual.cpu().numpy()
+    return unpack_codes(a, r, P, H, role)
+
+
+def check_encode(lynx, x_bits, role, enc=None):
+    P, _, H, _ = x_bits.shape
+    print("encode parity P=%d H=%d role=%d" % (P, H, role), flush=True)
+    if enc is None:
+        enc = oracle.encode(x_bits)
+    pl = lynx.quantize_pages(to_dev(x_bits), role)
+    torch.cuda.synchronize()
+    a, r, code = gpu_codes(pl, P, H, role)
+    ref = enc["codes"]
+    assert not (enc["flags"] & oracle.FLAG_SUM_INEXACT).any(), "input breaks the exact-sum precondition"
+    near = (enc["flags"] & oracle.FLAG_NEAR_HALF) != 0
+    mism = code != ref
+    assert not (mism & ~near).any(), "unflagged code mismatches: %d" % int((mism & ~near).sum())
+    assert (np.abs(code.astype(np.int16) - ref.astype(np.int16))[mism] <= 1).all()
+    for name in ("page_min", "page_range", "chunk_mean", "chunk_maxabs"):
+        got = getattr(pl, name).cpu().numpy().reshape(enc[name].shape)
+        assert np.array_equal(got.view(np.uint32), enc[name].view(np.uint32)), name
+    return pl, enc, (a, r, code), int(mism.sum())
+
+
+def check_dequant(lynx, pl, enc, gpu_code, full):
+    a_ref, r_ref = oracle.split(enc["codes"])
+    ref = oracle.dequant(a_ref, r_ref if full else None, enc)
+    got = lynx.dequantize(pl, full=full).cpu().numpy().astype(np.float64)
+    same = gpu_code == enc["codes"] if full else (gpu_code >> 4) == (enc["codes"] >> 4)
+    rg = np.broadcast_to(enc["page_range"][:, None].astype(np.float64), ref.shape)
+    err = np.abs(got - ref)
+    ok = (err <= RTOL_DQ * np.abs(ref)) | (err <= FLOOR_DQ * rg)
+    assert ok[same].all(), "dequant mismatch: max rel %g" % float((err / np.maximum(np.abs(ref), 1e-30))[same & ~ok].max())
+
+
+def oracle_attention_for(enc_k, enc_v, q_bits, page_lists, full, want_logits=False):
+    """Oracle attention for requests whose logical pages are page_lists[b] (pool indices)."""
+    ak, rk = oracle.split(enc_k["codes"])
+    av, rv = oracle.split(enc_v["codes"])
+    kh = oracle.dequant(ak, rk if full else None, enc_k)
+    vh = oracle.dequant(av, rv if full else None, enc_v)
+    q = oracle.bf16_bits_to_float(q_bits).astype(np.float64)
+    outs, logits = [], []
+    for b, pages in enumerate(page_lists):
+        H, D = kh.shape[2], kh.shape[3]
+        kk = kh[pages].reshape(1, -1, H, D)
+        vv = vh[pages].reshape(1, -1, H, D)
+        res = oracle.attention(q[b:b + 1], kk, vv, SM, want_logits=want_logits)
+        if want_logits:
+            outs.append(res[0][0])
+            logits.append(res[1][0])
+        else:
+            outs.append(res[0])
+    return (np.stack(outs), logits) if want_logits else np.stack(outs)
+
+
+def run_gpu_attention(lynx, q_bits, pk, pv, max_pages, full, block_table=None, seq_lens=None,
+                      scores=None):
+    q = to_dev(q_bits)
+    bt = None if block_table is None else torch.from_numpy(np.asarray(block_table, np.int32)).cuda()
+    sl = None if seq_lens is None else torch.from_numpy(np.asarray(seq_lens, np.int32)).cuda()
+    out = lynx.decode_attention(q, pk, pv, max_pages, full=full, block_table=bt, seq_lens=sl,
+                                sm_scale=SM, scores=scores)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def encode_pair(lynx, w, layer=0, request=0, tokens=None):
+    xk = synth.kv_pages(w, layer, 0, request, tokens=tokens)
+    xv = synth.kv_pages(w, layer, 1, request, tokens=tokens)
+    pk, ek, ck, _ = check_encode(lynx, xk, 0)
+    pv, ev, cv, _ = check_encode(lynx, xv, 1)
+    return pk, ek, ck, pv, ev, cv
+
+
+# ---------------------------------------------------------------------------
+# Tiny workload: 4 pages, 4 KV heads, 32 query heads
+# ---------------------------------------------------------------------------
+def test_tiny_encode_dequant_attention(lynx):
+    w = synth.WORKLOADS["tiny"]
+    pk, ek, ck, pv, ev, cv = encode_pair(lynx, w)
+    for full in (False, True):
+        check_dequant(lynx, pk, ek, ck[2], full)
+        check_dequant(lynx, pv, ev, cv[2], full)
+    q = synth.queries(w)
+    for full in (False, True):
+        ref = oracle_attention_for(ek, ev, q, [list(range(w.pages))], full)
+        got = run_gpu_attention(lynx, q, pk, pv, w.pages, full)
+        err = np.abs(got - ref).max()
+        print("tiny attention full=%s max abs err %.3g" % (full, err), flush=True)
+        assert err <= ATOL_ATTN
+
+
+def test_anchor_calls_never_need_the_residual(lynx):
+    w = synth.WORKLOADS["tiny"]
+    pk, ek, ck, pv, ev, cv = encode_pair(lynx, w)
+    q = synth.queries(w)
+    with_res = run_gpu_attention(lynx, q, pk, pv, w.pages, False)
+    without = run_gpu_attention(lynx, q, pk.without_residual(), pv.without_residual(), w.pages, False)
+    assert np.array_equal(with_res, without)
+    d1 = lynx.dequantize(pk.without_residual(), full=False).cpu().numpy()
+    d2 = lynx.dequantize(pk, full=False).cpu().numpy()
+    assert np.array_equal(d1, d2)
+    with pytest.raises(lynx.LynxError):
+        lynx.dequantize(pk.without_residual(), full=True)
+
+
+# ---------------------------------------------------------------------------
+# 32K context (the benchmark workload), full size
+# ---------------------------------------------------------------------------
+def test_ctx32k_full_size(lynx):
+    w = synth.WORKLOADS["ctx32k"]
+    pk, ek, ck, pv, ev, cv = encode_pair(lynx, w)
+    check_dequant(lynx, pk, ek, ck[2], True)
+    check_dequant(lynx, pv, ev, cv[2], False)
+    q = synth.queries(w)
+    T = w.tokens
+    for full in (False, True):
+        scores = torch.empty((1, w.q_heads, T), dtype=torch.float32, device="cuda")
+        ref, logits = oracle_attention_for(ek, ev, q, [list(range(w.pages))], full, want_logits=True)
+        got = run_gpu_attention(lynx, q, pk, pv, w.pages, full, scores=scores)
+        err = np.abs(got - ref).max()
+        print("ctx32k attention full=%s max abs err %.3g (max |out| %.1f)" % (full, err, np.abs(ref).max()),
+              flush=True)
+        assert err <= ATOL_ATTN
+        sc = scores.cpu().numpy()[0].astype(np.float64)
+        lg = logits[0]
+        assert np.abs(sc - lg).max() <= 1e-4 * max(1.0, np.abs(lg).max())
+        # top-1 token per head agrees unless the oracle's top-2 gap is tiny
+        srt = np.sort(lg, axis=1)
+        clear = (srt[:, -1] - srt[:, -2]) > 1e-3
+        assert np.array_equal(sc.argmax(1)[clear], lg.argmax(1)[clear])
+
+
+# ---------------------------------------------------------------------------
+# Batched decode: 64 requests x 16K; the GPU runs the full batch, the oracle
+# checks sampled requests (the others are copies, which must agree bitwise)
+# ---------------------------------------------------------------------------
+def test_batched_64x16k_sampled(lynx):
+    w = synth.WORKLOADS["batched64x16k"]
+    sampled = [0, 1]
+    P = w.pages
+    xk = [synth.kv_pages(w, 0, 0, r) for r in sampled]
+    xv = [synth.kv_pages(w, 0, 1, r) for r in sampled]
+    ek = [oracle.encode(x) for x in xk]
+    ev = [oracle.encode(x) for x in xv]
+    # pool: request b uses the pages of sampled request b % 2, laid out in a
+    # permuted order through the block table
+    pool_k = np.concatenate([xk[b % 2] for b in range(w.batch)])
+    pool_v = np.concatenate([xv[b % 2] for b in range(w.batch)])
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(w.batch * P)              # logical page -> pool slot
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size)
+    pk = lynx.quantize_pages(to_dev(pool_k[inv]), 0)
+    pv = lynx.quantize_pages(to_dev(pool_v[inv]), 1)
+    block_table = perm.reshape(w.batch, P).astype(np.int32)
+    q_all = synth.queries(w)
+    q = np.stack([q_all[b % 2] if b >= 2 else q_all[b] for b in range(w.batch)])
+    for full in (False, True):
+        got = run_gpu_attention(lynx, q, pk, pv, P, full, block_table=block_table)
+        for i, r in enumerate(sampled):
+            ref = oracle_attention_for(ek[i], ev[i], q[r:r + 1], [list(range(P))], full)
+            err = np.abs(got[r] - ref[0]).max()
+            print("batched request %d full=%s err %.3g" % (r, full, err), flush=True)
+            assert err <= ATOL_ATTN
+        for b in range(2, w.batch):
+            assert np.array_equal(got[b], got[b % 2])
+
+
+# ---------------------------------------------------------------------------
+# Qwen3-235B-A22B shape: encode of one layer (512 pages x 4 heads), K and V
+# ---------------------------------------------------------------------------
+def test_qwen3_235b_layer_encode(lynx):
+    w = synth.WORKLOADS["qwen3_235b_128k"]
+    for tensor, role in ((0, 0), (1, 1)):
+        x = synth.kv_pages(w, 47, tensor, 0)
+        check_encode(lynx, x, role)
+
+
+# ---------------------------------------------------------------------------
+# Progressive-arrival shape: one layer of 64K context, both variants
+# ---------------------------------------------------------------------------
+def test_progressive_layer_attention(lynx):
+    w = synth.WORKLOADS["progressive32x64k"]
+    pk, ek, ck, pv, ev, cv = encode_pair(lynx, w, layer=5)
+    q = synth.queries(w)
+    for full in (False, True):
+        ref = oracle_attention_for(ek, ev, q, [list(range(w.pages))], full)
+        got = run_gpu_attention(lynx, q, pk, pv, w.pages, full)
+        assert np.abs(got - ref).max() <= ATOL_ATTN
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+def test_degenerate_channels_and_chunks(lynx):
+    x = synth.laplace_pages(3, 2, 128, seed=91, scale_channels=((0, 5, 100.0), (1, 77, 100.0)))
+    xf = oracle.bf16_bits_to_float(x).copy()
+    xf[:, :, 0, 3] = 1.5                         # constant channel (range 0)
+    xf[1, 64:96, 1, 9] = xf[1, 70, 1, 9]         # constant chunk (max-abs 0)
+    xf[2, :, 1, 10] = np.arange(256) * 0.25      # exact ramp
+    xf[0, :, 0, 11] = np.float32(2.0 ** -20) * np.sign(xf[0, :, 0, 11])  # two-valued channel
+    x = synth.float_to_bf16_bits(xf)
+    for role in (0, 1):
+        pl, enc, codes, _ = check_encode(lynx, x, role)
+        check_dequant(lynx, pl, enc, codes[2], True)
+        check_dequant(lynx, pl, enc, codes[2], False)
+
+
+def test_empty_inputs(lynx):
+    x = np.zeros((0, 256, 2, 128), np.uint16)
+    pl = lynx.alloc_planes(1, 2, 0)
+    out = lynx.quantize_pages(to_dev(x), 0, out=pl)
+    torch.cuda.synchronize()
+    assert out is pl
+    q = to_dev(np.zeros((0, 16, 128), np.uint16))
+    o = lynx.decode_attention(q, pl, pl, 1, full=True)
+    assert o.shape == (0, 16, 128)
+
+
+def test_ragged_lengths_group_sizes_and_skipped_pages(lynx):
+    rng = np.random.default_rng(13)
+    for H, Hq in ((2, 32), (4, 4), (1, 8)):
+        P_pool = 9
+        x_k = synth.laplace_pages(P_pool, H, 128, seed=H * 100 + 1, scale_channels=((0, 2, 80.0),))
+        x_v = synth.laplace_pages(P_pool, H, 128, seed=H * 100 + 2, scale_channels=((H - 1, 100, 90.0),))
+        pk, ek, _, _ = check_encode(lynx, x_k, 0)
+        pv, ev, _, _ = check_encode(lynx, x_v, 1)
+        max_pages = 4
+        lengths = [1, 4, 3]
+        bt = np.full((3, max_pages), -1, np.int32)
+        pages = []
+        for b, n in enumerate(lengths):
+            pg = rng.choice(P_pool, size=n, replace=False)
+            bt[b, :n] = pg
+            pages.append(list(pg))
+        # an out-of-range entry inside a request's length is skipped
+        bt[1, 2] = P_pool + 7
+        pages[1] = [p for i, p in enumerate(pages[1]) if i != 2]
+        q = synth.float_to_bf16_bits(rng.laplace(0, 1, (3, Hq, 128)).astype(np.float32))
+        for full in (False, True):
+            ref = oracle_attention_for(ek, ev, q, pages, full)
+            got = run_gpu_attention(lynx, q, pk, pv, max_pages, full, block_table=bt,
+                                    seq_lens=[256 * n for n in lengths])
+            err = np.abs(got - ref).max()
+            print("ragged H=%d Hq=%d full=%s err %.3g" % (H, Hq, full, err), flush=True)
+            assert err <= ATOL_ATTN
+
+
+def test_repeat_runs_are_bitwise_identical(lynx):
+    w = synth.WORKLOADS["tiny"]
+    x = synth.kv_pages(w, 0, 0, 0)
+    t = to_dev(x)
+    p1 = lynx.quantize_pages(t, 1)
+    p2 = lynx.quantize_pages(t, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(p1.anchor, p2.anchor) and torch.equal(p1.residual, p2.residual)
+    q = to_dev(synth.queries(w))
+    o1 = lynx.decode_attention(q, lynx.quantize_pages(t, 0), p1, w.pages)
+    o2 = lynx.decode_attention(q, lynx.quantize_pages(t, 0), p2, w.pages)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_code_map_fast_path_is_exact_for_every_fp32_in_unit_interval(lynx):
+    """Exhaustive: all 1,065,353,217 fp32 values u in [0, 1]."""
+    assert lynx.selftest_code_map(0, 0x3F800001) == 0
