@@ -19,7 +19,8 @@
 // Numeric contract (shared with the C ABI header): the statistics are fp32
 // IEEE operations without contraction (this file is built with
 // -ffp-contract=off), reciprocals are correctly rounded, the chunk sum is
-// exact in fp64, and the level m is exactly #{k >= 1 : u >= T[k]}.
+// exact in fp64, the page range and chunk max-abs keep 7 significant bits
+// (rounded up), and the level m is exactly #{k >= 1 : u >= T[k]}.
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -63,6 +64,13 @@ __device__ __forceinline__ int level_of(float u, const float *T) {
   m = m > 127 ? 127 : m;
   if (f < kNearWindow || f > 1.0f - kNearWindow) m = level_exact(u, T);
   return m;
+}
+
+// Keep 7 significant bits, rounding towards +infinity (x >= 0, finite).
+__device__ __forceinline__ float round_up_7bits(float x) {
+  uint32_t b = __float_as_uint(x);
+  if (b & 0x1FFFFu) b = (b + 0x1FFFFu) & ~0x1FFFFu;
+  return __uint_as_float(b);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -134,7 +142,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
       a = fminf(a, s_min[cc][d]);
       b = fmaxf(b, s_max[cc][d]);
     }
-    const float rg = b - a;
+    // the range is kept with 7 significant bits (rounded up), which makes
+    // every scale product exact in the decoder's fp16 operand halves
+    const float rg = round_up_7bits(b - a);
     // correctly rounded fp32 reciprocal (fp64 quotient, one rounding)
     const float inv = rg > 0.0f ? static_cast<float>(1.0 / static_cast<double>(rg)) : 0.0f;
     s_mn[d] = a;
@@ -188,6 +198,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
   for (int i = 0; i < 8; ++i) {
     sabs[i] = fmaxf(sabs[i], __shfl_xor(sabs[i], 16));
     sabs[i] = fmaxf(sabs[i], __shfl_xor(sabs[i], 32));
+    sabs[i] = round_up_7bits(sabs[i]);
   }
   // each of the 4 lanes sharing these channels computes 2 of the 8
   // reciprocals; the rest are gathered from the other lanes

@@ -31,6 +31,9 @@
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
+ *   the page range and the chunk max-abs are kept with 7 significant bits,
+ *   rounded up (so normalised values stay inside [0,1] and [-1,1]); the
+ *   scales are stored as fp32 values carrying those 7 bits;
  *   alpha = 255 (mu-law constant); F(u) = ln(1+alpha u)/ln(1+alpha);
  *   magnitude m = floor(127 F(|y|) + 1/2) in 0..127;
  *   code q = m for y >= 0, q = -m-1 (= ~m) for y < 0;
@@ -104,6 +107,17 @@ static double yhat_of(int q)
     return q >= 0 ? g : -g;
 }
 
+/* Round a non-negative finite float up to 7 significant bits (clear the low
+ * 17 of the 23 stored mantissa bits, rounding towards +infinity). */
+static float round_up_7bits(float x)
+{
+    uint32_t b;
+    memcpy(&b, &x, sizeof b);
+    if ((b & 0x1FFFFu) != 0u) b = (b + 0x1FFFFu) & ~0x1FFFFu;
+    memcpy(&x, &b, sizeof x);
+    return x;
+}
+
 static int nthreads_or_default(int32_t n)
 {
 #ifdef _OPENMP
@@ -148,7 +162,7 @@ static void encode_channel(const uint16_t *x, int64_t p, int32_t h, int32_t d,
         if (v[t] < mn) mn = v[t];
         if (v[t] > mx) mx = v[t];
     }
-    float rg = mx - mn;                         /* fp32 */
+    float rg = round_up_7bits(mx - mn);          /* fp32 difference, then 7 bits */
     float inv_rg = rg > 0.0f ? 1.0f / rg : 0.0f; /* fp32, correctly rounded */
     for (int t = 0; t < OR_PAGE; ++t) {
         float diff = v[t] - mn;                  /* fp32 */
@@ -181,6 +195,7 @@ static void encode_channel(const uint16_t *x, int64_t p, int32_t h, int32_t d,
             float a = fabsf(dv[i]);
             if (a > s) s = a;
         }
+        s = round_up_7bits(s);
         float inv_s = s > 0.0f ? 1.0f / s : 0.0f;  /* fp32, correctly rounded */
         const int64_t cidx = (((p * H + h) * OR_NCHUNK + c) * (int64_t)D) + d;
         chunk_mean[cidx] = mu;

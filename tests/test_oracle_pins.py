@@ -315,11 +315,32 @@ def test_ramp_pages_closed_form_codes():
                 got = enc["codes"][p, :, h, d].astype(np.int32)
                 assert np.array_equal(got[safe], want[safe]), (p, h, d)
                 k = (d + 2 * h + p) % 6 - 2
-                assert enc["page_range"][p, h, d] == np.float32(255.0 * 2.0 ** k)
-                np.testing.assert_allclose(enc["chunk_mean"][p, h, :, d],
-                                           (32 * np.arange(8) + 15.5) / 255.0 if not rev
-                                           else (255 - 32 * np.arange(8) - 15.5) / 255.0, rtol=1e-6)
-                np.testing.assert_allclose(enc["chunk_maxabs"][p, h, :, d], 15.5 / 255.0, rtol=1e-5)
+                # span 255 * 2^k kept with 7 significant bits, rounded up: 256 * 2^k,
+                # so x' = t / 256 exactly and the chunk statistics are exact
+                assert enc["page_range"][p, h, d] == np.float32(256.0 * 2.0 ** k)
+                want_mu = (32 * np.arange(8) + 15.5) / 256.0 if not rev else (255 - 32 * np.arange(8) - 15.5) / 256.0
+                assert np.array_equal(enc["chunk_mean"][p, h, :, d], want_mu.astype(np.float32))
+                assert np.all(enc["chunk_maxabs"][p, h, :, d] == np.float32(15.5 / 256.0))
+
+
+def test_scales_carry_seven_significant_bits_rounded_up():
+    """Reading: the page range and chunk max-abs are kept with 7 significant
+    bits, rounded up, so they never undercut the true span / deviation and
+    exceed it by less than 2^-6 relative."""
+    x = synth.laplace_pages(4, 3, 32, seed=52, scale_channels=((1, 4, 100.0),))
+    enc = oracle.encode(x)
+    xf = oracle.bf16_bits_to_float(x).astype(np.float64)
+    for name in ("page_range", "chunk_maxabs"):
+        v = enc[name]
+        assert np.all((v.view(np.uint32) & 0x1FFFF) == 0), name
+    span = xf.max(axis=1) - xf.min(axis=1)                       # [P][H][D]
+    rg = enc["page_range"].astype(np.float64)
+    assert np.all(rg >= span * (1 - 2.0 ** -24)) and np.all(rg < span * (1 + 2.0 ** -6) + 1e-30)
+    pm, pr, cm, cs = _stats_per_element(enc, 256)
+    xn = (xf - pm) / pr
+    dev = np.abs(xn - cm).reshape(4, 8, 32, 3, 32).max(axis=2)  # [P][c][H][D]
+    s = np.transpose(enc["chunk_maxabs"], (0, 2, 1, 3)).astype(np.float64)
+    assert np.all(s >= dev * (1 - 2.0 ** -20)) and np.all(s <= dev * (1 + 2.0 ** -6) + 1e-12)
 
 
 # ---------------------------------------------------------------------------
