@@ -14,8 +14,9 @@
 //   score_tj = sum_d (sm*q_jd*c1_cd) yhat_td + sum_d sm*q_jd*c0_cd
 //            = dot(q'_cj, yhat_t) + bias_cj
 //   and o_jd = sum_c [c1v_cd * sum_{t in c} p_tj yhat_td + c0v_cd * sum_{t in c} p_tj].
-// The bias and the final score are assembled in fp64 so that the only fp32
-// roundings sit in the small per-channel products, never at the score's
+// q' = q * rg * s is exact in fp32 (the encoder keeps rg and s with 7
+// significant bits), the dot product runs in fp64, and the bias and the
+// softmax scale are applied in fp64, so no score is rounded to fp32 at its
 // full magnitude (with 100x outlier channels scores reach a few hundred).
 //
 // Split-K: each workgroup reduces a contiguous run of pages of one (request,
@@ -29,7 +30,8 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kMaxG = LYNX_MAX_GROUP;
-constexpr int kTargetBlocks = 2048;
+constexpr int kTargetBlocks = 2048;      // VALU kernel (group > 8)
+constexpr int kTargetBlocksMfma = 1024;  // MFMA kernel: 4 waves per block
 
 struct YTable {
   float y[256];
@@ -80,10 +82,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
   int p1 = p0 + s.pages_per_split;
   p1 = p1 > npages ? npages : p1;
 
-  __shared__ double s_q[kMaxG][kDim];     // sm * q in fp64
-  __shared__ float s_qp[kMaxG][kDim];     // q' = sm * q * c1 (per chunk)
+  __shared__ double s_q[kMaxG][kDim];     // q (exact bf16 values)
+  __shared__ float s_qp[kMaxG][kDim];     // q' = q * c1 (per chunk; exact in fp32)
   __shared__ double s_c0k[kDim], s_c1k[kDim];
-  __shared__ float s_c0v[kDim], s_c1v[kDim];
+  __shared__ double s_c0v[kDim], s_c1v[kDim];
   __shared__ double s_bias[kMaxG];
   __shared__ double s_score[kChunk][kMaxG];
   __shared__ float s_p[kChunk][kMaxG];
@@ -96,8 +98,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
   for (int e = tid; e < g * kDim; e += kAttnThreads) {
     const int j = e / kDim, d = e % kDim;
     const uint16_t bits = q[(static_cast<size_t>(b) * s.q_heads + h * g + j) * kDim + d];
-    s_q[j][d] = static_cast<double>(__uint_as_float(static_cast<uint32_t>(bits) << 16)) *
-                static_cast<double>(sm_scale);
+    s_q[j][d] = static_cast<double>(__uint_as_float(static_cast<uint32_t>(bits) << 16));
   }
   if (tid < kMaxG) {
     s_m[tid] = -INFINITY;
@@ -106,9 +107,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
   // value accumulators: thread (d, half) owns heads 8*half .. 8*half+7
   const int vd = tid & (kDim - 1);
   const int vhalf = tid >> 7;
-  float acc[8];
+  double acc[8];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) acc[jj] = 0.0f;
+  for (int jj = 0; jj < 8; ++jj) acc[jj] = 0.0;
   __syncthreads();
 
   const size_t T = static_cast<size_t>(s.max_pages) * kPage;
@@ -133,8 +134,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
         const double rg = vp.page_range[tile * kDim + d];
         const double mu = vp.chunk_mean[(tile * kChunks + c) * kDim + d];
         const double sc = vp.chunk_maxabs[(tile * kChunks + c) * kDim + d];
-        s_c0v[d] = static_cast<float>(mn + rg * mu);
-        s_c1v[d] = static_cast<float>(rg * sc);
+        s_c0v[d] = mn + rg * mu;
+        s_c1v[d] = rg * sc;
       }
       __syncthreads();
       for (int e = tid; e < g * kDim; e += kAttnThreads) {
@@ -171,14 +172,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
           y[8 + i] = s_y[table_index((a2.y >> (4 * i)) & 15u, (r2.y >> (4 * i)) & 15u)];
         }
         for (int j = 0; j < g; ++j) {
-          float dot = 0.0f;
+          // fp32 operands, fp64 accumulation: every product is exact and the
+          // sum is never rounded at the score's magnitude in fp32
+          double dot = 0.0;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) dot = __builtin_fmaf(s_qp[j][cg * 16 + i], y[i], dot);
+          for (int i = 0; i < 16; ++i)
+            dot = fma(static_cast<double>(s_qp[j][cg * 16 + i]), static_cast<double>(y[i]), dot);
           dot += __shfl_xor(dot, 1);
           dot += __shfl_xor(dot, 2);
           dot += __shfl_xor(dot, 4);
           if (cg == 0) {
-            const double sc = static_cast<double>(dot) + s_bias[j];
+            const double sc = (dot + s_bias[j]) * static_cast<double>(sm_scale);
             s_score[t][j] = sc;
             if (scores)
               scores[(static_cast<size_t>(b) * s.q_heads + h * g + j) * T +
@@ -243,8 +247,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
       for (int jj = 0; jj < 8; ++jj) {
         const int j = vhalf * 8 + jj;
         if (j < g) {
-          const float tot = s_part[0][j][vd] + s_part[1][j][vd];
-          acc[jj] = acc[jj] * s_scale[j] + s_c1v[vd] * tot + s_c0v[vd] * s_psum[j];
+          const double tot = static_cast<double>(s_part[0][j][vd]) + s_part[1][j][vd];
+          acc[jj] = acc[jj] * s_scale[j] + s_c1v[vd] * tot + s_c0v[vd] * static_cast<double>(s_psum[j]);
         }
       }
       __syncthreads();
@@ -261,10 +265,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const int j = vhalf * 8 + jj;
-    if (j < g) pt.o[(base + j) * kDim + vd] = acc[jj];
+    if (j < g) pt.o[(base + j) * kDim + vd] = static_cast<float>(acc[jj]);
   }
 }
 
+// Exact merge of the (m, l, o) partials of every split of one (request, KV
+// head): weights exp(m_s - M) are computed once per split into LDS, then
+// each thread sums its channel.
 __global__ __launch_bounds__(kDim) void attn_combine_kernel(AttnShape s, const void *ws,
                                                              float *__restrict__ out) {
   const int bj = blockIdx.x;  // b * Hq + head
@@ -275,17 +282,44 @@ __global__ __launch_bounds__(kDim) void attn_combine_kernel(AttnShape s, const v
   const int d = threadIdx.x;
   Partials pt = partials_of(const_cast<void *>(ws), s);
   const size_t first = (static_cast<size_t>(b) * s.heads + h) * s.splits;
+  __shared__ double s_red[kDim];
+  __shared__ float s_w[kDim];
   double M = -INFINITY;
-  for (int sp = 0; sp < s.splits; ++sp) M = fmax(M, pt.m[(first + sp) * s.group + j]);
-  double L = 0.0, O = 0.0;
-  for (int sp = 0; sp < s.splits; ++sp) {
-    const size_t r = (first + sp) * s.group + j;
-    const double m = pt.m[r];
-    if (m == -INFINITY) continue;
-    const double w = exp(m - M);
-    L += w * pt.l[r];
-    O += w * pt.o[r * kDim + d];
+  for (int sp = d; sp < s.splits; sp += kDim) M = fmax(M, pt.m[(first + sp) * s.group + j]);
+  s_red[d] = M;
+  __syncthreads();
+  for (int off = kDim / 2; off > 0; off >>= 1) {
+    if (d < off) s_red[d] = fmax(s_red[d], s_red[d + off]);
+    __syncthreads();
   }
+  M = s_red[0];
+  __syncthreads();
+  double L = 0.0, O = 0.0;
+  for (int sp0 = 0; sp0 < s.splits; sp0 += kDim) {
+    const int sp = sp0 + d;
+    float wgt = 0.0f;
+    if (sp < s.splits) {
+      const size_t r = (first + sp) * s.group + j;
+      const double m = pt.m[r];
+      wgt = m == -INFINITY ? 0.0f : static_cast<float>(exp(m - M));
+      L += static_cast<double>(wgt) * pt.l[r];
+    }
+    s_w[d] = wgt;
+    __syncthreads();
+    const int cnt = s.splits - sp0 < kDim ? s.splits - sp0 : kDim;
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = s_w[k];
+      if (wk != 0.0f) O += static_cast<double>(wk) * pt.o[((first + sp0 + k) * s.group + j) * kDim + d];
+    }
+    __syncthreads();
+  }
+  s_red[d] = L;
+  __syncthreads();
+  for (int off = kDim / 2; off > 0; off >>= 1) {
+    if (d < off) s_red[d] += s_red[d + off];
+    __syncthreads();
+  }
+  L = s_red[0];
   out[static_cast<size_t>(bj) * kDim + d] = L > 0.0 ? static_cast<float>(O / L) : 0.0f;
 }
 
@@ -300,7 +334,8 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
   s.max_pages = max_pages;
   s.pool_pages = 0;
   const long long units = static_cast<long long>(batch) * heads;
-  long long pps = units > 0 ? (units * max_pages + kTargetBlocks - 1) / kTargetBlocks : 1;
+  const long long target = attention_mfma_supported(s.group) ? kTargetBlocksMfma : kTargetBlocks;
+  long long pps = units > 0 ? (units * max_pages + target - 1) / target : 1;
   if (pps < 1) pps = 1;
   if (pps > max_pages) pps = max_pages > 0 ? max_pages : 1;
   s.pages_per_split = static_cast<int>(pps);
@@ -321,6 +356,14 @@ hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
                             float *scores, void *workspace,
                             hipStream_t stream) {
   if (s.batch == 0) return hipSuccess;
+  if (attention_mfma_supported(s.group)) {
+    const hipError_t e = launch_attention_mfma(q, k, v, block_table, seq_lens, s, sm_scale, full,
+                                               scores, workspace, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>(s.batch * s.q_heads)),
+                       dim3(kDim), 0, stream, s, static_cast<const void *>(workspace), out);
+    return hipGetLastError();
+  }
   YTable tab;
   const DecodeTable &dt = decode_table();
   for (int i = 0; i < 256; ++i) tab.y[i] = dt.y[i];
