@@ -5,8 +5,10 @@ One step = encode of the whole K and V cache of the workload (page/chunk
 statistics, alpha-law codes, anchor/residual planes), then anchor-only and
 full fused-dequant single-query decode attention.  Inputs are seeded
 synthetic Laplacian KV with outlier channels (long_context_serving_amd/synth.py),
-resident in HBM before timing starts.  To keep the 256 MB Infinity Cache from
-serving the data, every step works on one of several distinct buffer sets
+resident in HBM before timing starts.  Each step is one captured HIP graph;
+per-kernel timings come from graphs of back-to-back launches of one call.
+To keep the 256 MB Infinity Cache from serving the data, every step works
+on one of several distinct buffer sets
 (>= 1.5 GB in total): step i encodes set i % S and runs attention over the
 planes of set (i + S/2) % S, which were encoded S/2 steps earlier.
 
@@ -126,46 +128,75 @@ def main():
     out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
     ws = torch.empty(max(16, lynx.workspace_size(w.batch, w.kv_heads, w.q_heads, w.pages)),
                      dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
+    # One HIP graph per step (four phases).  The timed loop replays K of
+    # them; per-kernel averages come from graphs that hold the same call on
+    # every buffer set back to back, timed with events on the replay stream.
+    def phase_calls(i):
         e = sets[i % S]
         a = sets[(i + S // 2) % S]
-        if ev is not None:
-            ev[0].record(stream)
-        lynx.quantize_pages(e["k"], lynx.ROLE_KEY, out=e["pk"])
-        if ev is not None:
-            ev[1].record(stream)
-        lynx.quantize_pages(e["v"], lynx.ROLE_VALUE, out=e["pv"])
-        if ev is not None:
-            ev[2].record(stream)
-        lynx.decode_attention(q, a["pk"], a["pv"], w.pages, full=False, sm_scale=sm, out=out,
-                              workspace=ws)
-        if ev is not None:
-            ev[3].record(stream)
-        lynx.decode_attention(q, a["pk"], a["pv"], w.pages, full=True, sm_scale=sm, out=out,
-                              workspace=ws)
-        if ev is not None:
-            ev[4].record(stream)
+        return [
+            lambda: lynx.quantize_pages(e["k"], lynx.ROLE_KEY, out=e["pk"]),
+            lambda: lynx.quantize_pages(e["v"], lynx.ROLE_VALUE, out=e["pv"]),
+            lambda: lynx.decode_attention(q, a["pk"], a["pv"], w.pages, full=False, sm_scale=sm,
+                                          out=out, workspace=ws),
+            lambda: lynx.decode_attention(q, a["pk"], a["pv"], w.pages, full=True, sm_scale=sm,
+                                          out=out, workspace=ws),
+        ]
 
-    # every set encoded at least once before its planes are read
-    for i in range(max(args.warmup, S)):
-        step(i)
+    # eager pass: every set encoded before its planes are read
+    for i in range(S):
+        for call in phase_calls(i):
+            call()
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+
+    def capture(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for call in calls:
+                call()
+        return g
+
+    step_graphs = [capture(phase_calls(i)) for i in range(S)]
+    # per-kernel graphs: encode (K and V of every set), anchor, full
+    kernel_graphs = {
+        "encode": (capture([c for i in range(S) for c in phase_calls(i)[:2]]), 2 * S),
+        "decode_anchor": (capture([phase_calls(i)[2] for i in range(S)]), S),
+        "decode_full": (capture([phase_calls(i)[3] for i in range(S)]), S),
+    }
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        step_graphs[i % S].replay()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev0.record(stream)
     for i in range(K):
-        step(i, evs[i])
+        step_graphs[i % S].replay()
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    enc_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]
-    enc_v_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(K)]
-    anc_ms = [evs[i][2].elapsed_time(evs[i][3]) for i in range(K)]
-    full_ms = [evs[i][3].elapsed_time(evs[i][4]) for i in range(K)]
-    step_ms = evs[0][0].elapsed_time(evs[K - 1][4]) / K
+    step_ms = ev0.elapsed_time(ev1) / K
+
+    reps = max(2, K // S)
+    per_call_ms = {}
+    for name, (g, calls) in kernel_graphs.items():
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per_call_ms[name] = t0.elapsed_time(t1) / (reps * calls)
 
     if args.copy_probe:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -173,9 +204,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    enc_avg = float(np.mean(enc_ms + enc_v_ms))
-    anc_avg = float(np.mean(anc_ms))
-    full_avg = float(np.mean(full_ms))
+    enc_avg = per_call_ms["encode"]
+    anc_avg = per_call_ms["decode_anchor"]
+    full_avg = per_call_ms["decode_full"]
     gbps = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
     step_bytes = 2 * ab["encode"] + ab["decode_full"] + ab["decode_anchor"]
     kernels = {

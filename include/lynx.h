@@ -64,7 +64,9 @@ typedef enum lynx_status {
     LYNX_OK = 0,
     LYNX_ERR_NULL_ARG = -1,      /* a required pointer is NULL */
     LYNX_ERR_BAD_SHAPE = -2,     /* head_dim != 128, H < 1, P < 0, Hq % H,
-                                    Hq / H > 16, batch < 0, ... */
+                                    Hq / H > 16, batch < 0, a grid beyond
+                                    2^31 - 1 blocks (P*H tiles, 4*B*Hq, or
+                                    B*H*splits), ... */
     LYNX_ERR_MISALIGNED = -3,    /* a pointer is not 16-byte aligned */
     LYNX_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than required */
     LYNX_ERR_HIP = -5,           /* a HIP runtime call or launch failed */

@@ -88,7 +88,8 @@ int attention_common(const uint16_t *q, const lynx_planes *k, const lynx_planes 
   if (head_dim != LYNX_HEAD_DIM || batch < 0 || heads < 1 || q_heads < heads ||
       q_heads % heads != 0 || q_heads / heads > LYNX_MAX_GROUP || max_pages < 1)
     return LYNX_ERR_BAD_SHAPE;
-  if (static_cast<int64_t>(batch) * q_heads > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
+  // grid sizes: the combine launches 4 blocks per (request, query head)
+  if (static_cast<int64_t>(batch) * q_heads * 4 > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
   if (pool_pages < 0 || pool_pages * static_cast<int64_t>(heads) > 0x7FFFFFFFLL)
     return LYNX_ERR_BAD_SHAPE;
   if (!block_table && static_cast<int64_t>(batch) * max_pages > pool_pages)
@@ -104,6 +105,7 @@ int attention_common(const uint16_t *q, const lynx_planes *k, const lynx_planes 
     return LYNX_ERR_MISALIGNED;
   lynx::AttnShape s = lynx::attention_shape(batch, heads, q_heads, max_pages);
   s.pool_pages = pool_pages;
+  if (static_cast<int64_t>(batch) * heads * s.splits > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
   const size_t need = lynx::attention_workspace_bytes(s);
   if (!workspace || workspace_bytes < need) return LYNX_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LYNX_ERR_MISALIGNED;

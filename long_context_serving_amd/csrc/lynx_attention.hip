@@ -30,8 +30,16 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kMaxG = LYNX_MAX_GROUP;
-constexpr int kTargetBlocks = 2048;      // VALU kernel (group > 8)
-constexpr int kTargetBlocksMfma = 1024;  // MFMA kernel: 4 waves per block
+#ifndef LYNX_TARGET_BLOCKS_MFMA
+#define LYNX_TARGET_BLOCKS_MFMA 512
+#endif
+constexpr int kTargetBlocks = 2048;                         // VALU kernel (group > 8)
+constexpr int kTargetBlocksMfma = LYNX_TARGET_BLOCKS_MFMA;  // MFMA kernel: 4 waves per block
+// splits per (request, KV head) never exceed the block target (see
+// attention_shape), which bounds the combine kernel's weight array
+constexpr int kMaxSplits = kTargetBlocks > kTargetBlocksMfma ? kTargetBlocks : kTargetBlocksMfma;
+constexpr int kCombineThreads = 256;
+constexpr int kCombineParts = 4;  // the combine splits the head dimension into 4 x 32 channels
 
 struct YTable {
   float y[256];
@@ -55,7 +63,7 @@ __device__ __forceinline__ Partials partials_of(void *ws, const AttnShape &s) {
   const size_t n = static_cast<size_t>(s.batch) * s.heads * s.splits * s.group;
   Partials pt;
   pt.m = reinterpret_cast<double *>(ws);
-  pt.l = reinterpret_cast<float *>(pt.m + n);
+  pt.l = reinterpret_cast<float *>(pt.m + ((n + 1) & ~static_cast<size_t>(1)));
   pt.o = pt.l + ((n + 3) & ~static_cast<size_t>(3));
   return pt;
 }
@@ -270,57 +278,89 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
 }
 
 // Exact merge of the (m, l, o) partials of every split of one (request, KV
-// head): weights exp(m_s - M) are computed once per split into LDS, then
-// each thread sums its channel.
-__global__ __launch_bounds__(kDim) void attn_combine_kernel(AttnShape s, const void *ws,
-                                                             float *__restrict__ out) {
-  const int bj = blockIdx.x;  // b * Hq + head
+// head), for one query head and 32 of its channels per block:
+//   M = max m_s,  w_s = exp(m_s - M),  out = sum_s w_s o_s / sum_s w_s l_s.
+// The weights are computed once into LDS; 32 groups of 8 threads then sum
+// float4 slices of the o partials of every 32nd split (four loads in flight
+// per thread), in fp64, and one last pass adds the 32 group sums.
+__device__ __forceinline__ double block_reduce(double v, bool is_max, double *s_red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double o = __shfl_xor(v, off);
+    v = is_max ? fmax(v, o) : v + o;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[w] = v;
+  __syncthreads();
+  v = s_red[0];
+#pragma unroll
+  for (int k = 1; k < kCombineThreads / 64; ++k) v = is_max ? fmax(v, s_red[k]) : v + s_red[k];
+  return v;
+}
+
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnShape s, const void *ws,
+                                                                        float *__restrict__ out) {
+  const int bj = blockIdx.x / kCombineParts;  // b * Hq + query head
+  const int part = blockIdx.x % kCombineParts;
   const int b = bj / s.q_heads;
   const int jq = bj % s.q_heads;
   const int h = jq / s.group;
   const int j = jq % s.group;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   Partials pt = partials_of(const_cast<void *>(ws), s);
   const size_t first = (static_cast<size_t>(b) * s.heads + h) * s.splits;
-  __shared__ double s_red[kDim];
-  __shared__ float s_w[kDim];
+  __shared__ float s_w[kMaxSplits];
+  __shared__ double s_red[kCombineThreads / 64];
+  __shared__ double s_o[32][33];
+
   double M = -INFINITY;
-  for (int sp = d; sp < s.splits; sp += kDim) M = fmax(M, pt.m[(first + sp) * s.group + j]);
-  s_red[d] = M;
-  __syncthreads();
-  for (int off = kDim / 2; off > 0; off >>= 1) {
-    if (d < off) s_red[d] = fmax(s_red[d], s_red[d + off]);
-    __syncthreads();
+  for (int sp = tid; sp < s.splits; sp += kCombineThreads)
+    M = fmax(M, pt.m[(first + sp) * s.group + j]);
+  M = block_reduce(M, true, s_red);
+  double L = 0.0;
+  for (int sp = tid; sp < s.splits; sp += kCombineThreads) {
+    const size_t r = (first + sp) * s.group + j;
+    const double m = pt.m[r];
+    const float wgt = m == -INFINITY ? 0.0f : static_cast<float>(exp(m - M));
+    s_w[sp] = wgt;
+    L += static_cast<double>(wgt) * pt.l[r];
   }
-  M = s_red[0];
-  __syncthreads();
-  double L = 0.0, O = 0.0;
-  for (int sp0 = 0; sp0 < s.splits; sp0 += kDim) {
-    const int sp = sp0 + d;
-    float wgt = 0.0f;
-    if (sp < s.splits) {
-      const size_t r = (first + sp) * s.group + j;
-      const double m = pt.m[r];
-      wgt = m == -INFINITY ? 0.0f : static_cast<float>(exp(m - M));
-      L += static_cast<double>(wgt) * pt.l[r];
+  L = block_reduce(L, false, s_red);  // its barriers also publish s_w
+
+  const int c4 = tid & 7;   // float4 slice of the block's 32 channels
+  const int sg = tid >> 3;  // split group 0..31
+  const int d0 = part * 32 + 4 * c4;
+  double o[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int sp0 = sg; sp0 < s.splits; sp0 += 4 * 32) {
+    float4 v[4];
+    float wk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sp = sp0 + 32 * u;
+      const bool ok = sp < s.splits;
+      wk[u] = ok ? s_w[sp] : 0.0f;
+      v[u] = ok ? *reinterpret_cast<const float4 *>(pt.o + ((first + sp) * s.group + j) * kDim + d0)
+                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    s_w[d] = wgt;
-    __syncthreads();
-    const int cnt = s.splits - sp0 < kDim ? s.splits - sp0 : kDim;
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = s_w[k];
-      if (wk != 0.0f) O += static_cast<double>(wk) * pt.o[((first + sp0 + k) * s.group + j) * kDim + d];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const double wd = wk[u];
+      o[0] += wd * v[u].x;
+      o[1] += wd * v[u].y;
+      o[2] += wd * v[u].z;
+      o[3] += wd * v[u].w;
     }
-    __syncthreads();
   }
-  s_red[d] = L;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s_o[sg][4 * c4 + e] = o[e];
   __syncthreads();
-  for (int off = kDim / 2; off > 0; off >>= 1) {
-    if (d < off) s_red[d] += s_red[d + off];
-    __syncthreads();
+  if (tid < 32) {
+    double O = 0.0;
+#pragma unroll 8
+    for (int g2 = 0; g2 < 32; ++g2) O += s_o[g2][tid];
+    out[static_cast<size_t>(bj) * kDim + part * 32 + tid] = L > 0.0 ? static_cast<float>(O / L) : 0.0f;
   }
-  L = s_red[0];
-  out[static_cast<size_t>(bj) * kDim + d] = L > 0.0 ? static_cast<float>(O / L) : 0.0f;
 }
 
 }  // namespace
@@ -345,8 +385,8 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
 
 size_t attention_workspace_bytes(const AttnShape &s) {
   const size_t n = static_cast<size_t>(s.batch) * s.heads * s.splits * s.group;
-  return n * sizeof(double) + ((n + 3) & ~static_cast<size_t>(3)) * sizeof(float) +
-         n * kDim * sizeof(float);
+  return ((n + 1) & ~static_cast<size_t>(1)) * sizeof(double) +
+         ((n + 3) & ~static_cast<size_t>(3)) * sizeof(float) + n * kDim * sizeof(float);
 }
 
 hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
@@ -360,8 +400,9 @@ hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
     const hipError_t e = launch_attention_mfma(q, k, v, block_table, seq_lens, s, sm_scale, full,
                                                scores, workspace, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>(s.batch * s.q_heads)),
-                       dim3(kDim), 0, stream, s, static_cast<const void *>(workspace), out);
+    hipLaunchKernelGGL(attn_combine_kernel,
+                       dim3(static_cast<unsigned>(s.batch * s.q_heads * kCombineParts)),
+                       dim3(kCombineThreads), 0, stream, s, static_cast<const void *>(workspace), out);
     return hipGetLastError();
   }
   YTable tab;
@@ -376,8 +417,9 @@ hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
                        block_table, seq_lens, s, sm_scale, scores, workspace, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>(s.batch * s.q_heads)),
-                     dim3(kDim), 0, stream, s, static_cast<const void *>(workspace), out);
+  hipLaunchKernelGGL(attn_combine_kernel,
+                     dim3(static_cast<unsigned>(s.batch * s.q_heads * kCombineParts)),
+                     dim3(kCombineThreads), 0, stream, s, static_cast<const void *>(workspace), out);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ __device__ __forceinline__ Partials partials_of(void *ws, const AttnShape &s) {
   const size_t n = static_cast<size_t>(s.batch) * s.heads * s.splits * s.group;
   Partials pt;
   pt.m = reinterpret_cast<double *>(ws);
-  pt.l = reinterpret_cast<float *>(pt.m + n);
+  pt.l = reinterpret_cast<float *>(pt.m + ((n + 1) & ~static_cast<size_t>(1)));
   pt.o = pt.l + ((n + 3) & ~static_cast<size_t>(3));
   return pt;
 }
@@ -103,11 +103,7 @@ __device__ __forceinline__ void decode8_draft(uint32_t a, const uint2 *pairs, ui
   }
 }
 
-// fp16 bits of x (round to nearest even) and of the remainder x - hi.
-__device__ __forceinline__ uint32_t f16_bits(float x) {
-  const _Float16 h = static_cast<_Float16>(x);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
-}
+// fp16 bits of the hi part of x (round to nearest even) or of the remainder x - hi.
 __device__ __forceinline__ uint32_t split_part(float x, bool want_lo) {
   const _Float16 h = static_cast<_Float16>(x);
   const float rem = x - static_cast<float>(h);

@@ -346,6 +346,44 @@ def test_repeat_runs_are_bitwise_identical(lynx):
     assert torch.equal(o1, o2)
 
 
+def test_graph_replays_match_eager(lynx):
+    """The four calls of one step captured in a HIP graph: every replay, with
+    other eager work on the device in between, is bitwise the eager result."""
+    w = synth.WORKLOADS["tiny"]
+    xk, xv = to_dev(synth.kv_pages(w, 0, 0, 0)), to_dev(synth.kv_pages(w, 0, 1, 0))
+    other = to_dev(synth.kv_pages(w, 0, 0, 3))
+    q = to_dev(synth.queries(w))
+    pk = lynx.alloc_planes(w.pages, w.kv_heads, 0)
+    pv = lynx.alloc_planes(w.pages, w.kv_heads, 1)
+    po = lynx.alloc_planes(w.pages, w.kv_heads, 0)
+    ws = torch.empty(lynx.workspace_size(1, w.kv_heads, w.q_heads, w.pages), dtype=torch.uint8,
+                     device="cuda")
+    oa = torch.empty((1, w.q_heads, 128), dtype=torch.float32, device="cuda")
+    of = torch.empty_like(oa)
+
+    def step():
+        lynx.quantize_pages(xk, 0, out=pk)
+        lynx.quantize_pages(xv, 1, out=pv)
+        lynx.decode_attention(q, pk, pv, w.pages, full=False, sm_scale=SM, out=oa, workspace=ws)
+        lynx.decode_attention(q, pk, pv, w.pages, full=True, sm_scale=SM, out=of, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (pk.anchor, pk.residual, pv.anchor, pv.residual, pk.chunk_maxabs, oa, of)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (pk.anchor, pv.residual, oa, of, ws):
+            t.zero_()
+        lynx.quantize_pages(other, 0, out=po)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (pk.anchor, pk.residual, pv.anchor, pv.residual, pk.chunk_maxabs, oa, of)
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), "replay %d differs" % rep
+
+
 def test_code_map_fast_path_is_exact_for_every_fp32_in_unit_interval(lynx):
     """Exhaustive: all 1,065,353,217 fp32 values u in [0, 1]."""
     assert lynx.selftest_code_map(0, 0x3F800001) == 0
