@@ -59,11 +59,13 @@ extern "C" {
 #define LYNX_CHUNKS_PER_PAGE 8
 #define LYNX_HEAD_DIM 128    /* the only head_dim this build supports */
 #define LYNX_MAX_GROUP 16    /* largest supported Hq / H */
+#define LYNX_MAX_KV_HEADS 65535  /* largest H of an encoded tensor (a page of
+                                    256 tokens stays below 4 GiB) */
 
 typedef enum lynx_status {
     LYNX_OK = 0,
     LYNX_ERR_NULL_ARG = -1,      /* a required pointer is NULL */
-    LYNX_ERR_BAD_SHAPE = -2,     /* head_dim != 128, H < 1, P < 0, Hq % H,
+    LYNX_ERR_BAD_SHAPE = -2,     /* head_dim != 128, H < 1 or > 65535, P < 0, Hq % H,
                                     Hq / H > 16, batch < 0, a grid beyond
                                     2^31 - 1 blocks (P*H tiles, 4*B*Hq, or
                                     B*H*splits), ... */
@@ -206,10 +208,12 @@ void lynx_code_thresholds(float *out128);
 
 /*
  * Device self-test of the encoder's level computation: for every fp32 bit
- * pattern b in [begin_bits, end_bits) (end_bits <= 0x3F800001, i.e. values
- * in [0, 1]), compares the encoder's fast level path with the exact
- * threshold count and adds the number of disagreements to *mismatches (a
- * device uint64 the caller zeroes).  Errors: NULL_ARG, BAD_ARG, DEVICE, HIP.
+ * pattern b in [begin_bits, end_bits) (end_bits <= 0x40000000, i.e. values
+ * in [0, 2); the encoder meets u slightly above 1 through rounding and must
+ * give it the level of 1), compares the encoder's fast level path with the
+ * exact threshold count of min(u, 1) and adds the number of disagreements
+ * to *mismatches (a device uint64 the caller zeroes).  Errors: NULL_ARG,
+ * BAD_ARG, DEVICE, HIP.
  */
 int lynx_selftest_code_map(uint32_t begin_bits, uint32_t end_bits,
                            unsigned long long *mismatches, void *stream);

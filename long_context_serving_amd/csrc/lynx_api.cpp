@@ -56,7 +56,8 @@ PlanesArg to_arg(const lynx_planes *pl) {
 }
 
 int check_tile_shape(int64_t num_pages, int32_t heads, int32_t head_dim, int32_t role) {
-  if (head_dim != LYNX_HEAD_DIM || heads < 1 || num_pages < 0) return LYNX_ERR_BAD_SHAPE;
+  if (head_dim != LYNX_HEAD_DIM || heads < 1 || heads > LYNX_MAX_KV_HEADS || num_pages < 0)
+    return LYNX_ERR_BAD_SHAPE;
   if (num_pages * static_cast<int64_t>(heads) > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
   if (role != LYNX_ROLE_KEY && role != LYNX_ROLE_VALUE) return LYNX_ERR_BAD_ARG;
   return LYNX_OK;
@@ -234,7 +235,7 @@ void lynx_decode_table(float *out256) {
 int lynx_selftest_code_map(uint32_t begin_bits, uint32_t end_bits,
                            unsigned long long *mismatches, void *stream) {
   if (!mismatches) return LYNX_ERR_NULL_ARG;
-  if (end_bits > 0x3F800001u || begin_bits > end_bits) return LYNX_ERR_BAD_ARG;
+  if (end_bits > 0x40000000u || begin_bits > end_bits) return LYNX_ERR_BAD_ARG;
   if (begin_bits == end_bits) return LYNX_OK;
   const int rc = check_device();
   if (rc) return rc;

@@ -28,14 +28,11 @@ namespace {
 
 constexpr int kEncThreads = 512;
 
-// Level window of the fast path: if 127 F(u) computed with v_log_f32 lies
-// within this many levels of a rounding boundary, the level is recomputed
-// exactly from the threshold table.  The fast path's error is far smaller
-// (it is checked exhaustively over every fp32 u in [0, 1] by the tests).
-constexpr float kNearWindow = 1.0f / 4096.0f;
-
+// Kernel-argument copy of the host tables: thresholds T[0..127] and the level
+// at the start of each u bucket (see BucketTable).
 struct EncodeTables {
   float t[128];
+  uint8_t base[(kBuckets + 3) & ~3];
 };
 
 __device__ __forceinline__ int chunk_token(int r, int j) {
@@ -53,17 +50,51 @@ __device__ __forceinline__ int level_exact(float u, const float *T) {
   return m;
 }
 
-// Level of u in [0, 1]: 127 ln(1 + 255u)/ln 256 = 15.875 log2(1 + 255u),
-// rounded half up.
-__device__ __forceinline__ int level_of(float u, const float *T) {
-  const float w = __builtin_fmaf(u, 255.0f, 1.0f);
-  const float l2 = __builtin_amdgcn_logf(w);
-  const float t = __builtin_fmaf(l2, 15.875f, 0.5f);
-  int m = static_cast<int>(t);
-  const float f = t - static_cast<float>(m);
-  m = m > 127 ? 127 : m;
-  if (f < kNearWindow || f > 1.0f - kNearWindow) m = level_exact(u, T);
-  return m;
+// LDS bucket entry: (bits of the first threshold above the bucket start,
+// level at the bucket start); every bucket holds at most one threshold.
+__device__ __forceinline__ void fill_level_table(uint2 *lvl, const EncodeTables &tab) {
+  for (int i = threadIdx.x; i < kBuckets; i += blockDim.x) {
+    const int m = tab.base[i];
+    lvl[i] = make_uint2(m < 127 ? __float_as_uint(tab.t[m + 1]) : 0xFFFFFFFFu,
+                        static_cast<uint32_t>(m));
+  }
+}
+
+// Level of u in [0, 2) from its bits (u >= 1 gives 127, which is the level
+// of the clamped u): one table read and one comparison.  Positive floats
+// order like their bit patterns.
+__device__ __forceinline__ int level_fast(uint32_t ubits, const uint2 *lvl) {
+  uint32_t key = ubits >> kBucketShift;
+  key = key < kBucketFirstKey - 1u ? kBucketFirstKey - 1u : key;
+  key = key > kBucketLastKey ? kBucketLastKey : key;
+  const uint2 e = lvl[key - (kBucketFirstKey - 1u)];
+  return static_cast<int>(e.y) + (ubits >= e.x ? 1 : 0);
+}
+
+// Sign-aware code of the centred value d: m for d >= 0, ~m for d < 0 (d is
+// never -0: x' - mu rounds an exact zero to +0).  Only the low byte is used.
+__device__ __forceinline__ uint32_t code_of(float d, float inv_s, const uint2 *lvl) {
+  const float u = fabsf(d) * inv_s;
+  const int m = level_fast(__float_as_uint(u), lvl);
+  const int sgn = static_cast<int>(__float_as_uint(d)) >> 31;
+  return static_cast<uint32_t>(m ^ sgn);
+}
+
+// low bytes of a, b, c, d -> bytes 0..3 of one word
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// The cut of 8 codes (element k in nibble k): anchor = code >> 4 and
+// residual = code & 15 per element.  we / wo hold the even / odd elements'
+// code bytes.
+__device__ __forceinline__ uint32_t anchor_word(uint32_t we, uint32_t wo) {
+  return ((we >> 4) & 0x0F0F0F0Fu) | (wo & 0xF0F0F0F0u);
+}
+__device__ __forceinline__ uint32_t residual_word(uint32_t we, uint32_t wo) {
+  return (we & 0x0F0F0F0Fu) | ((wo << 4) & 0xF0F0F0F0u);
 }
 
 // Keep 7 significant bits, rounding towards +infinity (x >= 0, finite).
@@ -76,9 +107,14 @@ __device__ __forceinline__ float round_up_7bits(float x) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__global__ __launch_bounds__(kEncThreads) void encode_kernel(
-    const uint16_t *__restrict__ kv, int heads, int role, PlanesArg out,
-    EncodeTables tab) {
+// One workgroup per (page, head) tile; wave c owns chunk c; lane (cg, r)
+// holds channels 8cg..8cg+7 of the 8 tokens chunk_token(r, 0..7).  Two
+// workgroups fit on a CU (at most 128 VGPRs) so that one streams its tile in
+// while the other computes.  Addresses are a wave-uniform base plus a 32-bit
+// lane offset.
+template <int kRole>
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, EncodeTables tab) {
   const int tile = blockIdx.x;  // page * heads + head
   const int p = tile / heads;
   const int h = tile - p * heads;
@@ -87,23 +123,24 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
   const int cg = lane & 15;
   const int r = lane >> 4;
 
-  __shared__ float s_T[128];
+  __shared__ uint2 s_lvl[kBuckets];
   __shared__ float s_min[kChunks][kDim];
   __shared__ float s_max[kChunks][kDim];
   __shared__ float s_mn[kDim];
   __shared__ float s_inv[kDim];
 
-  if (threadIdx.x < 128) s_T[threadIdx.x] = tab.t[threadIdx.x];
+  fill_level_table(s_lvl, tab);  // published by the first __syncthreads below
 
   // ---- load the lane's 8 tokens x 8 channels (bf16 -> fp32 is exact) ----
-  const size_t row = static_cast<size_t>(heads) * kDim;
-  const uint16_t *base = kv + static_cast<size_t>(p) * kPage * row +
-                         static_cast<size_t>(h) * kDim + cg * 8;
+  const uint32_t row_bytes = static_cast<uint32_t>(heads) * kDim * 2;
+  const char *page = reinterpret_cast<const char *>(kv) +
+                     static_cast<size_t>(p) * kPage * row_bytes + static_cast<size_t>(h) * kDim * 2;
+  const uint32_t lane_off = static_cast<uint32_t>(c * kChunk) * row_bytes + cg * 16;
   float x[8][8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int t = c * kChunk + chunk_token(r, j);
-    const uint4 v = *reinterpret_cast<const uint4 *>(base + static_cast<size_t>(t) * row);
+    const uint32_t off = lane_off + static_cast<uint32_t>(chunk_token(r, j)) * row_bytes;
+    const uint4 v = *reinterpret_cast<const uint4 *>(page + off);
     x[j][0] = bf16_lo(v.x); x[j][1] = bf16_hi(v.x);
     x[j][2] = bf16_lo(v.y); x[j][3] = bf16_hi(v.y);
     x[j][4] = bf16_lo(v.z); x[j][5] = bf16_hi(v.z);
@@ -111,26 +148,27 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
   }
 
   // ---- page-level normalisation: per-channel min and max ----
-  float mn[8], mx[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    mn[i] = x[0][i];
-    mx[i] = x[0][i];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) {
-      mn[i] = fminf(mn[i], x[j][i]);
-      mx[i] = fmaxf(mx[i], x[j][i]);
-    }
-    mn[i] = fminf(mn[i], __shfl_xor(mn[i], 16));
-    mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 16));
-    mn[i] = fminf(mn[i], __shfl_xor(mn[i], 32));
-    mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 32));
-  }
-  if (r == 0) {
+  {
+    float mn[8], mx[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      s_min[c][cg * 8 + i] = mn[i];
-      s_max[c][cg * 8 + i] = mx[i];
+      mn[i] = x[0][i];
+      mx[i] = x[0][i];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) {
+        mn[i] = fminf(mn[i], x[j][i]);
+        mx[i] = fmaxf(mx[i], x[j][i]);
+      }
+      mn[i] = fminf(mn[i], __shfl_xor(mn[i], 16));
+      mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 16));
+      mn[i] = fminf(mn[i], __shfl_xor(mn[i], 32));
+      mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 32));
+    }
+    if (r == 0) {
+      reinterpret_cast<float4 *>(&s_min[c][cg * 8])[0] = make_float4(mn[0], mn[1], mn[2], mn[3]);
+      reinterpret_cast<float4 *>(&s_min[c][cg * 8])[1] = make_float4(mn[4], mn[5], mn[6], mn[7]);
+      reinterpret_cast<float4 *>(&s_max[c][cg * 8])[0] = make_float4(mx[0], mx[1], mx[2], mx[3]);
+      reinterpret_cast<float4 *>(&s_max[c][cg * 8])[1] = make_float4(mx[4], mx[5], mx[6], mx[7]);
     }
   }
   __syncthreads();
@@ -149,145 +187,135 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float inv = rg > 0.0f ? static_cast<float>(1.0 / static_cast<double>(rg)) : 0.0f;
     s_mn[d] = a;
     s_inv[d] = inv;
-    const size_t sidx = static_cast<size_t>(tile) * kDim + d;
-    out.page_min[sidx] = a;
-    out.page_range[sidx] = rg;
+    out.page_min[static_cast<size_t>(tile) * kDim + d] = a;
+    out.page_range[static_cast<size_t>(tile) * kDim + d] = rg;
   }
   __syncthreads();
 
-  float inv_rg[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    mn[i] = s_mn[cg * 8 + i];
-    inv_rg[i] = s_inv[cg * 8 + i];
-  }
-
   // ---- x' = (x - mn) * inv_rg, and the exact chunk sum in fp64 ----
-  double sum[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sum[i] = 0.0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  float mu[8];
+  {
+    const float4 mn0 = reinterpret_cast<const float4 *>(&s_mn[cg * 8])[0];
+    const float4 mn1 = reinterpret_cast<const float4 *>(&s_mn[cg * 8])[1];
+    const float4 iv0 = reinterpret_cast<const float4 *>(&s_inv[cg * 8])[0];
+    const float4 iv1 = reinterpret_cast<const float4 *>(&s_inv[cg * 8])[1];
+    const float mn[8] = {mn0.x, mn0.y, mn0.z, mn0.w, mn1.x, mn1.y, mn1.z, mn1.w};
+    const float inv_rg[8] = {iv0.x, iv0.y, iv0.z, iv0.w, iv1.x, iv1.y, iv1.z, iv1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float diff = x[j][i] - mn[i];
-      x[j][i] = diff * inv_rg[i];
-      sum[i] += static_cast<double>(x[j][i]);
-    }
-  }
-  float mu[8], sabs[8];
+      double sum = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    sum[i] += __shfl_xor(sum[i], 16);
-    sum[i] += __shfl_xor(sum[i], 32);
-    mu[i] = static_cast<float>(sum[i] * (1.0 / kChunk));
-    sabs[i] = 0.0f;
+      for (int j = 0; j < 8; ++j) {
+        x[j][i] = (x[j][i] - mn[i]) * inv_rg[i];
+        sum += static_cast<double>(x[j][i]);
+      }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      mu[i] = static_cast<float>(sum * (1.0 / kChunk));
+    }
   }
 
   // ---- chunk centring and max-abs ----
+  float sabs[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int i = 0; i < 8; ++i) {
+    sabs[i] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < 8; ++j) {
       x[j][i] = x[j][i] - mu[i];
       sabs[i] = fmaxf(sabs[i], fabsf(x[j][i]));
     }
-  }
-  float inv_s[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
     sabs[i] = fmaxf(sabs[i], __shfl_xor(sabs[i], 16));
     sabs[i] = fmaxf(sabs[i], __shfl_xor(sabs[i], 32));
     sabs[i] = round_up_7bits(sabs[i]);
   }
-  // each of the 4 lanes sharing these channels computes 2 of the 8
-  // reciprocals; the rest are gathered from the other lanes
-  float my_inv[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float s = sabs[2 * r + k];
-    my_inv[k] = s > 0.0f ? static_cast<float>(1.0 / static_cast<double>(s)) : 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int src = cg + 16 * (i >> 1);  // lane holding channel i's reciprocal
-    const float v0 = __shfl(my_inv[0], src);
-    const float v1 = __shfl(my_inv[1], src);
-    inv_s[i] = (i & 1) ? v1 : v0;
-  }
   if (r == 0) {
-    float *mean_out = out.chunk_mean + (static_cast<size_t>(tile) * kChunks + c) * kDim + cg * 8;
-    float *maxabs_out = out.chunk_maxabs + (static_cast<size_t>(tile) * kChunks + c) * kDim + cg * 8;
-    reinterpret_cast<float4 *>(mean_out)[0] = make_float4(mu[0], mu[1], mu[2], mu[3]);
-    reinterpret_cast<float4 *>(mean_out)[1] = make_float4(mu[4], mu[5], mu[6], mu[7]);
-    reinterpret_cast<float4 *>(maxabs_out)[0] = make_float4(sabs[0], sabs[1], sabs[2], sabs[3]);
-    reinterpret_cast<float4 *>(maxabs_out)[1] = make_float4(sabs[4], sabs[5], sabs[6], sabs[7]);
+    const size_t cidx = (static_cast<size_t>(tile) * kChunks + c) * kDim + cg * 8;
+    reinterpret_cast<float4 *>(out.chunk_mean + cidx)[0] = make_float4(mu[0], mu[1], mu[2], mu[3]);
+    reinterpret_cast<float4 *>(out.chunk_mean + cidx)[1] = make_float4(mu[4], mu[5], mu[6], mu[7]);
+    reinterpret_cast<float4 *>(out.chunk_maxabs + cidx)[0] =
+        make_float4(sabs[0], sabs[1], sabs[2], sabs[3]);
+    reinterpret_cast<float4 *>(out.chunk_maxabs + cidx)[1] =
+        make_float4(sabs[4], sabs[5], sabs[6], sabs[7]);
   }
-
-  // ---- sign-aware alpha-law code ----
-  int code[8][8];
+  // correctly rounded reciprocals: each of the 4 lanes sharing these
+  // channels computes 2 of the 8, the rest are gathered from the other lanes
+  float inv_s[8];
+  {
+    float my_inv[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+    for (int k = 0; k < 2; ++k) {
+      const float s = r == 0 ? sabs[k] : r == 1 ? sabs[2 + k] : r == 2 ? sabs[4 + k] : sabs[6 + k];
+      my_inv[k] = s > 0.0f ? static_cast<float>(1.0 / static_cast<double>(s)) : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float u = fabsf(x[j][i]) * inv_s[i];
-      u = fminf(u, 1.0f);
-      const int m = level_of(u, s_T);
-      code[j][i] = x[j][i] < 0.0f ? ~m : m;
+      const int src = cg + 16 * (i >> 1);  // lane holding channel i's reciprocal
+      inv_s[i] = __shfl(my_inv[i & 1], src);
     }
   }
 
-  // ---- the cut: anchor = code >> 4, residual = code & 15; pack nibbles ----
-  if (role == LYNX_ROLE_KEY) {
-    uint32_t *an = reinterpret_cast<uint32_t *>(out.anchor);
-    uint32_t *re = reinterpret_cast<uint32_t *>(out.residual);
+  // ---- sign-aware alpha-law codes and the cut into nibble planes ----
+  char *an = reinterpret_cast<char *>(out.anchor) + static_cast<size_t>(tile) * kPlaneTileBytes;
+  char *re = reinterpret_cast<char *>(out.residual) + static_cast<size_t>(tile) * kPlaneTileBytes;
+  if (kRole == LYNX_ROLE_KEY) {
+    // token-major [256 tokens][64 B]: one word = 8 channels of one token
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t a = 0, q = 0;
+      uint32_t q[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        a |= static_cast<uint32_t>((code[j][i] >> 4) & 15) << (4 * i);
-        q |= static_cast<uint32_t>(code[j][i] & 15) << (4 * i);
-      }
-      const int t = c * kChunk + chunk_token(r, j);
-      const size_t w = (static_cast<size_t>(tile) * kPage + t) * (kDim / 8) + cg;
-      an[w] = a;
-      re[w] = q;
+      for (int i = 0; i < 8; ++i) q[i] = code_of(x[j][i], inv_s[i], s_lvl);
+      const uint32_t we = pack4(q[0], q[2], q[4], q[6]);
+      const uint32_t wo = pack4(q[1], q[3], q[5], q[7]);
+      const uint32_t off = static_cast<uint32_t>(c * kChunk + chunk_token(r, j)) * 64 + cg * 4;
+      *reinterpret_cast<uint32_t *>(an + off) = anchor_word(we, wo);
+      *reinterpret_cast<uint32_t *>(re + off) = residual_word(we, wo);
     }
   } else {
-    uint32_t *an = reinterpret_cast<uint32_t *>(out.anchor);
-    uint32_t *re = reinterpret_cast<uint32_t *>(out.residual);
+    // channel-major [8 chunks][128 channels][16 B]: one word = the lane's 8
+    // tokens of one channel
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t a = 0, q = 0;
+      uint32_t q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        a |= static_cast<uint32_t>((code[j][i] >> 4) & 15) << (4 * j);
-        q |= static_cast<uint32_t>(code[j][i] & 15) << (4 * j);
-      }
-      const size_t w = ((static_cast<size_t>(tile) * kChunks + c) * kDim + cg * 8 + i) * 4 + r;
-      an[w] = a;
-      re[w] = q;
+      for (int j = 0; j < 8; ++j) q[j] = code_of(x[j][i], inv_s[i], s_lvl);
+      const uint32_t we = pack4(q[0], q[2], q[4], q[6]);
+      const uint32_t wo = pack4(q[1], q[3], q[5], q[7]);
+      const uint32_t off = static_cast<uint32_t>(c * kDim + cg * 8 + i) * 16 + r * 4;
+      *reinterpret_cast<uint32_t *>(an + off) = anchor_word(we, wo);
+      *reinterpret_cast<uint32_t *>(re + off) = residual_word(we, wo);
     }
   }
 }
 
-// Exhaustive check of the fast level path against the exact threshold count
-// over fp32 bit patterns [begin, end) (values in [0, 1]).
+// Exhaustive check of the bucket level path against the exact threshold
+// count over fp32 bit patterns [begin, end) (values in [0, 2); above 1 the
+// expected level is that of the clamped u, 127).
 __global__ __launch_bounds__(256) void code_map_check_kernel(uint32_t begin, uint32_t end,
                                                              unsigned long long *mismatches,
                                                              EncodeTables tab) {
   __shared__ float s_T[128];
+  __shared__ uint2 s_lvl[kBuckets];
   if (threadIdx.x < 128) s_T[threadIdx.x] = tab.t[threadIdx.x];
+  fill_level_table(s_lvl, tab);
   __syncthreads();
   unsigned long long bad = 0;
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t b = begin + blockIdx.x * blockDim.x + threadIdx.x; b < end && b >= begin;
        b += stride) {
     const float u = __uint_as_float(b);
-    bad += level_of(u, s_T) != level_exact(u, s_T);
+    bad += level_fast(b, s_lvl) != level_exact(fminf(u, 1.0f), s_T);
   }
   if (bad) atomicAdd(mismatches, bad);
+}
+
+EncodeTables encode_tables() {
+  EncodeTables tab = {};
+  const CodeTable &ct = code_table();
+  const BucketTable &bt = bucket_table();
+  for (int k = 0; k < 128; ++k) tab.t[k] = ct.t[k];
+  for (int i = 0; i < kBuckets; ++i) tab.base[i] = bt.base[i];
+  return tab;
 }
 
 }  // namespace
@@ -295,9 +323,7 @@ __global__ __launch_bounds__(256) void code_map_check_kernel(uint32_t begin, uin
 hipError_t launch_code_map_check(uint32_t begin, uint32_t end, unsigned long long *mismatches,
                                  hipStream_t stream) {
   if (end <= begin) return hipSuccess;
-  EncodeTables tab;
-  const CodeTable &ct = code_table();
-  for (int k = 0; k < 128; ++k) tab.t[k] = ct.t[k];
+  EncodeTables tab = encode_tables();
   hipLaunchKernelGGL(code_map_check_kernel, dim3(4096), dim3(256), 0, stream, begin, end,
                      mismatches, tab);
   return hipGetLastError();
@@ -306,12 +332,15 @@ hipError_t launch_code_map_check(uint32_t begin, uint32_t end, unsigned long lon
 hipError_t launch_encode(const uint16_t *kv, int64_t num_pages, int heads,
                          int role, const PlanesArg &out, hipStream_t stream) {
   if (num_pages == 0) return hipSuccess;
-  EncodeTables tab;
-  const CodeTable &ct = code_table();
-  for (int k = 0; k < 128; ++k) tab.t[k] = ct.t[k];
+  if (!bucket_table().ok) return hipErrorInvalidValue;
+  EncodeTables tab = encode_tables();
   const unsigned blocks = static_cast<unsigned>(num_pages * heads);
-  hipLaunchKernelGGL(encode_kernel, dim3(blocks), dim3(kEncThreads), 0, stream, kv,
-                     heads, role, out, tab);
+  if (role == LYNX_ROLE_KEY)
+    hipLaunchKernelGGL(encode_kernel<LYNX_ROLE_KEY>, dim3(blocks), dim3(kEncThreads), 0, stream,
+                       kv, heads, out, tab);
+  else
+    hipLaunchKernelGGL(encode_kernel<LYNX_ROLE_VALUE>, dim3(blocks), dim3(kEncThreads), 0, stream,
+                       kv, heads, out, tab);
   return hipGetLastError();
 }
 

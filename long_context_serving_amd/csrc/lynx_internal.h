@@ -37,6 +37,24 @@ struct DecodeTable {
 const CodeTable &code_table();
 const DecodeTable &decode_table();
 
+// Level buckets.  An fp32 u in [0, 2) is bucketed by key = bits(u) >> 18
+// (exponent and the top 5 mantissa bits).  Bucket 0 takes every u below
+// 2^-14 (all of level 0: T[1] > 2^-14), buckets 1..448 split the binades
+// 2^-14 .. 2^-1 into 32 parts each, and bucket 449 takes every u >= 1
+// (level 127).  Consecutive thresholds are more than 4.4% apart while a
+// bucket is at most 1/32 = 3.1% wide, so a bucket holds at most one
+// threshold and the level is base[b] + (u >= T[base[b] + 1]).  The builder
+// verifies this for every bucket (ok = false otherwise).
+constexpr uint32_t kBucketShift = 18;
+constexpr uint32_t kBucketFirstKey = 113u << 5;  // key of 2^-14
+constexpr uint32_t kBucketLastKey = 127u << 5;   // key of 1.0
+constexpr int kBuckets = static_cast<int>(kBucketLastKey - kBucketFirstKey) + 2;  // 450
+struct BucketTable {
+  uint8_t base[kBuckets];
+  bool ok;
+};
+const BucketTable &bucket_table();
+
 // Draft (anchor-only) values for the 16 anchor nibbles (index = nibble,
 // i.e. a & 15): yhat(16a + 7).
 struct DraftTable {

@@ -5,7 +5,9 @@
 // is m = round-half-up(127 ln(1 + alpha u) / ln(1 + alpha)), alpha = 255.
 // The encoder takes m exactly as the number of thresholds T[k] <= u, where
 // T[k] is found by bisection over fp32 bit patterns with the level evaluated
-// in double precision.
+// in double precision.  The bucket table (level at the start of each
+// 5-mantissa-bit bucket of u) lets the encoder find the level with one table
+// read and one comparison.
 //
 // Decode (same section, the cut; section 4 for draft vs full): the 8-bit
 // code q gives m = q >= 0 ? q : ~q and yhat = sign ((1 + alpha)^(m/127) - 1)
@@ -51,6 +53,28 @@ CodeTable build_code_table() {
   return t;
 }
 
+// number of thresholds T[1..127] not above u
+int count_thresholds(const CodeTable &t, float u) {
+  int m = 0;
+  for (int k = 1; k <= kLevels; ++k) m += t.t[k] <= u ? 1 : 0;
+  return m;
+}
+
+BucketTable build_bucket_table(const CodeTable &t) {
+  BucketTable b;
+  b.ok = t.t[1] > float_from_bits(kBucketFirstKey << kBucketShift);
+  b.base[0] = 0;
+  for (int i = 1; i < kBuckets - 1; ++i) {
+    const uint32_t key = kBucketFirstKey + static_cast<uint32_t>(i) - 1u;
+    const int lo = count_thresholds(t, float_from_bits(key << kBucketShift));
+    const int hi = count_thresholds(t, float_from_bits(((key + 1u) << kBucketShift) - 1u));
+    b.base[i] = static_cast<uint8_t>(lo);
+    if (hi > lo + 1) b.ok = false;
+  }
+  b.base[kBuckets - 1] = static_cast<uint8_t>(kLevels);
+  return b;
+}
+
 double yhat_of_code(int q) {
   const int m = q >= 0 ? q : -q - 1;
   const double g = (std::pow(1.0 + kAlpha, static_cast<double>(m) / kLevels) - 1.0) / kAlpha;
@@ -76,9 +100,11 @@ std::once_flag g_once;
 CodeTable g_code;
 DecodeTable g_decode;
 DraftTable g_draft;
+BucketTable g_bucket;
 
 void init_tables() {
   g_code = build_code_table();
+  g_bucket = build_bucket_table(g_code);
   g_decode = build_decode_table();
   g_draft = build_draft_table();
 }
@@ -98,6 +124,11 @@ const DecodeTable &decode_table() {
 const DraftTable &draft_table() {
   std::call_once(g_once, init_tables);
   return g_draft;
+}
+
+const BucketTable &bucket_table() {
+  std::call_once(g_once, init_tables);
+  return g_bucket;
 }
 
 }  // namespace lynx

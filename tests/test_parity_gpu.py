@@ -385,5 +385,7 @@ def test_graph_replays_match_eager(lynx):
 
 
 def test_code_map_fast_path_is_exact_for_every_fp32_in_unit_interval(lynx):
-    """Exhaustive: all 1,065,353,217 fp32 values u in [0, 1]."""
+    """Exhaustive: all 1,065,353,217 fp32 values u in [0, 1], and every u in
+    (1, 2), which rounding can produce and which must take level 127."""
     assert lynx.selftest_code_map(0, 0x3F800001) == 0
+    assert lynx.selftest_code_map(0x3F800001, 0x40000000) == 0
