@@ -22,6 +22,10 @@ SOURCES = ["lynx_tables.cpp", "lynx_api.cpp", "lynx_encode.hip", "lynx_dequant.h
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",
           "-I", INCLUDE]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source flags.  The encoder's input is finite by contract; without NaN
+# semantics its min/max need no canonicalising instructions (the named fp32
+# operations and their rounding are unchanged).
+EXTRA = {"lynx_encode.hip": ["-fno-honor-nans"]}
 
 
 def sources():
@@ -34,7 +38,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in sources():
         obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+        cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip", *DEVICE]
         if verbose:

@@ -17,20 +17,28 @@ using lynx::PlanesArg;
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_ok[kMaxDevices];
+int g_dev_cus[kMaxDevices];
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_device() {
+// Checks that the current device is a gfx950 and returns its compute-unit
+// count through *cus (both cached per device).
+int check_device(int *cus = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LYNX_ERR_HIP;
   if (dev < 0 || dev >= kMaxDevices) return LYNX_ERR_DEVICE;
   std::call_once(g_dev_once[dev], [dev]() {
     hipDeviceProp_t prop;
     g_dev_ok[dev] = 0;
-    if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+    g_dev_cus[dev] = 0;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
       g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+      g_dev_cus[dev] = prop.multiProcessorCount;
+    }
   });
-  return g_dev_ok[dev] ? LYNX_OK : LYNX_ERR_DEVICE;
+  if (!g_dev_ok[dev] || g_dev_cus[dev] < 1) return LYNX_ERR_DEVICE;
+  if (cus) *cus = g_dev_cus[dev];
+  return LYNX_OK;
 }
 
 int check_planes(const lynx_planes *pl, bool need_residual) {

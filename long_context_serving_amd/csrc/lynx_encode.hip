@@ -51,7 +51,9 @@ __device__ __forceinline__ int level_exact(float u, const float *T) {
 }
 
 // LDS bucket entry: (bits of the first threshold above the bucket start,
-// level at the bucket start); every bucket holds at most one threshold.
+// level at the bucket start); every bucket holds at most one threshold, so
+// for u in the bucket the level is base + (bits(u) >= next threshold):
+// positive floats order like their bit patterns.
 __device__ __forceinline__ void fill_level_table(uint2 *lvl, const EncodeTables &tab) {
   for (int i = threadIdx.x; i < kBuckets; i += blockDim.x) {
     const int m = tab.base[i];
@@ -60,25 +62,56 @@ __device__ __forceinline__ void fill_level_table(uint2 *lvl, const EncodeTables 
   }
 }
 
-// Level of u in [0, 2) from its bits (u >= 1 gives 127, which is the level
-// of the clamped u): one table read and one comparison.  Positive floats
-// order like their bit patterns.
-__device__ __forceinline__ int level_fast(uint32_t ubits, const uint2 *lvl) {
-  uint32_t key = ubits >> kBucketShift;
-  key = key < kBucketFirstKey - 1u ? kBucketFirstKey - 1u : key;
-  key = key > kBucketLastKey ? kBucketLastKey : key;
-  const uint2 e = lvl[key - (kBucketFirstKey - 1u)];
-  return static_cast<int>(e.y) + (ubits >= e.x ? 1 : 0);
+// Streaming accesses: the input is read once and the outputs are not read
+// back by this kernel, so both bypass cache retention (non-temporal).  The
+// non-temporal stores are whole 16-byte units, contiguous across a wave:
+// narrower ones could not be merged into full lines.
+__device__ __forceinline__ uint4 load_stream(const char *p) {
+  const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+  return make_uint4(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                    __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3));
+}
+__device__ __forceinline__ void store_stream(char *p, uint4 v) {
+  uint32_t *q = reinterpret_cast<uint32_t *>(p);
+  __builtin_nontemporal_store(v.x, q);
+  __builtin_nontemporal_store(v.y, q + 1);
+  __builtin_nontemporal_store(v.z, q + 2);
+  __builtin_nontemporal_store(v.w, q + 3);
+}
+__device__ __forceinline__ void store_stream(float *p, float4 v) {
+  __builtin_nontemporal_store(v.x, p);
+  __builtin_nontemporal_store(v.y, p + 1);
+  __builtin_nontemporal_store(v.z, p + 2);
+  __builtin_nontemporal_store(v.w, p + 3);
 }
 
-// Sign-aware code of the centred value d: m for d >= 0, ~m for d < 0 (d is
-// never -0: x' - mu rounds an exact zero to +0).  Only the low byte is used.
-__device__ __forceinline__ uint32_t code_of(float d, float inv_s, const uint2 *lvl) {
-  const float u = fabsf(d) * inv_s;
-  const int m = level_fast(__float_as_uint(u), lvl);
-  const int sgn = static_cast<int>(__float_as_uint(d)) >> 31;
-  return static_cast<uint32_t>(m ^ sgn);
+// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 without LDS:
+// v_permlane16_swap / v_permlane32_swap of a value with itself return the
+// pair (value of the even row, value of the odd row) of 16 lanes, resp. of
+// the low and the high 32 lanes, so op(pair) is the reduction in every lane.
+template <typename Op>
+__device__ __forceinline__ float xreduce_f32(float v, Op op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+__device__ __forceinline__ double xsum_f64(double v) {
+#pragma unroll
+  for (int step = 0; step < 2; ++step) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+    const auto l = step == 0 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                             : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = step == 0 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                             : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    v = __builtin_bit_cast(double, static_cast<uint64_t>(l[0]) | (static_cast<uint64_t>(h[0]) << 32)) +
+        __builtin_bit_cast(double, static_cast<uint64_t>(l[1]) | (static_cast<uint64_t>(h[1]) << 32));
+  }
+  return v;
+}
+struct MinOp { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+struct MaxOp { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
 
 // low bytes of a, b, c, d -> bytes 0..3 of one word
 __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -107,17 +140,45 @@ __device__ __forceinline__ float round_up_7bits(float x) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// One workgroup per (page, head) tile; wave c owns chunk c; lane (cg, r)
-// holds channels 8cg..8cg+7 of the 8 tokens chunk_token(r, 0..7).  Two
-// workgroups fit on a CU (at most 128 VGPRs) so that one streams its tile in
-// while the other computes.  Addresses are a wave-uniform base plus a 32-bit
-// lane offset.
+// Level of u >= 0 from its bits: the key bits(u) >> 18 is clamped into the
+// bucket range (u below 2^-14 -> bucket 0, u >= 1 -> bucket 449, which also
+// keeps any u from non-finite input inside the table), then one table read
+// and one comparison.
+__device__ __forceinline__ uint32_t level_of(float u, const uint2 *lvl) {
+  const uint32_t ubits = __float_as_uint(u);
+  uint32_t key = ubits >> kBucketShift;
+  key = key < kBucketFirstKey - 1u ? kBucketFirstKey - 1u : key;
+  key = key > kBucketLastKey ? kBucketLastKey : key;
+  const uint2 e = lvl[key - (kBucketFirstKey - 1u)];
+  return e.y + (ubits >= e.x ? 1u : 0u);
+}
+
+// sign masks: byte k = 0xFF where element k is negative (v_perm selectors
+// 9 and 11 replicate bit 31 of the low and the high source)
+__device__ __forceinline__ uint32_t signs4(float a, float b, float c, float d) {
+  const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0b09u);
+  const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x0b090c0cu);
+  return ab | cd;
+}
+
+// Sign-aware code bytes of 4 centred values: m for d >= 0, ~m for d < 0 (d
+// is never -0: x' - mu rounds an exact zero to +0).
+__device__ __forceinline__ uint32_t codes4(float d0, float d1, float d2, float d3,
+                                           float i0, float i1, float i2, float i3,
+                                           const uint2 *lvl) {
+  const uint32_t m = pack4(level_of(fabsf(d0) * i0, lvl), level_of(fabsf(d1) * i1, lvl),
+                           level_of(fabsf(d2) * i2, lvl), level_of(fabsf(d3) * i3, lvl));
+  return m ^ signs4(d0, d1, d2, d3);
+}
+
+// One workgroup of 8 waves per (page, head) tile; wave c owns chunk c; lane
+// (cg, r) holds channels 8cg..8cg+7 of the 8 tokens chunk_token(r, 0..7).
+// Two workgroups fit on a CU (at most 128 VGPRs), so that one streams its
+// tile in while the other computes.  Addresses are a wave-uniform base plus
+// 32-bit lane offsets.
 template <int kRole>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, EncodeTables tab) {
-  const int tile = blockIdx.x;  // page * heads + head
-  const int p = tile / heads;
-  const int h = tile - p * heads;
   const int c = threadIdx.x >> 6;  // chunk = wave
   const int lane = threadIdx.x & 63;
   const int cg = lane & 15;
@@ -128,169 +189,179 @@ void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, En
   __shared__ float s_max[kChunks][kDim];
   __shared__ float s_mn[kDim];
   __shared__ float s_inv[kDim];
+  // The planes are staged in LDS and written out as contiguous 16-byte
+  // units.  K rows of 16 words are padded to 20 and V's 16-byte units are
+  // XOR-swizzled (unit ^ (unit >> 3 & 7)), which spreads a wave's word
+  // writes over the banks and keeps every 16-byte unit contiguous.
+  __shared__ __align__(16) uint32_t s_pl[2][kPage * 20];
 
+  const int tile = blockIdx.x;  // page * heads + head
   fill_level_table(s_lvl, tab);  // published by the first __syncthreads below
 
   // ---- load the lane's 8 tokens x 8 channels (bf16 -> fp32 is exact) ----
-  const uint32_t row_bytes = static_cast<uint32_t>(heads) * kDim * 2;
-  const char *page = reinterpret_cast<const char *>(kv) +
-                     static_cast<size_t>(p) * kPage * row_bytes + static_cast<size_t>(h) * kDim * 2;
-  const uint32_t lane_off = static_cast<uint32_t>(c * kChunk) * row_bytes + cg * 16;
   float x[8][8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t off = lane_off + static_cast<uint32_t>(chunk_token(r, j)) * row_bytes;
-    const uint4 v = *reinterpret_cast<const uint4 *>(page + off);
-    x[j][0] = bf16_lo(v.x); x[j][1] = bf16_hi(v.x);
-    x[j][2] = bf16_lo(v.y); x[j][3] = bf16_hi(v.y);
-    x[j][4] = bf16_lo(v.z); x[j][5] = bf16_hi(v.z);
-    x[j][6] = bf16_lo(v.w); x[j][7] = bf16_hi(v.w);
-  }
-
-  // ---- page-level normalisation: per-channel min and max ----
   {
-    float mn[8], mx[8];
+    const int p = tile / heads;
+    const int h = tile - p * heads;
+    const uint32_t row_bytes = static_cast<uint32_t>(heads) * kDim * 2;
+    const char *page = reinterpret_cast<const char *>(kv) +
+                       static_cast<size_t>(p) * kPage * row_bytes + static_cast<size_t>(h) * kDim * 2;
+    const uint32_t lane_off = static_cast<uint32_t>(c * kChunk) * row_bytes + cg * 16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t off = lane_off + static_cast<uint32_t>(chunk_token(r, j)) * row_bytes;
+      const uint4 v = load_stream(page + off);
+      x[j][0] = bf16_lo(v.x); x[j][1] = bf16_hi(v.x);
+      x[j][2] = bf16_lo(v.y); x[j][3] = bf16_hi(v.y);
+      x[j][4] = bf16_lo(v.z); x[j][5] = bf16_hi(v.z);
+      x[j][6] = bf16_lo(v.w); x[j][7] = bf16_hi(v.w);
+    }
+  }
+  {
+    // ---- page-level normalisation: per-channel min and max ----
+    {
+      float mn[8], mx[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        mn[i] = fminf(fminf(fminf(x[0][i], x[1][i]), fminf(x[2][i], x[3][i])),
+                      fminf(fminf(x[4][i], x[5][i]), fminf(x[6][i], x[7][i])));
+        mx[i] = fmaxf(fmaxf(fmaxf(x[0][i], x[1][i]), fmaxf(x[2][i], x[3][i])),
+                      fmaxf(fmaxf(x[4][i], x[5][i]), fmaxf(x[6][i], x[7][i])));
+        mn[i] = xreduce_f32(mn[i], MinOp());
+        mx[i] = xreduce_f32(mx[i], MaxOp());
+      }
+      if (r == 0) {
+        reinterpret_cast<float4 *>(&s_min[c][cg * 8])[0] = make_float4(mn[0], mn[1], mn[2], mn[3]);
+        reinterpret_cast<float4 *>(&s_min[c][cg * 8])[1] = make_float4(mn[4], mn[5], mn[6], mn[7]);
+        reinterpret_cast<float4 *>(&s_max[c][cg * 8])[0] = make_float4(mx[0], mx[1], mx[2], mx[3]);
+        reinterpret_cast<float4 *>(&s_max[c][cg * 8])[1] = make_float4(mx[4], mx[5], mx[6], mx[7]);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kDim) {
+      const int d = threadIdx.x;
+      float a = s_min[0][d], b = s_max[0][d];
+#pragma unroll
+      for (int cc = 1; cc < kChunks; ++cc) {
+        a = fminf(a, s_min[cc][d]);
+        b = fmaxf(b, s_max[cc][d]);
+      }
+      // the range is kept with 7 significant bits (rounded up), which makes
+      // every scale product exact in the decoder's fp16 operand halves
+      const float rg = round_up_7bits(b - a);
+      // correctly rounded fp32 reciprocal (fp64 quotient, one rounding)
+      const float inv = rg > 0.0f ? static_cast<float>(1.0 / static_cast<double>(rg)) : 0.0f;
+      s_mn[d] = a;
+      s_inv[d] = inv;
+      __builtin_nontemporal_store(a, out.page_min + static_cast<size_t>(tile) * kDim + d);
+      __builtin_nontemporal_store(rg, out.page_range + static_cast<size_t>(tile) * kDim + d);
+    }
+    __syncthreads();
+
+    // ---- x' = (x - mn) * inv_rg, and the exact chunk sum in fp64 ----
+    float mu[8];
+    {
+      const float4 mn0 = reinterpret_cast<const float4 *>(&s_mn[cg * 8])[0];
+      const float4 mn1 = reinterpret_cast<const float4 *>(&s_mn[cg * 8])[1];
+      const float4 iv0 = reinterpret_cast<const float4 *>(&s_inv[cg * 8])[0];
+      const float4 iv1 = reinterpret_cast<const float4 *>(&s_inv[cg * 8])[1];
+      const float mn[8] = {mn0.x, mn0.y, mn0.z, mn0.w, mn1.x, mn1.y, mn1.z, mn1.w};
+      const float inv_rg[8] = {iv0.x, iv0.y, iv0.z, iv0.w, iv1.x, iv1.y, iv1.z, iv1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        double sum = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[j][i] = (x[j][i] - mn[i]) * inv_rg[i];
+          sum += static_cast<double>(x[j][i]);
+        }
+        sum = xsum_f64(sum);
+        mu[i] = static_cast<float>(sum * (1.0 / kChunk));
+      }
+    }
+
+    // ---- chunk centring and max-abs ----
+    float sabs[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      mn[i] = x[0][i];
-      mx[i] = x[0][i];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) {
-        mn[i] = fminf(mn[i], x[j][i]);
-        mx[i] = fmaxf(mx[i], x[j][i]);
-      }
-      mn[i] = fminf(mn[i], __shfl_xor(mn[i], 16));
-      mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 16));
-      mn[i] = fminf(mn[i], __shfl_xor(mn[i], 32));
-      mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], 32));
+      for (int j = 0; j < 8; ++j) x[j][i] = x[j][i] - mu[i];
+      sabs[i] = fmaxf(fmaxf(fmaxf(fabsf(x[0][i]), fabsf(x[1][i])),
+                            fmaxf(fabsf(x[2][i]), fabsf(x[3][i]))),
+                      fmaxf(fmaxf(fabsf(x[4][i]), fabsf(x[5][i])),
+                            fmaxf(fabsf(x[6][i]), fabsf(x[7][i]))));
+      sabs[i] = xreduce_f32(sabs[i], MaxOp());
+      sabs[i] = round_up_7bits(sabs[i]);
     }
     if (r == 0) {
-      reinterpret_cast<float4 *>(&s_min[c][cg * 8])[0] = make_float4(mn[0], mn[1], mn[2], mn[3]);
-      reinterpret_cast<float4 *>(&s_min[c][cg * 8])[1] = make_float4(mn[4], mn[5], mn[6], mn[7]);
-      reinterpret_cast<float4 *>(&s_max[c][cg * 8])[0] = make_float4(mx[0], mx[1], mx[2], mx[3]);
-      reinterpret_cast<float4 *>(&s_max[c][cg * 8])[1] = make_float4(mx[4], mx[5], mx[6], mx[7]);
+      const size_t cidx = (static_cast<size_t>(tile) * kChunks + c) * kDim + cg * 8;
+      store_stream(out.chunk_mean + cidx, make_float4(mu[0], mu[1], mu[2], mu[3]));
+      store_stream(out.chunk_mean + cidx + 4, make_float4(mu[4], mu[5], mu[6], mu[7]));
+      store_stream(out.chunk_maxabs + cidx, make_float4(sabs[0], sabs[1], sabs[2], sabs[3]));
+      store_stream(out.chunk_maxabs + cidx + 4, make_float4(sabs[4], sabs[5], sabs[6], sabs[7]));
     }
-  }
-  __syncthreads();
-  if (threadIdx.x < kDim) {
-    const int d = threadIdx.x;
-    float a = s_min[0][d], b = s_max[0][d];
+    // correctly rounded reciprocals: each of the 4 lanes sharing these
+    // channels computes 2 of the 8, the rest are gathered from the other lanes
+    float inv_s[8];
+    {
+      float my_inv[2];
 #pragma unroll
-    for (int cc = 1; cc < kChunks; ++cc) {
-      a = fminf(a, s_min[cc][d]);
-      b = fmaxf(b, s_max[cc][d]);
+      for (int k = 0; k < 2; ++k) {
+        const float s = r == 0 ? sabs[k] : r == 1 ? sabs[2 + k] : r == 2 ? sabs[4 + k] : sabs[6 + k];
+        my_inv[k] = s > 0.0f ? static_cast<float>(1.0 / static_cast<double>(s)) : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int src = cg + 16 * (i >> 1);  // lane holding channel i's reciprocal
+        inv_s[i] = __shfl(my_inv[i & 1], src);
+      }
     }
-    // the range is kept with 7 significant bits (rounded up), which makes
-    // every scale product exact in the decoder's fp16 operand halves
-    const float rg = round_up_7bits(b - a);
-    // correctly rounded fp32 reciprocal (fp64 quotient, one rounding)
-    const float inv = rg > 0.0f ? static_cast<float>(1.0 / static_cast<double>(rg)) : 0.0f;
-    s_mn[d] = a;
-    s_inv[d] = inv;
-    out.page_min[static_cast<size_t>(tile) * kDim + d] = a;
-    out.page_range[static_cast<size_t>(tile) * kDim + d] = rg;
-  }
-  __syncthreads();
 
-  // ---- x' = (x - mn) * inv_rg, and the exact chunk sum in fp64 ----
-  float mu[8];
-  {
-    const float4 mn0 = reinterpret_cast<const float4 *>(&s_mn[cg * 8])[0];
-    const float4 mn1 = reinterpret_cast<const float4 *>(&s_mn[cg * 8])[1];
-    const float4 iv0 = reinterpret_cast<const float4 *>(&s_inv[cg * 8])[0];
-    const float4 iv1 = reinterpret_cast<const float4 *>(&s_inv[cg * 8])[1];
-    const float mn[8] = {mn0.x, mn0.y, mn0.z, mn0.w, mn1.x, mn1.y, mn1.z, mn1.w};
-    const float inv_rg[8] = {iv0.x, iv0.y, iv0.z, iv0.w, iv1.x, iv1.y, iv1.z, iv1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      double sum = 0.0;
+    // ---- sign-aware alpha-law codes and the cut into nibble planes ----
+    if (kRole == LYNX_ROLE_KEY) {
+      // token-major [256 tokens][64 B]: one word = 8 channels of one token
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        x[j][i] = (x[j][i] - mn[i]) * inv_rg[i];
-        sum += static_cast<double>(x[j][i]);
+        const uint32_t we = codes4(x[j][0], x[j][2], x[j][4], x[j][6],
+                                   inv_s[0], inv_s[2], inv_s[4], inv_s[6], s_lvl);
+        const uint32_t wo = codes4(x[j][1], x[j][3], x[j][5], x[j][7],
+                                   inv_s[1], inv_s[3], inv_s[5], inv_s[7], s_lvl);
+        const int widx = (c * kChunk + chunk_token(r, j)) * 20 + cg;
+        s_pl[0][widx] = anchor_word(we, wo);
+        s_pl[1][widx] = residual_word(we, wo);
       }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      mu[i] = static_cast<float>(sum * (1.0 / kChunk));
-    }
-  }
-
-  // ---- chunk centring and max-abs ----
-  float sabs[8];
+    } else {
+      // channel-major [8 chunks][128 channels][16 B]: one word = the lane's
+      // 8 tokens of one channel
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    sabs[i] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x[j][i] = x[j][i] - mu[i];
-      sabs[i] = fmaxf(sabs[i], fabsf(x[j][i]));
+      for (int i = 0; i < 8; ++i) {
+        const float is = inv_s[i];
+        const uint32_t we = codes4(x[0][i], x[2][i], x[4][i], x[6][i], is, is, is, is, s_lvl);
+        const uint32_t wo = codes4(x[1][i], x[3][i], x[5][i], x[7][i], is, is, is, is, s_lvl);
+        const int unit = c * kDim + cg * 8 + i;
+        const int widx = (unit ^ ((unit >> 3) & 7)) * 4 + r;
+        s_pl[0][widx] = anchor_word(we, wo);
+        s_pl[1][widx] = residual_word(we, wo);
+      }
     }
-    sabs[i] = fmaxf(sabs[i], __shfl_xor(sabs[i], 16));
-    sabs[i] = fmaxf(sabs[i], __shfl_xor(sabs[i], 32));
-    sabs[i] = round_up_7bits(sabs[i]);
-  }
-  if (r == 0) {
-    const size_t cidx = (static_cast<size_t>(tile) * kChunks + c) * kDim + cg * 8;
-    reinterpret_cast<float4 *>(out.chunk_mean + cidx)[0] = make_float4(mu[0], mu[1], mu[2], mu[3]);
-    reinterpret_cast<float4 *>(out.chunk_mean + cidx)[1] = make_float4(mu[4], mu[5], mu[6], mu[7]);
-    reinterpret_cast<float4 *>(out.chunk_maxabs + cidx)[0] =
-        make_float4(sabs[0], sabs[1], sabs[2], sabs[3]);
-    reinterpret_cast<float4 *>(out.chunk_maxabs + cidx)[1] =
-        make_float4(sabs[4], sabs[5], sabs[6], sabs[7]);
-  }
-  // correctly rounded reciprocals: each of the 4 lanes sharing these
-  // channels computes 2 of the 8, the rest are gathered from the other lanes
-  float inv_s[8];
-  {
-    float my_inv[2];
+    __syncthreads();
+    // write-out: 1024 units of 16 B per plane, two per thread, contiguous
+    char *an = reinterpret_cast<char *>(out.anchor) + static_cast<size_t>(tile) * kPlaneTileBytes;
+    char *re = reinterpret_cast<char *>(out.residual) + static_cast<size_t>(tile) * kPlaneTileBytes;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const float s = r == 0 ? sabs[k] : r == 1 ? sabs[2 + k] : r == 2 ? sabs[4 + k] : sabs[6 + k];
-      my_inv[k] = s > 0.0f ? static_cast<float>(1.0 / static_cast<double>(s)) : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int src = cg + 16 * (i >> 1);  // lane holding channel i's reciprocal
-      inv_s[i] = __shfl(my_inv[i & 1], src);
-    }
-  }
-
-  // ---- sign-aware alpha-law codes and the cut into nibble planes ----
-  char *an = reinterpret_cast<char *>(out.anchor) + static_cast<size_t>(tile) * kPlaneTileBytes;
-  char *re = reinterpret_cast<char *>(out.residual) + static_cast<size_t>(tile) * kPlaneTileBytes;
-  if (kRole == LYNX_ROLE_KEY) {
-    // token-major [256 tokens][64 B]: one word = 8 channels of one token
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t q[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = code_of(x[j][i], inv_s[i], s_lvl);
-      const uint32_t we = pack4(q[0], q[2], q[4], q[6]);
-      const uint32_t wo = pack4(q[1], q[3], q[5], q[7]);
-      const uint32_t off = static_cast<uint32_t>(c * kChunk + chunk_token(r, j)) * 64 + cg * 4;
-      *reinterpret_cast<uint32_t *>(an + off) = anchor_word(we, wo);
-      *reinterpret_cast<uint32_t *>(re + off) = residual_word(we, wo);
-    }
-  } else {
-    // channel-major [8 chunks][128 channels][16 B]: one word = the lane's 8
-    // tokens of one channel
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t q[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = code_of(x[j][i], inv_s[i], s_lvl);
-      const uint32_t we = pack4(q[0], q[2], q[4], q[6]);
-      const uint32_t wo = pack4(q[1], q[3], q[5], q[7]);
-      const uint32_t off = static_cast<uint32_t>(c * kDim + cg * 8 + i) * 16 + r * 4;
-      *reinterpret_cast<uint32_t *>(an + off) = anchor_word(we, wo);
-      *reinterpret_cast<uint32_t *>(re + off) = residual_word(we, wo);
+      const int unit = k * kEncThreads + threadIdx.x;
+      const int widx = kRole == LYNX_ROLE_KEY ? (unit >> 2) * 20 + (unit & 3) * 4
+                                              : (unit ^ ((unit >> 3) & 7)) * 4;
+      store_stream(an + unit * 16, *reinterpret_cast<const uint4 *>(&s_pl[0][widx]));
+      store_stream(re + unit * 16, *reinterpret_cast<const uint4 *>(&s_pl[1][widx]));
     }
   }
 }
 
-// Exhaustive check of the bucket level path against the exact threshold
-// count over fp32 bit patterns [begin, end) (values in [0, 2); above 1 the
-// expected level is that of the clamped u, 127).
+// Exhaustive check of the encoder's level path (the bucket table) against
+// the exact threshold count over fp32 bit patterns [begin, end) (values in
+// [0, 2); above 1 the expected level is that of the clamped u, 127).
 __global__ __launch_bounds__(256) void code_map_check_kernel(uint32_t begin, uint32_t end,
                                                              unsigned long long *mismatches,
                                                              EncodeTables tab) {
@@ -304,7 +375,7 @@ __global__ __launch_bounds__(256) void code_map_check_kernel(uint32_t begin, uin
   for (uint32_t b = begin + blockIdx.x * blockDim.x + threadIdx.x; b < end && b >= begin;
        b += stride) {
     const float u = __uint_as_float(b);
-    bad += level_fast(b, s_lvl) != level_exact(fminf(u, 1.0f), s_T);
+    bad += static_cast<int>(level_of(u, s_lvl)) != level_exact(fminf(u, 1.0f), s_T);
   }
   if (bad) atomicAdd(mismatches, bad);
 }
