@@ -31,6 +31,103 @@ sys.path.insert(0, ROOT)
 
 METRIC = "encode GB/s + fused-dequant decode-attn GB/s (% of HBM peak), 1×MI355X"
 HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+ENCODER_SOURCE = os.path.join(ROOT, "long_context_serving_amd", "csrc", "lynx_encode.hip")
+TRAFFIC_SUMMARY = os.path.join(PROFILES, "encode_kernel_ctx32k_hbm_traffic.txt")
+COPY_PROBE_BYTES = 256 << 20
+
+
+def source_sha1(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per encoder launch from the committed counter summary, or
+    None when the summary is missing or was taken on another encoder source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    if kv.get("encoder_source_sha1", "").strip() != source_sha1(ENCODER_SOURCE):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize(kind, db_dir, out_path, command):
+    """Write a short text summary of rocprofv3 output (kernel trace with
+    --stats, or FETCH_SIZE / WRITE_SIZE counter runs) under profiles/."""
+    import glob
+    import sqlite3
+
+    def dbs(d):
+        return sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+
+    def short(name):
+        name = name.replace("lynx::(anonymous namespace)::", "").replace("void ", "")
+        return name.split("(")[0]
+
+    lines = ["command: %s" % command]
+    if kind == "kt":
+        lines.append("")
+        lines.append("%-44s %7s %11s %13s %6s" % ("kernel", "calls", "avg_us", "total_us", "pct"))
+        for db in dbs(db_dir):
+            con = sqlite3.connect(db)
+            for name, calls, total, avg, pct in con.execute(
+                    "select name, total_calls, total_duration, average, percentage from top_kernels"):
+                # the top_kernels view reports microseconds
+                lines.append("%-44s %7d %11.2f %13.1f %6.1f" % (short(name)[:44], calls, avg, total,
+                                                               pct))
+    else:
+        # kind == "pmc": db_dir = "<fetch dir>,<write dir>"
+        fetch_dir, write_dir = db_dir.split(",")
+        per = {}
+        probe = {}
+        for d, ctr in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+            for db in dbs(d):
+                con = sqlite3.connect(db)
+                for name, val in con.execute(
+                        "select kernel_name, value from counters_collection where counter_name = ?",
+                        (ctr,)):
+                    per.setdefault(short(name), {}).setdefault(ctr, []).append(val)
+                    # the 256 MiB probe copy runs as a few large blit dispatches;
+                    # other copies of the run are tiny
+                    if "copyBuffer" in name and val > 4096.0:
+                        probe[ctr] = probe.get(ctr, 0.0) + val
+        avg = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in per.items()}
+        if "FETCH_SIZE" not in probe or "WRITE_SIZE" not in probe:
+            raise SystemExit("no copy-probe dispatch in the counter runs (run bench.py --copy-probe)")
+        exp_kib = COPY_PROBE_BYTES / 1024.0
+        f_fetch = exp_kib / probe["FETCH_SIZE"]
+        f_write = exp_kib / probe["WRITE_SIZE"]
+        enc = [k for k in avg if k.startswith("encode_kernel")]
+        enc_fetch = sum(avg[k]["FETCH_SIZE"] for k in enc) / len(enc)
+        enc_write = sum(avg[k]["WRITE_SIZE"] for k in enc) / len(enc)
+        traffic = (enc_fetch * f_fetch + enc_write * f_write) * 1024.0
+        lines += [
+            "encoder_source_sha1: %s" % source_sha1(ENCODER_SOURCE),
+            "copy_probe: device copy of %d bytes; FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB in total" % (
+                COPY_PROBE_BYTES, probe["FETCH_SIZE"], probe["WRITE_SIZE"]),
+            "fetch_scale: %.4f" % f_fetch,
+            "write_scale: %.4f" % f_write,
+            "encode_fetch_kib_per_dispatch: %.1f" % enc_fetch,
+            "encode_write_kib_per_dispatch: %.1f" % enc_write,
+            "traffic_bytes_per_launch: %.0f" % traffic,
+            "",
+            "%-44s %16s %16s" % ("kernel", "FETCH_SIZE KiB", "WRITE_SIZE KiB"),
+        ]
+        for k in sorted(avg):
+            lines.append("%-44s %16.1f %16.1f" % (k[:44], avg[k].get("FETCH_SIZE", float("nan")),
+                                                  avg[k].get("WRITE_SIZE", float("nan"))))
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def algorithmic_bytes(w):
@@ -88,7 +185,13 @@ def main():
     ap.add_argument("--cpu-pages", type=int, default=128, help="pages in the CPU-baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 256 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize", nargs=4, metavar=("KIND", "DB_DIR", "OUT", "COMMAND"),
+                    help="write a text summary of rocprofv3 output (KIND kt or pmc; for pmc "
+                         "DB_DIR is '<FETCH_SIZE dir>,<WRITE_SIZE dir>') and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -199,7 +302,7 @@ def main():
         per_call_ms[name] = t0.elapsed_time(t1) / (reps * calls)
 
     if args.copy_probe:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
@@ -241,7 +344,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "encode_kernel",
                      "achieved": gbps(ab["encode"], enc_avg), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": gbps(ab["encode"], enc_avg) / HBM_PEAK_GBPS,
-                     "traffic": None},
+                     "traffic": measured_traffic(), "algorithmic_bytes": ab["encode"]},
         "wall_s_timed": wall,
     }
     if args.cpu:
