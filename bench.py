@@ -174,6 +174,65 @@ def cpu_baseline(w, xk, xv, qb, pages, sm):
     }
 
 
+def progressive_main(args):
+    """Progressive plane streaming of the 32-layer 64K workload (anchor
+    planes first, residual planes after; drafts start as anchors land).
+    Prints one JSON line; link rates are PCIe host-to-device rates."""
+    import statistics
+    import torch
+    from long_context_serving_amd import lynx, stream, synth
+
+    w = synth.WORKLOADS["progressive32x64k"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sm = float(np.float32(1.0 / math.sqrt(w.head_dim)))
+    log("bench: encoding %d layers of %d tokens into pinned host planes" % (w.layers, w.tokens))
+    t0 = time.perf_counter()
+    ps = stream.ProgressiveStream(stream.build_layers(w, device=dev), device=dev, sm_scale=sm)
+    log("bench: built in %.1f s" % (time.perf_counter() - t0))
+    runs = max(1, args.stream_runs)
+    prog = [ps.run_progressive() for _ in range(runs + 1)][1:]
+    int8 = [ps.run_layerwise_int8() for _ in range(runs + 1)][1:]
+    med = lambda rs, key: statistics.median(r[key] for r in rs)
+    # bf16 comparison: the raw cache of one layer (K and V) copied once per layer
+    bf16_layer = 2 * w.tokens * w.kv_heads * w.head_dim * 2
+    hb = torch.empty(bf16_layer, dtype=torch.uint8, pin_memory=True)
+    db = torch.empty(bf16_layer, dtype=torch.uint8, device=dev)
+    bf16_ms = []
+    for _ in range(runs + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(w.layers):
+            db.copy_(hb, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        bf16_ms.append(e0.elapsed_time(e1))
+    bf16_all = statistics.median(bf16_ms[1:])
+    overlap = ps.draft_full_topk_overlap((1, 16, 64))
+    ab, rb = ps.anchor_bytes(), ps.residual_bytes()
+    a_ms, r_ms = med(prog, "anchors_landed_ms"), med(prog, "residuals_landed_ms")
+    result = {
+        "metric": "progressive plane streaming: time to all drafts / all full attention (ms), 1xMI355X",
+        "value": med(prog, "all_drafts_ms"),
+        "unit": "ms",
+        "higher_is_better": False,
+        "n_gpus": 1,
+        "runs": runs,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads,
+                   "tokens": w.tokens, "q_heads": w.q_heads},
+        "anchor_bytes": ab, "residual_bytes": rb, "bf16_bytes": bf16_layer * w.layers,
+        "h2d_anchor_GBps": ab / (a_ms * 1e-3) / 1e9,
+        "h2d_residual_GBps": rb / ((r_ms - a_ms) * 1e-3) / 1e9,
+        "lynx": {k: med(prog, k) for k in prog[0]},
+        "lynx_int8_layerwise": {k: med(int8, k) for k in int8[0]},
+        "bf16_copy_all_layers_ms": bf16_all,
+        "draft_vs_full_topk_overlap": {str(k): v for k, v in overlap.items()},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +244,9 @@ def main():
     ap.add_argument("--cpu-pages", type=int, default=128, help="pages in the CPU-baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 256 MiB device copy (counter calibration)")
+    ap.add_argument("--progressive", action="store_true",
+                    help="run the progressive plane-streaming harness (32 layers x 64K) instead")
+    ap.add_argument("--stream-runs", type=int, default=3)
     ap.add_argument("--summarize", nargs=4, metavar=("KIND", "DB_DIR", "OUT", "COMMAND"),
                     help="write a text summary of rocprofv3 output (KIND kt or pmc; for pmc "
                          "DB_DIR is '<FETCH_SIZE dir>,<WRITE_SIZE dir>') and exit")
@@ -194,6 +256,9 @@ def main():
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.progressive and args.gpus == 1 and world == 1:
+        progressive_main(args)
+        return
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not "
               "supported. The multi-GPU sharding is a design note only." % (args.gpus, world),

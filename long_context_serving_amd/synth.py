@@ -139,6 +139,30 @@ def kv_pages(w: Workload, layer: int, tensor: int, request: int,
     return float_to_bf16_bits(x).reshape(T // PAGE, PAGE, w.kv_heads, w.head_dim)
 
 
+def device_kv_pages(w: Workload, layer: int, tensor: int, request: int, device="cuda",
+                    tokens: Optional[int] = None):
+    """kv_pages' recipe drawn on the device with torch's generator, for caches
+    of many GB (the progressive-streaming harness).  Same distribution, same
+    outlier channels and offsets, but not the same values as kv_pages:
+    Laplace(0, 1) by inverse CDF from u uniform in (0, 1),
+    z = -sign(u - 1/2) ln(1 - 2|u - 1/2|).  Returns bf16 bit patterns as int16
+    [tokens/256][256][H][D] on the device."""
+    import torch
+    T = w.tokens if tokens is None else tokens
+    if T % PAGE:
+        raise ValueError("tokens must be a multiple of 256")
+    mult, off = _channel_plan(w, layer, tensor)
+    seed = int(np.random.SeedSequence([w.seed, w.cfg_id, layer, tensor, request + 1, 0xD7]).generate_state(1)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    u = torch.rand((T, w.kv_heads, w.head_dim), generator=g, device=device, dtype=torch.float32)
+    c = u * (1.0 - 2.0 ** -24) + 2.0 ** -25 - 0.5          # u in (0, 1): |c| < 1/2
+    z = -torch.sign(c) * torch.log1p(-2.0 * c.abs())
+    x = z * torch.as_tensor(mult, dtype=torch.float32, device=device) + \
+        torch.as_tensor(off, dtype=torch.float32, device=device)
+    return x.to(torch.bfloat16).view(torch.int16).reshape(T // PAGE, PAGE, w.kv_heads, w.head_dim)
+
+
 def queries(w: Workload, batch: Optional[int] = None, first_request: int = 0,
             layer: int = 0, key_aligned: bool = True) -> np.ndarray:
     """bf16 bit patterns of the decode queries of one layer: uint16 [B][Hq][D]."""
