@@ -294,8 +294,7 @@ def main():
     qb = synth.queries(w)
     q = to_dev(qb)
     out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(16, lynx.workspace_size(w.batch, w.kv_heads, w.q_heads, w.pages)),
-                     dtype=torch.uint8, device=dev)
+    ws = lynx.alloc_workspace(w.batch, w.kv_heads, w.q_heads, w.pages, dev)
     # One HIP graph per step (four phases).  The timed loop replays K of
     # them; per-kernel averages come from graphs that hold the same call on
     # every buffer set back to back, timed with events on the replay stream.

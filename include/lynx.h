@@ -162,7 +162,8 @@ int lynx_dequantize_full(const lynx_planes *in, int64_t num_pages,
  *                logits, for ranking comparisons; NULL = not written
  *   workspace    device scratch of at least
  *                lynx_decode_attention_workspace_size(...) bytes, 16-byte
- *                aligned; contents need not be initialised
+ *                aligned; contents need not be initialised.  Calls that
+ *                overlap in time must not share a workspace.
  * The anchor variant never reads k->residual or v->residual.  batch = 0 is
  * a no-op once the shape arguments are valid (no pointer is inspected).
  * Errors: NULL_ARG, BAD_SHAPE, MISALIGNED, WORKSPACE, DEVICE, HIP.

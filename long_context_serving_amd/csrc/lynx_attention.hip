@@ -30,14 +30,10 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kMaxG = LYNX_MAX_GROUP;
-#ifndef LYNX_TARGET_BLOCKS_MFMA
-#define LYNX_TARGET_BLOCKS_MFMA 512
-#endif
-constexpr int kTargetBlocks = 2048;                         // VALU kernel (group > 8)
-constexpr int kTargetBlocksMfma = LYNX_TARGET_BLOCKS_MFMA;  // MFMA kernel: 4 waves per block
+constexpr int kTargetBlocks = 2048;  // VALU kernel (group > 8)
 // splits per (request, KV head) never exceed the block target (see
 // attention_shape), which bounds the combine kernel's weight array
-constexpr int kMaxSplits = kTargetBlocks > kTargetBlocksMfma ? kTargetBlocks : kTargetBlocksMfma;
+constexpr int kMaxSplits = kTargetBlocks;
 constexpr int kCombineThreads = 256;
 constexpr int kCombineParts = 4;  // the combine splits the head dimension into 4 x 32 channels
 
@@ -374,7 +370,8 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
   s.max_pages = max_pages;
   s.pool_pages = 0;
   const long long units = static_cast<long long>(batch) * heads;
-  const long long target = attention_mfma_supported(s.group) ? kTargetBlocksMfma : kTargetBlocks;
+  const long long target =
+      attention_mfma_supported(s.group) ? attention_mfma_target_blocks() : kTargetBlocks;
   long long pps = units > 0 ? (units * max_pages + target - 1) / target : 1;
   if (pps < 1) pps = 1;
   if (pps > max_pages) pps = max_pages > 0 ? max_pages : 1;
@@ -383,6 +380,7 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
   return s;
 }
 
+// Partials (m, l, o) of every split.
 size_t attention_workspace_bytes(const AttnShape &s) {
   const size_t n = static_cast<size_t>(s.batch) * s.heads * s.splits * s.group;
   return ((n + 1) & ~static_cast<size_t>(1)) * sizeof(double) +
@@ -396,15 +394,9 @@ hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
                             float *scores, void *workspace,
                             hipStream_t stream) {
   if (s.batch == 0) return hipSuccess;
-  if (attention_mfma_supported(s.group)) {
-    const hipError_t e = launch_attention_mfma(q, k, v, block_table, seq_lens, s, sm_scale, full,
-                                               scores, workspace, stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel,
-                       dim3(static_cast<unsigned>(s.batch * s.q_heads * kCombineParts)),
-                       dim3(kCombineThreads), 0, stream, s, static_cast<const void *>(workspace), out);
-    return hipGetLastError();
-  }
+  if (attention_mfma_supported(s.group))
+    return launch_attention_mfma(q, k, v, block_table, seq_lens, s, sm_scale, full, out, scores,
+                                 workspace, stream);
   YTable tab;
   const DecodeTable &dt = decode_table();
   for (int i = 0; i < 256; ++i) tab.y[i] = dt.y[i];

@@ -2,33 +2,43 @@
 //
 // Page "Lynx: the KV cache does not have to arrive whole", section 4 (draft
 // on the anchor stream, refinement on anchor + residual); page "LLM KV cache
-// quantization", sections "The architecture" and "End-to-end flow" (read
-// the compact cache, expand it only in registers, attention unchanged).
+// quantization", sections "The architecture" and "End-to-end flow" (read the
+// compact cache, expand it only in registers, attention unchanged).
 //
-// Per (request, KV head), each wave streams 32-token chunks.  With
-//   khat = c0 + c1*yhat, vhat = c0v + c1v*yhat   (c0 = mn + rg*mu, c1 = rg*s)
-// a chunk needs two dense products that run on v_mfma_f32_16x16x32_f16:
-//   S^T[16 tok][16 col] += Yk[16 tok][32 ch] * Q'[32 ch][16 col]  (4 K-steps)
-//   O  [16 col][16 ch ] += P [16 col][32 tok] * Yv[32 tok][16 ch]
-// yhat comes from a table as an fp16 pair hi + lo (22 bits).  The encoder
-// keeps the page range and chunk max-abs with 7 significant bits, so
-// q' = q * rg * s of a bf16 query has at most 22 bits and is split EXACTLY
-// into two fp16 halves (after a per-chunk power-of-two scale that keeps it
-// inside the fp16 range).  The 16 MFMA columns hold [Q'hi of the 8 heads |
-// Q'lo of the 8 heads] (and likewise P), so running the Y side twice (hi,
-// then lo, into separate accumulators) yields all four cross products.
-// With 100x outlier channels scores reach a few hundred and the output is
-// sensitive to one fp32 ulp of a score, so the score is never rounded to
-// fp32 at its full magnitude: the large (hi x hi) part and the small parts,
-// the fp64 chunk bias and the softmax shift are combined in fp64, and only
-// the small difference to the running max is rounded before exp().
+// Algebra.  With khat = c0 + c1*yhat and vhat = c0v + c1v*yhat per chunk
+// and channel (c0 = mn + rg*mu, c1 = rg*s), a 32-token chunk needs two dense
+// products, both on v_mfma_f32_16x16x32_f16:
+//   S^T[16 tok][16 col]  = Yk[16 tok][k] * Q'[k][16 col]          (8 steps)
+//   O^T[16 ch ][16 col] += Yv^T[16 ch][k] * P[k][16 col]          (2 steps)
+// yhat is stored in a table as an fp16 pair (hi, lo) with 22 significant
+// bits, and the pair occupies two consecutive k slots, so one table word is
+// two operand halves as is: k = 2*element + {0: hi, 1: lo}.  The other
+// operand repeats each value in both slots, so the product sums
+// (hi + lo) * x.  The 16 columns are [hi part of the 8 query heads | lo
+// part of the 8 query heads]: q' = q * rg * s of a bf16 query has at most
+// 22 bits, and after a power-of-two scale that keeps it inside the fp16
+// range it is split exactly into a truncated fp16 high part and the fp16
+// remainder (likewise the probabilities).  Scores are assembled in fp64
+// from the two column halves, the fp64 chunk bias sum_d q_d c0_d and the
+// softmax scale, and only the small difference to the running maximum is
+// rounded before exp2, because with 100x outlier channels scores reach a
+// few hundred and the output is sensitive to one fp32 ulp of a score.
 //
-// Lane l of a wave: n = l % 16 (MFMA column / token / channel index), r = l /
-// 16 (MFMA k-group).  Keys are token-major, so lane (n, r) of K-tile t reads
-// the 16 bytes of channels 32r..32r+31 of token 16t + n; values are
-// channel-major with the chunk's tokens permuted so that lane (n, r) reads
-// the 4 bytes of word r of channel 16ct + n, which hold exactly the 8 tokens
-// whose probabilities lane (n, r) produced on the score side.
+// Lane l of a wave: n = l % 16 (MFMA row / column), r = l / 16 (k group).
+// Keys are token-major: lane (n, r) of K tile t reads the 16 bytes of
+// channels 32r .. 32r+31 of token 16t + n and feeds channels 32r + 4st + i
+// (i < 4) in step st.  Values are channel-major with the chunk's tokens
+// permuted so that word r of channel 16ct + n holds exactly the 8 tokens
+// whose probabilities lane (n, r) provides: tokens 4r..4r+3 (step 0) and
+// 16+4r..16+4r+3 (step 1).
+//
+// Work split: one workgroup of 8 waves (one per CU: the replicated table
+// fills 64 KiB of LDS) per (request, KV head, run of pages); each wave
+// streams a contiguous run of chunks with the next chunk's codes and scales
+// in flight while the current one is computed.  The block merges its waves
+// through LDS and writes the output itself when one run covers the request;
+// otherwise it writes a partial (base-2 max m, sum l, unnormalised o) and a
+// second, small kernel merges the runs exactly.
 #include <math.h>
 
 #include "lynx_internal.h"
@@ -36,15 +46,33 @@
 namespace lynx {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kLutCopies = 32;  // full table replicated per LDS bank
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kHeads = 8;  // MFMA columns per part
+
+// LDS map in bytes.  The table: 256 entries x 256-byte rows; the full code
+// table keeps 64 copies of its 4-byte word per row (lane l reads copy l),
+// the draft table 32 copies of its 8-byte pair (lane l reads copy l % 32),
+// so a wave's reads never collide in a bank.
+constexpr int kLutBytes = 256 * 256;
+// Per wave, two slots (current and next chunk) of the chunk constants:
+// c1k (scaled) f32[128] | c1v f32[128] | c0v f32[128] | c0k f64[128].
+constexpr int kSlotBytes = 3 * 512 + 1024;
+constexpr int kScaleOff = kLutBytes;
+// q as f64 [8 heads][130]: rows padded by 16 bytes so that the 16 lanes of
+// one LDS pass (8 heads x 2 halves) read 16 different bank groups
+constexpr int kQStride = kDim + 2;
+constexpr int kQOff = kScaleOff + kWaves * 2 * kSlotBytes;
+constexpr int kMlOff = kQOff + kHeads * kQStride * 8;       // per wave m, l of 8 heads
+constexpr int kLdsBytes = kMlOff + kWaves * 2 * kHeads * 4;
+static_assert(kWaves * 16 * kDim * 4 <= kLutBytes, "combine area must fit the table space");
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct MfmaTables {
-  uint32_t full[256];  // raw code byte (a << 4 | r) -> fp16 hi | fp16 lo << 16 of yhat
+  uint32_t full[256];  // code byte (a << 4 | r) -> fp16 hi | fp16 lo << 16 of yhat
   uint32_t draft[16];  // anchor nibble -> fp16 hi | fp16 lo << 16 of the draft yhat
 };
 
@@ -63,108 +91,459 @@ __device__ __forceinline__ Partials partials_of(void *ws, const AttnShape &s) {
   return pt;
 }
 
-// [a.lo16 | b.lo16 << 16] and [a.hi16 | b.hi16 << 16]
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+// ---- cross-lane helpers -----------------------------------------------------
+// value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8)
+__device__ __forceinline__ float ror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
 }
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+__device__ __forceinline__ double ror8(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x128, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), 0x128, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, static_cast<uint64_t>(static_cast<uint32_t>(lo)) |
+                                        (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32));
 }
-
-__device__ __forceinline__ half8 as_half8(const uint32_t (&u)[4]) {
-  half8 h;
-  __builtin_memcpy(&h, u, sizeof h);
-  return h;
+// op over lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16_swap / v_permlane32_swap
+// of a value with itself return the values of the two rows being paired)
+template <typename Op>
+__device__ __forceinline__ float xrows(float v, Op op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-
-// 8 codes (nibble i of the anchor / residual words = element i) -> the hi and
-// lo fp16 operand words of yhat for elements (2k, 2k+1) in word k.
-__device__ __forceinline__ void decode8_full(uint32_t a, uint32_t r, const uint32_t *lut,
-                                             uint32_t bank, uint32_t (&hi)[4],
-                                             uint32_t (&lo)[4]) {
-  const uint32_t even = ((a << 4) & 0xF0F0F0F0u) | (r & 0x0F0F0F0Fu);
-  const uint32_t odd = (a & 0xF0F0F0F0u) | ((r >> 4) & 0x0F0F0F0Fu);
+__device__ __forceinline__ double xrows_sum(double v) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t e = lut[(((even >> (8 * k)) & 0xFFu) << 5) | bank];
-    const uint32_t o = lut[(((odd >> (8 * k)) & 0xFFu) << 5) | bank];
-    hi[k] = lo_halves(e, o);
-    lo[k] = hi_halves(e, o);
+  for (int step = 0; step < 2; ++step) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+    const auto l = step == 0 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                             : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = step == 0 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                             : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    v = __builtin_bit_cast(double, static_cast<uint64_t>(l[0]) | (static_cast<uint64_t>(h[0]) << 32)) +
+        __builtin_bit_cast(double, static_cast<uint64_t>(l[1]) | (static_cast<uint64_t>(h[1]) << 32));
+  }
+  return v;
+}
+struct MaxOp { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct SumOp { __device__ float operator()(float a, float b) const { return a + b; } };
+
+// max over all 64 lanes
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, ror8(v));
+  return xrows(v, MaxOp());
+}
+
+// ---- operand construction ---------------------------------------------------
+// 8 nibble-pair codes of one anchor word a and residual word r (element k in
+// nibble k): byte j of e is the code byte (a << 4 | r) of element 2j, byte j
+// of o that of element 2j+1.
+__device__ __forceinline__ void code_bytes(uint32_t a, uint32_t r, uint32_t &e, uint32_t &o) {
+  e = ((a << 4) & 0xF0F0F0F0u) | (r & 0x0F0F0F0Fu);
+  o = (a & 0xF0F0F0F0u) | ((r >> 4) & 0x0F0F0F0Fu);
+}
+
+// LDS byte address of table row x.byte[j], copy selected by the lane bits
+// (byte 0 of lb): row * 256 + lane offset.
+template <int J>
+__device__ __forceinline__ uint32_t lut_addr(uint32_t x, uint32_t lb) {
+  return __builtin_amdgcn_perm(x, lb, 0x0C0C0000u | ((4u + J) << 8));
+}
+
+// Operand of elements 4s .. 4s+3 of a word (hi, lo of each in consecutive k slots).
+template <int S>
+__device__ __forceinline__ half8 operand_full(uint32_t e, uint32_t o, uint32_t lb, const char *lut) {
+  u32x4 w;
+  w[0] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S>(e, lb));
+  w[1] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S>(o, lb));
+  w[2] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S + 1>(e, lb));
+  w[3] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S + 1>(o, lb));
+  return __builtin_bit_cast(half8, w);
+}
+template <int S>
+__device__ __forceinline__ half8 operand_draft(uint32_t a, uint32_t lb, const char *lut) {
+  const uint2 p0 = *reinterpret_cast<const uint2 *>(lut + lut_addr<2 * S>(a, lb));
+  const uint2 p1 = *reinterpret_cast<const uint2 *>(lut + lut_addr<2 * S + 1>(a, lb));
+  u32x4 w;
+  w[0] = p0.x;
+  w[1] = p0.y;
+  w[2] = p1.x;
+  w[3] = p1.y;
+  return __builtin_bit_cast(half8, w);
+}
+
+// x split for a column half: the high half keeps fp16(trunc x) (the
+// truncation is the f32 bit pattern with the low 13 mantissa bits cleared),
+// the low half the remainder; both land in the two k slots of one element.
+__device__ __forceinline__ uint32_t split_dup(float x, uint32_t keep_mask) {
+  const float y = x - __uint_as_float(__float_as_uint(x) & keep_mask);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(y, y));
+}
+
+// ---- streamed chunk data ----------------------------------------------------
+struct Codes {
+  u32x4 ka[2], kr[2];  // K tile t: anchor / residual of channels 32r.. of token 16t + n
+  uint32_t va[8], vr[8];  // V: word r of channel 16ct + n
+};
+struct Scales {
+  float2 mnk, rgk, muk, sk, mnv, rgv, muv, sv;  // channels 2l, 2l+1
+};
+
+__device__ __forceinline__ u32x4 load_nt(const u32x4 *p) {
+  return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ uint32_t load_nt(const uint32_t *p) {
+  return __builtin_nontemporal_load(p);
+}
+
+template <bool kFull>
+__device__ __forceinline__ void load_codes(Codes &cd, const PlanesArg &kp, const PlanesArg &vp,
+                                           size_t tile, int c, int n, int r) {
+  const size_t krow = tile * kPage + c * kChunk + n;  // token row of tile 0
+  const u32x4 *ka = reinterpret_cast<const u32x4 *>(kp.anchor) + krow * 4 + r;
+  cd.ka[0] = load_nt(ka);
+  cd.ka[1] = load_nt(ka + 16 * 4);
+  if (kFull) {
+    const u32x4 *kr = reinterpret_cast<const u32x4 *>(kp.residual) + krow * 4 + r;
+    cd.kr[0] = load_nt(kr);
+    cd.kr[1] = load_nt(kr + 16 * 4);
+  }
+  const size_t vw = ((tile * kChunks + c) * kDim + n) * 4 + r;
+  const uint32_t *va = reinterpret_cast<const uint32_t *>(vp.anchor) + vw;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) cd.va[ct] = load_nt(va + ct * 64);
+  if (kFull) {
+    const uint32_t *vr = reinterpret_cast<const uint32_t *>(vp.residual) + vw;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) cd.vr[ct] = load_nt(vr + ct * 64);
   }
 }
 
-__device__ __forceinline__ void decode8_draft(uint32_t a, const uint2 *pairs, uint32_t (&hi)[4],
-                                              uint32_t (&lo)[4]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint2 v = pairs[(a >> (8 * k)) & 0xFFu];
-    hi[k] = v.x;
-    lo[k] = v.y;
-  }
+__device__ __forceinline__ void load_scales(Scales &sc, const PlanesArg &kp, const PlanesArg &vp,
+                                            size_t tile, int c, int lane) {
+  const size_t pidx = tile * (kDim / 2) + lane;
+  const size_t cidx = (tile * kChunks + c) * (kDim / 2) + lane;
+  sc.muk = reinterpret_cast<const float2 *>(kp.chunk_mean)[cidx];
+  sc.sk = reinterpret_cast<const float2 *>(kp.chunk_maxabs)[cidx];
+  sc.muv = reinterpret_cast<const float2 *>(vp.chunk_mean)[cidx];
+  sc.sv = reinterpret_cast<const float2 *>(vp.chunk_maxabs)[cidx];
+  sc.mnk = reinterpret_cast<const float2 *>(kp.page_min)[pidx];
+  sc.rgk = reinterpret_cast<const float2 *>(kp.page_range)[pidx];
+  sc.mnv = reinterpret_cast<const float2 *>(vp.page_min)[pidx];
+  sc.rgv = reinterpret_cast<const float2 *>(vp.page_range)[pidx];
 }
 
-// fp16 bits of the hi part of x (round to nearest even) or of the remainder x - hi.
-__device__ __forceinline__ uint32_t split_part(float x, bool want_lo) {
-  const _Float16 h = static_cast<_Float16>(x);
-  const float rem = x - static_cast<float>(h);
-  const _Float16 l = static_cast<_Float16>(rem);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, want_lo ? l : h));
+// Chunk constants into an LDS slot.  c1k is scaled by the power of two
+// 2^(14 - e), e = exponent of qmax * max c1k (qmax = largest |q| of the
+// group), so every |q * c1k| stays below 2^15; returns its exact inverse.
+__device__ __forceinline__ double scale_stage(const Scales &sc, char *slot, int lane, float qmax) {
+  const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // exact (7 + 7 bits)
+  const float bound = qmax * wave_max(fmaxf(c1a, c1b));
+  float ks = 1.0f;
+  double inv_ks = 1.0;
+  const uint32_t eb = (__float_as_uint(bound) >> 23) & 0xFFu;
+  if (eb != 0u && eb != 0xFFu) {
+    int ex = 127 + 14 + 127 - static_cast<int>(eb);  // biased exponent of 2^(14 - e)
+    ex = ex < 1 ? 1 : (ex > 254 ? 254 : ex);
+    ks = __uint_as_float(static_cast<uint32_t>(ex) << 23);
+    inv_ks = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + 127 - ex) << 52);
+  }
+  float *c1k = reinterpret_cast<float *>(slot);
+  float *c1v = c1k + kDim;
+  float *c0v = c1v + kDim;
+  double *c0k = reinterpret_cast<double *>(c0v + kDim);
+  reinterpret_cast<float2 *>(c1k)[lane] = make_float2(c1a * ks, c1b * ks);
+  reinterpret_cast<float2 *>(c1v)[lane] = make_float2(sc.rgv.x * sc.sv.x, sc.rgv.y * sc.sv.y);
+  reinterpret_cast<float2 *>(c0v)[lane] =
+      make_float2(__builtin_fmaf(sc.rgv.x, sc.muv.x, sc.mnv.x), __builtin_fmaf(sc.rgv.y, sc.muv.y, sc.mnv.y));
+  reinterpret_cast<double2 *>(c0k)[lane] =
+      make_double2(static_cast<double>(sc.mnk.x) + static_cast<double>(sc.rgk.x) * sc.muk.x,
+                   static_cast<double>(sc.mnk.y) + static_cast<double>(sc.rgk.y) * sc.muk.y);
+  return inv_ks;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Running state of one wave: per lane, head n & 7, column n of the value sum.
+struct RunState {
+  float m;          // running max of the base-2 scores
+  float l;          // running sum of exp2(score - m)
+  floatx4 acc[8];   // O^T rows 16ct + 4r + i, column n
+};
+
+struct LaneConst {
+  int n, r, lane;
+  bool lo;
+  uint32_t lb;         // lane bits of the table address
+  uint32_t keep_mask;  // 0 for the high column half, ~0x1FFF for the low one
+  double sm2;          // sm_scale * log2(e)
+};
+
+// One chunk: scores, online softmax (base 2), value sum.
+template <bool kFull>
+__device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot, double inv_ks,
+                                              const float (&qv)[32], const double *q64,
+                                              const LaneConst &lc, const char *lut,
+                                              RunState &st, float *srow) {
+  const int n = lc.n, r = lc.r;
+  const float *c1k = reinterpret_cast<const float *>(slot);
+  const float *c1v = c1k + kDim;
+  const float *c0v = c1v + kDim;
+  const double *c0k = reinterpret_cast<const double *>(c0v + kDim);
+
+  // ---- chunk bias sum_d q_d c0k_d in fp64: lane takes channels 32r + 16*lo .. +15 ----
+  double bias;
+  {
+    const int d0 = 32 * r + (lc.lo ? 16 : 0);
+    const double *qh = q64 + (n & 7) * kQStride + d0;
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; k += 2) {
+      const double2 qq = *reinterpret_cast<const double2 *>(qh + k);
+      const double2 cc = *reinterpret_cast<const double2 *>(c0k + d0 + k);
+      a0 = fma(qq.x, cc.x, a0);
+      a1 = fma(qq.y, cc.y, a1);
+    }
+    bias = a0 + a1;
+    bias += ror8(bias);
+    bias = xrows_sum(bias);
+  }
+
+  // ---- scores: S^T = Yk * Q' (tiles t = 0, 1 share each Q' step) ----
+  floatx4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  {
+    uint32_t e0[4], o0[4], e1[4], o1[4];
+    const uint32_t ka0[4] = {cd.ka[0][0], cd.ka[0][1], cd.ka[0][2], cd.ka[0][3]};
+    const uint32_t ka1[4] = {cd.ka[1][0], cd.ka[1][1], cd.ka[1][2], cd.ka[1][3]};
+    if (kFull) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        code_bytes(ka0[w], cd.kr[0][w], e0[w], o0[w]);
+        code_bytes(ka1[w], cd.kr[1][w], e1[w], o1[w]);
+      }
+    }
+#pragma unroll
+    for (int stp = 0; stp < 8; ++stp) {
+      const float4 c1 = *reinterpret_cast<const float4 *>(c1k + 32 * r + 4 * stp);
+      u32x4 bw;
+      bw[0] = split_dup(qv[4 * stp + 0] * c1.x, lc.keep_mask);
+      bw[1] = split_dup(qv[4 * stp + 1] * c1.y, lc.keep_mask);
+      bw[2] = split_dup(qv[4 * stp + 2] * c1.z, lc.keep_mask);
+      bw[3] = split_dup(qv[4 * stp + 3] * c1.w, lc.keep_mask);
+      const half8 b = __builtin_bit_cast(half8, bw);
+      half8 a0, a1;
+      const int w = stp >> 1;
+      if (kFull) {
+        if (stp & 1) {
+          a0 = operand_full<1>(e0[w], o0[w], lc.lb, lut);
+          a1 = operand_full<1>(e1[w], o1[w], lc.lb, lut);
+        } else {
+          a0 = operand_full<0>(e0[w], o0[w], lc.lb, lut);
+          a1 = operand_full<0>(e1[w], o1[w], lc.lb, lut);
+        }
+      } else {
+        if (stp & 1) {
+          a0 = operand_draft<1>(ka0[w], lc.lb, lut);
+          a1 = operand_draft<1>(ka1[w], lc.lb, lut);
+        } else {
+          a0 = operand_draft<0>(ka0[w], lc.lb, lut);
+          a1 = operand_draft<0>(ka1[w], lc.lb, lut);
+        }
+      }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b, s1, 0, 0, 0);
+    }
+  }
+
+  // ---- assemble: lanes n < 8 take tile 0, lanes n >= 8 tile 1 (tokens 16t + 4r + i) ----
+  const double scale2 = lc.sm2 * inv_ks;
+  const double bias2 = bias * lc.sm2;
+  double sc2[4];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float mine = lc.lo ? s1[i] : s0[i];
+    const float recv = ror8(lc.lo ? s0[i] : s1[i]);
+    sc2[i] = fma(static_cast<double>(mine) + static_cast<double>(recv), scale2, bias2);
+    cmax = fmaxf(cmax, static_cast<float>(sc2[i]));
+  }
+  cmax = fmaxf(cmax, ror8(cmax));
+  cmax = xrows(cmax, MaxOp());
+  const float m_new = fmaxf(st.m, cmax);
+  const float alpha = st.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+  float p[4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(static_cast<float>(sc2[i] - static_cast<double>(m_new)));
+    psum += p[i];
+  }
+  psum += ror8(psum);
+  psum = xrows(psum, SumOp());
+  const bool rescale = __builtin_amdgcn_ballot_w64(m_new != st.m) != 0;
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  if (srow != nullptr) {
+    // natural-log logits of tokens (16 * lo + 4r .. +3) of this chunk
+    constexpr double kLn2 = 0.69314718055994530942;
+    *reinterpret_cast<float4 *>(srow + (lc.lo ? 16 : 0) + 4 * r) =
+        make_float4(static_cast<float>(sc2[0] * kLn2), static_cast<float>(sc2[1] * kLn2),
+                    static_cast<float>(sc2[2] * kLn2), static_cast<float>(sc2[3] * kLn2));
+  }
+
+  // ---- P operands: step h holds tokens 16h + 4r + i of column n ----
+  half8 pa0, pa1;
+  {
+    u32x4 w0, w1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float other = ror8(p[i]);
+      const float t0 = lc.lo ? other : p[i];
+      const float t1 = lc.lo ? p[i] : other;
+      w0[i] = split_dup(t0, lc.keep_mask);
+      w1[i] = split_dup(t1, lc.keep_mask);
+    }
+    pa0 = __builtin_bit_cast(half8, w0);
+    pa1 = __builtin_bit_cast(half8, w1);
+  }
+
+  // ---- values: O^T += Yv^T * P, then the chunk's affine map ----
+  if (rescale) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alpha;
+  }
+  const float pc0 = lc.lo ? 0.0f : psum;  // the c0v term once per head (high half)
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    half8 y0, y1;
+    if (kFull) {
+      uint32_t e, o;
+      code_bytes(cd.va[ct], cd.vr[ct], e, o);
+      y0 = operand_full<0>(e, o, lc.lb, lut);
+      y1 = operand_full<1>(e, o, lc.lb, lut);
+    } else {
+      y0 = operand_draft<0>(cd.va[ct], lc.lb, lut);
+      y1 = operand_draft<1>(cd.va[ct], lc.lb, lut);
+    }
+    floatx4 ov = {0.0f, 0.0f, 0.0f, 0.0f};
+    ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pa0, ov, 0, 0, 0);
+    ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(y1, pa1, ov, 0, 0, 0);
+    const float4 a1 = *reinterpret_cast<const float4 *>(c1v + 16 * ct + 4 * r);
+    const float4 a0 = *reinterpret_cast<const float4 *>(c0v + 16 * ct + 4 * r);
+    st.acc[ct][0] = __builtin_fmaf(a1.x, ov[0], __builtin_fmaf(a0.x, pc0, st.acc[ct][0]));
+    st.acc[ct][1] = __builtin_fmaf(a1.y, ov[1], __builtin_fmaf(a0.y, pc0, st.acc[ct][1]));
+    st.acc[ct][2] = __builtin_fmaf(a1.z, ov[2], __builtin_fmaf(a0.z, pc0, st.acc[ct][2]));
+    st.acc[ct][3] = __builtin_fmaf(a1.w, ov[3], __builtin_fmaf(a0.w, pc0, st.acc[ct][3]));
+  }
 }
 
 template <bool kFull>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
     const uint16_t *__restrict__ q, PlanesArg kp, PlanesArg vp,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
-    AttnShape s, float sm_scale, float *__restrict__ scores, void *ws, MfmaTables tab) {
-  const int split = blockIdx.x % s.splits;
-  const int bh = blockIdx.x / s.splits;
+    AttnShape s, float sm_scale, float *__restrict__ out, float *__restrict__ scores, void *ws,
+    MfmaTables tab) {
+  __shared__ __align__(16) char smem[kLdsBytes];
+  char *lut = smem;
+  double *q64 = reinterpret_cast<double *>(smem + kQOff);
+  float *s_ml = reinterpret_cast<float *>(smem + kMlOff);
+
+  // blocks of one (request, KV head) are consecutive logical blocks; spread
+  // over the 8 XCDs in contiguous groups so that they share one L2
+  const unsigned nblk = gridDim.x;
+  unsigned lb_idx = blockIdx.x;
+  if ((nblk & 7u) == 0u) lb_idx = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int split = static_cast<int>(lb_idx % static_cast<unsigned>(s.splits));
+  const int bh = static_cast<int>(lb_idx / static_cast<unsigned>(s.splits));
   const int h = bh % s.heads;
   const int b = bh / s.heads;
   const int g = s.group;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
-  const int lane = tid & 63;
-  const int n = lane & 15;
-  const int r = lane >> 4;
-  const bool lo_col = n >= 8;
-  const int head = n & 7;
-  const uint32_t bank = static_cast<uint32_t>(lane & (kLutCopies - 1));
 
-  // LDS: yhat tables (the full table is replicated once per bank so that a
-  // wave's 32-lane halves never conflict), per-wave chunk scales, and the
-  // end-of-block combine area (which reuses the table space).
-  __shared__ __align__(16) uint32_t s_big[256 * kLutCopies];  // 32 KiB
-  __shared__ __align__(16) uint2 s_pairs[256];
-  __shared__ __align__(16) float s_sc[kWaves][3][kDim];      // c1k (scaled), c1v, c0v
-  __shared__ __align__(16) double s_c0k[kWaves][kDim];       // c0k = mn + rg * mu (exact)
-  __shared__ float s_ml[kWaves][2][8];
+  LaneConst lc;
+  lc.lane = tid & 63;
+  lc.n = lc.lane & 15;
+  lc.r = lc.lane >> 4;
+  lc.lo = lc.n >= 8;
+  lc.keep_mask = lc.lo ? 0xFFFFE000u : 0u;
+  lc.lb = kFull ? static_cast<uint32_t>(lc.lane * 4) : static_cast<uint32_t>((lc.lane & 31) * 8);
+  lc.sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
 
-  if (kFull) {
-    for (int i = tid; i < 256 * kLutCopies; i += kThreads) s_big[i] = tab.full[i >> 5];
-  } else {
-    const uint32_t lo = tab.draft[tid & 15], hi = tab.draft[tid >> 4];
-    s_pairs[tid] = make_uint2(lo_halves(lo, hi), hi_halves(lo, hi));
-  }
-
+  // ---- this wave's run of chunks ----
   int npages = s.max_pages;
   if (seq_lens) {
     npages = seq_lens[b] / kPage;
     npages = npages < 0 ? 0 : (npages > s.max_pages ? s.max_pages : npages);
   }
-  const int p0 = split * s.pages_per_split;
-  int p1 = p0 + s.pages_per_split;
+  const int pps = s.pages_per_split;
+  const int p0 = split * pps;
+  int p1 = p0 + pps;
   p1 = p1 > npages ? npages : p1;
+  int cb = p0 * kChunks + w * pps;
+  int ce = cb + pps;
+  if (ce > p1 * kChunks) ce = p1 * kChunks;
+  if (cb > ce) cb = ce;
 
-  // q (exact bf16 values) for this lane's head, channels 32r .. 32r+31;
-  // sm_scale is applied in fp64 when the score is assembled
+  char *slots = smem + kScaleOff + w * 2 * kSlotBytes;
+  // page of chunk ci, or -1 when the block table marks it absent
+  auto page_of = [&](int ci) -> long long {
+    const int lp = ci >> 3;
+    const long long pg = block_table ? block_table[static_cast<size_t>(b) * s.max_pages + lp]
+                                     : static_cast<long long>(b) * s.max_pages + lp;
+    return (pg < 0 || pg >= s.pool_pages) ? -1 : pg;
+  };
+
+  // the first chunk's codes and scales are requested before the set-up below
+  Codes ca, cbuf;
+  Scales sc;
+  long long pa = cb < ce ? page_of(cb) : -1;
+  if (pa >= 0) {
+    const size_t tile = static_cast<size_t>(pa) * s.heads + h;
+    load_scales(sc, kp, vp, tile, cb & 7, lc.lane);
+    load_codes<kFull>(ca, kp, vp, tile, cb & 7, lc.n, lc.r);
+  }
+
+  // ---- tables (replicated rows) and the query group as f64 ----
+  {
+    const int e = tid & 255;
+    u32x4 v;
+    if (kFull) {
+      const uint32_t x = tab.full[e];
+      v = u32x4{x, x, x, x};
+    } else {
+      const uint32_t x0 = tab.draft[e & 15], x1 = tab.draft[e >> 4];
+      v = u32x4{x0, x1, x0, x1};
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + e * 256 + (tid >> 8) * 128);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[k] = v;
+  }
+  const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
+  for (int e = tid; e < kHeads * kDim; e += kThreads) {
+    const int j = e / kDim, d = e % kDim;
+    q64[j * kQStride + d] =
+        j < g ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(qg[e]) << 16)) : 0.0;
+  }
+  // q of this lane's head, channels 32r .. 32r+31 (exact bf16 values)
   float qv[32];
   float qmax = 0.0f;
   {
-    const bool valid = head < g;
-    const uint16_t *qrow = q + (static_cast<size_t>(b) * s.q_heads + h * g + (valid ? head : 0)) * kDim + 32 * r;
+    const int j = lc.n & 7;
+    const bool valid = j < g;
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(qg + (valid ? j : 0) * kDim + 32 * lc.r);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint4 v = reinterpret_cast<const uint4 *>(qrow)[k];
+      const uint4 v = qrow[k];
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -174,260 +553,230 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 32; ++k) qmax = fmaxf(qmax, fabsf(qv[k]));
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+    qmax = wave_max(qmax);
   }
-  const double sm64 = static_cast<double>(sm_scale);
-
-  float m_run = -INFINITY, l_run = 0.0f;
-  floatx4 acc[8];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) acc[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
   __syncthreads();
 
   const size_t T = static_cast<size_t>(s.max_pages) * kPage;
-  const int c_begin = p0 * kChunks, c_end = p1 * kChunks;
-  float *sc = &s_sc[w][0][0];
-  for (int ci = c_begin + w; ci < c_end; ci += kWaves) {
-    const int lp = ci >> 3;
-    const int c = ci & 7;
-    const int pg = block_table ? block_table[static_cast<size_t>(b) * s.max_pages + lp]
-                               : b * s.max_pages + lp;
-    if (pg < 0 || pg >= s.pool_pages) continue;  // invalid entry: page skipped (wave-uniform)
-    const size_t tile = static_cast<size_t>(pg) * s.heads + h;
+  float *srow_base = nullptr;
+  if (scores != nullptr && (lc.n & 7) < g)
+    srow_base = scores + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + (lc.n & 7)) * T;
 
-    // ---- code loads (issued first) ----
-    const uint4 *kan = reinterpret_cast<const uint4 *>(kp.anchor);
-    const uint4 *kre = reinterpret_cast<const uint4 *>(kp.residual);
-    uint4 ka[2], kr[2];
+  RunState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const size_t idx = (tile * kPage + c * kChunk + 16 * t + n) * 4 + r;
-      ka[t] = kan[idx];
-      kr[t] = kFull ? kre[idx] : make_uint4(0, 0, 0, 0);
-    }
-    const uint32_t *van = reinterpret_cast<const uint32_t *>(vp.anchor);
-    const uint32_t *vre = reinterpret_cast<const uint32_t *>(vp.residual);
-    uint32_t va[8], vr[8];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const size_t idx = ((tile * kChunks + c) * kDim + 16 * ct + n) * 4 + r;
-      va[ct] = van[idx];
-      vr[ct] = kFull ? vre[idx] : 0u;
-    }
+  for (int ct = 0; ct < 8; ++ct) st.acc[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // ---- chunk affine constants: lane handles channels 2l, 2l+1 ----
-    // c1 = rg * s is exact (7 + 7 significant bits); it is scaled by a power
-    // of two chosen so that every q * c1 stays inside the fp16 range.
-    float kscale;
-    {
-      const size_t pidx = tile * (kDim / 2) + lane;
-      const size_t cidx = (tile * kChunks + c) * (kDim / 2) + lane;
-      const float2 mnk = reinterpret_cast<const float2 *>(kp.page_min)[pidx];
-      const float2 rgk = reinterpret_cast<const float2 *>(kp.page_range)[pidx];
-      const float2 muk = reinterpret_cast<const float2 *>(kp.chunk_mean)[cidx];
-      const float2 sk = reinterpret_cast<const float2 *>(kp.chunk_maxabs)[cidx];
-      const float2 mnv = reinterpret_cast<const float2 *>(vp.page_min)[pidx];
-      const float2 rgv = reinterpret_cast<const float2 *>(vp.page_range)[pidx];
-      const float2 muv = reinterpret_cast<const float2 *>(vp.chunk_mean)[cidx];
-      const float2 sv = reinterpret_cast<const float2 *>(vp.chunk_maxabs)[cidx];
-      const float c1a = rgk.x * sk.x, c1b = rgk.y * sk.y;
-      float cmax = fmaxf(c1a, c1b);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
-      // largest |q'| <= qmax * cmax; keep it below 2^15
-      const float bound = qmax * cmax;
-      kscale = 1.0f;
-      if (bound >= 16384.0f) {
-        const int e = static_cast<int>((__float_as_uint(bound) >> 23) & 0xFFu) - 127;  // >= 14
-        kscale = __uint_as_float(static_cast<uint32_t>(127 + 13 - e) << 23);
+  if (cb < ce) {
+    long long pb = -1;
+    double ks_cur = 1.0, ks_next = 1.0;
+    if (pa >= 0) ks_cur = scale_stage(sc, slots, lc.lane, qmax);
+    int slot = 0;
+    for (int ci = cb; ci < ce; ci += 2) {
+      // chunk ci (codes ca, constants in slot) while chunk ci + 1 streams in
+      const bool has1 = ci + 1 < ce;
+      if (has1) {
+        pb = page_of(ci + 1);
+        if (pb >= 0) {
+          const size_t tile = static_cast<size_t>(pb) * s.heads + h;
+          load_scales(sc, kp, vp, tile, (ci + 1) & 7, lc.lane);
+          load_codes<kFull>(cbuf, kp, vp, tile, (ci + 1) & 7, lc.n, lc.r);
+        }
       }
-      reinterpret_cast<float2 *>(sc + 0 * kDim)[lane] = make_float2(c1a * kscale, c1b * kscale);
-      reinterpret_cast<float2 *>(sc + 1 * kDim)[lane] = make_float2(rgv.x * sv.x, rgv.y * sv.y);
-      reinterpret_cast<float2 *>(sc + 2 * kDim)[lane] =
-          make_float2(__builtin_fmaf(rgv.x, muv.x, mnv.x), __builtin_fmaf(rgv.y, muv.y, mnv.y));
-      reinterpret_cast<double2 *>(&s_c0k[w][0])[lane] =
-          make_double2(static_cast<double>(mnk.x) + static_cast<double>(rgk.x) * muk.x,
-                       static_cast<double>(mnk.y) + static_cast<double>(rgk.y) * muk.y);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- Q' operand (exact halves: hi in columns 0..7, lo in 8..15) ----
-    half8 bq[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const float4 c1a = reinterpret_cast<const float4 *>(sc + 0 * kDim + 32 * r + 8 * st)[0];
-      const float4 c1b = reinterpret_cast<const float4 *>(sc + 0 * kDim + 32 * r + 8 * st)[1];
-      const float c1[8] = {c1a.x, c1a.y, c1a.z, c1a.w, c1b.x, c1b.y, c1b.z, c1b.w};
-      uint32_t u[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x0 = qv[8 * st + 2 * k] * c1[2 * k];
-        const float x1 = qv[8 * st + 2 * k + 1] * c1[2 * k + 1];
-        u[k] = split_part(x0, lo_col) | (split_part(x1, lo_col) << 16);
+      if (pa >= 0) {
+        wave_lds_sync();
+        compute_chunk<kFull>(ca, slots + slot * kSlotBytes, ks_cur, qv, q64, lc, lut, st,
+                             srow_base ? srow_base + static_cast<size_t>(ci) * kChunk : nullptr);
       }
-      bq[st] = as_half8(u);
-    }
-    // ---- chunk bias sum_d q_d c0_d in fp64 (lanes n and n+8 take 16 channels each) ----
-    double bias;
-    {
-      const double *c0 = &s_c0k[w][32 * r + (lo_col ? 16 : 0)];
-      double acc0 = 0.0, acc1 = 0.0;
-#pragma unroll
-      for (int k = 0; k < 16; k += 2) {
-        const double2 cc = reinterpret_cast<const double2 *>(c0)[k / 2];
-        const float qa = lo_col ? qv[16 + k] : qv[k];
-        const float qb = lo_col ? qv[17 + k] : qv[k + 1];
-        acc0 = fma(static_cast<double>(qa), cc.x, acc0);
-        acc1 = fma(static_cast<double>(qb), cc.y, acc1);
+      if (!has1) break;
+      slot ^= 1;
+      if (pb >= 0) ks_next = scale_stage(sc, slots + slot * kSlotBytes, lc.lane, qmax);
+      // chunk ci + 1 (codes cbuf) while chunk ci + 2 streams in
+      const bool has2 = ci + 2 < ce;
+      if (has2) {
+        pa = page_of(ci + 2);
+        if (pa >= 0) {
+          const size_t tile = static_cast<size_t>(pa) * s.heads + h;
+          load_scales(sc, kp, vp, tile, (ci + 2) & 7, lc.lane);
+          load_codes<kFull>(ca, kp, vp, tile, (ci + 2) & 7, lc.n, lc.r);
+        }
       }
-      bias = acc0 + acc1;
-      bias += __shfl_xor(bias, 8);
-      bias += __shfl_xor(bias, 16);
-      bias += __shfl_xor(bias, 32);
-    }
-
-    // ---- scores: S^T = Yk * Q' on MFMA (yhat hi and lo into separate accumulators) ----
-    floatx4 shi[2], slo[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      shi[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      slo[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      const uint32_t aw[4] = {ka[t].x, ka[t].y, ka[t].z, ka[t].w};
-      const uint32_t rw[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        uint32_t hi[4], lo[4];
-        if (kFull)
-          decode8_full(aw[st], rw[st], s_big, bank, hi, lo);
-        else
-          decode8_draft(aw[st], s_pairs, hi, lo);
-        shi[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(hi), bq[st], shi[t], 0, 0, 0);
-        slo[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(lo), bq[st], slo[t], 0, 0, 0);
+      if (pb >= 0) {
+        wave_lds_sync();
+        compute_chunk<kFull>(cbuf, slots + slot * kSlotBytes, ks_next, qv, q64, lc, lut, st,
+                             srow_base ? srow_base + static_cast<size_t>(ci + 1) * kChunk : nullptr);
       }
+      if (!has2) break;
+      slot ^= 1;
+      if (pa >= 0) ks_cur = scale_stage(sc, slots + slot * kSlotBytes, lc.lane, qmax);
     }
-    // Column n (< 8) holds yhat_hi * q'hi: the only large part.  Everything
-    // else is small; it is summed in fp32, the large part joins in fp64.
-    // tokens of this lane: 16t + 4r + i; every lane ends with its head's score.
-    const double inv_k = 1.0 / static_cast<double>(kscale);
-    const double scale64 = sm64 * inv_k;
-    double sfull[8];
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = shi[t][i], bb = slo[t][i];
-        const float a2 = __shfl_xor(a, 8), b2 = __shfl_xor(bb, 8);
-        const float big = lo_col ? a2 : a;
-        const float small = (lo_col ? a : a2) + bb + b2;
-        const double sc64 = (static_cast<double>(big) + static_cast<double>(small) + bias * kscale) * scale64;
-        sfull[4 * t + i] = sc64;
-        cmax = fmaxf(cmax, static_cast<float>(sc64));
-      }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = m_run == -INFINITY ? 0.0f : __expf(m_run - m_new);
-    float p[8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      p[k] = __expf(static_cast<float>(sfull[k] - static_cast<double>(m_new)));
-      psum += p[k];
-    }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (scores != nullptr && !lo_col && head < g) {
-      float *srow = scores + (static_cast<size_t>(b) * s.q_heads + h * g + head) * T +
-                    static_cast<size_t>(lp) * kPage + c * kChunk;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) srow[16 * t + 4 * r + i] = static_cast<float>(sfull[4 * t + i]);
-    }
-
-    // ---- P operand: this lane's 8 probabilities, hi or lo part by column ----
-    half8 pop;
-    {
-      uint32_t u[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        u[k] = split_part(p[2 * k], lo_col) | (split_part(p[2 * k + 1], lo_col) << 16);
-      pop = as_half8(u);
-    }
-
-    // ---- rescale the running output of columns 4r + i ----
-    float acol[4], pcol[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int src = (4 * r + i) & 7;  // lane holding that head's values (r = 0 row)
-      acol[i] = __shfl(alpha, src);
-      pcol[i] = r < 2 ? __shfl(psum, src) : 0.0f;  // c0v term once, on the hi rows
-    }
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[ct][i] *= acol[i];
-
-    // ---- values: O += P * Yv on MFMA, then the chunk's affine map ----
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      uint32_t hi[4], lo[4];
-      if (kFull)
-        decode8_full(va[ct], vr[ct], s_big, bank, hi, lo);
-      else
-        decode8_draft(va[ct], s_pairs, hi, lo);
-      floatx4 ov = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, as_half8(hi), ov, 0, 0, 0);
-      ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, as_half8(lo), ov, 0, 0, 0);
-      const float c1v = sc[1 * kDim + 16 * ct + n];
-      const float c0v = sc[2 * kDim + 16 * ct + n];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[ct][i] = __builtin_fmaf(c1v, ov[i], __builtin_fmaf(c0v, pcol[i], acc[ct][i]));
-    }
-    __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- combine the 4 waves of the block, write one (m, l, o) partial ----
-  __syncthreads();  // every wave is done with the tables: reuse them
-  float *s_o = reinterpret_cast<float *>(s_big);  // [wave][16 col][128 ch]
-  if (r == 0 && n < 8) {
-    s_ml[w][0][n] = m_run;
-    s_ml[w][1][n] = l_run;
+  // ---- merge the 8 waves of the block ----
+  __syncthreads();  // every wave is done with the table: reuse its space
+  float *s_o = reinterpret_cast<float *>(lut);  // [wave][16 col][128 ch]
+  if (lc.r == 0 && lc.n < 8) {
+    s_ml[(w * 2 + 0) * kHeads + lc.n] = st.m;
+    s_ml[(w * 2 + 1) * kHeads + lc.n] = st.l;
   }
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[(w * 16 + 4 * r + i) * kDim + 16 * ct + n] = acc[ct][i];
+    *reinterpret_cast<float4 *>(s_o + (w * 16 + lc.n) * kDim + 16 * ct + 4 * lc.r) =
+        make_float4(st.acc[ct][0], st.acc[ct][1], st.acc[ct][2], st.acc[ct][3]);
   __syncthreads();
-  Partials pt = partials_of(ws, s);
-  const size_t base = static_cast<size_t>(blockIdx.x) * g;
-  for (int e = tid; e < g * kDim; e += kThreads) {
-    const int j = e / kDim, d = e % kDim;
+
+  // thread -> (head j, channels 4c .. 4c+3); the high and low column halves
+  // of a head are summed here
+  if (tid < g * (kDim / 4)) {
+    const int j = tid >> 5, c = tid & 31;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_ml[ww][0][j]);
-    float L = 0.0f, O = 0.0f;
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_ml[(ww * 2) * kHeads + j]);
+    float L = 0.0f;
+    float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float mw = s_ml[ww][0][j];
-      if (mw == -INFINITY) continue;
-      const float f = __expf(mw - M);
-      L += f * s_ml[ww][1][j];
-      O += f * (s_o[(ww * 16 + j) * kDim + d] + s_o[(ww * 16 + 8 + j) * kDim + d]);
+      const float mw = s_ml[(ww * 2) * kHeads + j];
+      const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      L += f * s_ml[(ww * 2 + 1) * kHeads + j];
+      const float4 hi = reinterpret_cast<const float4 *>(s_o + (ww * 16 + j) * kDim)[c];
+      const float4 lo = reinterpret_cast<const float4 *>(s_o + (ww * 16 + 8 + j) * kDim)[c];
+      O.x += f * (hi.x + lo.x);
+      O.y += f * (hi.y + lo.y);
+      O.z += f * (hi.z + lo.z);
+      O.w += f * (hi.w + lo.w);
     }
-    pt.o[(base + j) * kDim + d] = O;
-    if (d == 0) {
-      pt.m[base + j] = static_cast<double>(M);
-      pt.l[base + j] = L;
+    if (s.splits == 1) {
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      reinterpret_cast<float4 *>(
+          out + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + j) * kDim)[c] =
+          make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
+    } else {
+      Partials pt = partials_of(ws, s);
+      const size_t row = static_cast<size_t>(lb_idx) * g + j;  // = (bh * splits + split) * g + j
+      reinterpret_cast<float4 *>(pt.o + row * kDim)[c] = O;
+      if (c == 0) {
+        pt.m[row] = static_cast<double>(M);
+        pt.l[row] = L;
+      }
     }
+  }
+}
+
+// Merge of the split partials (base-2 maxima) of one (request, KV head)
+// into the output.  Block = (request, KV head, 16 channels).  The global
+// loads of a thread are issued up front; the per-head maximum and sum over
+// the splits are wave reductions (32 lanes per head).
+constexpr int kCombThreads = 256;
+constexpr int kCombChannels = 16;
+constexpr int kCombMaxSplits = 256;  // attention_shape never makes more
+
+// op over the 32 lanes of each half of a wave
+template <typename Op>
+__device__ __forceinline__ float half_wave_reduce(float v, Op op) {
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+  v = op(v, ror8(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+
+__global__ __launch_bounds__(kCombThreads) void attn_mfma_combine_kernel(AttnShape s, const void *ws,
+                                                                         float *__restrict__ out) {
+  const int per_bh = kDim / kCombChannels;
+  const int bh = blockIdx.x / per_bh;
+  const int cq = blockIdx.x % per_bh;
+  const int b = bh / s.heads, h = bh % s.heads;
+  const int g = s.group;
+  const int ns = s.splits;
+  const int tid = threadIdx.x;
+  Partials pt = partials_of(const_cast<void *>(ws), s);
+  const size_t first = static_cast<size_t>(bh) * ns * g;  // rows of split 0
+  const int units = g * (kCombChannels / 4);               // (head, float4) columns
+  const int nsg = kCombThreads / units;                    // split groups
+  __shared__ float c_w[kCombMaxSplits * kHeads];           // [split][head] weights
+  __shared__ float c_L[kHeads];
+  __shared__ float4 c_o[kCombThreads];
+
+  // o rows of this thread's first 8 splits
+  const int col = tid % units, sg = tid / units;
+  const int j = col / (kCombChannels / 4);
+  const int c4 = cq * (kCombChannels / 4) + col % (kCombChannels / 4);
+  const bool active = sg < nsg;
+  float4 v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int sp = sg + u * nsg;
+    v[u] = active && sp < ns
+               ? reinterpret_cast<const float4 *>(pt.o + (first + static_cast<size_t>(sp) * g + j) * kDim)[c4]
+               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  // per head: 32 lanes over the splits
+  {
+    const int jh = tid >> 5, i = tid & 31;
+    const bool valid = jh < g;
+    float mloc[kCombMaxSplits / 32], lloc[kCombMaxSplits / 32];
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kCombMaxSplits / 32; ++k) {
+      const int sp = i + 32 * k;
+      const bool ok = valid && sp < ns;
+      mloc[k] = ok ? static_cast<float>(pt.m[first + static_cast<size_t>(sp) * g + jh]) : -INFINITY;
+      lloc[k] = ok ? pt.l[first + static_cast<size_t>(sp) * g + jh] : 0.0f;
+      M = fmaxf(M, mloc[k]);
+    }
+    M = half_wave_reduce(M, MaxOp());
+    float L = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCombMaxSplits / 32; ++k) {
+      const int sp = i + 32 * k;
+      const float wgt = mloc[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mloc[k] - M);
+      L += wgt * lloc[k];
+      if (valid && sp < ns) c_w[sp * kHeads + jh] = wgt;
+    }
+    L = half_wave_reduce(L, SumOp());
+    if (valid && i == 0) c_L[jh] = L;
+  }
+  __syncthreads();
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = sg + u * nsg;
+      const float wgt = sp < ns ? c_w[sp * kHeads + j] : 0.0f;
+      acc.x += wgt * v[u].x;
+      acc.y += wgt * v[u].y;
+      acc.z += wgt * v[u].z;
+      acc.w += wgt * v[u].w;
+    }
+    for (int sp = sg + 8 * nsg; sp < ns; sp += nsg) {
+      const float4 x = reinterpret_cast<const float4 *>(
+          pt.o + (first + static_cast<size_t>(sp) * g + j) * kDim)[c4];
+      const float wgt = c_w[sp * kHeads + j];
+      acc.x += wgt * x.x;
+      acc.y += wgt * x.y;
+      acc.z += wgt * x.z;
+      acc.w += wgt * x.w;
+    }
+  }
+  c_o[tid] = acc;
+  __syncthreads();
+  if (tid < units) {
+    float4 o = c_o[tid];
+    for (int k = 1; k < nsg; ++k) {
+      const float4 x = c_o[k * units + tid];
+      o.x += x.x;
+      o.y += x.y;
+      o.z += x.z;
+      o.w += x.w;
+    }
+    const float Lj = c_L[j];
+    const float inv = Lj > 0.0f ? 1.0f / Lj : 0.0f;
+    reinterpret_cast<float4 *>(
+        out + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + j) * kDim)[c4] =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   }
 }
 
@@ -452,20 +801,30 @@ MfmaTables build_mfma_tables() {
 
 }  // namespace
 
-bool attention_mfma_supported(int group) { return group >= 1 && group <= 8; }
+bool attention_mfma_supported(int group) { return group >= 1 && group <= kHeads; }
+
+int attention_mfma_target_blocks() { return 256; }
 
 hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
                                  const int32_t *block_table, const int32_t *seq_lens,
-                                 const AttnShape &s, float sm_scale, bool full, float *scores,
-                                 void *workspace, hipStream_t stream) {
+                                 const AttnShape &s, float sm_scale, bool full, float *out,
+                                 float *scores, void *workspace, hipStream_t stream) {
   static const MfmaTables tables = build_mfma_tables();
+  if (s.splits > kCombMaxSplits) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(static_cast<long long>(s.batch) * s.heads * s.splits));
   if (full)
     hipLaunchKernelGGL(attn_mfma_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v,
-                       block_table, seq_lens, s, sm_scale, scores, workspace, tables);
+                       block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
   else
     hipLaunchKernelGGL(attn_mfma_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v,
-                       block_table, seq_lens, s, sm_scale, scores, workspace, tables);
+                       block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
+  if (s.splits == 1) return hipGetLastError();  // the blocks wrote the output
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 cgrid(static_cast<unsigned>(static_cast<long long>(s.batch) * s.heads *
+                                         (kDim / kCombChannels)));
+  hipLaunchKernelGGL(attn_mfma_combine_kernel, cgrid, dim3(kCombThreads), 0, stream, s,
+                     static_cast<const void *>(workspace), out);
   return hipGetLastError();
 }
 

@@ -100,10 +100,12 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages);
 size_t attention_workspace_bytes(const AttnShape &s);
 
 bool attention_mfma_supported(int group);
+int attention_mfma_target_blocks();
+// Writes `out` itself (the split partials are merged inside the launch).
 hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
                                  const int32_t *block_table, const int32_t *seq_lens,
-                                 const AttnShape &s, float sm_scale, bool full, float *scores,
-                                 void *workspace, hipStream_t stream);
+                                 const AttnShape &s, float sm_scale, bool full, float *out,
+                                 float *scores, void *workspace, hipStream_t stream);
 
 hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
                             const PlanesArg &v, const int32_t *block_table,

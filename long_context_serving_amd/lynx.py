@@ -200,6 +200,13 @@ def workspace_size(batch: int, heads: int, q_heads: int, max_pages: int) -> int:
     return int(_lib.lynx_decode_attention_workspace_size(batch, heads, q_heads, HEAD_DIM, max_pages))
 
 
+def alloc_workspace(batch: int, heads: int, q_heads: int, max_pages: int,
+                    device="cuda") -> torch.Tensor:
+    """Decode-attention workspace of the size the library asks for."""
+    need = workspace_size(batch, heads, q_heads, max_pages)
+    return torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
+
+
 def decode_attention(q: torch.Tensor, k: Planes, v: Planes, max_pages: int, full: bool = True,
                      block_table: Optional[torch.Tensor] = None,
                      seq_lens: Optional[torch.Tensor] = None,
@@ -221,9 +228,8 @@ def decode_attention(q: torch.Tensor, k: Planes, v: Planes, max_pages: int, full
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    need = workspace_size(B, H, Hq, max_pages)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = alloc_workspace(B, H, Hq, max_pages, q.device)
     fn = _lib.lynx_decode_attention_full if full else _lib.lynx_decode_attention_anchor
     kc, vc = k.c(), v.c()
     _check(fn(_ptr(q), ctypes.byref(kc), ctypes.byref(vc), _ptr(block_table), _ptr(seq_lens),

@@ -83,8 +83,7 @@ class ProgressiveStream:
         self.pages, self.heads = k0.num_pages, k0.heads
         self.q_heads = self.layers[0].q.shape[1]
         self.sm_scale = sm_scale
-        ws = lynx.workspace_size(1, self.heads, self.q_heads, self.pages)
-        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+        self.ws = lynx.alloc_workspace(1, self.heads, self.q_heads, self.pages, self.device)
         shape = (1, self.q_heads, lynx.HEAD_DIM)
         self.out_draft = [torch.empty(shape, dtype=torch.float32, device=self.device) for _ in self.layers]
         self.out_full = [torch.empty(shape, dtype=torch.float32, device=self.device) for _ in self.layers]

@@ -356,8 +356,7 @@ def test_graph_replays_match_eager(lynx):
     pk = lynx.alloc_planes(w.pages, w.kv_heads, 0)
     pv = lynx.alloc_planes(w.pages, w.kv_heads, 1)
     po = lynx.alloc_planes(w.pages, w.kv_heads, 0)
-    ws = torch.empty(lynx.workspace_size(1, w.kv_heads, w.q_heads, w.pages), dtype=torch.uint8,
-                     device="cuda")
+    ws = lynx.alloc_workspace(1, w.kv_heads, w.q_heads, w.pages)
     oa = torch.empty((1, w.q_heads, 128), dtype=torch.float32, device="cuda")
     of = torch.empty_like(oa)
 
