@@ -41,6 +41,8 @@
 // second, small kernel merges the runs exactly.
 #include <math.h>
 
+#include <type_traits>
+
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -49,6 +51,7 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kHeads = 8;  // MFMA columns per part
+constexpr float kSlack = 8.0f;  // log2 of the largest probability before rescaling
 
 // LDS map in bytes.  The table: 256 entries x 256-byte rows; the full code
 // table keeps 64 copies of its 4-byte word per row (lane l reads copy l),
@@ -63,7 +66,11 @@ constexpr int kScaleOff = kLutBytes;
 // one LDS pass (8 heads x 2 halves) read 16 different bank groups
 constexpr int kQStride = kDim + 2;
 constexpr int kQOff = kScaleOff + kWaves * 2 * kSlotBytes;
-constexpr int kMlOff = kQOff + kHeads * kQStride * 8;       // per wave m, l of 8 heads
+// q as f32 [8 heads][132] for the Q' operand: rows 16 bytes apart modulo the
+// 256-byte bank cycle, so the 8 heads of one LDS pass never collide
+constexpr int kQ32Stride = kDim + 4;
+constexpr int kQ32Off = kQOff + kHeads * kQStride * 8;
+constexpr int kMlOff = kQ32Off + kHeads * kQ32Stride * 4;   // per wave m, l of 8 heads
 constexpr int kLdsBytes = kMlOff + kWaves * 2 * kHeads * 4;
 static_assert(kWaves * 16 * kDim * 4 <= kLutBytes, "combine area must fit the table space");
 
@@ -92,7 +99,17 @@ __device__ __forceinline__ Partials partials_of(void *ws, const AttnShape &s) {
 }
 
 // ---- cross-lane helpers -----------------------------------------------------
-// value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8)
+// value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8);
+// the masked forms write only lanes n >= 8 (banks 2, 3 of each row) or only
+// lanes n < 8 (banks 0, 1) and leave `keep` in the others
+__device__ __forceinline__ float ror8_to_hi(float keep, float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, keep), __builtin_bit_cast(int, x), 0x128, 0xF, 0xC, false));
+}
+__device__ __forceinline__ float ror8_to_lo(float keep, float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, keep), __builtin_bit_cast(int, x), 0x128, 0xF, 0x3, false));
+}
 __device__ __forceinline__ float ror8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
       0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
@@ -201,41 +218,45 @@ __device__ __forceinline__ uint32_t load_nt(const uint32_t *p) {
   return __builtin_nontemporal_load(p);
 }
 
+// The tile and chunk are wave-uniform: the chunk's base address is scalar
+// and each lane adds a 32-bit offset (kept in one VGPR).
 template <bool kFull>
 __device__ __forceinline__ void load_codes(Codes &cd, const PlanesArg &kp, const PlanesArg &vp,
-                                           size_t tile, int c, int n, int r) {
-  const size_t krow = tile * kPage + c * kChunk + n;  // token row of tile 0
-  const u32x4 *ka = reinterpret_cast<const u32x4 *>(kp.anchor) + krow * 4 + r;
-  cd.ka[0] = load_nt(ka);
-  cd.ka[1] = load_nt(ka + 16 * 4);
+                                           size_t tile, int c, uint32_t koff, uint32_t voff) {
+  const size_t cbytes = tile * kPlaneTileBytes + static_cast<size_t>(c) * (kChunk * kDim / 2);
+  const char *ka = reinterpret_cast<const char *>(kp.anchor) + cbytes;
+  cd.ka[0] = load_nt(reinterpret_cast<const u32x4 *>(ka + koff));
+  cd.ka[1] = load_nt(reinterpret_cast<const u32x4 *>(ka + koff + 1024));
   if (kFull) {
-    const u32x4 *kr = reinterpret_cast<const u32x4 *>(kp.residual) + krow * 4 + r;
-    cd.kr[0] = load_nt(kr);
-    cd.kr[1] = load_nt(kr + 16 * 4);
+    const char *kr = reinterpret_cast<const char *>(kp.residual) + cbytes;
+    cd.kr[0] = load_nt(reinterpret_cast<const u32x4 *>(kr + koff));
+    cd.kr[1] = load_nt(reinterpret_cast<const u32x4 *>(kr + koff + 1024));
   }
-  const size_t vw = ((tile * kChunks + c) * kDim + n) * 4 + r;
-  const uint32_t *va = reinterpret_cast<const uint32_t *>(vp.anchor) + vw;
+  const char *va = reinterpret_cast<const char *>(vp.anchor) + cbytes;
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) cd.va[ct] = load_nt(va + ct * 64);
+  for (int ct = 0; ct < 8; ++ct) cd.va[ct] = load_nt(reinterpret_cast<const uint32_t *>(va + voff + ct * 256));
   if (kFull) {
-    const uint32_t *vr = reinterpret_cast<const uint32_t *>(vp.residual) + vw;
+    const char *vr = reinterpret_cast<const char *>(vp.residual) + cbytes;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) cd.vr[ct] = load_nt(vr + ct * 64);
+    for (int ct = 0; ct < 8; ++ct) cd.vr[ct] = load_nt(reinterpret_cast<const uint32_t *>(vr + voff + ct * 256));
   }
 }
 
 __device__ __forceinline__ void load_scales(Scales &sc, const PlanesArg &kp, const PlanesArg &vp,
-                                            size_t tile, int c, int lane) {
-  const size_t pidx = tile * (kDim / 2) + lane;
-  const size_t cidx = (tile * kChunks + c) * (kDim / 2) + lane;
-  sc.muk = reinterpret_cast<const float2 *>(kp.chunk_mean)[cidx];
-  sc.sk = reinterpret_cast<const float2 *>(kp.chunk_maxabs)[cidx];
-  sc.muv = reinterpret_cast<const float2 *>(vp.chunk_mean)[cidx];
-  sc.sv = reinterpret_cast<const float2 *>(vp.chunk_maxabs)[cidx];
-  sc.mnk = reinterpret_cast<const float2 *>(kp.page_min)[pidx];
-  sc.rgk = reinterpret_cast<const float2 *>(kp.page_range)[pidx];
-  sc.mnv = reinterpret_cast<const float2 *>(vp.page_min)[pidx];
-  sc.rgv = reinterpret_cast<const float2 *>(vp.page_range)[pidx];
+                                            size_t tile, int c, uint32_t soff) {
+  const size_t pb = tile * kDim * 4;
+  const size_t cb = (tile * kChunks + c) * kDim * 4;
+  auto f2 = [soff](const float *base, size_t off) {
+    return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(base) + off + soff);
+  };
+  sc.muk = f2(kp.chunk_mean, cb);
+  sc.sk = f2(kp.chunk_maxabs, cb);
+  sc.muv = f2(vp.chunk_mean, cb);
+  sc.sv = f2(vp.chunk_maxabs, cb);
+  sc.mnk = f2(kp.page_min, pb);
+  sc.rgk = f2(kp.page_range, pb);
+  sc.mnv = f2(vp.page_min, pb);
+  sc.rgv = f2(vp.page_range, pb);
 }
 
 // Chunk constants into an LDS slot.  c1k is scaled by the power of two
@@ -282,6 +303,7 @@ struct RunState {
 
 struct LaneConst {
   int n, r, lane;
+  uint32_t koff, voff, soff;  // lane byte offsets in a K chunk, a V chunk, a scale row
   bool lo;
   uint32_t lb;         // lane bits of the table address
   uint32_t keep_mask;  // 0 for the high column half, ~0x1FFF for the low one
@@ -291,7 +313,7 @@ struct LaneConst {
 // One chunk: scores, online softmax (base 2), value sum.
 template <bool kFull>
 __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot, double inv_ks,
-                                              const float (&qv)[32], const double *q64,
+                                              const float *q32, const double *q64,
                                               const LaneConst &lc, const char *lut,
                                               RunState &st, float *srow) {
   const int n = lc.n, r = lc.r;
@@ -331,14 +353,16 @@ __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot,
         code_bytes(ka1[w], cd.kr[1][w], e1[w], o1[w]);
       }
     }
+    const float *qrow = q32 + (n & 7) * kQ32Stride + 32 * r;
 #pragma unroll
     for (int stp = 0; stp < 8; ++stp) {
       const float4 c1 = *reinterpret_cast<const float4 *>(c1k + 32 * r + 4 * stp);
+      const float4 qq = *reinterpret_cast<const float4 *>(qrow + 4 * stp);
       u32x4 bw;
-      bw[0] = split_dup(qv[4 * stp + 0] * c1.x, lc.keep_mask);
-      bw[1] = split_dup(qv[4 * stp + 1] * c1.y, lc.keep_mask);
-      bw[2] = split_dup(qv[4 * stp + 2] * c1.z, lc.keep_mask);
-      bw[3] = split_dup(qv[4 * stp + 3] * c1.w, lc.keep_mask);
+      bw[0] = split_dup(qq.x * c1.x, lc.keep_mask);
+      bw[1] = split_dup(qq.y * c1.y, lc.keep_mask);
+      bw[2] = split_dup(qq.z * c1.z, lc.keep_mask);
+      bw[3] = split_dup(qq.w * c1.w, lc.keep_mask);
       const half8 b = __builtin_bit_cast(half8, bw);
       half8 a0, a1;
       const int w = stp >> 1;
@@ -371,27 +395,35 @@ __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot,
   float cmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float mine = lc.lo ? s1[i] : s0[i];
-    const float recv = ror8(lc.lo ? s0[i] : s1[i]);
-    sc2[i] = fma(static_cast<double>(mine) + static_cast<double>(recv), scale2, bias2);
+    // high part: own tile 0 (n < 8) or lane n - 8's tile 1; low part: lane
+    // n + 8's tile 0 (n < 8) or own tile 1
+    const float big = ror8_to_hi(s0[i], s1[i]);
+    const float small = ror8_to_lo(s1[i], s0[i]);
+    sc2[i] = fma(static_cast<double>(big) + static_cast<double>(small), scale2, bias2);
     cmax = fmaxf(cmax, static_cast<float>(sc2[i]));
   }
   cmax = fmaxf(cmax, ror8(cmax));
   cmax = xrows(cmax, MaxOp());
-  const float m_new = fmaxf(st.m, cmax);
-  const float alpha = st.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+  // The reference maximum moves only when a score exceeds it by more than
+  // 2^8 (base 2), so probabilities stay below 256 and most chunks need no
+  // rescaling of the running sums.
+  const bool rescale = __builtin_amdgcn_ballot_w64(cmax > st.m + kSlack) != 0;
+  float alpha = 1.0f;
+  if (rescale) {
+    const float m_new = fmaxf(st.m, cmax);
+    alpha = st.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+  }
   float p[4];
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(static_cast<float>(sc2[i] - static_cast<double>(m_new)));
+    p[i] = __builtin_amdgcn_exp2f(static_cast<float>(sc2[i] - static_cast<double>(st.m)));
     psum += p[i];
   }
   psum += ror8(psum);
   psum = xrows(psum, SumOp());
-  const bool rescale = __builtin_amdgcn_ballot_w64(m_new != st.m) != 0;
   st.l = st.l * alpha + psum;
-  st.m = m_new;
   if (srow != nullptr) {
     // natural-log logits of tokens (16 * lo + 4r .. +3) of this chunk
     constexpr double kLn2 = 0.69314718055994530942;
@@ -406,9 +438,8 @@ __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot,
     u32x4 w0, w1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float other = ror8(p[i]);
-      const float t0 = lc.lo ? other : p[i];
-      const float t1 = lc.lo ? p[i] : other;
+      const float t0 = ror8_to_hi(p[i], p[i]);  // tile 0: own (n < 8) or from n - 8
+      const float t1 = ror8_to_lo(p[i], p[i]);  // tile 1: from n + 8 (n < 8) or own
       w0[i] = split_dup(t0, lc.keep_mask);
       w1[i] = split_dup(t1, lc.keep_mask);
     }
@@ -455,6 +486,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   __shared__ __align__(16) char smem[kLdsBytes];
   char *lut = smem;
   double *q64 = reinterpret_cast<double *>(smem + kQOff);
+  float *q32 = reinterpret_cast<float *>(smem + kQ32Off);
   float *s_ml = reinterpret_cast<float *>(smem + kMlOff);
 
   // blocks of one (request, KV head) are consecutive logical blocks; spread
@@ -468,21 +500,31 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   const int b = bh / s.heads;
   const int g = s.group;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
 
   LaneConst lc;
   lc.lane = tid & 63;
   lc.n = lc.lane & 15;
   lc.r = lc.lane >> 4;
   lc.lo = lc.n >= 8;
+  lc.koff = static_cast<uint32_t>(lc.n * 64 + lc.r * 16);
+  lc.voff = static_cast<uint32_t>(lc.n * 16 + lc.r * 4);
+  lc.soff = static_cast<uint32_t>(lc.lane * 8);
   lc.keep_mask = lc.lo ? 0xFFFFE000u : 0u;
   lc.lb = kFull ? static_cast<uint32_t>(lc.lane * 4) : static_cast<uint32_t>((lc.lane & 31) * 8);
   lc.sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
 
   // ---- this wave's run of chunks ----
+  // request metadata is read-only for the launch: read it through the
+  // constant address space so the wave-uniform reads become scalar loads
+  // (counted apart from the streaming vector loads)
+  const __attribute__((address_space(4))) int32_t *bt_c =
+      (const __attribute__((address_space(4))) int32_t *)block_table;
+  const __attribute__((address_space(4))) int32_t *sl_c =
+      (const __attribute__((address_space(4))) int32_t *)seq_lens;
   int npages = s.max_pages;
   if (seq_lens) {
-    npages = seq_lens[b] / kPage;
+    npages = sl_c[b] / kPage;
     npages = npages < 0 ? 0 : (npages > s.max_pages ? s.max_pages : npages);
   }
   const int pps = s.pages_per_split;
@@ -498,20 +540,41 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   // page of chunk ci, or -1 when the block table marks it absent
   auto page_of = [&](int ci) -> long long {
     const int lp = ci >> 3;
-    const long long pg = block_table ? block_table[static_cast<size_t>(b) * s.max_pages + lp]
+    const long long pg = block_table ? bt_c[static_cast<size_t>(b) * s.max_pages + lp]
                                      : static_cast<long long>(b) * s.max_pages + lp;
     return (pg < 0 || pg >= s.pool_pages) ? -1 : pg;
   };
 
-  // the first chunk's codes and scales are requested before the set-up below
-  Codes ca, cbuf;
+  // Codes of NB chunks are held per wave: the chunk being computed and the
+  // next NB - 1 in flight (the draft's chunks are smaller, so it looks
+  // further ahead).  Scales of the next chunk are requested one chunk ahead
+  // and before the codes, so waiting for them never waits for those codes.
+  // Every step issues its loads unconditionally -- a chunk past the run or
+  // on an absent page reads chunk 0 of pool page 0 instead, and is not
+  // computed -- so the wait counts the compiler derives are exact and never
+  // wait for loads that are still ahead in the pipeline.
+  constexpr int NB = kFull ? 2 : 3;
+  constexpr int D = NB - 1;
+  if (s.pool_pages <= 0) cb = ce;  // no page can be read
+  Codes cds[NB];
+  long long pgs[NB];
   Scales sc;
-  long long pa = cb < ce ? page_of(cb) : -1;
-  if (pa >= 0) {
-    const size_t tile = static_cast<size_t>(pa) * s.heads + h;
-    load_scales(sc, kp, vp, tile, cb & 7, lc.lane);
-    load_codes<kFull>(ca, kp, vp, tile, cb & 7, lc.n, lc.r);
+  auto tile_of = [&](long long pg) { return pg >= 0 ? static_cast<size_t>(pg) * s.heads + h : 0; };
+  auto chunk_of = [&](long long pg, int c) { return pg >= 0 ? (c & 7) : 0; };
+  auto page_in_run = [&](int c) -> long long { return c < ce ? page_of(c) : -1; };
+  // The first chunks' codes and scales are requested before the set-up
+  // below, in the order a steady-state step leaves them (codes of chunk cb,
+  // its scales, then the codes of the next D - 1 chunks), so that the wait
+  // counts derived for the loop hold on entry as well.
+  if (cb < ce) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      pgs[d] = page_in_run(cb + d);
+      load_codes<kFull>(cds[d], kp, vp, tile_of(pgs[d]), chunk_of(pgs[d], cb + d), lc.koff, lc.voff);
+      if (d == 0) load_scales(sc, kp, vp, tile_of(pgs[0]), chunk_of(pgs[0], cb), lc.soff);
+    }
   }
+  pgs[NB - 1] = -1;
 
   // ---- tables (replicated rows) and the query group as f64 ----
   {
@@ -531,8 +594,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
   for (int e = tid; e < kHeads * kDim; e += kThreads) {
     const int j = e / kDim, d = e % kDim;
-    q64[j * kQStride + d] =
-        j < g ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(qg[e]) << 16)) : 0.0;
+    const float qf = j < g ? __uint_as_float(static_cast<uint32_t>(qg[e]) << 16) : 0.0f;
+    q64[j * kQStride + d] = static_cast<double>(qf);
+    q32[j * kQ32Stride + d] = qf;
   }
   // q of this lane's head, channels 32r .. 32r+31 (exact bf16 values)
   float qv[32];
@@ -569,47 +633,32 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   for (int ct = 0; ct < 8; ++ct) st.acc[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (cb < ce) {
-    long long pb = -1;
-    double ks_cur = 1.0, ks_next = 1.0;
-    if (pa >= 0) ks_cur = scale_stage(sc, slots, lc.lane, qmax);
-    int slot = 0;
-    for (int ci = cb; ci < ce; ci += 2) {
-      // chunk ci (codes ca, constants in slot) while chunk ci + 1 streams in
-      const bool has1 = ci + 1 < ce;
-      if (has1) {
-        pb = page_of(ci + 1);
-        if (pb >= 0) {
-          const size_t tile = static_cast<size_t>(pb) * s.heads + h;
-          load_scales(sc, kp, vp, tile, (ci + 1) & 7, lc.lane);
-          load_codes<kFull>(cbuf, kp, vp, tile, (ci + 1) & 7, lc.n, lc.r);
-        }
-      }
-      if (pa >= 0) {
+    double ks0 = 1.0, ks1 = 1.0;  // inverse Q' scales of LDS slots 0 and 1
+    ks0 = scale_stage(sc, slots, lc.lane, qmax);
+    // one chunk c held in code buffer J = (c - cb) % NB, constants in LDS slot (c - cb) & 1
+    auto step = [&](auto jc, int c) {
+      constexpr int J = decltype(jc)::value;
+      constexpr int J1 = (J + 1) % NB, JD = (J + D) % NB;
+      const int slot = (c - cb) & 1;
+      pgs[JD] = page_in_run(c + D);
+      load_scales(sc, kp, vp, tile_of(pgs[J1]), chunk_of(pgs[J1], c + 1), lc.soff);
+      load_codes<kFull>(cds[JD], kp, vp, tile_of(pgs[JD]), chunk_of(pgs[JD], c + D), lc.koff, lc.voff);
+      if (pgs[J] >= 0) {
         wave_lds_sync();
-        compute_chunk<kFull>(ca, slots + slot * kSlotBytes, ks_cur, qv, q64, lc, lut, st,
-                             srow_base ? srow_base + static_cast<size_t>(ci) * kChunk : nullptr);
+        compute_chunk<kFull>(cds[J], slots + slot * kSlotBytes, slot ? ks1 : ks0, q32, q64, lc, lut,
+                             st, srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
       }
-      if (!has1) break;
-      slot ^= 1;
-      if (pb >= 0) ks_next = scale_stage(sc, slots + slot * kSlotBytes, lc.lane, qmax);
-      // chunk ci + 1 (codes cbuf) while chunk ci + 2 streams in
-      const bool has2 = ci + 2 < ce;
-      if (has2) {
-        pa = page_of(ci + 2);
-        if (pa >= 0) {
-          const size_t tile = static_cast<size_t>(pa) * s.heads + h;
-          load_scales(sc, kp, vp, tile, (ci + 2) & 7, lc.lane);
-          load_codes<kFull>(ca, kp, vp, tile, (ci + 2) & 7, lc.n, lc.r);
-        }
+      const double k = scale_stage(sc, slots + (slot ^ 1) * kSlotBytes, lc.lane, qmax);
+      if (slot) ks0 = k; else ks1 = k;
+    };
+    for (int c = cb; c < ce; c += NB) {
+      step(std::integral_constant<int, 0>(), c);
+      if (c + 1 >= ce) break;
+      step(std::integral_constant<int, 1 % NB>(), c + 1);
+      if (NB > 2) {
+        if (c + 2 >= ce) break;
+        step(std::integral_constant<int, 2 % NB>(), c + 2);
       }
-      if (pb >= 0) {
-        wave_lds_sync();
-        compute_chunk<kFull>(cbuf, slots + slot * kSlotBytes, ks_next, qv, q64, lc, lut, st,
-                             srow_base ? srow_base + static_cast<size_t>(ci + 1) * kChunk : nullptr);
-      }
-      if (!has2) break;
-      slot ^= 1;
-      if (pa >= 0) ks_cur = scale_stage(sc, slots + slot * kSlotBytes, lc.lane, qmax);
     }
   }
 
