@@ -5,12 +5,12 @@ One step = encode of the whole K and V cache of the workload (page/chunk
 statistics, alpha-law codes, anchor/residual planes), then anchor-only and
 full fused-dequant single-query decode attention.  Inputs are seeded
 synthetic Laplacian KV with outlier channels (long_context_serving_amd/synth.py),
-resident in HBM before timing starts.  Each step is one captured HIP graph;
-per-kernel timings come from graphs of back-to-back launches of one call.
-To keep the 256 MB Infinity Cache from serving the data, every step works
-on one of several distinct buffer sets
-(>= 1.5 GB in total): step i encodes set i % S and runs attention over the
-planes of set (i + S/2) % S, which were encoded S/2 steps earlier.
+resident in HBM before timing starts.  A step encodes K and V of one buffer
+set and runs anchor-only and full decode over it.  To keep the 256 MB
+Infinity Cache from serving the data, S distinct buffer sets (>= 1.5 GB in
+total) are used; steps run in rounds of S, each phase of a round one HIP
+graph of back-to-back launches, with events on the launch stream between
+the phases giving every kernel's time inside the timed region.
 
 Prints ONE JSON line.  Throughput counts algorithmic bytes: encode
 3.28125 B per K/V element (2 read, 0.5 + 0.5 + 0.03125 + 0.25 written),
@@ -236,8 +236,8 @@ def progressive_main(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200, help="timed steps (rounded up to a multiple of --sets)")
+    ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="ctx32k")
     ap.add_argument("--sets", type=int, default=8, help="distinct buffer sets cycled per step")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
@@ -295,75 +295,65 @@ def main():
     q = to_dev(qb)
     out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
     ws = lynx.alloc_workspace(w.batch, w.kv_heads, w.q_heads, w.pages, dev)
-    # One HIP graph per step (four phases).  The timed loop replays K of
-    # them; per-kernel averages come from graphs that hold the same call on
-    # every buffer set back to back, timed with events on the replay stream.
-    def phase_calls(i):
-        e = sets[i % S]
-        a = sets[(i + S // 2) % S]
-        return [
-            lambda: lynx.quantize_pages(e["k"], lynx.ROLE_KEY, out=e["pk"]),
-            lambda: lynx.quantize_pages(e["v"], lynx.ROLE_VALUE, out=e["pv"]),
-            lambda: lynx.decode_attention(q, a["pk"], a["pv"], w.pages, full=False, sm_scale=sm,
-                                          out=out, workspace=ws),
-            lambda: lynx.decode_attention(q, a["pk"], a["pv"], w.pages, full=True, sm_scale=sm,
-                                          out=out, workspace=ws),
-        ]
-
-    # eager pass: every set encoded before its planes are read
-    for i in range(S):
-        for call in phase_calls(i):
-            call()
+    # A step is one pass of the hot path over one buffer set: encode K and V,
+    # anchor-only decode, full decode.  The timed loop runs the steps in
+    # rounds of S: one HIP graph encodes all S sets back to back, a second
+    # runs the anchor decode of all S sets, a third the full decode.  Events
+    # recorded on the launch stream between the three graphs give each
+    # kernel's average time inside the timed region (the graph boundaries
+    # are shared by 2S or S back-to-back launches).  Set j is decoded after
+    # the other sets were encoded, so its planes are no longer cached.
+    enc_calls = []
+    anc_calls = []
+    full_calls = []
+    for j in range(S):
+        e = sets[j]
+        enc_calls.append(lambda e=e: lynx.quantize_pages(e["k"], lynx.ROLE_KEY, out=e["pk"]))
+        enc_calls.append(lambda e=e: lynx.quantize_pages(e["v"], lynx.ROLE_VALUE, out=e["pv"]))
+        anc_calls.append(lambda e=e: lynx.decode_attention(q, e["pk"], e["pv"], w.pages, full=False,
+                                                           sm_scale=sm, out=out, workspace=ws))
+        full_calls.append(lambda e=e: lynx.decode_attention(q, e["pk"], e["pv"], w.pages, full=True,
+                                                            sm_scale=sm, out=out, workspace=ws))
+    for call in enc_calls + anc_calls + full_calls:  # eager pass
+        call()
     torch.cuda.synchronize()
-    cap = torch.cuda.Stream()
+    stream = torch.cuda.Stream()
 
     def capture(calls):
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
+        with torch.cuda.graph(g, stream=stream):
             for call in calls:
                 call()
         return g
 
-    step_graphs = [capture(phase_calls(i)) for i in range(S)]
-    # per-kernel graphs: encode (K and V of every set), anchor, full
-    kernel_graphs = {
-        "encode": (capture([c for i in range(S) for c in phase_calls(i)[:2]]), 2 * S),
-        "decode_anchor": (capture([phase_calls(i)[2] for i in range(S)]), S),
-        "decode_full": (capture([phase_calls(i)[3] for i in range(S)]), S),
-    }
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-
-    for i in range(args.warmup):
-        step_graphs[i % S].replay()
+    phases = [capture(enc_calls), capture(anc_calls), capture(full_calls)]
     torch.cuda.synchronize()
 
-    K = args.steps
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    def run_rounds(n, events=None):
+        with torch.cuda.stream(stream):
+            for r in range(n):
+                for p, g in enumerate(phases):
+                    if events is not None:
+                        events[r][p].record(stream)
+                    g.replay()
+                if events is not None:
+                    events[r][3].record(stream)
+
+    run_rounds(max(1, -(-args.warmup // S)))
+    torch.cuda.synchronize()
+
+    rounds = max(1, -(-args.steps // S))
+    K = rounds * S
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(rounds)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    ev0.record(stream)
-    for i in range(K):
-        step_graphs[i % S].replay()
-    ev1.record(stream)
+    run_rounds(rounds, evs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    step_ms = ev0.elapsed_time(ev1) / K
-
-    reps = max(2, K // S)
-    per_call_ms = {}
-    for name, (g, calls) in kernel_graphs.items():
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        per_call_ms[name] = t0.elapsed_time(t1) / (reps * calls)
+    step_ms = evs[0][0].elapsed_time(evs[rounds - 1][3]) / K
+    phase_ms = [sum(evs[r][p].elapsed_time(evs[r][p + 1]) for r in range(rounds)) for p in range(3)]
+    per_call_ms = {"encode": phase_ms[0] / (2 * K), "decode_anchor": phase_ms[1] / K,
+                   "decode_full": phase_ms[2] / K}
 
     if args.copy_probe:
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -406,6 +396,7 @@ def main():
                          "decode_full_kv_tokens": w.tokens * w.batch / (full_avg * 1e-3),
                          "decode_anchor_kv_tokens": w.tokens * w.batch / (anc_avg * 1e-3)},
         "roofline": {"bound": "hbm", "kernel": "encode_kernel",
+                     "timing": "events on the launch stream around graphs of back-to-back launches, timed region",
                      "achieved": gbps(ab["encode"], enc_avg), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": gbps(ab["encode"], enc_avg) / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(), "algorithmic_bytes": ab["encode"]},

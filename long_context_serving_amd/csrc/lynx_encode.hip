@@ -85,30 +85,30 @@ __device__ __forceinline__ void store_stream(float *p, float4 v) {
   __builtin_nontemporal_store(v.w, p + 3);
 }
 
-// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 without LDS:
-// v_permlane16_swap / v_permlane32_swap of a value with itself return the
-// pair (value of the even row, value of the odd row) of 16 lanes, resp. of
-// the low and the high 32 lanes, so op(pair) is the reduction in every lane.
+// Reductions over the 4 lanes of a quad (lanes 4j .. 4j+3 share their
+// channels): two DPP quad permutations, which fold into the reducing op.
+template <int kCtrl>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                               0xF, 0xF, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ double quad_perm(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), kCtrl, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), kCtrl, 0xF, 0xF, false));
+  return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
 template <typename Op>
 __device__ __forceinline__ float xreduce_f32(float v, Op op) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  v = op(v, quad_perm<kQuadXor1>(v));
+  return op(v, quad_perm<kQuadXor2>(v));
 }
 __device__ __forceinline__ double xsum_f64(double v) {
-#pragma unroll
-  for (int step = 0; step < 2; ++step) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
-    const auto l = step == 0 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
-                             : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    const auto h = step == 0 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
-                             : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    v = __builtin_bit_cast(double, static_cast<uint64_t>(l[0]) | (static_cast<uint64_t>(h[0]) << 32)) +
-        __builtin_bit_cast(double, static_cast<uint64_t>(l[1]) | (static_cast<uint64_t>(h[1]) << 32));
-  }
-  return v;
+  v = v + quad_perm<kQuadXor1>(v);
+  return v + quad_perm<kQuadXor2>(v);
 }
 struct MinOp { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
 struct MaxOp { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
@@ -181,8 +181,8 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, EncodeTables tab) {
   const int c = threadIdx.x >> 6;  // chunk = wave
   const int lane = threadIdx.x & 63;
-  const int cg = lane & 15;
-  const int r = lane >> 4;
+  const int cg = lane >> 2;  // channel group: channels 8cg .. 8cg+7
+  const int r = lane & 3;    // token group (the 4 lanes of a quad share channels)
 
   __shared__ uint2 s_lvl[kBuckets];
   __shared__ float s_min[kChunks][kDim];
@@ -310,11 +310,15 @@ void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, En
         const float s = r == 0 ? sabs[k] : r == 1 ? sabs[2 + k] : r == 2 ? sabs[4 + k] : sabs[6 + k];
         my_inv[k] = s > 0.0f ? static_cast<float>(1.0 / static_cast<double>(s)) : 0.0f;
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int src = cg + 16 * (i >> 1);  // lane holding channel i's reciprocal
-        inv_s[i] = __shfl(my_inv[i & 1], src);
-      }
+      // channel i's reciprocal is in lane r = i / 2 of the quad (DPP quad broadcast)
+      inv_s[0] = quad_perm<0x00>(my_inv[0]);
+      inv_s[1] = quad_perm<0x00>(my_inv[1]);
+      inv_s[2] = quad_perm<0x55>(my_inv[0]);
+      inv_s[3] = quad_perm<0x55>(my_inv[1]);
+      inv_s[4] = quad_perm<0xAA>(my_inv[0]);
+      inv_s[5] = quad_perm<0xAA>(my_inv[1]);
+      inv_s[6] = quad_perm<0xFF>(my_inv[0]);
+      inv_s[7] = quad_perm<0xFF>(my_inv[1]);
     }
 
     // ---- sign-aware alpha-law codes and the cut into nibble planes ----
