@@ -546,78 +546,100 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   };
 
   // Codes of NB chunks are held per wave: the chunk being computed and the
-  // next NB - 1 in flight (the draft's chunks are smaller, so it looks
-  // further ahead).  Scales of the next chunk are requested one chunk ahead
-  // and before the codes, so waiting for them never waits for those codes.
+  // next D = NB - 1 in flight (the draft's chunks are smaller, so it looks
+  // further ahead).  Scales run one chunk further ahead than codes: the step
+  // of chunk c requests the scales of chunk c + D + 1 and then the codes of
+  // chunk c + D, so the scales staged at the end of a step were requested
+  // before the codes that step waited for.  A wave whose run is short thus
+  // pays one memory round trip in its prologue and not one per chunk.
   // Every step issues its loads unconditionally -- a chunk past the run or
   // on an absent page reads chunk 0 of pool page 0 instead, and is not
   // computed -- so the wait counts the compiler derives are exact and never
   // wait for loads that are still ahead in the pipeline.
   constexpr int NB = kFull ? 2 : 3;
   constexpr int D = NB - 1;
-  if (s.pool_pages <= 0) cb = ce;  // no page can be read
-  Codes cds[NB];
-  long long pgs[NB];
-  Scales sc;
+  Codes cds[NB];    // codes of chunk c in buffer (c - cb) % NB
+  Scales scs[NB];   // scales of chunk c in buffer (c - cb) % NB
+  long long pgs[NB];  // page of chunk c, and after its step of chunk c + NB
   auto tile_of = [&](long long pg) { return pg >= 0 ? static_cast<size_t>(pg) * s.heads + h : 0; };
   auto chunk_of = [&](long long pg, int c) { return pg >= 0 ? (c & 7) : 0; };
   auto page_in_run = [&](int c) -> long long { return c < ce ? page_of(c) : -1; };
-  // The first chunks' codes and scales are requested before the set-up
-  // below, in the order a steady-state step leaves them (codes of chunk cb,
-  // its scales, then the codes of the next D - 1 chunks), so that the wait
-  // counts derived for the loop hold on entry as well.
-  if (cb < ce) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      pgs[d] = page_in_run(cb + d);
-      load_codes<kFull>(cds[d], kp, vp, tile_of(pgs[d]), chunk_of(pgs[d], cb + d), lc.koff, lc.voff);
-      if (d == 0) load_scales(sc, kp, vp, tile_of(pgs[0]), chunk_of(pgs[0], cb), lc.soff);
-    }
-  }
-  pgs[NB - 1] = -1;
-
-  // ---- tables (replicated rows) and the query group as f64 ----
+  // ---- set-up loads: this thread's table words and its lane's query
+  // values, issued ahead of the chunk loads so that waiting for them never
+  // waits for chunk data ----
+  uint32_t tw0, tw1;
   {
     const int e = tid & 255;
-    u32x4 v;
     if (kFull) {
-      const uint32_t x = tab.full[e];
-      v = u32x4{x, x, x, x};
+      tw0 = tab.full[e];
+      tw1 = tw0;
     } else {
-      const uint32_t x0 = tab.draft[e & 15], x1 = tab.draft[e >> 4];
-      v = u32x4{x0, x1, x0, x1};
+      tw0 = tab.draft[e & 15];
+      tw1 = tab.draft[e >> 4];
     }
-    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + e * 256 + (tid >> 8) * 128);
+  }
+  const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
+  const int jq = lc.n & 7;  // this lane's query head
+  const bool qvalid = jq < g;
+  uint4 qraw[4];  // channels 32r .. 32r+31 of head jq (row 0 stands in when jq >= g)
+  {
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(qg + (qvalid ? jq : 0) * kDim + 32 * lc.r);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qraw[k] = qrow[k];
+  }
+
+  // The first chunks' codes and scales are requested before the rest of the
+  // set-up, in the order the steps before chunk cb would have left them
+  // (scales of cb, then scales of cb + 1 + d and codes of cb + d for each
+  // d < D), so that the wait counts derived for the loop hold on entry.
+  // They are requested even by a wave with an empty run (page 0 stands in;
+  // the launcher guarantees the pool is not empty): a load on one path only
+  // would make every wait after the join count from the other path.
+#pragma unroll
+  for (int d = 0; d < NB; ++d) pgs[d] = page_in_run(cb + d);
+  load_scales(scs[0], kp, vp, tile_of(pgs[0]), chunk_of(pgs[0], cb), lc.soff);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load_scales(scs[d + 1], kp, vp, tile_of(pgs[d + 1]), chunk_of(pgs[d + 1], cb + d + 1), lc.soff);
+    load_codes<kFull>(cds[d], kp, vp, tile_of(pgs[d]), chunk_of(pgs[d], cb + d), lc.koff, lc.voff);
+  }
+
+  // ---- tables (replicated rows) ----
+  {
+    const u32x4 v = kFull ? u32x4{tw0, tw0, tw0, tw0} : u32x4{tw0, tw1, tw0, tw1};
+    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + (tid & 255) * 256 + (tid >> 8) * 128);
 #pragma unroll
     for (int k = 0; k < 8; ++k) dst[k] = v;
   }
-  const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
-  for (int e = tid; e < kHeads * kDim; e += kThreads) {
-    const int j = e / kDim, d = e % kDim;
-    const float qf = j < g ? __uint_as_float(static_cast<uint32_t>(qg[e]) << 16) : 0.0f;
-    q64[j * kQStride + d] = static_cast<double>(qf);
-    q32[j * kQ32Stride + d] = qf;
-  }
-  // q of this lane's head, channels 32r .. 32r+31 (exact bf16 values)
+  // ---- q of this lane's head, channels 32r .. 32r+31 (exact bf16 values) ----
   float qv[32];
   float qmax = 0.0f;
   {
-    const int j = lc.n & 7;
-    const bool valid = j < g;
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(qg + (valid ? j : 0) * kDim + 32 * lc.r);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint4 v = qrow[k];
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t u[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qv[8 * k + 2 * e] = valid ? __uint_as_float(u[e] << 16) : 0.0f;
-        qv[8 * k + 2 * e + 1] = valid ? __uint_as_float(u[e] & 0xFFFF0000u) : 0.0f;
+        qv[8 * k + 2 * e] = qvalid ? __uint_as_float(u[e] << 16) : 0.0f;
+        qv[8 * k + 2 * e + 1] = qvalid ? __uint_as_float(u[e] & 0xFFFF0000u) : 0.0f;
       }
     }
 #pragma unroll
     for (int k = 0; k < 32; ++k) qmax = fmaxf(qmax, fabsf(qv[k]));
     qmax = wave_max(qmax);
+  }
+  // the query group in LDS, f64 and f32 (zero rows for heads >= g): wave w
+  // writes head w's row from the lanes n = w (first 16 of their 32
+  // channels) and n = w + 8 (last 16)
+  if (jq == w) {
+    const bool second = lc.n >= 8;
+    const int d0 = 32 * lc.r + (second ? 16 : 0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float x = second ? qv[16 + k] : qv[k];
+      q64[w * kQStride + d0 + k] = static_cast<double>(x);
+      q32[w * kQ32Stride + d0 + k] = x;
+    }
   }
   __syncthreads();
 
@@ -634,21 +656,22 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
 
   if (cb < ce) {
     double ks0 = 1.0, ks1 = 1.0;  // inverse Q' scales of LDS slots 0 and 1
-    ks0 = scale_stage(sc, slots, lc.lane, qmax);
-    // one chunk c held in code buffer J = (c - cb) % NB, constants in LDS slot (c - cb) & 1
+    ks0 = scale_stage(scs[0], slots, lc.lane, qmax);
+    // one chunk c held in buffers J = (c - cb) % NB, constants in LDS slot (c - cb) & 1
     auto step = [&](auto jc, int c) {
       constexpr int J = decltype(jc)::value;
       constexpr int J1 = (J + 1) % NB, JD = (J + D) % NB;
       const int slot = (c - cb) & 1;
-      pgs[JD] = page_in_run(c + D);
-      load_scales(sc, kp, vp, tile_of(pgs[J1]), chunk_of(pgs[J1], c + 1), lc.soff);
+      const long long cur = pgs[J];
+      pgs[J] = page_in_run(c + D + 1);  // buffer J next holds chunk c + NB = c + D + 1
+      load_scales(scs[J], kp, vp, tile_of(pgs[J]), chunk_of(pgs[J], c + D + 1), lc.soff);
       load_codes<kFull>(cds[JD], kp, vp, tile_of(pgs[JD]), chunk_of(pgs[JD], c + D), lc.koff, lc.voff);
-      if (pgs[J] >= 0) {
+      if (cur >= 0) {
         wave_lds_sync();
         compute_chunk<kFull>(cds[J], slots + slot * kSlotBytes, slot ? ks1 : ks0, q32, q64, lc, lut,
                              st, srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
       }
-      const double k = scale_stage(sc, slots + (slot ^ 1) * kSlotBytes, lc.lane, qmax);
+      const double k = scale_stage(scs[J1], slots + (slot ^ 1) * kSlotBytes, lc.lane, qmax);
       if (slot) ks0 = k; else ks1 = k;
     };
     for (int c = cb; c < ce; c += NB) {
@@ -829,6 +852,12 @@ __global__ __launch_bounds__(kCombThreads) void attn_mfma_combine_kernel(AttnSha
   }
 }
 
+// Output of requests whose every page is skipped (an empty pool): zeros.
+__global__ __launch_bounds__(256) void attn_zero_kernel(float *__restrict__ out, size_t n) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) out[i] = 0.0f;
+}
+
 MfmaTables build_mfma_tables() {
   MfmaTables t;
   const DecodeTable &dt = decode_table();
@@ -860,6 +889,13 @@ hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const Pl
                                  float *scores, void *workspace, hipStream_t stream) {
   static const MfmaTables tables = build_mfma_tables();
   if (s.splits > kCombMaxSplits) return hipErrorInvalidValue;
+  if (s.pool_pages <= 0) {
+    // no page can be read: every request's context is empty
+    const size_t n = static_cast<size_t>(s.batch) * s.q_heads * kDim;
+    hipLaunchKernelGGL(attn_zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                       stream, out, n);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>(static_cast<long long>(s.batch) * s.heads * s.splits));
   if (full)
     hipLaunchKernelGGL(attn_mfma_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v,

@@ -15,6 +15,7 @@ Bar (element by element, same seeded inputs):
   peaked      with one-hot softmax (plain Laplace queries), where fp32 itself
               misses 2e-3 by up to 7x: no worse than that fp32 evaluation.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -302,6 +303,18 @@ def test_empty_inputs(lynx):
     q = to_dev(np.zeros((0, 16, 128), np.uint16))
     o = lynx.decode_attention(q, pl, pl, 1, full=True)
     assert o.shape == (0, 16, 128)
+    # requests over an empty pool: every block-table entry is skipped, the
+    # context is empty and the output is zero (group 8: matrix-core kernel;
+    # group 16: the other kernel)
+    empty = dataclasses.replace(pl, num_pages=0)  # valid pointers, pool of 0 pages
+    for Hq in (16, 32):
+        q = to_dev(synth.float_to_bf16_bits(np.ones((3, Hq, 128), np.float32)))
+        bt = torch.full((3, 2), -1, dtype=torch.int32, device="cuda")
+        for full in (False, True):
+            o = lynx.decode_attention(q, empty, empty, 2, full=full, block_table=bt,
+                                      out=torch.full((3, Hq, 128), 7.0, device="cuda"))
+            torch.cuda.synchronize()
+            assert torch.count_nonzero(o).item() == 0, (Hq, full)
 
 
 def test_ragged_lengths_group_sizes_and_skipped_pages(lynx):
