@@ -53,6 +53,9 @@ def _load():
     lib.oracle_attention.argtypes = [P, P, P, i32, i64, i32, i32, i32,
                                      ctypes.c_double, P, P, i32]
     lib.oracle_attention.restype = i32
+    lib.oracle_prefix_attention.argtypes = [P, P, P, P, i32, i32, i64, i32, i32, i32,
+                                            ctypes.c_double, P, i32]
+    lib.oracle_prefix_attention.restype = i32
     lib.oracle_uniform_codes.argtypes = [P, i64, i64, i32, P]
     lib.oracle_uniform_codes.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -176,6 +179,57 @@ def attention(q, k, v, sm_scale: float, want_logits: bool = False, nthreads: int
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments")
     return (out, logits) if want_logits else out
+
+
+def prefix_attention(q, k, v, visible, sm_scale: float, nthreads: int = 0):
+    """Several query tokens per request, token i over the first visible[b][i]
+    cached tokens, in float64.
+
+    q: [B][Tq][Hq][D]; k, v: [B][T][H][D]; visible: [B][Tq].  Returns
+    out [B][Tq][Hq][D].
+    """
+    q = _c(q, np.float64)
+    k = _c(k, np.float64)
+    v = _c(v, np.float64)
+    vis = _c(visible, np.int64)
+    B, Tq, Hq, D = q.shape
+    _, T, H, _ = k.shape
+    if vis.shape != (B, Tq):
+        raise ValueError("visible must be [B][Tq]")
+    out = np.empty((B, Tq, Hq, D), np.float64)
+    rc = _load().oracle_prefix_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(vis), B, Tq, T, H, Hq, D,
+                                         float(sm_scale), _ptr(out), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_prefix_attention rejected its arguments")
+    return out
+
+
+def verify_attention(q_bits, pages_k, pages_v, tail_k_bits, tail_v_bits, tail_len, sm_scale: float,
+                     nthreads: int = 0):
+    """Attention of the Tq newest tokens of each request over its cache.
+
+    q_bits [B][Tq][Hq][D] bf16 bits.  pages_k / pages_v: per request, the
+    dequantized pages as float64 [n_b * 256][H][D] (n_b may be 0).
+    tail_k_bits / tail_v_bits: per request, bf16 bits [>= tail_len[b]][H][D];
+    the last Tq tail tokens are the query tokens themselves, so token i sees
+    every page token and tail tokens 0 .. tail_len - Tq + i.
+    Returns out [B][Tq][Hq][D] (float64).
+    """
+    qf = bf16_bits_to_float(q_bits).astype(np.float64)
+    B, Tq = qf.shape[0], qf.shape[1]
+    outs = []
+    for b in range(B):
+        n_tail = int(tail_len[b])
+        if n_tail < Tq:
+            raise ValueError("the tail must hold the query tokens")
+        tk = bf16_bits_to_float(np.asarray(tail_k_bits[b])[:n_tail]).astype(np.float64)
+        tv = bf16_bits_to_float(np.asarray(tail_v_bits[b])[:n_tail]).astype(np.float64)
+        k = np.concatenate([np.asarray(pages_k[b], np.float64), tk])[None]
+        v = np.concatenate([np.asarray(pages_v[b], np.float64), tv])[None]
+        n_pages_tok = len(pages_k[b])
+        vis = (n_pages_tok + n_tail - Tq + 1 + np.arange(Tq, dtype=np.int64))[None]
+        outs.append(prefix_attention(qf[b:b + 1], k, v, vis, sm_scale, nthreads)[0])
+    return np.stack(outs)
 
 
 def uniform_codes(x, bits: int):

@@ -378,6 +378,68 @@ int32_t oracle_attention(const double *q, const double *k, const double *v,
 }
 
 /* ---------------------------------------------------------------------------
+ * Attention of several query tokens per request, each over a prefix of the
+ * cached sequence, brute force in double precision.  This is the verify
+ * pass of speculative decoding (page "Lynx: the KV cache does not have to
+ * arrive whole", section 4: drafts run on the anchor stream, the refined
+ * cache Q_full verifies them): the Tq speculative tokens are scored at once,
+ * token i seeing the cache and the speculative tokens up to itself.
+ *   q       [B][Tq][Hq][D]
+ *   k,v     [B][T][H][D]      (dequantized pages followed by the bf16 tail)
+ *   visible [B][Tq]           tokens 0 .. visible-1 are seen (1 <= visible <= T)
+ *   out     [B][Tq][Hq][D]
+ * Query head j reads KV head j / (Hq / H).
+ * ------------------------------------------------------------------------- */
+int32_t oracle_prefix_attention(const double *q, const double *k, const double *v,
+                                const int64_t *visible, int32_t B, int32_t Tq,
+                                int64_t T, int32_t H, int32_t Hq, int32_t D,
+                                double sm_scale, double *out, int32_t nthreads)
+{
+    if (!q || !k || !v || !visible || !out || B < 0 || Tq < 1 || T < 1 || H < 1 ||
+        Hq < H || Hq % H != 0 || D < 1)
+        return -1;
+    for (int64_t i = 0; i < (int64_t)B * Tq; ++i)
+        if (visible[i] < 1 || visible[i] > T) return -1;
+    const int32_t g = Hq / H;
+    const int nt = nthreads_or_default(nthreads);
+#pragma omp parallel num_threads(nt)
+    {
+        double *s = (double *)malloc((size_t)T * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t row = 0; row < (int64_t)B * Tq * Hq; ++row) {
+            const int64_t bi = row / Hq;             /* b * Tq + i */
+            const int32_t j = (int32_t)(row % Hq);
+            const int32_t b = (int32_t)(bi / Tq);
+            const int32_t h = j / g;
+            const int64_t n = visible[bi];
+            const double *qv = q + row * D;
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < n; ++t) {
+                const double *kv = k + (((int64_t)b * T + t) * H + h) * D;
+                double acc = 0.0;
+                for (int32_t d = 0; d < D; ++d) acc += qv[d] * kv[d];
+                s[t] = sm_scale * acc;
+                if (s[t] > mx) mx = s[t];
+            }
+            double z = 0.0;
+            for (int64_t t = 0; t < n; ++t) {
+                s[t] = exp(s[t] - mx);
+                z += s[t];
+            }
+            double *o = out + row * D;
+            for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+            for (int64_t t = 0; t < n; ++t) {
+                const double p = s[t] / z;
+                const double *vv = v + (((int64_t)b * T + t) * H + h) * D;
+                for (int32_t d = 0; d < D; ++d) o[d] += p * vv[d];
+            }
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Baseline for the effective-bin check of section 2 ("Not all bits are
  * equal"): a uniform B-bit grid shared by all columns of a row.
  * x [rows][cols] fp32; codes [rows][cols] int32 in 0 .. 2^bits - 1.

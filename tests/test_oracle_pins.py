@@ -433,6 +433,68 @@ def test_attention_special_cases():
 
 
 # ---------------------------------------------------------------------------
+# Pin 10b: several query tokens over prefixes of the cache (the verify pass)
+# against torch's SDPA with an explicit mask (float64, CPU)
+# ---------------------------------------------------------------------------
+def test_prefix_attention_matches_masked_sdpa_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(17)
+    B, Tq, T, H, g, D = 2, 5, 40, 2, 3, 16
+    q = rng.standard_normal((B, Tq, H * g, D))
+    k = rng.standard_normal((B, T, H, D)) * 3
+    v = rng.standard_normal((B, T, H, D))
+    vis = np.array([[36, 37, 38, 39, 40], [1, 2, 17, 30, 40]])
+    sc = 1.0 / math.sqrt(D)
+    out = oracle.prefix_attention(q, k, v, vis, sc)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3).contiguous()                 # [B][Hq][Tq][D]
+    kt = torch.from_numpy(np.repeat(k, g, axis=2)).permute(0, 2, 1, 3).contiguous()
+    vt = torch.from_numpy(np.repeat(v, g, axis=2)).permute(0, 2, 1, 3).contiguous()
+    mask = torch.from_numpy(np.arange(T)[None, None, :] < vis[:, :, None])[:, None]  # [B][1][Tq][T]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=sc)
+    np.testing.assert_allclose(out, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=1e-12)
+
+
+def test_prefix_attention_special_cases():
+    rng = np.random.default_rng(18)
+    B, Tq, T, H, D = 1, 3, 12, 1, 8
+    q = rng.standard_normal((B, Tq, 2, D))
+    k = rng.standard_normal((B, T, H, D))
+    v = rng.standard_normal((B, T, H, D))
+    vis = np.array([[1, 6, 12]])
+    out = oracle.prefix_attention(q, k, v, vis, 0.4)
+    # one visible token: its value
+    np.testing.assert_array_equal(out[0, 0, 0], v[0, 0, 0])
+    # tokens past a query's prefix do not reach it
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 6:] += 50.0
+    v2[0, 6:] -= 7.0
+    out2 = oracle.prefix_attention(q, k2, v2, vis, 0.4)
+    np.testing.assert_array_equal(out2[0, :2], out[0, :2])
+    assert not np.allclose(out2[0, 2], out[0, 2])
+    # the whole sequence visible: the single-query attention
+    full = oracle.attention(q[:, 2], k, v, 0.4)
+    np.testing.assert_allclose(out[0, 2], full[0], atol=1e-15)
+
+
+def test_verify_attention_sees_pages_and_tail_up_to_itself():
+    rng = np.random.default_rng(19)
+    H, D, Tq = 1, 8, 3
+    pages = rng.standard_normal((256, H, D))
+    tail = rng.standard_normal((10, H, D)).astype(np.float32)
+    tail_bits = (tail.view(np.uint32) >> 16).astype(np.uint16)   # truncated to bf16
+    tail_f = oracle.bf16_bits_to_float(tail_bits).astype(np.float64)
+    q_bits = (rng.standard_normal((1, Tq, 2, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out = oracle.verify_attention(q_bits, [pages], [pages * 0.5], [tail_bits], [tail_bits], [7], 0.3)
+    # token i (of the Tq = 3 newest of 7 tail tokens) sees 256 + 5 + i tokens
+    k = np.concatenate([pages, tail_f[:7]])[None]
+    v = np.concatenate([pages * 0.5, tail_f[:7]])[None]
+    qf = oracle.bf16_bits_to_float(q_bits).astype(np.float64)
+    for i in range(Tq):
+        ref = oracle.attention(qf[:, i], k[:, :256 + 5 + i], v[:, :256 + 5 + i], 0.3)
+        np.testing.assert_allclose(out[0, i], ref[0], atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
 # Pin 11: the size arithmetic of section 1
 # ---------------------------------------------------------------------------
 def test_qwen3_235b_kv_size():
