@@ -61,6 +61,10 @@ extern "C" {
 #define LYNX_MAX_GROUP 16    /* largest supported Hq / H */
 #define LYNX_MAX_KV_HEADS 65535  /* largest H of an encoded tensor (a page of
                                     256 tokens stays below 4 GiB) */
+#define LYNX_MAX_QUERY_TOKENS 64 /* largest number of speculative tokens a
+                                    verify pass scores at once */
+#define LYNX_TAIL_TOKENS 320     /* capacity of a request's bf16 tail: a page
+                                    not yet full plus the speculative tokens */
 
 typedef enum lynx_status {
     LYNX_OK = 0,
@@ -193,6 +197,64 @@ int lynx_decode_attention_full(const uint16_t *q, const lynx_planes *k,
                                float *out, float *scores,
                                void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * Attention of the tq newest tokens of each request over its compact pages
+ * and its bf16 tail (page "Lynx: the KV cache does not have to arrive
+ * whole", section 4: drafts run on the anchor stream alone, the refined
+ * cache Q_full verifies them).  Pages are quantized whole (section 3), so
+ * the tokens that have not filled a page yet -- including the speculative
+ * tokens being scored -- stay in bf16 in the tail until their page fills.
+ * lynx_verify_attention reads anchor and residual (the verify pass over
+ * Q_full, tq up to 64); lynx_draft_attention reads the anchor plane alone
+ * (a draft step, usually tq = 1).
+ *   q            bf16 bits [B][tq][Hq][128]: row (b, i) is the i-th of the
+ *                request's tq newest tokens
+ *   tq           1 .. LYNX_MAX_QUERY_TOKENS
+ *   k, v         encoded page pools as for the decode calls; a pool of 0
+ *                pages is allowed (then only the tail is read)
+ *   block_table  int32 [B][max_pages_per_seq] as for the decode calls
+ *   page_tokens  int32 [B] tokens in quantized pages per request, a multiple
+ *                of 256 in [0, 256*max_pages_per_seq]; NULL = every request
+ *                has max_pages_per_seq pages.  Device memory; values outside
+ *                the range are clamped (output unspecified).
+ *   tail_k/v     bf16 bits [B][LYNX_TAIL_TOKENS][H][128]: the request's
+ *                tokens after its pages, in order
+ *   tail_len     int32 [B] tokens in the tail, in [tq, LYNX_TAIL_TOKENS]
+ *                (device memory; clamped, output unspecified outside).  The
+ *                last tq tail tokens are the query tokens: token i sees
+ *                every page token and tail tokens 0 .. tail_len - tq + i.
+ *   out          fp32 [B][tq][Hq][128]
+ *   workspace    at least lynx_verify_attention_workspace_size(...) bytes,
+ *                16-byte aligned, contents need not be initialised; calls
+ *                that overlap in time must not share a workspace.
+ * The draft variant never reads k->residual or v->residual.  batch = 0 is a
+ * no-op once the shape arguments are valid.  Errors: NULL_ARG, BAD_SHAPE,
+ * MISALIGNED, WORKSPACE, DEVICE, HIP.
+ */
+size_t lynx_verify_attention_workspace_size(int32_t batch, int32_t tq,
+                                            int32_t num_kv_heads,
+                                            int32_t num_q_heads,
+                                            int32_t head_dim,
+                                            int32_t max_pages_per_seq);
+int lynx_verify_attention(const uint16_t *q, int32_t tq, const lynx_planes *k,
+                          const lynx_planes *v, const int32_t *block_table,
+                          const int32_t *page_tokens, const uint16_t *tail_k,
+                          const uint16_t *tail_v, const int32_t *tail_len,
+                          int32_t batch, int32_t num_kv_heads,
+                          int32_t num_q_heads, int32_t head_dim,
+                          int32_t max_pages_per_seq, int64_t pool_pages,
+                          float sm_scale, float *out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+int lynx_draft_attention(const uint16_t *q, int32_t tq, const lynx_planes *k,
+                         const lynx_planes *v, const int32_t *block_table,
+                         const int32_t *page_tokens, const uint16_t *tail_k,
+                         const uint16_t *tail_v, const int32_t *tail_len,
+                         int32_t batch, int32_t num_kv_heads,
+                         int32_t num_q_heads, int32_t head_dim,
+                         int32_t max_pages_per_seq, int64_t pool_pages,
+                         float sm_scale, float *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /* Static string for a status code (never NULL). */
 const char *lynx_status_string(int status);

@@ -131,6 +131,58 @@ int attention_common(const uint16_t *q, const lynx_planes *k, const lynx_planes 
   return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
 }
 
+int tail_attention_common(const uint16_t *q, int32_t tq, const lynx_planes *k,
+                          const lynx_planes *v, const int32_t *block_table,
+                          const int32_t *page_tokens, const uint16_t *tail_k,
+                          const uint16_t *tail_v, const int32_t *tail_len, int32_t batch,
+                          int32_t heads, int32_t q_heads, int32_t head_dim, int32_t max_pages,
+                          int64_t pool_pages, float sm_scale, float *out, void *workspace,
+                          size_t workspace_bytes, void *stream, bool full) {
+  if (head_dim != LYNX_HEAD_DIM || batch < 0 || tq < 1 || tq > LYNX_MAX_QUERY_TOKENS ||
+      heads < 1 || q_heads < heads || q_heads % heads != 0 ||
+      q_heads / heads > LYNX_MAX_GROUP || max_pages < 1)
+    return LYNX_ERR_BAD_SHAPE;
+  const int64_t rows = static_cast<int64_t>(batch) * tq;
+  if (rows * q_heads * 4 > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
+  if (pool_pages < 0 || pool_pages * static_cast<int64_t>(heads) > 0x7FFFFFFFLL)
+    return LYNX_ERR_BAD_SHAPE;
+  if (!block_table && pool_pages > 0 && static_cast<int64_t>(batch) * max_pages > pool_pages)
+    return LYNX_ERR_BAD_SHAPE;
+  if (batch == 0) return LYNX_OK;
+  if (!q || !out || !tail_k || !tail_v || !tail_len) return LYNX_ERR_NULL_ARG;
+  if (pool_pages > 0) {
+    int rc = check_planes(k, full);
+    if (rc) return rc;
+    rc = check_planes(v, full);
+    if (rc) return rc;
+  }
+  if (!aligned16(q) || !aligned16(out) || !aligned16(tail_k) || !aligned16(tail_v) ||
+      !aligned16(tail_len) || (block_table && !aligned16(block_table)) ||
+      (page_tokens && !aligned16(page_tokens)))
+    return LYNX_ERR_MISALIGNED;
+  lynx::AttnShape s = lynx::attention_shape_tail(batch, tq, heads, q_heads, max_pages);
+  s.pool_pages = pool_pages;
+  if (rows * heads * s.splits > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
+  const size_t need = lynx::attention_workspace_bytes(s);
+  if (!workspace || workspace_bytes < need) return LYNX_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LYNX_ERR_MISALIGNED;
+  const int rc = check_device();
+  if (rc) return rc;
+  PlanesArg ka{}, va{};
+  if (pool_pages > 0) {
+    ka = to_arg(k);
+    va = to_arg(v);
+    if (!full) {
+      ka.residual = nullptr;
+      va.residual = nullptr;
+    }
+  }
+  const hipError_t e = lynx::launch_attention_with_tail(
+      q, ka, va, block_table, page_tokens, tail_k, tail_v, tail_len, LYNX_TAIL_TOKENS, s, sm_scale,
+      full, out, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,6 +264,41 @@ int lynx_decode_attention_full(const uint16_t *q, const lynx_planes *k, const ly
                           head_dim, max_pages_per_seq, pool_pages, sm_scale, out, scores,
                           workspace,
                           workspace_bytes, stream, true);
+}
+
+size_t lynx_verify_attention_workspace_size(int32_t batch, int32_t tq, int32_t num_kv_heads,
+                                            int32_t num_q_heads, int32_t head_dim,
+                                            int32_t max_pages_per_seq) {
+  if (head_dim != LYNX_HEAD_DIM || batch < 0 || tq < 1 || tq > LYNX_MAX_QUERY_TOKENS ||
+      num_kv_heads < 1 || num_q_heads < num_kv_heads || num_q_heads % num_kv_heads != 0 ||
+      num_q_heads / num_kv_heads > LYNX_MAX_GROUP || max_pages_per_seq < 1)
+    return 0;
+  return lynx::attention_workspace_bytes(
+      lynx::attention_shape_tail(batch, tq, num_kv_heads, num_q_heads, max_pages_per_seq));
+}
+
+int lynx_verify_attention(const uint16_t *q, int32_t tq, const lynx_planes *k, const lynx_planes *v,
+                          const int32_t *block_table, const int32_t *page_tokens,
+                          const uint16_t *tail_k, const uint16_t *tail_v, const int32_t *tail_len,
+                          int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
+                          int32_t head_dim, int32_t max_pages_per_seq, int64_t pool_pages,
+                          float sm_scale, float *out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  return tail_attention_common(q, tq, k, v, block_table, page_tokens, tail_k, tail_v, tail_len,
+                               batch, num_kv_heads, num_q_heads, head_dim, max_pages_per_seq,
+                               pool_pages, sm_scale, out, workspace, workspace_bytes, stream, true);
+}
+
+int lynx_draft_attention(const uint16_t *q, int32_t tq, const lynx_planes *k, const lynx_planes *v,
+                         const int32_t *block_table, const int32_t *page_tokens,
+                         const uint16_t *tail_k, const uint16_t *tail_v, const int32_t *tail_len,
+                         int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
+                         int32_t head_dim, int32_t max_pages_per_seq, int64_t pool_pages,
+                         float sm_scale, float *out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  return tail_attention_common(q, tq, k, v, block_table, page_tokens, tail_k, tail_v, tail_len,
+                               batch, num_kv_heads, num_q_heads, head_dim, max_pages_per_seq,
+                               pool_pages, sm_scale, out, workspace, workspace_bytes, stream, false);
 }
 
 const char *lynx_status_string(int status) {

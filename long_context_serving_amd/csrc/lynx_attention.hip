@@ -56,7 +56,7 @@ struct Partials {
 };
 
 __device__ __forceinline__ Partials partials_of(void *ws, const AttnShape &s) {
-  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.splits * s.group;
+  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.parts * s.group;
   Partials pt;
   pt.m = reinterpret_cast<double *>(ws);
   pt.l = reinterpret_cast<float *>(pt.m + ((n + 1) & ~static_cast<size_t>(1)));
@@ -73,13 +73,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
   const int split = blockIdx.x % s.splits;
   const int bh = blockIdx.x / s.splits;
   const int h = bh % s.heads;
-  const int b = bh / s.heads;
+  const int b = bh / s.heads;  // query row
+  const int req = b / s.tq;     // its request
   const int g = s.group;
   const int tid = threadIdx.x;
 
   int npages = s.max_pages;
   if (seq_lens) {
-    npages = seq_lens[b] / kPage;
+    npages = seq_lens[req] / kPage;
     npages = npages < 0 ? 0 : (npages > s.max_pages ? s.max_pages : npages);
   }
   const int p0 = split * s.pages_per_split;
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
 
   const size_t T = static_cast<size_t>(s.max_pages) * kPage;
   for (int lp = p0; lp < p1; ++lp) {
-    const int pg = block_table ? block_table[static_cast<size_t>(b) * s.max_pages + lp]
+    const int pg = block_table ? block_table[static_cast<size_t>(req) * s.max_pages + lp]
                                : b * s.max_pages + lp;
     if (pg < 0 || pg >= s.pool_pages) continue;  // invalid entry: page skipped
     const size_t tile = static_cast<size_t>(pg) * s.heads + h;
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
 
   // ---- write (m, l, o) partials ----
   Partials pt = partials_of(ws, s);
-  const size_t base = static_cast<size_t>(blockIdx.x) * g;
+  const size_t base = (static_cast<size_t>(bh) * s.parts + split) * g;
   if (tid < g) {
     pt.m[base + tid] = s_m[tid];
     pt.l[base + tid] = s_l[tid];
@@ -305,17 +306,17 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnShape
   const int j = jq % s.group;
   const int tid = threadIdx.x;
   Partials pt = partials_of(const_cast<void *>(ws), s);
-  const size_t first = (static_cast<size_t>(b) * s.heads + h) * s.splits;
-  __shared__ float s_w[kMaxSplits];
+  const size_t first = (static_cast<size_t>(b) * s.heads + h) * s.parts;
+  __shared__ float s_w[kMaxSplits + 1];
   __shared__ double s_red[kCombineThreads / 64];
   __shared__ double s_o[32][33];
 
   double M = -INFINITY;
-  for (int sp = tid; sp < s.splits; sp += kCombineThreads)
+  for (int sp = tid; sp < s.parts; sp += kCombineThreads)
     M = fmax(M, pt.m[(first + sp) * s.group + j]);
   M = block_reduce(M, true, s_red);
   double L = 0.0;
-  for (int sp = tid; sp < s.splits; sp += kCombineThreads) {
+  for (int sp = tid; sp < s.parts; sp += kCombineThreads) {
     const size_t r = (first + sp) * s.group + j;
     const double m = pt.m[r];
     const float wgt = m == -INFINITY ? 0.0f : static_cast<float>(exp(m - M));
@@ -328,13 +329,13 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnShape
   const int sg = tid >> 3;  // split group 0..31
   const int d0 = part * 32 + 4 * c4;
   double o[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int sp0 = sg; sp0 < s.splits; sp0 += 4 * 32) {
+  for (int sp0 = sg; sp0 < s.parts; sp0 += 4 * 32) {
     float4 v[4];
     float wk[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int sp = sp0 + 32 * u;
-      const bool ok = sp < s.splits;
+      const bool ok = sp < s.parts;
       wk[u] = ok ? s_w[sp] : 0.0f;
       v[u] = ok ? *reinterpret_cast<const float4 *>(pt.o + ((first + sp) * s.group + j) * kDim + d0)
                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -364,6 +365,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnShape
 AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
   AttnShape s;
   s.batch = batch;
+  s.tq = 1;
   s.heads = heads;
   s.q_heads = q_heads;
   s.group = heads > 0 ? q_heads / heads : 0;
@@ -377,12 +379,20 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
   if (pps > max_pages) pps = max_pages > 0 ? max_pages : 1;
   s.pages_per_split = static_cast<int>(pps);
   s.splits = max_pages > 0 ? static_cast<int>((max_pages + pps - 1) / pps) : 1;
+  s.parts = s.splits;
+  return s;
+}
+
+AttnShape attention_shape_tail(int requests, int tq, int heads, int q_heads, int max_pages) {
+  AttnShape s = attention_shape(requests * tq, heads, q_heads, max_pages);
+  s.tq = tq;
+  s.parts = s.splits + 1;
   return s;
 }
 
 // Partials (m, l, o) of every split.
 size_t attention_workspace_bytes(const AttnShape &s) {
-  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.splits * s.group;
+  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.parts * s.group;
   return ((n + 1) & ~static_cast<size_t>(1)) * sizeof(double) +
          ((n + 3) & ~static_cast<size_t>(3)) * sizeof(float) + n * kDim * sizeof(float);
 }
@@ -396,7 +406,7 @@ hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
   if (s.batch == 0) return hipSuccess;
   if (attention_mfma_supported(s.group))
     return launch_attention_mfma(q, k, v, block_table, seq_lens, s, sm_scale, full, out, scores,
-                                 workspace, stream);
+                                 workspace, true, stream);
   YTable tab;
   const DecodeTable &dt = decode_table();
   for (int i = 0; i < 256; ++i) tab.y[i] = dt.y[i];
@@ -412,6 +422,48 @@ hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
   hipLaunchKernelGGL(attn_combine_kernel,
                      dim3(static_cast<unsigned>(s.batch * s.q_heads * kCombineParts)),
                      dim3(kCombineThreads), 0, stream, s, static_cast<const void *>(workspace), out);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_with_tail(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
+                                      const int32_t *block_table, const int32_t *page_tokens,
+                                      const uint16_t *tail_k, const uint16_t *tail_v,
+                                      const int32_t *tail_len, int tail_cap, const AttnShape &s,
+                                      float sm_scale, bool full, float *out, void *workspace,
+                                      hipStream_t stream) {
+  if (s.batch == 0) return hipSuccess;
+  const bool mfma = attention_mfma_supported(s.group);
+  AttnShape sp = s;
+  hipError_t e;
+  if (s.pool_pages <= 0) {
+    // no page can be read: the tail is the whole context
+    sp.splits = 0;
+    sp.parts = 1;
+  } else if (mfma) {
+    e = launch_attention_mfma(q, k, v, block_table, page_tokens, sp, sm_scale, full, out, nullptr,
+                              workspace, false, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    YTable tab;
+    const DecodeTable &dt = decode_table();
+    for (int i = 0; i < 256; ++i) tab.y[i] = dt.y[i];
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(sp.batch) * sp.heads * sp.splits));
+    if (full)
+      hipLaunchKernelGGL(attn_split_kernel<true>, grid, dim3(kAttnThreads), 0, stream, q, k, v,
+                         block_table, page_tokens, sp, sm_scale, nullptr, workspace, tab);
+    else
+      hipLaunchKernelGGL(attn_split_kernel<false>, grid, dim3(kAttnThreads), 0, stream, q, k, v,
+                         block_table, page_tokens, sp, sm_scale, nullptr, workspace, tab);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  e = launch_attention_tail_part(q, tail_k, tail_v, tail_len, tail_cap, sp, sm_scale, mfma,
+                                 workspace, stream);
+  if (e != hipSuccess) return e;
+  if (mfma) return launch_attention_mfma_combine(sp, workspace, out, stream);
+  hipLaunchKernelGGL(attn_combine_kernel,
+                     dim3(static_cast<unsigned>(sp.batch * sp.q_heads * kCombineParts)),
+                     dim3(kCombineThreads), 0, stream, sp, static_cast<const void *>(workspace), out);
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ struct Partials {
 };
 
 __device__ __forceinline__ Partials partials_of(void *ws, const AttnShape &s) {
-  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.splits * s.group;
+  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.parts * s.group;
   Partials pt;
   pt.m = reinterpret_cast<double *>(ws);
   pt.l = reinterpret_cast<float *>(pt.m + ((n + 1) & ~static_cast<size_t>(1)));
@@ -497,7 +497,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   const int split = static_cast<int>(lb_idx % static_cast<unsigned>(s.splits));
   const int bh = static_cast<int>(lb_idx / static_cast<unsigned>(s.splits));
   const int h = bh % s.heads;
-  const int b = bh / s.heads;
+  const int b = bh / s.heads;  // query row
+  const int req = b / s.tq;     // its request
   const int g = s.group;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
@@ -524,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
       (const __attribute__((address_space(4))) int32_t *)seq_lens;
   int npages = s.max_pages;
   if (seq_lens) {
-    npages = sl_c[b] / kPage;
+    npages = sl_c[req] / kPage;
     npages = npages < 0 ? 0 : (npages > s.max_pages ? s.max_pages : npages);
   }
   const int pps = s.pages_per_split;
@@ -540,8 +541,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   // page of chunk ci, or -1 when the block table marks it absent
   auto page_of = [&](int ci) -> long long {
     const int lp = ci >> 3;
-    const long long pg = block_table ? bt_c[static_cast<size_t>(b) * s.max_pages + lp]
-                                     : static_cast<long long>(b) * s.max_pages + lp;
+    const long long pg = block_table ? bt_c[static_cast<size_t>(req) * s.max_pages + lp]
+                                     : static_cast<long long>(req) * s.max_pages + lp;
     return (pg < 0 || pg >= s.pool_pages) ? -1 : pg;
   };
 
@@ -719,14 +720,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
       O.z += f * (hi.z + lo.z);
       O.w += f * (hi.w + lo.w);
     }
-    if (s.splits == 1) {
+    if (s.parts == 1) {
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       reinterpret_cast<float4 *>(
           out + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + j) * kDim)[c] =
           make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
     } else {
       Partials pt = partials_of(ws, s);
-      const size_t row = static_cast<size_t>(lb_idx) * g + j;  // = (bh * splits + split) * g + j
+      const size_t row = (static_cast<size_t>(bh) * s.parts + split) * g + j;
       reinterpret_cast<float4 *>(pt.o + row * kDim)[c] = O;
       if (c == 0) {
         pt.m[row] = static_cast<double>(M);
@@ -742,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
 // the splits are wave reductions (32 lanes per head).
 constexpr int kCombThreads = 256;
 constexpr int kCombChannels = 16;
-constexpr int kCombMaxSplits = 256;  // attention_shape never makes more
+constexpr int kCombMaxSplits = 288;  // attention_shape makes at most 256 splits, the tail one more part
 
 // op over the 32 lanes of each half of a wave
 template <typename Op>
@@ -762,7 +763,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_mfma_combine_kernel(AttnSha
   const int cq = blockIdx.x % per_bh;
   const int b = bh / s.heads, h = bh % s.heads;
   const int g = s.group;
-  const int ns = s.splits;
+  const int ns = s.parts;
   const int tid = threadIdx.x;
   Partials pt = partials_of(const_cast<void *>(ws), s);
   const size_t first = static_cast<size_t>(bh) * ns * g;  // rows of split 0
@@ -886,9 +887,9 @@ int attention_mfma_target_blocks() { return 256; }
 hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
                                  const int32_t *block_table, const int32_t *seq_lens,
                                  const AttnShape &s, float sm_scale, bool full, float *out,
-                                 float *scores, void *workspace, hipStream_t stream) {
+                                 float *scores, void *workspace, bool merge, hipStream_t stream) {
   static const MfmaTables tables = build_mfma_tables();
-  if (s.splits > kCombMaxSplits) return hipErrorInvalidValue;
+  if (s.parts > kCombMaxSplits) return hipErrorInvalidValue;
   if (s.pool_pages <= 0) {
     // no page can be read: every request's context is empty
     const size_t n = static_cast<size_t>(s.batch) * s.q_heads * kDim;
@@ -903,13 +904,19 @@ hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const Pl
   else
     hipLaunchKernelGGL(attn_mfma_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v,
                        block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
-  if (s.splits == 1) return hipGetLastError();  // the blocks wrote the output
+  if (s.parts == 1 || !merge) return hipGetLastError();  // output or partials written
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_attention_mfma_combine(s, workspace, out, stream);
+}
+
+hipError_t launch_attention_mfma_combine(const AttnShape &s, const void *workspace, float *out,
+                                         hipStream_t stream) {
+  if (s.parts > kCombMaxSplits) return hipErrorInvalidValue;
   const dim3 cgrid(static_cast<unsigned>(static_cast<long long>(s.batch) * s.heads *
                                          (kDim / kCombChannels)));
-  hipLaunchKernelGGL(attn_mfma_combine_kernel, cgrid, dim3(kCombThreads), 0, stream, s,
-                     static_cast<const void *>(workspace), out);
+  hipLaunchKernelGGL(attn_mfma_combine_kernel, cgrid, dim3(kCombThreads), 0, stream, s, workspace,
+                     out);
   return hipGetLastError();
 }
 

@@ -85,27 +85,51 @@ hipError_t launch_dequant(const PlanesArg &in, int64_t num_pages, int heads,
                           int role, bool full, float *out,
                           hipStream_t stream);
 
+// Query rows b = 0 .. batch-1 each hold Hq query heads; row b belongs to
+// request b / tq (tq query tokens per request; 1 for decode).  The pages of
+// a (row, KV head) are reduced in `splits` runs; `parts` partial rows are
+// merged per (row, KV head): the splits, plus one for the bf16 tail page
+// when there is one.
 struct AttnShape {
-  int batch;
+  int batch;         // query rows (requests * tq)
+  int tq;            // query tokens per request
   int heads;         // KV heads H
   int q_heads;       // Hq
   int group;         // Hq / H
   int max_pages;     // per request
   int pages_per_split;
   int splits;
+  int parts;         // partial rows merged per (row, KV head)
   long long pool_pages;  // pages in the k / v pools (block-table bound)
 };
 
 AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages);
+// Shape of `requests` requests with tq query tokens each over their pages
+// and a bf16 tail page.
+AttnShape attention_shape_tail(int requests, int tq, int heads, int q_heads, int max_pages);
 size_t attention_workspace_bytes(const AttnShape &s);
 
 bool attention_mfma_supported(int group);
 int attention_mfma_target_blocks();
-// Writes `out` itself (the split partials are merged inside the launch).
+// Page runs of every (row, KV head): writes `out` itself when parts == 1,
+// else the split partials.  With merge set and parts > 1 the partials are
+// merged into `out` inside the launch.
 hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
                                  const int32_t *block_table, const int32_t *seq_lens,
                                  const AttnShape &s, float sm_scale, bool full, float *out,
-                                 float *scores, void *workspace, hipStream_t stream);
+                                 float *scores, void *workspace, bool merge, hipStream_t stream);
+hipError_t launch_attention_mfma_combine(const AttnShape &s, const void *workspace, float *out,
+                                         hipStream_t stream);
+
+// bf16 tail page of each request (tail_k / tail_v [requests][tail_cap][H][128],
+// tail_len [requests] on the device): query token i of a request sees tail
+// tokens 0 .. tail_len - tq + i.  Writes partial row `s.splits` of every
+// (row, KV head); base2 selects the maxima convention of the page kernels
+// (base-2 scores for the matrix-core kernel, natural ones otherwise).
+hipError_t launch_attention_tail_part(const uint16_t *q, const uint16_t *tail_k,
+                                      const uint16_t *tail_v, const int32_t *tail_len,
+                                      int tail_cap, const AttnShape &s, float sm_scale, bool base2,
+                                      void *workspace, hipStream_t stream);
 
 hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
                             const PlanesArg &v, const int32_t *block_table,
@@ -113,5 +137,14 @@ hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
                             float sm_scale, bool full, float *out,
                             float *scores, void *workspace,
                             hipStream_t stream);
+
+// Pages plus the bf16 tail page, merged into out [batch][Hq][128]
+// (s from attention_shape_tail).
+hipError_t launch_attention_with_tail(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
+                                      const int32_t *block_table, const int32_t *page_tokens,
+                                      const uint16_t *tail_k, const uint16_t *tail_v,
+                                      const int32_t *tail_len, int tail_cap, const AttnShape &s,
+                                      float sm_scale, bool full, float *out, void *workspace,
+                                      hipStream_t stream);
 
 }  // namespace lynx

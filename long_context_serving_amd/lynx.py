@@ -20,6 +20,8 @@ CHUNK = 32
 CHUNKS = 8
 HEAD_DIM = 128
 MAX_GROUP = 16
+MAX_QUERY_TOKENS = 64
+TAIL_TOKENS = 320
 ROLE_KEY = 0
 ROLE_VALUE = 1
 
@@ -57,6 +59,13 @@ for _name in ("lynx_decode_attention_anchor", "lynx_decode_attention_full"):
     getattr(_lib, _name).argtypes = [_P, ctypes.POINTER(_CPlanes), ctypes.POINTER(_CPlanes), _P, _P,
                                      _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _P, _P, _P,
                                      _sz, _P]
+    getattr(_lib, _name).restype = ctypes.c_int
+_lib.lynx_verify_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+_lib.lynx_verify_attention_workspace_size.restype = _sz
+for _name in ("lynx_verify_attention", "lynx_draft_attention"):
+    getattr(_lib, _name).argtypes = [_P, _i32, ctypes.POINTER(_CPlanes), ctypes.POINTER(_CPlanes),
+                                     _P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _i32, _i64,
+                                     ctypes.c_float, _P, _P, _sz, _P]
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.lynx_status_string.argtypes = [ctypes.c_int]
 _lib.lynx_status_string.restype = ctypes.c_char_p
@@ -237,3 +246,72 @@ def decode_attention(q: torch.Tensor, k: Planes, v: Planes, max_pages: int, full
               _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream)),
            "lynx_decode_attention_%s" % ("full" if full else "anchor"))
     return out
+
+
+def alloc_verify_workspace(batch: int, tq: int, heads: int, q_heads: int, max_pages: int,
+                           device="cuda") -> torch.Tensor:
+    """Workspace for verify_attention (its contents need no initialisation)."""
+    n = _lib.lynx_verify_attention_workspace_size(batch, tq, heads, q_heads, HEAD_DIM, max_pages)
+    if n == 0:
+        raise ValueError("unsupported verify attention shape")
+    return torch.zeros((n + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def alloc_tail(batch: int, heads: int, device="cuda") -> torch.Tensor:
+    """bf16 tail buffer [B][TAIL_TOKENS][H][128] (as int16 bit patterns)."""
+    return torch.zeros((batch, TAIL_TOKENS, heads, HEAD_DIM), dtype=torch.int16, device=device)
+
+
+def verify_attention(q: torch.Tensor, k: Planes, v: Planes, max_pages: int,
+                     tail_k: torch.Tensor, tail_v: torch.Tensor, tail_len: torch.Tensor,
+                     full: bool = True, block_table: Optional[torch.Tensor] = None,
+                     page_tokens: Optional[torch.Tensor] = None,
+                     sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention of each request's tq newest tokens over its pages and bf16 tail.
+
+    q: bf16 [B][tq][Hq][128]; tail_k / tail_v: bf16 [B][TAIL_TOKENS][H][128];
+    tail_len: int32 [B] on the device.  full=True is the verify pass over
+    Q_full, full=False the draft (anchor plane only).  Returns fp32
+    [B][tq][Hq][128].
+    """
+    q = _bf16_bits(q)
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][tq][Hq][128] bf16 tensor")
+    B, tq, Hq, D = q.shape
+    H = k.heads
+    tk, tv = _bf16_bits(tail_k), _bf16_bits(tail_v)
+    for t in (tk, tv):
+        if tuple(t.shape) != (B, TAIL_TOKENS, H, HEAD_DIM) or not t.is_contiguous():
+            raise ValueError("tail tensors must be contiguous [B][%d][H][128] bf16" % TAIL_TOKENS)
+    if tail_len.dtype != torch.int32 or tail_len.numel() != B:
+        raise ValueError("tail_len must be int32 [B]")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, tq, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_verify_workspace(B, tq, H, Hq, max_pages, q.device)
+    fn = _lib.lynx_verify_attention if full else _lib.lynx_draft_attention
+    kc, vc = k.c(), v.c()
+    _check(fn(_ptr(q), tq, ctypes.byref(kc), ctypes.byref(vc), _ptr(block_table), _ptr(page_tokens),
+              _ptr(tk), _ptr(tv), _ptr(tail_len), B, H, Hq, D, max_pages,
+              min(k.num_pages, v.num_pages), float(sm_scale), _ptr(out), _ptr(workspace),
+              workspace.numel(), _stream(stream)),
+           "lynx_%s_attention" % ("verify" if full else "draft"))
+    return out
+
+
+def planes_view(p: Planes, first_page: int, num_pages: int) -> Planes:
+    """Planes of pages first_page .. first_page + num_pages - 1 of a pool
+    (views into the same memory; the layouts are page-major)."""
+    if first_page < 0 or num_pages < 0 or first_page + num_pages > p.num_pages:
+        raise ValueError("page range outside the pool")
+    tile = _lib.lynx_plane_bytes(1, p.heads)
+    a0, a1 = first_page * tile, (first_page + num_pages) * tile
+    return Planes(p.anchor[a0:a1], None if p.residual is None else p.residual[a0:a1],
+                  p.page_min[first_page:first_page + num_pages],
+                  p.page_range[first_page:first_page + num_pages],
+                  p.chunk_mean[first_page:first_page + num_pages],
+                  p.chunk_maxabs[first_page:first_page + num_pages],
+                  num_pages=num_pages, heads=p.heads, role=p.role)

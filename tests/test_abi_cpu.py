@@ -112,6 +112,37 @@ def test_argument_errors_are_reported_before_any_launch(lib):
         assert call(args(q=P(0x50002))) == -3
         assert call(args(B=0)) == 0                 # empty batch: no-op
 
+    lib.lynx_verify_attention_workspace_size.restype = ctypes.c_size_t
+    lib.lynx_verify_attention_workspace_size.argtypes = [ctypes.c_int32] * 6
+    vneed = lib.lynx_verify_attention_workspace_size(2, 4, 8, 64, 128, 16)
+    assert vneed > lib.lynx_decode_attention_workspace_size(2, 8, 64, 128, 16)
+    assert lib.lynx_verify_attention_workspace_size(2, 0, 8, 64, 128, 16) == 0    # tq < 1
+    assert lib.lynx_verify_attention_workspace_size(2, 65, 8, 64, 128, 16) == 0   # tq > 64
+    for name in ("lynx_verify_attention", "lynx_draft_attention"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, ctypes.c_int32, ctypes.POINTER(CPlanes), ctypes.POINTER(CPlanes), P, P, P,
+                       P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_int32, ctypes.c_int64, ctypes.c_float, P, P, ctypes.c_size_t, P]
+        q, out, ws, tk, tv, tl = (P(0x50000), P(0x60000), P(0x70000), P(0x80000), P(0x90000),
+                                  P(0xA0000))
+        args = lambda **kw: dict(dict(q=q, tq=4, bt=None, pt=None, tk=tk, tv=tv, tl=tl, B=2, H=8,
+                                      Hq=64, D=128, mp=16, pool=32, ws=ws, wsb=vneed), **kw)
+
+        def vcall(a):
+            return fn(a["q"], a["tq"], ctypes.byref(pl), ctypes.byref(pl), a["bt"], a["pt"], a["tk"],
+                      a["tv"], a["tl"], a["B"], a["H"], a["Hq"], a["D"], a["mp"], a["pool"], 0.088,
+                      out, a["ws"], a["wsb"], None)
+        assert vcall(args(q=None)) == -1
+        assert vcall(args(tk=None)) == -1
+        assert vcall(args(tl=None)) == -1
+        assert vcall(args(tq=0)) == -2
+        assert vcall(args(tq=65)) == -2
+        assert vcall(args(D=96)) == -2
+        assert vcall(args(pool=31)) == -2
+        assert vcall(args(wsb=vneed - 1)) == -4
+        assert vcall(args(tv=P(0x90008))) == -3
+        assert vcall(args(B=0)) == 0
+
 
 def test_status_strings(lib):
     lib.lynx_status_string.restype = ctypes.c_char_p
