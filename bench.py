@@ -146,31 +146,42 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, xk, xv, qb, pages, sm):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(w, xk, xv, qb, pages, sm, min_seconds=10.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    the sample (encode K and V, then anchor and full decode) is repeated
+    until at least min_seconds of CPU time have passed, and the rate is the
+    average over the passes."""
     import oracle
     nt = oracle.max_threads()
     xk, xv = xk[:pages], xv[:pages]
-    t0 = time.perf_counter()
-    ek, ev = oracle.encode(xk), oracle.encode(xv)
-    t1 = time.perf_counter()
     q = oracle.bf16_bits_to_float(qb).astype(np.float64)
-    ak, rk = oracle.split(ek["codes"])
-    av, rv = oracle.split(ev["codes"])
-    for full in (False, True):
-        kh = oracle.dequant(ak, rk if full else None, ek).reshape(1, -1, w.kv_heads, w.head_dim)
-        vh = oracle.dequant(av, rv if full else None, ev).reshape(1, -1, w.kv_heads, w.head_dim)
-        oracle.attention(q[:1], kh, vh, sm)
-    t2 = time.perf_counter()
+    t_enc = t_dec = 0.0
+    passes = 0
+    while passes == 0 or t_enc + t_dec < min_seconds:
+        t0 = time.perf_counter()
+        ek, ev = oracle.encode(xk), oracle.encode(xv)
+        t1 = time.perf_counter()
+        ak, rk = oracle.split(ek["codes"])
+        av, rv = oracle.split(ev["codes"])
+        for full in (False, True):
+            kh = oracle.dequant(ak, rk if full else None, ek).reshape(1, -1, w.kv_heads, w.head_dim)
+            vh = oracle.dequant(av, rv if full else None, ev).reshape(1, -1, w.kv_heads, w.head_dim)
+            oracle.attention(q[:1], kh, vh, sm)
+        t2 = time.perf_counter()
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+        passes += 1
     elems = pages * 256 * w.kv_heads * w.head_dim
     qo = w.q_heads * w.head_dim * 6
     nbytes = 2 * elems * 3.28125 + 2 * elems * (1.28125 + 0.78125) + 2 * qo
     return {
-        "value": nbytes / (t2 - t0) / 1e9, "unit": "GB/s", "cores": nt, "kind": "oracle",
-        "sample": "%d of %d pages of one request (K and V): encode, then anchor and full "
-                  "dequant + brute-force attention for all %d query heads; encode %.2f s, "
-                  "decode %.2f s" % (pages, w.pages, w.q_heads, t1 - t0, t2 - t1),
-        "seconds": t2 - t0,
+        "value": passes * nbytes / (t_enc + t_dec) / 1e9, "unit": "GB/s", "cores": nt,
+        "kind": "oracle",
+        "sample": "%d passes over %d of %d pages of one request (K and V): encode, then anchor "
+                  "and full dequant + brute-force attention for all %d query heads; per pass "
+                  "encode %.2f s, decode %.2f s" % (passes, pages, w.pages, w.q_heads,
+                                                    t_enc / passes, t_dec / passes),
+        "seconds": t_enc + t_dec,
     }
 
 
@@ -233,6 +244,56 @@ def progressive_main(args):
     print(json.dumps(result), flush=True)
 
 
+def verify_leg(args, w, sets, dev, sm, stream):
+    """Verify pass after the timed region: the newest tq tokens of the
+    request (its speculative tokens) attend to the full planes of every
+    buffer set in turn (cache-cold) plus a bf16 tail of tq + 36 tokens."""
+    import torch
+    from long_context_serving_amd import lynx, synth
+    tq = args.verify_tq
+    tail_len = tq + 36
+    rng = np.random.default_rng(4242)
+    tail = lambda: torch.from_numpy(synth.float_to_bf16_bits(
+        rng.laplace(0, 1, (w.batch, lynx.TAIL_TOKENS, w.kv_heads, w.head_dim)).astype(np.float32))
+        .view(np.int16)).to(dev)
+    tk, tv = tail(), tail()
+    tl = torch.full((w.batch,), tail_len, dtype=torch.int32, device=dev)
+    qv = torch.from_numpy(synth.float_to_bf16_bits(
+        rng.laplace(0, 1, (w.batch, tq, w.q_heads, w.head_dim)).astype(np.float32)).view(np.int16)).to(dev)
+    out = torch.empty((w.batch, tq, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = lynx.alloc_verify_workspace(w.batch, tq, w.kv_heads, w.q_heads, w.pages, dev)
+    calls = [lambda e=e: lynx.verify_attention(qv, e["pk"], e["pv"], w.pages, tk, tv, tl, full=True,
+                                               sm_scale=sm, out=out, workspace=ws) for e in sets]
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.verify_reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (args.verify_reps * len(calls))
+    ctx = w.tokens + tail_len - tq  # cached tokens before the speculative ones
+    # score and value products of every query row with every visible token
+    flops = 4.0 * w.batch * w.q_heads * w.head_dim * sum(ctx + i + 1 for i in range(tq))
+    plane_bytes = algorithmic_bytes(w)["decode_full"]
+    return {"tq": tq, "tail_tokens": tail_len, "us_per_call": ms * 1e3,
+            "speculative_tokens_per_s": w.batch * tq / (ms * 1e-3),
+            "algorithmic_TFLOPs": flops / (ms * 1e-3) / 1e12,
+            "frac_of_fp16_mfma_peak": flops / (ms * 1e-3) / 2.5e15,
+            "plane_GBps": plane_bytes / (ms * 1e-3) / 1e9,
+            "timing": "events around graph replays of one call per buffer set, after the timed region"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +308,12 @@ def main():
     ap.add_argument("--progressive", action="store_true",
                     help="run the progressive plane-streaming harness (32 layers x 64K) instead")
     ap.add_argument("--stream-runs", type=int, default=3)
+    ap.add_argument("--no-verify", dest="verify", action="store_false",
+                    help="skip the verify-pass measurement (64 speculative tokens over the planes)")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="encode the buffer sets, then time the verify pass alone")
+    ap.add_argument("--verify-tq", type=int, default=64)
+    ap.add_argument("--verify-reps", type=int, default=4)
     ap.add_argument("--summarize", nargs=4, metavar=("KIND", "DB_DIR", "OUT", "COMMAND"),
                     help="write a text summary of rocprofv3 output (KIND kt or pmc; for pmc "
                          "DB_DIR is '<FETCH_SIZE dir>,<WRITE_SIZE dir>') and exit")
@@ -314,10 +381,18 @@ def main():
                                                            sm_scale=sm, out=out, workspace=ws))
         full_calls.append(lambda e=e: lynx.decode_attention(q, e["pk"], e["pv"], w.pages, full=True,
                                                             sm_scale=sm, out=out, workspace=ws))
+    stream = torch.cuda.Stream()
+    if args.verify_only:
+        # only the verify pass (its kernels share names with the decode ones)
+        for call in enc_calls:
+            call()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": w.name, "verify": verify_leg(args, w, sets, dev, sm, stream)}),
+              flush=True)
+        return
     for call in enc_calls + anc_calls + full_calls:  # eager pass
         call()
     torch.cuda.synchronize()
-    stream = torch.cuda.Stream()
 
     def capture(calls):
         g = torch.cuda.CUDAGraph()
@@ -354,6 +429,8 @@ def main():
     phase_ms = [sum(evs[r][p].elapsed_time(evs[r][p + 1]) for r in range(rounds)) for p in range(3)]
     per_call_ms = {"encode": phase_ms[0] / (2 * K), "decode_anchor": phase_ms[1] / K,
                    "decode_full": phase_ms[2] / K}
+
+    verify = verify_leg(args, w, sets, dev, sm, stream) if args.verify else None
 
     if args.copy_probe:
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -402,6 +479,8 @@ def main():
                      "traffic": measured_traffic(), "algorithmic_bytes": ab["encode"]},
         "wall_s_timed": wall,
     }
+    if verify is not None:
+        result["verify"] = verify
     if args.cpu:
         log("bench: CPU baseline (oracle) on %d pages" % args.cpu_pages)
         result["cpu_baseline"] = cpu_baseline(w, xk0, xv0, qb, min(args.cpu_pages, w.pages), sm)
