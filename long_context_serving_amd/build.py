@@ -22,10 +22,11 @@ SOURCES = ["lynx_tables.cpp", "lynx_api.cpp", "lynx_encode.hip", "lynx_dequant.h
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",
           "-I", INCLUDE]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source flags.  The encoder's input is finite by contract; without NaN
-# semantics its min/max need no canonicalising instructions (the named fp32
-# operations and their rounding are unchanged).
-EXTRA = {"lynx_encode.hip": ["-fno-honor-nans"]}
+# Per-source flags.  The encoder's and the matrix-core attention's inputs are
+# finite by contract; without NaN semantics their min/max need no
+# canonicalising instructions (every operation and its rounding are
+# unchanged; infinities keep their meaning).
+EXTRA = {"lynx_encode.hip": ["-fno-honor-nans"], "lynx_attention_mfma.hip": ["-fno-honor-nans"]}
 
 
 def sources():

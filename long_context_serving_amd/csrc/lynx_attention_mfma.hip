@@ -110,14 +110,19 @@ __device__ __forceinline__ float ror8_to_lo(float keep, float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
       __builtin_bit_cast(int, keep), __builtin_bit_cast(int, x), 0x128, 0xF, 0x3, false));
 }
+// (a rotation within the row reads a valid lane for every lane, so the
+// destination needs no previous value)
+template <int kCtrl>
+__device__ __forceinline__ int dpp_all(int x) {
+  return __builtin_amdgcn_mov_dpp(x, kCtrl, 0xF, 0xF, true);
+}
 __device__ __forceinline__ float ror8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-      0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, dpp_all<0x128>(__builtin_bit_cast(int, x)));
 }
 __device__ __forceinline__ double ror8(double x) {
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x128, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), 0x128, 0xF, 0xF, false);
+  const int lo = dpp_all<0x128>(static_cast<int>(u));
+  const int hi = dpp_all<0x128>(static_cast<int>(u >> 32));
   return __builtin_bit_cast(double, static_cast<uint64_t>(static_cast<uint32_t>(lo)) |
                                         (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32));
 }
@@ -149,9 +154,9 @@ struct SumOp { __device__ float operator()(float a, float b) const { return a + 
 
 // max over all 64 lanes
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, dpp_all<0xB1>(__builtin_bit_cast(int, v))));
+  v = fmaxf(v, __builtin_bit_cast(float, dpp_all<0x4E>(__builtin_bit_cast(int, v))));
+  v = fmaxf(v, __builtin_bit_cast(float, dpp_all<0x124>(__builtin_bit_cast(int, v))));
   v = fmaxf(v, ror8(v));
   return xrows(v, MaxOp());
 }
