@@ -222,6 +222,20 @@ def progressive_main(args):
     bf16_all = statistics.median(bf16_ms[1:])
     overlap = ps.draft_full_topk_overlap((1, 16, 64))
     ab, rb = ps.anchor_bytes(), ps.residual_bytes()
+    # the same schedules on an emulated inter-server link (one run per rate)
+    paced = {}
+    for gbps in [float(x) for x in args.link_gbps.split(",") if x]:
+        log("bench: emulated link at %g Gbps" % gbps)
+        link = stream.PacedLink(gbps, ps.copy_stream)
+        lp = ps.paced_progressive(link)
+        li = ps.paced_layerwise_int8(link)
+        lb = ps.paced_bf16(link, hb, db)
+        paced["%g" % gbps] = {
+            "lynx": lp, "lynx_int8_layerwise": li, "bf16_layerwise": lb,
+            "first_draft_vs_int8_first_layer": li["first_full_layer_ms"] / lp["first_draft_ms"],
+            "first_draft_vs_bf16_first_layer": lb["first_layer_landed_ms"] / lp["first_draft_ms"],
+            "all_drafts_vs_int8_all_layers": li["all_full_ms"] / lp["all_drafts_ms"],
+        }
     a_ms, r_ms = med(prog, "anchors_landed_ms"), med(prog, "residuals_landed_ms")
     result = {
         "metric": "progressive plane streaming: time to all drafts / all full attention (ms), 1xMI355X",
@@ -240,6 +254,9 @@ def progressive_main(args):
         "lynx_int8_layerwise": {k: med(int8, k) for k in int8[0]},
         "bf16_copy_all_layers_ms": bf16_all,
         "draft_vs_full_topk_overlap": {str(k): v for k, v in overlap.items()},
+        "emulated_link": {"pacing": "pieces of 4 MiB released on the host at cumulative bytes / rate; "
+                                    "times from an event at the link's start",
+                          "by_gbps": paced},
     }
     print(json.dumps(result), flush=True)
 
@@ -308,6 +325,8 @@ def main():
     ap.add_argument("--progressive", action="store_true",
                     help="run the progressive plane-streaming harness (32 layers x 64K) instead")
     ap.add_argument("--stream-runs", type=int, default=3)
+    ap.add_argument("--link-gbps", default="10,25,50",
+                    help="emulated link rates for the progressive timeline (empty: none)")
     ap.add_argument("--no-verify", dest="verify", action="store_false",
                     help="skip the verify-pass measurement (64 speculative tokens over the planes)")
     ap.add_argument("--verify-only", action="store_true",

@@ -21,6 +21,7 @@ cache (its attention is not part of this library; only the copy is timed).
 Everything here is orchestration of copies, events and calls into liblynx:
 the arithmetic runs in the HIP kernels.
 """
+import time
 from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
 
@@ -60,6 +61,47 @@ def copy_planes(dst: lynx.Planes, src: lynx.Planes, anchor: bool, residual: bool
 
 def planes_bytes(p: lynx.Planes, anchor: bool, residual: bool) -> int:
     return sum(t.numel() * t.element_size() for t in _planes_tensors(p, anchor, residual))
+
+
+class PacedLink:
+    """An emulated link of `gbps` gigabits per second from pinned host memory
+    to the GPU (page "Lynx: the KV cache does not have to arrive whole",
+    section 5: the benefit is measured at 10-50 Gbps between servers).
+
+    Copies are cut into pieces; a piece is released to the copy stream only
+    when the emulated link would have delivered its last byte (start time +
+    cumulative bytes / rate), the host waiting for that moment.  The PCIe
+    copy that follows is 5-40x faster than the emulated rates, so a piece
+    lands shortly after its release time.
+    """
+
+    def __init__(self, gbps: float, copy_stream: torch.cuda.Stream, piece_bytes: int = 4 << 20):
+        self.rate = gbps * 1e9 / 8.0
+        self.piece = piece_bytes
+        self.stream = copy_stream
+        self.sent = 0
+        self.t0 = 0.0
+
+    def start(self, event: torch.cuda.Event):
+        """Begin the link's clock; `event` is recorded on the copy stream at
+        the same moment (the reference of every reported time)."""
+        torch.cuda.synchronize()
+        self.sent = 0
+        event.record(self.stream)
+        self.t0 = time.perf_counter()
+
+    def send(self, dst: torch.Tensor, src: torch.Tensor):
+        d, s = dst.view(-1), src.view(-1)
+        es = s.element_size()
+        step = max(1, self.piece // es)
+        with torch.cuda.stream(self.stream):
+            for a in range(0, s.numel(), step):
+                b = min(s.numel(), a + step)
+                self.sent += (b - a) * es
+                release = self.t0 + self.sent / self.rate
+                while time.perf_counter() < release:
+                    pass
+                d[a:b].copy_(s[a:b], non_blocking=True)
 
 
 @dataclass
@@ -178,6 +220,66 @@ class ProgressiveStream:
         torch.cuda.synchronize(self.device)
         return {"first_layer_ms": start.elapsed_time(done[0]),
                 "all_full_ms": start.elapsed_time(done[-1]),
+                "all_landed_ms": start.elapsed_time(landed[-1])}
+
+    # -- schedules on an emulated link -----------------------------------
+    def paced_progressive(self, link: PacedLink) -> Dict[str, float]:
+        """Anchor-first streaming over the emulated link; drafts run as each
+        layer's anchors land, full attention as its residual lands."""
+        n = len(self.layers)
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        start, a_in, r_in = ev(), [ev() for _ in range(n)], [ev() for _ in range(n)]
+        d_end, f_end = [ev() for _ in range(n)], [ev() for _ in range(n)]
+        link.start(start)
+        for phase, (anchor, residual, landed, done, full) in enumerate(
+                ((True, False, a_in, d_end, False), (False, True, r_in, f_end, True))):
+            for i, l in enumerate(self.layers):
+                for d, h in ((self.dev_k[i], l.host_k), (self.dev_v[i], l.host_v)):
+                    for dt, ht in zip(_planes_tensors(d, anchor, residual),
+                                      _planes_tensors(h, anchor, residual)):
+                        link.send(dt, ht)
+                landed[i].record(self.copy_stream)
+                self.compute_stream.wait_event(landed[i])
+                self._attend(i, full=full)
+                done[i].record(self.compute_stream)
+        torch.cuda.synchronize(self.device)
+        t = lambda e: start.elapsed_time(e)
+        return {"first_draft_ms": t(d_end[0]), "all_drafts_ms": t(d_end[-1]),
+                "anchors_landed_ms": t(a_in[-1]), "first_full_layer_ms": t(f_end[0]),
+                "all_full_ms": t(f_end[-1]), "residuals_landed_ms": t(r_in[-1])}
+
+    def paced_layerwise_int8(self, link: PacedLink) -> Dict[str, float]:
+        """Lynx-INT8 layer-wise over the emulated link: each layer's complete
+        planes, then its full attention."""
+        n = len(self.layers)
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        start, landed, done = ev(), [ev() for _ in range(n)], [ev() for _ in range(n)]
+        link.start(start)
+        for i, l in enumerate(self.layers):
+            for d, h in ((self.dev_k[i], l.host_k), (self.dev_v[i], l.host_v)):
+                for dt, ht in zip(_planes_tensors(d, True, True), _planes_tensors(h, True, True)):
+                    link.send(dt, ht)
+            landed[i].record(self.copy_stream)
+            self.compute_stream.wait_event(landed[i])
+            self._attend(i, full=True)
+            done[i].record(self.compute_stream)
+        torch.cuda.synchronize(self.device)
+        return {"first_full_layer_ms": start.elapsed_time(done[0]),
+                "all_full_ms": start.elapsed_time(done[-1])}
+
+    def paced_bf16(self, link: PacedLink, host_layer: torch.Tensor,
+                   dev_layer: torch.Tensor) -> Dict[str, float]:
+        """The raw bf16 cache (K and V of one layer per step) over the
+        emulated link; its attention is not part of this library."""
+        n = len(self.layers)
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        start, landed = ev(), [ev() for _ in range(n)]
+        link.start(start)
+        for i in range(n):
+            link.send(dev_layer, host_layer)
+            landed[i].record(self.copy_stream)
+        torch.cuda.synchronize(self.device)
+        return {"first_layer_landed_ms": start.elapsed_time(landed[0]),
                 "all_landed_ms": start.elapsed_time(landed[-1])}
 
     def draft_full_topk_overlap(self, ks: Sequence[int] = (1, 16, 64)) -> Dict[int, float]:

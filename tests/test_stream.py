@@ -94,3 +94,50 @@ def test_progressive_stream_small():
 
     ov = ps.draft_full_topk_overlap((1, 16))
     assert all(0.0 <= v <= 1.0 for v in ov.values())
+
+
+@pytest.mark.gpu
+def test_paced_link_timeline():
+    """Throttled link (10 Gbps): the planes land when the link would have
+    delivered them, in the order of each schedule, and arrive intact."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_serving_amd import lynx, stream, synth
+
+    w = synth.WORKLOADS["progressive32x64k"]
+    L, T, gbps = 3, 4096, 10.0
+    print("paced link: %d layers x %d tokens at %.0f Gbps" % (L, T, gbps), flush=True)
+    layers = stream.build_layers(w, device="cuda", layers=L, tokens=T)
+    ps = stream.ProgressiveStream(layers, device="cuda", sm_scale=SM)
+    link = stream.PacedLink(gbps, ps.copy_stream, piece_bytes=1 << 20)
+    rate = gbps * 1e9 / 8 / 1e3  # bytes per ms
+    ab, rb = ps.anchor_bytes(), ps.residual_bytes()
+    # the start event runs on the GPU a little after the host starts the
+    # link's clock, so lower bounds get a small allowance
+    lo = lambda nbytes: 0.98 * nbytes / rate - 0.3
+
+    p = ps.paced_progressive(link)
+    print("progressive:", p, flush=True)
+    # the anchors of every layer take ab / rate on the link, then the residuals
+    assert lo(ab) <= p["anchors_landed_ms"] <= 1.25 * ab / rate + 3.0
+    assert lo(ab + rb) <= p["residuals_landed_ms"] <= 1.25 * (ab + rb) / rate + 3.0
+    assert p["first_draft_ms"] <= p["all_drafts_ms"] <= p["first_full_layer_ms"] <= p["all_full_ms"]
+    for i, l in enumerate(layers):
+        ref = lynx.decode_attention(l.q, ps.dev_k[i], ps.dev_v[i], ps.pages, full=True, sm_scale=SM)
+        torch.cuda.synchronize()
+        assert torch.equal(ps.out_full[i], ref)
+
+    i8 = ps.paced_layerwise_int8(link)
+    print("int8 layer-wise:", i8, flush=True)
+    assert lo((ab + rb) / L) <= i8["first_full_layer_ms"] <= i8["all_full_ms"]
+    assert lo(ab + rb) <= i8["all_full_ms"]
+
+    bf16_layer = 2 * T * w.kv_heads * 128 * 2
+    hb = torch.zeros(bf16_layer, dtype=torch.uint8, pin_memory=True)
+    db = torch.empty(bf16_layer, dtype=torch.uint8, device="cuda")
+    bf = ps.paced_bf16(link, hb, db)
+    print("bf16 layer-wise:", bf, flush=True)
+    assert lo(L * bf16_layer) <= bf["all_landed_ms"] <= 1.25 * L * bf16_layer / rate + 3.0
+    # the first draft needs a layer's anchors, the first full INT8 layer its
+    # whole planes, the first bf16 layer twice the INT8 bytes and more
+    assert p["first_draft_ms"] < i8["first_full_layer_ms"] < bf["first_layer_landed_ms"]
