@@ -86,17 +86,19 @@ __device__ __forceinline__ void store_stream(float *p, float4 v) {
 }
 
 // Reductions over the 4 lanes of a quad (lanes 4j .. 4j+3 share their
-// channels): two DPP quad permutations, which fold into the reducing op.
+// channels): two DPP quad permutations, which fold into the reducing op.  A
+// quad permutation reads a lane of the same quad for every lane, so the
+// destination needs no previous value.
 template <int kCtrl>
 __device__ __forceinline__ float quad_perm(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
-                                                               0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl,
+                                                            0xF, 0xF, true));
 }
 template <int kCtrl>
 __device__ __forceinline__ double quad_perm(double v) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), kCtrl, 0xF, 0xF, false));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), kCtrl, 0xF, 0xF, false));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), kCtrl, 0xF, 0xF, true));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), kCtrl, 0xF, 0xF, true));
   return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
 }
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
@@ -269,9 +271,10 @@ void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, En
       const float inv_rg[8] = {iv0.x, iv0.y, iv0.z, iv0.w, iv1.x, iv1.y, iv1.z, iv1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        double sum = 0.0;
+        x[0][i] = (x[0][i] - mn[i]) * inv_rg[i];
+        double sum = static_cast<double>(x[0][i]);  // (x' >= 0: no signed zero to keep)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 1; j < 8; ++j) {
           x[j][i] = (x[j][i] - mn[i]) * inv_rg[i];
           sum += static_cast<double>(x[j][i]);
         }
