@@ -53,6 +53,12 @@ def _load():
     lib.oracle_attention.argtypes = [P, P, P, i32, i64, i32, i32, i32,
                                      ctypes.c_double, P, P, i32]
     lib.oracle_attention.restype = i32
+    lib.oracle_split_bits.argtypes = [P, i64, i32, P, P]
+    lib.oracle_split_bits.restype = i32
+    lib.oracle_join_bits.argtypes = [P, P, i64, i32, P]
+    lib.oracle_join_bits.restype = i32
+    lib.oracle_dequant_bits.argtypes = [P, P, i32, P, P, P, P, i64, i32, i32, P, i32]
+    lib.oracle_dequant_bits.restype = i32
     lib.oracle_prefix_attention.argtypes = [P, P, P, P, i32, i32, i64, i32, i32, i32,
                                             ctypes.c_double, P, i32]
     lib.oracle_prefix_attention.restype = i32
@@ -179,6 +185,43 @@ def attention(q, k, v, sm_scale: float, want_logits: bool = False, nthreads: int
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments")
     return (out, logits) if want_logits else out
+
+
+def split_bits(q, anchor_bits: int):
+    """A b + (8 - b) cut of the 8-bit codes: (anchor int8, residual uint8)."""
+    q = _c(q, np.int8)
+    a = np.empty(q.shape, np.int8)
+    r = np.empty(q.shape, np.uint8)
+    if _load().oracle_split_bits(_ptr(q), q.size, anchor_bits, _ptr(a), _ptr(r)) != 0:
+        raise ValueError("anchor_bits must be 1 .. 8")
+    return a, r
+
+
+def join_bits(anchor, residual, anchor_bits: int):
+    """Full code (residual given) or draft code (residual None) of a cut."""
+    a = _c(anchor, np.int8)
+    r = None if residual is None else _c(residual, np.uint8)
+    q = np.empty(a.shape, np.int32)
+    if _load().oracle_join_bits(_ptr(a), _ptr(r), a.size, anchor_bits, _ptr(q)) != 0:
+        raise ValueError("anchor_bits must be 1 .. 8")
+    return q
+
+
+def dequant_bits(anchor, residual, anchor_bits: int, scales, nthreads: int = 0):
+    """xhat (float64 [P][256][H][D]) of a b + (8 - b) cut; residual None = draft."""
+    a = _c(anchor, np.int8)
+    r = None if residual is None else _c(residual, np.uint8)
+    P, _, H, D = a.shape
+    pm = _c(scales["page_min"], np.float32)
+    pr = _c(scales["page_range"], np.float32)
+    cm = _c(scales["chunk_mean"], np.float32)
+    cs = _c(scales["chunk_maxabs"], np.float32)
+    out = np.empty(a.shape, np.float64)
+    rc = _load().oracle_dequant_bits(_ptr(a), _ptr(r), anchor_bits, _ptr(pm), _ptr(pr), _ptr(cm),
+                                     _ptr(cs), P, H, D, _ptr(out), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_dequant_bits rejected its arguments")
+    return out
 
 
 def prefix_attention(q, k, v, visible, sm_scale: float, nthreads: int = 0):

@@ -282,6 +282,45 @@ void oracle_join(const int8_t *anchor, const uint8_t *residual, int64_t n,
 }
 
 /* ---------------------------------------------------------------------------
+ * Other cuts of the 8-bit code (section 3 cuts it 4 + 4; section 7 of the
+ * page lists 6 + 2, 2 + 6 and 5 + 3 as untried).  A b + (8 - b) cut keeps
+ * the top b bits as the anchor (arithmetic shift: -2^(b-1) .. 2^(b-1) - 1)
+ * and the low 8 - b bits as the residual; the draft code of anchor a is
+ * a * 2^(8-b) + 2^(7-b) - 1, the round-half-down centre of the anchor's
+ * 2^(8-b) codes (16 a + 7 for the 4 + 4 cut; the anchor itself for 8 + 0).
+ * ------------------------------------------------------------------------- */
+static int draft_offset(int anchor_bits)
+{
+    const int rb = 8 - anchor_bits;
+    return rb > 0 ? (1 << (rb - 1)) - 1 : 0;
+}
+
+int32_t oracle_split_bits(const int8_t *q, int64_t n, int32_t anchor_bits,
+                          int8_t *anchor, uint8_t *residual)
+{
+    if (anchor_bits < 1 || anchor_bits > 8) return -1;
+    const int rb = 8 - anchor_bits;
+    for (int64_t i = 0; i < n; ++i) {
+        const int v = q[i];
+        anchor[i] = (int8_t)(v >> rb);
+        residual[i] = (uint8_t)(v & ((1 << rb) - 1));
+    }
+    return 0;
+}
+
+/* Full code a * 2^(8-b) + r; draft code with the centre (residual NULL). */
+int32_t oracle_join_bits(const int8_t *anchor, const uint8_t *residual,
+                         int64_t n, int32_t anchor_bits, int32_t *q)
+{
+    if (anchor_bits < 1 || anchor_bits > 8) return -1;
+    const int rb = 8 - anchor_bits;
+    const int mid = draft_offset(anchor_bits);
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = (int32_t)anchor[i] * (1 << rb) + (residual ? (int32_t)residual[i] : mid);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Dequantizer.  anchor int8 [P][256][H][D] in -8..7; residual uint8 same
  * shape in 0..15, or NULL for the anchor-only (draft) reconstruction.
  * Scales as written by oracle_encode.  Output double [P][256][H][D].
@@ -315,6 +354,47 @@ int32_t oracle_dequant(const int8_t *anchor, const uint8_t *residual,
                          (double)page_range[sidx] *
                              ((double)chunk_mean[cidx] +
                               (double)chunk_maxabs[cidx] * yh);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Dequantizer of a b + (8 - b) cut: anchor int8 [P][256][H][D] in
+ * -2^(b-1) .. 2^(b-1) - 1; residual uint8 in 0 .. 2^(8-b) - 1, or NULL for
+ * the draft.  Same scales and output as oracle_dequant.
+ * ------------------------------------------------------------------------- */
+int32_t oracle_dequant_bits(const int8_t *anchor, const uint8_t *residual,
+                            int32_t anchor_bits, const float *page_min,
+                            const float *page_range, const float *chunk_mean,
+                            const float *chunk_maxabs, int64_t num_pages,
+                            int32_t H, int32_t D, double *out, int32_t nthreads)
+{
+    if (!anchor || !page_min || !page_range || !chunk_mean || !chunk_maxabs ||
+        !out || num_pages < 0 || H < 1 || D < 1 || anchor_bits < 1 ||
+        anchor_bits > 8)
+        return -1;
+    const int rb = 8 - anchor_bits;
+    const int mid = draft_offset(anchor_bits);
+    const int64_t row = (int64_t)H * D;
+    const int64_t units = num_pages * OR_PAGE;
+    const int nt = nthreads_or_default(nthreads);
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t p = u / OR_PAGE;
+        const int t = (int)(u % OR_PAGE);
+        const int c = t / OR_CHUNK;
+        for (int32_t h = 0; h < H; ++h) {
+            for (int32_t d = 0; d < D; ++d) {
+                const int64_t e = u * row + (int64_t)h * D + d;
+                const int q = (int)anchor[e] * (1 << rb) + (residual ? (int)residual[e] : mid);
+                const int64_t sidx = (p * H + h) * (int64_t)D + d;
+                const int64_t cidx = ((p * H + h) * OR_NCHUNK + c) * (int64_t)D + d;
+                out[e] = (double)page_min[sidx] +
+                         (double)page_range[sidx] *
+                             ((double)chunk_mean[cidx] +
+                              (double)chunk_maxabs[cidx] * yhat_of(q));
             }
         }
     }

@@ -433,6 +433,53 @@ def test_attention_special_cases():
 
 
 # ---------------------------------------------------------------------------
+# Pin 9b: other cuts of the 8-bit code (b + (8 - b))
+# ---------------------------------------------------------------------------
+def test_other_cuts_split_join_and_draft_centre():
+    q = np.arange(-128, 128).astype(np.int8)
+    for b in range(1, 9):
+        a, r = oracle.split_bits(q, b)
+        rb = 8 - b
+        # a lossless cut: anchor and residual give the code back
+        np.testing.assert_array_equal(oracle.join_bits(a, r, b), q.astype(np.int32))
+        assert a.min() == -(1 << (b - 1)) and a.max() == (1 << (b - 1)) - 1
+        assert r.max() == (1 << rb) - 1
+        # the draft is the round-half-down centre of the anchor's codes
+        lo = a.astype(np.int64) * (1 << rb)
+        hi = lo + (1 << rb) - 1
+        d = oracle.join_bits(a, None, b)
+        np.testing.assert_array_equal(d, np.floor((lo + hi) / 2).astype(np.int64))
+        assert (np.diff(d) >= 0).all()
+    # b = 4 is the page's cut (+7 centre)
+    a4, r4 = oracle.split(q)
+    a, r = oracle.split_bits(q, 4)
+    np.testing.assert_array_equal(a, a4)
+    np.testing.assert_array_equal(r, r4)
+    np.testing.assert_array_equal(oracle.join_bits(a, None, 4), 16 * a4.astype(np.int32) + 7)
+
+
+def test_other_cuts_dequant():
+    x = synth.laplace_pages(2, 2, 16, seed=31, scale_channels=((1, 3, 60.0),))
+    enc = oracle.encode(x)
+    a4, r4 = oracle.split(enc["codes"])
+    full = oracle.dequant(a4, r4, enc)
+    draft4 = oracle.dequant(a4, None, enc)
+    for b in range(1, 9):
+        a, r = oracle.split_bits(enc["codes"], b)
+        # the full reconstruction does not depend on the cut
+        np.testing.assert_array_equal(oracle.dequant_bits(a, r, b, enc), full)
+        d = oracle.dequant_bits(a, None, b, enc)
+        if b == 4:
+            np.testing.assert_array_equal(d, draft4)
+        if b == 8:
+            np.testing.assert_array_equal(d, full)
+    # more anchor bits, closer drafts (mean squared error against the full code)
+    err = [float(((oracle.dequant_bits(*oracle.split_bits(enc["codes"], b)[:1], None, b, enc) - full) ** 2).mean())
+           for b in range(1, 8)]
+    assert all(err[i + 1] < err[i] for i in range(6)), err
+
+
+# ---------------------------------------------------------------------------
 # Pin 10b: several query tokens over prefixes of the cache (the verify pass)
 # against torch's SDPA with an explicit mask (float64, CPU)
 # ---------------------------------------------------------------------------
