@@ -199,6 +199,42 @@ int lynx_decode_attention_full(const uint16_t *q, const lynx_planes *k,
                                void *stream);
 
 /*
+ * Other cuts of the 8-bit code (page "Lynx: the KV cache does not have to
+ * arrive whole", section 3 cuts it 4 + 4; section 7 names 6 + 2, 2 + 6 and
+ * 5 + 3 as untried).  A b + (8 - b) cut keeps the top b bits of each code as
+ * the anchor (two's complement, -2^(b-1) .. 2^(b-1) - 1) and the low 8 - b
+ * bits as the residual; the draft code of anchor a is
+ * a * 2^(8-b) + 2^(7-b) - 1, the round-half-down centre of its codes.
+ * Streams: element k of a (page, head) tile -- the k-th nibble of the
+ * tile's 4-bit planes, in their role-dependent order -- occupies bits
+ * k*b .. k*b + b - 1 (least significant first) of the tile's anchor stream
+ * and bits k*(8-b) .. of its residual stream; tiles follow each other
+ * page-major as in the 4-bit planes.
+ *   lynx_split_stream_bytes  bytes of one stream of `bits` bits per element
+ *                           for P pages x H heads (bits * 4096 per tile);
+ *                           0 for an invalid shape
+ *   lynx_split_planes        re-cut planes written by lynx_quantize_pages
+ *                           (anchor and residual read) into the two streams
+ *   lynx_dequantize_split    fp32 [P][256][H][128] from the streams: full
+ *                           (residual given; bit-identical to
+ *                           lynx_dequantize_full) or draft (residual NULL);
+ *                           only the four scale pointers of `scales` are read
+ * anchor_bits: 1 .. 7.  Pointers are device pointers, 16-byte aligned.
+ * P = 0 is a no-op.  Errors: NULL_ARG, BAD_SHAPE (also P*H*4 >= 2^31),
+ * BAD_ARG (anchor_bits, role), MISALIGNED, DEVICE, HIP.
+ */
+size_t lynx_split_stream_bytes(int64_t num_pages, int32_t num_kv_heads, int32_t bits);
+int lynx_split_planes(const lynx_planes *in, int64_t num_pages,
+                      int32_t num_kv_heads, int32_t head_dim,
+                      int32_t anchor_bits, uint8_t *anchor_out,
+                      uint8_t *residual_out, void *stream);
+int lynx_dequantize_split(const uint8_t *anchor, const uint8_t *residual,
+                          int32_t anchor_bits, const lynx_planes *scales,
+                          int64_t num_pages, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t role, float *out,
+                          void *stream);
+
+/*
  * Attention of the tq newest tokens of each request over its compact pages
  * and its bf16 tail (page "Lynx: the KV cache does not have to arrive
  * whole", section 4: drafts run on the anchor stream alone, the refined

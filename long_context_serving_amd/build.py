@@ -17,7 +17,8 @@ LIB = os.path.join(OUT_DIR, "liblynx.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["lynx_tables.cpp", "lynx_api.cpp", "lynx_encode.hip", "lynx_dequant.hip",
-           "lynx_attention.hip", "lynx_attention_mfma.hip", "lynx_tail.hip"]
+           "lynx_attention.hip", "lynx_attention_mfma.hip", "lynx_tail.hip",
+           "lynx_split.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",
           "-I", INCLUDE]

@@ -266,6 +266,59 @@ int lynx_decode_attention_full(const uint16_t *q, const lynx_planes *k, const ly
                           workspace_bytes, stream, true);
 }
 
+size_t lynx_split_stream_bytes(int64_t num_pages, int32_t num_kv_heads, int32_t bits) {
+  if (num_pages < 0 || num_kv_heads < 1 || bits < 1 || bits > 8) return 0;
+  return static_cast<size_t>(num_pages) * num_kv_heads * static_cast<size_t>(bits) * 4096u;
+}
+
+int lynx_split_planes(const lynx_planes *in, int64_t num_pages, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t anchor_bits, uint8_t *anchor_out,
+                      uint8_t *residual_out, void *stream) {
+  int rc = check_tile_shape(num_pages, num_kv_heads, head_dim, LYNX_ROLE_KEY);
+  if (rc) return rc;
+  if (num_pages * static_cast<int64_t>(num_kv_heads) * 4 > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
+  if (anchor_bits < 1 || anchor_bits > 7) return LYNX_ERR_BAD_ARG;
+  if (num_pages == 0) return LYNX_OK;
+  if (!in || !in->anchor || !in->residual || !anchor_out || !residual_out) return LYNX_ERR_NULL_ARG;
+  if (!aligned16(in->anchor) || !aligned16(in->residual) || !aligned16(anchor_out) ||
+      !aligned16(residual_out))
+    return LYNX_ERR_MISALIGNED;
+  rc = check_device();
+  if (rc) return rc;
+  const hipError_t e = lynx::launch_split_planes(to_arg(in), num_pages, num_kv_heads, anchor_bits,
+                                                 anchor_out, residual_out,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
+}
+
+int lynx_dequantize_split(const uint8_t *anchor, const uint8_t *residual, int32_t anchor_bits,
+                          const lynx_planes *scales, int64_t num_pages, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t role, float *out, void *stream) {
+  int rc = check_tile_shape(num_pages, num_kv_heads, head_dim, role);
+  if (rc) return rc;
+  if (num_pages * static_cast<int64_t>(num_kv_heads) * 4 > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
+  if (anchor_bits < 1 || anchor_bits > 7) return LYNX_ERR_BAD_ARG;
+  if (num_pages == 0) return LYNX_OK;
+  if (!anchor || !out || !scales || !scales->page_min || !scales->page_range ||
+      !scales->chunk_mean || !scales->chunk_maxabs)
+    return LYNX_ERR_NULL_ARG;
+  if (!aligned16(anchor) || (residual && !aligned16(residual)) || !aligned16(out) ||
+      !aligned16(scales->page_min) || !aligned16(scales->page_range) ||
+      !aligned16(scales->chunk_mean) || !aligned16(scales->chunk_maxabs))
+    return LYNX_ERR_MISALIGNED;
+  rc = check_device();
+  if (rc) return rc;
+  PlanesArg sc{};
+  sc.page_min = scales->page_min;
+  sc.page_range = scales->page_range;
+  sc.chunk_mean = scales->chunk_mean;
+  sc.chunk_maxabs = scales->chunk_maxabs;
+  const hipError_t e = lynx::launch_dequant_split(anchor, residual, anchor_bits, sc, num_pages,
+                                                  num_kv_heads, role, out,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
+}
+
 size_t lynx_verify_attention_workspace_size(int32_t batch, int32_t tq, int32_t num_kv_heads,
                                             int32_t num_q_heads, int32_t head_dim,
                                             int32_t max_pages_per_seq) {

@@ -90,6 +90,15 @@ hipError_t launch_dequant(const PlanesArg &in, int64_t num_pages, int heads,
 // a (row, KV head) are reduced in `splits` runs; `parts` partial rows are
 // merged per (row, KV head): the splits, plus one for the bf16 tail page
 // when there is one.
+// b + (8 - b) cuts: re-cut 4 + 4 planes into a b-bit anchor stream and an
+// (8 - b)-bit residual stream (b * 4096 and (8 - b) * 4096 bytes per tile),
+// and dequantize from such streams (residual NULL: the draft).
+hipError_t launch_split_planes(const PlanesArg &in, int64_t num_pages, int heads, int anchor_bits,
+                               uint8_t *anchor_out, uint8_t *residual_out, hipStream_t stream);
+hipError_t launch_dequant_split(const uint8_t *anchor, const uint8_t *residual, int anchor_bits,
+                                const PlanesArg &scales, int64_t num_pages, int heads, int role,
+                                float *out, hipStream_t stream);
+
 struct AttnShape {
   int batch;         // query rows (requests * tq)
   int tq;            // query tokens per request

@@ -1,0 +1,235 @@
+// Other cuts of the 8-bit code: a b + (8 - b) split into an anchor stream of
+// b bits and a residual stream of 8 - b bits per element.
+//
+// Page "Lynx: the KV cache does not have to arrive whole", section 3 cuts
+// the code 4 + 4 (the anchor names a geometric interval, the residual a
+// position in it); section 7 names 6 + 2, 2 + 6 and 5 + 3 as untried.  A
+// cut keeps the top b bits of the code as the anchor and the low 8 - b bits
+// as the residual; the draft code of anchor a is a * 2^(8-b) + 2^(7-b) - 1,
+// the round-half-down centre of the anchor's codes.
+//
+// Streams: element k of a (page, head) tile -- the k-th nibble of the
+// tile's 4-bit planes, in their role-dependent order -- occupies bits
+// k*b .. k*b + b - 1 (least significant first) of the tile's anchor
+// stream (b * 4096 bytes) and bits k*(8-b) .. of its residual stream.  A
+// unit of 32 elements (16 bytes of each 4-bit plane) is exactly b words of
+// the anchor stream and 8 - b words of the residual stream, so every
+// thread here reads and writes whole words of its own unit.
+#include "lynx_internal.h"
+
+namespace lynx {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSplitThreads = 256;
+constexpr int kUnitsPerTile = kPage * kDim / 32;  // 1024
+
+struct YTable {
+  float y[256];
+};
+
+// 32 codes of a unit, from the 16 bytes of each 4-bit plane: element 8w + i
+// is nibble i of word w; the code is (anchor nibble << 4 | residual nibble)
+// read as int8.
+__device__ __forceinline__ int code_of(const uint32_t *a4, const uint32_t *r4, int k) {
+  const uint32_t an = (a4[k >> 3] >> (4 * (k & 7))) & 15u;
+  const uint32_t rn = (r4[k >> 3] >> (4 * (k & 7))) & 15u;
+  return static_cast<int8_t>(static_cast<uint8_t>((an << 4) | rn));
+}
+
+// Pack 32 values of B bits (low bits of v[k]) into B words, least
+// significant first.
+template <int B>
+__device__ __forceinline__ void pack32(const uint32_t *v, uint32_t *w) {
+  uint64_t acc = 0;
+  int nb = 0, wi = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    acc |= static_cast<uint64_t>(v[k] & ((1u << B) - 1u)) << nb;
+    nb += B;
+    if (nb >= 32) {
+      w[wi++] = static_cast<uint32_t>(acc);
+      acc >>= 32;
+      nb -= 32;
+    }
+  }
+}
+
+// Field k of B bits of a unit's words (B <= 7, so a field spans at most
+// two words), sign-extended or not.
+template <int B, bool kSigned>
+__device__ __forceinline__ int field(const uint32_t *w, int k) {
+  const int o = k * B;
+  const uint32_t lo = w[o >> 5];
+  const uint32_t hi = ((o & 31) + B > 32) ? w[(o >> 5) + 1] : 0u;
+  const uint32_t x = static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> (o & 31));
+  return kSigned ? __builtin_amdgcn_sbfe(static_cast<int>(x), 0, B)
+                 : static_cast<int>(__builtin_amdgcn_ubfe(x, 0, B));
+}
+
+template <int B>
+__global__ __launch_bounds__(kSplitThreads) void split_planes_kernel(
+    const u32x4 *__restrict__ a4, const u32x4 *__restrict__ r4, uint32_t *__restrict__ aout,
+    uint32_t *__restrict__ rout, size_t units) {
+  constexpr int RB = 8 - B;
+  const size_t u = static_cast<size_t>(blockIdx.x) * kSplitThreads + threadIdx.x;
+  if (u >= units) return;
+  const u32x4 av = __builtin_nontemporal_load(a4 + u);
+  const u32x4 rv = __builtin_nontemporal_load(r4 + u);
+  const uint32_t aw[4] = {av[0], av[1], av[2], av[3]};
+  const uint32_t rw[4] = {rv[0], rv[1], rv[2], rv[3]};
+  uint32_t va[32], vr[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int q = code_of(aw, rw, k);
+    va[k] = static_cast<uint32_t>(q >> RB);  // arithmetic: the signed anchor
+    vr[k] = static_cast<uint32_t>(q) & ((1u << RB) - 1u);
+  }
+  uint32_t wa[B], wr[RB];
+  pack32<B>(va, wa);
+  pack32<RB>(vr, wr);
+#pragma unroll
+  for (int i = 0; i < B; ++i) __builtin_nontemporal_store(wa[i], aout + u * B + i);
+#pragma unroll
+  for (int i = 0; i < RB; ++i) __builtin_nontemporal_store(wr[i], rout + u * RB + i);
+}
+
+// xhat = mn + rg * (mu + s * yhat(code)), the arithmetic of the 4 + 4
+// dequantizers (so a full reconstruction is bit-identical to theirs).
+template <int B, int kRole, bool kFull>
+__global__ __launch_bounds__(kSplitThreads) void dequant_split_kernel(
+    const uint32_t *__restrict__ astream, const uint32_t *__restrict__ rstream, PlanesArg sc,
+    int heads, size_t units, float *__restrict__ out, YTable tab) {
+  constexpr int RB = 8 - B;
+  constexpr int kMid = RB > 0 ? (1 << (RB - 1)) - 1 : 0;
+  __shared__ float s_y[256];
+  s_y[threadIdx.x] = tab.y[threadIdx.x];
+  __syncthreads();
+  const size_t u = static_cast<size_t>(blockIdx.x) * kSplitThreads + threadIdx.x;
+  if (u >= units) return;
+  uint32_t wa[B], wr[RB > 0 ? RB : 1];
+#pragma unroll
+  for (int i = 0; i < B; ++i) wa[i] = astream[u * B + i];
+  if (kFull) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) wr[i] = rstream[u * RB + i];
+  }
+  const size_t tile = u / kUnitsPerTile;
+  const int uu = static_cast<int>(u % kUnitsPerTile);
+  const size_t p = tile / static_cast<size_t>(heads);
+  const int h = static_cast<int>(tile % static_cast<size_t>(heads));
+  const size_t row = static_cast<size_t>(heads) * kDim;
+  auto yhat = [&](int k) {
+    const int a = field<B, true>(wa, k);
+    const int r = kFull ? field<RB, false>(wr, k) : kMid;
+    return s_y[a * (1 << RB) + r + 128];
+  };
+  if (kRole == LYNX_ROLE_KEY) {
+    // unit = 32 consecutive channels of one token
+    const int t = uu >> 2, d0 = (uu & 3) * 32;
+    const int c = t / kChunk;
+    const float *pm = sc.page_min + tile * kDim + d0;
+    const float *pr = sc.page_range + tile * kDim + d0;
+    const float *cm = sc.chunk_mean + (tile * kChunks + c) * kDim + d0;
+    const float *cs = sc.chunk_maxabs + (tile * kChunks + c) * kDim + d0;
+    float *dst = out + (p * kPage + t) * row + static_cast<size_t>(h) * kDim + d0;
+#pragma unroll
+    for (int k4 = 0; k4 < 8; ++k4) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * k4 + e;
+        const float inner = __builtin_fmaf(cs[k], yhat(k), cm[k]);
+        o[e] = __builtin_fmaf(pr[k], inner, pm[k]);
+      }
+      reinterpret_cast<float4 *>(dst)[k4] = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  } else {
+    // unit = the 32 tokens of one chunk of one channel; nibble i of word w
+    // is token 4w + i (i < 4) or 16 + 4w + i - 4
+    const int c = uu >> 7, d = uu & 127;
+    const float mn = sc.page_min[tile * kDim + d];
+    const float rg = sc.page_range[tile * kDim + d];
+    const float mu = sc.chunk_mean[(tile * kChunks + c) * kDim + d];
+    const float s = sc.chunk_maxabs[(tile * kChunks + c) * kDim + d];
+    float *dst = out + (p * kPage + static_cast<size_t>(c) * kChunk) * row + static_cast<size_t>(h) * kDim + d;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int w = k >> 3, i = k & 7;
+      const int t = i < 4 ? 4 * w + i : 16 + 4 * w + (i - 4);
+      dst[static_cast<size_t>(t) * row] = __builtin_fmaf(rg, __builtin_fmaf(s, yhat(k), mu), mn);
+    }
+  }
+}
+
+template <int B>
+hipError_t launch_split_b(const PlanesArg &in, size_t units, uint8_t *aout, uint8_t *rout,
+                          hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((units + kSplitThreads - 1) / kSplitThreads));
+  hipLaunchKernelGGL(split_planes_kernel<B>, grid, dim3(kSplitThreads), 0, stream,
+                     reinterpret_cast<const u32x4 *>(in.anchor),
+                     reinterpret_cast<const u32x4 *>(in.residual), reinterpret_cast<uint32_t *>(aout),
+                     reinterpret_cast<uint32_t *>(rout), units);
+  return hipGetLastError();
+}
+
+template <int B, int kRole, bool kFull>
+hipError_t launch_dq_split(const uint8_t *a, const uint8_t *r, const PlanesArg &sc, int heads,
+                           size_t units, float *out, hipStream_t stream) {
+  YTable tab;
+  const DecodeTable &dt = decode_table();
+  for (int i = 0; i < 256; ++i) tab.y[i] = dt.y[i];
+  const dim3 grid(static_cast<unsigned>((units + kSplitThreads - 1) / kSplitThreads));
+  hipLaunchKernelGGL((dequant_split_kernel<B, kRole, kFull>), grid, dim3(kSplitThreads), 0, stream,
+                     reinterpret_cast<const uint32_t *>(a), reinterpret_cast<const uint32_t *>(r), sc,
+                     heads, units, out, tab);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_dq_b(const uint8_t *a, const uint8_t *r, const PlanesArg &sc, int heads,
+                       int role, size_t units, float *out, hipStream_t stream) {
+  if (role == LYNX_ROLE_KEY)
+    return r ? launch_dq_split<B, LYNX_ROLE_KEY, true>(a, r, sc, heads, units, out, stream)
+             : launch_dq_split<B, LYNX_ROLE_KEY, false>(a, r, sc, heads, units, out, stream);
+  return r ? launch_dq_split<B, LYNX_ROLE_VALUE, true>(a, r, sc, heads, units, out, stream)
+           : launch_dq_split<B, LYNX_ROLE_VALUE, false>(a, r, sc, heads, units, out, stream);
+}
+
+}  // namespace
+
+hipError_t launch_split_planes(const PlanesArg &in, int64_t num_pages, int heads, int anchor_bits,
+                               uint8_t *anchor_out, uint8_t *residual_out, hipStream_t stream) {
+  const size_t units = static_cast<size_t>(num_pages) * heads * kUnitsPerTile;
+  if (units == 0) return hipSuccess;
+  switch (anchor_bits) {
+    case 1: return launch_split_b<1>(in, units, anchor_out, residual_out, stream);
+    case 2: return launch_split_b<2>(in, units, anchor_out, residual_out, stream);
+    case 3: return launch_split_b<3>(in, units, anchor_out, residual_out, stream);
+    case 4: return launch_split_b<4>(in, units, anchor_out, residual_out, stream);
+    case 5: return launch_split_b<5>(in, units, anchor_out, residual_out, stream);
+    case 6: return launch_split_b<6>(in, units, anchor_out, residual_out, stream);
+    case 7: return launch_split_b<7>(in, units, anchor_out, residual_out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_dequant_split(const uint8_t *anchor, const uint8_t *residual, int anchor_bits,
+                                const PlanesArg &scales, int64_t num_pages, int heads, int role,
+                                float *out, hipStream_t stream) {
+  const size_t units = static_cast<size_t>(num_pages) * heads * kUnitsPerTile;
+  if (units == 0) return hipSuccess;
+  switch (anchor_bits) {
+    case 1: return launch_dq_b<1>(anchor, residual, scales, heads, role, units, out, stream);
+    case 2: return launch_dq_b<2>(anchor, residual, scales, heads, role, units, out, stream);
+    case 3: return launch_dq_b<3>(anchor, residual, scales, heads, role, units, out, stream);
+    case 4: return launch_dq_b<4>(anchor, residual, scales, heads, role, units, out, stream);
+    case 5: return launch_dq_b<5>(anchor, residual, scales, heads, role, units, out, stream);
+    case 6: return launch_dq_b<6>(anchor, residual, scales, heads, role, units, out, stream);
+    case 7: return launch_dq_b<7>(anchor, residual, scales, heads, role, units, out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lynx

@@ -67,6 +67,13 @@ for _name in ("lynx_verify_attention", "lynx_draft_attention"):
                                      _P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _i32, _i64,
                                      ctypes.c_float, _P, _P, _sz, _P]
     getattr(_lib, _name).restype = ctypes.c_int
+_lib.lynx_split_stream_bytes.argtypes = [_i64, _i32, _i32]
+_lib.lynx_split_stream_bytes.restype = _sz
+_lib.lynx_split_planes.argtypes = [ctypes.POINTER(_CPlanes), _i64, _i32, _i32, _i32, _P, _P, _P]
+_lib.lynx_split_planes.restype = ctypes.c_int
+_lib.lynx_dequantize_split.argtypes = [_P, _P, _i32, ctypes.POINTER(_CPlanes), _i64, _i32, _i32,
+                                       _i32, _P, _P]
+_lib.lynx_dequantize_split.restype = ctypes.c_int
 _lib.lynx_status_string.argtypes = [ctypes.c_int]
 _lib.lynx_status_string.restype = ctypes.c_char_p
 _lib.lynx_code_thresholds.argtypes = [_P]
@@ -315,3 +322,31 @@ def planes_view(p: Planes, first_page: int, num_pages: int) -> Planes:
                   p.chunk_mean[first_page:first_page + num_pages],
                   p.chunk_maxabs[first_page:first_page + num_pages],
                   num_pages=num_pages, heads=p.heads, role=p.role)
+
+
+def split_planes(p: Planes, anchor_bits: int, stream=None):
+    """b + (8 - b) cut of encoded planes: (anchor stream, residual stream),
+    uint8 tensors of b * 4096 and (8 - b) * 4096 bytes per (page, head)."""
+    P, H = p.num_pages, p.heads
+    na = _lib.lynx_split_stream_bytes(P, H, anchor_bits)
+    nr = _lib.lynx_split_stream_bytes(P, H, 8 - anchor_bits)
+    a = torch.empty(max(na, 16), dtype=torch.uint8, device=p.anchor.device)
+    r = torch.empty(max(nr, 16), dtype=torch.uint8, device=p.anchor.device)
+    cp = p.c()
+    _check(_lib.lynx_split_planes(ctypes.byref(cp), P, H, HEAD_DIM, anchor_bits, _ptr(a), _ptr(r),
+                                  _stream(stream)), "lynx_split_planes")
+    return a[:na], r[:nr]
+
+
+def dequantize_split(anchor: torch.Tensor, residual: Optional[torch.Tensor], anchor_bits: int,
+                     scales: Planes, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp32 reconstruction [P][256][H][128] from b + (8 - b) streams; residual
+    None is the draft.  `scales` supplies the page and chunk scales."""
+    P, H = scales.num_pages, scales.heads
+    if out is None:
+        out = torch.empty((P, PAGE, H, HEAD_DIM), dtype=torch.float32, device=anchor.device)
+    cp = scales.c()
+    _check(_lib.lynx_dequantize_split(_ptr(anchor), _ptr(residual), anchor_bits, ctypes.byref(cp), P,
+                                      H, HEAD_DIM, scales.role, _ptr(out), _stream(stream)),
+           "lynx_dequantize_split")
+    return out

@@ -144,6 +144,33 @@ def test_argument_errors_are_reported_before_any_launch(lib):
         assert vcall(args(B=0)) == 0
 
 
+def test_cut_entry_points_reject_bad_arguments(lib):
+    P = ctypes.c_void_p
+    lib.lynx_split_stream_bytes.restype = ctypes.c_size_t
+    lib.lynx_split_stream_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    assert lib.lynx_split_stream_bytes(3, 2, 5) == 3 * 2 * 5 * 4096
+    assert lib.lynx_split_stream_bytes(3, 2, 0) == 0
+    lib.lynx_split_planes.argtypes = [ctypes.POINTER(CPlanes), ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, P, P, P]
+    pl = _fake_planes()
+    a, r = P(0x80000), P(0x90000)
+    assert lib.lynx_split_planes(ctypes.byref(pl), 4, 8, 128, 0, a, r, None) == -7   # bits 0
+    assert lib.lynx_split_planes(ctypes.byref(pl), 4, 8, 128, 8, a, r, None) == -7   # bits 8
+    assert lib.lynx_split_planes(ctypes.byref(pl), 4, 8, 64, 3, a, r, None) == -2
+    assert lib.lynx_split_planes(ctypes.byref(pl), 4, 8, 128, 3, None, r, None) == -1
+    assert lib.lynx_split_planes(ctypes.byref(pl), 4, 8, 128, 3, P(0x80004), r, None) == -3
+    assert lib.lynx_split_planes(ctypes.byref(pl), 0, 8, 128, 3, None, None, None) == 0
+    lib.lynx_dequantize_split.argtypes = [P, P, ctypes.c_int32, ctypes.POINTER(CPlanes),
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, P, P]
+    out = P(0xA0000)
+    assert lib.lynx_dequantize_split(a, None, 9, ctypes.byref(pl), 4, 8, 128, 0, out, None) == -7
+    assert lib.lynx_dequantize_split(a, None, 3, ctypes.byref(pl), 4, 8, 128, 2, out, None) == -7
+    assert lib.lynx_dequantize_split(None, None, 3, ctypes.byref(pl), 4, 8, 128, 0, out, None) == -1
+    assert lib.lynx_dequantize_split(a, P(0x90008), 3, ctypes.byref(pl), 4, 8, 128, 1, out, None) == -3
+    assert lib.lynx_dequantize_split(a, None, 3, ctypes.byref(pl), 0, 8, 128, 1, None, None) == 0
+
+
 def test_status_strings(lib):
     lib.lynx_status_string.restype = ctypes.c_char_p
     for code in range(-7, 1):
