@@ -261,6 +261,48 @@ def progressive_main(args):
     print(json.dumps(result), flush=True)
 
 
+def cuts_leg(args, w, sets, stream):
+    """The b + (8 - b) cuts after the timed region: re-cutting one tensor's
+    planes into the two streams, and the draft reconstruction from the
+    anchor stream, each cycled over the buffer sets (cache-cold)."""
+    import torch
+    from long_context_serving_amd import lynx
+    elems = w.batch * w.tokens * w.kv_heads * w.head_dim
+    scale_bytes = 0.28125  # fp32 page and chunk scales per element
+    res = {}
+    for b in (2, 3, 5, 6):
+        streams = [lynx.split_planes(e["pk"], b) for e in sets]
+        outs = torch.empty((w.pages * w.batch, 256, w.kv_heads, w.head_dim), dtype=torch.float32,
+                           device=sets[0]["pk"].anchor.device)
+        split_calls = [lambda e=e: lynx.split_planes(e["pk"], b) for e in sets]
+        draft_calls = [lambda e=e, st=st: lynx.dequantize_split(st[0], None, b, e["pk"], out=outs)
+                       for e, st in zip(sets, streams)]
+        times = []
+        for calls in (split_calls, draft_calls):
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                for _ in range(4):
+                    for c in calls:
+                        c()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / (4 * len(calls)))
+        split_bytes = elems * 2.0                    # 4 + 4 planes in, both streams out
+        draft_bytes = elems * (b / 8.0 + scale_bytes + 4.0)
+        res["%d+%d" % (b, 8 - b)] = {
+            "split_us": times[0] * 1e3, "split_GBps": split_bytes / (times[0] * 1e-3) / 1e9,
+            "draft_dequant_us": times[1] * 1e3,
+            "draft_dequant_GBps": draft_bytes / (times[1] * 1e-3) / 1e9,
+            "anchor_stream_bytes_per_elem": b / 8.0}
+    return {"tensor": "K of one buffer set per call, all %d sets in turn" % len(sets),
+            "timing": "events around 4 passes over the sets, after the timed region (eager launches)",
+            "by_cut": res}
+
+
 def verify_leg(args, w, sets, dev, sm, stream):
     """Verify pass after the timed region: the newest tq tokens of the
     request (its speculative tokens) attend to the full planes of every
@@ -329,6 +371,8 @@ def main():
                     help="emulated link rates for the progressive timeline (empty: none)")
     ap.add_argument("--no-verify", dest="verify", action="store_false",
                     help="skip the verify-pass measurement (64 speculative tokens over the planes)")
+    ap.add_argument("--no-cuts", dest="cuts", action="store_false",
+                    help="skip the measurement of the other code cuts")
     ap.add_argument("--verify-only", action="store_true",
                     help="encode the buffer sets, then time the verify pass alone")
     ap.add_argument("--verify-tq", type=int, default=64)
@@ -450,6 +494,7 @@ def main():
                    "decode_full": phase_ms[2] / K}
 
     verify = verify_leg(args, w, sets, dev, sm, stream) if args.verify else None
+    cuts = cuts_leg(args, w, sets, stream) if args.cuts else None
 
     if args.copy_probe:
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -500,6 +545,8 @@ def main():
     }
     if verify is not None:
         result["verify"] = verify
+    if cuts is not None:
+        result["cuts"] = cuts
     if args.cpu:
         log("bench: CPU baseline (oracle) on %d pages" % args.cpu_pages)
         result["cpu_baseline"] = cpu_baseline(w, xk0, xv0, qb, min(args.cpu_pages, w.pages), sm)

@@ -96,18 +96,25 @@ __global__ __launch_bounds__(kSplitThreads) void split_planes_kernel(
 }
 
 // xhat = mn + rg * (mu + s * yhat(code)), the arithmetic of the 4 + 4
-// dequantizers (so a full reconstruction is bit-identical to theirs).
+// dequantizers (so a full reconstruction is bit-identical to theirs).  A
+// block takes 256 units of one tile.  Values: a unit is the 32 tokens of
+// one channel of a chunk, and consecutive lanes hold consecutive channels,
+// so each lane keeps its channel's four scales and every store instruction
+// is contiguous.  Keys: a unit is 32 channels of one token; the block's 256
+// units are 64 whole tokens, so each lane first unpacks its unit's codes
+// into an LDS tile of 64 tokens x 128 channels, then takes one channel of
+// one chunk (32 tokens) as for the values.
 template <int B, int kRole, bool kFull>
 __global__ __launch_bounds__(kSplitThreads) void dequant_split_kernel(
     const uint32_t *__restrict__ astream, const uint32_t *__restrict__ rstream, PlanesArg sc,
-    int heads, size_t units, float *__restrict__ out, YTable tab) {
+    int heads, float *__restrict__ out, YTable tab) {
   constexpr int RB = 8 - B;
   constexpr int kMid = RB > 0 ? (1 << (RB - 1)) - 1 : 0;
   __shared__ float s_y[256];
+  __shared__ uint32_t s_code[kRole == LYNX_ROLE_KEY ? 64 * kDim / 4 : 1];  // [token][128 codes]
   s_y[threadIdx.x] = tab.y[threadIdx.x];
-  __syncthreads();
+  // the launch covers whole tiles: kUnitsPerTile is a multiple of the block
   const size_t u = static_cast<size_t>(blockIdx.x) * kSplitThreads + threadIdx.x;
-  if (u >= units) return;
   uint32_t wa[B], wr[RB > 0 ? RB : 1];
 #pragma unroll
   for (int i = 0; i < B; ++i) wa[i] = astream[u * B + i];
@@ -115,51 +122,54 @@ __global__ __launch_bounds__(kSplitThreads) void dequant_split_kernel(
 #pragma unroll
     for (int i = 0; i < RB; ++i) wr[i] = rstream[u * RB + i];
   }
+  // table index (code + 128) of field k of this lane's unit
+  auto index = [&](int k) {
+    const int a = field<B, true>(wa, k);
+    const int r = kFull ? field<RB, false>(wr, k) : kMid;
+    return static_cast<uint32_t>(a * (1 << RB) + r + 128);
+  };
   const size_t tile = u / kUnitsPerTile;
-  const int uu = static_cast<int>(u % kUnitsPerTile);
   const size_t p = tile / static_cast<size_t>(heads);
   const int h = static_cast<int>(tile % static_cast<size_t>(heads));
   const size_t row = static_cast<size_t>(heads) * kDim;
-  auto yhat = [&](int k) {
-    const int a = field<B, true>(wa, k);
-    const int r = kFull ? field<RB, false>(wr, k) : kMid;
-    return s_y[a * (1 << RB) + r + 128];
-  };
+  const int ub = static_cast<int>((static_cast<size_t>(blockIdx.x) * kSplitThreads) % kUnitsPerTile);
+  int d, c, t0;  // this lane's channel, chunk and first token in the tile
+  uint32_t idx[32];
   if (kRole == LYNX_ROLE_KEY) {
-    // unit = 32 consecutive channels of one token
-    const int t = uu >> 2, d0 = (uu & 3) * 32;
-    const int c = t / kChunk;
-    const float *pm = sc.page_min + tile * kDim + d0;
-    const float *pr = sc.page_range + tile * kDim + d0;
-    const float *cm = sc.chunk_mean + (tile * kChunks + c) * kDim + d0;
-    const float *cs = sc.chunk_maxabs + (tile * kChunks + c) * kDim + d0;
-    float *dst = out + (p * kPage + t) * row + static_cast<size_t>(h) * kDim + d0;
+    // unit ub + i: token (ub + i) / 4, channels ((ub + i) % 4) * 32 ..
 #pragma unroll
-    for (int k4 = 0; k4 < 8; ++k4) {
-      float o[4];
+    for (int w4 = 0; w4 < 8; ++w4)
+      s_code[threadIdx.x * 8 + w4] = index(4 * w4) | (index(4 * w4 + 1) << 8) |
+                                      (index(4 * w4 + 2) << 16) | (index(4 * w4 + 3) << 24);
+    __syncthreads();
+    d = threadIdx.x & 127;
+    const int half = threadIdx.x >> 7;  // tokens 32 half .. of the block's 64
+    t0 = ub / 4 + 32 * half;
+    c = t0 / kChunk;
+    const uint8_t *codes = reinterpret_cast<const uint8_t *>(s_code);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k = 4 * k4 + e;
-        const float inner = __builtin_fmaf(cs[k], yhat(k), cm[k]);
-        o[e] = __builtin_fmaf(pr[k], inner, pm[k]);
-      }
-      reinterpret_cast<float4 *>(dst)[k4] = make_float4(o[0], o[1], o[2], o[3]);
-    }
+    for (int k = 0; k < 32; ++k) idx[k] = codes[(32 * half + k) * kDim + d];
   } else {
-    // unit = the 32 tokens of one chunk of one channel; nibble i of word w
-    // is token 4w + i (i < 4) or 16 + 4w + i - 4
-    const int c = uu >> 7, d = uu & 127;
-    const float mn = sc.page_min[tile * kDim + d];
-    const float rg = sc.page_range[tile * kDim + d];
-    const float mu = sc.chunk_mean[(tile * kChunks + c) * kDim + d];
-    const float s = sc.chunk_maxabs[(tile * kChunks + c) * kDim + d];
-    float *dst = out + (p * kPage + static_cast<size_t>(c) * kChunk) * row + static_cast<size_t>(h) * kDim + d;
+    const int uu = ub + static_cast<int>(threadIdx.x);
+    c = uu >> 7;
+    d = uu & 127;
+    t0 = c * kChunk;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const int w = k >> 3, i = k & 7;
-      const int t = i < 4 ? 4 * w + i : 16 + 4 * w + (i - 4);
-      dst[static_cast<size_t>(t) * row] = __builtin_fmaf(rg, __builtin_fmaf(s, yhat(k), mu), mn);
-    }
+    for (int k = 0; k < 32; ++k) idx[k] = index(k);
+    __syncthreads();  // the table
+  }
+  const float mn = sc.page_min[tile * kDim + d];
+  const float rg = sc.page_range[tile * kDim + d];
+  const float mu = sc.chunk_mean[(tile * kChunks + c) * kDim + d];
+  const float s = sc.chunk_maxabs[(tile * kChunks + c) * kDim + d];
+  float *dst = out + (p * kPage + static_cast<size_t>(t0)) * row + static_cast<size_t>(h) * kDim + d;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    // keys: token k of the lane's 32; values: field k is token 4w + i
+    // (i < 4) or 16 + 4w + i - 4 of the chunk, w = k / 8, i = k % 8
+    const int w = k >> 3, i = k & 7;
+    const int t = kRole == LYNX_ROLE_KEY ? k : (i < 4 ? 4 * w + i : 16 + 4 * w + (i - 4));
+    dst[static_cast<size_t>(t) * row] = __builtin_fmaf(rg, __builtin_fmaf(s, s_y[idx[k]], mu), mn);
   }
 }
 
@@ -180,10 +190,11 @@ hipError_t launch_dq_split(const uint8_t *a, const uint8_t *r, const PlanesArg &
   YTable tab;
   const DecodeTable &dt = decode_table();
   for (int i = 0; i < 256; ++i) tab.y[i] = dt.y[i];
-  const dim3 grid(static_cast<unsigned>((units + kSplitThreads - 1) / kSplitThreads));
+  static_assert(kUnitsPerTile % kSplitThreads == 0, "blocks cover whole tiles");
+  const dim3 grid(static_cast<unsigned>(units / kSplitThreads));
   hipLaunchKernelGGL((dequant_split_kernel<B, kRole, kFull>), grid, dim3(kSplitThreads), 0, stream,
                      reinterpret_cast<const uint32_t *>(a), reinterpret_cast<const uint32_t *>(r), sc,
-                     heads, units, out, tab);
+                     heads, out, tab);
   return hipGetLastError();
 }
 
