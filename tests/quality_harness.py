@@ -60,6 +60,12 @@ def lynx_reconstruct(x: np.ndarray, chunk: int = 32, page_norm: bool = True, log
     and 8 - anchor_bits low bits (the residual); the draft keeps the anchor
     and the round-half-down centre of the residual range."""
     P, T, H, D = x.shape
+    if P > 1:  # pages are independent; page-sized temporaries stay in cache
+        out = np.empty_like(x)
+        for i in range(P):
+            out[i:i + 1], bits = lynx_reconstruct(x[i:i + 1], chunk, page_norm, log_map, sign_aware,
+                                                  midpoint, anchor_only, alpha, anchor_bits)
+        return out, bits
     if page_norm:
         mn = x.min(axis=1, keepdims=True)
         rg = _round_up_7(x.max(axis=1, keepdims=True) - mn)
@@ -94,6 +100,9 @@ def uniform_reconstruct(x: np.ndarray, bits: int, per: str):
     """Asymmetric uniform grid of 2^bits levels per token ('token': over the
     channels of one head) or per channel ('channel': over a page's tokens)."""
     axis = 3 if per == "token" else 1
+    if x.shape[0] > 1:
+        parts = [uniform_reconstruct(x[i:i + 1], bits, per) for i in range(x.shape[0])]
+        return np.concatenate([p[0] for p in parts]), parts[0][1]
     lo = x.min(axis=axis, keepdims=True)
     hi = x.max(axis=axis, keepdims=True)
     step = np.where(hi > lo, (hi - lo) / (2 ** bits - 1), 1.0)
@@ -122,7 +131,7 @@ def nmse(o_hat: np.ndarray, o: np.ndarray) -> float:
 
 
 def study(cases, sm: float, chunks=(8, 16, 32, 64), alphas=(3, 15, 63),
-          splits=(2, 3, 5, 6)) -> Dict[str, Dict[str, float]]:
+          splits=(2, 3, 5, 6), pooled_parts: bool = False) -> Dict[str, Dict[str, float]]:
     """NMSE and bits per coordinate of every configuration, pooled over the
     cases (each a tuple xk, xv float64 [P][256][H][D] of one request and its
     queries q float64 [Hq][D]): the squared errors and the squared norms are
@@ -164,26 +173,43 @@ def study(cases, sm: float, chunks=(8, 16, 32, 64), alphas=(3, 15, 63),
             vh, bv = f(xv)
             num[name] += float(((attention(q, flat(kh), flat(vh), sm) - ref) ** 2).sum())
             bits[name] = 0.5 * (bk + bv)
+    if pooled_parts:  # the sums themselves, to pool over several processes
+        out = {name: {"num": num[name], "bits": bits[name]} for name, _ in configs}
+        out["__den"] = den
+        return out
     return {name: {"nmse": num[name] / den, "bits": bits[name]} for name, _ in configs}
 
 
-def synthetic_cases(workload: str = "ctx32k", tokens: int = 4096, requests: int = 1):
-    """bf16 K, V pages and queries of the first requests of a workload, as
-    float64 (xk, xv [P][256][H][D], q [Hq][D]) per request."""
+def synthetic_cases(workload: str = "ctx32k", tokens: int = 4096, requests: int = 1,
+                    first_request: int = 0):
+    """bf16 K, V pages and queries of requests first_request .. + requests of
+    a workload, as float64 (xk, xv [P][256][H][D], q [Hq][D]) per request."""
     from long_context_serving_amd import synth
     w = synth.WORKLOADS[workload]
     to_f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    qs = to_f(synth.queries(w, batch=requests, first_request=0))
+    qs = to_f(synth.queries(w, batch=requests, first_request=first_request))
+    rs = range(first_request, first_request + requests)
     return w, [(to_f(synth.kv_pages(w, 0, 0, r, tokens=tokens)),
-                to_f(synth.kv_pages(w, 0, 1, r, tokens=tokens)), qs[r]) for r in range(requests)]
+                to_f(synth.kv_pages(w, 0, 1, r, tokens=tokens)), qs[i]) for i, r in enumerate(rs)]
+
+
+def _one_request(args):
+    tokens, r = args
+    _, cases = synthetic_cases(tokens=tokens, requests=1, first_request=r)
+    return study(cases, 1.0 / np.sqrt(128.0), pooled_parts=True)
 
 
 if __name__ == "__main__":
     import json
+    import multiprocessing
     import sys
     tokens = int(sys.argv[1]) if len(sys.argv) > 1 else 8192
     requests = int(sys.argv[2]) if len(sys.argv) > 2 else 8
-    w, cases = synthetic_cases(tokens=tokens, requests=requests)
-    r = study(cases, 1.0 / np.sqrt(128.0))
-    print(json.dumps({"workload": w.name, "tokens": tokens, "requests": requests, "results": r},
-                     indent=1))
+    workers = int(sys.argv[3]) if len(sys.argv) > 3 else 4
+    with multiprocessing.Pool(workers) as pool:
+        parts = pool.map(_one_request, [(tokens, r) for r in range(requests)])
+    den = sum(p["__den"] for p in parts)
+    res = {k: {"nmse": sum(p[k]["num"] for p in parts) / den, "bits": parts[0][k]["bits"]}
+           for k in parts[0] if k != "__den"}
+    print(json.dumps({"workload": "ctx32k", "tokens": tokens, "requests": requests,
+                      "results": res}, indent=1))
