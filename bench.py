@@ -261,10 +261,11 @@ def progressive_main(args):
     print(json.dumps(result), flush=True)
 
 
-def cuts_leg(args, w, sets, stream):
+def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
     """The b + (8 - b) cuts after the timed region: re-cutting one tensor's
-    planes into the two streams, and the draft reconstruction from the
-    anchor stream, each cycled over the buffer sets (cache-cold)."""
+    planes into the two streams, the draft reconstruction from the anchor
+    stream, and the fused draft decode attention over the K and V anchor
+    streams, each cycled over the buffer sets (cache-cold)."""
     import torch
     from long_context_serving_amd import lynx
     elems = w.batch * w.tokens * w.kv_heads * w.head_dim
@@ -277,8 +278,20 @@ def cuts_leg(args, w, sets, stream):
         split_calls = [lambda e=e: lynx.split_planes(e["pk"], b) for e in sets]
         draft_calls = [lambda e=e, st=st: lynx.dequantize_split(st[0], None, b, e["pk"], out=outs)
                        for e, st in zip(sets, streams)]
+        cut_k = [lynx.cut_planes(e["pk"], b) for e in sets]
+        cut_v = [lynx.cut_planes(e["pv"], b) for e in sets]
+        attn_calls = [lambda ck=ck, cv=cv: lynx.decode_attention_split(
+            q, ck, cv, b, w.pages, full=False, sm_scale=sm, out=out_attn, workspace=ws)
+            for ck, cv in zip(cut_k, cut_v)]
+        for c in attn_calls:
+            c()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in attn_calls:
+                c()
         times = []
-        for calls in (split_calls, draft_calls):
+        for calls in (split_calls, draft_calls, [g.replay]):
             for c in calls:
                 c()
             torch.cuda.synchronize()
@@ -290,16 +303,20 @@ def cuts_leg(args, w, sets, stream):
                         c()
                 e1.record(stream)
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) / (4 * len(calls)))
+            times.append(e0.elapsed_time(e1) / (4 * len(sets)))  # one call per set per pass
         split_bytes = elems * 2.0                    # 4 + 4 planes in, both streams out
         draft_bytes = elems * (b / 8.0 + scale_bytes + 4.0)
+        attn_bytes = 2 * elems * (b / 8.0 + scale_bytes)  # K and V anchor streams and scales
         res["%d+%d" % (b, 8 - b)] = {
+            "draft_attention_us": times[2] * 1e3,
+            "draft_attention_GBps": attn_bytes / (times[2] * 1e-3) / 1e9,
             "split_us": times[0] * 1e3, "split_GBps": split_bytes / (times[0] * 1e-3) / 1e9,
             "draft_dequant_us": times[1] * 1e3,
             "draft_dequant_GBps": draft_bytes / (times[1] * 1e-3) / 1e9,
             "anchor_stream_bytes_per_elem": b / 8.0}
     return {"tensor": "K of one buffer set per call, all %d sets in turn" % len(sets),
-            "timing": "events around 4 passes over the sets, after the timed region (eager launches)",
+            "timing": "events around 4 passes over the sets, after the timed region (packer and "
+                      "dequantizer: eager launches; draft attention: one HIP graph over the sets)",
             "by_cut": res}
 
 
@@ -494,7 +511,7 @@ def main():
                    "decode_full": phase_ms[2] / K}
 
     verify = verify_leg(args, w, sets, dev, sm, stream) if args.verify else None
-    cuts = cuts_leg(args, w, sets, stream) if args.cuts else None
+    cuts = cuts_leg(args, w, sets, stream, q, out, ws, sm) if args.cuts else None
 
     if args.copy_probe:
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)

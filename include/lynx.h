@@ -235,6 +235,36 @@ int lynx_dequantize_split(const uint8_t *anchor, const uint8_t *residual,
                           void *stream);
 
 /*
+ * Fused-dequant decode attention over b + (8 - b) streams (page "Lynx: the
+ * KV cache does not have to arrive whole", section 4: drafts on the anchor
+ * stream alone, the full code on both; section 7: other cuts).  Arguments
+ * as lynx_decode_attention_anchor / _full, except:
+ *   k, v         k->anchor and v->anchor are anchor streams of anchor_bits
+ *                bits per element, k->residual and v->residual residual
+ *                streams of 8 - anchor_bits bits (read only when full),
+ *                both as written by lynx_split_planes from K (role key) and
+ *                V (role value) planes; the scale pointers are those of the
+ *                planes they were cut from
+ *   anchor_bits  1 .. 7 (4: the streams are the 4-bit planes themselves)
+ *   full         0: the draft, the anchor's round-half-down centre code
+ *                a * 2^(8-b) + 2^(7-b) - 1; otherwise the full code (equal
+ *                to lynx_decode_attention_full over the uncut planes)
+ * The workspace size is lynx_decode_attention_workspace_size's.  GQA groups
+ * up to 8 only (BAD_SHAPE otherwise).  Errors: as the decode calls, plus
+ * BAD_ARG for anchor_bits.
+ */
+int lynx_decode_attention_split(const uint16_t *q, const lynx_planes *k,
+                                const lynx_planes *v, int32_t anchor_bits,
+                                int32_t full, const int32_t *block_table,
+                                const int32_t *seq_lens, int32_t batch,
+                                int32_t num_kv_heads, int32_t num_q_heads,
+                                int32_t head_dim, int32_t max_pages_per_seq,
+                                int64_t pool_pages, float sm_scale,
+                                float *out, float *scores,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
  * Attention of the tq newest tokens of each request over its compact pages
  * and its bf16 tail (page "Lynx: the KV cache does not have to arrive
  * whole", section 4: drafts run on the anchor stream alone, the refined

@@ -93,10 +93,12 @@ int attention_common(const uint16_t *q, const lynx_planes *k, const lynx_planes 
                      const int32_t *block_table, const int32_t *seq_lens, int32_t batch,
                      int32_t heads, int32_t q_heads, int32_t head_dim, int32_t max_pages,
                      int64_t pool_pages, float sm_scale, float *out, float *scores, void *workspace,
-                     size_t workspace_bytes, void *stream, bool full) {
+                     size_t workspace_bytes, void *stream, bool full, int anchor_bits = 4) {
   if (head_dim != LYNX_HEAD_DIM || batch < 0 || heads < 1 || q_heads < heads ||
       q_heads % heads != 0 || q_heads / heads > LYNX_MAX_GROUP || max_pages < 1)
     return LYNX_ERR_BAD_SHAPE;
+  // cut streams are read by the matrix-core kernel (GQA groups up to 8)
+  if (anchor_bits != 4 && !lynx::attention_mfma_supported(q_heads / heads)) return LYNX_ERR_BAD_SHAPE;
   // grid sizes: the combine launches 4 blocks per (request, query head)
   if (static_cast<int64_t>(batch) * q_heads * 4 > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
   if (pool_pages < 0 || pool_pages * static_cast<int64_t>(heads) > 0x7FFFFFFFLL)
@@ -127,7 +129,7 @@ int attention_common(const uint16_t *q, const lynx_planes *k, const lynx_planes 
   }
   const hipError_t e = lynx::launch_attention(q, ka, va, block_table, seq_lens, s, sm_scale,
                                               full, out, scores, workspace,
-                                              static_cast<hipStream_t>(stream));
+                                              static_cast<hipStream_t>(stream), anchor_bits);
   return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
 }
 
@@ -317,6 +319,18 @@ int lynx_dequantize_split(const uint8_t *anchor, const uint8_t *residual, int32_
                                                   num_kv_heads, role, out,
                                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
+}
+
+int lynx_decode_attention_split(const uint16_t *q, const lynx_planes *k, const lynx_planes *v,
+                                int32_t anchor_bits, int32_t full, const int32_t *block_table,
+                                const int32_t *seq_lens, int32_t batch, int32_t num_kv_heads,
+                                int32_t num_q_heads, int32_t head_dim, int32_t max_pages_per_seq,
+                                int64_t pool_pages, float sm_scale, float *out, float *scores,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  if (anchor_bits < 1 || anchor_bits > 7) return LYNX_ERR_BAD_ARG;
+  return attention_common(q, k, v, block_table, seq_lens, batch, num_kv_heads, num_q_heads,
+                          head_dim, max_pages_per_seq, pool_pages, sm_scale, out, scores,
+                          workspace, workspace_bytes, stream, full != 0, anchor_bits);
 }
 
 size_t lynx_verify_attention_workspace_size(int32_t batch, int32_t tq, int32_t num_kv_heads,

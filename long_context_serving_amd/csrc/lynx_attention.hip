@@ -402,11 +402,12 @@ hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
                             const int32_t *seq_lens, const AttnShape &s,
                             float sm_scale, bool full, float *out,
                             float *scores, void *workspace,
-                            hipStream_t stream) {
+                            hipStream_t stream, int anchor_bits) {
   if (s.batch == 0) return hipSuccess;
   if (attention_mfma_supported(s.group))
     return launch_attention_mfma(q, k, v, block_table, seq_lens, s, sm_scale, full, out, scores,
-                                 workspace, true, stream);
+                                 workspace, true, stream, anchor_bits);
+  if (anchor_bits != 4) return hipErrorInvalidValue;  // cut streams: matrix-core kernel only
   YTable tab;
   const DecodeTable &dt = decode_table();
   for (int i = 0; i < 256; ++i) tab.y[i] = dt.y[i];

@@ -39,6 +39,17 @@
 // through LDS and writes the output itself when one run covers the request;
 // otherwise it writes a partial (base-2 max m, sum l, unnormalised o) and a
 // second, small kernel merges the runs exactly.
+//
+// Other cuts of the code (page "Lynx: the KV cache does not have to arrive
+// whole", section 7 names 6 + 2, 2 + 6 and 5 + 3): the same kernel reads a
+// b-bit anchor stream (and an (8 - b)-bit residual stream), where a unit of
+// 32 elements -- the 16 bytes of a 4-bit plane -- is b words with the
+// fields least significant first.  A key lane reads its whole unit; a value
+// lane reads the 2 or 3 words that hold its 8 fields and aligns them with
+// v_alignbyte.  The fields become one table index byte per element: the
+// code byte (a << (8 - b) | r) for the full code, which indexes the same
+// table as the 4 + 4 code, or the anchor field for the draft, whose table
+// row holds the draft value of the anchor's round-half-down centre.
 #include <math.h>
 
 #include <type_traits>
@@ -207,10 +218,68 @@ __device__ __forceinline__ uint32_t split_dup(float x, uint32_t keep_mask) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(y, y));
 }
 
+// ---- b + (8 - b) cut streams --------------------------------------------------
+// Words of a b-bit stream that hold the 8 fields of value lane r (fields
+// 8r .. 8r + 7 of a unit, bytes r*b .. r*b + b - 1), over the 4 lanes r.
+constexpr int cut_window_words(int b) {
+  int n = 1;
+  for (int r = 0; r < 4; ++r) {
+    const int span = ((r * b + b - 1) >> 2) - ((r * b) >> 2) + 1;
+    n = span > n ? span : n;
+  }
+  return n;
+}
+
+// Field k of B bits (least significant first) of a little-endian word array.
+template <int B, int N>
+__device__ __forceinline__ uint32_t cut_field(const uint32_t (&w)[N], int k) {
+  const int p = k * B, i = p >> 5, o = p & 31;
+  constexpr uint32_t kMask = (1u << B) - 1u;
+  if (o + B <= 32) return (w[i] >> o) & kMask;
+  return __builtin_amdgcn_alignbit(w[i + 1], w[i], static_cast<uint32_t>(o)) & kMask;
+}
+
+// Fields k0 .. k0 + 3 as the bytes of one word.
+template <int B, int N>
+__device__ __forceinline__ uint32_t cut_bytes(const uint32_t (&w)[N], int k0) {
+  return cut_field<B>(w, k0) | (cut_field<B>(w, k0 + 1) << 8) | (cut_field<B>(w, k0 + 2) << 16) |
+         (cut_field<B>(w, k0 + 3) << 24);
+}
+
+// 64 bits of a value lane's window starting at its first byte (shift in
+// bytes, 0 .. 3).
+template <int NW>
+__device__ __forceinline__ void cut_align(const uint32_t (&w)[NW], uint32_t shift, uint32_t (&o)[2]) {
+  const uint32_t w1 = NW > 1 ? w[NW > 1 ? 1 : 0] : 0u;
+  const uint32_t w2 = NW > 2 ? w[NW > 2 ? 2 : 0] : 0u;
+  o[0] = __builtin_amdgcn_alignbyte(w1, w[0], shift);
+  o[1] = __builtin_amdgcn_alignbyte(w2, w1, shift);
+}
+
+// Operand of the 4 elements whose table index bytes are x.
+__device__ __forceinline__ half8 operand_bytes(uint32_t x, uint32_t lb, const char *lut) {
+  u32x4 w;
+  w[0] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<0>(x, lb));
+  w[1] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<1>(x, lb));
+  w[2] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2>(x, lb));
+  w[3] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<3>(x, lb));
+  return __builtin_bit_cast(half8, w);
+}
+
 // ---- streamed chunk data ----------------------------------------------------
 struct Codes {
   u32x4 ka[2], kr[2];  // K tile t: anchor / residual of channels 32r.. of token 16t + n
   uint32_t va[8], vr[8];  // V: word r of channel 16ct + n
+};
+// Codes of a chunk in b + (8 - b) streams: K tile t (token 16t + n,
+// channels 32r ..) is a whole unit; V channel 16ct + n holds the lane's
+// fields in its window words.
+template <int B>
+struct CutCodes {
+  static constexpr int RB = 8 - B;
+  static constexpr int VA = cut_window_words(B), VR = cut_window_words(RB);
+  uint32_t ka[2][B], kr[2][RB];
+  uint32_t va[8][VA], vr[8][VR];
 };
 struct Scales {
   float2 mnk, rgk, muk, sk, mnv, rgv, muv, sv;  // channels 2l, 2l+1
@@ -313,11 +382,85 @@ struct LaneConst {
   uint32_t lb;         // lane bits of the table address
   uint32_t keep_mask;  // 0 for the high column half, ~0x1FFF for the low one
   double sm2;          // sm_scale * log2(e)
+  // cut streams: byte offsets of the lane's K unit within a chunk of the
+  // anchor / residual stream, of its V window words (channel n, chunk
+  // start), and the window's byte shift
+  uint32_t kca, kcr;
+  uint32_t vwa[3], vwr[3];
+  uint32_t vsa, vsr;
 };
 
-// One chunk: scores, online softmax (base 2), value sum.
-template <bool kFull>
-__device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot, double inv_ks,
+// Lane offsets into b-bit and (8 - b)-bit streams.
+template <int B>
+__device__ __forceinline__ void cut_lane_offsets(LaneConst &lc) {
+  constexpr int RB = 8 - B;
+  lc.kca = static_cast<uint32_t>((4 * lc.n + lc.r) * 4 * B);
+  lc.kcr = static_cast<uint32_t>((4 * lc.n + lc.r) * 4 * RB);
+  const int ia = (lc.r * B) >> 2, ir = (lc.r * RB) >> 2;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    // a window word past the unit is never needed: read the unit's last word
+    lc.vwa[j] = static_cast<uint32_t>(lc.n * 4 * B + 4 * (ia + j < B ? ia + j : B - 1));
+    lc.vwr[j] = static_cast<uint32_t>(lc.n * 4 * RB + 4 * (ir + j < RB ? ir + j : RB - 1));
+  }
+  lc.vsa = static_cast<uint32_t>((lc.r * B) & 3);
+  lc.vsr = static_cast<uint32_t>((lc.r * RB) & 3);
+}
+
+// Codes of chunk c of a tile from b + (8 - b) streams: a tile is 1024
+// units, a chunk 128 (4 * B bytes per unit of the anchor stream).
+template <bool kFull, int B>
+__device__ __forceinline__ void load_codes_cut(CutCodes<B> &cd, const PlanesArg &kp,
+                                               const PlanesArg &vp, size_t tile, int c,
+                                               const LaneConst &lc) {
+  using C = CutCodes<B>;
+  constexpr int RB = C::RB;
+  const size_t unit0 = tile * 1024 + static_cast<size_t>(c) * 128;
+  const char *ka = reinterpret_cast<const char *>(kp.anchor) + unit0 * (4 * B);
+  const char *va = reinterpret_cast<const char *>(vp.anchor) + unit0 * (4 * B);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+      cd.ka[t][i] = load_nt(reinterpret_cast<const uint32_t *>(ka + lc.kca + t * 256 * B + 4 * i));
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int j = 0; j < C::VA; ++j)
+      cd.va[ct][j] = load_nt(reinterpret_cast<const uint32_t *>(va + ct * 64 * B + lc.vwa[j]));
+  if (kFull) {
+    const char *kr = reinterpret_cast<const char *>(kp.residual) + unit0 * (4 * RB);
+    const char *vr = reinterpret_cast<const char *>(vp.residual) + unit0 * (4 * RB);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        cd.kr[t][i] = load_nt(reinterpret_cast<const uint32_t *>(kr + lc.kcr + t * 256 * RB + 4 * i));
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int j = 0; j < C::VR; ++j)
+        cd.vr[ct][j] = load_nt(reinterpret_cast<const uint32_t *>(vr + ct * 64 * RB + lc.vwr[j]));
+  }
+}
+
+// Table index bytes of a K unit: x[w][h] holds elements 8w + 4h .. + 3.
+template <bool kFull, int B>
+__device__ __forceinline__ void cut_key_bytes(const uint32_t (&a)[B], const uint32_t (&r)[8 - B],
+                                              uint32_t (&x)[4][2]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      x[w][h] = cut_bytes<B>(a, 8 * w + 4 * h);
+      if (kFull) x[w][h] = (x[w][h] << (8 - B)) | cut_bytes<8 - B>(r, 8 * w + 4 * h);
+    }
+}
+
+// One chunk: scores, online softmax (base 2), value sum.  kBits = 4 reads
+// the 4-bit planes, other values b + (8 - b) streams.
+template <bool kFull, int kBits, class CodesT>
+__device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot, double inv_ks,
                                               const float *q32, const double *q64,
                                               const LaneConst &lc, const char *lut,
                                               RunState &st, float *srow) {
@@ -348,15 +491,26 @@ __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot,
   // ---- scores: S^T = Yk * Q' (tiles t = 0, 1 share each Q' step) ----
   floatx4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
   {
+    // 4 + 4: code bytes of even / odd elements (full) or the anchor words
+    // (draft); cuts: table index bytes of elements 8w + 4h ..
     uint32_t e0[4], o0[4], e1[4], o1[4];
-    const uint32_t ka0[4] = {cd.ka[0][0], cd.ka[0][1], cd.ka[0][2], cd.ka[0][3]};
-    const uint32_t ka1[4] = {cd.ka[1][0], cd.ka[1][1], cd.ka[1][2], cd.ka[1][3]};
-    if (kFull) {
+    uint32_t x0[4][2], x1[4][2];
+    if constexpr (kBits == 4) {
+      const uint32_t ka0[4] = {cd.ka[0][0], cd.ka[0][1], cd.ka[0][2], cd.ka[0][3]};
+      const uint32_t ka1[4] = {cd.ka[1][0], cd.ka[1][1], cd.ka[1][2], cd.ka[1][3]};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        code_bytes(ka0[w], cd.kr[0][w], e0[w], o0[w]);
-        code_bytes(ka1[w], cd.kr[1][w], e1[w], o1[w]);
+        if (kFull) {
+          code_bytes(ka0[w], cd.kr[0][w], e0[w], o0[w]);
+          code_bytes(ka1[w], cd.kr[1][w], e1[w], o1[w]);
+        } else {
+          e0[w] = ka0[w];
+          e1[w] = ka1[w];
+        }
       }
+    } else {
+      cut_key_bytes<kFull, kBits>(cd.ka[0], cd.kr[0], x0);
+      cut_key_bytes<kFull, kBits>(cd.ka[1], cd.kr[1], x1);
     }
     const float *qrow = q32 + (n & 7) * kQ32Stride + 32 * r;
 #pragma unroll
@@ -371,7 +525,10 @@ __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot,
       const half8 b = __builtin_bit_cast(half8, bw);
       half8 a0, a1;
       const int w = stp >> 1;
-      if (kFull) {
+      if constexpr (kBits != 4) {
+        a0 = operand_bytes(x0[w][stp & 1], lc.lb, lut);
+        a1 = operand_bytes(x1[w][stp & 1], lc.lb, lut);
+      } else if (kFull) {
         if (stp & 1) {
           a0 = operand_full<1>(e0[w], o0[w], lc.lb, lut);
           a1 = operand_full<1>(e1[w], o1[w], lc.lb, lut);
@@ -381,11 +538,11 @@ __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot,
         }
       } else {
         if (stp & 1) {
-          a0 = operand_draft<1>(ka0[w], lc.lb, lut);
-          a1 = operand_draft<1>(ka1[w], lc.lb, lut);
+          a0 = operand_draft<1>(e0[w], lc.lb, lut);
+          a1 = operand_draft<1>(e1[w], lc.lb, lut);
         } else {
-          a0 = operand_draft<0>(ka0[w], lc.lb, lut);
-          a1 = operand_draft<0>(ka1[w], lc.lb, lut);
+          a0 = operand_draft<0>(e0[w], lc.lb, lut);
+          a1 = operand_draft<0>(e1[w], lc.lb, lut);
         }
       }
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b, s0, 0, 0, 0);
@@ -461,7 +618,19 @@ __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot,
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
     half8 y0, y1;
-    if (kFull) {
+    if constexpr (kBits != 4) {
+      uint32_t win[2];
+      cut_align<CodesT::VA>(cd.va[ct], lc.vsa, win);
+      uint32_t xa = cut_bytes<kBits>(win, 0), xb = cut_bytes<kBits>(win, 4);
+      if (kFull) {
+        uint32_t wr[2];
+        cut_align<CodesT::VR>(cd.vr[ct], lc.vsr, wr);
+        xa = (xa << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 0);
+        xb = (xb << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 4);
+      }
+      y0 = operand_bytes(xa, lc.lb, lut);
+      y1 = operand_bytes(xb, lc.lb, lut);
+    } else if (kFull) {
       uint32_t e, o;
       code_bytes(cd.va[ct], cd.vr[ct], e, o);
       y0 = operand_full<0>(e, o, lc.lb, lut);
@@ -482,7 +651,7 @@ __device__ __forceinline__ void compute_chunk(const Codes &cd, const char *slot,
   }
 }
 
-template <bool kFull>
+template <bool kFull, int kBits>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
     const uint16_t *__restrict__ q, PlanesArg kp, PlanesArg vp,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -517,7 +686,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   lc.voff = static_cast<uint32_t>(lc.n * 16 + lc.r * 4);
   lc.soff = static_cast<uint32_t>(lc.lane * 8);
   lc.keep_mask = lc.lo ? 0xFFFFE000u : 0u;
-  lc.lb = kFull ? static_cast<uint32_t>(lc.lane * 4) : static_cast<uint32_t>((lc.lane & 31) * 8);
+  // 4-byte table rows for the full code and for every cut's index bytes;
+  // 8-byte pair rows for the 4 + 4 draft
+  constexpr bool kWordTable = kFull || kBits != 4;
+  lc.lb = kWordTable ? static_cast<uint32_t>(lc.lane * 4) : static_cast<uint32_t>((lc.lane & 31) * 8);
+  if constexpr (kBits != 4) cut_lane_offsets<kBits>(lc);
   lc.sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
 
   // ---- this wave's run of chunks ----
@@ -553,7 +726,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
 
   // Codes of NB chunks are held per wave: the chunk being computed and the
   // next D = NB - 1 in flight (the draft's chunks are smaller, so it looks
-  // further ahead).  Scales run one chunk further ahead than codes: the step
+  // further ahead; drafts of more than 4 bits hold as many words as the
+  // full code and look as far).  Scales run one chunk further ahead than codes: the step
   // of chunk c requests the scales of chunk c + D + 1 and then the codes of
   // chunk c + D, so the scales staged at the end of a step were requested
   // before the codes that step waited for.  A wave whose run is short thus
@@ -562,21 +736,36 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   // on an absent page reads chunk 0 of pool page 0 instead, and is not
   // computed -- so the wait counts the compiler derives are exact and never
   // wait for loads that are still ahead in the pipeline.
-  constexpr int NB = kFull ? 2 : 3;
+  constexpr int NB = (kFull || kBits > 4) ? 2 : 3;
   constexpr int D = NB - 1;
-  Codes cds[NB];    // codes of chunk c in buffer (c - cb) % NB
+  using CodesT = std::conditional_t<kBits == 4, Codes, CutCodes<kBits>>;
+  CodesT cds[NB];   // codes of chunk c in buffer (c - cb) % NB
   Scales scs[NB];   // scales of chunk c in buffer (c - cb) % NB
   long long pgs[NB];  // page of chunk c, and after its step of chunk c + NB
   auto tile_of = [&](long long pg) { return pg >= 0 ? static_cast<size_t>(pg) * s.heads + h : 0; };
   auto chunk_of = [&](long long pg, int c) { return pg >= 0 ? (c & 7) : 0; };
   auto page_in_run = [&](int c) -> long long { return c < ce ? page_of(c) : -1; };
+  auto load_chunk = [&](CodesT &cd, long long pg, int c) {
+    if constexpr (kBits == 4)
+      load_codes<kFull>(cd, kp, vp, tile_of(pg), chunk_of(pg, c), lc.koff, lc.voff);
+    else
+      load_codes_cut<kFull, kBits>(cd, kp, vp, tile_of(pg), chunk_of(pg, c), lc);
+  };
   // ---- set-up loads: this thread's table words and its lane's query
   // values, issued ahead of the chunk loads so that waiting for them never
   // waits for chunk data ----
   uint32_t tw0, tw1;
   {
     const int e = tid & 255;
-    if (kFull) {
+    if constexpr (kBits != 4 && !kFull) {
+      // row f: the draft of anchor field f (sign-extended), the code
+      // a * 2^(8-b) + 2^(7-b) - 1
+      constexpr int RB = 8 - kBits;
+      const int f = e & ((1 << kBits) - 1);
+      const int a = f >= (1 << (kBits - 1)) ? f - (1 << kBits) : f;
+      tw0 = tab.full[(a * (1 << RB) + (1 << (RB - 1)) - 1) & 255];
+      tw1 = tw0;
+    } else if (kFull) {
       tw0 = tab.full[e];
       tw1 = tw0;
     } else {
@@ -607,12 +796,12 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     load_scales(scs[d + 1], kp, vp, tile_of(pgs[d + 1]), chunk_of(pgs[d + 1], cb + d + 1), lc.soff);
-    load_codes<kFull>(cds[d], kp, vp, tile_of(pgs[d]), chunk_of(pgs[d], cb + d), lc.koff, lc.voff);
+    load_chunk(cds[d], pgs[d], cb + d);
   }
 
   // ---- tables (replicated rows) ----
   {
-    const u32x4 v = kFull ? u32x4{tw0, tw0, tw0, tw0} : u32x4{tw0, tw1, tw0, tw1};
+    const u32x4 v = kWordTable ? u32x4{tw0, tw0, tw0, tw0} : u32x4{tw0, tw1, tw0, tw1};
     u32x4 *dst = reinterpret_cast<u32x4 *>(lut + (tid & 255) * 256 + (tid >> 8) * 128);
 #pragma unroll
     for (int k = 0; k < 8; ++k) dst[k] = v;
@@ -671,10 +860,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
       const long long cur = pgs[J];
       pgs[J] = page_in_run(c + D + 1);  // buffer J next holds chunk c + NB = c + D + 1
       load_scales(scs[J], kp, vp, tile_of(pgs[J]), chunk_of(pgs[J], c + D + 1), lc.soff);
-      load_codes<kFull>(cds[JD], kp, vp, tile_of(pgs[JD]), chunk_of(pgs[JD], c + D), lc.koff, lc.voff);
+      load_chunk(cds[JD], pgs[JD], c + D);
       if (cur >= 0) {
         wave_lds_sync();
-        compute_chunk<kFull>(cds[J], slots + slot * kSlotBytes, slot ? ks1 : ks0, q32, q64, lc, lut,
+        compute_chunk<kFull, kBits>(cds[J], slots + slot * kSlotBytes, slot ? ks1 : ks0, q32, q64, lc, lut,
                              st, srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
       }
       const double k = scale_stage(scs[J1], slots + (slot ^ 1) * kSlotBytes, lc.lane, qmax);
@@ -883,6 +1072,28 @@ MfmaTables build_mfma_tables() {
   return t;
 }
 
+template <bool kFull, int kBits>
+void launch_mfma_kernel(dim3 grid, hipStream_t stream, const uint16_t *q, const PlanesArg &k,
+                        const PlanesArg &v, const int32_t *block_table, const int32_t *seq_lens,
+                        const AttnShape &s, float sm_scale, float *out, float *scores,
+                        void *workspace, const MfmaTables &tables) {
+  hipLaunchKernelGGL((attn_mfma_kernel<kFull, kBits>), grid, dim3(kThreads), 0, stream, q, k, v,
+                     block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
+}
+
+template <int kBits>
+void launch_mfma_bits(bool full, dim3 grid, hipStream_t stream, const uint16_t *q,
+                      const PlanesArg &k, const PlanesArg &v, const int32_t *block_table,
+                      const int32_t *seq_lens, const AttnShape &s, float sm_scale, float *out,
+                      float *scores, void *workspace, const MfmaTables &tables) {
+  if (full)
+    launch_mfma_kernel<true, kBits>(grid, stream, q, k, v, block_table, seq_lens, s, sm_scale, out,
+                                    scores, workspace, tables);
+  else
+    launch_mfma_kernel<false, kBits>(grid, stream, q, k, v, block_table, seq_lens, s, sm_scale,
+                                     out, scores, workspace, tables);
+}
+
 }  // namespace
 
 bool attention_mfma_supported(int group) { return group >= 1 && group <= kHeads; }
@@ -892,9 +1103,10 @@ int attention_mfma_target_blocks() { return 256; }
 hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
                                  const int32_t *block_table, const int32_t *seq_lens,
                                  const AttnShape &s, float sm_scale, bool full, float *out,
-                                 float *scores, void *workspace, bool merge, hipStream_t stream) {
+                                 float *scores, void *workspace, bool merge, hipStream_t stream,
+                                 int anchor_bits) {
   static const MfmaTables tables = build_mfma_tables();
-  if (s.parts > kCombMaxSplits) return hipErrorInvalidValue;
+  if (s.parts > kCombMaxSplits || anchor_bits < 1 || anchor_bits > 7) return hipErrorInvalidValue;
   if (s.pool_pages <= 0) {
     // no page can be read: every request's context is empty
     const size_t n = static_cast<size_t>(s.batch) * s.q_heads * kDim;
@@ -903,12 +1115,19 @@ hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const Pl
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>(static_cast<long long>(s.batch) * s.heads * s.splits));
-  if (full)
-    hipLaunchKernelGGL(attn_mfma_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v,
-                       block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
-  else
-    hipLaunchKernelGGL(attn_mfma_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v,
-                       block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
+  auto go = [&](auto bits) {
+    launch_mfma_bits<decltype(bits)::value>(full, grid, stream, q, k, v, block_table, seq_lens, s,
+                                            sm_scale, out, scores, workspace, tables);
+  };
+  switch (anchor_bits) {
+    case 1: go(std::integral_constant<int, 1>()); break;
+    case 2: go(std::integral_constant<int, 2>()); break;
+    case 3: go(std::integral_constant<int, 3>()); break;
+    case 5: go(std::integral_constant<int, 5>()); break;
+    case 6: go(std::integral_constant<int, 6>()); break;
+    case 7: go(std::integral_constant<int, 7>()); break;
+    default: go(std::integral_constant<int, 4>()); break;
+  }
   if (s.parts == 1 || !merge) return hipGetLastError();  // output or partials written
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -122,11 +122,14 @@ bool attention_mfma_supported(int group);
 int attention_mfma_target_blocks();
 // Page runs of every (row, KV head): writes `out` itself when parts == 1,
 // else the split partials.  With merge set and parts > 1 the partials are
-// merged into `out` inside the launch.
+// merged into `out` inside the launch.  anchor_bits 4 reads the 4-bit
+// planes; 1 .. 7 otherwise read b + (8 - b) streams (k.anchor, v.anchor:
+// b bits per element; k.residual, v.residual: 8 - b).
 hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
                                  const int32_t *block_table, const int32_t *seq_lens,
                                  const AttnShape &s, float sm_scale, bool full, float *out,
-                                 float *scores, void *workspace, bool merge, hipStream_t stream);
+                                 float *scores, void *workspace, bool merge, hipStream_t stream,
+                                 int anchor_bits = 4);
 hipError_t launch_attention_mfma_combine(const AttnShape &s, const void *workspace, float *out,
                                          hipStream_t stream);
 
@@ -140,12 +143,13 @@ hipError_t launch_attention_tail_part(const uint16_t *q, const uint16_t *tail_k,
                                       int tail_cap, const AttnShape &s, float sm_scale, bool base2,
                                       void *workspace, hipStream_t stream);
 
+// anchor_bits other than 4: b + (8 - b) streams, matrix-core groups only.
 hipError_t launch_attention(const uint16_t *q, const PlanesArg &k,
                             const PlanesArg &v, const int32_t *block_table,
                             const int32_t *seq_lens, const AttnShape &s,
                             float sm_scale, bool full, float *out,
                             float *scores, void *workspace,
-                            hipStream_t stream);
+                            hipStream_t stream, int anchor_bits = 4);
 
 // Pages plus the bf16 tail page, merged into out [batch][Hq][128]
 // (s from attention_shape_tail).

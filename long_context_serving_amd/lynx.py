@@ -74,6 +74,10 @@ _lib.lynx_split_planes.restype = ctypes.c_int
 _lib.lynx_dequantize_split.argtypes = [_P, _P, _i32, ctypes.POINTER(_CPlanes), _i64, _i32, _i32,
                                        _i32, _P, _P]
 _lib.lynx_dequantize_split.restype = ctypes.c_int
+_lib.lynx_decode_attention_split.argtypes = [_P, ctypes.POINTER(_CPlanes), ctypes.POINTER(_CPlanes),
+                                             _i32, _i32, _P, _P, _i32, _i32, _i32, _i32, _i32, _i64,
+                                             ctypes.c_float, _P, _P, _P, _sz, _P]
+_lib.lynx_decode_attention_split.restype = ctypes.c_int
 _lib.lynx_status_string.argtypes = [ctypes.c_int]
 _lib.lynx_status_string.restype = ctypes.c_char_p
 _lib.lynx_code_thresholds.argtypes = [_P]
@@ -349,4 +353,40 @@ def dequantize_split(anchor: torch.Tensor, residual: Optional[torch.Tensor], anc
     _check(_lib.lynx_dequantize_split(_ptr(anchor), _ptr(residual), anchor_bits, ctypes.byref(cp), P,
                                       H, HEAD_DIM, scales.role, _ptr(out), _stream(stream)),
            "lynx_dequantize_split")
+    return out
+
+
+def cut_planes(p: Planes, anchor_bits: int, stream=None) -> Planes:
+    """The planes of p re-cut b + (8 - b): anchor and residual are the two
+    streams, the scales are p's own tensors (shared, not copied)."""
+    a, r = split_planes(p, anchor_bits, stream)
+    return Planes(a, r, p.page_min, p.page_range, p.chunk_mean, p.chunk_maxabs,
+                  num_pages=p.num_pages, heads=p.heads, role=p.role)
+
+
+def decode_attention_split(q: torch.Tensor, k: Planes, v: Planes, anchor_bits: int, max_pages: int,
+                           full: bool = True, block_table: Optional[torch.Tensor] = None,
+                           seq_lens: Optional[torch.Tensor] = None,
+                           sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                           scores: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """decode_attention over b + (8 - b) streams (k, v from cut_planes with
+    the same anchor_bits); full=False is the draft of the b-bit anchor."""
+    q = _bf16_bits(q)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][Hq][128] bf16 tensor")
+    B, Hq, D = q.shape
+    H = k.heads
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, Hq, max_pages, q.device)
+    kc, vc = k.c(), v.c()
+    _check(_lib.lynx_decode_attention_split(
+        _ptr(q), ctypes.byref(kc), ctypes.byref(vc), anchor_bits, int(bool(full)), _ptr(block_table),
+        _ptr(seq_lens), B, H, Hq, D, max_pages, min(k.num_pages, v.num_pages), float(sm_scale),
+        _ptr(out), _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream)),
+        "lynx_decode_attention_split")
     return out

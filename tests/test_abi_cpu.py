@@ -170,6 +170,30 @@ def test_cut_entry_points_reject_bad_arguments(lib):
     assert lib.lynx_dequantize_split(a, P(0x90008), 3, ctypes.byref(pl), 4, 8, 128, 1, out, None) == -3
     assert lib.lynx_dequantize_split(a, None, 3, ctypes.byref(pl), 0, 8, 128, 1, None, None) == 0
 
+    # fused attention over cut streams
+    lib.lynx_decode_attention_split.argtypes = [P, ctypes.POINTER(CPlanes), ctypes.POINTER(CPlanes),
+                                                ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int64, ctypes.c_float, P, P,
+                                                P, ctypes.c_size_t, P]
+    kp, vp = _fake_planes(0x10000), _fake_planes(0x40000)
+    q, o, ws = P(0x20000), P(0x30000), P(0x50000)
+
+    def acall(bits=3, full=1, B=2, H=8, Hq=64, D=128, mp=4, pool=8, qq=q, k=kp, v=vp, wsb=1 << 20):
+        return lib.lynx_decode_attention_split(qq, ctypes.byref(k), ctypes.byref(v), bits, full, None,
+                                               None, B, H, Hq, D, mp, pool, 0.088, o, None, ws, wsb,
+                                               None)
+    assert acall(bits=0) == -7
+    assert acall(bits=8) == -7
+    assert acall(D=64) == -2
+    assert acall(Hq=96) == -2            # group 12: cut streams need the matrix-core kernel
+    assert acall(pool=7) == -2           # batch * max_pages pages must exist without a block table
+    assert acall(qq=None) == -1
+    nores = CPlanes(kp.anchor, None, kp.page_min, kp.page_range, kp.chunk_mean, kp.chunk_maxabs)
+    assert acall(k=nores) == -1          # the full code reads the residual stream
+    assert acall(wsb=0) == -4
+    assert acall(B=0) == 0
+
 
 def test_status_strings(lib):
     lib.lynx_status_string.restype = ctypes.c_char_p

@@ -91,3 +91,118 @@ def test_empty_cut_is_a_noop(lynx):
     pl = lynx.alloc_planes(0, 2, 0)
     a, r = lynx.split_planes(pl, 3)
     assert a.numel() == 0 and r.numel() == 0
+
+
+# ---------------------------------------------------------------------------
+# Fused decode attention over the streams of a cut
+# ---------------------------------------------------------------------------
+ATOL_ATTN = 2e-3
+RTOL_ATTN = 1e-5
+SM = float(np.float32(1.0 / np.sqrt(128.0)))
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def cut_oracle_attention(ek, ev, q_bits, page_lists, b, full):
+    """Oracle attention over the oracle's b + (8 - b) reconstruction; request
+    i reads pool pages page_lists[i]."""
+    ak, rk = oracle.split_bits(ek["codes"], b)
+    av, rv = oracle.split_bits(ev["codes"], b)
+    kh = oracle.dequant_bits(ak, rk if full else None, b, ek)
+    vh = oracle.dequant_bits(av, rv if full else None, b, ev)
+    q = oracle.bf16_bits_to_float(q_bits).astype(np.float64)
+    H, D = kh.shape[2], kh.shape[3]
+    return np.stack([oracle.attention(q[i:i + 1], kh[p].reshape(1, -1, H, D),
+                                      vh[p].reshape(1, -1, H, D), SM)[0]
+                     for i, p in enumerate(page_lists)])
+
+
+def check_attention(got, ref, label):
+    got = got.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    bound = ATOL_ATTN + RTOL_ATTN * np.abs(ref)
+    print("%s: max abs err %.3g (max |out| %.1f), max err/bound %.3f" %
+          (label, err.max(), np.abs(ref).max(), (err / bound).max()), flush=True)
+    assert (err <= bound).all(), label
+
+
+def _cut_case(lynx, w, tokens=None):
+    xk = synth.kv_pages(w, 0, 0, 0, tokens=tokens)
+    xv = synth.kv_pages(w, 0, 1, 0, tokens=tokens)
+    pk = lynx.quantize_pages(to_dev(xk), lynx.ROLE_KEY)
+    pv = lynx.quantize_pages(to_dev(xv), lynx.ROLE_VALUE)
+    return pk, pv, oracle.encode(xk), oracle.encode(xv), synth.queries(w)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 5, 6, 7])
+def test_cut_attention_tiny(lynx, b):
+    w = synth.WORKLOADS["tiny"]
+    pk, pv, ek, ev, q = _cut_case(lynx, w)
+    ck, cv = lynx.cut_planes(pk, b), lynx.cut_planes(pv, b)
+    qd = to_dev(q)
+    print("cut attention tiny b=%d" % b, flush=True)
+    # the full code of any cut is the 4 + 4 full code: the same operands
+    ref_full = lynx.decode_attention(qd, pk, pv, w.pages, full=True, sm_scale=SM)
+    got_full = lynx.decode_attention_split(qd, ck, cv, b, w.pages, full=True, sm_scale=SM)
+    torch.cuda.synchronize()
+    assert torch.equal(got_full, ref_full)
+    got = lynx.decode_attention_split(qd, ck, cv, b, w.pages, full=False, sm_scale=SM)
+    torch.cuda.synchronize()
+    check_attention(got, cut_oracle_attention(ek, ev, q, [list(range(w.pages))], b, False),
+                    "tiny draft b=%d" % b)
+
+
+def test_cut_attention_ctx32k(lynx):
+    w = synth.WORKLOADS["ctx32k"]
+    pk, pv, ek, ev, q = _cut_case(lynx, w)
+    qd = to_dev(q)
+    # 4-bit streams are the planes: the cut call equals the decode calls
+    for full in (False, True):
+        a = lynx.decode_attention_split(qd, lynx.cut_planes(pk, 4), lynx.cut_planes(pv, 4), 4,
+                                        w.pages, full=full, sm_scale=SM)
+        r = lynx.decode_attention(qd, pk, pv, w.pages, full=full, sm_scale=SM)
+        torch.cuda.synchronize()
+        assert torch.equal(a, r), full
+    ref_full = lynx.decode_attention(qd, pk, pv, w.pages, full=True, sm_scale=SM)
+    for b in (2, 3, 5, 6):
+        print("cut attention ctx32k b=%d" % b, flush=True)
+        ck, cv = lynx.cut_planes(pk, b), lynx.cut_planes(pv, b)
+        got_full = lynx.decode_attention_split(qd, ck, cv, b, w.pages, full=True, sm_scale=SM)
+        got = lynx.decode_attention_split(qd, ck, cv, b, w.pages, full=False, sm_scale=SM)
+        torch.cuda.synchronize()
+        assert torch.equal(got_full, ref_full), b
+        check_attention(got, cut_oracle_attention(ek, ev, q, [list(range(w.pages))], b, False),
+                        "ctx32k draft b=%d" % b)
+
+
+def test_cut_attention_ragged_groups_and_skipped_pages(lynx):
+    rng = np.random.default_rng(29)
+    for H, Hq, b in ((2, 6, 3), (4, 4, 7), (1, 8, 1)):
+        P_pool = 9
+        xk = synth.laplace_pages(P_pool, H, 128, seed=H * 10 + 1, scale_channels=((0, 2, 80.0),))
+        xv = synth.laplace_pages(P_pool, H, 128, seed=H * 10 + 2, scale_channels=((H - 1, 100, 90.0),))
+        pk = lynx.quantize_pages(to_dev(xk), lynx.ROLE_KEY)
+        pv = lynx.quantize_pages(to_dev(xv), lynx.ROLE_VALUE)
+        ek, ev = oracle.encode(xk), oracle.encode(xv)
+        ck, cv = lynx.cut_planes(pk, b), lynx.cut_planes(pv, b)
+        max_pages, lengths = 4, [2, 4, 1]
+        bt = np.full((3, max_pages), -1, np.int32)
+        pages = []
+        for i, n in enumerate(lengths):
+            pg = rng.choice(P_pool, size=n, replace=False)
+            bt[i, :n] = pg
+            pages.append(list(pg))
+        bt[1, 1] = -3  # skipped inside the request's length
+        pages[1] = [p for i, p in enumerate(pages[1]) if i != 1]
+        q = synth.float_to_bf16_bits(rng.laplace(0, 1, (3, Hq, 128)).astype(np.float32))
+        btd = torch.from_numpy(bt).cuda()
+        sl = torch.from_numpy(np.asarray([256 * n for n in lengths], np.int32)).cuda()
+        print("cut attention ragged H=%d Hq=%d b=%d" % (H, Hq, b), flush=True)
+        for full in (False, True):
+            got = lynx.decode_attention_split(to_dev(q), ck, cv, b, max_pages, full=full,
+                                              block_table=btd, seq_lens=sl, sm_scale=SM)
+            torch.cuda.synchronize()
+            check_attention(got, cut_oracle_attention(ek, ev, q, pages, b, full),
+                            "ragged H=%d Hq=%d b=%d full=%s" % (H, Hq, b, full))
