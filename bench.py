@@ -262,10 +262,11 @@ def progressive_main(args):
 
 
 def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
-    """The b + (8 - b) cuts after the timed region: re-cutting one tensor's
-    planes into the two streams, the draft reconstruction from the anchor
-    stream, and the fused draft decode attention over the K and V anchor
-    streams, each cycled over the buffer sets (cache-cold)."""
+    """The b + (8 - b) cuts after the timed region: encoding one tensor
+    straight into the two streams, re-cutting its 4 + 4 planes into them,
+    the draft reconstruction from the anchor stream, and the fused draft
+    decode attention over the K and V anchor streams, each cycled over the
+    buffer sets (cache-cold)."""
     import torch
     from long_context_serving_amd import lynx
     elems = w.batch * w.tokens * w.kv_heads * w.head_dim
@@ -276,6 +277,10 @@ def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
         outs = torch.empty((w.pages * w.batch, 256, w.kv_heads, w.head_dim), dtype=torch.float32,
                            device=sets[0]["pk"].anchor.device)
         split_calls = [lambda e=e: lynx.split_planes(e["pk"], b) for e in sets]
+        enc_out = lynx.alloc_cut_planes(w.pages * w.batch, w.kv_heads, lynx.ROLE_KEY, b,
+                                        sets[0]["pk"].anchor.device)
+        enc_calls = [lambda e=e: lynx.quantize_pages_split(e["k"], lynx.ROLE_KEY, b, out=enc_out)
+                     for e in sets]
         draft_calls = [lambda e=e, st=st: lynx.dequantize_split(st[0], None, b, e["pk"], out=outs)
                        for e, st in zip(sets, streams)]
         cut_k = [lynx.cut_planes(e["pk"], b) for e in sets]
@@ -283,31 +288,32 @@ def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
         attn_calls = [lambda ck=ck, cv=cv: lynx.decode_attention_split(
             q, ck, cv, b, w.pages, full=False, sm_scale=sm, out=out_attn, workspace=ws)
             for ck, cv in zip(cut_k, cut_v)]
-        for c in attn_calls:
-            c()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for c in attn_calls:
-                c()
         times = []
-        for calls in (split_calls, draft_calls, [g.replay]):
+        for calls in (split_calls, draft_calls, attn_calls, enc_calls):
             for c in calls:
                 c()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for c in calls:
+                    c()
+            with torch.cuda.stream(stream):
+                g.replay()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
                 e0.record(stream)
                 for _ in range(4):
-                    for c in calls:
-                        c()
+                    g.replay()
                 e1.record(stream)
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) / (4 * len(sets)))  # one call per set per pass
+            times.append(e0.elapsed_time(e1) / (4 * len(sets)))  # one call per set per replay
         split_bytes = elems * 2.0                    # 4 + 4 planes in, both streams out
         draft_bytes = elems * (b / 8.0 + scale_bytes + 4.0)
         attn_bytes = 2 * elems * (b / 8.0 + scale_bytes)  # K and V anchor streams and scales
         res["%d+%d" % (b, 8 - b)] = {
+            "encode_direct_us": times[3] * 1e3,
+            "encode_direct_GBps": elems * 3.28125 / (times[3] * 1e-3) / 1e9,
             "draft_attention_us": times[2] * 1e3,
             "draft_attention_GBps": attn_bytes / (times[2] * 1e-3) / 1e9,
             "split_us": times[0] * 1e3, "split_GBps": split_bytes / (times[0] * 1e-3) / 1e9,
@@ -315,8 +321,8 @@ def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
             "draft_dequant_GBps": draft_bytes / (times[1] * 1e-3) / 1e9,
             "anchor_stream_bytes_per_elem": b / 8.0}
     return {"tensor": "K of one buffer set per call, all %d sets in turn" % len(sets),
-            "timing": "events around 4 passes over the sets, after the timed region (packer and "
-                      "dequantizer: eager launches; draft attention: one HIP graph over the sets)",
+            "timing": "events around 4 replays of a HIP graph of one call per set, after the "
+                      "timed region",
             "by_cut": res}
 
 

@@ -224,6 +224,19 @@ int lynx_decode_attention_full(const uint16_t *q, const lynx_planes *k,
  * BAD_ARG (anchor_bits, role), MISALIGNED, DEVICE, HIP.
  */
 size_t lynx_split_stream_bytes(int64_t num_pages, int32_t num_kv_heads, int32_t bits);
+/*
+ * lynx_quantize_pages_split: lynx_quantize_pages writing a b + (8 - b) cut
+ * directly: out->anchor receives the anchor stream (anchor_bits * 4096
+ * bytes per tile), out->residual the residual stream ((8 - anchor_bits) *
+ * 4096), the scale pointers the scales; byte-identical to
+ * lynx_quantize_pages followed by lynx_split_planes.  anchor_bits 1 .. 7
+ * (4: the 4-bit planes).  Errors: as lynx_quantize_pages, plus BAD_ARG for
+ * anchor_bits.
+ */
+int lynx_quantize_pages_split(const uint16_t *kv, int64_t num_pages,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              int32_t role, int32_t anchor_bits,
+                              const lynx_planes *out, void *stream);
 int lynx_split_planes(const lynx_planes *in, int64_t num_pages,
                       int32_t num_kv_heads, int32_t head_dim,
                       int32_t anchor_bits, uint8_t *anchor_out,

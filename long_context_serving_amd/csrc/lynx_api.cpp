@@ -221,6 +221,24 @@ int lynx_quantize_pages(const uint16_t *kv, int64_t num_pages, int32_t num_kv_he
   return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
 }
 
+int lynx_quantize_pages_split(const uint16_t *kv, int64_t num_pages, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t role, int32_t anchor_bits,
+                              const lynx_planes *out, void *stream) {
+  int rc = check_tile_shape(num_pages, num_kv_heads, head_dim, role);
+  if (rc) return rc;
+  if (anchor_bits < 1 || anchor_bits > 7) return LYNX_ERR_BAD_ARG;
+  if (num_pages == 0) return LYNX_OK;
+  if (!kv) return LYNX_ERR_NULL_ARG;
+  rc = check_planes(out, true);
+  if (rc) return rc;
+  if (!aligned16(kv)) return LYNX_ERR_MISALIGNED;
+  rc = check_device();
+  if (rc) return rc;
+  const hipError_t e = lynx::launch_encode(kv, num_pages, num_kv_heads, role, to_arg(out),
+                                           static_cast<hipStream_t>(stream), anchor_bits);
+  return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
+}
+
 int lynx_dequantize_anchor(const lynx_planes *in, int64_t num_pages, int32_t num_kv_heads,
                            int32_t head_dim, int32_t role, float *out, void *stream) {
   return dequant_common(in, num_pages, num_kv_heads, head_dim, role, out, stream, false);

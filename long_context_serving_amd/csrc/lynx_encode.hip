@@ -21,6 +21,7 @@
 // -ffp-contract=off), reciprocals are correctly rounded, the chunk sum is
 // exact in fp64, the page range and chunk max-abs keep 7 significant bits
 // (rounded up), and the level m is exactly #{k >= 1 : u >= T[k]}.
+#include "lynx_cut.h"
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -177,8 +178,10 @@ __device__ __forceinline__ uint32_t codes4(float d0, float d1, float d2, float d
 // (cg, r) holds channels 8cg..8cg+7 of the 8 tokens chunk_token(r, 0..7).
 // Two workgroups fit on a CU (at most 128 VGPRs), so that one streams its
 // tile in while the other computes.  Addresses are a wave-uniform base plus
-// 32-bit lane offsets.
-template <int kRole>
+// 32-bit lane offsets.  kBits = 4 writes the 4-bit planes; other values
+// write the b + (8 - b) streams of the same codes (out.anchor: b bits per
+// element, out.residual: 8 - b), re-cut from the staged planes.
+template <int kRole, int kBits>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, EncodeTables tab) {
   const int c = threadIdx.x >> 6;  // chunk = wave
@@ -353,15 +356,35 @@ void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, En
     }
     __syncthreads();
     // write-out: 1024 units of 16 B per plane, two per thread, contiguous
-    char *an = reinterpret_cast<char *>(out.anchor) + static_cast<size_t>(tile) * kPlaneTileBytes;
-    char *re = reinterpret_cast<char *>(out.residual) + static_cast<size_t>(tile) * kPlaneTileBytes;
+    // (or, for a cut, b and 8 - b words per unit)
+    constexpr int kUnits = kPlaneTileBytes / 16;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int unit = k * kEncThreads + threadIdx.x;
       const int widx = kRole == LYNX_ROLE_KEY ? (unit >> 2) * 20 + (unit & 3) * 4
                                               : (unit ^ ((unit >> 3) & 7)) * 4;
-      store_stream(an + unit * 16, *reinterpret_cast<const uint4 *>(&s_pl[0][widx]));
-      store_stream(re + unit * 16, *reinterpret_cast<const uint4 *>(&s_pl[1][widx]));
+      const uint4 a = *reinterpret_cast<const uint4 *>(&s_pl[0][widx]);
+      const uint4 rr = *reinterpret_cast<const uint4 *>(&s_pl[1][widx]);
+      if constexpr (kBits == 4) {
+        char *an = reinterpret_cast<char *>(out.anchor) + static_cast<size_t>(tile) * kPlaneTileBytes;
+        char *re = reinterpret_cast<char *>(out.residual) + static_cast<size_t>(tile) * kPlaneTileBytes;
+        store_stream(an + unit * 16, a);
+        store_stream(re + unit * 16, rr);
+      } else {
+        constexpr int RB = 8 - kBits;
+        const uint32_t a4[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t r4[4] = {rr.x, rr.y, rr.z, rr.w};
+        uint32_t wa[kBits], wr[RB];
+        cut::unit<kBits>(a4, r4, wa, wr);
+        uint32_t *an = reinterpret_cast<uint32_t *>(out.anchor) +
+                       (static_cast<size_t>(tile) * kUnits + unit) * kBits;
+        uint32_t *re = reinterpret_cast<uint32_t *>(out.residual) +
+                       (static_cast<size_t>(tile) * kUnits + unit) * RB;
+#pragma unroll
+        for (int i = 0; i < kBits; ++i) __builtin_nontemporal_store(wa[i], an + i);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) __builtin_nontemporal_store(wr[i], re + i);
+      }
     }
   }
 }
@@ -407,18 +430,34 @@ hipError_t launch_code_map_check(uint32_t begin, uint32_t end, unsigned long lon
   return hipGetLastError();
 }
 
+namespace {
+template <int kBits>
+void launch_encode_bits(const uint16_t *kv, unsigned blocks, int heads, int role,
+                        const PlanesArg &out, const EncodeTables &tab, hipStream_t stream) {
+  if (role == LYNX_ROLE_KEY)
+    hipLaunchKernelGGL((encode_kernel<LYNX_ROLE_KEY, kBits>), dim3(blocks), dim3(kEncThreads), 0,
+                       stream, kv, heads, out, tab);
+  else
+    hipLaunchKernelGGL((encode_kernel<LYNX_ROLE_VALUE, kBits>), dim3(blocks), dim3(kEncThreads), 0,
+                       stream, kv, heads, out, tab);
+}
+}  // namespace
+
 hipError_t launch_encode(const uint16_t *kv, int64_t num_pages, int heads,
-                         int role, const PlanesArg &out, hipStream_t stream) {
+                         int role, const PlanesArg &out, hipStream_t stream, int anchor_bits) {
   if (num_pages == 0) return hipSuccess;
-  if (!bucket_table().ok) return hipErrorInvalidValue;
+  if (!bucket_table().ok || anchor_bits < 1 || anchor_bits > 7) return hipErrorInvalidValue;
   EncodeTables tab = encode_tables();
   const unsigned blocks = static_cast<unsigned>(num_pages * heads);
-  if (role == LYNX_ROLE_KEY)
-    hipLaunchKernelGGL(encode_kernel<LYNX_ROLE_KEY>, dim3(blocks), dim3(kEncThreads), 0, stream,
-                       kv, heads, out, tab);
-  else
-    hipLaunchKernelGGL(encode_kernel<LYNX_ROLE_VALUE>, dim3(blocks), dim3(kEncThreads), 0, stream,
-                       kv, heads, out, tab);
+  switch (anchor_bits) {
+    case 1: launch_encode_bits<1>(kv, blocks, heads, role, out, tab, stream); break;
+    case 2: launch_encode_bits<2>(kv, blocks, heads, role, out, tab, stream); break;
+    case 3: launch_encode_bits<3>(kv, blocks, heads, role, out, tab, stream); break;
+    case 5: launch_encode_bits<5>(kv, blocks, heads, role, out, tab, stream); break;
+    case 6: launch_encode_bits<6>(kv, blocks, heads, role, out, tab, stream); break;
+    case 7: launch_encode_bits<7>(kv, blocks, heads, role, out, tab, stream); break;
+    default: launch_encode_bits<4>(kv, blocks, heads, role, out, tab, stream); break;
+  }
   return hipGetLastError();
 }
 

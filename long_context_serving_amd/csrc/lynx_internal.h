@@ -75,8 +75,11 @@ struct PlanesArg {
   float *chunk_maxabs;
 };
 
+// anchor_bits 4 writes the 4-bit planes; 1 .. 7 the b + (8 - b) streams
+// (out.anchor b * 4096 and out.residual (8 - b) * 4096 bytes per tile).
 hipError_t launch_encode(const uint16_t *kv, int64_t num_pages, int heads,
-                         int role, const PlanesArg &out, hipStream_t stream);
+                         int role, const PlanesArg &out, hipStream_t stream,
+                         int anchor_bits = 4);
 
 hipError_t launch_code_map_check(uint32_t begin, uint32_t end,
                                  unsigned long long *mismatches, hipStream_t stream);

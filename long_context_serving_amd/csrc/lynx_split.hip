@@ -15,6 +15,7 @@
 // unit of 32 elements (16 bytes of each 4-bit plane) is exactly b words of
 // the anchor stream and 8 - b words of the residual stream, so every
 // thread here reads and writes whole words of its own unit.
+#include "lynx_cut.h"
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -28,33 +29,6 @@ constexpr int kUnitsPerTile = kPage * kDim / 32;  // 1024
 struct YTable {
   float y[256];
 };
-
-// 32 codes of a unit, from the 16 bytes of each 4-bit plane: element 8w + i
-// is nibble i of word w; the code is (anchor nibble << 4 | residual nibble)
-// read as int8.
-__device__ __forceinline__ int code_of(const uint32_t *a4, const uint32_t *r4, int k) {
-  const uint32_t an = (a4[k >> 3] >> (4 * (k & 7))) & 15u;
-  const uint32_t rn = (r4[k >> 3] >> (4 * (k & 7))) & 15u;
-  return static_cast<int8_t>(static_cast<uint8_t>((an << 4) | rn));
-}
-
-// Pack 32 values of B bits (low bits of v[k]) into B words, least
-// significant first.
-template <int B>
-__device__ __forceinline__ void pack32(const uint32_t *v, uint32_t *w) {
-  uint64_t acc = 0;
-  int nb = 0, wi = 0;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    acc |= static_cast<uint64_t>(v[k] & ((1u << B) - 1u)) << nb;
-    nb += B;
-    if (nb >= 32) {
-      w[wi++] = static_cast<uint32_t>(acc);
-      acc >>= 32;
-      nb -= 32;
-    }
-  }
-}
 
 // Field k of B bits of a unit's words (B <= 7, so a field spans at most
 // two words), sign-extended or not.
@@ -79,16 +53,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_planes_kernel(
   const u32x4 rv = __builtin_nontemporal_load(r4 + u);
   const uint32_t aw[4] = {av[0], av[1], av[2], av[3]};
   const uint32_t rw[4] = {rv[0], rv[1], rv[2], rv[3]};
-  uint32_t va[32], vr[32];
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int q = code_of(aw, rw, k);
-    va[k] = static_cast<uint32_t>(q >> RB);  // arithmetic: the signed anchor
-    vr[k] = static_cast<uint32_t>(q) & ((1u << RB) - 1u);
-  }
   uint32_t wa[B], wr[RB];
-  pack32<B>(va, wa);
-  pack32<RB>(vr, wr);
+  cut::unit<B>(aw, rw, wa, wr);
 #pragma unroll
   for (int i = 0; i < B; ++i) __builtin_nontemporal_store(wa[i], aout + u * B + i);
 #pragma unroll

@@ -74,6 +74,8 @@ _lib.lynx_split_planes.restype = ctypes.c_int
 _lib.lynx_dequantize_split.argtypes = [_P, _P, _i32, ctypes.POINTER(_CPlanes), _i64, _i32, _i32,
                                        _i32, _P, _P]
 _lib.lynx_dequantize_split.restype = ctypes.c_int
+_lib.lynx_quantize_pages_split.argtypes = [_P, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_CPlanes), _P]
+_lib.lynx_quantize_pages_split.restype = ctypes.c_int
 _lib.lynx_decode_attention_split.argtypes = [_P, ctypes.POINTER(_CPlanes), ctypes.POINTER(_CPlanes),
                                              _i32, _i32, _P, _P, _i32, _i32, _i32, _i32, _i32, _i64,
                                              ctypes.c_float, _P, _P, _P, _sz, _P]
@@ -389,4 +391,34 @@ def decode_attention_split(q: torch.Tensor, k: Planes, v: Planes, anchor_bits: i
         _ptr(seq_lens), B, H, Hq, D, max_pages, min(k.num_pages, v.num_pages), float(sm_scale),
         _ptr(out), _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream)),
         "lynx_decode_attention_split")
+    return out
+
+
+def alloc_cut_planes(num_pages: int, heads: int, role: int, anchor_bits: int,
+                     device="cuda") -> Planes:
+    """Planes whose anchor / residual hold b + (8 - b) streams."""
+    na = _lib.lynx_split_stream_bytes(num_pages, heads, anchor_bits)
+    nr = _lib.lynx_split_stream_bytes(num_pages, heads, 8 - anchor_bits)
+    return Planes(torch.empty(max(na, 16), dtype=torch.uint8, device=device)[:na],
+                  torch.empty(max(nr, 16), dtype=torch.uint8, device=device)[:nr],
+                  torch.empty((num_pages, heads, HEAD_DIM), dtype=torch.float32, device=device),
+                  torch.empty((num_pages, heads, HEAD_DIM), dtype=torch.float32, device=device),
+                  torch.empty((num_pages, heads, CHUNKS, HEAD_DIM), dtype=torch.float32, device=device),
+                  torch.empty((num_pages, heads, CHUNKS, HEAD_DIM), dtype=torch.float32, device=device),
+                  num_pages=num_pages, heads=heads, role=role)
+
+
+def quantize_pages_split(kv: torch.Tensor, role: int, anchor_bits: int, out: Optional[Planes] = None,
+                         stream=None) -> Planes:
+    """Encode bf16 pages [P][256][H][128] straight into a b + (8 - b) cut
+    (the streams cut_planes(quantize_pages(kv, role), b) would give)."""
+    kv = _bf16_bits(kv)
+    if kv.dim() != 4 or kv.shape[1] != PAGE or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous [P][256][H][128] bf16 tensor")
+    P, _, H, D = kv.shape
+    if out is None:
+        out = alloc_cut_planes(P, H, role, anchor_bits, kv.device)
+    cp = out.c()
+    _check(_lib.lynx_quantize_pages_split(_ptr(kv), P, H, D, role, anchor_bits, ctypes.byref(cp),
+                                          _stream(stream)), "lynx_quantize_pages_split")
     return out

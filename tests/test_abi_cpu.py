@@ -170,6 +170,18 @@ def test_cut_entry_points_reject_bad_arguments(lib):
     assert lib.lynx_dequantize_split(a, P(0x90008), 3, ctypes.byref(pl), 4, 8, 128, 1, out, None) == -3
     assert lib.lynx_dequantize_split(a, None, 3, ctypes.byref(pl), 0, 8, 128, 1, None, None) == 0
 
+    # the encoder writing a cut directly
+    lib.lynx_quantize_pages_split.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(CPlanes), P]
+    kvp = P(0x20000)
+    assert lib.lynx_quantize_pages_split(kvp, 4, 8, 128, 0, 0, ctypes.byref(pl), None) == -7
+    assert lib.lynx_quantize_pages_split(kvp, 4, 8, 128, 0, 8, ctypes.byref(pl), None) == -7
+    assert lib.lynx_quantize_pages_split(kvp, 4, 8, 128, 2, 3, ctypes.byref(pl), None) == -7
+    assert lib.lynx_quantize_pages_split(kvp, 4, 8, 96, 0, 3, ctypes.byref(pl), None) == -2
+    assert lib.lynx_quantize_pages_split(None, 4, 8, 128, 0, 3, ctypes.byref(pl), None) == -1
+    assert lib.lynx_quantize_pages_split(P(0x20008), 4, 8, 128, 0, 3, ctypes.byref(pl), None) == -3
+    assert lib.lynx_quantize_pages_split(None, 0, 8, 128, 0, 3, ctypes.byref(pl), None) == 0
+
     # fused attention over cut streams
     lib.lynx_decode_attention_split.argtypes = [P, ctypes.POINTER(CPlanes), ctypes.POINTER(CPlanes),
                                                 ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32,

@@ -87,6 +87,22 @@ def test_cut_4_draft_equals_the_anchor_dequantizer(lynx):
         assert torch.equal(d, lynx.dequantize(pl, full=False))
 
 
+@pytest.mark.parametrize("role", [0, 1])
+def test_encoder_writes_cuts_directly(lynx, role):
+    P, H = 5, 2
+    x = synth.laplace_pages(P, H, 128, seed=90 + role, scale_channels=((0, 9, 60.0),))
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    pl = lynx.quantize_pages(xd, role)
+    for b in range(1, 8):
+        print("direct cut encode %d + %d role %d" % (b, 8 - b, role), flush=True)
+        sa, sr = lynx.split_planes(pl, b)
+        d = lynx.quantize_pages_split(xd, role, b)
+        torch.cuda.synchronize()
+        assert torch.equal(d.anchor, sa) and torch.equal(d.residual, sr), b
+        for f in ("page_min", "page_range", "chunk_mean", "chunk_maxabs"):
+            assert torch.equal(getattr(d, f), getattr(pl, f)), f
+
+
 def test_empty_cut_is_a_noop(lynx):
     pl = lynx.alloc_planes(0, 2, 0)
     a, r = lynx.split_planes(pl, 3)
