@@ -49,19 +49,10 @@ __device__ __forceinline__ int table_index(uint32_t a_nib, uint32_t r_nib) {
   return static_cast<int>(((a_nib << 4) | r_nib) ^ 0x80u);
 }
 
-struct Partials {
-  double *m;  // [n][g]
-  float *l;   // [n][g]
-  float *o;   // [n][g][128]
-};
+using Partials = AttnPartials;
 
 __device__ __forceinline__ Partials partials_of(void *ws, const AttnShape &s) {
-  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.parts * s.group;
-  Partials pt;
-  pt.m = reinterpret_cast<double *>(ws);
-  pt.l = reinterpret_cast<float *>(pt.m + ((n + 1) & ~static_cast<size_t>(1)));
-  pt.o = pt.l + ((n + 3) & ~static_cast<size_t>(3));
-  return pt;
+  return attn_partials(ws, s);
 }
 
 template <bool kFull>

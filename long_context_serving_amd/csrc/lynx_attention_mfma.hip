@@ -94,19 +94,10 @@ struct MfmaTables {
   uint32_t draft[16];  // anchor nibble -> fp16 hi | fp16 lo << 16 of the draft yhat
 };
 
-struct Partials {
-  double *m;
-  float *l;
-  float *o;
-};
+using Partials = AttnPartials;
 
 __device__ __forceinline__ Partials partials_of(void *ws, const AttnShape &s) {
-  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.parts * s.group;
-  Partials pt;
-  pt.m = reinterpret_cast<double *>(ws);
-  pt.l = reinterpret_cast<float *>(pt.m + ((n + 1) & ~static_cast<size_t>(1)));
-  pt.o = pt.l + ((n + 3) & ~static_cast<size_t>(3));
-  return pt;
+  return attn_partials(ws, s);
 }
 
 // ---- cross-lane helpers -----------------------------------------------------

@@ -115,6 +115,25 @@ struct AttnShape {
   long long pool_pages;  // pages in the k / v pools (block-table bound)
 };
 
+// Split partials in an attention workspace: n = batch * heads * parts *
+// group rows of the running maximum m (double), the sum l and the
+// unnormalised output o[128]; query head j of (row, head) and part p is
+// row ((row * heads + head) * parts + p) * group + j.
+struct AttnPartials {
+  double *m;
+  float *l;
+  float *o;
+};
+
+__host__ __device__ inline AttnPartials attn_partials(void *ws, const AttnShape &s) {
+  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.parts * s.group;
+  AttnPartials pt;
+  pt.m = reinterpret_cast<double *>(ws);
+  pt.l = reinterpret_cast<float *>(pt.m + ((n + 1) & ~static_cast<size_t>(1)));
+  pt.o = pt.l + ((n + 3) & ~static_cast<size_t>(3));
+  return pt;
+}
+
 AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages);
 // Shape of `requests` requests with tq query tokens each over their pages
 // and a bf16 tail page.

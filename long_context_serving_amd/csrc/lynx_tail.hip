@@ -27,19 +27,10 @@ constexpr int kMaxG = LYNX_MAX_GROUP;
 
 // (m, l, o) partial rows, laid out as the page kernels lay them out:
 // m fp64 [n], l fp32 [n], o fp32 [n][128], n = rows * H * parts * group
-struct TailPartials {
-  double *m;
-  float *l;
-  float *o;
-};
+using TailPartials = AttnPartials;
 
 __device__ __forceinline__ TailPartials tail_partials_of(void *ws, const AttnShape &s) {
-  const size_t n = static_cast<size_t>(s.batch) * s.heads * s.parts * s.group;
-  TailPartials pt;
-  pt.m = reinterpret_cast<double *>(ws);
-  pt.l = reinterpret_cast<float *>(pt.m + ((n + 1) & ~static_cast<size_t>(1)));
-  pt.o = pt.l + ((n + 3) & ~static_cast<size_t>(3));
-  return pt;
+  return attn_partials(ws, s);
 }
 
 __device__ __forceinline__ double bf16_to_double(uint32_t bits16) {
