@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["lynx_tables.cpp", "lynx_api.cpp", "lynx_encode.hip", "lynx_dequant.hip",
            "lynx_attention.hip", "lynx_attention_mfma.hip", "lynx_tail.hip",
-           "lynx_split.hip"]
+           "lynx_split.hip", "lynx_verify.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",
           "-I", INCLUDE]
@@ -27,7 +27,8 @@ DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-pa
 # finite by contract; without NaN semantics their min/max need no
 # canonicalising instructions (every operation and its rounding are
 # unchanged; infinities keep their meaning).
-EXTRA = {"lynx_encode.hip": ["-fno-honor-nans"], "lynx_attention_mfma.hip": ["-fno-honor-nans"]}
+EXTRA = {"lynx_encode.hip": ["-fno-honor-nans"], "lynx_attention_mfma.hip": ["-fno-honor-nans"],
+         "lynx_verify.hip": ["-fno-honor-nans"]}
 
 
 def sources():

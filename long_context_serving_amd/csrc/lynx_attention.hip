@@ -377,6 +377,16 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
 AttnShape attention_shape_tail(int requests, int tq, int heads, int q_heads, int max_pages) {
   AttnShape s = attention_shape(requests * tq, heads, q_heads, max_pages);
   s.tq = tq;
+  if (verify_mfma_supported(s.group) && tq > 0 && max_pages > 0) {
+    // the verify kernel's blocks: (request, KV head, run, group of 16 rows)
+    const long long units = static_cast<long long>(requests) * heads * verify_row_blocks(tq);
+    const long long target = attention_mfma_target_blocks();
+    long long pps = units > 0 ? (units * max_pages + target - 1) / target : 1;
+    if (pps < 1) pps = 1;
+    if (pps > max_pages) pps = max_pages;
+    s.pages_per_split = static_cast<int>(pps);
+    s.splits = static_cast<int>((max_pages + pps - 1) / pps);
+  }
   s.parts = s.splits + 1;
   return s;
 }
@@ -431,6 +441,9 @@ hipError_t launch_attention_with_tail(const uint16_t *q, const PlanesArg &k, con
     // no page can be read: the tail is the whole context
     sp.splits = 0;
     sp.parts = 1;
+  } else if (verify_mfma_supported(s.group)) {
+    e = launch_verify_mfma(q, k, v, block_table, page_tokens, sp, sm_scale, full, workspace, stream);
+    if (e != hipSuccess) return e;
   } else if (mfma) {
     e = launch_attention_mfma(q, k, v, block_table, page_tokens, sp, sm_scale, full, out, nullptr,
                               workspace, false, stream);

@@ -155,6 +155,16 @@ hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const Pl
 hipError_t launch_attention_mfma_combine(const AttnShape &s, const void *workspace, float *out,
                                          hipStream_t stream);
 
+// Verify-pass page kernel (GQA group 8): up to 16 query rows of one
+// request and KV head per block, one block per (request, KV head, run of
+// pages, group of 16 rows); writes the split partials of its rows.
+bool verify_mfma_supported(int group);
+int verify_row_blocks(int tq);
+hipError_t launch_verify_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
+                              const int32_t *block_table, const int32_t *page_tokens,
+                              const AttnShape &s, float sm_scale, bool full, void *workspace,
+                              hipStream_t stream);
+
 // bf16 tail page of each request (tail_k / tail_v [requests][tail_cap][H][128],
 // tail_len [requests] on the device): query token i of a request sees tail
 // tokens 0 .. tail_len - tq + i.  Writes partial row `s.splits` of every

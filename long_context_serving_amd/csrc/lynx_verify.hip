@@ -1,0 +1,563 @@
+// Verify-pass attention on matrix cores: the speculative tokens of a
+// request attend to its compact pages (GQA group 8).
+//
+// Page "Lynx: the KV cache does not have to arrive whole", section 4: the
+// drafted tokens are verified in one pass over the refined cache; section 3
+// gives the reconstruction x = mn + rg * (mu + s * yhat).  The decode
+// kernel serves one query token per row and rebuilds every chunk's operands
+// per row; here up to 16 query rows of one request and KV head share a
+// block, and each chunk's operands are built once per block in LDS:
+//
+//   K' = c1 * yhat (c1 = rg * s, times a power of two ks), so the score of
+//        a token is q . K' / ks + q . c0 (c0 = mn + rg * mu, the chunk bias,
+//        summed in fp64); q enters the product unsplit (a bf16 value is an
+//        fp16 value after a power-of-two scale), so one 16 x 16 x 32 product
+//        covers 16 tokens x (2 query rows x 8 heads) x 16 channels;
+//   V  = the reconstructed values themselves, whose rounding error reaches
+//        the output only through the softmax weights (a convex combination).
+//
+// K' and V are stored as fp16 (hi, lo) pairs (hi = the value truncated to
+// 11 significant bits, lo = the rounded remainder), in consecutive k slots;
+// the other operand repeats its value in both slots.  The probabilities are
+// split into hi and lo column halves as in the decode kernel.  Scores are
+// assembled in fp64 (MFMA sum times 1/ks, plus the fp64 bias), the running
+// maximum is base 2 and moves only when exceeded by 2^8, and each wave
+// keeps its two rows' accumulators in the matrix-core C operand for the
+// whole run.  A block covers one run of pages; the runs' partials (m, l, o)
+// are merged with the bf16 tail's by the split combine kernel.
+#include <math.h>
+
+#include "lynx_internal.h"
+#include "lynx_lanes.h"
+
+namespace lynx {
+namespace {
+
+using namespace lanes;
+
+constexpr int kVW = 8;                      // waves per block
+constexpr int kVT = 64 * kVW;
+constexpr int kVRows = 2 * kVW;             // query rows per block
+constexpr int kG = 8;                       // query heads per KV head
+constexpr float kVSlack = 8.0f;             // log2 of the largest probability before rescaling
+constexpr int kKRowB = kDim * 4 + 16;       // one token of K': 128 (hi, lo) words + 16 B pad
+constexpr int kKTileB = kChunk * kKRowB;
+constexpr int kVRowB = kChunk * 4 + 16;     // one channel of V: 32 (hi, lo) words + 16 B pad
+constexpr int kVTileB = kDim * kVRowB;
+constexpr int kSlotB = kDim * 4 + kDim * 8 + 16;  // c1k * ks f32[128] | c0k f64[128] | 1/(ks qs) f64
+// LDS map: yhat table (256 codes x 64 copies, lane l reads copy l), two K'
+// tiles, two V tiles, three scale slots, and the block's |q| maxima.
+constexpr int kYOff = 0;
+constexpr int kKOff = 256 * 256;
+constexpr int kVOff = kKOff + 2 * kKTileB;
+constexpr int kSOff = kVOff + 2 * kVTileB;
+constexpr int kQmOff = kSOff + 3 * kSlotB;
+constexpr int kVLds = kQmOff + kVW * 4;
+static_assert(kVLds <= 160 * 1024, "LDS of one block");
+
+struct VerifyTable {
+  float y[256];  // code byte (the code read as int8) -> yhat
+};
+
+// Per-thread inputs of one chunk's build: the K word of token t / 16,
+// channels 8 (t % 16) .. + 7, and the V word t % 4 of channel t / 4, with
+// that channel's V scales.
+struct BuildIn {
+  uint32_t ka, kr, va, vr;
+  float mnv, rgv, muv, sv;
+};
+// K scales of channels 2l, 2l + 1 (every wave loads all 128 channels).
+struct KScale {
+  float2 mnk, rgk, muk, sk;
+};
+
+__device__ __forceinline__ uint32_t ldg_nt(const uint8_t *base, size_t off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(base + off));
+}
+
+// LDS byte address of table row x.byte[J], copy of lane bits lb.
+template <int J>
+__device__ __forceinline__ uint32_t yaddr(uint32_t x, uint32_t lb) {
+  return __builtin_amdgcn_perm(x, lb, 0x0C0C0000u | ((4u + J) << 8));
+}
+
+// fp16 (hi, lo) pair of x: hi = x truncated to 11 significant bits, lo =
+// the remainder rounded to fp16.
+__device__ __forceinline__ uint32_t pair16(float x) {
+  const float hi = __uint_as_float(__float_as_uint(x) & 0xFFFFE000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi, x - hi));
+}
+
+// 8 code bytes of a word pair: byte j of e = element 2j, of o = element
+// 2j + 1 (element i is nibble i); the draft code is (a << 4) | 7.
+template <bool kFull>
+__device__ __forceinline__ void code_bytes8(uint32_t a, uint32_t r, uint32_t &e, uint32_t &o) {
+  if (kFull) {
+    e = ((a << 4) & 0xF0F0F0F0u) | (r & 0x0F0F0F0Fu);
+    o = (a & 0xF0F0F0F0u) | ((r >> 4) & 0x0F0F0F0Fu);
+  } else {
+    e = ((a << 4) & 0xF0F0F0F0u) | 0x07070707u;
+    o = (a & 0xF0F0F0F0u) | 0x07070707u;
+  }
+}
+
+// yhat of the 8 elements (in element order) of a word pair.
+template <bool kFull>
+__device__ __forceinline__ void yhat8(uint32_t a, uint32_t r, uint32_t lb, const char *ytab,
+                                      float (&y)[8]) {
+  uint32_t e, o;
+  code_bytes8<kFull>(a, r, e, o);
+  auto rd = [&](uint32_t addr) { return *reinterpret_cast<const float *>(ytab + addr); };
+  y[0] = rd(yaddr<0>(e, lb));
+  y[1] = rd(yaddr<0>(o, lb));
+  y[2] = rd(yaddr<1>(e, lb));
+  y[3] = rd(yaddr<1>(o, lb));
+  y[4] = rd(yaddr<2>(e, lb));
+  y[5] = rd(yaddr<2>(o, lb));
+  y[6] = rd(yaddr<3>(e, lb));
+  y[7] = rd(yaddr<3>(o, lb));
+}
+
+template <bool kFull>
+__device__ __forceinline__ void load_build(BuildIn &in, const PlanesArg &kp, const PlanesArg &vp,
+                                           size_t tile, int c, int t) {
+  const size_t cb = tile * kPlaneTileBytes + static_cast<size_t>(c) * (kChunk * kDim / 2);
+  const size_t koff = cb + static_cast<size_t>((t >> 4) * 64 + (t & 15) * 4);
+  const size_t voff = cb + static_cast<size_t>((t >> 2) * 16 + (t & 3) * 4);
+  in.ka = ldg_nt(kp.anchor, koff);
+  in.va = ldg_nt(vp.anchor, voff);
+  if (kFull) {
+    in.kr = ldg_nt(kp.residual, koff);
+    in.vr = ldg_nt(vp.residual, voff);
+  } else {
+    in.kr = 0u;
+    in.vr = 0u;
+  }
+  const int ch = t >> 2;
+  const size_t pidx = tile * kDim + ch;
+  const size_t cidx = (tile * kChunks + c) * kDim + ch;
+  in.mnv = vp.page_min[pidx];
+  in.rgv = vp.page_range[pidx];
+  in.muv = vp.chunk_mean[cidx];
+  in.sv = vp.chunk_maxabs[cidx];
+}
+
+__device__ __forceinline__ void load_kscale(KScale &ks, const PlanesArg &kp, size_t tile, int c,
+                                            int lane) {
+  const size_t pidx = tile * kDim + 2 * lane;
+  const size_t cidx = (tile * kChunks + c) * kDim + 2 * lane;
+  ks.mnk = *reinterpret_cast<const float2 *>(kp.page_min + pidx);
+  ks.rgk = *reinterpret_cast<const float2 *>(kp.page_range + pidx);
+  ks.muk = *reinterpret_cast<const float2 *>(kp.chunk_mean + cidx);
+  ks.sk = *reinterpret_cast<const float2 *>(kp.chunk_maxabs + cidx);
+}
+
+// Scale slot of a chunk: c1k * ks and c0k for every channel (wave w writes
+// channels 16w .. 16w + 15), and 1 / (ks * qs) (wave 0).  ks = 2^(14 - e),
+// e the exponent of the largest c1k, keeps every K' below 2^15.
+__device__ __forceinline__ void stage_slot(const KScale &k, char *slot, int w, int lane,
+                                           double inv_qs) {
+  const float c1a = k.rgk.x * k.sk.x, c1b = k.rgk.y * k.sk.y;  // exact (7 + 7 bits)
+  const float top = wave_max(fmaxf(c1a, c1b));
+  float ks = 1.0f;
+  double inv_ks = 1.0;
+  const uint32_t eb = (__float_as_uint(top) >> 23) & 0xFFu;
+  if (eb != 0u && eb != 0xFFu) {
+    int ex = 127 + 14 + 127 - static_cast<int>(eb);
+    ex = ex < 1 ? 1 : (ex > 254 ? 254 : ex);
+    ks = __uint_as_float(static_cast<uint32_t>(ex) << 23);
+    inv_ks = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + 127 - ex) << 52);
+  }
+  if ((lane >> 3) == w) {
+    reinterpret_cast<float2 *>(slot)[lane] = make_float2(c1a * ks, c1b * ks);
+    reinterpret_cast<double2 *>(slot + kDim * 4)[lane] =
+        make_double2(static_cast<double>(k.mnk.x) + static_cast<double>(k.rgk.x) * k.muk.x,
+                     static_cast<double>(k.mnk.y) + static_cast<double>(k.rgk.y) * k.muk.y);
+  }
+  if (w == 0 && lane == 0) *reinterpret_cast<double *>(slot + kDim * 12) = inv_ks * inv_qs;
+}
+
+// Build the K' and V tiles of one chunk from thread t's inputs.
+template <bool kFull>
+__device__ __forceinline__ void build_chunk(const BuildIn &in, const char *slot, char *ktile,
+                                            char *vtile, const char *ytab, int t, uint32_t lb) {
+  {
+    // K': token t / 16, channels 8 (t % 16) .. + 7
+    float y[8];
+    yhat8<kFull>(in.ka, in.kr, lb, ytab, y);
+    const int ch0 = (t & 15) * 8;
+    const float4 c0 = *reinterpret_cast<const float4 *>(slot + ch0 * 4);
+    const float4 c1 = *reinterpret_cast<const float4 *>(slot + ch0 * 4 + 16);
+    u32x4 w0, w1;
+    w0[0] = pair16(y[0] * c0.x);
+    w0[1] = pair16(y[1] * c0.y);
+    w0[2] = pair16(y[2] * c0.z);
+    w0[3] = pair16(y[3] * c0.w);
+    w1[0] = pair16(y[4] * c1.x);
+    w1[1] = pair16(y[5] * c1.y);
+    w1[2] = pair16(y[6] * c1.z);
+    w1[3] = pair16(y[7] * c1.w);
+    char *dst = ktile + (t >> 4) * kKRowB + ch0 * 4;
+    *reinterpret_cast<u32x4 *>(dst) = w0;
+    *reinterpret_cast<u32x4 *>(dst + 16) = w1;
+  }
+  {
+    // V: channel t / 4, word t % 4 = tokens 4g .. 4g + 3 (elements 0..3)
+    // and 16 + 4g .. (elements 4..7)
+    float y[8];
+    yhat8<kFull>(in.va, in.vr, lb, ytab, y);
+    u32x4 w0, w1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w0[i] = pair16(__builtin_fmaf(in.rgv, __builtin_fmaf(in.sv, y[i], in.muv), in.mnv));
+      w1[i] = pair16(__builtin_fmaf(in.rgv, __builtin_fmaf(in.sv, y[4 + i], in.muv), in.mnv));
+    }
+    const int g4 = (t & 3) * 4;
+    char *dst = vtile + (t >> 2) * kVRowB;
+    *reinterpret_cast<u32x4 *>(dst + g4 * 4) = w0;
+    *reinterpret_cast<u32x4 *>(dst + (16 + g4) * 4) = w1;
+  }
+}
+
+// Running state of a wave: lane (n, r) follows column n = (row n / 8,
+// head n % 8) for the softmax and holds rows 16ct + 4r + i of the value
+// columns (head n % 8, half n / 8) of both rows.
+struct VState {
+  float m, l;
+  floatx4 acc_a[8], acc_b[8];
+};
+
+template <bool kFull>
+__global__ __launch_bounds__(kVT) void verify_mfma_kernel(
+    const uint16_t *__restrict__ q, PlanesArg kp, PlanesArg vp,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ page_tokens,
+    AttnShape s, int row_blocks, float sm_scale, void *ws, VerifyTable tab) {
+  __shared__ __align__(16) char smem[kVLds];
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int n = lane & 15, r = lane >> 4;
+  const bool lo = n >= 8;
+  const uint32_t lb = static_cast<uint32_t>(lane * 4);
+
+  // blocks of one (request, KV head, run) are consecutive logical blocks
+  // (their row groups share the run's pages); spread over the 8 XCDs in
+  // contiguous groups
+  const unsigned nblk = gridDim.x;
+  unsigned lbi = blockIdx.x;
+  if ((nblk & 7u) == 0u) lbi = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int rb = static_cast<int>(lbi % static_cast<unsigned>(row_blocks));
+  const unsigned rest = lbi / static_cast<unsigned>(row_blocks);
+  const int split = static_cast<int>(rest % static_cast<unsigned>(s.splits));
+  const int bh = static_cast<int>(rest / static_cast<unsigned>(s.splits));
+  const int h = bh % s.heads;
+  const int req = bh / s.heads;
+
+  // ---- this wave's rows and its lane's query values ----
+  const int row_a = rb * kVRows + 2 * w;      // rows of the request: row_a, row_a + 1
+  const int my_row = row_a + (n >> 3);        // row of this lane's score column
+  const bool row_ok = my_row < s.tq;
+  const size_t qrow = static_cast<size_t>(req) * s.tq + (row_ok ? my_row : s.tq - 1);
+  const uint16_t *qg = q + (qrow * s.q_heads + static_cast<size_t>(h) * kG + (n & 7)) * kDim;
+  uint2 qraw[8];  // channels 16st + 4r .. + 3
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+    qraw[st] = *reinterpret_cast<const uint2 *>(qg + 16 * st + 4 * r);
+
+  // ---- this block's run of chunks ----
+  const __attribute__((address_space(4))) int32_t *bt_c =
+      (const __attribute__((address_space(4))) int32_t *)block_table;
+  const __attribute__((address_space(4))) int32_t *pt_c =
+      (const __attribute__((address_space(4))) int32_t *)page_tokens;
+  int npages = s.max_pages;
+  if (page_tokens) {
+    npages = pt_c[req] / kPage;
+    npages = npages < 0 ? 0 : (npages > s.max_pages ? s.max_pages : npages);
+  }
+  const int p0 = split * s.pages_per_split;
+  int p1 = p0 + s.pages_per_split;
+  p1 = p1 > npages ? npages : p1;
+  const int cb = p0 * kChunks;
+  const int ce = p1 > p0 ? p1 * kChunks : cb;
+  auto page_of = [&](int c) -> long long {
+    if (c >= ce) return -1;
+    const int lp = c >> 3;
+    const long long pg = block_table ? bt_c[static_cast<size_t>(req) * s.max_pages + lp]
+                                     : static_cast<long long>(req) * s.max_pages + lp;
+    return (pg < 0 || pg >= s.pool_pages) ? -1 : pg;
+  };
+  auto tile_of = [&](long long pg) { return pg >= 0 ? static_cast<size_t>(pg) * s.heads + h : 0; };
+  auto chunk_of = [&](long long pg, int c) { return pg >= 0 ? (c & 7) : 0; };
+
+  // ---- first loads: inputs of chunk cb, K scales of cb and cb + 1 ----
+  BuildIn bin;
+  KScale ksa, ring;
+  {
+    const long long g0 = page_of(cb), g1 = page_of(cb + 1);
+    load_kscale(ksa, kp, tile_of(g0), chunk_of(g0, cb), lane);
+    load_kscale(ring, kp, tile_of(g1), chunk_of(g1, cb + 1), lane);
+    load_build<kFull>(bin, kp, vp, tile_of(g0), chunk_of(g0, cb), t);
+  }
+
+  // ---- yhat table: 64 copies of each entry ----
+  char *ytab = smem + kYOff;
+  {
+    const float yv = tab.y[t & 255];
+    const uint32_t yb = __float_as_uint(yv);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(ytab + (t & 255) * 256 + (t >> 8) * 128);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[k] = u32x4{yb, yb, yb, yb};
+  }
+
+  // ---- q (exact bf16 values) for the bias, and the block-wide power of
+  // two qs that brings max |q| into [2^14, 2^15) for the fp16 operand ----
+  float q32[32];
+  float qmax = 0.0f;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const uint32_t u[2] = {qraw[st].x, qraw[st].y};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float a = row_ok ? __uint_as_float(u[e] << 16) : 0.0f;
+      const float b = row_ok ? __uint_as_float(u[e] & 0xFFFF0000u) : 0.0f;
+      q32[4 * st + 2 * e] = a;
+      q32[4 * st + 2 * e + 1] = b;
+      qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(b)));
+    }
+  }
+  qmax = wave_max(qmax);
+  float *s_qm = reinterpret_cast<float *>(smem + kQmOff);
+  if (lane == 0) s_qm[w] = qmax;
+  __syncthreads();  // table and maxima
+  qmax = s_qm[0];
+#pragma unroll
+  for (int k = 1; k < kVW; ++k) qmax = fmaxf(qmax, s_qm[k]);
+  float qs = 1.0f;
+  double inv_qs = 1.0;
+  {
+    const uint32_t eb = (__float_as_uint(qmax) >> 23) & 0xFFu;
+    if (eb != 0u && eb != 0xFFu) {
+      int ex = 127 + 14 + 127 - static_cast<int>(eb);
+      ex = ex < 1 ? 1 : (ex > 254 ? 254 : ex);
+      qs = __uint_as_float(static_cast<uint32_t>(ex) << 23);
+      inv_qs = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + 127 - ex) << 52);
+    }
+  }
+  half8 qb[8];  // B operand of step st: q * qs of channels 16st + 4r + i, in both slots
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = q32[4 * st + i] * qs;
+      v[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, x));
+    }
+    qb[st] = __builtin_bit_cast(half8, v);
+  }
+
+  char *ktiles = smem + kKOff;
+  char *vtiles = smem + kVOff;
+  char *slots = smem + kSOff;
+  const double sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
+  const uint32_t keep_mask = lo ? 0xFFFFE000u : 0u;
+
+  VState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    st.acc_a[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.acc_b[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  if (cb < ce) {
+    stage_slot(ksa, slots, w, lane, inv_qs);
+    stage_slot(ring, slots + kSlotB, w, lane, inv_qs);
+    __syncthreads();
+    build_chunk<kFull>(bin, slots, ktiles, vtiles, ytab, t, lb);
+    __syncthreads();
+
+    // step j: load the build inputs of chunk c + 1 and the K scales of
+    // chunk c + 2, compute chunk c = cb + j from tiles j & 1 and slot j % 3,
+    // then build chunk c + 1 and stage slot (j + 2) % 3 (the loads have had
+    // the compute of chunk c to land)
+    for (int j = 0; cb + j < ce; ++j) {
+      const int c = cb + j;
+      const int tb = j & 1;
+      {
+        const long long g1 = page_of(c + 1), g2 = page_of(c + 2);
+        load_build<kFull>(bin, kp, vp, tile_of(g1), chunk_of(g1, c + 1), t);
+        load_kscale(ring, kp, tile_of(g2), chunk_of(g2, c + 2), lane);
+      }
+      if (page_of(c) >= 0) {
+        const char *kt = ktiles + tb * kKTileB;
+        const char *vt = vtiles + tb * kVTileB;
+        const char *slot = slots + (j % 3) * kSlotB;
+        // chunk bias sum_d q_d c0k_d (fp64) of column n over channels 16st + 4r + i
+        double bias;
+        {
+          const double *c0k = reinterpret_cast<const double *>(slot + kDim * 4);
+          double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+          for (int s8 = 0; s8 < 8; ++s8) {
+            const double2 x0 = *reinterpret_cast<const double2 *>(c0k + 16 * s8 + 4 * r);
+            const double2 x1 = *reinterpret_cast<const double2 *>(c0k + 16 * s8 + 4 * r + 2);
+            a0 = fma(static_cast<double>(q32[4 * s8]), x0.x, a0);
+            a1 = fma(static_cast<double>(q32[4 * s8 + 1]), x0.y, a1);
+            a0 = fma(static_cast<double>(q32[4 * s8 + 2]), x1.x, a0);
+            a1 = fma(static_cast<double>(q32[4 * s8 + 3]), x1.y, a1);
+          }
+          bias = xrows_sum(a0 + a1);
+        }
+        // scores S^T[16 tok][16 col] for tiles 0, 1
+        floatx4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+          const half8 a0 = *reinterpret_cast<const half8 *>(kt + n * kKRowB + (16 * s8 + 4 * r) * 4);
+          const half8 a1 =
+              *reinterpret_cast<const half8 *>(kt + (16 + n) * kKRowB + (16 * s8 + 4 * r) * 4);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[s8], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[s8], s1, 0, 0, 0);
+          // keep the operand reads of at most two steps in flight
+          if (s8 & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+        const double scale2 = sm2 * *reinterpret_cast<const double *>(slot + kDim * 12);
+        const double bias2 = bias * sm2;
+        double sc[8];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[i] = fma(static_cast<double>(s0[i]), scale2, bias2);
+          sc[4 + i] = fma(static_cast<double>(s1[i]), scale2, bias2);
+          cmax = fmaxf(cmax, fmaxf(static_cast<float>(sc[i]), static_cast<float>(sc[4 + i])));
+        }
+        cmax = xrows(cmax, MaxOp());
+        const bool rescale = __builtin_amdgcn_ballot_w64(cmax > st.m + kVSlack) != 0;
+        float alpha = 1.0f;
+        if (rescale) {
+          const float m_new = fmaxf(st.m, cmax);
+          alpha = st.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+          st.m = m_new;
+          const float x = ror8(alpha);
+          const float al_a = lo ? x : alpha, al_b = lo ? alpha : x;
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct) {
+            st.acc_a[ct] *= al_a;
+            st.acc_b[ct] *= al_b;
+          }
+        }
+        float p[8];
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(static_cast<float>(sc[i] - static_cast<double>(st.m)));
+          psum += p[i];
+        }
+        psum = xrows(psum, SumOp());
+        st.l = st.l * alpha + psum;
+        // P operands of each row: column (head n % 8, half n / 8) takes the
+        // probabilities of lane n (row a, n < 8) or n ^ 8
+        half8 pa[2], pb[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          u32x4 wa, wb;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float own = p[4 * tt + i];
+            const float x = ror8(own);
+            wa[i] = split_dup(lo ? x : own, keep_mask);
+            wb[i] = split_dup(lo ? own : x, keep_mask);
+          }
+          pa[tt] = __builtin_bit_cast(half8, wa);
+          pb[tt] = __builtin_bit_cast(half8, wb);
+        }
+        // values: O^T[16 ch][16 col] += V^T[16 ch][32 k] * P[32 k][16 col]
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          const char *vrow = vt + (16 * ct + n) * kVRowB;
+          const half8 y0 = *reinterpret_cast<const half8 *>(vrow + (4 * r) * 4);
+          const half8 y1 = *reinterpret_cast<const half8 *>(vrow + (16 + 4 * r) * 4);
+          st.acc_a[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pa[0], st.acc_a[ct], 0, 0, 0);
+          st.acc_a[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y1, pa[1], st.acc_a[ct], 0, 0, 0);
+          st.acc_b[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pb[0], st.acc_b[ct], 0, 0, 0);
+          st.acc_b[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y1, pb[1], st.acc_b[ct], 0, 0, 0);
+          if (ct & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (c + 1 < ce)
+        build_chunk<kFull>(bin, slots + ((j + 1) % 3) * kSlotB, ktiles + (tb ^ 1) * kKTileB,
+                           vtiles + (tb ^ 1) * kVTileB, ytab, t, lb);
+      stage_slot(ring, slots + ((j + 2) % 3) * kSlotB, w, lane, inv_qs);
+      __syncthreads();
+    }
+  }
+
+  // ---- partials of both rows: lanes n < 8 write head n ----
+  {
+    AttnPartials pt = attn_partials(ws, s);
+    const float m_other = ror8(st.m), l_other = ror8(st.l);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int row = row_a + k;
+      const float mk = k == 0 ? st.m : m_other;  // lanes n < 8: row a is their own column
+      const float lk = k == 0 ? st.l : l_other;
+      floatx4 o[8];
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const floatx4 a = k == 0 ? st.acc_a[ct] : st.acc_b[ct];
+        floatx4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = a[i] + ror8(a[i]);
+        o[ct] = x;
+      }
+      if (!lo && row < s.tq) {
+        const size_t grow = static_cast<size_t>(req) * s.tq + row;
+        const size_t prow = ((grow * s.heads + h) * s.parts + split) * kG + n;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+          *reinterpret_cast<float4 *>(pt.o + prow * kDim + 16 * ct + 4 * r) =
+              make_float4(o[ct][0], o[ct][1], o[ct][2], o[ct][3]);
+        if (r == 0) {
+          pt.m[prow] = static_cast<double>(mk);
+          pt.l[prow] = lk;
+        }
+      }
+    }
+  }
+}
+
+VerifyTable build_verify_table() {
+  VerifyTable t;
+  const DecodeTable &dt = decode_table();
+  for (int byte = 0; byte < 256; ++byte) {
+    const int code = byte >= 128 ? byte - 256 : byte;
+    t.y[byte] = dt.y[code + 128];
+  }
+  return t;
+}
+
+}  // namespace
+
+bool verify_mfma_supported(int group) { return group == kG; }
+
+int verify_row_blocks(int tq) { return (tq + kVRows - 1) / kVRows; }
+
+hipError_t launch_verify_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
+                              const int32_t *block_table, const int32_t *page_tokens,
+                              const AttnShape &s, float sm_scale, bool full, void *workspace,
+                              hipStream_t stream) {
+  static const VerifyTable table = build_verify_table();
+  if (s.group != kG || s.tq < 1 || s.splits < 1 || s.pool_pages <= 0) return hipErrorInvalidValue;
+  const int requests = s.batch / s.tq;
+  const int rbs = verify_row_blocks(s.tq);
+  const dim3 grid(static_cast<unsigned>(static_cast<long long>(requests) * s.heads * s.splits * rbs));
+  if (full)
+    hipLaunchKernelGGL(verify_mfma_kernel<true>, grid, dim3(kVT), 0, stream, q, k, v, block_table,
+                       page_tokens, s, rbs, sm_scale, workspace, table);
+  else
+    hipLaunchKernelGGL(verify_mfma_kernel<false>, grid, dim3(kVT), 0, stream, q, k, v, block_table,
+                       page_tokens, s, rbs, sm_scale, workspace, table);
+  return hipGetLastError();
+}
+
+}  // namespace lynx
