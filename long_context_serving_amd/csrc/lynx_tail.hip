@@ -37,7 +37,18 @@ __device__ __forceinline__ double bf16_to_double(uint32_t bits16) {
   return static_cast<double>(__uint_as_float(bits16 << 16));
 }
 
-// Block = (query row b, KV head h).
+// Tail tokens staged in LDS per pass: 64 tokens x 128 bf16, rows padded by
+// 16 bytes so that lanes reading different tokens at one channel hit
+// different banks.
+constexpr int kSlab = 64;
+constexpr int kSlabRow = kDim + 8;
+// q rows in LDS are padded by 16 bytes, so lanes reading different heads'
+// rows at one channel hit different banks.
+constexpr int kQStride = kDim + 2;
+
+// Block = (query row b, KV head h).  The visible tail tokens pass through
+// LDS in slabs of 64 (K for the scores, then V for the values), each slab
+// loaded by the whole block with 16-byte loads at once.
 __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ tail_k,
     const uint16_t *__restrict__ tail_v, const int32_t *__restrict__ tail_len, AttnShape s,
@@ -50,9 +61,10 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
   const int g = s.group;
   const int tid = threadIdx.x;
 
-  __shared__ double s_q[kMaxG][kDim];
+  __shared__ double s_q[kMaxG * kQStride];
   __shared__ double s_p[kTailCap][kMaxG];  // scores, then probabilities
   __shared__ double s_m[kMaxG], s_l[kMaxG];
+  __shared__ __align__(16) uint16_t s_slab[kSlab * kSlabRow];
 
   int n = tail_len[req];
   n = n < 0 ? 0 : (n > tail_cap ? tail_cap : n);
@@ -61,33 +73,70 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
 
   for (int e = tid; e < g * kDim; e += kTailThreads) {
     const int j = e / kDim, d = e % kDim;
-    s_q[j][d] = bf16_to_double(q[(static_cast<size_t>(b) * s.q_heads + h * g + j) * kDim + d]);
+    s_q[j * kQStride + d] =
+        bf16_to_double(q[(static_cast<size_t>(b) * s.q_heads + h * g + j) * kDim + d]);
   }
-  __syncthreads();
 
-  // ---- scores: thread t takes tail token t (and t + 256) for every head ----
   const size_t row_stride = static_cast<size_t>(s.heads) * kDim;  // one token of the tail
-  const uint16_t *kbase = tail_k + (static_cast<size_t>(req) * tail_cap * s.heads + h) * kDim;
-  for (int t = tid; t < vis; t += kTailThreads) {
-    double acc[kMaxG];
+  const size_t tail0 = (static_cast<size_t>(req) * tail_cap * s.heads + h) * kDim;
+  // slab of tokens t0 .. t0 + 63 (< vis) of one tail tensor into s_slab:
+  // thread tid loads 16-byte pieces tid, tid + 256, ... (16 per token)
+  auto stage = [&](const uint16_t *tail, int t0) {
+    const int cnt = vis - t0 < kSlab ? vis - t0 : kSlab;
+    uint4 piece[4];
 #pragma unroll
-    for (int j = 0; j < kMaxG; ++j) acc[j] = 0.0;
-    const uint4 *krow = reinterpret_cast<const uint4 *>(kbase + t * row_stride);
-    for (int d8 = 0; d8 < kDim / 8; ++d8) {
-      const uint4 w = krow[d8];
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const double k0 = bf16_to_double(u[e] & 0xFFFFu), k1 = bf16_to_double(u[e] >> 16);
-        const int d = 8 * d8 + 2 * e;
-#pragma unroll
-        for (int j = 0; j < kMaxG; ++j)
-          if (j < g) acc[j] = fma(s_q[j][d + 1], k1, fma(s_q[j][d], k0, acc[j]));
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int e = tid + k * kTailThreads;  // piece e: token e / 16, channels 8 (e % 16) ..
+      const int tk = e >> 4;
+      piece[k] = tk < cnt ? *reinterpret_cast<const uint4 *>(
+                                tail + tail0 + static_cast<size_t>(t0 + tk) * row_stride + (e & 15) * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int j = 0; j < kMaxG; ++j)
-      if (j < g) s_p[t][j] = acc[j] * score_scale;
+    for (int k = 0; k < 4; ++k) {
+      const int e = tid + k * kTailThreads;
+      *reinterpret_cast<uint4 *>(s_slab + (e >> 4) * kSlabRow + (e & 15) * 8) = piece[k];
+    }
+    return cnt;
+  };
+
+  // ---- scores: 4 tail tokens of one head per thread and pass (each q
+  // value read from LDS serves 4 products) ----
+  for (int t0 = 0; t0 < vis; t0 += kSlab) {
+    __syncthreads();  // q staged / the previous slab consumed
+    const int cnt = stage(tail_k, t0);
+    __syncthreads();
+    const int groups = (cnt + 3) >> 2;  // tokens past cnt are zero in the slab
+    for (int item = tid; item < groups * g; item += kTailThreads) {
+      const int tg = item / g, j = item - tg * g;
+      const double *qj = s_q + j * kQStride;
+      const uint16_t *k0 = s_slab + 4 * tg * kSlabRow;
+      double a[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+      for (int d8 = 0; d8 < kDim / 8; ++d8) {
+        uint32_t u[4][4];
+#pragma unroll
+        for (int tk = 0; tk < 4; ++tk) {
+          const uint4 w = *reinterpret_cast<const uint4 *>(k0 + tk * kSlabRow + 8 * d8);
+          u[tk][0] = w.x;
+          u[tk][1] = w.y;
+          u[tk][2] = w.z;
+          u[tk][3] = w.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double q0 = qj[8 * d8 + 2 * e], q1 = qj[8 * d8 + 2 * e + 1];
+#pragma unroll
+          for (int tk = 0; tk < 4; ++tk) {
+            a[tk] = fma(q0, bf16_to_double(u[tk][e] & 0xFFFFu), a[tk]);
+            a[tk] = fma(q1, bf16_to_double(u[tk][e] >> 16), a[tk]);
+          }
+        }
+      }
+#pragma unroll
+      for (int tk = 0; tk < 4; ++tk)
+        if (4 * tg + tk < cnt) s_p[t0 + 4 * tg + tk][j] = a[tk] * score_scale;
+    }
   }
   __syncthreads();
 
@@ -114,29 +163,33 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
       s_l[j] = sum;
     }
   }
-  __syncthreads();
 
-  // ---- values: thread (channel d, heads 8*half .. 8*half + 7) ----
+  // ---- values: thread (channel d, heads half, half + 2, ...) ----
   const int d = tid & (kDim - 1);
   const int half = tid >> 7;
-  double o[8];
+  double o[kMaxG / 2];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) o[jj] = 0.0;
-  const uint16_t *vbase = tail_v + (static_cast<size_t>(req) * tail_cap * s.heads + h) * kDim + d;
-  for (int t = 0; t < vis; ++t) {
-    const double v = bf16_to_double(vbase[t * row_stride]);
+  for (int jj = 0; jj < kMaxG / 2; ++jj) o[jj] = 0.0;
+  for (int t0 = 0; t0 < vis; t0 += kSlab) {
+    __syncthreads();  // probabilities written / the previous slab consumed
+    const int cnt = stage(tail_v, t0);
+    __syncthreads();
+    for (int tk = 0; tk < cnt; ++tk) {
+      const double v = bf16_to_double(s_slab[tk * kSlabRow + d]);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = 8 * half + jj;
-      if (j < g) o[jj] = fma(s_p[t][j], v, o[jj]);
+      for (int jj = 0; jj < kMaxG / 2; ++jj) {
+        const int j = half + 2 * jj;
+        if (j < g) o[jj] = fma(s_p[t0 + tk][j], v, o[jj]);
+      }
     }
   }
+  __syncthreads();  // s_m, s_l of a row that sees no tail token
 
   TailPartials pt = tail_partials_of(ws, s);
   const size_t row0 = (static_cast<size_t>(bh) * s.parts + s.splits) * g;
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int j = 8 * half + jj;
+  for (int jj = 0; jj < kMaxG / 2; ++jj) {
+    const int j = half + 2 * jj;
     if (j < g) pt.o[(row0 + j) * kDim + d] = static_cast<float>(o[jj]);
   }
   if (tid < g) {
