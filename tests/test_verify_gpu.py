@@ -87,10 +87,12 @@ def run_case(lynx, H, Hq, tq, page_lists, tail_len, P_pool, seed, full, max_page
                                 block_table=torch.from_numpy(bt).cuda(),
                                 page_tokens=torch.from_numpy(page_tokens).cuda(), sm_scale=SM)
     torch.cuda.synchronize()
+    # a block-table entry outside the pool is skipped by the kernels
+    present = [[p for p in pl if 0 <= p < P_pool] for pl in page_lists]
     pages_k = [np.concatenate([deq["k", full][p] for p in pl]).astype(np.float64) if pl else
-               np.zeros((0, H, 128)) for pl in page_lists]
+               np.zeros((0, H, 128)) for pl in present]
     pages_v = [np.concatenate([deq["v", full][p] for p in pl]).astype(np.float64) if pl else
-               np.zeros((0, H, 128)) for pl in page_lists]
+               np.zeros((0, H, 128)) for pl in present]
     ref = oracle.verify_attention(q, pages_k, pages_v, tk, tv, tail_len, SM)
     check(got.cpu().numpy().astype(np.float64), ref,
           "H=%d Hq=%d tq=%d full=%s" % (H, Hq, tq, full))
@@ -101,6 +103,13 @@ def test_verify_group8_ragged_pages_and_tails(lynx, full):
     # matrix-core page kernel (group 8); a request with no full page
     for tq, tail_len in ((1, [1, 200, 320]), (5, [5, 64, 319]), (64, [64, 300, 320])):
         run_case(lynx, 2, 16, tq, [[4, 1, 6], [], [0, 2, 5, 3]], tail_len, 7, 101 + tq, full)
+
+
+@pytest.mark.parametrize("full", [True, False])
+def test_verify_group8_absent_pages_and_a_partial_row_group(lynx, full):
+    # 20 tokens: a second group of 16 rows with 4 of them; entries 9 and -4
+    # lie outside the pool of 7 pages and are skipped
+    run_case(lynx, 2, 16, 20, [[4, 9, 1], [2, -4, 6, 0]], [20, 150], 7, 211, full)
 
 
 @pytest.mark.parametrize("full", [True, False])
