@@ -61,7 +61,8 @@ def measured_traffic():
 
 def summarize(kind, db_dir, out_path, command):
     """Write a short text summary of rocprofv3 output (kernel trace with
-    --stats, or FETCH_SIZE / WRITE_SIZE counter runs) under profiles/."""
+    --stats, FETCH_SIZE / WRITE_SIZE counter runs, or a run of SQ counters
+    and derived metrics) under profiles/."""
     import glob
     import sqlite3
 
@@ -73,7 +74,26 @@ def summarize(kind, db_dir, out_path, command):
         return name.split("(")[0]
 
     lines = ["command: %s" % command]
-    if kind == "kt":
+    if kind == "sq":
+        # per kernel: the average of every collected counter over its dispatches
+        per = {}
+        for db in dbs(db_dir):
+            con = sqlite3.connect(db)
+            for name, ctr, val in con.execute(
+                    "select kernel_name, counter_name, value from counters_collection"):
+                per.setdefault(short(name), {}).setdefault(ctr, []).append(val)
+        ctrs = sorted({c for d in per.values() for c in d})
+        lines.append("")
+        lines.append("per dispatch, averaged over the kernel's dispatches; VALU/wave = "
+                     "SQ_INSTS_VALU / SQ_WAVES (instructions per wave)")
+        lines.append("%-40s %s %10s" % ("kernel", " ".join("%16s" % c[:16] for c in ctrs), "VALU/wave"))
+        for k in sorted(per):
+            avg = {c: sum(v) / len(v) for c, v in per[k].items()}
+            vpw = (avg["SQ_INSTS_VALU"] / avg["SQ_WAVES"]
+                   if avg.get("SQ_WAVES") and "SQ_INSTS_VALU" in avg else float("nan"))
+            lines.append("%-40s %s %10.1f" % (k[:40], " ".join(
+                "%16.4g" % avg.get(c, float("nan")) for c in ctrs), vpw))
+    elif kind == "kt":
         lines.append("")
         lines.append("%-44s %7s %11s %13s %6s" % ("kernel", "calls", "avg_us", "total_us", "pct"))
         for db in dbs(db_dir):
