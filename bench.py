@@ -150,6 +150,30 @@ def summarize(kind, db_dir, out_path, command):
     print("\n".join(lines))
 
 
+COPY_CEILING_BYTES = 1 << 30
+
+
+def copy_ceiling(dev, stream):
+    """Measured device-copy ceiling after the timed region: a 1 GiB
+    device-to-device copy, read + write bytes over the average time of 5
+    copies."""
+    import torch
+    a = torch.ones(COPY_CEILING_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    with torch.cuda.stream(stream):
+        b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            b.copy_(a)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del a, b
+    return {"GBps": 2 * COPY_CEILING_BYTES / (ms * 1e-3) / 1e9, "bytes_per_copy": 2 * COPY_CEILING_BYTES,
+            "how": "torch device copy of 1 GiB (read + write bytes), average of 5 after the timed region"}
+
+
 def algorithmic_bytes(w):
     """Per-launch algorithmic bytes of each kernel for workload w (one layer)."""
     per_tensor = w.batch * w.tokens * w.kv_heads * w.head_dim
@@ -544,6 +568,7 @@ def main():
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+    ceiling = copy_ceiling(dev, stream)
 
     enc_avg = per_call_ms["encode"]
     anc_avg = per_call_ms["decode_anchor"]
@@ -557,6 +582,7 @@ def main():
     }
     for k in kernels.values():
         k["pct_of_hbm_peak"] = 100.0 * k["GBps"] / HBM_PEAK_GBPS
+        k["pct_of_copy_ceiling"] = 100.0 * k["GBps"] / ceiling["GBps"]
 
     result = {
         "metric": METRIC,
@@ -575,6 +601,7 @@ def main():
                    "head_dim": w.head_dim, "tokens": w.tokens, "batch": w.batch,
                    "q_heads": w.q_heads, "buffer_sets": S},
         "pct_of_hbm_peak": 100.0 * gbps(step_bytes, step_ms) / HBM_PEAK_GBPS,
+        "copy_ceiling": ceiling,
         "kernels": kernels,
         "tokens_per_s": {"encode_kv_tokens": w.tokens * w.batch / (2 * enc_avg * 1e-3),
                          "decode_full_kv_tokens": w.tokens * w.batch / (full_avg * 1e-3),
