@@ -377,7 +377,7 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
 AttnShape attention_shape_tail(int requests, int tq, int heads, int q_heads, int max_pages) {
   AttnShape s = attention_shape(requests * tq, heads, q_heads, max_pages);
   s.tq = tq;
-  if (verify_mfma_supported(s.group) && tq > 0 && max_pages > 0) {
+  if (verify_mfma_used(s.group, tq) && max_pages > 0) {
     // the verify kernel's blocks: (request, KV head, run, group of 16 rows)
     const long long units = static_cast<long long>(requests) * heads * verify_row_blocks(tq);
     const long long target = attention_mfma_target_blocks();
@@ -441,7 +441,7 @@ hipError_t launch_attention_with_tail(const uint16_t *q, const PlanesArg &k, con
     // no page can be read: the tail is the whole context
     sp.splits = 0;
     sp.parts = 1;
-  } else if (verify_mfma_supported(s.group)) {
+  } else if (verify_mfma_used(s.group, s.tq)) {
     e = launch_verify_mfma(q, k, v, block_table, page_tokens, sp, sm_scale, full, workspace, stream);
     if (e != hipSuccess) return e;
   } else if (mfma) {

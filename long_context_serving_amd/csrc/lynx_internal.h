@@ -155,10 +155,11 @@ hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const Pl
 hipError_t launch_attention_mfma_combine(const AttnShape &s, const void *workspace, float *out,
                                          hipStream_t stream);
 
-// Verify-pass page kernel (GQA group 8): up to 16 query rows of one
+// Verify-pass page kernel (GQA group 8, 5 or more query tokens per
+// request; fewer run on the decode kernels): up to 16 query rows of one
 // request and KV head per block, one block per (request, KV head, run of
 // pages, group of 16 rows); writes the split partials of its rows.
-bool verify_mfma_supported(int group);
+bool verify_mfma_used(int group, int tq);
 int verify_row_blocks(int tq);
 hipError_t launch_verify_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
                               const int32_t *block_table, const int32_t *page_tokens,

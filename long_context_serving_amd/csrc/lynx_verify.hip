@@ -538,7 +538,12 @@ VerifyTable build_verify_table() {
 
 }  // namespace
 
-bool verify_mfma_supported(int group) { return group == kG; }
+// A block's cost per chunk does not depend on how many of its rows are
+// used, so few query tokens per request are cheaper on the decode kernels
+// (one row per query token); the crossover is measured.
+constexpr int kVerifyMinTokens = 5;
+
+bool verify_mfma_used(int group, int tq) { return group == kG && tq >= kVerifyMinTokens; }
 
 int verify_row_blocks(int tq) { return (tq + kVRows - 1) / kVRows; }
 
