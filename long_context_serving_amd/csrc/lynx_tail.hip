@@ -10,10 +10,9 @@
 // partials of the quantized pages; query token i of a request sees tail
 // tokens 0 .. tail_len - tq + i (itself and everything before it).
 //
-// The tail holds at most LYNX_TAIL_TOKENS tokens per request, so a block of
-// 256 threads keeps every score of its row group in LDS.  Products of bf16
-// values are exact in fp64 and the sums run in fp64, so the only roundings
-// are those of the fp64 sums and of storing l and o as fp32 partials.
+// Products of bf16 values are exact in fp64 and the sums run in fp64, so
+// the only roundings are those of the fp64 sums and exponentials, of the
+// rescaling between slabs of 64 tokens, and of storing l and o as fp32.
 #include <math.h>
 
 #include "lynx_internal.h"
@@ -24,6 +23,7 @@ namespace {
 constexpr int kTailThreads = 256;
 constexpr int kTailCap = LYNX_TAIL_TOKENS;
 constexpr int kMaxG = LYNX_MAX_GROUP;
+static_assert(kMaxG <= 4 * (kTailThreads / 64), "four heads per wave at most");
 
 // (m, l, o) partial rows, laid out as the page kernels lay them out:
 // m fp64 [n], l fp32 [n], o fp32 [n][128], n = rows * H * parts * group
@@ -37,18 +37,41 @@ __device__ __forceinline__ double bf16_to_double(uint32_t bits16) {
   return static_cast<double>(__uint_as_float(bits16 << 16));
 }
 
-// Tail tokens staged in LDS per pass: 64 tokens x 128 bf16, rows padded by
-// 16 bytes so that lanes reading different tokens at one channel hit
-// different banks.
+// Tail tokens staged in LDS per pass: 64 tokens x 128 bf16.  K rows are
+// padded by 16 bytes so that lanes reading different tokens at one channel
+// hit different banks; every lane reads the same V row at once, so V rows
+// are not padded.
 constexpr int kSlab = 64;
-constexpr int kSlabRow = kDim + 8;
-// q rows in LDS are padded by 16 bytes, so lanes reading different heads'
-// rows at one channel hit different banks.
-constexpr int kQStride = kDim + 2;
+constexpr int kKRow = kDim + 8;
+constexpr int kWaves = kTailThreads / 64;
 
-// Block = (query row b, KV head h).  The visible tail tokens pass through
-// LDS in slabs of 64 (K for the scores, then V for the values), each slab
-// loaded by the whole block with 16-byte loads at once.
+// value of x in lane t (t uniform over the wave)
+__device__ __forceinline__ double lane_value(double x, int t) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), t));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), t));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Block = (query row b, KV head h), four waves; wave w owns the query heads
+// w, w + 4, ... of the group (kHpw of them).  Per slab of 64 visible tail
+// tokens the whole block stages K and V in LDS with one round of 16-byte
+// loads (q with the first slab), then each wave works alone: lane t scores
+// token t against its heads, the wave reduces the maximum and the sum of the
+// exponentials (an online softmax across slabs), and lane c accumulates
+// channels 2c, 2c + 1 of the value sums, reading each token's probability
+// from the lane that holds it.
+template <int kHpw>
 __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ tail_k,
     const uint16_t *__restrict__ tail_v, const int32_t *__restrict__ tail_len, AttnShape s,
@@ -60,141 +83,142 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
   const int i = b % s.tq;  // query token within the request
   const int g = s.group;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
 
-  __shared__ double s_q[kMaxG * kQStride];
-  __shared__ double s_p[kTailCap][kMaxG];  // scores, then probabilities
-  __shared__ double s_m[kMaxG], s_l[kMaxG];
-  __shared__ __align__(16) uint16_t s_slab[kSlab * kSlabRow];
+  __shared__ double s_q[kWaves * kHpw][kDim];  // head j at row j (zero past g)
+  __shared__ __align__(16) uint16_t s_k[kSlab * kKRow];
+  __shared__ __align__(16) uint16_t s_v[kSlab * kDim];
 
   int n = tail_len[req];
   n = n < 0 ? 0 : (n > tail_cap ? tail_cap : n);
   int vis = n - s.tq + i + 1;  // tail tokens this query token sees
   vis = vis < 0 ? 0 : (vis > n ? n : vis);
 
-  for (int e = tid; e < g * kDim; e += kTailThreads) {
-    const int j = e / kDim, d = e % kDim;
-    s_q[j * kQStride + d] =
-        bf16_to_double(q[(static_cast<size_t>(b) * s.q_heads + h * g + j) * kDim + d]);
+  // q: 16-byte pieces e = tid, tid + 256 (16 per head, heads of the group
+  // contiguous in the row)
+  constexpr int kQPieces = kWaves * kHpw * (kDim / 8);
+  constexpr int kQPer = (kQPieces + kTailThreads - 1) / kTailThreads;
+  const uint16_t *qrow = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
+  uint4 qp[kQPer];
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int e = tid + k * kTailThreads;
+    qp[k] = e < kQPieces && (e >> 4) < g ? *reinterpret_cast<const uint4 *>(qrow + 8 * e)
+                                         : make_uint4(0u, 0u, 0u, 0u);
   }
 
   const size_t row_stride = static_cast<size_t>(s.heads) * kDim;  // one token of the tail
   const size_t tail0 = (static_cast<size_t>(req) * tail_cap * s.heads + h) * kDim;
-  // slab of tokens t0 .. t0 + 63 (< vis) of one tail tensor into s_slab:
-  // thread tid loads 16-byte pieces tid, tid + 256, ... (16 per token)
-  auto stage = [&](const uint16_t *tail, int t0) {
+
+  double m_run[kHpw], l_run[kHpw], o[kHpw][2];
+#pragma unroll
+  for (int hh = 0; hh < kHpw; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.0;
+    o[hh][0] = o[hh][1] = 0.0;
+  }
+
+  for (int t0 = 0; t0 < vis; t0 += kSlab) {
     const int cnt = vis - t0 < kSlab ? vis - t0 : kSlab;
-    uint4 piece[4];
+    // K and V pieces e = tid + 256 k: token e / 16, channels 8 (e % 16) ..
+    uint4 kp[4], vp[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int e = tid + k * kTailThreads;  // piece e: token e / 16, channels 8 (e % 16) ..
+      const int e = tid + k * kTailThreads;
       const int tk = e >> 4;
-      piece[k] = tk < cnt ? *reinterpret_cast<const uint4 *>(
-                                tail + tail0 + static_cast<size_t>(t0 + tk) * row_stride + (e & 15) * 8)
-                          : make_uint4(0u, 0u, 0u, 0u);
+      const size_t at = tail0 + static_cast<size_t>(t0 + tk) * row_stride + (e & 15) * 8;
+      kp[k] = tk < cnt ? *reinterpret_cast<const uint4 *>(tail_k + at) : make_uint4(0u, 0u, 0u, 0u);
+      vp[k] = tk < cnt ? *reinterpret_cast<const uint4 *>(tail_v + at) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (t0 > 0) __syncthreads();  // the previous slab consumed
+    else {
+#pragma unroll
+      for (int k = 0; k < kQPer; ++k) {
+        const int e = tid + k * kTailThreads;
+        if (e < kQPieces) {
+          const uint32_t w4[4] = {qp[k].x, qp[k].y, qp[k].z, qp[k].w};
+          double *dst = &s_q[e >> 4][8 * (e & 15)];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            dst[2 * c] = bf16_to_double(w4[c] & 0xFFFFu);
+            dst[2 * c + 1] = bf16_to_double(w4[c] >> 16);
+          }
+        }
+      }
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int e = tid + k * kTailThreads;
-      *reinterpret_cast<uint4 *>(s_slab + (e >> 4) * kSlabRow + (e & 15) * 8) = piece[k];
+      *reinterpret_cast<uint4 *>(s_k + (e >> 4) * kKRow + (e & 15) * 8) = kp[k];
+      *reinterpret_cast<uint4 *>(s_v + (e >> 4) * kDim + (e & 15) * 8) = vp[k];
     }
-    return cnt;
-  };
-
-  // ---- scores: 4 tail tokens of one head per thread and pass (each q
-  // value read from LDS serves 4 products) ----
-  for (int t0 = 0; t0 < vis; t0 += kSlab) {
-    __syncthreads();  // q staged / the previous slab consumed
-    const int cnt = stage(tail_k, t0);
     __syncthreads();
-    const int groups = (cnt + 3) >> 2;  // tokens past cnt are zero in the slab
-    for (int item = tid; item < groups * g; item += kTailThreads) {
-      const int tg = item / g, j = item - tg * g;
-      const double *qj = s_q + j * kQStride;
-      const uint16_t *k0 = s_slab + 4 * tg * kSlabRow;
-      double a[4] = {0.0, 0.0, 0.0, 0.0};
+    if (wave >= g) continue;  // no head of the group in this wave (uniform)
+
+    // ---- scores: lane t against token t (rows past cnt are zero) ----
+    double acc[kHpw][2];
+#pragma unroll
+    for (int hh = 0; hh < kHpw; ++hh) acc[hh][0] = acc[hh][1] = 0.0;
+    const uint16_t *krow = s_k + lane * kKRow;
 #pragma unroll 2
-      for (int d8 = 0; d8 < kDim / 8; ++d8) {
-        uint32_t u[4][4];
+    for (int d8 = 0; d8 < kDim / 8; ++d8) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(krow + 8 * d8);
+      const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+      double kv[8];
 #pragma unroll
-        for (int tk = 0; tk < 4; ++tk) {
-          const uint4 w = *reinterpret_cast<const uint4 *>(k0 + tk * kSlabRow + 8 * d8);
-          u[tk][0] = w.x;
-          u[tk][1] = w.y;
-          u[tk][2] = w.z;
-          u[tk][3] = w.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double q0 = qj[8 * d8 + 2 * e], q1 = qj[8 * d8 + 2 * e + 1];
-#pragma unroll
-          for (int tk = 0; tk < 4; ++tk) {
-            a[tk] = fma(q0, bf16_to_double(u[tk][e] & 0xFFFFu), a[tk]);
-            a[tk] = fma(q1, bf16_to_double(u[tk][e] >> 16), a[tk]);
-          }
-        }
+      for (int c = 0; c < 4; ++c) {
+        kv[2 * c] = bf16_to_double(w4[c] & 0xFFFFu);
+        kv[2 * c + 1] = bf16_to_double(w4[c] >> 16);
       }
 #pragma unroll
-      for (int tk = 0; tk < 4; ++tk)
-        if (4 * tg + tk < cnt) s_p[t0 + 4 * tg + tk][j] = a[tk] * score_scale;
+      for (int hh = 0; hh < kHpw; ++hh) {
+        const double *qj = &s_q[wave + kWaves * hh][8 * d8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[hh][d8 & 1] = fma(qj[c], kv[c], acc[hh][d8 & 1]);
+      }
     }
-  }
-  __syncthreads();
 
-  // ---- per head: maximum, probabilities, their sum (16 lanes per head) ----
-  {
-    const int j = tid >> 4, l16 = tid & 15;
-    double mx = -INFINITY;
-    if (j < g)
-      for (int t = l16; t < vis; t += 16) mx = fmax(mx, s_p[t][j]);
+    // ---- online softmax over the slab, then the value sums ----
+    double p[kHpw];
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off, 16));
-    double sum = 0.0;
-    if (j < g)
-      for (int t = l16; t < vis; t += 16) {
-        const double x = s_p[t][j] - mx;
-        const double p = base2 ? exp2(x) : exp(x);
-        s_p[t][j] = p;
-        sum += p;
-      }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
-    if (j < g && l16 == 0) {
-      s_m[j] = mx;
-      s_l[j] = sum;
+    for (int hh = 0; hh < kHpw; ++hh) {
+      const double x = lane < cnt ? (acc[hh][0] + acc[hh][1]) * score_scale : -INFINITY;
+      const double m_new = fmax(m_run[hh], wave_max_d(x));  // finite: cnt >= 1
+      const double dm = m_run[hh] - m_new;
+      const double alpha = base2 ? exp2(dm) : exp(dm);  // 0 on the first slab
+      const double xm = x - m_new;
+      p[hh] = lane < cnt ? (base2 ? exp2(xm) : exp(xm)) : 0.0;
+      l_run[hh] = l_run[hh] * alpha + wave_sum_d(p[hh]);
+      m_run[hh] = m_new;
+      o[hh][0] *= alpha;
+      o[hh][1] *= alpha;
     }
-  }
-
-  // ---- values: thread (channel d, heads half, half + 2, ...) ----
-  const int d = tid & (kDim - 1);
-  const int half = tid >> 7;
-  double o[kMaxG / 2];
+    for (int t = 0; t < cnt; ++t) {
+      const uint32_t v2 = *reinterpret_cast<const uint32_t *>(s_v + t * kDim + 2 * lane);
+      const double v0 = bf16_to_double(v2 & 0xFFFFu), v1 = bf16_to_double(v2 >> 16);
 #pragma unroll
-  for (int jj = 0; jj < kMaxG / 2; ++jj) o[jj] = 0.0;
-  for (int t0 = 0; t0 < vis; t0 += kSlab) {
-    __syncthreads();  // probabilities written / the previous slab consumed
-    const int cnt = stage(tail_v, t0);
-    __syncthreads();
-    for (int tk = 0; tk < cnt; ++tk) {
-      const double v = bf16_to_double(s_slab[tk * kSlabRow + d]);
-#pragma unroll
-      for (int jj = 0; jj < kMaxG / 2; ++jj) {
-        const int j = half + 2 * jj;
-        if (j < g) o[jj] = fma(s_p[t0 + tk][j], v, o[jj]);
+      for (int hh = 0; hh < kHpw; ++hh) {
+        const double pt = lane_value(p[hh], t);
+        o[hh][0] = fma(pt, v0, o[hh][0]);
+        o[hh][1] = fma(pt, v1, o[hh][1]);
       }
     }
   }
-  __syncthreads();  // s_m, s_l of a row that sees no tail token
 
   TailPartials pt = tail_partials_of(ws, s);
   const size_t row0 = (static_cast<size_t>(bh) * s.parts + s.splits) * g;
 #pragma unroll
-  for (int jj = 0; jj < kMaxG / 2; ++jj) {
-    const int j = half + 2 * jj;
-    if (j < g) pt.o[(row0 + j) * kDim + d] = static_cast<float>(o[jj]);
-  }
-  if (tid < g) {
-    pt.m[row0 + tid] = s_m[tid];  // -inf when the token sees no tail token
-    pt.l[row0 + tid] = static_cast<float>(s_l[tid]);
+  for (int hh = 0; hh < kHpw; ++hh) {
+    const int j = wave + kWaves * hh;
+    if (j < g) {
+      reinterpret_cast<float2 *>(pt.o + (row0 + j) * kDim)[lane] =
+          make_float2(static_cast<float>(o[hh][0]), static_cast<float>(o[hh][1]));
+      if (lane == 0) {
+        pt.m[row0 + j] = m_run[hh];  // -inf when the token sees no tail token
+        pt.l[row0 + j] = static_cast<float>(l_run[hh]);
+      }
+    }
   }
 }
 
@@ -209,8 +233,15 @@ hipError_t launch_attention_tail_part(const uint16_t *q, const uint16_t *tail_k,
   const double scale = base2 ? static_cast<double>(sm_scale) * 1.4426950408889634074
                              : static_cast<double>(sm_scale);
   const dim3 grid(static_cast<unsigned>(static_cast<long long>(s.batch) * s.heads));
-  hipLaunchKernelGGL(attn_tail_kernel, grid, dim3(kTailThreads), 0, stream, q, tail_k, tail_v,
-                     tail_len, s, tail_cap, scale, base2, workspace);
+  if (s.group <= kWaves)
+    hipLaunchKernelGGL(attn_tail_kernel<1>, grid, dim3(kTailThreads), 0, stream, q, tail_k,
+                       tail_v, tail_len, s, tail_cap, scale, base2, workspace);
+  else if (s.group <= 2 * kWaves)
+    hipLaunchKernelGGL(attn_tail_kernel<2>, grid, dim3(kTailThreads), 0, stream, q, tail_k,
+                       tail_v, tail_len, s, tail_cap, scale, base2, workspace);
+  else
+    hipLaunchKernelGGL(attn_tail_kernel<4>, grid, dim3(kTailThreads), 0, stream, q, tail_k,
+                       tail_v, tail_len, s, tail_cap, scale, base2, workspace);
   return hipGetLastError();
 }
 

@@ -117,6 +117,13 @@ def test_verify_group16_valu_path(lynx, full):
     run_case(lynx, 2, 32, 7, [[3, 5], [1], [6, 0, 2]], [7, 100, 256], 7, 303, full)
 
 
+@pytest.mark.parametrize("H,Hq", [(4, 8), (2, 10)])
+def test_verify_small_groups_tails_across_slabs(lynx, H, Hq):
+    # groups of 2 and 5 query heads (a wave with one head, waves with none);
+    # tails that end just before, on and just after 64-token slab edges
+    run_case(lynx, H, Hq, 3, [[2], [], [0, 1], [3]], [63, 64, 65, 131], 4, 404 + Hq, True)
+
+
 def test_verify_pool_of_zero_pages(lynx):
     # the tail is the whole context
     run_case(lynx, 1, 8, 3, [[], []], [3, 250], 0, 505, True)
