@@ -13,7 +13,8 @@ graph of back-to-back launches, with events on the launch stream between
 the phases giving every kernel's time inside the timed region.
 
 Prints ONE JSON line.  Throughput counts algorithmic bytes: encode
-3.28125 B per K/V element (2 read, 0.5 + 0.5 + 0.03125 + 0.25 written),
+3.28125 B per K/V element (2 read, 0.5 + 0.5 + 0.03125 + 0.25 written; one
+launch encodes K and V),
 full decode 1.28125 B and anchor-only decode 0.78125 B per element (plus
 query and output).
 """
@@ -33,7 +34,7 @@ METRIC = "encode GB/s + fused-dequant decode-attn GB/s (% of HBM peak), 1×MI355
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 ENCODER_SOURCE = os.path.join(ROOT, "long_context_serving_amd", "csrc", "lynx_encode.hip")
-TRAFFIC_SUMMARY = os.path.join(PROFILES, "encode_kernel_ctx32k_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(PROFILES, "encode_kv_kernel_ctx32k_hbm_traffic.txt")
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -125,7 +126,7 @@ def summarize(kind, db_dir, out_path, command):
         exp_kib = COPY_PROBE_BYTES / 1024.0
         f_fetch = exp_kib / probe["FETCH_SIZE"]
         f_write = exp_kib / probe["WRITE_SIZE"]
-        enc = [k for k in avg if k.startswith("encode_kernel")]
+        enc = [k for k in avg if k.startswith("encode_kv_kernel")]
         enc_fetch = sum(avg[k]["FETCH_SIZE"] for k in enc) / len(enc)
         enc_write = sum(avg[k]["WRITE_SIZE"] for k in enc) / len(enc)
         traffic = (enc_fetch * f_fetch + enc_write * f_write) * 1024.0
@@ -179,7 +180,7 @@ def algorithmic_bytes(w):
     per_tensor = w.batch * w.tokens * w.kv_heads * w.head_dim
     qo = w.batch * w.q_heads * w.head_dim * (2 + 4)
     return {
-        "encode": per_tensor * 3.28125,                 # one tensor (K or V) per launch
+        "encode": 2 * per_tensor * 3.28125,             # K and V in one launch
         "decode_full": 2 * per_tensor * 1.28125 + qo,
         "decode_anchor": 2 * per_tensor * 0.78125 + qo,
         "elements_per_tensor": per_tensor,
@@ -466,8 +467,9 @@ def main():
     from long_context_serving_amd import lynx, synth
 
     w = synth.WORKLOADS[args.workload]
-    if w.layers != 1 or w.batch < 1 or not w.q_heads:
-        raise SystemExit("bench workload must be a single-layer decode workload")
+    if w.layers != 1 or w.batch != 1 or not w.q_heads:
+        raise SystemExit("bench workload must be a single-request, single-layer decode workload "
+                         "(the batched and multi-layer configurations are parity-test cases)")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     S = max(2, args.sets)
@@ -505,8 +507,8 @@ def main():
     full_calls = []
     for j in range(S):
         e = sets[j]
-        enc_calls.append(lambda e=e: lynx.quantize_pages(e["k"], lynx.ROLE_KEY, out=e["pk"]))
-        enc_calls.append(lambda e=e: lynx.quantize_pages(e["v"], lynx.ROLE_VALUE, out=e["pv"]))
+        enc_calls.append(lambda e=e: lynx.quantize_kv_pages(e["k"], e["v"], out_k=e["pk"],
+                                                            out_v=e["pv"]))
         anc_calls.append(lambda e=e: lynx.decode_attention(q, e["pk"], e["pv"], w.pages, full=False,
                                                            sm_scale=sm, out=out, workspace=ws))
         full_calls.append(lambda e=e: lynx.decode_attention(q, e["pk"], e["pv"], w.pages, full=True,
@@ -557,7 +559,7 @@ def main():
     wall = time.perf_counter() - t_start
     step_ms = evs[0][0].elapsed_time(evs[rounds - 1][3]) / K
     phase_ms = [sum(evs[r][p].elapsed_time(evs[r][p + 1]) for r in range(rounds)) for p in range(3)]
-    per_call_ms = {"encode": phase_ms[0] / (2 * K), "decode_anchor": phase_ms[1] / K,
+    per_call_ms = {"encode": phase_ms[0] / K, "decode_anchor": phase_ms[1] / K,
                    "decode_full": phase_ms[2] / K}
 
     verify = verify_leg(args, w, sets, dev, sm, stream) if args.verify else None
@@ -568,13 +570,14 @@ def main():
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
-    ceiling = copy_ceiling(dev, stream)
+    # counter runs (--copy-probe) leave the probe as the only large copy
+    ceiling = None if args.copy_probe else copy_ceiling(dev, stream)
 
     enc_avg = per_call_ms["encode"]
     anc_avg = per_call_ms["decode_anchor"]
     full_avg = per_call_ms["decode_full"]
     gbps = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
-    step_bytes = 2 * ab["encode"] + ab["decode_full"] + ab["decode_anchor"]
+    step_bytes = ab["encode"] + ab["decode_full"] + ab["decode_anchor"]
     kernels = {
         "encode": {"us_per_launch": enc_avg * 1e3, "GBps": gbps(ab["encode"], enc_avg)},
         "decode_anchor": {"us_per_call": anc_avg * 1e3, "GBps": gbps(ab["decode_anchor"], anc_avg)},
@@ -582,7 +585,8 @@ def main():
     }
     for k in kernels.values():
         k["pct_of_hbm_peak"] = 100.0 * k["GBps"] / HBM_PEAK_GBPS
-        k["pct_of_copy_ceiling"] = 100.0 * k["GBps"] / ceiling["GBps"]
+        if ceiling is not None:
+            k["pct_of_copy_ceiling"] = 100.0 * k["GBps"] / ceiling["GBps"]
 
     result = {
         "metric": METRIC,
@@ -603,10 +607,10 @@ def main():
         "pct_of_hbm_peak": 100.0 * gbps(step_bytes, step_ms) / HBM_PEAK_GBPS,
         "copy_ceiling": ceiling,
         "kernels": kernels,
-        "tokens_per_s": {"encode_kv_tokens": w.tokens * w.batch / (2 * enc_avg * 1e-3),
+        "tokens_per_s": {"encode_kv_tokens": w.tokens * w.batch / (enc_avg * 1e-3),
                          "decode_full_kv_tokens": w.tokens * w.batch / (full_avg * 1e-3),
                          "decode_anchor_kv_tokens": w.tokens * w.batch / (anc_avg * 1e-3)},
-        "roofline": {"bound": "hbm", "kernel": "encode_kernel",
+        "roofline": {"bound": "hbm", "kernel": "encode_kv_kernel",
                      "timing": "events on the launch stream around graphs of back-to-back launches, timed region",
                      "achieved": gbps(ab["encode"], enc_avg), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": gbps(ab["encode"], enc_avg) / HBM_PEAK_GBPS,

@@ -129,6 +129,23 @@ int lynx_quantize_pages(const uint16_t *kv, int64_t num_pages,
                         const lynx_planes *out, void *stream);
 
 /*
+ * The K and the V tensor of one layer in one call (section 3's quantizer on
+ * both caches of a layer): the same planes, byte for byte, as
+ * lynx_quantize_pages(k, ..., LYNX_ROLE_KEY, k_out) followed by
+ * lynx_quantize_pages(v, ..., LYNX_ROLE_VALUE, v_out), from one kernel
+ * launch, so that the V tiles start as the K tiles finish.
+ *   k, v          bf16 bit patterns [P][256][H][128] each, 16-byte aligned
+ *   k_out, v_out  planes as for one tensor (every member non-NULL, 16-byte
+ *                 aligned); the four inputs and outputs must not overlap
+ * 2 * P * H must not exceed 2^31 - 1.  P = 0 is a no-op.  Errors: NULL_ARG,
+ * BAD_SHAPE, MISALIGNED, DEVICE, HIP.
+ */
+int lynx_quantize_kv_pages(const uint16_t *k, const uint16_t *v, int64_t num_pages,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           const lynx_planes *k_out, const lynx_planes *v_out,
+                           void *stream);
+
+/*
  * Standalone dequantizers (section 4: the draft reads the anchor stream
  * alone; the refined cache reads anchor and residual).  `in` as written by
  * lynx_quantize_pages with the same role; the anchor variant never reads

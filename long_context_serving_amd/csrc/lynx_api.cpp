@@ -221,6 +221,26 @@ int lynx_quantize_pages(const uint16_t *kv, int64_t num_pages, int32_t num_kv_he
   return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
 }
 
+int lynx_quantize_kv_pages(const uint16_t *k, const uint16_t *v, int64_t num_pages,
+                           int32_t num_kv_heads, int32_t head_dim, const lynx_planes *k_out,
+                           const lynx_planes *v_out, void *stream) {
+  int rc = check_tile_shape(num_pages, num_kv_heads, head_dim, LYNX_ROLE_KEY);
+  if (rc) return rc;
+  if (2 * num_pages * static_cast<int64_t>(num_kv_heads) > 0x7FFFFFFFLL) return LYNX_ERR_BAD_SHAPE;
+  if (num_pages == 0) return LYNX_OK;
+  if (!k || !v) return LYNX_ERR_NULL_ARG;
+  rc = check_planes(k_out, true);
+  if (rc) return rc;
+  rc = check_planes(v_out, true);
+  if (rc) return rc;
+  if (!aligned16(k) || !aligned16(v)) return LYNX_ERR_MISALIGNED;
+  rc = check_device();
+  if (rc) return rc;
+  const hipError_t e = lynx::launch_encode_kv(k, v, num_pages, num_kv_heads, to_arg(k_out),
+                                              to_arg(v_out), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LYNX_OK : LYNX_ERR_HIP;
+}
+
 int lynx_quantize_pages_split(const uint16_t *kv, int64_t num_pages, int32_t num_kv_heads,
                               int32_t head_dim, int32_t role, int32_t anchor_bits,
                               const lynx_planes *out, void *stream) {

@@ -181,26 +181,36 @@ __device__ __forceinline__ uint32_t codes4(float d0, float d1, float d2, float d
 // 32-bit lane offsets.  kBits = 4 writes the 4-bit planes; other values
 // write the b + (8 - b) streams of the same codes (out.anchor: b bits per
 // element, out.residual: 8 - b), re-cut from the staged planes.
+// Workgroup storage of one tile.  The planes are staged in LDS and written
+// out as contiguous 16-byte units.  K rows of 16 words are padded to 20 and
+// V's 16-byte units are XOR-swizzled (unit ^ (unit >> 3 & 7)), which spreads
+// a wave's word writes over the banks and keeps every 16-byte unit
+// contiguous.
+struct EncodeSmem {
+  uint2 lvl[kBuckets];
+  float min[kChunks][kDim];
+  float max[kChunks][kDim];
+  float mn[kDim];
+  float inv[kDim];
+  __align__(16) uint32_t pl[2][kPage * 20];
+};
+
 template <int kRole, int kBits>
-__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, EncodeTables tab) {
+__device__ __forceinline__ void encode_tile(EncodeSmem &sm, const uint16_t *__restrict__ kv,
+                                            int heads, int tile, const PlanesArg &out,
+                                            const EncodeTables &tab) {
   const int c = threadIdx.x >> 6;  // chunk = wave
   const int lane = threadIdx.x & 63;
   const int cg = lane >> 2;  // channel group: channels 8cg .. 8cg+7
   const int r = lane & 3;    // token group (the 4 lanes of a quad share channels)
+  uint2 *const s_lvl = sm.lvl;
+  float (*const s_min)[kDim] = sm.min;
+  float (*const s_max)[kDim] = sm.max;
+  float *const s_mn = sm.mn;
+  float *const s_inv = sm.inv;
+  uint32_t (*const s_pl)[kPage * 20] = sm.pl;
 
-  __shared__ uint2 s_lvl[kBuckets];
-  __shared__ float s_min[kChunks][kDim];
-  __shared__ float s_max[kChunks][kDim];
-  __shared__ float s_mn[kDim];
-  __shared__ float s_inv[kDim];
-  // The planes are staged in LDS and written out as contiguous 16-byte
-  // units.  K rows of 16 words are padded to 20 and V's 16-byte units are
-  // XOR-swizzled (unit ^ (unit >> 3 & 7)), which spreads a wave's word
-  // writes over the banks and keeps every 16-byte unit contiguous.
-  __shared__ __align__(16) uint32_t s_pl[2][kPage * 20];
-
-  const int tile = blockIdx.x;  // page * heads + head
+  // tile = page * heads + head
   fill_level_table(s_lvl, tab);  // published by the first __syncthreads below
 
   // ---- load the lane's 8 tokens x 8 channels (bf16 -> fp32 is exact) ----
@@ -389,6 +399,27 @@ void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, En
   }
 }
 
+template <int kRole, int kBits>
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, EncodeTables tab) {
+  __shared__ EncodeSmem sm;
+  encode_tile<kRole, kBits>(sm, kv, heads, static_cast<int>(blockIdx.x), out, tab);
+}
+
+// K and V of one layer in one launch: blocks 0 .. n - 1 encode the K tiles,
+// blocks n .. 2n - 1 the V tiles, so that the second tensor's tiles start as
+// the first one's finish instead of after a launch boundary.
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void encode_kv_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int heads,
+                      int ntiles, PlanesArg kout, PlanesArg vout, EncodeTables tab) {
+  __shared__ EncodeSmem sm;
+  const int t = static_cast<int>(blockIdx.x);
+  if (t < ntiles)
+    encode_tile<LYNX_ROLE_KEY, 4>(sm, k, heads, t, kout, tab);
+  else
+    encode_tile<LYNX_ROLE_VALUE, 4>(sm, v, heads, t - ntiles, vout, tab);
+}
+
 // Exhaustive check of the encoder's level path (the bucket table) against
 // the exact threshold count over fp32 bit patterns [begin, end) (values in
 // [0, 2); above 1 the expected level is that of the clamped u, 127).
@@ -442,6 +473,17 @@ void launch_encode_bits(const uint16_t *kv, unsigned blocks, int heads, int role
                        stream, kv, heads, out, tab);
 }
 }  // namespace
+
+hipError_t launch_encode_kv(const uint16_t *k, const uint16_t *v, int64_t num_pages, int heads,
+                            const PlanesArg &kout, const PlanesArg &vout, hipStream_t stream) {
+  if (num_pages == 0) return hipSuccess;
+  if (!bucket_table().ok || 2 * num_pages * heads > INT32_MAX) return hipErrorInvalidValue;
+  EncodeTables tab = encode_tables();
+  const int ntiles = static_cast<int>(num_pages * heads);
+  hipLaunchKernelGGL(encode_kv_kernel, dim3(static_cast<unsigned>(2 * ntiles)), dim3(kEncThreads), 0,
+                     stream, k, v, heads, ntiles, kout, vout, tab);
+  return hipGetLastError();
+}
 
 hipError_t launch_encode(const uint16_t *kv, int64_t num_pages, int heads,
                          int role, const PlanesArg &out, hipStream_t stream, int anchor_bits) {

@@ -81,6 +81,10 @@ hipError_t launch_encode(const uint16_t *kv, int64_t num_pages, int heads,
                          int role, const PlanesArg &out, hipStream_t stream,
                          int anchor_bits = 4);
 
+// K and V of one layer (4 + 4 planes) in one launch.
+hipError_t launch_encode_kv(const uint16_t *k, const uint16_t *v, int64_t num_pages, int heads,
+                            const PlanesArg &kout, const PlanesArg &vout, hipStream_t stream);
+
 hipError_t launch_code_map_check(uint32_t begin, uint32_t end,
                                  unsigned long long *mismatches, hipStream_t stream);
 

@@ -50,6 +50,9 @@ _lib.lynx_chunk_scale_bytes.argtypes = [_i64, _i32]
 _lib.lynx_chunk_scale_bytes.restype = _sz
 _lib.lynx_quantize_pages.argtypes = [_P, _i64, _i32, _i32, _i32, ctypes.POINTER(_CPlanes), _P]
 _lib.lynx_quantize_pages.restype = ctypes.c_int
+_lib.lynx_quantize_kv_pages.argtypes = [_P, _P, _i64, _i32, _i32, ctypes.POINTER(_CPlanes),
+                                        ctypes.POINTER(_CPlanes), _P]
+_lib.lynx_quantize_kv_pages.restype = ctypes.c_int
 for _name in ("lynx_dequantize_anchor", "lynx_dequantize_full"):
     getattr(_lib, _name).argtypes = [ctypes.POINTER(_CPlanes), _i64, _i32, _i32, _i32, _P, _P]
     getattr(_lib, _name).restype = ctypes.c_int
@@ -203,6 +206,29 @@ def quantize_pages(kv: torch.Tensor, role: int, out: Optional[Planes] = None, st
     _check(_lib.lynx_quantize_pages(_ptr(kv), P, H, D, role, ctypes.byref(cp), _stream(stream)),
            "lynx_quantize_pages")
     return out
+
+
+def quantize_kv_pages(k: torch.Tensor, v: torch.Tensor, out_k: Optional[Planes] = None,
+                      out_v: Optional[Planes] = None, stream=None):
+    """Encode a layer's K and V pages (bf16 [P][256][H][128] each) in one
+    launch; the same planes as quantize_pages on each.  Returns (K, V) planes."""
+    k, v = _bf16_bits(k), _bf16_bits(v)
+    for name, x in (("k", k), ("v", v)):
+        if x.dim() != 4 or x.shape[1] != PAGE or not x.is_contiguous():
+            raise ValueError("%s must be a contiguous [P][256][H][128] bf16 tensor" % name)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    P, _, H, D = k.shape
+    if out_k is None:
+        out_k = alloc_planes(P, H, ROLE_KEY, k.device)
+    if out_v is None:
+        out_v = alloc_planes(P, H, ROLE_VALUE, v.device)
+    if out_k.role != ROLE_KEY or out_v.role != ROLE_VALUE:
+        raise ValueError("out_k must be key planes and out_v value planes")
+    ck, cv = out_k.c(), out_v.c()
+    _check(_lib.lynx_quantize_kv_pages(_ptr(k), _ptr(v), P, H, D, ctypes.byref(ck), ctypes.byref(cv),
+                                       _stream(stream)), "lynx_quantize_kv_pages")
+    return out_k, out_v
 
 
 def dequantize(planes: Planes, full: bool = True, out: Optional[torch.Tensor] = None,

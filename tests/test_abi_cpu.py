@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("lynx_quantize_pages", "lynx_dequantize_anchor", "lynx_dequantize_full",
+    for required in ("lynx_quantize_pages", "lynx_quantize_kv_pages", "lynx_dequantize_anchor",
+                     "lynx_dequantize_full",
                      "lynx_decode_attention_anchor", "lynx_decode_attention_full",
                      "lynx_decode_attention_workspace_size", "lynx_status_string"):
         assert required in names
@@ -71,6 +72,22 @@ def test_argument_errors_are_reported_before_any_launch(lib):
     assert lib.lynx_quantize_pages(kv, 4, 8, 128, 1, ctypes.byref(bad), None) == -3
     # zero pages is a no-op that needs no device
     assert lib.lynx_quantize_pages(kv, 0, 8, 128, 0, ctypes.byref(pl), None) == 0
+
+    lib.lynx_quantize_kv_pages.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(CPlanes), ctypes.POINTER(CPlanes), P]
+    kv2 = P(0x50000)
+    pv = _fake_planes(0x60000)
+    q2 = lib.lynx_quantize_kv_pages
+    assert q2(kv, None, 4, 8, 128, ctypes.byref(pl), ctypes.byref(pv), None) == -1
+    assert q2(kv, kv2, 4, 8, 128, ctypes.byref(pl), None, None) == -1
+    assert q2(kv, kv2, 4, 8, 64, ctypes.byref(pl), ctypes.byref(pv), None) == -2
+    assert q2(kv, kv2, -1, 8, 128, ctypes.byref(pl), ctypes.byref(pv), None) == -2
+    assert q2(kv, kv2, 1 << 28, 8, 128, ctypes.byref(pl), ctypes.byref(pv), None) == -2  # 2 P H > 2^31 - 1
+    assert q2(kv, P(0x50008), 4, 8, 128, ctypes.byref(pl), ctypes.byref(pv), None) == -3
+    bad = _fake_planes()
+    bad.residual = None
+    assert q2(kv, kv2, 4, 8, 128, ctypes.byref(pl), ctypes.byref(bad), None) == -1
+    assert q2(kv, kv2, 0, 8, 128, ctypes.byref(pl), ctypes.byref(pv), None) == 0
 
     for name in ("lynx_dequantize_anchor", "lynx_dequantize_full"):
         fn = getattr(lib, name)

@@ -53,12 +53,13 @@ def gpu_codes(pl, P, H, role):
     return unpack_codes(a, r, P, H, role)
 
 
-def check_encode(lynx, x_bits, role, enc=None):
+def check_encode(lynx, x_bits, role, enc=None, pl=None):
     P, _, H, _ = x_bits.shape
     print("encode parity P=%d H=%d role=%d" % (P, H, role), flush=True)
     if enc is None:
         enc = oracle.encode(x_bits)
-    pl = lynx.quantize_pages(to_dev(x_bits), role)
+    if pl is None:
+        pl = lynx.quantize_pages(to_dev(x_bits), role)
     torch.cuda.synchronize()
     a, r, code = gpu_codes(pl, P, H, role)
     ref = enc["codes"]
@@ -342,6 +343,26 @@ def test_ragged_lengths_group_sizes_and_skipped_pages(lynx):
             got = run_gpu_attention(lynx, q, pk, pv, max_pages, full, block_table=bt,
                                     seq_lens=[256 * n for n in lengths])
             check_attention(got, ref, "ragged H=%d Hq=%d full=%s" % (H, Hq, full))
+
+
+@pytest.mark.parametrize("P,H", [(1, 1), (3, 5), (128, 8)])
+def test_kv_encode_in_one_launch_equals_one_launch_per_tensor(lynx, P, H):
+    # lynx_quantize_kv_pages: every byte of both tensors' planes as written by
+    # lynx_quantize_pages per tensor; the small shapes also against the oracle
+    w = dataclasses.replace(synth.WORKLOADS["ctx32k"], kv_heads=H, tokens=P * 256)
+    xk, xv = synth.kv_pages(w, 0, 0, 0), synth.kv_pages(w, 0, 1, 0)
+    print("kv encode P=%d H=%d" % (P, H), flush=True)
+    k, v = to_dev(xk), to_dev(xv)
+    pk1 = lynx.quantize_pages(k, lynx.ROLE_KEY)
+    pv1 = lynx.quantize_pages(v, lynx.ROLE_VALUE)
+    pk2, pv2 = lynx.quantize_kv_pages(k, v)
+    torch.cuda.synchronize()
+    for one, two in ((pk1, pk2), (pv1, pv2)):
+        for name in ("anchor", "residual", "page_min", "page_range", "chunk_mean", "chunk_maxabs"):
+            assert torch.equal(getattr(one, name), getattr(two, name)), name
+    if P * H <= 16:
+        check_encode(lynx, xk, lynx.ROLE_KEY, pl=pk2)
+        check_encode(lynx, xv, lynx.ROLE_VALUE, pl=pv2)
 
 
 def test_repeat_runs_are_bitwise_identical(lynx):
