@@ -380,9 +380,11 @@ def test_repeat_runs_are_bitwise_identical(lynx):
     assert torch.equal(o1, o2)
 
 
-def test_graph_replays_match_eager(lynx):
-    """The four calls of one step captured in a HIP graph: every replay, with
-    other eager work on the device in between, is bitwise the eager result."""
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_graph_replays_match_eager(lynx, one_launch):
+    """The calls of one step captured in a HIP graph (K and V encoded by one
+    launch or one launch each): every replay, with other eager work on the
+    device in between, is bitwise the eager result."""
     w = synth.WORKLOADS["tiny"]
     xk, xv = to_dev(synth.kv_pages(w, 0, 0, 0)), to_dev(synth.kv_pages(w, 0, 1, 0))
     other = to_dev(synth.kv_pages(w, 0, 0, 3))
@@ -395,8 +397,11 @@ def test_graph_replays_match_eager(lynx):
     of = torch.empty_like(oa)
 
     def step():
-        lynx.quantize_pages(xk, 0, out=pk)
-        lynx.quantize_pages(xv, 1, out=pv)
+        if one_launch:
+            lynx.quantize_kv_pages(xk, xv, out_k=pk, out_v=pv)
+        else:
+            lynx.quantize_pages(xk, 0, out=pk)
+            lynx.quantize_pages(xv, 1, out=pv)
         lynx.decode_attention(q, pk, pv, w.pages, full=False, sm_scale=SM, out=oa, workspace=ws)
         lynx.decode_attention(q, pk, pv, w.pages, full=True, sm_scale=SM, out=of, workspace=ws)
 
