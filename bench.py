@@ -494,13 +494,13 @@ def main():
     q = to_dev(qb)
     out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
     ws = lynx.alloc_workspace(w.batch, w.kv_heads, w.q_heads, w.pages, dev)
-    # A step is one pass of the hot path over one buffer set: encode K and V,
-    # anchor-only decode, full decode.  The timed loop runs the steps in
+    # A step is one pass of the hot path over one buffer set: encode K and V
+    # (one launch), anchor-only decode, full decode.  The timed loop runs the steps in
     # rounds of S: one HIP graph encodes all S sets back to back, a second
     # runs the anchor decode of all S sets, a third the full decode.  Events
     # recorded on the launch stream between the three graphs give each
     # kernel's average time inside the timed region (the graph boundaries
-    # are shared by 2S or S back-to-back launches).  Set j is decoded after
+    # are shared by S back-to-back launches).  Set j is decoded after
     # the other sets were encoded, so its planes are no longer cached.
     enc_calls = []
     anc_calls = []

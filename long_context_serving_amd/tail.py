@@ -17,6 +17,7 @@ tokens after its last full page and the pool pages it owns:
 
 Everything here is bookkeeping, copies and calls into liblynx.
 """
+import contextlib
 from typing import List, Optional
 
 import torch
@@ -83,15 +84,20 @@ class TailCache:
             if len(self._pages[r]) >= self.max_pages:
                 raise RuntimeError("request %d has max_pages pages" % r)
             p = self._free.pop(0)
-            for tail, pool, role in ((self.tail_k, self.k_pool, lynx.ROLE_KEY),
-                                     (self.tail_v, self.v_pool, lynx.ROLE_VALUE)):
-                lynx.quantize_pages(tail[r, :lynx.PAGE].unsqueeze(0), role,
-                                    out=lynx.planes_view(pool, p, 1), stream=stream)
-                rest = self._tail[r] - lynx.PAGE
+            # K and V of the page in one launch, then both tails shift down
+            lynx.quantize_kv_pages(self.tail_k[r, :lynx.PAGE].unsqueeze(0),
+                                   self.tail_v[r, :lynx.PAGE].unsqueeze(0),
+                                   out_k=lynx.planes_view(self.k_pool, p, 1),
+                                   out_v=lynx.planes_view(self.v_pool, p, 1), stream=stream)
+            rest = self._tail[r] - lynx.PAGE
+            # the shift and the block-table entry go on the encoder's stream,
+            # so the shift cannot overwrite tokens before the encoder reads them
+            with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
                 if rest:
-                    tail[r, :rest].copy_(tail[r, lynx.PAGE:lynx.PAGE + rest].clone())
+                    for tail in (self.tail_k, self.tail_v):
+                        tail[r, :rest].copy_(tail[r, lynx.PAGE:lynx.PAGE + rest].clone())
+                self.block_table[r, len(self._pages[r])] = p
             self._tail[r] -= lynx.PAGE
-            self.block_table[r, len(self._pages[r])] = p
             self._pages[r].append(p)
             written += 1
         self._publish(r)
