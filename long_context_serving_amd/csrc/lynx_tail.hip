@@ -20,7 +20,7 @@
 namespace lynx {
 namespace {
 
-constexpr int kTailThreads = 256;
+constexpr int kTailThreads = 512;
 constexpr int kTailCap = LYNX_TAIL_TOKENS;
 constexpr int kMaxG = LYNX_MAX_GROUP;
 static_assert(kMaxG <= 4 * (kTailThreads / 64), "four heads per wave at most");
@@ -63,8 +63,8 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-// Block = (query row b, KV head h), four waves; wave w owns the query heads
-// w, w + 4, ... of the group (kHpw of them).  Per slab of 64 visible tail
+// Block = (query row b, KV head h), eight waves; wave w owns the query heads
+// w, w + 8, ... of the group (kHpw of them).  Per slab of 64 visible tail
 // tokens the whole block stages K and V in LDS with one round of 16-byte
 // loads (q with the first slab), then each wave works alone: lane t scores
 // token t against its heads, the wave reduces the maximum and the sum of the
@@ -90,13 +90,8 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
   __shared__ __align__(16) uint16_t s_k[kSlab * kKRow];
   __shared__ __align__(16) uint16_t s_v[kSlab * kDim];
 
-  int n = tail_len[req];
-  n = n < 0 ? 0 : (n > tail_cap ? tail_cap : n);
-  int vis = n - s.tq + i + 1;  // tail tokens this query token sees
-  vis = vis < 0 ? 0 : (vis > n ? n : vis);
-
-  // q: 16-byte pieces e = tid, tid + 256 (16 per head, heads of the group
-  // contiguous in the row)
+  // q: 16-byte pieces e = tid, tid + 512, ... (16 per head, heads of the
+  // group contiguous in the row)
   constexpr int kQPieces = kWaves * kHpw * (kDim / 8);
   constexpr int kQPer = (kQPieces + kTailThreads - 1) / kTailThreads;
   const uint16_t *qrow = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
@@ -111,6 +106,31 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
   const size_t row_stride = static_cast<size_t>(s.heads) * kDim;  // one token of the tail
   const size_t tail0 = (static_cast<size_t>(req) * tail_cap * s.heads + h) * kDim;
 
+  // K and V pieces e = tid + 512 k of a slab: token e / 16, channels
+  // 8 (e % 16) .. 8 (e % 16) + 7; rows from `rows` on are zero
+  constexpr int kPer = kSlab * (kDim / 8) / kTailThreads;
+  uint4 kp[kPer], vp[kPer];
+  auto load_slab = [&](int t0, int rows) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + k * kTailThreads;
+      const int tk = e >> 4;
+      const size_t at = tail0 + static_cast<size_t>(t0 + tk) * row_stride + (e & 15) * 8;
+      kp[k] = tk < rows ? *reinterpret_cast<const uint4 *>(tail_k + at) : make_uint4(0u, 0u, 0u, 0u);
+      vp[k] = tk < rows ? *reinterpret_cast<const uint4 *>(tail_v + at) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  // The first slab is requested before the tail length is known: its rows
+  // below min(64, tail_cap) lie in this request's tail, and rows past the
+  // visible count are never used (their scores are replaced by -inf and
+  // their values are not read).
+  load_slab(0, tail_cap < kSlab ? tail_cap : kSlab);
+
+  int n = tail_len[req];
+  n = n < 0 ? 0 : (n > tail_cap ? tail_cap : n);
+  int vis = n - s.tq + i + 1;  // tail tokens this query token sees
+  vis = vis < 0 ? 0 : (vis > n ? n : vis);
+
   double m_run[kHpw], l_run[kHpw], o[kHpw][2];
 #pragma unroll
   for (int hh = 0; hh < kHpw; ++hh) {
@@ -121,18 +141,10 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
 
   for (int t0 = 0; t0 < vis; t0 += kSlab) {
     const int cnt = vis - t0 < kSlab ? vis - t0 : kSlab;
-    // K and V pieces e = tid + 256 k: token e / 16, channels 8 (e % 16) ..
-    uint4 kp[4], vp[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = tid + k * kTailThreads;
-      const int tk = e >> 4;
-      const size_t at = tail0 + static_cast<size_t>(t0 + tk) * row_stride + (e & 15) * 8;
-      kp[k] = tk < cnt ? *reinterpret_cast<const uint4 *>(tail_k + at) : make_uint4(0u, 0u, 0u, 0u);
-      vp[k] = tk < cnt ? *reinterpret_cast<const uint4 *>(tail_v + at) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (t0 > 0) __syncthreads();  // the previous slab consumed
-    else {
+    if (t0 > 0) {
+      load_slab(t0, cnt);
+      __syncthreads();  // the previous slab consumed
+    } else {
 #pragma unroll
       for (int k = 0; k < kQPer; ++k) {
         const int e = tid + k * kTailThreads;
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
       }
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kPer; ++k) {
       const int e = tid + k * kTailThreads;
       *reinterpret_cast<uint4 *>(s_k + (e >> 4) * kKRow + (e & 15) * 8) = kp[k];
       *reinterpret_cast<uint4 *>(s_v + (e >> 4) * kDim + (e & 15) * 8) = vp[k];
@@ -156,7 +168,7 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
     __syncthreads();
     if (wave >= g) continue;  // no head of the group in this wave (uniform)
 
-    // ---- scores: lane t against token t (rows past cnt are zero) ----
+    // ---- scores: lane t against token t (only lanes t < cnt count) ----
     double acc[kHpw][2];
 #pragma unroll
     for (int hh = 0; hh < kHpw; ++hh) acc[hh][0] = acc[hh][1] = 0.0;
