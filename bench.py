@@ -458,8 +458,8 @@ def main():
         progressive_main(args)
         return
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not "
-              "supported. The multi-GPU sharding is a design note only." % (args.gpus, world),
+        print("bench.py: the benchmark runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not "
+              "supported (the library has no multi-GPU path)." % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
 

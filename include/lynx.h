@@ -57,7 +57,7 @@ extern "C" {
 #define LYNX_PAGE_TOKENS 256 /* tokens per page (section 3) */
 #define LYNX_CHUNK_TOKENS 32 /* C, tokens per chunk (section 3) */
 #define LYNX_CHUNKS_PER_PAGE 8
-#define LYNX_HEAD_DIM 128    /* the only head_dim this build supports */
+#define LYNX_HEAD_DIM 128    /* the only head_dim the library supports */
 #define LYNX_MAX_GROUP 16    /* largest supported Hq / H */
 #define LYNX_MAX_KV_HEADS 65535  /* largest H of an encoded tensor (a page of
                                     256 tokens stays below 4 GiB) */
