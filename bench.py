@@ -126,6 +126,11 @@ def summarize(kind, db_dir, out_path, command):
         exp_kib = COPY_PROBE_BYTES / 1024.0
         f_fetch = exp_kib / probe["FETCH_SIZE"]
         f_write = exp_kib / probe["WRITE_SIZE"]
+        # a copy of N bytes reads and writes N bytes: counters that miss it by
+        # more than 4x mean other large copies were taken for the probe
+        if not (0.25 <= f_fetch <= 4.0 and 0.25 <= f_write <= 4.0):
+            raise SystemExit("copy probe counters off by more than 4x (fetch scale %.3g, write "
+                             "scale %.3g): was another large copy in the run?" % (f_fetch, f_write))
         enc = [k for k in avg if k.startswith("encode_kv_kernel")]
         enc_fetch = sum(avg[k]["FETCH_SIZE"] for k in enc) / len(enc)
         enc_write = sum(avg[k]["WRITE_SIZE"] for k in enc) / len(enc)
