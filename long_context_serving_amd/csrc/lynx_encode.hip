@@ -406,18 +406,19 @@ void encode_kernel(const uint16_t *__restrict__ kv, int heads, PlanesArg out, En
   encode_tile<kRole, kBits>(sm, kv, heads, static_cast<int>(blockIdx.x), out, tab);
 }
 
-// K and V of one layer in one launch: blocks 0 .. n - 1 encode the K tiles,
-// blocks n .. 2n - 1 the V tiles, so that the second tensor's tiles start as
-// the first one's finish instead of after a launch boundary.
+// K and V of one layer in one launch: block 2t encodes K tile t and block
+// 2t + 1 V tile t, so that no launch boundary separates the two tensors and
+// blocks of the two roles (whose compute and store patterns differ) share
+// the chip throughout.
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void encode_kv_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int heads,
                       int ntiles, PlanesArg kout, PlanesArg vout, EncodeTables tab) {
   __shared__ EncodeSmem sm;
   const int t = static_cast<int>(blockIdx.x);
-  if (t < ntiles)
-    encode_tile<LYNX_ROLE_KEY, 4>(sm, k, heads, t, kout, tab);
+  if ((t & 1) == 0)
+    encode_tile<LYNX_ROLE_KEY, 4>(sm, k, heads, t >> 1, kout, tab);
   else
-    encode_tile<LYNX_ROLE_VALUE, 4>(sm, v, heads, t - ntiles, vout, tab);
+    encode_tile<LYNX_ROLE_VALUE, 4>(sm, v, heads, t >> 1, vout, tab);
 }
 
 // Exhaustive check of the encoder's level path (the bucket table) against
