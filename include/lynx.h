@@ -7,11 +7,11 @@
  * boundary"):
  *
  *   encode, per page of 256 tokens, per KV head h, per channel d:
- *     mn = min_t x, rg = up7(fl32(max_t x - mn)), inv_rg = fl32(1/rg) (0 if 0)
+ *     mn = min_t x, rg = fl32(max_t x - mn), inv_rg = fl32(1/rg) (0 if 0)
  *     x'_t = fl32(fl32(x_t - mn) * inv_rg)                    (map to [0,1])
  *     per chunk c of C = 32 tokens:
  *       mu = fl32(exact_sum(x'_t) / 32), d_t = fl32(x'_t - mu)
- *       s  = up7(max_t |d_t|),  inv_s = fl32(1/s) (0 if s = 0)
+ *       s  = max_t |d_t|,  inv_s = fl32(1/s) (0 if s = 0)
  *       u_t = min(1, fl32(|d_t| * inv_s))                     (y = sign(d) u)
  *     m_t = round_half_up(127 * ln(1 + 255 u_t) / ln 256)      (0..127)
  *     q_t = d_t < 0 ? -m_t - 1 : m_t                           (int8, sign-aware)
@@ -27,10 +27,14 @@
  *   The compact planes are expanded only in registers.
  *
  * fl32() is one IEEE binary32 operation rounded to nearest even (no fused
- * multiply-add); the chunk sum is exact; up7() keeps 7 significant bits,
- * rounding up (so normalised values stay inside [0,1] and [-1,1] and the
- * product q * rg * s of a bf16 query with two scales fits in 22 bits).
- * alpha = 255, 127 levels, C = 32, 7-bit scales and the +7 draft point are
+ * multiply-add).  exact_sum() is the exact sum, which the encoder forms in
+ * binary64: that sum is exact whenever every nonzero x'_t of the chunk is at
+ * least 2^-24 (the 32 terms then span at most 53 bits), so the scales and
+ * codes are bit-exact under that condition.  A chunk that breaks it (a
+ * value above the page minimum by less than 2^-24 of the page range) may
+ * see its sum rounded once more: its mean is then
+ * within one ulp of the exact one and its codes within one level.
+ * alpha = 255, 127 levels, C = 32, fp32 scales and the +7 draft point are
  * the readings documented with the repository.
  *
  * Conventions for every entry point:

@@ -14,10 +14,10 @@
 //   score_tj = sum_d (sm*q_jd*c1_cd) yhat_td + sum_d sm*q_jd*c0_cd
 //            = dot(q'_cj, yhat_t) + bias_cj
 //   and o_jd = sum_c [c1v_cd * sum_{t in c} p_tj yhat_td + c0v_cd * sum_{t in c} p_tj].
-// q' = q * rg * s is exact in fp32 (the encoder keeps rg and s with 7
-// significant bits), the dot product runs in fp64, and the bias and the
-// softmax scale are applied in fp64, so no score is rounded to fp32 at its
-// full magnitude (with 100x outlier channels scores reach a few hundred).
+// q' = q * rg * s is formed in fp64 (bf16 q times the fp32 scales), the dot
+// product with the fp32 yhat runs in fp64, and the bias and the softmax
+// scale are applied in fp64, so no score is rounded to fp32 at its full
+// magnitude (with 100x outlier channels scores reach a few hundred).
 //
 // Split-K: each workgroup reduces a contiguous run of pages of one (request,
 // KV head) to (m, l, o) partials; a combine kernel merges them exactly.
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
   p1 = p1 > npages ? npages : p1;
 
   __shared__ double s_q[kMaxG][kDim];     // q (exact bf16 values)
-  __shared__ float s_qp[kMaxG][kDim];     // q' = q * c1 (per chunk; exact in fp32)
+  __shared__ double s_qp[kMaxG][kDim];    // q' = q * c1 (per chunk, fp64)
   __shared__ double s_c0k[kDim], s_c1k[kDim];
   __shared__ double s_c0v[kDim], s_c1v[kDim];
   __shared__ double s_bias[kMaxG];
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
 
   const size_t T = static_cast<size_t>(s.max_pages) * kPage;
   for (int lp = p0; lp < p1; ++lp) {
-    const int pg = block_table ? block_table[static_cast<size_t>(req) * s.max_pages + lp]
-                               : b * s.max_pages + lp;
+    const long long pg = block_table ? block_table[static_cast<size_t>(req) * s.max_pages + lp]
+                                     : static_cast<long long>(req) * s.max_pages + lp;
     if (pg < 0 || pg >= s.pool_pages) continue;  // invalid entry: page skipped
     const size_t tile = static_cast<size_t>(pg) * s.heads + h;
     for (int c = 0; c < kChunks; ++c) {
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
       __syncthreads();
       for (int e = tid; e < g * kDim; e += kAttnThreads) {
         const int j = e / kDim, d = e % kDim;
-        s_qp[j][d] = static_cast<float>(s_q[j][d] * s_c1k[d]);
+        s_qp[j][d] = s_q[j][d] * s_c1k[d];
       }
       {
         const int j = tid >> 4, part = tid & 15;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
           double dot = 0.0;
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            dot = fma(static_cast<double>(s_qp[j][cg * 16 + i]), static_cast<double>(y[i]), dot);
+            dot = fma(s_qp[j][cg * 16 + i], static_cast<double>(y[i]), dot);
           dot += __shfl_xor(dot, 1);
           dot += __shfl_xor(dot, 2);
           dot += __shfl_xor(dot, 4);

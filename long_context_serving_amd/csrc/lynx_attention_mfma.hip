@@ -15,10 +15,10 @@
 // two operand halves as is: k = 2*element + {0: hi, 1: lo}.  The other
 // operand repeats each value in both slots, so the product sums
 // (hi + lo) * x.  The 16 columns are [hi part of the 8 query heads | lo
-// part of the 8 query heads]: q' = q * rg * s of a bf16 query has at most
-// 22 bits, and after a power-of-two scale that keeps it inside the fp16
-// range it is split exactly into a truncated fp16 high part and the fp16
-// remainder (likewise the probabilities).  Scores are assembled in fp64
+// part of the 8 query heads]: q' = q * rg * s (fp32), after a power-of-two
+// scale that keeps it inside the fp16 range, is split into a truncated fp16
+// high part (11 bits) and the fp16 remainder (the next 11 bits; likewise the
+// probabilities).  Scores are assembled in fp64
 // from the two column halves, the fp64 chunk bias sum_d q_d c0_d and the
 // softmax scale, and only the small difference to the running maximum is
 // rounded before exp2, because with 100x outlier channels scores reach a
@@ -257,7 +257,7 @@ __device__ __forceinline__ void load_scales(Scales &sc, const PlanesArg &kp, con
 // 2^(14 - e), e = exponent of qmax * max c1k (qmax = largest |q| of the
 // group), so every |q * c1k| stays below 2^15; returns its exact inverse.
 __device__ __forceinline__ double scale_stage(const Scales &sc, char *slot, int lane, float qmax) {
-  const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // exact (7 + 7 bits)
+  const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // fp32
   const float bound = qmax * wave_max(fmaxf(c1a, c1b));
   float ks = 1.0f;
   double inv_ks = 1.0;

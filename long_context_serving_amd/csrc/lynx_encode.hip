@@ -19,8 +19,9 @@
 // Numeric contract (shared with the C ABI header): the statistics are fp32
 // IEEE operations without contraction (this file is built with
 // -ffp-contract=off), reciprocals are correctly rounded, the chunk sum is
-// exact in fp64, the page range and chunk max-abs keep 7 significant bits
-// (rounded up), and the level m is exactly #{k >= 1 : u >= T[k]}.
+// exact in fp64 (whenever every nonzero normalised value of the chunk is at
+// least 2^-24, see the header), the page range and chunk max-abs are the
+// plain fp32 values, and the level m is exactly #{k >= 1 : u >= T[k]}.
 #include "lynx_cut.h"
 #include "lynx_internal.h"
 
@@ -131,13 +132,6 @@ __device__ __forceinline__ uint32_t anchor_word(uint32_t we, uint32_t wo) {
 }
 __device__ __forceinline__ uint32_t residual_word(uint32_t we, uint32_t wo) {
   return (we & 0x0F0F0F0Fu) | ((wo << 4) & 0xF0F0F0F0u);
-}
-
-// Keep 7 significant bits, rounding towards +infinity (x >= 0, finite).
-__device__ __forceinline__ float round_up_7bits(float x) {
-  uint32_t b = __float_as_uint(x);
-  if (b & 0x1FFFFu) b = (b + 0x1FFFFu) & ~0x1FFFFu;
-  return __uint_as_float(b);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -261,9 +255,7 @@ __device__ __forceinline__ void encode_tile(EncodeSmem &sm, const uint16_t *__re
         a = fminf(a, s_min[cc][d]);
         b = fmaxf(b, s_max[cc][d]);
       }
-      // the range is kept with 7 significant bits (rounded up), which makes
-      // every scale product exact in the decoder's fp16 operand halves
-      const float rg = round_up_7bits(b - a);
+      const float rg = b - a;  // fp32
       // correctly rounded fp32 reciprocal (fp64 quotient, one rounding)
       const float inv = rg > 0.0f ? static_cast<float>(1.0 / static_cast<double>(rg)) : 0.0f;
       s_mn[d] = a;
@@ -307,7 +299,6 @@ __device__ __forceinline__ void encode_tile(EncodeSmem &sm, const uint16_t *__re
                       fmaxf(fmaxf(fabsf(x[4][i]), fabsf(x[5][i])),
                             fmaxf(fabsf(x[6][i]), fabsf(x[7][i]))));
       sabs[i] = xreduce_f32(sabs[i], MaxOp());
-      sabs[i] = round_up_7bits(sabs[i]);
     }
     if (r == 0) {
       const size_t cidx = (static_cast<size_t>(tile) * kChunks + c) * kDim + cg * 8;

@@ -157,7 +157,7 @@ __device__ __forceinline__ void load_kscale(KScale &ks, const PlanesArg &kp, siz
 // e the exponent of the largest c1k, keeps every K' below 2^15.
 __device__ __forceinline__ void stage_slot(const KScale &k, char *slot, int w, int lane,
                                            double inv_qs) {
-  const float c1a = k.rgk.x * k.sk.x, c1b = k.rgk.y * k.sk.y;  // exact (7 + 7 bits)
+  const float c1a = k.rgk.x * k.sk.x, c1b = k.rgk.y * k.sk.y;  // fp32
   const float top = wave_max(fmaxf(c1a, c1b));
   float ks = 1.0f;
   double inv_ks = 1.0;

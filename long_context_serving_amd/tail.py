@@ -78,6 +78,11 @@ class TailCache:
         """Encode the full pages at the front of request r's tail; returns
         the number of pages written."""
         written = 0
+        cur = torch.cuda.current_stream()
+        side = stream is not None and stream != cur
+        if side and self._tail[r] >= lynx.PAGE:
+            # the tail rows were written by append() on the current stream
+            stream.wait_stream(cur)
         while self._tail[r] >= lynx.PAGE:
             if not self._free:
                 raise RuntimeError("page pool exhausted")
@@ -100,6 +105,10 @@ class TailCache:
             self._tail[r] -= lynx.PAGE
             self._pages[r].append(p)
             written += 1
+        if side and written:
+            # tail lengths, page counts and every later attention call run on
+            # the current stream: they follow the shift and the table write
+            cur.wait_stream(stream)
         self._publish(r)
         return written
 

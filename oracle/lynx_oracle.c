@@ -31,9 +31,8 @@
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
- *   the page range and the chunk max-abs are kept with 7 significant bits,
- *   rounded up (so normalised values stay inside [0,1] and [-1,1]); the
- *   scales are stored as fp32 values carrying those 7 bits;
+ *   the scales are plain fp32 values: the page range is the fp32 difference
+ *   max - min, the chunk max-abs the largest |x' - mean| of the chunk;
  *   alpha = 255 (mu-law constant); F(u) = ln(1+alpha u)/ln(1+alpha);
  *   magnitude m = floor(127 F(|y|) + 1/2) in 0..127;
  *   code q = m for y >= 0, q = -m-1 (= ~m) for y < 0;
@@ -44,7 +43,8 @@
  * Numeric contract for the statistics (so that codes are reproducible
  * bit for bit): every step below marked "fp32" is one IEEE single-precision
  * operation rounded to nearest even, with no fused multiply-add (this file
- * is compiled with -ffp-contract=off), and the chunk sum is exact.
+ * is compiled with -ffp-contract=off), and the chunk mean is the exact sum
+ * of the chunk's 32 normalised values divided by 32, rounded once to fp32.
  * Everything else is evaluated in double precision.
  */
 #include <math.h>
@@ -63,7 +63,7 @@
 
 /* Flag bits written per element by oracle_encode. */
 #define OR_FLAG_NEAR_HALF 1u   /* 127 F(u) within 2^-20 of a half-level  */
-#define OR_FLAG_SUM_INEXACT 2u /* chunk sum exactness precondition broken */
+#define OR_FLAG_SUM_INEXACT 2u /* a nonzero x' below 2^-24 in the chunk */
 
 static float bf16_to_float(uint16_t h)
 {
@@ -107,15 +107,62 @@ static double yhat_of(int q)
     return q >= 0 ? g : -g;
 }
 
-/* Round a non-negative finite float up to 7 significant bits (clear the low
- * 17 of the 23 stored mantissa bits, rounding towards +infinity). */
-static float round_up_7bits(float x)
+/* Exact sum of non-negative finite fp32 values, held as a 192-bit integer
+ * in units of 2^-149 (the smallest fp32 denormal): a value below 2 is at
+ * most 2^150 units, so 32 of them stay below 2^155. */
+typedef struct {
+    uint64_t w[3];
+} exact_sum;
+
+static void exact_sum_add(exact_sum *a, float f)
 {
     uint32_t b;
-    memcpy(&b, &x, sizeof b);
-    if ((b & 0x1FFFFu) != 0u) b = (b + 0x1FFFFu) & ~0x1FFFFu;
-    memcpy(&x, &b, sizeof x);
-    return x;
+    memcpy(&b, &f, sizeof b);
+    const uint32_t e = b >> 23;                    /* sign bit is 0 */
+    uint64_t m = b & 0x7FFFFFu;
+    int shift = 0;
+    if (e != 0) {                                  /* normal: (2^23 + m) 2^(e-150) */
+        m |= 0x800000u;
+        shift = (int)e - 1;
+    }
+    /* add m << shift (m < 2^24, shift <= 127) */
+    const int word = shift / 64, off = shift % 64;
+    uint64_t add[3] = {0, 0, 0};
+    add[word] = m << off;
+    if (off > 40 && word < 2) add[word + 1] = m >> (64 - off);
+    uint64_t carry = 0;
+    for (int i = 0; i < 3; ++i) {
+        const uint64_t t = a->w[i] + carry;
+        const uint64_t c1 = t < carry;
+        const uint64_t r = t + add[i];
+        carry = c1 + (r < t);
+        a->w[i] = r;
+    }
+}
+
+/* bit i of the 192-bit integer */
+static int exact_sum_bit(const exact_sum *a, int i)
+{
+    return (int)((a->w[i / 64] >> (i % 64)) & 1u);
+}
+
+/* fp32 value of sum * 2^-149 / 32, rounded once to nearest even. */
+static float exact_sum_mean32(const exact_sum *a)
+{
+    int top = -1;
+    for (int i = 191; i >= 0; --i)
+        if (exact_sum_bit(a, i)) { top = i; break; }
+    if (top < 0) return 0.0f;
+    /* the value is sum * 2^-154; keep 24 significant bits, or the
+     * denormal quantum 2^-149 (= 2^5 units of the sum) below 2^-126 */
+    const int drop = top - 23 > 5 ? top - 23 : 5;
+    uint64_t kept = 0;
+    for (int i = top; i >= drop; --i) kept = (kept << 1) | (uint64_t)exact_sum_bit(a, i);
+    const int half = exact_sum_bit(a, drop - 1);
+    int sticky = 0;
+    for (int i = drop - 2; i >= 0; --i) sticky |= exact_sum_bit(a, i);
+    if (half && (sticky || (kept & 1u))) ++kept;   /* round half to even */
+    return (float)ldexp((double)kept, drop - 154);  /* exact: kept <= 2^24 */
 }
 
 static int nthreads_or_default(int32_t n)
@@ -162,7 +209,7 @@ static void encode_channel(const uint16_t *x, int64_t p, int32_t h, int32_t d,
         if (v[t] < mn) mn = v[t];
         if (v[t] > mx) mx = v[t];
     }
-    float rg = round_up_7bits(mx - mn);          /* fp32 difference, then 7 bits */
+    float rg = mx - mn;                          /* fp32 */
     float inv_rg = rg > 0.0f ? 1.0f / rg : 0.0f; /* fp32, correctly rounded */
     for (int t = 0; t < OR_PAGE; ++t) {
         float diff = v[t] - mn;                  /* fp32 */
@@ -175,19 +222,15 @@ static void encode_channel(const uint16_t *x, int64_t p, int32_t h, int32_t d,
     /* Chunk-wise outlier isolation, C = 32 consecutive tokens. */
     for (int c = 0; c < OR_NCHUNK; ++c) {
         const int t0 = c * OR_CHUNK;
+        /* a nonzero term below 2^-24 is flagged: a double-precision sum of
+         * such a chunk need not be exact (its terms span more than 53 bits) */
         int inexact = 0;
-        double sum = 0.0;
+        exact_sum sum = {{0, 0, 0}};
         for (int t = t0; t < t0 + OR_CHUNK; ++t) {
-            /* every nonzero term >= 2^-24 keeps the double sum exact */
             if (xn[t] != 0.0f && xn[t] < 0x1p-24f) inexact = 1;
-            sum += (double)xn[t];
+            exact_sum_add(&sum, xn[t]);
         }
-        if (inexact) {
-            long double s2 = 0.0L;
-            for (int t = t0; t < t0 + OR_CHUNK; ++t) s2 += (long double)xn[t];
-            sum = (double)s2;
-        }
-        float mu = (float)(sum / (double)OR_CHUNK); /* one rounding */
+        float mu = exact_sum_mean32(&sum);         /* one rounding */
         float dv[OR_CHUNK];
         float s = 0.0f;
         for (int i = 0; i < OR_CHUNK; ++i) {
@@ -195,7 +238,6 @@ static void encode_channel(const uint16_t *x, int64_t p, int32_t h, int32_t d,
             float a = fabsf(dv[i]);
             if (a > s) s = a;
         }
-        s = round_up_7bits(s);
         float inv_s = s > 0.0f ? 1.0f / s : 0.0f;  /* fp32, correctly rounded */
         const int64_t cidx = (((p * H + h) * OR_NCHUNK + c) * (int64_t)D) + d;
         chunk_mean[cidx] = mu;

@@ -41,16 +41,6 @@ def _inv(v, alpha=ALPHA):
     return ((1.0 + alpha) ** v - 1.0) / alpha
 
 
-def _round_up_7(x):
-    """Keep 7 significant bits, rounding up (x >= 0)."""
-    out = np.zeros_like(x)
-    nz = x > 0
-    e = np.floor(np.log2(x[nz]))
-    step = 2.0 ** (e - 6)
-    out[nz] = np.ceil(x[nz] / step) * step
-    return out
-
-
 def lynx_reconstruct(x: np.ndarray, chunk: int = 32, page_norm: bool = True, log_map: bool = True,
                      sign_aware: bool = True, midpoint: bool = True, anchor_only: bool = False,
                      alpha: float = ALPHA, anchor_bits: int = 4):
@@ -68,14 +58,14 @@ def lynx_reconstruct(x: np.ndarray, chunk: int = 32, page_norm: bool = True, log
         return out, bits
     if page_norm:
         mn = x.min(axis=1, keepdims=True)
-        rg = _round_up_7(x.max(axis=1, keepdims=True) - mn)
+        rg = x.max(axis=1, keepdims=True) - mn
         xn = np.where(rg > 0, (x - mn) / np.where(rg > 0, rg, 1.0), 0.0)
     else:
         xn = x
     xc = xn.reshape(P, T // chunk, chunk, H, D)
     mu = xc.mean(axis=2, keepdims=True)
     d = xc - mu
-    s = _round_up_7(np.abs(d).max(axis=2, keepdims=True))
+    s = np.abs(d).max(axis=2, keepdims=True)
     y = np.clip(np.where(s > 0, d / np.where(s > 0, s, 1.0), 0.0), -1.0, 1.0)
     mag = np.abs(y)
     m = np.floor(127.0 * (_map(mag, alpha) if log_map else mag) + 0.5).astype(np.int64)

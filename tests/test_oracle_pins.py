@@ -4,6 +4,7 @@ Each test names the passage it pins.  Page references are to
 "Lynx: the KV cache does not have to arrive whole" (sections 1-3) unless
 stated.  None of these tests runs the HIP path.
 """
+import functools
 import json
 import math
 import os
@@ -114,10 +115,12 @@ def test_code_map_exhaustive_monotone_and_thresholds():
     block = 1 << 24
     prev_last = -1
     first_u = {}
+    flagged = 0
     for start in range(0, top + 1, block):
         bits = np.arange(start, min(start + block, top + 1), dtype=np.uint32)
         u = bits.view(np.float32)
         q, flag = oracle.codes(u)
+        flagged += int(flag.sum())
         qi = q.astype(np.int16)
         assert qi[0] >= prev_last
         assert np.all(np.diff(qi) >= 0)
@@ -128,10 +131,81 @@ def test_code_map_exhaustive_monotone_and_thresholds():
             first_u[int(qi[i])] = (float(u[i - 1]), float(u[i]), int(flag[i]) | int(flag[i - 1]))
     assert prev_last == 127
     assert sorted(first_u) == list(range(1, 128))
+    # every flagged u of [0, 1] lies in the windows around the 127 boundaries
+    assert flagged == near_half_flag_count()
     for k, (below, at, flagged) in first_u.items():
         t = G((k - 0.5) / 127.0)
         if not flagged:
             assert below < t <= at or math.isclose(at, t, rel_tol=1e-6), (k, below, at, t)
+
+
+# ---------------------------------------------------------------------------
+# The near-half flag: set exactly where tau = 127 F(u) lies within 2^-20 of
+# a rounding boundary k + 1/2 (the window in which the spec bar lets a
+# code differ by one), with tau evaluated here in 40-digit decimal
+# arithmetic, independently of the oracle's double-precision log1p.
+# ---------------------------------------------------------------------------
+_WINDOW = 64        # fp32 steps scanned on each side of every boundary
+
+
+def _tau_decimal(u):
+    from decimal import Decimal, getcontext
+    getcontext().prec = 40
+    return 127 * (1 + 255 * Decimal(float(u))).ln() / Decimal(256).ln()
+
+
+@functools.lru_cache(maxsize=1)
+def _near_half_windows():
+    """Per boundary k + 1/2 (k = 0..126): the fp32 bit patterns of u within
+    _WINDOW steps of the first u with tau >= k + 1/2, and whether each lies
+    within 2^-20 of the boundary (None where that is closer to 1e-12 than
+    decimal vs double evaluation can decide)."""
+    from decimal import Decimal
+    band = Decimal(2) ** -20
+    out = []
+    for k in range(127):
+        half = Decimal(k) + Decimal(1) / 2
+        lo, hi = 0, 0x3F800000                       # tau(0) < half <= tau(1)
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if _tau_decimal(np.uint32(mid).view(np.float32)) >= half:
+                hi = mid
+            else:
+                lo = mid
+        bits = np.arange(hi - _WINDOW, hi + _WINDOW + 1, dtype=np.uint32)
+        want = []
+        for b in bits:
+            dist = abs(_tau_decimal(b.view(np.float32)) - half)
+            want.append(None if abs(dist - band) < Decimal("1e-12") else dist < band)
+        out.append((k, bits, want))
+    return out
+
+
+def test_near_half_flag_is_set_exactly_within_two_to_minus_20_of_a_boundary():
+    total = 0
+    for k, bits, want in _near_half_windows():
+        _, flag = oracle.codes(bits.view(np.float32))
+        assert not flag[0] and not flag[-1], k          # the band lies inside the window
+        for f, w in zip(flag, want):
+            if w is not None:
+                assert bool(f) == w, (k, f, w)
+        total += int(flag.sum())
+    assert total > 0
+    # away from the boundaries the flag is never set
+    rng = np.random.default_rng(11)
+    u = rng.random(200000).astype(np.float32)
+    tau = oracle.tau(u)
+    _, flag = oracle.codes(u)
+    far = np.abs(tau - np.floor(tau) - 0.5) > 2.0 ** -19
+    assert not flag[far].any()
+
+
+def near_half_flag_count():
+    """Number of fp32 u in [0, 1] the windows above flag."""
+    total = 0
+    for _, bits, _ in _near_half_windows():
+        total += int(oracle.codes(bits.view(np.float32))[1].sum())
+    return total
 
 
 def test_yhat_monotone_and_closed_form():
@@ -273,30 +347,42 @@ def test_maxabs_element_and_degenerate_channels():
     assert np.all(enc["codes"][0, 64:96, 1, 5] == 0)
     want = float(enc["page_min"][0, 1, 5]) + float(enc["page_range"][0, 1, 5]) * float(enc["chunk_mean"][0, 1, 2, 5])
     assert np.all(full[0, 64:96, 1, 5] == want)
-    # the element of largest deviation in every chunk lands on level 127
+    # every element whose deviation equals the chunk max-abs has |y| = 1 up
+    # to the rounding of |d| / s (at most one ulp below 1), so lands on
+    # level 127 (the closed form |y| = 1 -> 127 -> yhat = +-1)
     q = enc["codes"].astype(np.int32)
     m = np.where(q >= 0, q, -q - 1)
+    xn, _ = _fp32_chain(x)
     for c in range(8):
-        blkm = m[0, 32 * c:32 * c + 32]
         for h in range(2):
             for d in range(8):
-                if enc["chunk_maxabs"][0, h, c, d] > 0:
-                    assert blkm[:, h, d].max() == 127
+                s = enc["chunk_maxabs"][0, h, c, d]
+                if s > 0:
+                    dev = np.abs((xn[0, 32 * c:32 * c + 32, h, d] -
+                                  enc["chunk_mean"][0, h, c, d]).astype(np.float32))
+                    top = dev == s
+                    assert top.any()
+                    assert np.all(m[0, 32 * c:32 * c + 32, h, d][top] == 127)
+                    y = (dev[top] * np.float32(1.0 / np.float64(s))).astype(np.float32)
+                    assert np.all(y >= np.float32(1.0) - np.float32(2.0 ** -23))
 
 
 def test_ramp_pages_closed_form_codes():
-    """Exact ramps x_t = t * 2^k (or reversed) give mean and max-abs in closed
-    form, so codes are known per token: m = round(127 F(|2(t - 32c) - 31| / 31)).
-    Different heads/channels carry different ramps, pinning the oracle's page,
-    chunk, head and channel indexing."""
+    """Exact ramps give page and chunk statistics in closed form, so codes
+    are known per token: m = round(127 F(|2(t - 32c) - 31| / 31)).  The ramp
+    counts 0..255 with a step skipped after 127 (values t + [t >= 128], times
+    2^k, or reversed), so the page range is 256 * 2^k and x' = value / 256
+    exactly.  Different heads/channels carry different ramps, pinning the
+    oracle's page, chunk, head and channel indexing."""
     H, D = 3, 8
     x = np.empty((2, 256, H, D), np.float32)
     t = np.arange(256, dtype=np.float32)
+    tp = t + (t >= 128)                       # 0 .. 127, 129 .. 256
     for p in range(2):
         for h in range(H):
             for d in range(D):
                 k = (d + 2 * h + p) % 6 - 2
-                ramp = t if (d + h + p) % 2 == 0 else 255.0 - t
+                ramp = tp if (d + h + p) % 2 == 0 else 256.0 - tp
                 x[p, :, h, d] = ramp * np.float32(2.0 ** k) - np.float32(2.0 ** (k + 5)) * h
     xb = synth.float_to_bf16_bits(x)
     assert np.array_equal(oracle.bf16_bits_to_float(xb), x)   # exactly representable
@@ -306,6 +392,8 @@ def test_ramp_pages_closed_form_codes():
     tau = 127.0 * np.log1p(ALPHA * u) / np.log1p(ALPHA)
     want_m = np.floor(tau + 0.5).astype(np.int32)
     safe = np.abs(tau - np.floor(tau) - 0.5) > 1e-3
+    c = np.arange(8)
+    up_mu = (32 * c + 15.5 + (c >= 4)) / 256.0
     for p in range(2):
         for h in range(H):
             for d in range(D):
@@ -315,32 +403,80 @@ def test_ramp_pages_closed_form_codes():
                 got = enc["codes"][p, :, h, d].astype(np.int32)
                 assert np.array_equal(got[safe], want[safe]), (p, h, d)
                 k = (d + 2 * h + p) % 6 - 2
-                # span 255 * 2^k kept with 7 significant bits, rounded up: 256 * 2^k,
-                # so x' = t / 256 exactly and the chunk statistics are exact
                 assert enc["page_range"][p, h, d] == np.float32(256.0 * 2.0 ** k)
-                want_mu = (32 * np.arange(8) + 15.5) / 256.0 if not rev else (255 - 32 * np.arange(8) - 15.5) / 256.0
+                want_mu = up_mu if not rev else 1.0 - up_mu
                 assert np.array_equal(enc["chunk_mean"][p, h, :, d], want_mu.astype(np.float32))
                 assert np.all(enc["chunk_maxabs"][p, h, :, d] == np.float32(15.5 / 256.0))
 
 
-def test_scales_carry_seven_significant_bits_rounded_up():
-    """Reading: the page range and chunk max-abs are kept with 7 significant
-    bits, rounded up, so they never undercut the true span / deviation and
-    exceed it by less than 2^-6 relative."""
-    x = synth.laplace_pages(4, 3, 32, seed=52, scale_channels=((1, 4, 100.0),))
+def _fp32_chain(x_bits):
+    """x' = RN32(RN32(x - min) * RN32(1/range)) per page and channel, with
+    numpy's IEEE float32 operations: ([P][256][H][D], range [P][H][D])."""
+    xf = oracle.bf16_bits_to_float(x_bits)
+    mn = xf.min(axis=1, keepdims=True)
+    rg = (xf.max(axis=1, keepdims=True) - mn).astype(np.float32)
+    inv = np.where(rg > 0, (1.0 / rg.astype(np.float64)).astype(np.float32), np.float32(0.0))
+    return ((xf - mn).astype(np.float32) * inv).astype(np.float32), rg[:, 0]
+
+
+def _rn32(fr):
+    """Round an exact rational to the nearest fp32 (ties to even)."""
+    from fractions import Fraction
+    f = np.float32(float(fr))             # within one ulp of the answer
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+
+    def key(c):
+        return (abs(Fraction(float(c)) - fr), int(np.float32(c).view(np.uint32)) & 1)
+    return min(cands, key=key)
+
+
+def test_scales_are_plain_fp32_range_mean_and_maxabs():
+    """Section 3: the page range is the page's max minus min (one fp32
+    subtraction), the chunk mean the exact mean of the chunk's 32
+    normalised values rounded once to fp32 (exact rational arithmetic here),
+    and the chunk max-abs the largest |x' - mean| -- no extra rounding of
+    any scale."""
+    from fractions import Fraction
+    x = synth.laplace_pages(2, 2, 16, seed=52, scale_channels=((1, 4, 100.0),))
     enc = oracle.encode(x)
-    xf = oracle.bf16_bits_to_float(x).astype(np.float64)
-    for name in ("page_range", "chunk_maxabs"):
-        v = enc[name]
-        assert np.all((v.view(np.uint32) & 0x1FFFF) == 0), name
-    span = xf.max(axis=1) - xf.min(axis=1)                       # [P][H][D]
-    rg = enc["page_range"].astype(np.float64)
-    assert np.all(rg >= span * (1 - 2.0 ** -24)) and np.all(rg < span * (1 + 2.0 ** -6) + 1e-30)
-    pm, pr, cm, cs = _stats_per_element(enc, 256)
-    xn = (xf - pm) / pr
-    dev = np.abs(xn - cm).reshape(4, 8, 32, 3, 32).max(axis=2)  # [P][c][H][D]
-    s = np.transpose(enc["chunk_maxabs"], (0, 2, 1, 3)).astype(np.float64)
-    assert np.all(s >= dev * (1 - 2.0 ** -20)) and np.all(s <= dev * (1 + 2.0 ** -6) + 1e-12)
+    xn, rg = _fp32_chain(x)
+    assert np.array_equal(enc["page_range"].view(np.uint32), rg.view(np.uint32))
+    P, _, H, D = x.shape
+    for p in range(P):
+        for h in range(H):
+            for c in range(8):
+                for d in range(D):
+                    vals = xn[p, 32 * c:32 * c + 32, h, d]
+                    mu = _rn32(sum(Fraction(float(v)) for v in vals) / 32)
+                    assert enc["chunk_mean"][p, h, c, d] == mu, (p, h, c, d)
+                    s = np.abs((vals - mu).astype(np.float32)).max()
+                    assert enc["chunk_maxabs"][p, h, c, d] == s, (p, h, c, d)
+
+
+def test_chunk_mean_is_exact_when_a_double_sum_would_round():
+    """Values far below the page range (nonzero x' under 2^-24) next to a
+    large one: a plain double-precision sum of such a chunk can round; the
+    oracle's mean is still the exactly rounded one, and exactly those chunks
+    are flagged."""
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    xf = np.zeros((1, 256, 1, 8), np.float32)
+    for d in range(8):
+        base = np.float32(-(2.0 ** -(20 + d)))
+        xf[0, :, 0, d] = base * (1 + rng.integers(0, 128, 256) / np.float32(128.0))
+        xf[0, 200, 0, d] = np.float32(96.0 * (d + 1))       # sets the range
+    xb = synth.float_to_bf16_bits(xf)
+    enc = oracle.encode(xb)
+    xn, _ = _fp32_chain(xb)
+    tiny = (xn != 0) & (xn < 2.0 ** -24)
+    assert tiny[0, :192].any()
+    for c in range(8):
+        for d in range(8):
+            vals = xn[0, 32 * c:32 * c + 32, 0, d]
+            assert enc["chunk_mean"][0, 0, c, d] == _rn32(sum(Fraction(float(v)) for v in vals) / 32)
+            chunk_tiny = tiny[0, 32 * c:32 * c + 32, 0, d].any()
+            flags = enc["flags"][0, 32 * c:32 * c + 32, 0, d]
+            assert np.all(((flags & oracle.FLAG_SUM_INEXACT) != 0) == chunk_tiny)
 
 
 # ---------------------------------------------------------------------------

@@ -66,12 +66,18 @@ def check_encode(lynx, x_bits, role, enc=None, pl=None):
     assert not (enc["flags"] & oracle.FLAG_SUM_INEXACT).any(), "input breaks the exact-sum precondition"
     near = (enc["flags"] & oracle.FLAG_NEAR_HALF) != 0
     mism = code != ref
+    n_mism, n_near = int(mism.sum()), int(near.sum())
+    print("  codes: %d mismatches, %d elements flagged near a half-level" % (n_mism, n_near), flush=True)
     assert not (mism & ~near).any(), "unflagged code mismatches: %d" % int((mism & ~near).sum())
     assert (np.abs(code.astype(np.int16) - ref.astype(np.int16))[mism] <= 1).all()
+    # The bar allows +-1 on flagged elements; the kernel's level thresholds
+    # are the oracle's own rounding points (checked for every fp32 u on the
+    # host and on the device), so none is used.
+    assert n_mism == 0, "flagged code mismatches: %d" % n_mism
     for name in ("page_min", "page_range", "chunk_mean", "chunk_maxabs"):
         got = getattr(pl, name).cpu().numpy().reshape(enc[name].shape)
         assert np.array_equal(got.view(np.uint32), enc[name].view(np.uint32)), name
-    return pl, enc, (a, r, code), int(mism.sum())
+    return pl, enc, (a, r, code), n_mism
 
 
 def check_dequant(lynx, pl, enc, gpu_code, full):
@@ -106,11 +112,17 @@ def oracle_attention_for(enc_k, enc_v, q_bits, page_lists, full, want_logits=Fal
     return (np.stack(outs), logits) if want_logits else np.stack(outs)
 
 
-def check_attention(got, ref, label):
+def check_attention(got, ref, label, fp32_err=None):
+    """The attention bar.  fp32_err (plain Laplace queries, a one-hot
+    softmax over scores of a few hundred): the max-abs error of a plain fp32
+    evaluation of the same attention, which the bar then also admits."""
     err = np.abs(got - ref)
     bound = ATOL_ATTN + RTOL_ATTN * np.abs(ref)
-    print("%s: max abs err %.3g (max |out| %.1f), max err/bound %.3f" %
-          (label, err.max(), np.abs(ref).max(), (err / bound).max()), flush=True)
+    print("%s: max abs err %.3g (max |out| %.1f), max err/bound %.3f%s" %
+          (label, err.max(), np.abs(ref).max(), (err / bound).max(),
+           "" if fp32_err is None else ", plain fp32 evaluation %.3g" % fp32_err), flush=True)
+    if fp32_err is not None:
+        bound = np.maximum(bound, fp32_err)
     assert (err <= bound).all(), label
 
 
@@ -157,11 +169,13 @@ def test_tiny_encode_dequant_attention(lynx):
     for full in (False, True):
         check_dequant(lynx, pk, ek, ck[2], full)
         check_dequant(lynx, pv, ev, cv[2], full)
-    q = synth.queries(w)
-    for full in (False, True):
-        ref = oracle_attention_for(ek, ev, q, [list(range(w.pages))], full)
-        got = run_gpu_attention(lynx, q, pk, pv, w.pages, full)
-        check_attention(got, ref, "tiny full=%s" % full)
+    for aligned in (True, False):
+        q = synth.queries(w, key_aligned=aligned)
+        for full in (False, True):
+            ref = oracle_attention_for(ek, ev, q, [list(range(w.pages))], full)
+            got = run_gpu_attention(lynx, q, pk, pv, w.pages, full)
+            e32 = None if aligned else float(np.abs(fp32_attention(ek, ev, q, full) - ref).max())
+            check_attention(got, ref, "tiny full=%s aligned=%s" % (full, aligned), e32)
 
 
 def test_anchor_calls_never_need_the_residual(lynx):
@@ -207,18 +221,15 @@ def test_ctx32k_full_size(lynx, ctx32k):
         assert np.array_equal(sc.argmax(1)[clear], lg.argmax(1)[clear])
 
 
-def test_ctx32k_peaked_softmax_no_worse_than_fp32(lynx, ctx32k):
+def test_ctx32k_plain_laplace_queries(lynx, ctx32k):
     w = synth.WORKLOADS["ctx32k"]
     pk, ek, ck, pv, ev, cv = ctx32k
     q = synth.queries(w, key_aligned=False)
     for full in (False, True):
         ref = oracle_attention_for(ek, ev, q, [list(range(w.pages))], full)
         got = run_gpu_attention(lynx, q, pk, pv, w.pages, full)
-        e32 = np.abs(fp32_attention(ek, ev, q, full) - ref).max()
-        err = np.abs(got - ref).max()
-        print("ctx32k peaked full=%s: max abs err %.3g, plain fp32 evaluation %.3g" % (full, err, e32),
-              flush=True)
-        assert err <= max(ATOL_ATTN, e32)
+        e32 = float(np.abs(fp32_attention(ek, ev, q, full) - ref).max())
+        check_attention(got, ref, "ctx32k plain queries full=%s" % full, e32)
 
 
 # ---------------------------------------------------------------------------
@@ -244,15 +255,19 @@ def test_batched_64x16k_sampled(lynx):
     pk = lynx.quantize_pages(to_dev(pool_k[inv]), 0)
     pv = lynx.quantize_pages(to_dev(pool_v[inv]), 1)
     block_table = perm.reshape(w.batch, P).astype(np.int32)
-    q_all = synth.queries(w)
-    q = np.stack([q_all[b % 2] if b >= 2 else q_all[b] for b in range(w.batch)])
-    for full in (False, True):
-        got = run_gpu_attention(lynx, q, pk, pv, P, full, block_table=block_table)
-        for i, r in enumerate(sampled):
-            ref = oracle_attention_for(ek[i], ev[i], q[r:r + 1], [list(range(P))], full)
-            check_attention(got[r], ref[0], "batched request %d full=%s" % (r, full))
-        for b in range(2, w.batch):
-            assert np.array_equal(got[b], got[b % 2])
+    for aligned in (True, False):
+        q_all = synth.queries(w, key_aligned=aligned)
+        q = np.stack([q_all[b % 2] if b >= 2 else q_all[b] for b in range(w.batch)])
+        for full in (False, True):
+            got = run_gpu_attention(lynx, q, pk, pv, P, full, block_table=block_table)
+            for i, r in enumerate(sampled):
+                ref = oracle_attention_for(ek[i], ev[i], q[r:r + 1], [list(range(P))], full)
+                e32 = None if aligned else float(
+                    np.abs(fp32_attention(ek[i], ev[i], q[r:r + 1], full) - ref).max())
+                check_attention(got[r], ref[0], "batched request %d full=%s aligned=%s" %
+                                (r, full, aligned), e32)
+            for b in range(2, w.batch):
+                assert np.array_equal(got[b], got[b % 2])
 
 
 # ---------------------------------------------------------------------------
@@ -271,11 +286,13 @@ def test_qwen3_235b_layer_encode(lynx):
 def test_progressive_layer_attention(lynx):
     w = synth.WORKLOADS["progressive32x64k"]
     pk, ek, ck, pv, ev, cv = encode_pair(lynx, w, layer=5)
-    q = synth.queries(w, layer=5)
-    for full in (False, True):
-        ref = oracle_attention_for(ek, ev, q, [list(range(w.pages))], full)
-        got = run_gpu_attention(lynx, q, pk, pv, w.pages, full)
-        check_attention(got, ref, "progressive layer 5 full=%s" % full)
+    for aligned in (True, False):
+        q = synth.queries(w, layer=5, key_aligned=aligned)
+        for full in (False, True):
+            ref = oracle_attention_for(ek, ev, q, [list(range(w.pages))], full)
+            got = run_gpu_attention(lynx, q, pk, pv, w.pages, full)
+            e32 = None if aligned else float(np.abs(fp32_attention(ek, ev, q, full) - ref).max())
+            check_attention(got, ref, "progressive layer 5 full=%s aligned=%s" % (full, aligned), e32)
 
 
 # ---------------------------------------------------------------------------
@@ -293,6 +310,48 @@ def test_degenerate_channels_and_chunks(lynx):
         pl, enc, codes, _ = check_encode(lynx, x, role)
         check_dequant(lynx, pl, enc, codes[2], True)
         check_dequant(lynx, pl, enc, codes[2], False)
+
+
+def test_chunks_outside_the_exact_sum_precondition(lynx):
+    """A nonzero normalised value below 2^-24 next to a large page range:
+    the kernel's double-precision chunk sum may round there (the header's
+    contract), so its mean is within one ulp of the oracle's exactly rounded
+    one, codes within +-1 and the max-abs within the ulp that moves; every
+    other chunk and every page statistic stays bit-exact."""
+    rng = np.random.default_rng(3)
+    xf = np.zeros((2, 256, 2, 128), np.float32)
+    xf[:] = rng.laplace(0, 1, xf.shape).astype(np.float32)
+    for d in range(0, 128, 3):
+        base = np.float32(-(2.0 ** -(20 + d % 9)))
+        xf[0, :, 1, d] = base * (1 + rng.integers(0, 128, 256) / np.float32(128.0))
+        xf[0, 200, 1, d] = np.float32(96.0 * (d + 1))
+    x = synth.float_to_bf16_bits(xf)
+    enc = oracle.encode(x)
+    flagged_chunk = ((enc["flags"] & oracle.FLAG_SUM_INEXACT) != 0).reshape(2, 8, 32, 2, 128).any(axis=2)
+    assert flagged_chunk.any()
+    fc = np.transpose(flagged_chunk, (0, 2, 1, 3))                   # [P][H][8][D]
+    for role in (0, 1):
+        pl = lynx.quantize_pages(to_dev(x), role)
+        torch.cuda.synchronize()
+        _, _, code = gpu_codes(pl, 2, 2, role)
+        for name in ("page_min", "page_range"):
+            got = getattr(pl, name).cpu().numpy().reshape(enc[name].shape)
+            assert np.array_equal(got.view(np.uint32), enc[name].view(np.uint32)), name
+        mu = pl.chunk_mean.cpu().numpy().reshape(enc["chunk_mean"].shape)
+        sd = pl.chunk_maxabs.cpu().numpy().reshape(enc["chunk_maxabs"].shape)
+        assert np.array_equal(mu[~fc].view(np.uint32), enc["chunk_mean"][~fc].view(np.uint32))
+        assert np.array_equal(sd[~fc].view(np.uint32), enc["chunk_maxabs"][~fc].view(np.uint32))
+        ulp_mu = np.spacing(np.abs(enc["chunk_mean"][fc]))
+        assert np.all(np.abs(mu[fc] - enc["chunk_mean"][fc]) <= ulp_mu)
+        ulp_s = np.spacing(np.abs(enc["chunk_maxabs"][fc]))
+        assert np.all(np.abs(sd[fc] - enc["chunk_maxabs"][fc]) <= ulp_mu + 2 * ulp_s)
+        el = np.repeat(flagged_chunk, 32, axis=1).reshape(2, 256, 2, 128)
+        ref = enc["codes"]
+        assert np.array_equal(code[~el], ref[~el])
+        assert np.all(np.abs(code[el].astype(np.int16) - ref[el].astype(np.int16)) <= 1)
+        print("role %d: %d flagged chunks, %d chunk means differ by one ulp, %d codes by one" %
+              (role, int(fc.sum()), int((mu[fc] != enc["chunk_mean"][fc]).sum()),
+               int((code[el] != ref[el]).sum())), flush=True)
 
 
 def test_empty_inputs(lynx):

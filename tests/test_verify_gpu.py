@@ -65,8 +65,14 @@ def tails(B, H, seed):
     return x.reshape(B, 2 * 256, H, 128)[:, :TAIL].copy()
 
 
-def run_case(lynx, H, Hq, tq, page_lists, tail_len, P_pool, seed, full, max_pages=4):
+def run_case(lynx, H, Hq, tq, page_lists, tail_len, P_pool, seed, full, max_pages=4,
+             contiguous=False):
+    """contiguous: no block table; request b reads pool pages
+    b * max_pages .. b * max_pages + len(page_lists[b]) - 1."""
     B = len(page_lists)
+    if contiguous:
+        assert all(pl == list(range(b * max_pages, b * max_pages + len(pl)))
+                   for b, pl in enumerate(page_lists))
     pk, pv, deq = pool_and_oracle(lynx, P_pool, H, seed) if P_pool else (None, None, None)
     if P_pool == 0:
         pk = lynx.alloc_planes(1, H, lynx.ROLE_KEY)
@@ -84,7 +90,7 @@ def run_case(lynx, H, Hq, tq, page_lists, tail_len, P_pool, seed, full, max_page
           (H, Hq, tq, page_lists, tail_len, full), flush=True)
     got = lynx.verify_attention(to_dev(q), pk, pv, max_pages, to_dev(tk), to_dev(tv),
                                 torch.tensor(tail_len, dtype=torch.int32, device="cuda"), full=full,
-                                block_table=torch.from_numpy(bt).cuda(),
+                                block_table=None if contiguous else torch.from_numpy(bt).cuda(),
                                 page_tokens=torch.from_numpy(page_tokens).cuda(), sm_scale=SM)
     torch.cuda.synchronize()
     # a block-table entry outside the pool is skipped by the kernels
@@ -115,6 +121,15 @@ def test_verify_group8_absent_pages_and_a_partial_row_group(lynx, full):
 @pytest.mark.parametrize("full", [True, False])
 def test_verify_group16_valu_path(lynx, full):
     run_case(lynx, 2, 32, 7, [[3, 5], [1], [6, 0, 2]], [7, 100, 256], 7, 303, full)
+
+
+@pytest.mark.parametrize("Hq", [16, 32])
+def test_verify_without_block_table(lynx, Hq):
+    # no block table: request b owns pool pages b * max_pages ..; several
+    # query tokens per request, so every row must read its request's pages
+    # (group 8: matrix-core page kernel; group 16: the other kernel)
+    run_case(lynx, 2, Hq, 6, [[0, 1], [3], [6, 7, 8]], [6, 40, 100], 9, 606, True, max_pages=3,
+             contiguous=True)
 
 
 @pytest.mark.parametrize("H,Hq", [(4, 8), (2, 10)])
@@ -175,3 +190,32 @@ def test_append_commit_writes_the_pages_directly_encoded(lynx):
     cache.truncate(1, 5)
     assert cache.tail_tokens(1) == 47
     assert int(cache.tail_len[1].item()) == 47
+
+
+def test_commit_on_a_side_stream(lynx):
+    """Rows appended on the current stream, pages committed on a side
+    stream, attention on the current stream: the commit orders itself after
+    the appends and the attention after the commit."""
+    from long_context_serving_amd.tail import TailCache
+    H = 2
+    cache = TailCache(requests=1, heads=H, pool_pages=3, max_pages=3)
+    x = synth.laplace_pages(2, H, 128, seed=919, scale_channels=((0, 4, 50.0),))
+    y = synth.laplace_pages(2, H, 128, seed=920)
+    xk, xv = x.reshape(512, H, 128), y.reshape(512, H, 128)
+    side = torch.cuda.Stream()
+    cache.append(0, to_dev(xk[:300]), to_dev(xv[:300]))
+    assert cache.commit(0, stream=side) == 1
+    cache.append(0, to_dev(xk[300:306]), to_dev(xv[300:306]))
+    rng = np.random.default_rng(12)
+    q = synth.float_to_bf16_bits(rng.laplace(0, 1, (1, 6, 16, 128)).astype(np.float32))
+    out = cache.attention(to_dev(q), full=True, sm_scale=SM)
+    torch.cuda.synchronize()
+    enc_k, enc_v = oracle.encode(xk[:256][None]), oracle.encode(xv[:256][None])
+    ak, rk = oracle.split(enc_k["codes"])
+    av, rv = oracle.split(enc_v["codes"])
+    pk = oracle.dequant(ak, rk, enc_k).reshape(256, H, 128)
+    pv = oracle.dequant(av, rv, enc_v).reshape(256, H, 128)
+    tk = np.concatenate([xk[256:306], np.zeros((TAIL - 50, H, 128), np.uint16)])[None]
+    tv = np.concatenate([xv[256:306], np.zeros((TAIL - 50, H, 128), np.uint16)])[None]
+    ref = oracle.verify_attention(q, [pk], [pv], tk, tv, [50], SM)
+    check(out.cpu().numpy().astype(np.float64), ref, "commit on a side stream")
