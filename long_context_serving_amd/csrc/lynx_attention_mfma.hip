@@ -6,23 +6,32 @@
 // compact cache, expand it only in registers, attention unchanged).
 //
 // Algebra.  With khat = c0 + c1*yhat and vhat = c0v + c1v*yhat per chunk
-// and channel (c0 = mn + rg*mu, c1 = rg*s), a 32-token chunk needs two dense
-// products, both on v_mfma_f32_16x16x32_f16:
-//   S^T[16 tok][16 col]  = Yk[16 tok][k] * Q'[k][16 col]          (8 steps)
-//   O^T[16 ch ][16 col] += Yv^T[16 ch][k] * P[k][16 col]          (2 steps)
-// yhat is stored in a table as an fp16 pair (hi, lo) with 22 significant
-// bits, and the pair occupies two consecutive k slots, so one table word is
-// two operand halves as is: k = 2*element + {0: hi, 1: lo}.  The other
-// operand repeats each value in both slots, so the product sums
-// (hi + lo) * x.  The 16 columns are [hi part of the 8 query heads | lo
-// part of the 8 query heads]: q' = q * rg * s (fp32), after a power-of-two
-// scale that keeps it inside the fp16 range, is split into a truncated fp16
-// high part (11 bits) and the fp16 remainder (the next 11 bits; likewise the
-// probabilities).  Scores are assembled in fp64
-// from the two column halves, the fp64 chunk bias sum_d q_d c0_d and the
-// softmax scale, and only the small difference to the running maximum is
-// rounded before exp2, because with 100x outlier channels scores reach a
-// few hundred and the output is sensitive to one fp32 ulp of a score.
+// and channel (c0 = mn + rg*mu, c1 = rg*s), a score is
+//   sum_d q_d c0_d  +  sum_d (q_d c1_d) yhat_td
+// and a 32-token chunk needs two dense products:
+//   S^T[16 tok][16 col]  = Yk[16 tok][k] * W[k][16 col]   (v_mfma_i32_16x16x64_i8)
+//   O^T[16 ch ][16 col] += Yv^T[16 ch][k] * P[k][16 col]  (v_mfma_f32_16x16x32_f16)
+// Scores are exact integer products.  With 100x outlier channels a score
+// reaches a few hundred and the output moves with a few fp32 ulps of it, so
+// no part of a score is accumulated in fp32: yhat is held in fixed point,
+// Y = round(yhat 2^30), and w = q c1 (bf16 query times the fp64 scale
+// product) as W = floor(w 2^S), S per chunk so that |W| < 2^30.  Both are
+// split into 4 signed bytes (Y = sum_i Y_i 2^(8i), likewise W), a table word
+// holds the 4 bytes of one element's Y, so k = 4*element + i.  Column n of
+// the 16 holds query head n % 8 at level L (the byte products Y_i W_j with
+// i + j = L, weight 2^(8L)): its W operand for element d is the byte string
+// (W_L, W_(L-1), W_(L-2), W_(L-3)) of that element (0 outside 0..3), one
+// v_perm.  Three products per step take levels (6, 5), (4, 3) and (2, 1) for
+// columns n < 8 and n >= 8; int32 accumulation is exact, and the dropped
+// level 0 (Y_0 W_0) weighs 2^-48 of the largest term.  The six level sums of
+// a (token, head) are combined in fp64 and scaled by 2^-(S + 22).  The chunk
+// bias sum_d q_d c0_d is summed in fp64, and only the small difference of a
+// score to the running maximum is rounded before exp2.
+// For the value product yhat is an fp16 pair (hi, lo) with 22 significant
+// bits in two consecutive k slots (k = 2*element + {0: hi, 1: lo}), and the
+// 16 columns are [hi part | lo part] of the probabilities of the 8 query
+// heads: a probability p is split into a truncated fp16 high part and the
+// fp16 remainder, so the product sums (hi + lo) * p.
 //
 // Lane l of a wave: n = l % 16 (MFMA row / column), r = l / 16 (k group).
 // Keys are token-major: lane (n, r) of K tile t reads the 16 bytes of
@@ -67,31 +76,34 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kHeads = 8;  // MFMA columns per part
 constexpr float kSlack = 8.0f;  // log2 of the largest probability before rescaling
 
-// LDS map in bytes.  The table: 256 entries x 256-byte rows; the full code
-// table keeps 64 copies of its 4-byte word per row (lane l reads copy l),
-// the draft table 32 copies of its 8-byte pair (lane l reads copy l % 32),
-// so a wave's reads never collide in a bank.
+// LDS map in bytes.  The table: 256 rows x 256 bytes, one row per code
+// byte.  Full code: 32 copies of the pair (Y word of the key table, fp16
+// pair word of the value table), copy l % 32 for lane l; 4 + 4 draft (row =
+// two anchor nibbles, element 2j in the low one): 16 copies of (Y words of
+// both elements, fp16 pair words of both), copy l % 16 for lane l.  A key
+// and a value read of one element share the address and differ in the
+// instruction's offset field.
 constexpr int kLutBytes = 256 * 256;
+constexpr int kValOffFull = 4;   // value word after the key word
+constexpr int kValOffDraft = 8;  // value pair after the key pair
 // Per wave, two slots (current and next chunk) of the chunk constants:
-// c1k (scaled) f32[128] | c1v f32[128] | c0v f32[128] | c0k f64[128].
-constexpr int kSlotBytes = 3 * 512 + 1024;
+// c1k * 2^S f64[128] | c0k f64[128] | c1v f32[128] | c0v f32[128].
+constexpr int kSlotBytes = 1024 + 1024 + 512 + 512;
 constexpr int kScaleOff = kLutBytes;
 // q as f64 [8 heads][130]: rows padded by 16 bytes so that the 16 lanes of
 // one LDS pass (8 heads x 2 halves) read 16 different bank groups
 constexpr int kQStride = kDim + 2;
 constexpr int kQOff = kScaleOff + kWaves * 2 * kSlotBytes;
-// q as f32 [8 heads][132] for the Q' operand: rows 16 bytes apart modulo the
-// 256-byte bank cycle, so the 8 heads of one LDS pass never collide
-constexpr int kQ32Stride = kDim + 4;
-constexpr int kQ32Off = kQOff + kHeads * kQStride * 8;
-constexpr int kMlOff = kQ32Off + kHeads * kQ32Stride * 4;   // per wave m, l of 8 heads
+constexpr int kMlOff = kQOff + kHeads * kQStride * 8;   // per wave m, l of 8 heads
 constexpr int kLdsBytes = kMlOff + kWaves * 2 * kHeads * 4;
 static_assert(kWaves * 16 * kDim * 4 <= kLutBytes, "combine area must fit the table space");
-
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 
 struct MfmaTables {
-  uint32_t full[256];  // code byte (a << 4 | r) -> fp16 hi | fp16 lo << 16 of yhat
-  uint32_t draft[16];  // anchor nibble -> fp16 hi | fp16 lo << 16 of the draft yhat
+  uint32_t full[256];   // code byte (a << 4 | r) -> fp16 hi | fp16 lo << 16 of yhat
+  uint32_t draft[16];   // anchor nibble -> fp16 hi | fp16 lo << 16 of the draft yhat
+  uint32_t kfull[256];  // code byte -> the 4 signed bytes of round(yhat 2^30)
+  uint32_t kdraft[16];  // anchor nibble -> the same for the draft yhat
 };
 
 using Partials = AttnPartials;
@@ -116,26 +128,28 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t x, uint32_t lb) {
   return __builtin_amdgcn_perm(x, lb, 0x0C0C0000u | ((4u + J) << 8));
 }
 
-// Operand of elements 4s .. 4s+3 of a word (hi, lo of each in consecutive k slots).
-template <int S>
-__device__ __forceinline__ half8 operand_full(uint32_t e, uint32_t o, uint32_t lb, const char *lut) {
+// Table words of elements 4s .. 4s+3 of a code word pair (key words at
+// offset 0, value words at kValOffFull): an i8 key operand (4 bytes per
+// element) or an f16 value operand (hi, lo of each in consecutive k slots).
+template <int S, int kOff>
+__device__ __forceinline__ u32x4 operand_full(uint32_t e, uint32_t o, uint32_t lb, const char *lut) {
   u32x4 w;
-  w[0] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S>(e, lb));
-  w[1] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S>(o, lb));
-  w[2] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S + 1>(e, lb));
-  w[3] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S + 1>(o, lb));
-  return __builtin_bit_cast(half8, w);
+  w[0] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2 * S>(e, lb));
+  w[1] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2 * S>(o, lb));
+  w[2] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2 * S + 1>(e, lb));
+  w[3] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2 * S + 1>(o, lb));
+  return w;
 }
-template <int S>
-__device__ __forceinline__ half8 operand_draft(uint32_t a, uint32_t lb, const char *lut) {
-  const uint2 p0 = *reinterpret_cast<const uint2 *>(lut + lut_addr<2 * S>(a, lb));
-  const uint2 p1 = *reinterpret_cast<const uint2 *>(lut + lut_addr<2 * S + 1>(a, lb));
+template <int S, int kOff>
+__device__ __forceinline__ u32x4 operand_draft(uint32_t a, uint32_t lb, const char *lut) {
+  const uint2 p0 = *reinterpret_cast<const uint2 *>(lut + kOff + lut_addr<2 * S>(a, lb));
+  const uint2 p1 = *reinterpret_cast<const uint2 *>(lut + kOff + lut_addr<2 * S + 1>(a, lb));
   u32x4 w;
   w[0] = p0.x;
   w[1] = p0.y;
   w[2] = p1.x;
   w[3] = p1.y;
-  return __builtin_bit_cast(half8, w);
+  return w;
 }
 
 // ---- b + (8 - b) cut streams --------------------------------------------------
@@ -176,14 +190,15 @@ __device__ __forceinline__ void cut_align(const uint32_t (&w)[NW], uint32_t shif
   o[1] = __builtin_amdgcn_alignbyte(w2, w1, shift);
 }
 
-// Operand of the 4 elements whose table index bytes are x.
-__device__ __forceinline__ half8 operand_bytes(uint32_t x, uint32_t lb, const char *lut) {
+// Table words of the 4 elements whose table index bytes are x.
+template <int kOff>
+__device__ __forceinline__ u32x4 operand_bytes(uint32_t x, uint32_t lb, const char *lut) {
   u32x4 w;
-  w[0] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<0>(x, lb));
-  w[1] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<1>(x, lb));
-  w[2] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2>(x, lb));
-  w[3] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<3>(x, lb));
-  return __builtin_bit_cast(half8, w);
+  w[0] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<0>(x, lb));
+  w[1] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<1>(x, lb));
+  w[2] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2>(x, lb));
+  w[3] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<3>(x, lb));
+  return w;
 }
 
 // ---- streamed chunk data ----------------------------------------------------
@@ -253,33 +268,39 @@ __device__ __forceinline__ void load_scales(Scales &sc, const PlanesArg &kp, con
   sc.rgv = f2(vp.page_range, pb);
 }
 
-// Chunk constants into an LDS slot.  c1k is scaled by the power of two
-// 2^(14 - e), e = exponent of qmax * max c1k (qmax = largest |q| of the
-// group), so every |q * c1k| stays below 2^15; returns its exact inverse.
+// Chunk constants into an LDS slot.  c1k = rg * s is formed in fp64
+// (exact) and scaled by 2^S, S = 29 - e with e the exponent of qmax *
+// max c1k (qmax = largest |q| of the group), so every |q * c1k * 2^S| stays
+// below 2^30 (the fp32 maximum can undercut the fp64 one by an ulp, which
+// still leaves it below 2^31 - 2^24, the range of a 4-byte signed split);
+// returns 2^-(S + 22), the weight of the level sum assembled in
+// compute_chunk.
 __device__ __forceinline__ double scale_stage(const Scales &sc, char *slot, int lane, float qmax) {
-  const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // fp32
+  const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // bound only
   const float bound = qmax * wave_max(fmaxf(c1a, c1b));
-  float ks = 1.0f;
-  double inv_ks = 1.0;
+  int S = 0;
   const uint32_t eb = (__float_as_uint(bound) >> 23) & 0xFFu;
-  if (eb != 0u && eb != 0xFFu) {
-    int ex = 127 + 14 + 127 - static_cast<int>(eb);  // biased exponent of 2^(14 - e)
-    ex = ex < 1 ? 1 : (ex > 254 ? 254 : ex);
-    ks = __uint_as_float(static_cast<uint32_t>(ex) << 23);
-    inv_ks = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + 127 - ex) << 52);
+  if (bound > 0.0f && eb != 0xFFu) {
+    // exponent of a normal or subnormal positive float
+    const int e = eb != 0u ? static_cast<int>(eb) - 127
+                           : -127 - __builtin_clz(__float_as_uint(bound)) + 9;
+    S = 29 - e;
   }
-  float *c1k = reinterpret_cast<float *>(slot);
-  float *c1v = c1k + kDim;
+  const double ks = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + S) << 52);
+  const double inv = __builtin_bit_cast(double, static_cast<uint64_t>(1023 - S - 22) << 52);
+  double *c1k = reinterpret_cast<double *>(slot);
+  double *c0k = c1k + kDim;
+  float *c1v = reinterpret_cast<float *>(c0k + kDim);
   float *c0v = c1v + kDim;
-  double *c0k = reinterpret_cast<double *>(c0v + kDim);
-  reinterpret_cast<float2 *>(c1k)[lane] = make_float2(c1a * ks, c1b * ks);
-  reinterpret_cast<float2 *>(c1v)[lane] = make_float2(sc.rgv.x * sc.sv.x, sc.rgv.y * sc.sv.y);
-  reinterpret_cast<float2 *>(c0v)[lane] =
-      make_float2(__builtin_fmaf(sc.rgv.x, sc.muv.x, sc.mnv.x), __builtin_fmaf(sc.rgv.y, sc.muv.y, sc.mnv.y));
+  reinterpret_cast<double2 *>(c1k)[lane] =
+      make_double2(static_cast<double>(sc.rgk.x) * sc.sk.x * ks, static_cast<double>(sc.rgk.y) * sc.sk.y * ks);
   reinterpret_cast<double2 *>(c0k)[lane] =
       make_double2(static_cast<double>(sc.mnk.x) + static_cast<double>(sc.rgk.x) * sc.muk.x,
                    static_cast<double>(sc.mnk.y) + static_cast<double>(sc.rgk.y) * sc.muk.y);
-  return inv_ks;
+  reinterpret_cast<float2 *>(c1v)[lane] = make_float2(sc.rgv.x * sc.sv.x, sc.rgv.y * sc.sv.y);
+  reinterpret_cast<float2 *>(c0v)[lane] =
+      make_float2(__builtin_fmaf(sc.rgv.x, sc.muv.x, sc.mnv.x), __builtin_fmaf(sc.rgv.y, sc.muv.y, sc.mnv.y));
+  return inv;
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -301,6 +322,7 @@ struct LaneConst {
   bool lo;
   uint32_t lb;         // lane bits of the table address
   uint32_t keep_mask;  // 0 for the high column half, ~0x1FFF for the low one
+  uint32_t lvl[3];     // v_perm selectors of this column's W bytes in the 3 level products
   double sm2;          // sm_scale * log2(e)
   // cut streams: byte offsets of the lane's K unit within a chunk of the
   // anchor / residual stream, of its V window words (channel n, chunk
@@ -377,18 +399,30 @@ __device__ __forceinline__ void cut_key_bytes(const uint32_t (&a)[B], const uint
     }
 }
 
+// W bytes of one element for the level products: the floor of w * 2^S
+// (here w * 2^S + 0x80808080, so the truncating conversion is a floor and
+// every byte carries a +128 bias), with the bias of each byte flipped back,
+// is the 4-byte signed split (byte j = W_j); each product then takes the
+// bytes its column's level needs.
+__device__ __forceinline__ uint32_t w_bytes(double q, double c1s) {
+  constexpr double kBias = 2155905152.0;  // 0x80808080
+  return static_cast<uint32_t>(__builtin_fma(q, c1s, kBias)) ^ 0x80808080u;
+}
+
 // One chunk: scores, online softmax (base 2), value sum.  kBits = 4 reads
 // the 4-bit planes, other values b + (8 - b) streams.
 template <bool kFull, int kBits, class CodesT>
-__device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot, double inv_ks,
-                                              const float *q32, const double *q64,
-                                              const LaneConst &lc, const char *lut,
-                                              RunState &st, float *srow) {
+__device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot, double inv_s,
+                                              const double *q64, const LaneConst &lc,
+                                              const char *lut, RunState &st, float *srow) {
   const int n = lc.n, r = lc.r;
-  const float *c1k = reinterpret_cast<const float *>(slot);
-  const float *c1v = c1k + kDim;
+  const double *c1k = reinterpret_cast<const double *>(slot);
+  const double *c0k = c1k + kDim;
+  const float *c1v = reinterpret_cast<const float *>(c0k + kDim);
   const float *c0v = c1v + kDim;
-  const double *c0k = reinterpret_cast<const double *>(c0v + kDim);
+  // value words sit after the key words (full code, cuts) or key pairs (4 + 4 draft)
+  constexpr bool kWordTable = kFull || kBits != 4;
+  constexpr int kVOff = kWordTable ? kValOffFull : kValOffDraft;
 
   // ---- chunk bias sum_d q_d c0k_d in fp64: lane takes channels 32r + 16*lo .. +15 ----
   double bias;
@@ -408,8 +442,9 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
     bias = xrows_sum(bias);
   }
 
-  // ---- scores: S^T = Yk * Q' (tiles t = 0, 1 share each Q' step) ----
-  floatx4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  // ---- scores: S^T = Yk * W, three level products per tile (exact int32) ----
+  i32x4 sa0 = {0, 0, 0, 0}, sb0 = {0, 0, 0, 0}, sc0 = {0, 0, 0, 0};
+  i32x4 sa1 = {0, 0, 0, 0}, sb1 = {0, 0, 0, 0}, sc1 = {0, 0, 0, 0};
   {
     // 4 + 4: code bytes of even / odd elements (full) or the anchor words
     // (draft); cuts: table index bytes of elements 8w + 4h ..
@@ -432,56 +467,82 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
       cut_key_bytes<kFull, kBits>(cd.ka[0], cd.kr[0], x0);
       cut_key_bytes<kFull, kBits>(cd.ka[1], cd.kr[1], x1);
     }
-    const float *qrow = q32 + (n & 7) * kQ32Stride + 32 * r;
+    const double *qrow = q64 + (n & 7) * kQStride + 32 * r;
 #pragma unroll
     for (int stp = 0; stp < 8; ++stp) {
-      const float4 c1 = *reinterpret_cast<const float4 *>(c1k + 32 * r + 4 * stp);
-      const float4 qq = *reinterpret_cast<const float4 *>(qrow + 4 * stp);
-      u32x4 bw;
-      bw[0] = split_dup(qq.x * c1.x, lc.keep_mask);
-      bw[1] = split_dup(qq.y * c1.y, lc.keep_mask);
-      bw[2] = split_dup(qq.z * c1.z, lc.keep_mask);
-      bw[3] = split_dup(qq.w * c1.w, lc.keep_mask);
-      const half8 b = __builtin_bit_cast(half8, bw);
-      half8 a0, a1;
+      // W of channels 32r + 4stp .. +3 for this lane's query head
+      const double2 c1a = *reinterpret_cast<const double2 *>(c1k + 32 * r + 4 * stp);
+      const double2 c1b = *reinterpret_cast<const double2 *>(c1k + 32 * r + 4 * stp + 2);
+      const double2 qa = *reinterpret_cast<const double2 *>(qrow + 4 * stp);
+      const double2 qb = *reinterpret_cast<const double2 *>(qrow + 4 * stp + 2);
+      const uint32_t wv[4] = {w_bytes(qa.x, c1a.x), w_bytes(qa.y, c1a.y), w_bytes(qb.x, c1b.x),
+                              w_bytes(qb.y, c1b.y)};
+      i32x4 ba, bb, bc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ba[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[0]));
+        bb[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[1]));
+        bc[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[2]));
+      }
+      u32x4 a0, a1;
       const int w = stp >> 1;
       if constexpr (kBits != 4) {
-        a0 = operand_bytes(x0[w][stp & 1], lc.lb, lut);
-        a1 = operand_bytes(x1[w][stp & 1], lc.lb, lut);
+        a0 = operand_bytes<0>(x0[w][stp & 1], lc.lb, lut);
+        a1 = operand_bytes<0>(x1[w][stp & 1], lc.lb, lut);
       } else if (kFull) {
         if (stp & 1) {
-          a0 = operand_full<1>(e0[w], o0[w], lc.lb, lut);
-          a1 = operand_full<1>(e1[w], o1[w], lc.lb, lut);
+          a0 = operand_full<1, 0>(e0[w], o0[w], lc.lb, lut);
+          a1 = operand_full<1, 0>(e1[w], o1[w], lc.lb, lut);
         } else {
-          a0 = operand_full<0>(e0[w], o0[w], lc.lb, lut);
-          a1 = operand_full<0>(e1[w], o1[w], lc.lb, lut);
+          a0 = operand_full<0, 0>(e0[w], o0[w], lc.lb, lut);
+          a1 = operand_full<0, 0>(e1[w], o1[w], lc.lb, lut);
         }
       } else {
         if (stp & 1) {
-          a0 = operand_draft<1>(e0[w], lc.lb, lut);
-          a1 = operand_draft<1>(e1[w], lc.lb, lut);
+          a0 = operand_draft<1, 0>(e0[w], lc.lb, lut);
+          a1 = operand_draft<1, 0>(e1[w], lc.lb, lut);
         } else {
-          a0 = operand_draft<0>(e0[w], lc.lb, lut);
-          a1 = operand_draft<0>(e1[w], lc.lb, lut);
+          a0 = operand_draft<0, 0>(e0[w], lc.lb, lut);
+          a1 = operand_draft<0, 0>(e1[w], lc.lb, lut);
         }
       }
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b, s1, 0, 0, 0);
+      const i32x4 y0 = __builtin_bit_cast(i32x4, a0), y1 = __builtin_bit_cast(i32x4, a1);
+      sa0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, ba, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, ba, sa1, 0, 0, 0);
+      sb0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, bb, sb0, 0, 0, 0);
+      sb1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, bb, sb1, 0, 0, 0);
+      sc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, bc, sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, bc, sc1, 0, 0, 0);
     }
   }
 
   // ---- assemble: lanes n < 8 take tile 0, lanes n >= 8 tile 1 (tokens 16t + 4r + i) ----
-  const double scale2 = lc.sm2 * inv_ks;
+  // Levels 6, 4, 2 sit in columns n < 8, levels 5, 3, 1 in columns n >= 8:
+  // the high levels are this lane's own tile 0 (n < 8) or lane n - 8's tile
+  // 1, the low levels lane n + 8's tile 0 (n < 8) or this lane's tile 1.
+  const double scale2 = lc.sm2 * inv_s;
   const double bias2 = bias * lc.sm2;
   double sc2[4];
   float cmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // high part: own tile 0 (n < 8) or lane n - 8's tile 1; low part: lane
-    // n + 8's tile 0 (n < 8) or own tile 1
-    const float big = ror8_to_hi(s0[i], s1[i]);
-    const float small = ror8_to_lo(s1[i], s0[i]);
-    sc2[i] = fma(static_cast<double>(big) + static_cast<double>(small), scale2, bias2);
+    auto hi = [](int t0, int t1) {
+      return __builtin_bit_cast(int, ror8_to_hi(__builtin_bit_cast(float, t0), __builtin_bit_cast(float, t1)));
+    };
+    auto lo = [](int t1, int t0) {
+      return __builtin_bit_cast(int, ror8_to_lo(__builtin_bit_cast(float, t1), __builtin_bit_cast(float, t0)));
+    };
+    const int l6 = hi(sa0[i], sa1[i]), l5 = lo(sa1[i], sa0[i]);
+    const int l4 = hi(sb0[i], sb1[i]), l3 = lo(sb1[i], sb0[i]);
+    const int l2 = hi(sc0[i], sc1[i]), l1 = lo(sc1[i], sc0[i]);
+    // sum_L C_L 2^(8L) / 2^8 by Horner (each |C_L| < 2^23)
+    double t = static_cast<double>(l6);
+    t = fma(t, 256.0, static_cast<double>(l5));
+    t = fma(t, 256.0, static_cast<double>(l4));
+    t = fma(t, 256.0, static_cast<double>(l3));
+    t = fma(t, 256.0, static_cast<double>(l2));
+    t = fma(t, 256.0, static_cast<double>(l1));
+    sc2[i] = fma(t, scale2, bias2);
     cmax = fmaxf(cmax, static_cast<float>(sc2[i]));
   }
   cmax = fmaxf(cmax, ror8(cmax));
@@ -548,16 +609,16 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
         xa = (xa << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 0);
         xb = (xb << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 4);
       }
-      y0 = operand_bytes(xa, lc.lb, lut);
-      y1 = operand_bytes(xb, lc.lb, lut);
+      y0 = __builtin_bit_cast(half8, operand_bytes<kVOff>(xa, lc.lb, lut));
+      y1 = __builtin_bit_cast(half8, operand_bytes<kVOff>(xb, lc.lb, lut));
     } else if (kFull) {
       uint32_t e, o;
       code_bytes(cd.va[ct], cd.vr[ct], e, o);
-      y0 = operand_full<0>(e, o, lc.lb, lut);
-      y1 = operand_full<1>(e, o, lc.lb, lut);
+      y0 = __builtin_bit_cast(half8, operand_full<0, kVOff>(e, o, lc.lb, lut));
+      y1 = __builtin_bit_cast(half8, operand_full<1, kVOff>(e, o, lc.lb, lut));
     } else {
-      y0 = operand_draft<0>(cd.va[ct], lc.lb, lut);
-      y1 = operand_draft<1>(cd.va[ct], lc.lb, lut);
+      y0 = __builtin_bit_cast(half8, operand_draft<0, kVOff>(cd.va[ct], lc.lb, lut));
+      y1 = __builtin_bit_cast(half8, operand_draft<1, kVOff>(cd.va[ct], lc.lb, lut));
     }
     floatx4 ov = {0.0f, 0.0f, 0.0f, 0.0f};
     ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pa0, ov, 0, 0, 0);
@@ -580,7 +641,6 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   __shared__ __align__(16) char smem[kLdsBytes];
   char *lut = smem;
   double *q64 = reinterpret_cast<double *>(smem + kQOff);
-  float *q32 = reinterpret_cast<float *>(smem + kQ32Off);
   float *s_ml = reinterpret_cast<float *>(smem + kMlOff);
 
   // blocks of one (request, KV head) are consecutive logical blocks; spread
@@ -606,10 +666,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   lc.voff = static_cast<uint32_t>(lc.n * 16 + lc.r * 4);
   lc.soff = static_cast<uint32_t>(lc.lane * 8);
   lc.keep_mask = lc.lo ? 0xFFFFE000u : 0u;
-  // 4-byte table rows for the full code and for every cut's index bytes;
-  // 8-byte pair rows for the 4 + 4 draft
+  // (key word, value word) copies for the full code and for every cut's
+  // index bytes; (key pair, value pair) copies for the 4 + 4 draft
   constexpr bool kWordTable = kFull || kBits != 4;
-  lc.lb = kWordTable ? static_cast<uint32_t>(lc.lane * 4) : static_cast<uint32_t>((lc.lane & 31) * 8);
+  lc.lb = kWordTable ? static_cast<uint32_t>((lc.lane & 31) * 8) : static_cast<uint32_t>((lc.lane & 15) * 16);
+  // W bytes of this column's levels: 6, 4, 2 (n < 8) or 5, 3, 1 (n >= 8)
+  lc.lvl[0] = lc.lo ? 0x02030C0Cu : 0x030C0C0Cu;
+  lc.lvl[1] = lc.lo ? 0x00010203u : 0x0102030Cu;
+  lc.lvl[2] = lc.lo ? 0x0C0C0001u : 0x0C000102u;
   if constexpr (kBits != 4) cut_lane_offsets<kBits>(lc);
   lc.sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
 
@@ -645,9 +709,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   };
 
   // Codes of NB chunks are held per wave: the chunk being computed and the
-  // next D = NB - 1 in flight (the draft's chunks are smaller, so it looks
-  // further ahead; drafts of more than 4 bits hold as many words as the
-  // full code and look as far).  Scales run one chunk further ahead than codes: the step
+  // next D = NB - 1 in flight (the 4 + 4 draft's chunks are smaller, so it
+  // looks further ahead; the cuts' unpacking leaves no registers for a
+  // third chunk).  Scales run one chunk further ahead than codes: the step
   // of chunk c requests the scales of chunk c + D + 1 and then the codes of
   // chunk c + D, so the scales staged at the end of a step were requested
   // before the codes that step waited for.  A wave whose run is short thus
@@ -656,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   // on an absent page reads chunk 0 of pool page 0 instead, and is not
   // computed -- so the wait counts the compiler derives are exact and never
   // wait for loads that are still ahead in the pipeline.
-  constexpr int NB = (kFull || kBits > 4) ? 2 : 3;
+  constexpr int NB = (kFull || kBits != 4) ? 2 : 3;
   constexpr int D = NB - 1;
   using CodesT = std::conditional_t<kBits == 4, Codes, CutCodes<kBits>>;
   CodesT cds[NB];   // codes of chunk c in buffer (c - cb) % NB
@@ -674,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   // ---- set-up loads: this thread's table words and its lane's query
   // values, issued ahead of the chunk loads so that waiting for them never
   // waits for chunk data ----
-  uint32_t tw0, tw1;
+  uint32_t tw0, tw1, kw0, kw1;  // value and key table words of this thread's row
   {
     const int e = tid & 255;
     if constexpr (kBits != 4 && !kFull) {
@@ -683,14 +747,21 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
       constexpr int RB = 8 - kBits;
       const int f = e & ((1 << kBits) - 1);
       const int a = f >= (1 << (kBits - 1)) ? f - (1 << kBits) : f;
-      tw0 = tab.full[(a * (1 << RB) + (1 << (RB - 1)) - 1) & 255];
+      const int c = (a * (1 << RB) + (1 << (RB - 1)) - 1) & 255;
+      tw0 = tab.full[c];
+      kw0 = tab.kfull[c];
       tw1 = tw0;
+      kw1 = kw0;
     } else if (kFull) {
       tw0 = tab.full[e];
+      kw0 = tab.kfull[e];
       tw1 = tw0;
+      kw1 = kw0;
     } else {
       tw0 = tab.draft[e & 15];
       tw1 = tab.draft[e >> 4];
+      kw0 = tab.kdraft[e & 15];
+      kw1 = tab.kdraft[e >> 4];
     }
   }
   const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
@@ -721,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
 
   // ---- tables (replicated rows) ----
   {
-    const u32x4 v = kWordTable ? u32x4{tw0, tw0, tw0, tw0} : u32x4{tw0, tw1, tw0, tw1};
+    const u32x4 v = kWordTable ? u32x4{kw0, tw0, kw0, tw0} : u32x4{kw0, kw1, tw0, tw1};
     u32x4 *dst = reinterpret_cast<u32x4 *>(lut + (tid & 255) * 256 + (tid >> 8) * 128);
 #pragma unroll
     for (int k = 0; k < 8; ++k) dst[k] = v;
@@ -743,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
     for (int k = 0; k < 32; ++k) qmax = fmaxf(qmax, fabsf(qv[k]));
     qmax = wave_max(qmax);
   }
-  // the query group in LDS, f64 and f32 (zero rows for heads >= g): wave w
+  // the query group in LDS as f64 (zero rows for heads >= g): wave w
   // writes head w's row from the lanes n = w (first 16 of their 32
   // channels) and n = w + 8 (last 16)
   if (jq == w) {
@@ -753,7 +824,6 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
     for (int k = 0; k < 16; ++k) {
       const float x = second ? qv[16 + k] : qv[k];
       q64[w * kQStride + d0 + k] = static_cast<double>(x);
-      q32[w * kQ32Stride + d0 + k] = x;
     }
   }
   __syncthreads();
@@ -770,7 +840,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   for (int ct = 0; ct < 8; ++ct) st.acc[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (cb < ce) {
-    double ks0 = 1.0, ks1 = 1.0;  // inverse Q' scales of LDS slots 0 and 1
+    double ks0 = 1.0, ks1 = 1.0;  // score weights 2^-(S + 22) of LDS slots 0 and 1
     ks0 = scale_stage(scs[0], slots, lc.lane, qmax);
     // one chunk c held in buffers J = (c - cb) % NB, constants in LDS slot (c - cb) & 1
     auto step = [&](auto jc, int c) {
@@ -783,8 +853,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
       load_chunk(cds[JD], pgs[JD], c + D);
       if (cur >= 0) {
         wave_lds_sync();
-        compute_chunk<kFull, kBits>(cds[J], slots + slot * kSlotBytes, slot ? ks1 : ks0, q32, q64, lc, lut,
-                             st, srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
+        compute_chunk<kFull, kBits>(cds[J], slots + slot * kSlotBytes, slot ? ks1 : ks0, q64, lc, lut,
+                                    st, srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
       }
       const double k = scale_stage(scs[J1], slots + (slot ^ 1) * kSlotBytes, lc.lane, qmax);
       if (slot) ks0 = k; else ks1 = k;
@@ -989,6 +1059,16 @@ MfmaTables build_mfma_tables() {
     t.full[byte] = pair(dt.y[code + 128]);
   }
   for (int nib = 0; nib < 16; ++nib) t.draft[nib] = pair(df.y[nib]);
+  // fixed-point yhat as 4 signed bytes: Y + 0x80808080 puts a +128 bias on
+  // every byte, and flipping each byte's top bit removes it again, so byte j
+  // holds Y_j in -128 .. 127 with sum_j Y_j 2^(8j) = Y (|Y| <= 2^30)
+  const FixedDecodeTable &fx = fixed_decode_table();
+  auto bytes = [](int32_t y) { return (static_cast<uint32_t>(y) + 0x80808080u) ^ 0x80808080u; };
+  for (int byte = 0; byte < 256; ++byte) {
+    const int code = byte >= 128 ? byte - 256 : byte;
+    t.kfull[byte] = bytes(fx.y[code + 128]);
+  }
+  for (int nib = 0; nib < 16; ++nib) t.kdraft[nib] = bytes(fx.draft[nib]);
   return t;
 }
 

@@ -62,6 +62,16 @@ struct DraftTable {
 };
 const DraftTable &draft_table();
 
+// yhat in fixed point for the exact integer score products: round(yhat *
+// 2^30) of every 8-bit code (index code + 128) and of the 16 draft codes
+// 16a + 7 (index = nibble).  |yhat| <= 1, so every value fits 31 bits.
+constexpr int kFixedYBits = 30;
+struct FixedDecodeTable {
+  int32_t y[256];
+  int32_t draft[16];
+};
+const FixedDecodeTable &fixed_decode_table();
+
 // ---------------------------------------------------------------------------
 // Launchers (return hipError_t of the launch; argument checking happens in
 // the API layer).

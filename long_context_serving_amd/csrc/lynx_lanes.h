@@ -13,6 +13,7 @@ namespace lanes {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // ---- cross-lane helpers -----------------------------------------------------
 // value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8);

@@ -96,10 +96,22 @@ DraftTable build_draft_table() {
   return d;
 }
 
+FixedDecodeTable build_fixed_table() {
+  FixedDecodeTable d;
+  for (int q = -128; q < 128; ++q)
+    d.y[q + 128] = static_cast<int32_t>(std::llround(std::ldexp(yhat_of_code(q), kFixedYBits)));
+  for (int nib = 0; nib < 16; ++nib) {
+    const int a = nib >= 8 ? nib - 16 : nib;
+    d.draft[nib] = static_cast<int32_t>(std::llround(std::ldexp(yhat_of_code(16 * a + 7), kFixedYBits)));
+  }
+  return d;
+}
+
 std::once_flag g_once;
 CodeTable g_code;
 DecodeTable g_decode;
 DraftTable g_draft;
+FixedDecodeTable g_fixed;
 BucketTable g_bucket;
 
 void init_tables() {
@@ -107,6 +119,7 @@ void init_tables() {
   g_bucket = build_bucket_table(g_code);
   g_decode = build_decode_table();
   g_draft = build_draft_table();
+  g_fixed = build_fixed_table();
 }
 
 }  // namespace
@@ -124,6 +137,11 @@ const DecodeTable &decode_table() {
 const DraftTable &draft_table() {
   std::call_once(g_once, init_tables);
   return g_draft;
+}
+
+const FixedDecodeTable &fixed_decode_table() {
+  std::call_once(g_once, init_tables);
+  return g_fixed;
 }
 
 const BucketTable &bucket_table() {

@@ -7,13 +7,13 @@ Bar (element by element, same seeded inputs):
   dequant     |gpu - oracle| <= 1e-3 |oracle|, or <= 1e-6 * page range where
               the reconstruction cancels to ~0;
   attention   |gpu - oracle| <= 2e-3 + 1e-5 |oracle| per element (oracle in
-              fp64 over its own dequantized K and V).  The 2e-3 is the
-              stated bar against fp32; the 1e-5 relative part is what a plain
-              fp32 evaluation of the same attention (fp32 K, V, scores,
-              softmax) needs itself: at 64K tokens with 100x channels in K
-              and V it misses the oracle by 3.4e-3 on outputs of ~300.
-  peaked      with one-hot softmax (plain Laplace queries), where fp32 itself
-              misses 2e-3 by up to 7x: no worse than that fp32 evaluation.
+              fp64 over its own dequantized K and V), for key-aligned and for
+              plain Laplace queries alike.  The 2e-3 is the stated bar
+              against fp32; the 1e-5 relative part covers the fp32 value
+              sums of outputs of several hundred.  A plain fp32 evaluation
+              of the same attention misses this bar on plain Laplace queries
+              (one-hot softmax over scores of a few hundred); the kernel's
+              scores are exact integer products, so it does not.
 """
 import dataclasses
 import math
@@ -113,16 +113,15 @@ def oracle_attention_for(enc_k, enc_v, q_bits, page_lists, full, want_logits=Fal
 
 
 def check_attention(got, ref, label, fp32_err=None):
-    """The attention bar.  fp32_err (plain Laplace queries, a one-hot
-    softmax over scores of a few hundred): the max-abs error of a plain fp32
-    evaluation of the same attention, which the bar then also admits."""
+    """The attention bar, on both query classes.  fp32_err, printed for
+    comparison only: the max-abs error of a plain fp32 evaluation of the
+    same attention (with plain Laplace queries the softmax is one-hot over
+    scores of a few hundred, and fp32 alone misses the bar)."""
     err = np.abs(got - ref)
     bound = ATOL_ATTN + RTOL_ATTN * np.abs(ref)
     print("%s: max abs err %.3g (max |out| %.1f), max err/bound %.3f%s" %
           (label, err.max(), np.abs(ref).max(), (err / bound).max(),
            "" if fp32_err is None else ", plain fp32 evaluation %.3g" % fp32_err), flush=True)
-    if fp32_err is not None:
-        bound = np.maximum(bound, fp32_err)
     assert (err <= bound).all(), label
 
 
