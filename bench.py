@@ -196,43 +196,247 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, xk, xv, qb, pages, sm, min_seconds=10.0):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    the sample (encode K and V, then anchor and full decode) is repeated
-    until at least min_seconds of CPU time have passed, and the rate is the
-    average over the passes."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_leg(w, xk, xv, qb, pages, sm, nthreads, min_seconds):
+    """One timing leg of the CPU oracle: encode K and V, then anchor and full
+    dequantization of K and V, then brute-force attention for every query
+    head over both reconstructions, repeated until min_seconds have passed.
+    Rates use the GPU's algorithmic-byte accounting (dequantization counted
+    with fp32 output)."""
     import oracle
-    nt = oracle.max_threads()
     xk, xv = xk[:pages], xv[:pages]
     q = oracle.bf16_bits_to_float(qb).astype(np.float64)
-    t_enc = t_dec = 0.0
+    t = {"encode": 0.0, "dequant": 0.0, "attention": 0.0}
     passes = 0
-    while passes == 0 or t_enc + t_dec < min_seconds:
+    while passes == 0 or sum(t.values()) < min_seconds:
         t0 = time.perf_counter()
-        ek, ev = oracle.encode(xk), oracle.encode(xv)
+        ek, ev = oracle.encode(xk, nthreads), oracle.encode(xv, nthreads)
         t1 = time.perf_counter()
         ak, rk = oracle.split(ek["codes"])
         av, rv = oracle.split(ev["codes"])
+        recon = {}
         for full in (False, True):
-            kh = oracle.dequant(ak, rk if full else None, ek).reshape(1, -1, w.kv_heads, w.head_dim)
-            vh = oracle.dequant(av, rv if full else None, ev).reshape(1, -1, w.kv_heads, w.head_dim)
-            oracle.attention(q[:1], kh, vh, sm)
+            recon[full] = (oracle.dequant(ak, rk if full else None, ek, nthreads),
+                           oracle.dequant(av, rv if full else None, ev, nthreads))
         t2 = time.perf_counter()
-        t_enc += t1 - t0
-        t_dec += t2 - t1
+        for full in (False, True):
+            kh, vh = (r.reshape(1, -1, w.kv_heads, w.head_dim) for r in recon[full])
+            oracle.attention(q[:1], kh, vh, sm, nthreads=nthreads)
+        t3 = time.perf_counter()
+        t["encode"] += t1 - t0
+        t["dequant"] += t2 - t1
+        t["attention"] += t3 - t2
         passes += 1
-    elems = pages * 256 * w.kv_heads * w.head_dim
+    elems = 2 * pages * 256 * w.kv_heads * w.head_dim          # K and V
     qo = w.q_heads * w.head_dim * 6
-    nbytes = 2 * elems * 3.28125 + 2 * elems * (1.28125 + 0.78125) + 2 * qo
+    nbytes = {"encode": elems * 3.28125,
+              "dequant": elems * (1.28125 + 4.0) + elems * (0.78125 + 4.0),
+              "attention": elems * (1.28125 + 0.78125) + 2 * qo}
+    total = sum(t.values())
+    leg = {"threads": nthreads, "pages": pages, "passes": passes, "seconds": total,
+           "GBps": passes * sum(nbytes.values()) / total / 1e9}
+    for k in t:
+        leg[k] = {"s_per_pass": t[k] / passes, "GBps": passes * nbytes[k] / t[k] / 1e9,
+                  "elements_per_s": passes * elems / t[k]}
+    return leg
+
+
+def cpu_baseline(w, xk, xv, qb, sm, pages_all=32, pages_one=4):
+    """The CPU oracle, as it stands, on bounded samples of the same workload,
+    on all host cores and on one core.  value: the all-cores rate of the
+    whole step (encode, anchor and full reconstruction, attention) in the
+    step's byte accounting."""
+    import oracle
+    nt = oracle.max_threads()
+    allc = cpu_leg(w, xk, xv, qb, min(pages_all, w.pages), sm, nt, 8.0)
+    one = cpu_leg(w, xk, xv, qb, min(pages_one, w.pages), sm, 1, 4.0)
     return {
-        "value": passes * nbytes / (t_enc + t_dec) / 1e9, "unit": "GB/s", "cores": nt,
-        "kind": "oracle",
-        "sample": "%d passes over %d of %d pages of one request (K and V): encode, then anchor "
-                  "and full dequant + brute-force attention for all %d query heads; per pass "
-                  "encode %.2f s, decode %.2f s" % (passes, pages, w.pages, w.q_heads,
-                                                    t_enc / passes, t_dec / passes),
-        "seconds": t_enc + t_dec,
+        "value": allc["GBps"], "unit": "GB/s", "cores": nt, "kind": "oracle",
+        "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+        "sample": "the first %d (all cores) and %d (one core) of the %d pages of one request of %s, "
+                  "K and V: encode, anchor and full dequant, brute-force attention of all %d "
+                  "query heads over both, repeated for at least 8 s / 4 s" % (
+                      allc["pages"], one["pages"], w.pages, w.name, w.q_heads),
+        "all_cores": allc, "one_core": one,
     }
+
+
+def time_graph(calls, stream, reps=3):
+    """Average time (ms) of one replay of a HIP graph of the given calls,
+    measured with events on the launch stream over `reps` replays after one
+    untimed replay."""
+    import torch
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / reps
+
+
+def tiny_leg(dev, stream, launches=64):
+    """Latency of every call on the tiny workload (1 layer, 4 KV heads, 1024
+    tokens, 32 query heads): graphs of `launches` back-to-back launches."""
+    import torch
+    from long_context_serving_amd import lynx, synth
+    w = synth.WORKLOADS["tiny"]
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    k, v = to_dev(synth.kv_pages(w, 0, 0, 0)), to_dev(synth.kv_pages(w, 0, 1, 0))
+    q = to_dev(synth.queries(w))
+    pk = lynx.alloc_planes(w.pages, w.kv_heads, lynx.ROLE_KEY, dev)
+    pv = lynx.alloc_planes(w.pages, w.kv_heads, lynx.ROLE_VALUE, dev)
+    out = torch.empty((1, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    deq = torch.empty((w.pages, 256, w.kv_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = lynx.alloc_workspace(1, w.kv_heads, w.q_heads, w.pages, dev)
+    sm = float(np.float32(1.0 / math.sqrt(w.head_dim)))
+    calls = {
+        "encode_kv": lambda: lynx.quantize_kv_pages(k, v, out_k=pk, out_v=pv),
+        "dequant_anchor_k": lambda: lynx.dequantize(pk, full=False, out=deq),
+        "dequant_full_k": lambda: lynx.dequantize(pk, full=True, out=deq),
+        "decode_anchor": lambda: lynx.decode_attention(q, pk, pv, w.pages, full=False, sm_scale=sm,
+                                                       out=out, workspace=ws),
+        "decode_full": lambda: lynx.decode_attention(q, pk, pv, w.pages, full=True, sm_scale=sm,
+                                                     out=out, workspace=ws),
+    }
+    calls["encode_kv"]()
+    res = {}
+    for name, c in calls.items():
+        res[name + "_us"] = time_graph([c] * launches, stream) / launches * 1e3
+    return {"workload": w.name, "latency": res,
+            "timing": "events around replays of a HIP graph of %d back-to-back launches of one call "
+                      "(inputs cache-resident: a launch-bound shape)" % launches}
+
+
+def qwen3_leg(dev, stream, reps=3):
+    """Streaming encode of the Qwen3-235B-A22B-shaped request: 94 layers x
+    K and V of 4 KV heads x 128K tokens (25.2 GB of bf16) into planes resident
+    in HBM (16.2 GB).  Inputs are drawn on the device (synth.device_kv_pages),
+    so the timed region holds only the 94 encode launches."""
+    import torch
+    from long_context_serving_amd import lynx, synth
+    w = synth.WORKLOADS["qwen3_235b_128k"]
+    log("bench: qwen3 shape: drawing %d layers of K and V on the device" % w.layers)
+    t0 = time.perf_counter()
+    ins, outs = [], []
+    for layer in range(w.layers):
+        ins.append((synth.device_kv_pages(w, layer, 0, 0, device=dev),
+                    synth.device_kv_pages(w, layer, 1, 0, device=dev)))
+        outs.append((lynx.alloc_planes(w.pages, w.kv_heads, lynx.ROLE_KEY, dev),
+                     lynx.alloc_planes(w.pages, w.kv_heads, lynx.ROLE_VALUE, dev)))
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    calls = [lambda i=i, o=o: lynx.quantize_kv_pages(i[0], i[1], out_k=o[0], out_v=o[1])
+             for i, o in zip(ins, outs)]
+    ms = time_graph(calls, stream, reps)
+    E = w.elements()
+    nbytes = E * 3.28125
+    del ins, outs, calls
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads, "tokens": w.tokens,
+            "bf16_in_bytes": 2 * E, "encoded_bytes": int(E * 1.28125),
+            "ms_all_layers": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "pct_of_hbm_peak": 100.0 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "kv_tokens_per_s": w.tokens * w.layers / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "inputs_drawn_s": gen_s,
+            "timing": "events around %d replays of a HIP graph of the %d per-layer K and V encode "
+                      "launches (inputs 25 GB: no cache reuse)" % (reps, w.layers)}
+
+
+def batched_leg(dev, stream, reps=5):
+    """One decode step over the 64 x 16K batch (8 KV heads, 64 query heads):
+    full and anchor-only fused attention over all requests, one launch each.
+    K and V are drawn on the device and encoded (also timed) beforehand."""
+    import torch
+    from long_context_serving_amd import lynx, synth
+    w = synth.WORKLOADS["batched64x16k"]
+    log("bench: batched 64 x 16K: drawing and encoding the pool")
+    P = w.pages
+    shape = (w.batch * P, 256, w.kv_heads, w.head_dim)
+    k = torch.empty(shape, dtype=torch.int16, device=dev)
+    v = torch.empty(shape, dtype=torch.int16, device=dev)
+    for r in range(w.batch):
+        k[r * P:(r + 1) * P] = synth.device_kv_pages(w, 0, 0, r, device=dev)
+        v[r * P:(r + 1) * P] = synth.device_kv_pages(w, 0, 1, r, device=dev)
+    pk = lynx.alloc_planes(w.batch * P, w.kv_heads, lynx.ROLE_KEY, dev)
+    pv = lynx.alloc_planes(w.batch * P, w.kv_heads, lynx.ROLE_VALUE, dev)
+    q = torch.from_numpy(synth.queries(w).view(np.int16)).to(dev)
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = lynx.alloc_workspace(w.batch, w.kv_heads, w.q_heads, P, dev)
+    sm = float(np.float32(1.0 / math.sqrt(w.head_dim)))
+    enc_ms = time_graph([lambda: lynx.quantize_kv_pages(k, v, out_k=pk, out_v=pv)], stream, reps)
+    del k, v
+    torch.cuda.empty_cache()
+    ab = algorithmic_bytes(w)
+    res = {"workload": w.name, "batch": w.batch, "tokens": w.tokens, "kv_heads": w.kv_heads,
+           "q_heads": w.q_heads,
+           "encode": {"us_per_launch": enc_ms * 1e3, "GBps": ab["encode"] / (enc_ms * 1e-3) / 1e9}}
+    for full, name in ((True, "decode_full"), (False, "decode_anchor")):
+        ms = time_graph([lambda: lynx.decode_attention(q, pk, pv, P, full=full, sm_scale=sm,
+                                                       out=out, workspace=ws)], stream, reps)
+        res[name] = {"us_per_call": ms * 1e3, "GBps": ab[name] / (ms * 1e-3) / 1e9,
+                     "decode_tokens_per_s": w.batch / (ms * 1e-3),
+                     "kv_tokens_per_s": w.batch * w.tokens / (ms * 1e-3)}
+    for key in ("encode", "decode_full", "decode_anchor"):
+        res[key]["pct_of_hbm_peak"] = 100.0 * res[key]["GBps"] / HBM_PEAK_GBPS
+    res["timing"] = "events around %d replays of a HIP graph of one launch (2.75 GB of planes: " \
+                    "no cache reuse)" % reps
+    del pk, pv
+    torch.cuda.empty_cache()
+    return res
+
+
+def progressive_leg(dev):
+    """One progressive-streaming run of the 32-layer 64K workload (planes in
+    pinned host memory, anchors first): times to all drafts and all full
+    attention, against the Lynx-INT8 layer-wise schedule; one warm-up run."""
+    import torch
+    from long_context_serving_amd import stream, synth
+    w = synth.WORKLOADS["progressive32x64k"]
+    sm = float(np.float32(1.0 / math.sqrt(w.head_dim)))
+    t0 = time.perf_counter()
+    ps = stream.ProgressiveStream(stream.build_layers(w, device=dev), device=dev, sm_scale=sm)
+    build_s = time.perf_counter() - t0
+    ps.run_progressive()
+    prog = ps.run_progressive()
+    int8 = ps.run_layerwise_int8()
+    ab, rb = ps.anchor_bytes(), ps.residual_bytes()
+    res = {"workload": w.name, "layers": w.layers, "tokens": w.tokens,
+           "all_drafts_ms": prog["all_drafts_ms"], "all_full_ms": prog["all_full_ms"],
+           "first_draft_ms": prog["first_draft_layer_ms"],
+           "draft_attention_ms": prog["draft_attention_ms"],
+           "full_attention_ms": prog["full_attention_ms"],
+           "h2d_anchor_GBps": ab / (prog["anchors_landed_ms"] * 1e-3) / 1e9,
+           "h2d_residual_GBps": rb / ((prog["residuals_landed_ms"] - prog["anchors_landed_ms"]) * 1e-3) / 1e9,
+           "lynx_int8_layerwise_first_layer_ms": int8["first_layer_ms"],
+           "lynx_int8_layerwise_all_ms": int8["all_full_ms"],
+           "build_s": build_s,
+           "timing": "one run after one warm-up run; bench.py --progressive runs the full harness"}
+    del ps
+    torch.cuda.empty_cache()
+    return res
 
 
 def progressive_main(args):
@@ -429,12 +633,14 @@ def verify_leg(args, w, sets, dev, sm, stream):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200, help="timed steps (rounded up to a multiple of --sets)")
+    ap.add_argument("--steps", type=int, default=200, help="timed steps")
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="ctx32k")
     ap.add_argument("--sets", type=int, default=8, help="distinct buffer sets cycled per step")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
-    ap.add_argument("--cpu-pages", type=int, default=128, help="pages in the CPU-baseline sample")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the other workloads (tiny latency, 94-layer encode, 64 x 16K batch, "
+                         "progressive streaming) after the timed region")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 256 MiB device copy (counter calibration)")
     ap.add_argument("--progressive", action="store_true",
@@ -538,32 +744,37 @@ def main():
                 call()
         return g
 
+    # exactly K steps: full rounds of all S sets, then one round of the first
+    # K mod S sets (graphs of their own)
+    K = max(1, args.steps)
+    full_rounds, rem = divmod(K, S)
     phases = [capture(enc_calls), capture(anc_calls), capture(full_calls)]
+    tail_phases = ([capture(enc_calls[:rem]), capture(anc_calls[:rem]), capture(full_calls[:rem])]
+                   if rem else None)
     torch.cuda.synchronize()
+    plan = [phases] * full_rounds + ([tail_phases] if rem else [])
 
-    def run_rounds(n, events=None):
+    def run_rounds(rounds, events=None):
         with torch.cuda.stream(stream):
-            for r in range(n):
-                for p, g in enumerate(phases):
+            for r, graphs in enumerate(rounds):
+                for p, g in enumerate(graphs):
                     if events is not None:
                         events[r][p].record(stream)
                     g.replay()
                 if events is not None:
                     events[r][3].record(stream)
 
-    run_rounds(max(1, -(-args.warmup // S)))
+    run_rounds([phases] * max(1, -(-args.warmup // S)))
     torch.cuda.synchronize()
 
-    rounds = max(1, -(-args.steps // S))
-    K = rounds * S
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(rounds)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(len(plan))]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    run_rounds(rounds, evs)
+    run_rounds(plan, evs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    step_ms = evs[0][0].elapsed_time(evs[rounds - 1][3]) / K
-    phase_ms = [sum(evs[r][p].elapsed_time(evs[r][p + 1]) for r in range(rounds)) for p in range(3)]
+    step_ms = evs[0][0].elapsed_time(evs[-1][3]) / K
+    phase_ms = [sum(evs[r][p].elapsed_time(evs[r][p + 1]) for r in range(len(plan))) for p in range(3)]
     per_call_ms = {"encode": phase_ms[0] / K, "decode_anchor": phase_ms[1] / K,
                    "decode_full": phase_ms[2] / K}
 
@@ -605,6 +816,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "input_dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads,
                    "head_dim": w.head_dim, "tokens": w.tokens, "batch": w.batch,
@@ -626,9 +838,29 @@ def main():
         result["verify"] = verify
     if cuts is not None:
         result["cuts"] = cuts
+    if args.configs:
+        del sets, enc_calls, anc_calls, full_calls, phases, tail_phases, plan
+        torch.cuda.empty_cache()
+        configs = {}
+        log("bench: tiny latencies")
+        configs["tiny"] = tiny_leg(dev, stream)
+        log("bench: 94-layer streaming encode")
+        configs["qwen3_235b_128k"] = qwen3_leg(dev, stream)
+        log("bench: 64 x 16K batched decode")
+        configs["batched64x16k"] = batched_leg(dev, stream)
+        log("bench: progressive streaming run")
+        configs["progressive32x64k"] = progressive_leg(dev)
+        result["configs"] = configs
+        for key, leg in (("qwen3_235b_128k_encode", configs["qwen3_235b_128k"]),):
+            kernels[key] = {"ms_per_pass": leg["ms_all_layers"], "GBps": leg["GBps"],
+                            "pct_of_hbm_peak": leg["pct_of_hbm_peak"]}
+        for name in ("decode_full", "decode_anchor", "encode"):
+            b = configs["batched64x16k"][name]
+            kernels["batched64x16k_" + name] = {"us_per_call": b.get("us_per_call", b.get("us_per_launch")),
+                                                "GBps": b["GBps"], "pct_of_hbm_peak": b["pct_of_hbm_peak"]}
     if args.cpu:
-        log("bench: CPU baseline (oracle) on %d pages" % args.cpu_pages)
-        result["cpu_baseline"] = cpu_baseline(w, xk0, xv0, qb, min(args.cpu_pages, w.pages), sm)
+        log("bench: CPU baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, xk0, xv0, qb, sm)
     print(json.dumps(result), flush=True)
 
 
