@@ -69,6 +69,8 @@ extern "C" {
                                     verify pass scores at once */
 #define LYNX_TAIL_TOKENS 320     /* capacity of a request's bf16 tail: a page
                                     not yet full plus the speculative tokens */
+#define LYNX_STATIC_SCRATCH_BYTES (32u << 20) /* library-owned scratch of
+                                    lynx_decode_attention_full_static, per GPU */
 
 typedef enum lynx_status {
     LYNX_OK = 0,
@@ -81,7 +83,9 @@ typedef enum lynx_status {
     LYNX_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than required */
     LYNX_ERR_HIP = -5,           /* a HIP runtime call or launch failed */
     LYNX_ERR_DEVICE = -6,        /* current device is not gfx950 */
-    LYNX_ERR_BAD_ARG = -7        /* unknown role or other invalid value */
+    LYNX_ERR_BAD_ARG = -7,       /* unknown role or other invalid value */
+    LYNX_ERR_SCRATCH = -8        /* the shape needs more than the library's
+                                    static scratch (LYNX_STATIC_SCRATCH_BYTES) */
 } lynx_status;
 
 /*
@@ -218,6 +222,33 @@ int lynx_decode_attention_full(const uint16_t *q, const lynx_planes *k,
                                float *out, float *scores,
                                void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * lynx_decode_attention_full without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The split partials go to a
+ * library-owned static device array of LYNX_STATIC_SCRATCH_BYTES that every
+ * GPU the library runs on holds until the process ends; the call allocates
+ * nothing.  Arguments, layouts and results are those of
+ * lynx_decode_attention_full (the same kernels), on the CURRENT device (the
+ * stream must belong to it).
+ *   returns LYNX_ERR_SCRATCH, before any launch, when
+ *   lynx_decode_attention_workspace_size() of the shape exceeds
+ *   LYNX_STATIC_SCRATCH_BYTES; LYNX_ERR_HIP if the scratch's device address
+ *   cannot be looked up.
+ * Every call on a GPU shares that GPU's scratch, whose contents persist
+ * between calls: a call writes every partial it reads, so nothing needs
+ * clearing, but calls that overlap on one GPU (concurrent streams, or
+ * threads) race and must be serialized by the caller.
+ */
+int lynx_decode_attention_full_static(const uint16_t *q, const lynx_planes *k,
+                                      const lynx_planes *v,
+                                      const int32_t *block_table,
+                                      const int32_t *seq_lens, int32_t batch,
+                                      int32_t num_kv_heads, int32_t num_q_heads,
+                                      int32_t head_dim, int32_t max_pages_per_seq,
+                                      int64_t pool_pages, float sm_scale,
+                                      float *out, float *scores, void *stream);
 
 /*
  * Other cuts of the 8-bit code (page "Lynx: the KV cache does not have to

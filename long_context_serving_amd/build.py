@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["lynx_tables.cpp", "lynx_api.cpp", "lynx_encode.hip", "lynx_dequant.hip",
            "lynx_attention.hip", "lynx_attention_mfma.hip", "lynx_tail.hip",
-           "lynx_split.hip", "lynx_verify.hip"]
+           "lynx_split.hip", "lynx_verify.hip", "lynx_scratch.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall",
           "-I", INCLUDE]

@@ -306,6 +306,33 @@ int lynx_decode_attention_full(const uint16_t *q, const lynx_planes *k, const ly
                           workspace_bytes, stream, true);
 }
 
+int lynx_decode_attention_full_static(const uint16_t *q, const lynx_planes *k,
+                                      const lynx_planes *v, const int32_t *block_table,
+                                      const int32_t *seq_lens, int32_t batch,
+                                      int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t max_pages_per_seq, int64_t pool_pages,
+                                      float sm_scale, float *out, float *scores, void *stream) {
+  // shape errors first, with the same checks and codes as the workspace call
+  if (head_dim != LYNX_HEAD_DIM || batch < 0 || num_kv_heads < 1 || num_q_heads < num_kv_heads ||
+      num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > LYNX_MAX_GROUP ||
+      max_pages_per_seq < 1)
+    return LYNX_ERR_BAD_SHAPE;
+  if (batch == 0)
+    return attention_common(q, k, v, block_table, seq_lens, batch, num_kv_heads, num_q_heads,
+                            head_dim, max_pages_per_seq, pool_pages, sm_scale, out, scores,
+                            nullptr, 0, stream, true);
+  const size_t need = lynx::attention_workspace_bytes(
+      lynx::attention_shape(batch, num_kv_heads, num_q_heads, max_pages_per_seq));
+  if (need > lynx::scratch_capacity()) return LYNX_ERR_SCRATCH;
+  int rc = check_device();
+  if (rc) return rc;
+  void *scratch = nullptr;
+  if (lynx::scratch_address(&scratch) != hipSuccess) return LYNX_ERR_HIP;
+  return attention_common(q, k, v, block_table, seq_lens, batch, num_kv_heads, num_q_heads,
+                          head_dim, max_pages_per_seq, pool_pages, sm_scale, out, scores, scratch,
+                          lynx::scratch_capacity(), stream, true);
+}
+
 size_t lynx_split_stream_bytes(int64_t num_pages, int32_t num_kv_heads, int32_t bits) {
   if (num_pages < 0 || num_kv_heads < 1 || bits < 1 || bits > 8) return 0;
   return static_cast<size_t>(num_pages) * num_kv_heads * static_cast<size_t>(bits) * 4096u;
@@ -416,6 +443,7 @@ const char *lynx_status_string(int status) {
     case LYNX_ERR_HIP: return "HIP runtime error";
     case LYNX_ERR_DEVICE: return "current device is not gfx950";
     case LYNX_ERR_BAD_ARG: return "invalid argument value";
+    case LYNX_ERR_SCRATCH: return "shape needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

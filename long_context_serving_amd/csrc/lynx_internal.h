@@ -207,4 +207,10 @@ hipError_t launch_attention_with_tail(const uint16_t *q, const PlanesArg &k, con
                                       float sm_scale, bool full, float *out, void *workspace,
                                       hipStream_t stream);
 
+// Library-owned scratch (lynx_scratch.hip): capacity in bytes, and the
+// scratch's device address on the current device (looked up on the first
+// call per device).
+size_t scratch_capacity();
+hipError_t scratch_address(void **ptr);
+
 }  // namespace lynx

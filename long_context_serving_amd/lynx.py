@@ -63,6 +63,11 @@ for _name in ("lynx_decode_attention_anchor", "lynx_decode_attention_full"):
                                      _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _P, _P, _P,
                                      _sz, _P]
     getattr(_lib, _name).restype = ctypes.c_int
+_lib.lynx_decode_attention_full_static.argtypes = [_P, ctypes.POINTER(_CPlanes),
+                                                   ctypes.POINTER(_CPlanes), _P, _P, _i32, _i32,
+                                                   _i32, _i32, _i32, _i64, ctypes.c_float, _P, _P,
+                                                   _P]
+_lib.lynx_decode_attention_full_static.restype = ctypes.c_int
 _lib.lynx_verify_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 _lib.lynx_verify_attention_workspace_size.restype = _sz
 for _name in ("lynx_verify_attention", "lynx_draft_attention"):
@@ -284,6 +289,32 @@ def decode_attention(q: torch.Tensor, k: Planes, v: Planes, max_pages: int, full
               B, H, Hq, D, max_pages, min(k.num_pages, v.num_pages), float(sm_scale), _ptr(out),
               _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream)),
            "lynx_decode_attention_%s" % ("full" if full else "anchor"))
+    return out
+
+
+def decode_attention_full_static(q: torch.Tensor, k: Planes, v: Planes, max_pages: int,
+                                 block_table: Optional[torch.Tensor] = None,
+                                 seq_lens: Optional[torch.Tensor] = None,
+                                 sm_scale: Optional[float] = None,
+                                 out: torch.Tensor = None, scores: Optional[torch.Tensor] = None,
+                                 stream=None) -> torch.Tensor:
+    """decode_attention(full=True) with the library's static scratch in
+    place of a workspace (lynx_decode_attention_full_static): the library
+    allocates nothing; `out` must be given.  Calls on one GPU must not
+    overlap."""
+    q = _bf16_bits(q)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][Hq][128] bf16 tensor")
+    if out is None:
+        raise ValueError("out must be given: this call allocates nothing")
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    kc, vc = k.c(), v.c()
+    _check(_lib.lynx_decode_attention_full_static(
+        _ptr(q), ctypes.byref(kc), ctypes.byref(vc), _ptr(block_table), _ptr(seq_lens), B, k.heads,
+        Hq, D, max_pages, min(k.num_pages, v.num_pages), float(sm_scale), _ptr(out), _ptr(scores),
+        _stream(stream)), "lynx_decode_attention_full_static")
     return out
 
 

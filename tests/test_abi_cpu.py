@@ -226,7 +226,7 @@ def test_cut_entry_points_reject_bad_arguments(lib):
 
 def test_status_strings(lib):
     lib.lynx_status_string.restype = ctypes.c_char_p
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert lib.lynx_status_string(code)
     assert lib.lynx_status_string(-99) == b"unknown status"
 
@@ -253,3 +253,28 @@ def test_decode_table_agrees_with_the_oracle(lib):
     y = np.array(buf[:], np.float32)
     ref = oracle.yhat(np.arange(-128, 128))
     assert np.array_equal(y, ref.astype(np.float32))     # correctly rounded fp32 of the fp64 value
+
+
+def test_static_scratch_call_rejects_shapes_beyond_its_scratch(lib):
+    """lynx_decode_attention_full_static: shape errors and shapes whose
+    partials exceed the library's static scratch are refused on the host,
+    before any device is touched."""
+    P = ctypes.c_void_p
+    lib.lynx_decode_attention_full_static.argtypes = [
+        P, ctypes.POINTER(CPlanes), ctypes.POINTER(CPlanes), P, P, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, P, P, P]
+    lib.lynx_decode_attention_workspace_size.argtypes = [ctypes.c_int32] * 5
+    lib.lynx_decode_attention_workspace_size.restype = ctypes.c_size_t
+    kp, vp = _fake_planes(0x10000), _fake_planes(0x40000)
+
+    def call(B, H=1, Hq=8, D=128, mp=4):
+        return lib.lynx_decode_attention_full_static(P(0x20000), ctypes.byref(kp), ctypes.byref(vp),
+                                                     P(0x50000), None, B, H, Hq, D, mp, 1 << 20,
+                                                     0.088, P(0x30000), None, None)
+    cap = 32 << 20
+    big = 16384
+    assert lib.lynx_decode_attention_workspace_size(big, 1, 8, 128, 4) > cap
+    assert call(big) == -8
+    assert call(4, D=64) == -2
+    assert call(4, H=3, Hq=8) == -2
+    assert call(0) == 0
