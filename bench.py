@@ -656,6 +656,9 @@ def main():
                     help="encode the buffer sets, then time the verify pass alone")
     ap.add_argument("--verify-tq", type=int, default=64)
     ap.add_argument("--verify-reps", type=int, default=4)
+    ap.add_argument("--config-only", choices=("tiny", "qwen3_235b_128k", "batched64x16k",
+                                              "progressive32x64k"),
+                    help="run only that workload's leg and print its JSON (for profiling)")
     ap.add_argument("--summarize", nargs=4, metavar=("KIND", "DB_DIR", "OUT", "COMMAND"),
                     help="write a text summary of rocprofv3 output (KIND kt or pmc; for pmc "
                          "DB_DIR is '<FETCH_SIZE dir>,<WRITE_SIZE dir>') and exit")
@@ -665,6 +668,16 @@ def main():
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.config_only and args.gpus == 1 and world == 1:
+        import torch
+        dev = torch.device("cuda", 0)
+        torch.cuda.set_device(dev)
+        stream = torch.cuda.Stream()
+        leg = {"tiny": lambda: tiny_leg(dev, stream), "qwen3_235b_128k": lambda: qwen3_leg(dev, stream),
+               "batched64x16k": lambda: batched_leg(dev, stream),
+               "progressive32x64k": lambda: progressive_leg(dev)}[args.config_only]
+        print(json.dumps(leg()), flush=True)
+        return
     if args.progressive and args.gpus == 1 and world == 1:
         progressive_main(args)
         return

@@ -76,27 +76,30 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kHeads = 8;  // MFMA columns per part
 constexpr float kSlack = 8.0f;  // log2 of the largest probability before rescaling
 
-// LDS map in bytes.  The table: 256 rows x 256 bytes, one row per code
-// byte.  Full code: 32 copies of the pair (Y word of the key table, fp16
-// pair word of the value table), copy l % 32 for lane l; 4 + 4 draft (row =
-// two anchor nibbles, element 2j in the low one): 16 copies of (Y words of
-// both elements, fp16 pair words of both), copy l % 16 for lane l.  A key
-// and a value read of one element share the address and differ in the
-// instruction's offset field.
+// LDS map in bytes.  Two tables of 256 rows x 256 bytes, one row per code
+// byte: the key table (Y words) at 0 and the value table (fp16 pair words)
+// at 64 KiB.  Full code and cuts: 64 copies of the row's word, copy l for
+// lane l; 4 + 4 draft (row = two anchor nibbles, element 2j in the low
+// one): 32 copies of the pair of words, copy l % 32 for lane l.  So a
+// wave's table reads never share a bank.  The lane bits of a value read
+// carry the 64 KiB offset in their third byte.
 constexpr int kLutBytes = 256 * 256;
-constexpr int kValOffFull = 4;   // value word after the key word
-constexpr int kValOffDraft = 8;  // value pair after the key pair
-// Per wave, two slots (current and next chunk) of the chunk constants:
+constexpr int kTableBytes = 2 * kLutBytes;
+// Per wave, one slot of the chunk constants (the next chunk's are staged
+// after the current chunk's products have read it):
 // c1k * 2^S f64[128] | c0k f64[128] | c1v f32[128] | c0v f32[128].
 constexpr int kSlotBytes = 1024 + 1024 + 512 + 512;
-constexpr int kScaleOff = kLutBytes;
-// q as f64 [8 heads][130]: rows padded by 16 bytes so that the 16 lanes of
-// one LDS pass (8 heads x 2 halves) read 16 different bank groups
-constexpr int kQStride = kDim + 2;
-constexpr int kQOff = kScaleOff + kWaves * 2 * kSlotBytes;
-constexpr int kMlOff = kQOff + kHeads * kQStride * 8;   // per wave m, l of 8 heads
-constexpr int kLdsBytes = kMlOff + kWaves * 2 * kHeads * 4;
-static_assert(kWaves * 16 * kDim * 4 <= kLutBytes, "combine area must fit the table space");
+constexpr int kScaleOff = kTableBytes;
+// q as f64 [8 heads][128]; channel d of head h sits at d ^ 2h, so that the
+// lanes of one LDS pass, which read the same channels of different heads,
+// meet different banks
+constexpr int kQStride = kDim;
+constexpr int kQOff = kScaleOff + kWaves * kSlotBytes;
+constexpr int kLdsBytes = kQOff + kHeads * kQStride * 8;
+// after the chunk loop the table space holds the block merge: o of every
+// wave [wave][16 col][128 ch] f32, then m, l of every wave's 8 heads
+constexpr int kMlOff = kWaves * 16 * kDim * 4;
+static_assert(kMlOff + kWaves * 2 * kHeads * 4 <= kTableBytes, "merge area must fit the table space");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 
 struct MfmaTables {
@@ -121,29 +124,29 @@ __device__ __forceinline__ void code_bytes(uint32_t a, uint32_t r, uint32_t &e, 
   o = (a & 0xF0F0F0F0u) | ((r >> 4) & 0x0F0F0F0Fu);
 }
 
-// LDS byte address of table row x.byte[j], copy selected by the lane bits
-// (byte 0 of lb): row * 256 + lane offset.
+// LDS byte address of table row x.byte[j]: byte 0 the lane's copy offset
+// (byte 0 of lb), byte 1 the row, byte 2 the table (byte 2 of lb).
 template <int J>
 __device__ __forceinline__ uint32_t lut_addr(uint32_t x, uint32_t lb) {
-  return __builtin_amdgcn_perm(x, lb, 0x0C0C0000u | ((4u + J) << 8));
+  return __builtin_amdgcn_perm(x, lb, 0x0C020000u | ((4u + J) << 8));
 }
 
-// Table words of elements 4s .. 4s+3 of a code word pair (key words at
-// offset 0, value words at kValOffFull): an i8 key operand (4 bytes per
-// element) or an f16 value operand (hi, lo of each in consecutive k slots).
-template <int S, int kOff>
+// Table words of elements 4s .. 4s+3 of a code word pair (key table or
+// value table by the lane bits): an i8 key operand (4 bytes per element) or
+// an f16 value operand (hi, lo of each in consecutive k slots).
+template <int S>
 __device__ __forceinline__ u32x4 operand_full(uint32_t e, uint32_t o, uint32_t lb, const char *lut) {
   u32x4 w;
-  w[0] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2 * S>(e, lb));
-  w[1] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2 * S>(o, lb));
-  w[2] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2 * S + 1>(e, lb));
-  w[3] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2 * S + 1>(o, lb));
+  w[0] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S>(e, lb));
+  w[1] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S>(o, lb));
+  w[2] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S + 1>(e, lb));
+  w[3] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2 * S + 1>(o, lb));
   return w;
 }
-template <int S, int kOff>
+template <int S>
 __device__ __forceinline__ u32x4 operand_draft(uint32_t a, uint32_t lb, const char *lut) {
-  const uint2 p0 = *reinterpret_cast<const uint2 *>(lut + kOff + lut_addr<2 * S>(a, lb));
-  const uint2 p1 = *reinterpret_cast<const uint2 *>(lut + kOff + lut_addr<2 * S + 1>(a, lb));
+  const uint2 p0 = *reinterpret_cast<const uint2 *>(lut + lut_addr<2 * S>(a, lb));
+  const uint2 p1 = *reinterpret_cast<const uint2 *>(lut + lut_addr<2 * S + 1>(a, lb));
   u32x4 w;
   w[0] = p0.x;
   w[1] = p0.y;
@@ -191,13 +194,12 @@ __device__ __forceinline__ void cut_align(const uint32_t (&w)[NW], uint32_t shif
 }
 
 // Table words of the 4 elements whose table index bytes are x.
-template <int kOff>
 __device__ __forceinline__ u32x4 operand_bytes(uint32_t x, uint32_t lb, const char *lut) {
   u32x4 w;
-  w[0] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<0>(x, lb));
-  w[1] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<1>(x, lb));
-  w[2] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<2>(x, lb));
-  w[3] = *reinterpret_cast<const uint32_t *>(lut + kOff + lut_addr<3>(x, lb));
+  w[0] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<0>(x, lb));
+  w[1] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<1>(x, lb));
+  w[2] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<2>(x, lb));
+  w[3] = *reinterpret_cast<const uint32_t *>(lut + lut_addr<3>(x, lb));
   return w;
 }
 
@@ -320,7 +322,7 @@ struct LaneConst {
   int n, r, lane;
   uint32_t koff, voff, soff;  // lane byte offsets in a K chunk, a V chunk, a scale row
   bool lo;
-  uint32_t lb;         // lane bits of the table address
+  uint32_t lbk, lbv;   // lane bits of key and value table addresses
   uint32_t keep_mask;  // 0 for the high column half, ~0x1FFF for the low one
   uint32_t lvl[3];     // v_perm selectors of this column's W bytes in the 3 level products
   double sm2;          // sm_scale * log2(e)
@@ -409,6 +411,17 @@ __device__ __forceinline__ uint32_t w_bytes(double q, double c1s) {
   return static_cast<uint32_t>(__builtin_fma(q, c1s, kBias)) ^ 0x80808080u;
 }
 
+// A word of lane n < 8 in both lanes n and n + 8 (row rotation by 8 into
+// lanes n >= 8), or of lane n >= 8 in both (into lanes n < 8).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
+                                                            0x128, 0xF, 0xC, false));
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
+                                                            0x128, 0xF, 0x3, false));
+}
+
 // One chunk: scores, online softmax (base 2), value sum.  kBits = 4 reads
 // the 4-bit planes, other values b + (8 - b) streams.
 template <bool kFull, int kBits, class CodesT>
@@ -420,19 +433,17 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
   const double *c0k = c1k + kDim;
   const float *c1v = reinterpret_cast<const float *>(c0k + kDim);
   const float *c0v = c1v + kDim;
-  // value words sit after the key words (full code, cuts) or key pairs (4 + 4 draft)
-  constexpr bool kWordTable = kFull || kBits != 4;
-  constexpr int kVOff = kWordTable ? kValOffFull : kValOffDraft;
 
   // ---- chunk bias sum_d q_d c0k_d in fp64: lane takes channels 32r + 16*lo .. +15 ----
   double bias;
   {
     const int d0 = 32 * r + (lc.lo ? 16 : 0);
+    const int hs = 2 * (n & 7);  // the head's channel swizzle
     const double *qh = q64 + (n & 7) * kQStride + d0;
     double a0 = 0.0, a1 = 0.0;
 #pragma unroll
     for (int k = 0; k < 16; k += 2) {
-      const double2 qq = *reinterpret_cast<const double2 *>(qh + k);
+      const double2 qq = *reinterpret_cast<const double2 *>(qh + (k ^ hs));
       const double2 cc = *reinterpret_cast<const double2 *>(c0k + d0 + k);
       a0 = fma(qq.x, cc.x, a0);
       a1 = fma(qq.y, cc.y, a1);
@@ -467,16 +478,18 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
       cut_key_bytes<kFull, kBits>(cd.ka[0], cd.kr[0], x0);
       cut_key_bytes<kFull, kBits>(cd.ka[1], cd.kr[1], x1);
     }
-    const double *qrow = q64 + (n & 7) * kQStride + 32 * r;
+    // lanes n and n + 8 hold the same query head: each forms the W of two of
+    // a step's four channels (n < 8 channels 0, 1; n >= 8 channels 2, 3) and
+    // takes the other two from its partner
+    const int hs = 2 * (n & 7);
+    const double *qrow = q64 + (n & 7) * kQStride;
+    const int i0 = 32 * r + (lc.lo ? 2 : 0);
 #pragma unroll
     for (int stp = 0; stp < 8; ++stp) {
-      // W of channels 32r + 4stp .. +3 for this lane's query head
-      const double2 c1a = *reinterpret_cast<const double2 *>(c1k + 32 * r + 4 * stp);
-      const double2 c1b = *reinterpret_cast<const double2 *>(c1k + 32 * r + 4 * stp + 2);
-      const double2 qa = *reinterpret_cast<const double2 *>(qrow + 4 * stp);
-      const double2 qb = *reinterpret_cast<const double2 *>(qrow + 4 * stp + 2);
-      const uint32_t wv[4] = {w_bytes(qa.x, c1a.x), w_bytes(qa.y, c1a.y), w_bytes(qb.x, c1b.x),
-                              w_bytes(qb.y, c1b.y)};
+      const double2 c1 = *reinterpret_cast<const double2 *>(c1k + i0 + 4 * stp);
+      const double2 qq = *reinterpret_cast<const double2 *>(qrow + ((i0 + 4 * stp) ^ hs));
+      const uint32_t u0 = w_bytes(qq.x, c1.x), u1 = w_bytes(qq.y, c1.y);
+      const uint32_t wv[4] = {pair_lo(u0), pair_lo(u1), pair_hi(u0), pair_hi(u1)};
       i32x4 ba, bb, bc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -487,23 +500,23 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
       u32x4 a0, a1;
       const int w = stp >> 1;
       if constexpr (kBits != 4) {
-        a0 = operand_bytes<0>(x0[w][stp & 1], lc.lb, lut);
-        a1 = operand_bytes<0>(x1[w][stp & 1], lc.lb, lut);
+        a0 = operand_bytes(x0[w][stp & 1], lc.lbk, lut);
+        a1 = operand_bytes(x1[w][stp & 1], lc.lbk, lut);
       } else if (kFull) {
         if (stp & 1) {
-          a0 = operand_full<1, 0>(e0[w], o0[w], lc.lb, lut);
-          a1 = operand_full<1, 0>(e1[w], o1[w], lc.lb, lut);
+          a0 = operand_full<1>(e0[w], o0[w], lc.lbk, lut);
+          a1 = operand_full<1>(e1[w], o1[w], lc.lbk, lut);
         } else {
-          a0 = operand_full<0, 0>(e0[w], o0[w], lc.lb, lut);
-          a1 = operand_full<0, 0>(e1[w], o1[w], lc.lb, lut);
+          a0 = operand_full<0>(e0[w], o0[w], lc.lbk, lut);
+          a1 = operand_full<0>(e1[w], o1[w], lc.lbk, lut);
         }
       } else {
         if (stp & 1) {
-          a0 = operand_draft<1, 0>(e0[w], lc.lb, lut);
-          a1 = operand_draft<1, 0>(e1[w], lc.lb, lut);
+          a0 = operand_draft<1>(e0[w], lc.lbk, lut);
+          a1 = operand_draft<1>(e1[w], lc.lbk, lut);
         } else {
-          a0 = operand_draft<0, 0>(e0[w], lc.lb, lut);
-          a1 = operand_draft<0, 0>(e1[w], lc.lb, lut);
+          a0 = operand_draft<0>(e0[w], lc.lbk, lut);
+          a1 = operand_draft<0>(e1[w], lc.lbk, lut);
         }
       }
       const i32x4 y0 = __builtin_bit_cast(i32x4, a0), y1 = __builtin_bit_cast(i32x4, a1);
@@ -535,13 +548,12 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
     const int l6 = hi(sa0[i], sa1[i]), l5 = lo(sa1[i], sa0[i]);
     const int l4 = hi(sb0[i], sb1[i]), l3 = lo(sb1[i], sb0[i]);
     const int l2 = hi(sc0[i], sc1[i]), l1 = lo(sc1[i], sc0[i]);
-    // sum_L C_L 2^(8L) / 2^8 by Horner (each |C_L| < 2^23)
-    double t = static_cast<double>(l6);
-    t = fma(t, 256.0, static_cast<double>(l5));
-    t = fma(t, 256.0, static_cast<double>(l4));
-    t = fma(t, 256.0, static_cast<double>(l3));
-    t = fma(t, 256.0, static_cast<double>(l2));
-    t = fma(t, 256.0, static_cast<double>(l1));
+    // sum_L C_L 2^(8L) / 2^8.  C_L sums at most 128 * min(L + 1, 7 - L) byte
+    // products of magnitude <= 2^14, so C_6 * 2^8 + C_5, C_4 * 2^8 + C_3 and
+    // C_2 * 2^8 + C_1 stay inside int32, and the rest is fp64.
+    const int a = l6 * 256 + l5, b2 = l4 * 256 + l3, c2 = l2 * 256 + l1;
+    const double t = fma(fma(static_cast<double>(a), 65536.0, static_cast<double>(b2)), 65536.0,
+                         static_cast<double>(c2));
     sc2[i] = fma(t, scale2, bias2);
     cmax = fmaxf(cmax, static_cast<float>(sc2[i]));
   }
@@ -609,16 +621,16 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
         xa = (xa << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 0);
         xb = (xb << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 4);
       }
-      y0 = __builtin_bit_cast(half8, operand_bytes<kVOff>(xa, lc.lb, lut));
-      y1 = __builtin_bit_cast(half8, operand_bytes<kVOff>(xb, lc.lb, lut));
+      y0 = __builtin_bit_cast(half8, operand_bytes(xa, lc.lbv, lut));
+      y1 = __builtin_bit_cast(half8, operand_bytes(xb, lc.lbv, lut));
     } else if (kFull) {
       uint32_t e, o;
       code_bytes(cd.va[ct], cd.vr[ct], e, o);
-      y0 = __builtin_bit_cast(half8, operand_full<0, kVOff>(e, o, lc.lb, lut));
-      y1 = __builtin_bit_cast(half8, operand_full<1, kVOff>(e, o, lc.lb, lut));
+      y0 = __builtin_bit_cast(half8, operand_full<0>(e, o, lc.lbv, lut));
+      y1 = __builtin_bit_cast(half8, operand_full<1>(e, o, lc.lbv, lut));
     } else {
-      y0 = __builtin_bit_cast(half8, operand_draft<0, kVOff>(cd.va[ct], lc.lb, lut));
-      y1 = __builtin_bit_cast(half8, operand_draft<1, kVOff>(cd.va[ct], lc.lb, lut));
+      y0 = __builtin_bit_cast(half8, operand_draft<0>(cd.va[ct], lc.lbv, lut));
+      y1 = __builtin_bit_cast(half8, operand_draft<1>(cd.va[ct], lc.lbv, lut));
     }
     floatx4 ov = {0.0f, 0.0f, 0.0f, 0.0f};
     ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pa0, ov, 0, 0, 0);
@@ -666,10 +678,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   lc.voff = static_cast<uint32_t>(lc.n * 16 + lc.r * 4);
   lc.soff = static_cast<uint32_t>(lc.lane * 8);
   lc.keep_mask = lc.lo ? 0xFFFFE000u : 0u;
-  // (key word, value word) copies for the full code and for every cut's
-  // index bytes; (key pair, value pair) copies for the 4 + 4 draft
+  // word copies for the full code and for every cut's index bytes, pair
+  // copies for the 4 + 4 draft; the value table sits 64 KiB up
   constexpr bool kWordTable = kFull || kBits != 4;
-  lc.lb = kWordTable ? static_cast<uint32_t>((lc.lane & 31) * 8) : static_cast<uint32_t>((lc.lane & 15) * 16);
+  lc.lbk = kWordTable ? static_cast<uint32_t>(lc.lane * 4) : static_cast<uint32_t>((lc.lane & 31) * 8);
+  lc.lbv = lc.lbk | static_cast<uint32_t>(kLutBytes);
   // W bytes of this column's levels: 6, 4, 2 (n < 8) or 5, 3, 1 (n >= 8)
   lc.lvl[0] = lc.lo ? 0x02030C0Cu : 0x030C0C0Cu;
   lc.lvl[1] = lc.lo ? 0x00010203u : 0x0102030Cu;
@@ -699,7 +712,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   if (ce > p1 * kChunks) ce = p1 * kChunks;
   if (cb > ce) cb = ce;
 
-  char *slots = smem + kScaleOff + w * 2 * kSlotBytes;
+  char *slot = smem + kScaleOff + w * kSlotBytes;
   // page of chunk ci, or -1 when the block table marks it absent
   auto page_of = [&](int ci) -> long long {
     const int lp = ci >> 3;
@@ -790,12 +803,15 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
     load_chunk(cds[d], pgs[d], cb + d);
   }
 
-  // ---- tables (replicated rows) ----
+  // ---- tables (replicated rows): thread t fills row t % 256 of the key
+  // table (t < 256) or of the value table ----
   {
-    const u32x4 v = kWordTable ? u32x4{kw0, tw0, kw0, tw0} : u32x4{kw0, kw1, tw0, tw1};
-    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + (tid & 255) * 256 + (tid >> 8) * 128);
+    const bool val = tid >= 256;
+    const uint32_t w0 = val ? tw0 : kw0, w1 = val ? tw1 : kw1;
+    const u32x4 v = kWordTable ? u32x4{w0, w0, w0, w0} : u32x4{w0, w1, w0, w1};
+    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + (val ? kLutBytes : 0) + (tid & 255) * 256);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k] = v;
+    for (int k = 0; k < 16; ++k) dst[k] = v;
   }
   // ---- q of this lane's head, channels 32r .. 32r+31 (exact bf16 values) ----
   float qv[32];
@@ -823,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float x = second ? qv[16 + k] : qv[k];
-      q64[w * kQStride + d0 + k] = static_cast<double>(x);
+      q64[w * kQStride + ((d0 + k) ^ (2 * w))] = static_cast<double>(x);
     }
   }
   __syncthreads();
@@ -840,24 +856,26 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   for (int ct = 0; ct < 8; ++ct) st.acc[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (cb < ce) {
-    double ks0 = 1.0, ks1 = 1.0;  // score weights 2^-(S + 22) of LDS slots 0 and 1
-    ks0 = scale_stage(scs[0], slots, lc.lane, qmax);
-    // one chunk c held in buffers J = (c - cb) % NB, constants in LDS slot (c - cb) & 1
+    // the chunk's score weight 2^-(S + 22); the slot holds chunk c's
+    // constants during its step and chunk c + 1's after it (the products
+    // of chunk c have read the slot by then: a wave's LDS accesses complete
+    // in order)
+    double ks = scale_stage(scs[0], slot, lc.lane, qmax);
+    // one chunk c held in buffers J = (c - cb) % NB
     auto step = [&](auto jc, int c) {
       constexpr int J = decltype(jc)::value;
       constexpr int J1 = (J + 1) % NB, JD = (J + D) % NB;
-      const int slot = (c - cb) & 1;
       const long long cur = pgs[J];
       pgs[J] = page_in_run(c + D + 1);  // buffer J next holds chunk c + NB = c + D + 1
       load_scales(scs[J], kp, vp, tile_of(pgs[J]), chunk_of(pgs[J], c + D + 1), lc.soff);
       load_chunk(cds[JD], pgs[JD], c + D);
       if (cur >= 0) {
         wave_lds_sync();
-        compute_chunk<kFull, kBits>(cds[J], slots + slot * kSlotBytes, slot ? ks1 : ks0, q64, lc, lut,
-                                    st, srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
+        compute_chunk<kFull, kBits>(cds[J], slot, ks, q64, lc, lut, st,
+                                    srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
       }
-      const double k = scale_stage(scs[J1], slots + (slot ^ 1) * kSlotBytes, lc.lane, qmax);
-      if (slot) ks0 = k; else ks1 = k;
+      wave_lds_sync();
+      ks = scale_stage(scs[J1], slot, lc.lane, qmax);
     };
     for (int c = cb; c < ce; c += NB) {
       step(std::integral_constant<int, 0>(), c);
