@@ -116,9 +116,10 @@ def summarize(kind, db_dir, out_path, command):
                         "select kernel_name, value from counters_collection where counter_name = ?",
                         (ctr,)):
                     per.setdefault(short(name), {}).setdefault(ctr, []).append(val)
-                    # the 256 MiB probe copy runs as a few large blit dispatches;
-                    # other copies of the run are tiny
-                    if "copyBuffer" in name and val > 4096.0:
+                    # the 256 MiB probe copy runs as one or a few large blit
+                    # dispatches; the other copies of a run (input uploads,
+                    # slices of a pool) move at most 64 MiB each
+                    if "copyBuffer" in name and val > 65536.0:
                         probe[ctr] = probe.get(ctr, 0.0) + val
         avg = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in per.items()}
         if "FETCH_SIZE" not in probe or "WRITE_SIZE" not in probe:
@@ -132,9 +133,11 @@ def summarize(kind, db_dir, out_path, command):
             raise SystemExit("copy probe counters off by more than 4x (fetch scale %.3g, write "
                              "scale %.3g): was another large copy in the run?" % (f_fetch, f_write))
         enc = [k for k in avg if k.startswith("encode_kv_kernel")]
-        enc_fetch = sum(avg[k]["FETCH_SIZE"] for k in enc) / len(enc)
-        enc_write = sum(avg[k]["WRITE_SIZE"] for k in enc) / len(enc)
+        enc_fetch = sum(avg[k]["FETCH_SIZE"] for k in enc) / len(enc) if enc else float("nan")
+        enc_write = sum(avg[k]["WRITE_SIZE"] for k in enc) / len(enc) if enc else float("nan")
         traffic = (enc_fetch * f_fetch + enc_write * f_write) * 1024.0
+        scaled = {k: (v.get("FETCH_SIZE", 0.0) * f_fetch + v.get("WRITE_SIZE", 0.0) * f_write) * 1024.0
+                  for k, v in avg.items()}
         lines += [
             "encoder_source_sha1: %s" % source_sha1(ENCODER_SOURCE),
             "copy_probe: device copy of %d bytes; FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB in total" % (
@@ -145,11 +148,12 @@ def summarize(kind, db_dir, out_path, command):
             "encode_write_kib_per_dispatch: %.1f" % enc_write,
             "traffic_bytes_per_launch: %.0f" % traffic,
             "",
-            "%-44s %16s %16s" % ("kernel", "FETCH_SIZE KiB", "WRITE_SIZE KiB"),
+            "%-44s %16s %16s %18s" % ("kernel", "FETCH_SIZE KiB", "WRITE_SIZE KiB",
+                                      "HBM bytes (scaled)"),
         ]
         for k in sorted(avg):
-            lines.append("%-44s %16.1f %16.1f" % (k[:44], avg[k].get("FETCH_SIZE", float("nan")),
-                                                  avg[k].get("WRITE_SIZE", float("nan"))))
+            lines.append("%-44s %16.1f %16.1f %18.0f" % (k[:44], avg[k].get("FETCH_SIZE", float("nan")),
+                                                         avg[k].get("WRITE_SIZE", float("nan")), scaled[k]))
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -676,7 +680,12 @@ def main():
         leg = {"tiny": lambda: tiny_leg(dev, stream), "qwen3_235b_128k": lambda: qwen3_leg(dev, stream),
                "batched64x16k": lambda: batched_leg(dev, stream),
                "progressive32x64k": lambda: progressive_leg(dev)}[args.config_only]
-        print(json.dumps(leg()), flush=True)
+        res = leg()
+        if args.copy_probe:
+            a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+            torch.empty_like(a).copy_(a)
+            torch.cuda.synchronize()
+        print(json.dumps(res), flush=True)
         return
     if args.progressive and args.gpus == 1 and world == 1:
         progressive_main(args)

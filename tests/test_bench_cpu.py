@@ -48,6 +48,15 @@ def test_traffic_scales_the_counters_by_the_copy_probe(tmp_path):
 
 def test_other_large_copies_are_not_taken_for_the_probe(tmp_path):
     # six copies of 1 GiB beside the probe would scale the counters 25x down
+    # (copies of up to 64 MiB, like pool uploads, are not taken for the probe)
     with pytest.raises(SystemExit):
         bench.summarize("pmc", _runs(tmp_path, extra_copies=[1 << 20] * 6),
                         str(tmp_path / "summary.txt"), "test")
+
+
+def test_pool_sized_copies_are_not_taken_for_the_probe(tmp_path):
+    out = str(tmp_path / "summary.txt")
+    bench.summarize("pmc", _runs(tmp_path, extra_copies=[32 << 10] * 300), out, "test")
+    kv = dict(line.split(":", 1) for line in open(out) if ":" in line)
+    assert float(kv["fetch_scale"]) == pytest.approx(2.0)
+    assert float(kv["write_scale"]) == pytest.approx(1.0)
