@@ -279,6 +279,35 @@ def test_qwen3_235b_layer_encode(lynx):
         check_encode(lynx, x, role)
 
 
+# The same shape at full size in the benchmark's launch configuration: the
+# 94 layers' pages in one K and one V pool drawn on the device (12.6 GB
+# each), encoded by one launch; pages of the first, middle and last layers
+# (and a few drawn at random) checked against the oracle one by one.
+def test_qwen3_235b_all_layers_one_launch_sampled_pages(lynx):
+    w = synth.WORKLOADS["qwen3_235b_128k"]
+    P = w.pages
+    shape = (w.layers * P, 256, w.kv_heads, w.head_dim)
+    k = torch.empty(shape, dtype=torch.int16, device="cuda")
+    v = torch.empty(shape, dtype=torch.int16, device="cuda")
+    for layer in range(w.layers):
+        k[layer * P:(layer + 1) * P] = synth.device_kv_pages(w, layer, 0, 0)
+        v[layer * P:(layer + 1) * P] = synth.device_kv_pages(w, layer, 1, 0)
+    print("qwen3 pools drawn: %d pages" % (w.layers * P), flush=True)
+    pk, pv = lynx.quantize_kv_pages(k, v)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(94)
+    picks = [(0, 0), (0, P - 1), (w.layers // 2, P // 2), (w.layers - 1, 0), (w.layers - 1, P - 1)]
+    picks += [(int(a), int(b)) for a, b in zip(rng.integers(0, w.layers, 3), rng.integers(0, P, 3))]
+    for layer, page in picks:
+        g = layer * P + page
+        for x_dev, pl, role in ((k, pk, 0), (v, pv, 1)):
+            print("qwen3 layer %d page %d role %d" % (layer, page, role), flush=True)
+            x = x_dev[g:g + 1].cpu().numpy().view(np.uint16)
+            check_encode(lynx, x, role, pl=lynx.planes_view(pl, g, 1))
+    del k, v, pk, pv
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # Progressive-arrival shape: one layer of 64K context, both variants
 # ---------------------------------------------------------------------------
