@@ -269,6 +269,45 @@ def test_batched_64x16k_sampled(lynx):
                 assert np.array_equal(got[b], got[b % 2])
 
 
+# The benchmark's launch configuration: 64 distinct requests drawn on the
+# device into contiguous K and V pools (no block table), encoded by one
+# launch, one decode launch per variant over the whole batch; the first,
+# a middle and the last request checked against the oracle.
+def test_batched_64x16k_bench_configuration_sampled(lynx):
+    w = synth.WORKLOADS["batched64x16k"]
+    P = w.pages
+    shape = (w.batch * P, 256, w.kv_heads, w.head_dim)
+    k = torch.empty(shape, dtype=torch.int16, device="cuda")
+    v = torch.empty(shape, dtype=torch.int16, device="cuda")
+    for r in range(w.batch):
+        k[r * P:(r + 1) * P] = synth.device_kv_pages(w, 0, 0, r)
+        v[r * P:(r + 1) * P] = synth.device_kv_pages(w, 0, 1, r)
+    pk, pv = lynx.quantize_kv_pages(k, v)
+    torch.cuda.synchronize()
+    sampled = (0, w.batch // 2 - 1, w.batch - 1)
+    encs = {}
+    for r in sampled:
+        sl = slice(r * P, (r + 1) * P)
+        print("batched request %d: encode parity" % r, flush=True)
+        _, ek, _, _ = check_encode(lynx, k[sl].cpu().numpy().view(np.uint16), 0,
+                                   pl=lynx.planes_view(pk, r * P, P))
+        _, ev, _, _ = check_encode(lynx, v[sl].cpu().numpy().view(np.uint16), 1,
+                                   pl=lynx.planes_view(pv, r * P, P))
+        encs[r] = (ek, ev)
+    del k, v
+    for aligned in (True, False):
+        q = synth.queries(w, key_aligned=aligned)
+        for full in (False, True):
+            got = run_gpu_attention(lynx, q, pk, pv, P, full)
+            for r in sampled:
+                ek, ev = encs[r]
+                ref = oracle_attention_for(ek, ev, q[r:r + 1], [list(range(P))], full)
+                check_attention(got[r], ref[0], "batched (bench layout) request %d full=%s aligned=%s"
+                                % (r, full, aligned))
+    del pk, pv
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # Qwen3-235B-A22B shape: encode of one layer (512 pages x 4 heads), K and V
 # ---------------------------------------------------------------------------
