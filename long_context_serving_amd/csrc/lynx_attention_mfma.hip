@@ -41,10 +41,13 @@
 // whose probabilities lane (n, r) provides: tokens 4r..4r+3 (step 0) and
 // 16+4r..16+4r+3 (step 1).
 //
-// Work split: one workgroup of 8 waves (one per CU: the replicated table
-// fills 64 KiB of LDS) per (request, KV head, run of pages); each wave
-// streams a contiguous run of chunks with the next chunk's codes and scales
-// in flight while the current one is computed.  The block merges its waves
+// Work split: one workgroup of 8 waves (one per CU: the registers of a
+// chunk in flight allow 2 waves per SIMD) per (request, KV head, run of
+// pages); each wave streams a contiguous run of chunks with the next
+// chunk's codes and scales in flight while the current one is computed.
+// Between chunks a wave stages the next chunk's constants in LDS, the W
+// words of all its (channel, head) pairs among them, so that a score step
+// only reads its four W words.  The block merges its waves
 // through LDS and writes the output itself when one run covers the request;
 // otherwise it writes a partial (base-2 max m, sum l, unnormalised o) and a
 // second, small kernel merges the runs exactly.
@@ -76,31 +79,36 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kHeads = 8;  // MFMA columns per part
 constexpr float kSlack = 8.0f;  // log2 of the largest probability before rescaling
 
-// LDS map in bytes.  Two tables of 256 rows x 256 bytes, one row per code
-// byte: the key table (Y words) at 0 and the value table (fp16 pair words)
-// at 64 KiB.  Full code and cuts: 64 copies of the row's word, copy l for
-// lane l; 4 + 4 draft (row = two anchor nibbles, element 2j in the low
-// one): 32 copies of the pair of words, copy l % 32 for lane l.  So a
-// wave's table reads never share a bank.  The lane bits of a value read
-// carry the 64 KiB offset in their third byte.
-constexpr int kLutBytes = 256 * 256;
-constexpr int kTableBytes = 2 * kLutBytes;
+// LDS map in bytes.  The tables: 256 rows of 256 bytes, one row per code
+// byte; a row's first 128 bytes hold the key table word (Y), its last 128
+// the value table word (fp16 pair).  Full code and cuts: 32 copies of the
+// word, copy l % 32 for lane l; 4 + 4 draft (row = two anchor nibbles,
+// element 2j in the low one): 16 copies of the pair of words, copy l % 16.
+// A wave reads a table 128 bytes per pass (32 words or 16 pairs), so the
+// lanes of one pass never share a bank.  The lane bits of a value read
+// carry the 128-byte offset.
+constexpr int kValueHalf = 128;
+constexpr int kTableBytes = 256 * 256;
 // Per wave, one slot of the chunk constants (the next chunk's are staged
-// after the current chunk's products have read it):
-// c1k * 2^S f64[128] | c0k f64[128] | c1v f32[128] | c0v f32[128].
-constexpr int kSlotBytes = 1024 + 1024 + 512 + 512;
+// after the current chunk's products have read it): the W words of the
+// score products, [8 heads][32 units of 4 channels + 1 pad unit] x 16 B
+// (the pad turns each head's row by 4 banks, so the 8 heads of one read
+// pass meet different banks), then c0k f64[128] | c1v f32[128] | c0v f32[128].
+constexpr int kWRowBytes = 33 * 16;
+constexpr int kWBytes = kHeads * kWRowBytes;
+constexpr int kSlotBytes = kWBytes + 1024 + 512 + 512;
 constexpr int kScaleOff = kTableBytes;
-// q as f64 [8 heads][128]; channel d of head h sits at d ^ 2h, so that the
-// lanes of one LDS pass, which read the same channels of different heads,
-// meet different banks
-constexpr int kQStride = kDim;
+// q as f64 [8 heads][130]: rows padded by 16 bytes, which turns each head's
+// row by 4 banks, so the lanes of one LDS pass, which read the same
+// channels of different heads, meet different banks
+constexpr int kQStride = kDim + 2;
 constexpr int kQOff = kScaleOff + kWaves * kSlotBytes;
 constexpr int kLdsBytes = kQOff + kHeads * kQStride * 8;
-// after the chunk loop the table space holds the block merge: o of every
-// wave [wave][16 col][128 ch] f32, then m, l of every wave's 8 heads
+// after the chunk loop the table and slot space holds the block merge: o of
+// every wave [wave][16 col][128 ch] f32, then m, l of every wave's 8 heads
 constexpr int kMlOff = kWaves * 16 * kDim * 4;
-static_assert(kMlOff + kWaves * 2 * kHeads * 4 <= kTableBytes, "merge area must fit the table space");
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(kMlOff + kWaves * 2 * kHeads * 4 <= kQOff, "merge area must fit the table and slot space");
+static_assert(kSlotBytes % 16 == 0 && kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 
 struct MfmaTables {
   uint32_t full[256];   // code byte (a << 4 | r) -> fp16 hi | fp16 lo << 16 of yhat
@@ -125,10 +133,10 @@ __device__ __forceinline__ void code_bytes(uint32_t a, uint32_t r, uint32_t &e, 
 }
 
 // LDS byte address of table row x.byte[j]: byte 0 the lane's copy offset
-// (byte 0 of lb), byte 1 the row, byte 2 the table (byte 2 of lb).
+// and table half (byte 0 of lb), byte 1 the row.
 template <int J>
 __device__ __forceinline__ uint32_t lut_addr(uint32_t x, uint32_t lb) {
-  return __builtin_amdgcn_perm(x, lb, 0x0C020000u | ((4u + J) << 8));
+  return __builtin_amdgcn_perm(x, lb, 0x0C0C0000u | ((4u + J) << 8));
 }
 
 // Table words of elements 4s .. 4s+3 of a code word pair (key table or
@@ -270,14 +278,26 @@ __device__ __forceinline__ void load_scales(Scales &sc, const PlanesArg &kp, con
   sc.rgv = f2(vp.page_range, pb);
 }
 
+// W word of one (channel, head) for the level products: the floor of
+// w * 2^S (here w * 2^S + 0x80808080, so the truncating conversion is a
+// floor and every byte carries a +128 bias), with the bias of each byte
+// flipped back, is the 4-byte signed split (byte j = W_j); each product
+// then takes the bytes its column's level needs.
+__device__ __forceinline__ uint32_t w_bytes(double q, double c1s) {
+  constexpr double kBias = 2155905152.0;  // 0x80808080
+  return static_cast<uint32_t>(__builtin_fma(q, c1s, kBias)) ^ 0x80808080u;
+}
+
 // Chunk constants into an LDS slot.  c1k = rg * s is formed in fp64
 // (exact) and scaled by 2^S, S = 29 - e with e the exponent of qmax *
 // max c1k (qmax = largest |q| of the group), so every |q * c1k * 2^S| stays
 // below 2^30 (the fp32 maximum can undercut the fp64 one by an ulp, which
-// still leaves it below 2^31 - 2^24, the range of a 4-byte signed split);
-// returns 2^-(S + 22), the weight of the level sum assembled in
-// compute_chunk.
-__device__ __forceinline__ double scale_stage(const Scales &sc, char *slot, int lane, float qmax) {
+// still leaves it below 2^31 - 2^24, the range of a 4-byte signed split).
+// Lane l forms the W words of channels 2l, 2l + 1 for the 8 heads (q from
+// the block's f64 copy) and c0k, c1v, c0v of its two channels; returns
+// 2^-(S + 22), the weight of the level sum assembled in compute_chunk.
+__device__ __forceinline__ double scale_stage(const Scales &sc, char *slot, int lane, float qmax,
+                                              const double *q64) {
   const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // bound only
   const float bound = qmax * wave_max(fmaxf(c1a, c1b));
   int S = 0;
@@ -290,12 +310,19 @@ __device__ __forceinline__ double scale_stage(const Scales &sc, char *slot, int 
   }
   const double ks = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + S) << 52);
   const double inv = __builtin_bit_cast(double, static_cast<uint64_t>(1023 - S - 22) << 52);
-  double *c1k = reinterpret_cast<double *>(slot);
-  double *c0k = c1k + kDim;
+  const double c1x = static_cast<double>(sc.rgk.x) * sc.sk.x * ks;
+  const double c1y = static_cast<double>(sc.rgk.y) * sc.sk.y * ks;
+  // W of channels 2l, 2l + 1 sit in unit l / 2 of each head's row
+  char *wdst = slot + (lane >> 1) * 16 + (lane & 1) * 8;
+  const double *qsrc = q64 + 2 * lane;
+#pragma unroll
+  for (int hh = 0; hh < kHeads; ++hh) {
+    const double2 qq = *reinterpret_cast<const double2 *>(qsrc + hh * kQStride);
+    *reinterpret_cast<uint2 *>(wdst + hh * kWRowBytes) = make_uint2(w_bytes(qq.x, c1x), w_bytes(qq.y, c1y));
+  }
+  double *c0k = reinterpret_cast<double *>(slot + kWBytes);
   float *c1v = reinterpret_cast<float *>(c0k + kDim);
   float *c0v = c1v + kDim;
-  reinterpret_cast<double2 *>(c1k)[lane] =
-      make_double2(static_cast<double>(sc.rgk.x) * sc.sk.x * ks, static_cast<double>(sc.rgk.y) * sc.sk.y * ks);
   reinterpret_cast<double2 *>(c0k)[lane] =
       make_double2(static_cast<double>(sc.mnk.x) + static_cast<double>(sc.rgk.x) * sc.muk.x,
                    static_cast<double>(sc.mnk.y) + static_cast<double>(sc.rgk.y) * sc.muk.y);
@@ -401,27 +428,6 @@ __device__ __forceinline__ void cut_key_bytes(const uint32_t (&a)[B], const uint
     }
 }
 
-// W bytes of one element for the level products: the floor of w * 2^S
-// (here w * 2^S + 0x80808080, so the truncating conversion is a floor and
-// every byte carries a +128 bias), with the bias of each byte flipped back,
-// is the 4-byte signed split (byte j = W_j); each product then takes the
-// bytes its column's level needs.
-__device__ __forceinline__ uint32_t w_bytes(double q, double c1s) {
-  constexpr double kBias = 2155905152.0;  // 0x80808080
-  return static_cast<uint32_t>(__builtin_fma(q, c1s, kBias)) ^ 0x80808080u;
-}
-
-// A word of lane n < 8 in both lanes n and n + 8 (row rotation by 8 into
-// lanes n >= 8), or of lane n >= 8 in both (into lanes n < 8).
-__device__ __forceinline__ uint32_t pair_lo(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
-                                                            0x128, 0xF, 0xC, false));
-}
-__device__ __forceinline__ uint32_t pair_hi(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
-                                                            0x128, 0xF, 0x3, false));
-}
-
 // One chunk: scores, online softmax (base 2), value sum.  kBits = 4 reads
 // the 4-bit planes, other values b + (8 - b) streams.
 template <bool kFull, int kBits, class CodesT>
@@ -429,8 +435,7 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
                                               const double *q64, const LaneConst &lc,
                                               const char *lut, RunState &st, float *srow) {
   const int n = lc.n, r = lc.r;
-  const double *c1k = reinterpret_cast<const double *>(slot);
-  const double *c0k = c1k + kDim;
+  const double *c0k = reinterpret_cast<const double *>(slot + kWBytes);
   const float *c1v = reinterpret_cast<const float *>(c0k + kDim);
   const float *c0v = c1v + kDim;
 
@@ -438,12 +443,11 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
   double bias;
   {
     const int d0 = 32 * r + (lc.lo ? 16 : 0);
-    const int hs = 2 * (n & 7);  // the head's channel swizzle
     const double *qh = q64 + (n & 7) * kQStride + d0;
     double a0 = 0.0, a1 = 0.0;
 #pragma unroll
     for (int k = 0; k < 16; k += 2) {
-      const double2 qq = *reinterpret_cast<const double2 *>(qh + (k ^ hs));
+      const double2 qq = *reinterpret_cast<const double2 *>(qh + k);
       const double2 cc = *reinterpret_cast<const double2 *>(c0k + d0 + k);
       a0 = fma(qq.x, cc.x, a0);
       a1 = fma(qq.y, cc.y, a1);
@@ -478,18 +482,12 @@ __device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot
       cut_key_bytes<kFull, kBits>(cd.ka[0], cd.kr[0], x0);
       cut_key_bytes<kFull, kBits>(cd.ka[1], cd.kr[1], x1);
     }
-    // lanes n and n + 8 hold the same query head: each forms the W of two of
-    // a step's four channels (n < 8 channels 0, 1; n >= 8 channels 2, 3) and
-    // takes the other two from its partner
-    const int hs = 2 * (n & 7);
-    const double *qrow = q64 + (n & 7) * kQStride;
-    const int i0 = 32 * r + (lc.lo ? 2 : 0);
+    // W words of channels 32r + 4 stp .. + 3 of the lane's head (lanes n
+    // and n + 8 read the same unit)
+    const char *wrow = slot + (n & 7) * kWRowBytes + r * 128;
 #pragma unroll
     for (int stp = 0; stp < 8; ++stp) {
-      const double2 c1 = *reinterpret_cast<const double2 *>(c1k + i0 + 4 * stp);
-      const double2 qq = *reinterpret_cast<const double2 *>(qrow + ((i0 + 4 * stp) ^ hs));
-      const uint32_t u0 = w_bytes(qq.x, c1.x), u1 = w_bytes(qq.y, c1.y);
-      const uint32_t wv[4] = {pair_lo(u0), pair_lo(u1), pair_hi(u0), pair_hi(u1)};
+      const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + stp * 16);
       i32x4 ba, bb, bc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -681,8 +679,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   // word copies for the full code and for every cut's index bytes, pair
   // copies for the 4 + 4 draft; the value table sits 64 KiB up
   constexpr bool kWordTable = kFull || kBits != 4;
-  lc.lbk = kWordTable ? static_cast<uint32_t>(lc.lane * 4) : static_cast<uint32_t>((lc.lane & 31) * 8);
-  lc.lbv = lc.lbk | static_cast<uint32_t>(kLutBytes);
+  lc.lbk = kWordTable ? static_cast<uint32_t>((lc.lane & 31) * 4) : static_cast<uint32_t>((lc.lane & 15) * 8);
+  lc.lbv = lc.lbk | static_cast<uint32_t>(kValueHalf);
   // W bytes of this column's levels: 6, 4, 2 (n < 8) or 5, 3, 1 (n >= 8)
   lc.lvl[0] = lc.lo ? 0x02030C0Cu : 0x030C0C0Cu;
   lc.lvl[1] = lc.lo ? 0x00010203u : 0x0102030Cu;
@@ -803,15 +801,15 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
     load_chunk(cds[d], pgs[d], cb + d);
   }
 
-  // ---- tables (replicated rows): thread t fills row t % 256 of the key
-  // table (t < 256) or of the value table ----
+  // ---- tables (replicated words): thread t fills the key half (t < 256)
+  // or the value half of row t % 256 ----
   {
     const bool val = tid >= 256;
     const uint32_t w0 = val ? tw0 : kw0, w1 = val ? tw1 : kw1;
     const u32x4 v = kWordTable ? u32x4{w0, w0, w0, w0} : u32x4{w0, w1, w0, w1};
-    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + (val ? kLutBytes : 0) + (tid & 255) * 256);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + (val ? kValueHalf : 0) + (tid & 255) * 256);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) dst[k] = v;
+    for (int k = 0; k < 8; ++k) dst[k] = v;
   }
   // ---- q of this lane's head, channels 32r .. 32r+31 (exact bf16 values) ----
   float qv[32];
@@ -839,7 +837,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float x = second ? qv[16 + k] : qv[k];
-      q64[w * kQStride + ((d0 + k) ^ (2 * w))] = static_cast<double>(x);
+      q64[w * kQStride + d0 + k] = static_cast<double>(x);
     }
   }
   __syncthreads();
@@ -860,7 +858,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
     // constants during its step and chunk c + 1's after it (the products
     // of chunk c have read the slot by then: a wave's LDS accesses complete
     // in order)
-    double ks = scale_stage(scs[0], slot, lc.lane, qmax);
+    double ks = scale_stage(scs[0], slot, lc.lane, qmax, q64);
     // one chunk c held in buffers J = (c - cb) % NB
     auto step = [&](auto jc, int c) {
       constexpr int J = decltype(jc)::value;
@@ -875,7 +873,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
                                     srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
       }
       wave_lds_sync();
-      ks = scale_stage(scs[J1], slot, lc.lane, qmax);
+      ks = scale_stage(scs[J1], slot, lc.lane, qmax, q64);
     };
     for (int c = cb; c < ce; c += NB) {
       step(std::integral_constant<int, 0>(), c);
