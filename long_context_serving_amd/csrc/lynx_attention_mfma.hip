@@ -937,6 +937,616 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   }
 }
 
+// ---- K/V wave pairs (4 + 4 planes) --------------------------------------------
+// The 4 + 4 planes take a second form of the kernel with the roles of a
+// chunk split between two waves, so that each holds half the registers and a
+// CU runs 16 waves (4 per SIMD) instead of 8.  Wave p < 8 (the K wave of pair
+// p) streams the key codes and scales of its run of chunks and computes each
+// chunk's scores, running maximum and probabilities; wave p + 8 (the V wave)
+// streams the value codes and scales of the same run and accumulates the
+// value sums one chunk behind.  The K wave hands each chunk's probabilities,
+// rescale factor and probability sum to its V wave through LDS (two buffers
+// per pair); the block steps in lockstep, one barrier per chunk step.  The
+// arithmetic of every score, probability and value product is that of
+// attn_mfma_kernel, so the outputs are the same.
+constexpr int kPairs = 8;
+constexpr int kPThreads = 128 * kPairs;
+constexpr int kKSlotBytes = kWBytes + 1024;  // W words | c0k f64[128]
+constexpr int kVSlotBytes = 512 + 512;       // c1v f32[128] | c0v f32[128]
+// probabilities [tile][r][head][4 tokens] f32 (lane (n, r) of the K wave
+// holds tokens 16 tile + 4r .. + 3 of head n % 8, tile = n / 8), then the
+// rescale factor and the probability sum of the 8 heads
+constexpr int kHandBytes = 1024 + 32 + 32;
+constexpr int kPKSlotOff = kTableBytes;
+constexpr int kPVSlotOff = kPKSlotOff + kPairs * kKSlotBytes;
+constexpr int kPHandOff = kPVSlotOff + kPairs * kVSlotBytes;
+constexpr int kPQOff = kPHandOff + kPairs * 2 * kHandBytes;
+constexpr int kPLdsBytes = kPQOff + kHeads * kQStride * 8;
+// after the chunk loop: o of every pair [pair][16 col][128 ch] f32 over the
+// table space, then m, l of every pair's 8 heads
+constexpr int kPMlOff = kPairs * 16 * kDim * 4;
+static_assert(kPMlOff + kPairs * 2 * kHeads * 4 <= kPQOff, "merge area must fit below q");
+static_assert(kKSlotBytes % 16 == 0 && kHandBytes % 16 == 0 && kPLdsBytes <= 160 * 1024,
+              "LDS budget of one workgroup");
+
+struct KCodes {
+  u32x4 ka[2], kr[2];  // tile t: anchor / residual of channels 32r.. of token 16t + n
+};
+struct VCodes {
+  uint32_t va[8], vr[8];  // word r of channel 16ct + n
+};
+struct KScales {
+  float2 mnk, rgk, muk, sk;  // channels 2l, 2l+1
+};
+struct VScales {
+  float2 mnv, rgv, muv, sv;
+};
+
+template <bool kFull>
+__device__ __forceinline__ void load_kcodes(KCodes &cd, const PlanesArg &kp, size_t tile, int c,
+                                            uint32_t koff) {
+  const size_t cbytes = tile * kPlaneTileBytes + static_cast<size_t>(c) * (kChunk * kDim / 2);
+  const char *ka = reinterpret_cast<const char *>(kp.anchor) + cbytes;
+  cd.ka[0] = load_nt(reinterpret_cast<const u32x4 *>(ka + koff));
+  cd.ka[1] = load_nt(reinterpret_cast<const u32x4 *>(ka + koff + 1024));
+  if (kFull) {
+    const char *kr = reinterpret_cast<const char *>(kp.residual) + cbytes;
+    cd.kr[0] = load_nt(reinterpret_cast<const u32x4 *>(kr + koff));
+    cd.kr[1] = load_nt(reinterpret_cast<const u32x4 *>(kr + koff + 1024));
+  }
+}
+
+template <bool kFull>
+__device__ __forceinline__ void load_vcodes(VCodes &cd, const PlanesArg &vp, size_t tile, int c,
+                                            uint32_t voff) {
+  const size_t cbytes = tile * kPlaneTileBytes + static_cast<size_t>(c) * (kChunk * kDim / 2);
+  const char *va = reinterpret_cast<const char *>(vp.anchor) + cbytes;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) cd.va[ct] = load_nt(reinterpret_cast<const uint32_t *>(va + voff + ct * 256));
+  if (kFull) {
+    const char *vr = reinterpret_cast<const char *>(vp.residual) + cbytes;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) cd.vr[ct] = load_nt(reinterpret_cast<const uint32_t *>(vr + voff + ct * 256));
+  }
+}
+
+__device__ __forceinline__ float2 scale_pair(const float *base, size_t off, uint32_t soff) {
+  return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(base) + off + soff);
+}
+
+__device__ __forceinline__ void load_kscales(KScales &sc, const PlanesArg &kp, size_t tile, int c,
+                                             uint32_t soff) {
+  const size_t pb = tile * kDim * 4;
+  const size_t cb = (tile * kChunks + c) * kDim * 4;
+  sc.muk = scale_pair(kp.chunk_mean, cb, soff);
+  sc.sk = scale_pair(kp.chunk_maxabs, cb, soff);
+  sc.mnk = scale_pair(kp.page_min, pb, soff);
+  sc.rgk = scale_pair(kp.page_range, pb, soff);
+}
+
+__device__ __forceinline__ void load_vscales(VScales &sc, const PlanesArg &vp, size_t tile, int c,
+                                             uint32_t soff) {
+  const size_t pb = tile * kDim * 4;
+  const size_t cb = (tile * kChunks + c) * kDim * 4;
+  sc.muv = scale_pair(vp.chunk_mean, cb, soff);
+  sc.sv = scale_pair(vp.chunk_maxabs, cb, soff);
+  sc.mnv = scale_pair(vp.page_min, pb, soff);
+  sc.rgv = scale_pair(vp.page_range, pb, soff);
+}
+
+// The key half of scale_stage: W words and c0k of the K wave's next chunk;
+// returns 2^-(S + 22).
+__device__ __forceinline__ double stage_kslot(const KScales &sc, char *slot, int lane, float qmax,
+                                              const double *q64) {
+  const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // bound only
+  const float bound = qmax * wave_max(fmaxf(c1a, c1b));
+  int S = 0;
+  const uint32_t eb = (__float_as_uint(bound) >> 23) & 0xFFu;
+  if (bound > 0.0f && eb != 0xFFu) {
+    const int e = eb != 0u ? static_cast<int>(eb) - 127
+                           : -127 - __builtin_clz(__float_as_uint(bound)) + 9;
+    S = 29 - e;
+  }
+  const double ks = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + S) << 52);
+  const double inv = __builtin_bit_cast(double, static_cast<uint64_t>(1023 - S - 22) << 52);
+  const double c1x = static_cast<double>(sc.rgk.x) * sc.sk.x * ks;
+  const double c1y = static_cast<double>(sc.rgk.y) * sc.sk.y * ks;
+  char *wdst = slot + (lane >> 1) * 16 + (lane & 1) * 8;
+  const double *qsrc = q64 + 2 * lane;
+#pragma unroll
+  for (int hh = 0; hh < kHeads; ++hh) {
+    const double2 qq = *reinterpret_cast<const double2 *>(qsrc + hh * kQStride);
+    *reinterpret_cast<uint2 *>(wdst + hh * kWRowBytes) = make_uint2(w_bytes(qq.x, c1x), w_bytes(qq.y, c1y));
+  }
+  double *c0k = reinterpret_cast<double *>(slot + kWBytes);
+  reinterpret_cast<double2 *>(c0k)[lane] =
+      make_double2(static_cast<double>(sc.mnk.x) + static_cast<double>(sc.rgk.x) * sc.muk.x,
+                   static_cast<double>(sc.mnk.y) + static_cast<double>(sc.rgk.y) * sc.muk.y);
+  return inv;
+}
+
+// Chunk bias sum_d q_d c0k_d in fp64 of the lane's head: lane (n, r) takes
+// channels 32r + 16 (n >= 8) .. + 15, then lanes n, n ^ 8 and the 4 rows
+// are summed.
+__device__ __forceinline__ double chunk_bias(const char *slot, const double *q64, const LaneConst &lc) {
+  const double *c0k = reinterpret_cast<const double *>(slot + kWBytes);
+  const int d0 = 32 * lc.r + (lc.lo ? 16 : 0);
+  const double *qh = q64 + (lc.n & 7) * kQStride + d0;
+  double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; k += 2) {
+    const double2 qq = *reinterpret_cast<const double2 *>(qh + k);
+    const double2 cc = *reinterpret_cast<const double2 *>(c0k + d0 + k);
+    a0 = fma(qq.x, cc.x, a0);
+    a1 = fma(qq.y, cc.y, a1);
+  }
+  double bias = a0 + a1;
+  bias += ror8(bias);
+  return xrows_sum(bias);
+}
+
+// Table index bytes of a K chunk: 4 + 4 code bytes of even / odd elements
+// (full) or the anchor words (draft), per tile and word.
+template <bool kFull>
+__device__ __forceinline__ void key_bytes(const KCodes &cd, uint32_t (&e)[2][4], uint32_t (&o)[2][4]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (kFull) {
+        code_bytes(cd.ka[t][w], cd.kr[t][w], e[t][w], o[t][w]);
+      } else {
+        e[t][w] = cd.ka[t][w];
+        o[t][w] = 0u;
+      }
+    }
+}
+
+// The value half of scale_stage: c1v and c0v of the V wave's next chunk.
+__device__ __forceinline__ void stage_vslot(const VScales &sc, char *slot, int lane) {
+  float *c1v = reinterpret_cast<float *>(slot);
+  float *c0v = c1v + kDim;
+  reinterpret_cast<float2 *>(c1v)[lane] = make_float2(sc.rgv.x * sc.sv.x, sc.rgv.y * sc.sv.y);
+  reinterpret_cast<float2 *>(c0v)[lane] =
+      make_float2(__builtin_fmaf(sc.rgv.x, sc.muv.x, sc.mnv.x), __builtin_fmaf(sc.rgv.y, sc.muv.y, sc.mnv.y));
+}
+
+// K wave, one chunk: scores, online softmax (base 2); the probabilities, the
+// rescale factor and the probability sum go to the hand-off buffer.
+template <bool kFull>
+__device__ __forceinline__ void score_chunk(const uint32_t (&e)[2][4], const uint32_t (&o)[2][4],
+                                            const char *slot, double inv_s, double bias,
+                                            const LaneConst &lc, const char *lut,
+                                            float &m_run, float &l_run, float *srow, char *hand) {
+  const int n = lc.n, r = lc.r;
+
+  // ---- scores: S^T = Yk * W, three level products per tile (exact int32) ----
+  i32x4 sa0 = {0, 0, 0, 0}, sb0 = {0, 0, 0, 0}, sc0 = {0, 0, 0, 0};
+  i32x4 sa1 = {0, 0, 0, 0}, sb1 = {0, 0, 0, 0}, sc1 = {0, 0, 0, 0};
+  {
+    const char *wrow = slot + (n & 7) * kWRowBytes + r * 128;
+#pragma unroll
+    for (int stp = 0; stp < 8; ++stp) {
+      const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + stp * 16);
+      i32x4 ba, bb, bc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ba[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[0]));
+        bb[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[1]));
+        bc[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[2]));
+      }
+      u32x4 a0, a1;
+      const int w = stp >> 1;
+      if (kFull) {
+        if (stp & 1) {
+          a0 = operand_full<1>(e[0][w], o[0][w], lc.lbk, lut);
+          a1 = operand_full<1>(e[1][w], o[1][w], lc.lbk, lut);
+        } else {
+          a0 = operand_full<0>(e[0][w], o[0][w], lc.lbk, lut);
+          a1 = operand_full<0>(e[1][w], o[1][w], lc.lbk, lut);
+        }
+      } else {
+        if (stp & 1) {
+          a0 = operand_draft<1>(e[0][w], lc.lbk, lut);
+          a1 = operand_draft<1>(e[1][w], lc.lbk, lut);
+        } else {
+          a0 = operand_draft<0>(e[0][w], lc.lbk, lut);
+          a1 = operand_draft<0>(e[1][w], lc.lbk, lut);
+        }
+      }
+      const i32x4 y0 = __builtin_bit_cast(i32x4, a0), y1 = __builtin_bit_cast(i32x4, a1);
+      sa0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, ba, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, ba, sa1, 0, 0, 0);
+      sb0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, bb, sb0, 0, 0, 0);
+      sb1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, bb, sb1, 0, 0, 0);
+      sc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, bc, sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, bc, sc1, 0, 0, 0);
+    }
+  }
+
+  // ---- assemble: lanes n < 8 take tile 0, lanes n >= 8 tile 1 (tokens 16t + 4r + i) ----
+  const double scale2 = lc.sm2 * inv_s;
+  const double bias2 = bias * lc.sm2;
+  double sc2[4];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    auto hi = [](int t0, int t1) {
+      return __builtin_bit_cast(int, ror8_to_hi(__builtin_bit_cast(float, t0), __builtin_bit_cast(float, t1)));
+    };
+    auto lo = [](int t1, int t0) {
+      return __builtin_bit_cast(int, ror8_to_lo(__builtin_bit_cast(float, t1), __builtin_bit_cast(float, t0)));
+    };
+    const int l6 = hi(sa0[i], sa1[i]), l5 = lo(sa1[i], sa0[i]);
+    const int l4 = hi(sb0[i], sb1[i]), l3 = lo(sb1[i], sb0[i]);
+    const int l2 = hi(sc0[i], sc1[i]), l1 = lo(sc1[i], sc0[i]);
+    const int a = l6 * 256 + l5, b2 = l4 * 256 + l3, c2 = l2 * 256 + l1;
+    const double t = fma(fma(static_cast<double>(a), 65536.0, static_cast<double>(b2)), 65536.0,
+                         static_cast<double>(c2));
+    sc2[i] = fma(t, scale2, bias2);
+    cmax = fmaxf(cmax, static_cast<float>(sc2[i]));
+  }
+  cmax = fmaxf(cmax, ror8(cmax));
+  cmax = xrows(cmax, MaxOp());
+  const bool rescale = __builtin_amdgcn_ballot_w64(cmax > m_run + kSlack) != 0;
+  float alpha = 1.0f;
+  if (rescale) {
+    const float m_new = fmaxf(m_run, cmax);
+    alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+  }
+  float p[4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(static_cast<float>(sc2[i] - static_cast<double>(m_run)));
+    psum += p[i];
+  }
+  psum += ror8(psum);
+  psum = xrows(psum, SumOp());
+  l_run = l_run * alpha + psum;
+  if (srow != nullptr) {
+    constexpr double kLn2 = 0.69314718055994530942;
+    *reinterpret_cast<float4 *>(srow + (lc.lo ? 16 : 0) + 4 * r) =
+        make_float4(static_cast<float>(sc2[0] * kLn2), static_cast<float>(sc2[1] * kLn2),
+                    static_cast<float>(sc2[2] * kLn2), static_cast<float>(sc2[3] * kLn2));
+  }
+  *reinterpret_cast<float4 *>(hand + (lc.lo ? 512 : 0) + r * 128 + (n & 7) * 16) =
+      make_float4(p[0], p[1], p[2], p[3]);
+  if (r == 0 && !lc.lo) {
+    reinterpret_cast<float *>(hand + 1024)[n] = alpha;
+    reinterpret_cast<float *>(hand + 1056)[n] = psum;
+  }
+}
+
+// V wave, one chunk: O^T += Yv^T * P with the K wave's probabilities, then
+// the chunk's affine map; acc is rescaled first when the K wave moved its
+// running maximum.
+template <bool kFull>
+__device__ __forceinline__ void value_chunk(const VCodes &cd, const char *slot, const LaneConst &lc,
+                                            const char *lut, floatx4 (&acc)[8], const char *hand) {
+  const int n = lc.n, r = lc.r;
+  const float *c1v = reinterpret_cast<const float *>(slot);
+  const float *c0v = c1v + kDim;
+  const float alpha = reinterpret_cast<const float *>(hand + 1024)[n & 7];
+  const float psum = reinterpret_cast<const float *>(hand + 1056)[n & 7];
+  const float4 p0 = *reinterpret_cast<const float4 *>(hand + r * 128 + (n & 7) * 16);
+  const float4 p1 = *reinterpret_cast<const float4 *>(hand + 512 + r * 128 + (n & 7) * 16);
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] *= alpha;
+  }
+  // ---- P operands: step h holds tokens 16h + 4r + i of column n ----
+  half8 pa0, pa1;
+  {
+    u32x4 w0, w1;
+    w0[0] = split_dup(p0.x, lc.keep_mask);
+    w0[1] = split_dup(p0.y, lc.keep_mask);
+    w0[2] = split_dup(p0.z, lc.keep_mask);
+    w0[3] = split_dup(p0.w, lc.keep_mask);
+    w1[0] = split_dup(p1.x, lc.keep_mask);
+    w1[1] = split_dup(p1.y, lc.keep_mask);
+    w1[2] = split_dup(p1.z, lc.keep_mask);
+    w1[3] = split_dup(p1.w, lc.keep_mask);
+    pa0 = __builtin_bit_cast(half8, w0);
+    pa1 = __builtin_bit_cast(half8, w1);
+  }
+  const float pc0 = lc.lo ? 0.0f : psum;  // the c0v term once per head (high half)
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    half8 y0, y1;
+    if (kFull) {
+      uint32_t e, o;
+      code_bytes(cd.va[ct], cd.vr[ct], e, o);
+      y0 = __builtin_bit_cast(half8, operand_full<0>(e, o, lc.lbv, lut));
+      y1 = __builtin_bit_cast(half8, operand_full<1>(e, o, lc.lbv, lut));
+    } else {
+      y0 = __builtin_bit_cast(half8, operand_draft<0>(cd.va[ct], lc.lbv, lut));
+      y1 = __builtin_bit_cast(half8, operand_draft<1>(cd.va[ct], lc.lbv, lut));
+    }
+    floatx4 ov = {0.0f, 0.0f, 0.0f, 0.0f};
+    ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pa0, ov, 0, 0, 0);
+    ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(y1, pa1, ov, 0, 0, 0);
+    const float4 a1 = *reinterpret_cast<const float4 *>(c1v + 16 * ct + 4 * r);
+    const float4 a0 = *reinterpret_cast<const float4 *>(c0v + 16 * ct + 4 * r);
+    acc[ct][0] = __builtin_fmaf(a1.x, ov[0], __builtin_fmaf(a0.x, pc0, acc[ct][0]));
+    acc[ct][1] = __builtin_fmaf(a1.y, ov[1], __builtin_fmaf(a0.y, pc0, acc[ct][1]));
+    acc[ct][2] = __builtin_fmaf(a1.z, ov[2], __builtin_fmaf(a0.z, pc0, acc[ct][2]));
+    acc[ct][3] = __builtin_fmaf(a1.w, ov[3], __builtin_fmaf(a0.w, pc0, acc[ct][3]));
+  }
+}
+
+template <bool kFull>
+__global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
+    const uint16_t *__restrict__ q, PlanesArg kp, PlanesArg vp,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
+    AttnShape s, float sm_scale, float *__restrict__ out, float *__restrict__ scores, void *ws,
+    MfmaTables tab) {
+  __shared__ __align__(16) char smem[kPLdsBytes];
+  char *lut = smem;
+  double *q64 = reinterpret_cast<double *>(smem + kPQOff);
+  float *s_ml = reinterpret_cast<float *>(smem + kPMlOff);
+
+  const unsigned nblk = gridDim.x;
+  unsigned lb_idx = blockIdx.x;
+  if ((nblk & 7u) == 0u) lb_idx = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int split = static_cast<int>(lb_idx % static_cast<unsigned>(s.splits));
+  const int bh = static_cast<int>(lb_idx / static_cast<unsigned>(s.splits));
+  const int h = bh % s.heads;
+  const int b = bh / s.heads;  // query row
+  const int req = b / s.tq;     // its request
+  const int g = s.group;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
+  const bool kwave = w < kPairs;
+  const int pr = kwave ? w : w - kPairs;  // pair
+
+  LaneConst lc;
+  lc.lane = tid & 63;
+  lc.n = lc.lane & 15;
+  lc.r = lc.lane >> 4;
+  lc.lo = lc.n >= 8;
+  lc.koff = static_cast<uint32_t>(lc.n * 64 + lc.r * 16);
+  lc.voff = static_cast<uint32_t>(lc.n * 16 + lc.r * 4);
+  lc.soff = static_cast<uint32_t>(lc.lane * 8);
+  lc.keep_mask = lc.lo ? 0xFFFFE000u : 0u;
+  lc.lbk = kFull ? static_cast<uint32_t>((lc.lane & 31) * 4) : static_cast<uint32_t>((lc.lane & 15) * 8);
+  lc.lbv = lc.lbk | static_cast<uint32_t>(kValueHalf);
+  lc.lvl[0] = lc.lo ? 0x02030C0Cu : 0x030C0C0Cu;
+  lc.lvl[1] = lc.lo ? 0x00010203u : 0x0102030Cu;
+  lc.lvl[2] = lc.lo ? 0x0C0C0001u : 0x0C000102u;
+  lc.sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
+
+  // ---- this pair's run of chunks (as the waves of attn_mfma_kernel) ----
+  const __attribute__((address_space(4))) int32_t *bt_c =
+      (const __attribute__((address_space(4))) int32_t *)block_table;
+  const __attribute__((address_space(4))) int32_t *sl_c =
+      (const __attribute__((address_space(4))) int32_t *)seq_lens;
+  int npages = s.max_pages;
+  if (seq_lens) {
+    npages = sl_c[req] / kPage;
+    npages = npages < 0 ? 0 : (npages > s.max_pages ? s.max_pages : npages);
+  }
+  const int pps = s.pages_per_split;
+  const int p0 = split * pps;
+  int p1 = p0 + pps;
+  p1 = p1 > npages ? npages : p1;
+  auto run_of = [&](int pp, int &rb, int &re) {
+    rb = p0 * kChunks + pp * pps;
+    re = rb + pps;
+    if (re > p1 * kChunks) re = p1 * kChunks;
+    if (rb > re) rb = re;
+  };
+  int cb, ce, cb0, ce0;
+  run_of(pr, cb, ce);
+  run_of(0, cb0, ce0);
+  const int nrun = ce - cb;
+  const int nsteps = ce0 - cb0 + 1;  // pair 0 has the longest run; the V waves lag one step
+
+  auto page_of = [&](int ci) -> long long {
+    const int lp = ci >> 3;
+    const long long pg = block_table ? bt_c[static_cast<size_t>(req) * s.max_pages + lp]
+                                     : static_cast<long long>(req) * s.max_pages + lp;
+    return (pg < 0 || pg >= s.pool_pages) ? -1 : pg;
+  };
+  auto page_in_run = [&](int c) -> long long { return c < ce ? page_of(c) : -1; };
+  auto tile_of = [&](long long pg) { return pg >= 0 ? static_cast<size_t>(pg) * s.heads + h : 0; };
+  auto chunk_of = [&](long long pg, int c) { return pg >= 0 ? (c & 7) : 0; };
+
+  // ---- set-up loads: table words, the lane's query values ----
+  uint32_t tw0, tw1;  // this thread's table words: 64 bytes of the key or value half of a row
+  const int trow = (tid >> 1) & 255;
+  const bool tval = tid >= 512;
+  {
+    if (kFull) {
+      tw0 = tval ? tab.full[trow] : tab.kfull[trow];
+      tw1 = tw0;
+    } else {
+      tw0 = tval ? tab.draft[trow & 15] : tab.kdraft[trow & 15];
+      tw1 = tval ? tab.draft[trow >> 4] : tab.kdraft[trow >> 4];
+    }
+  }
+  const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
+  const int jq = lc.n & 7;
+  const bool qvalid = jq < g;
+  uint4 qraw[4];
+  {
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(qg + (qvalid ? jq : 0) * kDim + 32 * lc.r);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qraw[k] = qrow[k];
+  }
+
+  // ---- tables: 1024 threads, 64 bytes each ----
+  {
+    const u32x4 v = kFull ? u32x4{tw0, tw0, tw0, tw0} : u32x4{tw0, tw1, tw0, tw1};
+    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + trow * 256 + (tval ? kValueHalf : 0) + (tid & 1) * 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[k] = v;
+  }
+  float qv[32];
+  float qmax = 0.0f;
+  {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t u[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[8 * k + 2 * e] = qvalid ? __uint_as_float(u[e] << 16) : 0.0f;
+        qv[8 * k + 2 * e + 1] = qvalid ? __uint_as_float(u[e] & 0xFFFF0000u) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) qmax = fmaxf(qmax, fabsf(qv[k]));
+    qmax = wave_max(qmax);
+  }
+  // the query group in LDS as f64 (zero rows for heads >= g): K wave w
+  // writes head w's row from the lanes n = w and n = w + 8
+  if (kwave && jq == w) {
+    const bool second = lc.n >= 8;
+    const int d0 = 32 * lc.r + (second ? 16 : 0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) q64[w * kQStride + d0 + k] = static_cast<double>(second ? qv[16 + k] : qv[k]);
+  }
+
+  const size_t T = static_cast<size_t>(s.max_pages) * kPage;
+  float m_run = -INFINITY, l_run = 0.0f;
+  floatx4 acc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) acc[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  char *hand0 = smem + kPHandOff + pr * 2 * kHandBytes;
+
+  if (kwave) {
+    char *kslot = smem + kPKSlotOff + pr * kKSlotBytes;
+    float *srow_base = nullptr;
+    if (scores != nullptr && (lc.n & 7) < g)
+      srow_base = scores + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + (lc.n & 7)) * T;
+    // One buffer each: a step turns its chunk's codes into table index
+    // bytes before it requests the next chunk's codes into the same
+    // registers, and stages the next chunk's constants before it requests
+    // the scales of the chunk after that.
+    KCodes kc;
+    KScales ks;
+    long long pg_c = page_in_run(cb);      // page of the chunk whose codes kc holds
+    long long pg_s = page_in_run(cb + 1);  // page of the chunk whose scales ks holds next
+    load_kscales(ks, kp, tile_of(pg_c), chunk_of(pg_c, cb), lc.soff);
+    load_kcodes<kFull>(kc, kp, tile_of(pg_c), chunk_of(pg_c, cb), lc.koff);
+    __syncthreads();  // tables and q
+    double inv = stage_kslot(ks, kslot, lc.lane, qmax, q64);
+    wave_lds_sync();
+    double bias = chunk_bias(kslot, q64, lc);
+    load_kscales(ks, kp, tile_of(pg_s), chunk_of(pg_s, cb + 1), lc.soff);
+    for (int si = 0; si < nsteps; ++si) {
+      const int c = cb + si;
+      if (si < nrun) {
+        const long long cur = pg_c;
+        uint32_t e[2][4], o[2][4];
+        key_bytes<kFull>(kc, e, o);
+        pg_c = pg_s;
+        load_kcodes<kFull>(kc, kp, tile_of(pg_c), chunk_of(pg_c, c + 1), lc.koff);
+        if (cur >= 0)
+          score_chunk<kFull>(e, o, kslot, inv, bias, lc, lut, m_run, l_run,
+                             srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr,
+                             hand0 + (si & 1) * kHandBytes);
+        wave_lds_sync();
+        inv = stage_kslot(ks, kslot, lc.lane, qmax, q64);  // constants of chunk c + 1
+        wave_lds_sync();
+        bias = chunk_bias(kslot, q64, lc);
+        pg_s = page_in_run(c + 2);
+        load_kscales(ks, kp, tile_of(pg_s), chunk_of(pg_s, c + 2), lc.soff);
+      }
+      __syncthreads();
+    }
+  } else {
+    char *vslot = smem + kPVSlotOff + pr * kVSlotBytes;
+    // codes of chunk c in buffer (c - cb) % 2; one scale buffer, refilled
+    // after the next chunk's constants are staged
+    VCodes vc[2];
+    VScales vs;
+    long long pg[2];
+    pg[0] = page_in_run(cb);
+    pg[1] = page_in_run(cb + 1);
+    load_vscales(vs, vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc.soff);
+    load_vcodes<kFull>(vc[0], vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc.voff);
+    __syncthreads();  // tables and q
+    stage_vslot(vs, vslot, lc.lane);
+    load_vscales(vs, vp, tile_of(pg[1]), chunk_of(pg[1], cb + 1), lc.soff);
+    __syncthreads();  // step 0: the K waves score the first chunks
+    // step si >= 1 takes chunk c = cb + si - 1, whose probabilities the K
+    // wave left in buffer (si - 1) & 1
+    auto step = [&](auto jc, int si) {
+      constexpr int J = decltype(jc)::value;
+      const int c = cb + si - 1;
+      if (si - 1 < nrun) {
+        const long long cur = pg[J];
+        pg[J] = page_in_run(c + 2);
+        load_vcodes<kFull>(vc[J ^ 1], vp, tile_of(pg[J ^ 1]), chunk_of(pg[J ^ 1], c + 1), lc.voff);
+        if (cur >= 0)
+          value_chunk<kFull>(vc[J], vslot, lc, lut, acc, hand0 + ((si - 1) & 1) * kHandBytes);
+        wave_lds_sync();
+        stage_vslot(vs, vslot, lc.lane);  // constants of chunk c + 1
+        load_vscales(vs, vp, tile_of(pg[J]), chunk_of(pg[J], c + 2), lc.soff);
+      }
+      __syncthreads();
+    };
+    for (int si = 1; si < nsteps; si += 2) {
+      step(std::integral_constant<int, 0>(), si);
+      if (si + 1 >= nsteps) break;
+      step(std::integral_constant<int, 1>(), si + 1);
+    }
+  }
+
+  // ---- merge the 8 pairs of the block ----
+  __syncthreads();  // every wave is done with the tables: reuse their space
+  float *s_o = reinterpret_cast<float *>(lut);  // [pair][16 col][128 ch]
+  if (kwave) {
+    if (lc.r == 0 && lc.n < 8) {
+      s_ml[(pr * 2 + 0) * kHeads + lc.n] = m_run;
+      s_ml[(pr * 2 + 1) * kHeads + lc.n] = l_run;
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      *reinterpret_cast<float4 *>(s_o + (pr * 16 + lc.n) * kDim + 16 * ct + 4 * lc.r) =
+          make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
+  }
+  __syncthreads();
+
+  if (tid < g * (kDim / 4)) {
+    const int j = tid >> 5, c = tid & 31;
+    float M = -INFINITY;
+#pragma unroll
+    for (int pp = 0; pp < kPairs; ++pp) M = fmaxf(M, s_ml[(pp * 2) * kHeads + j]);
+    float L = 0.0f;
+    float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int pp = 0; pp < kPairs; ++pp) {
+      const float mw = s_ml[(pp * 2) * kHeads + j];
+      const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      L += f * s_ml[(pp * 2 + 1) * kHeads + j];
+      const float4 hi = reinterpret_cast<const float4 *>(s_o + (pp * 16 + j) * kDim)[c];
+      const float4 lo = reinterpret_cast<const float4 *>(s_o + (pp * 16 + 8 + j) * kDim)[c];
+      O.x += f * (hi.x + lo.x);
+      O.y += f * (hi.y + lo.y);
+      O.z += f * (hi.z + lo.z);
+      O.w += f * (hi.w + lo.w);
+    }
+    if (s.parts == 1) {
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      reinterpret_cast<float4 *>(
+          out + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + j) * kDim)[c] =
+          make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
+    } else {
+      Partials pt = partials_of(ws, s);
+      const size_t row = (static_cast<size_t>(bh) * s.parts + split) * g + j;
+      reinterpret_cast<float4 *>(pt.o + row * kDim)[c] = O;
+      if (c == 0) {
+        pt.m[row] = static_cast<double>(M);
+        pt.l[row] = L;
+      }
+    }
+  }
+}
+
 // Merge of the split partials (base-2 maxima) of one (request, KV head)
 // into the output.  Block = (request, KV head, 16 channels).  The global
 // loads of a thread are issued up front; the per-head maximum and sum over
@@ -1093,8 +1703,12 @@ void launch_mfma_kernel(dim3 grid, hipStream_t stream, const uint16_t *q, const 
                         const PlanesArg &v, const int32_t *block_table, const int32_t *seq_lens,
                         const AttnShape &s, float sm_scale, float *out, float *scores,
                         void *workspace, const MfmaTables &tables) {
-  hipLaunchKernelGGL((attn_mfma_kernel<kFull, kBits>), grid, dim3(kThreads), 0, stream, q, k, v,
-                     block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
+  if constexpr (kBits == 4)
+    hipLaunchKernelGGL((attn_pair_kernel<kFull>), grid, dim3(kPThreads), 0, stream, q, k, v,
+                       block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<kFull, kBits>), grid, dim3(kThreads), 0, stream, q, k, v,
+                       block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
 }
 
 template <int kBits>
