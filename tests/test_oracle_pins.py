@@ -415,7 +415,8 @@ def _fp32_chain(x_bits):
     xf = oracle.bf16_bits_to_float(x_bits)
     mn = xf.min(axis=1, keepdims=True)
     rg = (xf.max(axis=1, keepdims=True) - mn).astype(np.float32)
-    inv = np.where(rg > 0, (1.0 / rg.astype(np.float64)).astype(np.float32), np.float32(0.0))
+    with np.errstate(divide="ignore"):  # degenerate channels take 0 below
+        inv = np.where(rg > 0, (1.0 / rg.astype(np.float64)).astype(np.float32), np.float32(0.0))
     return ((xf - mn).astype(np.float32) * inv).astype(np.float32), rg[:, 0]
 
 
