@@ -1435,27 +1435,29 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     wave_lds_sync();
     double bias = chunk_bias(kslot, q64, lc);
     load_kscales(ks, kp, tile_of(pg_s), chunk_of(pg_s, cb + 1), lc.soff);
-    for (int si = 0; si < nsteps; ++si) {
+    // the run's steps, then barrier-only steps up to the block's count (two
+    // loops, so the code registers need no copies at a join)
+    int si = 0;
+    for (; si < nrun; ++si) {
       const int c = cb + si;
-      if (si < nrun) {
-        const long long cur = pg_c;
-        uint32_t e[2][4], o[2][4];
-        key_bytes<kFull>(kc, e, o);
-        pg_c = pg_s;
-        load_kcodes<kFull>(kc, kp, tile_of(pg_c), chunk_of(pg_c, c + 1), lc.koff);
-        if (cur >= 0)
-          score_chunk<kFull>(e, o, kslot, inv, bias, lc, lut, m_run, l_run,
-                             srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr,
-                             hand0 + (si & 1) * kHandBytes);
-        wave_lds_sync();
-        inv = stage_kslot(ks, kslot, lc.lane, qmax, q64);  // constants of chunk c + 1
-        wave_lds_sync();
-        bias = chunk_bias(kslot, q64, lc);
-        pg_s = page_in_run(c + 2);
-        load_kscales(ks, kp, tile_of(pg_s), chunk_of(pg_s, c + 2), lc.soff);
-      }
+      const long long cur = pg_c;
+      uint32_t e[2][4], o[2][4];
+      key_bytes<kFull>(kc, e, o);
+      pg_c = pg_s;
+      load_kcodes<kFull>(kc, kp, tile_of(pg_c), chunk_of(pg_c, c + 1), lc.koff);
+      if (cur >= 0)
+        score_chunk<kFull>(e, o, kslot, inv, bias, lc, lut, m_run, l_run,
+                           srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr,
+                           hand0 + (si & 1) * kHandBytes);
+      wave_lds_sync();
+      inv = stage_kslot(ks, kslot, lc.lane, qmax, q64);  // constants of chunk c + 1
+      wave_lds_sync();
+      bias = chunk_bias(kslot, q64, lc);
+      pg_s = page_in_run(c + 2);
+      load_kscales(ks, kp, tile_of(pg_s), chunk_of(pg_s, c + 2), lc.soff);
       __syncthreads();
     }
+    for (; si < nsteps; ++si) __syncthreads();
   } else {
     char *vslot = smem + kPVSlotOff + pr * kVSlotBytes;
     // codes of chunk c in buffer (c - cb) % 2; one scale buffer, refilled
