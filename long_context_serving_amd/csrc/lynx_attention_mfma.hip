@@ -1353,11 +1353,15 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
   auto tile_of = [&](long long pg) { return pg >= 0 ? static_cast<size_t>(pg) * s.heads + h : 0; };
   auto chunk_of = [&](long long pg, int c) { return pg >= 0 ? (c & 7) : 0; };
 
-  // ---- set-up loads: table words, the lane's query values ----
-  uint32_t tw0, tw1;  // this thread's table words: 64 bytes of the key or value half of a row
-  const int trow = (tid >> 1) & 255;
-  const bool tval = tid >= 512;
-  {
+  // ---- set-up, run by each role after it has requested its first chunks
+  // (their latency overlaps it): the tables (1024 threads, 64 bytes each),
+  // and in the K waves the query group in LDS as f64 (zero rows for heads
+  // >= g; K wave w writes head w's row from the lanes n = w and n = w + 8),
+  // which returns the group's largest |q| ----
+  auto setup_tables = [&]() {
+    const int trow = (tid >> 1) & 255;
+    const bool tval = tid >= 512;
+    uint32_t tw0, tw1;  // this thread's table words
     if (kFull) {
       tw0 = tval ? tab.full[trow] : tab.kfull[trow];
       tw1 = tw0;
@@ -1365,27 +1369,22 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
       tw0 = tval ? tab.draft[trow & 15] : tab.kdraft[trow & 15];
       tw1 = tval ? tab.draft[trow >> 4] : tab.kdraft[trow >> 4];
     }
-  }
-  const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
-  const int jq = lc.n & 7;
-  const bool qvalid = jq < g;
-  uint4 qraw[4];
-  {
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(qg + (qvalid ? jq : 0) * kDim + 32 * lc.r);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) qraw[k] = qrow[k];
-  }
-
-  // ---- tables: 1024 threads, 64 bytes each ----
-  {
     const u32x4 v = kFull ? u32x4{tw0, tw0, tw0, tw0} : u32x4{tw0, tw1, tw0, tw1};
     u32x4 *dst = reinterpret_cast<u32x4 *>(lut + trow * 256 + (tval ? kValueHalf : 0) + (tid & 1) * 64);
 #pragma unroll
     for (int k = 0; k < 4; ++k) dst[k] = v;
-  }
-  float qv[32];
-  float qmax = 0.0f;
-  {
+  };
+  auto setup_query = [&]() -> float {
+    const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
+    const int jq = lc.n & 7;
+    const bool qvalid = jq < g;
+    uint4 qraw[4];
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(qg + (qvalid ? jq : 0) * kDim + 32 * lc.r);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qraw[k] = qrow[k];
+    setup_tables();
+    float qv[32];
+    float qmax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t u[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
@@ -1398,15 +1397,14 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
 #pragma unroll
     for (int k = 0; k < 32; ++k) qmax = fmaxf(qmax, fabsf(qv[k]));
     qmax = wave_max(qmax);
-  }
-  // the query group in LDS as f64 (zero rows for heads >= g): K wave w
-  // writes head w's row from the lanes n = w and n = w + 8
-  if (kwave && jq == w) {
-    const bool second = lc.n >= 8;
-    const int d0 = 32 * lc.r + (second ? 16 : 0);
+    if (jq == w) {
+      const bool second = lc.n >= 8;
+      const int d0 = 32 * lc.r + (second ? 16 : 0);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) q64[w * kQStride + d0 + k] = static_cast<double>(second ? qv[16 + k] : qv[k]);
-  }
+      for (int k = 0; k < 16; ++k) q64[w * kQStride + d0 + k] = static_cast<double>(second ? qv[16 + k] : qv[k]);
+    }
+    return qmax;
+  };
 
   const size_t T = static_cast<size_t>(s.max_pages) * kPage;
   float m_run = -INFINITY, l_run = 0.0f;
@@ -1430,6 +1428,7 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     long long pg_s = page_in_run(cb + 1);  // page of the chunk whose scales ks holds next
     load_kscales(ks, kp, tile_of(pg_c), chunk_of(pg_c, cb), lc.soff);
     load_kcodes<kFull>(kc, kp, tile_of(pg_c), chunk_of(pg_c, cb), lc.koff);
+    const float qmax = setup_query();
     __syncthreads();  // tables and q
     double inv = stage_kslot(ks, kslot, lc.lane, qmax, q64);
     wave_lds_sync();
@@ -1469,6 +1468,7 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     pg[1] = page_in_run(cb + 1);
     load_vscales(vs, vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc.soff);
     load_vcodes<kFull>(vc[0], vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc.voff);
+    setup_tables();
     __syncthreads();  // tables and q
     stage_vslot(vs, vslot, lc.lane);
     load_vscales(vs, vp, tile_of(pg[1]), chunk_of(pg[1], cb + 1), lc.soff);
