@@ -106,7 +106,11 @@ constexpr int kQOff = kScaleOff + kWaves * kSlotBytes;
 constexpr int kLdsBytes = kQOff + kHeads * kQStride * 8;
 // after the chunk loop the table and slot space holds the block merge: o of
 // every wave [wave][16 col][128 ch] f32, then m, l of every wave's 8 heads
-constexpr int kMlOff = kWaves * 16 * kDim * 4;
+// Merge staging of the waves' value sums: rows of 128 floats padded to 132,
+// so that the 8 lanes of each 128-byte pass of a 16-byte store (8 rows, one
+// per lane) fall on 8 different 4-bank groups.
+constexpr int kORow = kDim + 4;
+constexpr int kMlOff = kWaves * 16 * kORow * 4;
 static_assert(kMlOff + kWaves * 2 * kHeads * 4 <= kQOff, "merge area must fit the table and slot space");
 static_assert(kSlotBytes % 16 == 0 && kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 
@@ -888,14 +892,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
 
   // ---- merge the 8 waves of the block ----
   __syncthreads();  // every wave is done with the table: reuse its space
-  float *s_o = reinterpret_cast<float *>(lut);  // [wave][16 col][128 ch]
+  float *s_o = reinterpret_cast<float *>(lut);  // [wave][16 col][128 ch, padded to kORow]
   if (lc.r == 0 && lc.n < 8) {
     s_ml[(w * 2 + 0) * kHeads + lc.n] = st.m;
     s_ml[(w * 2 + 1) * kHeads + lc.n] = st.l;
   }
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct)
-    *reinterpret_cast<float4 *>(s_o + (w * 16 + lc.n) * kDim + 16 * ct + 4 * lc.r) =
+    *reinterpret_cast<float4 *>(s_o + (w * 16 + lc.n) * kORow + 16 * ct + 4 * lc.r) =
         make_float4(st.acc[ct][0], st.acc[ct][1], st.acc[ct][2], st.acc[ct][3]);
   __syncthreads();
 
@@ -913,8 +917,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
       const float mw = s_ml[(ww * 2) * kHeads + j];
       const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
       L += f * s_ml[(ww * 2 + 1) * kHeads + j];
-      const float4 hi = reinterpret_cast<const float4 *>(s_o + (ww * 16 + j) * kDim)[c];
-      const float4 lo = reinterpret_cast<const float4 *>(s_o + (ww * 16 + 8 + j) * kDim)[c];
+      const float4 hi = reinterpret_cast<const float4 *>(s_o + (ww * 16 + j) * kORow)[c];
+      const float4 lo = reinterpret_cast<const float4 *>(s_o + (ww * 16 + 8 + j) * kORow)[c];
       O.x += f * (hi.x + lo.x);
       O.y += f * (hi.y + lo.y);
       O.z += f * (hi.z + lo.z);
@@ -964,7 +968,7 @@ constexpr int kPQOff = kPHandOff + kPairs * 2 * kHandBytes;
 constexpr int kPLdsBytes = kPQOff + kHeads * kQStride * 8;
 // after the chunk loop: o of every pair [pair][16 col][128 ch] f32 over the
 // table space, then m, l of every pair's 8 heads
-constexpr int kPMlOff = kPairs * 16 * kDim * 4;
+constexpr int kPMlOff = kPairs * 16 * kORow * 4;
 static_assert(kPMlOff + kPairs * 2 * kHeads * 4 <= kPQOff, "merge area must fit below q");
 static_assert(kKSlotBytes % 16 == 0 && kHandBytes % 16 == 0 && kPLdsBytes <= 160 * 1024,
               "LDS budget of one workgroup");
@@ -1499,7 +1503,7 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
 
   // ---- merge the 8 pairs of the block ----
   __syncthreads();  // every wave is done with the tables: reuse their space
-  float *s_o = reinterpret_cast<float *>(lut);  // [pair][16 col][128 ch]
+  float *s_o = reinterpret_cast<float *>(lut);  // [pair][16 col][128 ch, padded to kORow]
   if (kwave) {
     if (lc.r == 0 && lc.n < 8) {
       s_ml[(pr * 2 + 0) * kHeads + lc.n] = m_run;
@@ -1508,7 +1512,7 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
   } else {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
-      *reinterpret_cast<float4 *>(s_o + (pr * 16 + lc.n) * kDim + 16 * ct + 4 * lc.r) =
+      *reinterpret_cast<float4 *>(s_o + (pr * 16 + lc.n) * kORow + 16 * ct + 4 * lc.r) =
           make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
   }
   __syncthreads();
@@ -1525,8 +1529,8 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
       const float mw = s_ml[(pp * 2) * kHeads + j];
       const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
       L += f * s_ml[(pp * 2 + 1) * kHeads + j];
-      const float4 hi = reinterpret_cast<const float4 *>(s_o + (pp * 16 + j) * kDim)[c];
-      const float4 lo = reinterpret_cast<const float4 *>(s_o + (pp * 16 + 8 + j) * kDim)[c];
+      const float4 hi = reinterpret_cast<const float4 *>(s_o + (pp * 16 + j) * kORow)[c];
+      const float4 lo = reinterpret_cast<const float4 *>(s_o + (pp * 16 + 8 + j) * kORow)[c];
       O.x += f * (hi.x + lo.x);
       O.y += f * (hi.y + lo.y);
       O.z += f * (hi.z + lo.z);
