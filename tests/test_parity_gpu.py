@@ -471,6 +471,29 @@ def test_ragged_lengths_group_sizes_and_skipped_pages(lynx):
             check_attention(got, ref, "ragged H=%d Hq=%d full=%s" % (H, Hq, full))
 
 
+def test_uneven_runs_across_the_pairs_of_a_block(lynx):
+    """Runs of 3 pages per block, so each of a block's 8 K/V wave pairs takes
+    3 chunks; the last block of request 1 (2 pages left by its length) gives
+    pairs 0-4 three chunks, pair 5 one and pairs 6-7 none, and the block's
+    step count follows pair 0.  Request 0 is 150 pages long, request 1 149
+    (no block table: each owns 150 contiguous pool pages)."""
+    H, Hq, max_pages = 2, 16, 150
+    x_k = synth.laplace_pages(2 * max_pages, H, 128, seed=71, scale_channels=((1, 5, 70.0),))
+    x_v = synth.laplace_pages(2 * max_pages, H, 128, seed=72, scale_channels=((0, 9, 60.0),))
+    pk, ek, _, _ = check_encode(lynx, x_k, 0)
+    pv, ev, _, _ = check_encode(lynx, x_v, 1)
+    lengths = [150, 149]
+    pages = [list(range(0, 150)), list(range(150, 150 + 149))]
+    rng = np.random.default_rng(73)
+    q = synth.float_to_bf16_bits(rng.laplace(0, 1, (2, Hq, 128)).astype(np.float32))
+    for full in (False, True):
+        print("uneven runs full=%s" % full, flush=True)
+        ref = oracle_attention_for(ek, ev, q, pages, full)
+        got = run_gpu_attention(lynx, q, pk, pv, max_pages, full,
+                                seq_lens=[256 * n for n in lengths])
+        check_attention(got, ref, "uneven pair runs full=%s" % full)
+
+
 @pytest.mark.parametrize("P,H", [(1, 1), (3, 5), (128, 8)])
 def test_kv_encode_in_one_launch_equals_one_launch_per_tensor(lynx, P, H):
     # lynx_quantize_kv_pages: every byte of both tensors' planes as written by
