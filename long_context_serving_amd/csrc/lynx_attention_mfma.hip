@@ -84,9 +84,12 @@ constexpr float kSlack = 8.0f;  // log2 of the largest probability before rescal
 // the value table word (fp16 pair).  Full code and cuts: 32 copies of the
 // word, copy l % 32 for lane l; 4 + 4 draft (row = two anchor nibbles,
 // element 2j in the low one): 16 copies of the pair of words, copy l % 16.
-// A wave reads a table 128 bytes per pass (32 words or 16 pairs), so the
-// lanes of one pass never share a bank.  The lane bits of a value read
-// carry the 128-byte offset.
+// A wave's 4-byte reads are served 32 lanes (128 bytes) per pass, so no two
+// lanes of a pass share a bank.  Its 8-byte reads are served 32 lanes per
+// pass over 64 banks: lanes l and l + 16 read the same copy, which costs a
+// second pass when their rows differ (32 copies of the pairs would avoid
+// it at twice the table space).  The lane bits of a value read carry the
+// 128-byte offset.
 constexpr int kValueHalf = 128;
 constexpr int kTableBytes = 256 * 256;
 // Per wave, one slot of the chunk constants (the next chunk's are staged
