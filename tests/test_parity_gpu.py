@@ -488,10 +488,15 @@ def test_uneven_runs_across_the_pairs_of_a_block(lynx):
     q = synth.float_to_bf16_bits(rng.laplace(0, 1, (2, Hq, 128)).astype(np.float32))
     for full in (False, True):
         print("uneven runs full=%s" % full, flush=True)
-        ref = oracle_attention_for(ek, ev, q, pages, full)
+        ref, logits = oracle_attention_for(ek, ev, q, pages, full, want_logits=True)
+        scores = torch.empty((2, Hq, 256 * max_pages), dtype=torch.float32, device="cuda")
         got = run_gpu_attention(lynx, q, pk, pv, max_pages, full,
-                                seq_lens=[256 * n for n in lengths])
+                                seq_lens=[256 * n for n in lengths], scores=scores)
         check_attention(got, ref, "uneven pair runs full=%s" % full)
+        sc = scores.cpu().numpy().astype(np.float64)
+        for b, n in enumerate(lengths):
+            lg = logits[b]
+            assert np.abs(sc[b, :, :256 * n] - lg).max() <= 1e-4 * max(1.0, np.abs(lg).max())
 
 
 @pytest.mark.parametrize("P,H", [(1, 1), (3, 5), (128, 8)])
