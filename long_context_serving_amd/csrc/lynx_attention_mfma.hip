@@ -944,10 +944,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
   }
 }
 
-// ---- K/V wave pairs (4 + 4 planes) --------------------------------------------
-// The 4 + 4 planes take a second form of the kernel with the roles of a
-// chunk split between two waves, so that each holds half the registers and a
-// CU runs 16 waves (4 per SIMD) instead of 8.  Wave p < 8 (the K wave of pair
+// ---- K/V wave pairs (4 + 4 planes, drafts of the other cuts) -----------------
+// The 4 + 4 planes (draft and full) and the drafts of the other cuts take a
+// second form of the kernel with the roles of a chunk split between two
+// waves, so that each holds half the registers and a CU runs 16 waves (4 per
+// SIMD) instead of 8.  Wave p < 8 (the K wave of pair
 // p) streams the key codes and scales of its run of chunks and computes each
 // chunk's scores, running maximum and probabilities; wave p + 8 (the V wave)
 // streams the value codes and scales of the same run and accumulates the
@@ -976,11 +977,25 @@ static_assert(kPMlOff + kPairs * 2 * kHeads * 4 <= kPQOff, "merge area must fit 
 static_assert(kKSlotBytes % 16 == 0 && kHandBytes % 16 == 0 && kPLdsBytes <= 160 * 1024,
               "LDS budget of one workgroup");
 
+// Codes of a chunk.  4 + 4 planes: K tile t, anchor / residual of channels
+// 32r .. of token 16t + n; V word r of channel 16ct + n.  Drafts from a
+// b-bit anchor stream (b != 4): the lane's K unit words of each tile, and
+// the window words of its V fields in channel 16ct + n.
+template <int kBits>
 struct KCodes {
-  u32x4 ka[2], kr[2];  // tile t: anchor / residual of channels 32r.. of token 16t + n
+  uint32_t ka[2][kBits];
 };
+template <>
+struct KCodes<4> {
+  u32x4 ka[2], kr[2];
+};
+template <int kBits>
 struct VCodes {
-  uint32_t va[8], vr[8];  // word r of channel 16ct + n
+  uint32_t va[8][cut_window_words(kBits)];
+};
+template <>
+struct VCodes<4> {
+  uint32_t va[8], vr[8];
 };
 struct KScales {
   float2 mnk, rgk, muk, sk;  // channels 2l, 2l+1
@@ -989,9 +1004,21 @@ struct VScales {
   float2 mnv, rgv, muv, sv;
 };
 
-template <bool kFull>
-__device__ __forceinline__ void load_kcodes(KCodes &cd, const PlanesArg &kp, size_t tile, int c,
-                                            uint32_t koff) {
+template <bool kFull, int kBits>
+__device__ __forceinline__ void load_kcodes(KCodes<kBits> &cd, const PlanesArg &kp, size_t tile, int c,
+                                            const LaneConst &lc) {
+  if constexpr (kBits != 4) {
+    // a tile is 1024 units of 4 * b bytes, a chunk 128 of them
+    const size_t unit0 = tile * 1024 + static_cast<size_t>(c) * 128;
+    const char *ka = reinterpret_cast<const char *>(kp.anchor) + unit0 * (4 * kBits);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < kBits; ++i)
+        cd.ka[t][i] = load_nt(reinterpret_cast<const uint32_t *>(ka + lc.kca + t * 256 * kBits + 4 * i));
+    return;
+  } else {
+  const uint32_t koff = lc.koff;
   const size_t cbytes = tile * kPlaneTileBytes + static_cast<size_t>(c) * (kChunk * kDim / 2);
   const char *ka = reinterpret_cast<const char *>(kp.anchor) + cbytes;
   cd.ka[0] = load_nt(reinterpret_cast<const u32x4 *>(ka + koff));
@@ -1001,11 +1028,23 @@ __device__ __forceinline__ void load_kcodes(KCodes &cd, const PlanesArg &kp, siz
     cd.kr[0] = load_nt(reinterpret_cast<const u32x4 *>(kr + koff));
     cd.kr[1] = load_nt(reinterpret_cast<const u32x4 *>(kr + koff + 1024));
   }
+  }
 }
 
-template <bool kFull>
-__device__ __forceinline__ void load_vcodes(VCodes &cd, const PlanesArg &vp, size_t tile, int c,
-                                            uint32_t voff) {
+template <bool kFull, int kBits>
+__device__ __forceinline__ void load_vcodes(VCodes<kBits> &cd, const PlanesArg &vp, size_t tile, int c,
+                                            const LaneConst &lc) {
+  if constexpr (kBits != 4) {
+    const size_t unit0 = tile * 1024 + static_cast<size_t>(c) * 128;
+    const char *va = reinterpret_cast<const char *>(vp.anchor) + unit0 * (4 * kBits);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int j = 0; j < cut_window_words(kBits); ++j)
+        cd.va[ct][j] = load_nt(reinterpret_cast<const uint32_t *>(va + ct * 64 * kBits + lc.vwa[j]));
+    return;
+  } else {
+  const uint32_t voff = lc.voff;
   const size_t cbytes = tile * kPlaneTileBytes + static_cast<size_t>(c) * (kChunk * kDim / 2);
   const char *va = reinterpret_cast<const char *>(vp.anchor) + cbytes;
 #pragma unroll
@@ -1014,6 +1053,7 @@ __device__ __forceinline__ void load_vcodes(VCodes &cd, const PlanesArg &vp, siz
     const char *vr = reinterpret_cast<const char *>(vp.residual) + cbytes;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) cd.vr[ct] = load_nt(reinterpret_cast<const uint32_t *>(vr + voff + ct * 256));
+  }
   }
 }
 
@@ -1093,14 +1133,19 @@ __device__ __forceinline__ double chunk_bias(const char *slot, const double *q64
 }
 
 // Table index bytes of a K chunk: 4 + 4 code bytes of even / odd elements
-// (full) or the anchor words (draft), per tile and word.
-template <bool kFull>
-__device__ __forceinline__ void key_bytes(const KCodes &cd, uint32_t (&e)[2][4], uint32_t (&o)[2][4]) {
+// (full) or the anchor words (draft), per tile and word; drafts from a
+// b-bit stream: the anchor fields of elements 8w .. 8w + 3 (e) and
+// 8w + 4 .. 8w + 7 (o), one byte each.
+template <bool kFull, int kBits>
+__device__ __forceinline__ void key_bytes(const KCodes<kBits> &cd, uint32_t (&e)[2][4], uint32_t (&o)[2][4]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      if (kFull) {
+      if constexpr (kBits != 4) {
+        e[t][w] = cut_bytes<kBits>(cd.ka[t], 8 * w);
+        o[t][w] = cut_bytes<kBits>(cd.ka[t], 8 * w + 4);
+      } else if (kFull) {
         code_bytes(cd.ka[t][w], cd.kr[t][w], e[t][w], o[t][w]);
       } else {
         e[t][w] = cd.ka[t][w];
@@ -1120,7 +1165,7 @@ __device__ __forceinline__ void stage_vslot(const VScales &sc, char *slot, int l
 
 // K wave, one chunk: scores, online softmax (base 2); the probabilities, the
 // rescale factor and the probability sum go to the hand-off buffer.
-template <bool kFull>
+template <bool kFull, int kBits>
 __device__ __forceinline__ void score_chunk(const uint32_t (&e)[2][4], const uint32_t (&o)[2][4],
                                             const char *slot, double inv_s, double bias,
                                             const LaneConst &lc, const char *lut,
@@ -1144,7 +1189,10 @@ __device__ __forceinline__ void score_chunk(const uint32_t (&e)[2][4], const uin
       }
       u32x4 a0, a1;
       const int w = stp >> 1;
-      if (kFull) {
+      if constexpr (kBits != 4) {
+        a0 = operand_bytes((stp & 1) ? o[0][w] : e[0][w], lc.lbk, lut);
+        a1 = operand_bytes((stp & 1) ? o[1][w] : e[1][w], lc.lbk, lut);
+      } else if (kFull) {
         if (stp & 1) {
           a0 = operand_full<1>(e[0][w], o[0][w], lc.lbk, lut);
           a1 = operand_full<1>(e[1][w], o[1][w], lc.lbk, lut);
@@ -1229,8 +1277,8 @@ __device__ __forceinline__ void score_chunk(const uint32_t (&e)[2][4], const uin
 // V wave, one chunk: O^T += Yv^T * P with the K wave's probabilities, then
 // the chunk's affine map; acc is rescaled first when the K wave moved its
 // running maximum.
-template <bool kFull>
-__device__ __forceinline__ void value_chunk(const VCodes &cd, const char *slot, const LaneConst &lc,
+template <bool kFull, int kBits>
+__device__ __forceinline__ void value_chunk(const VCodes<kBits> &cd, const char *slot, const LaneConst &lc,
                                             const char *lut, floatx4 (&acc)[8], const char *hand) {
   const int n = lc.n, r = lc.r;
   const float *c1v = reinterpret_cast<const float *>(slot);
@@ -1262,7 +1310,12 @@ __device__ __forceinline__ void value_chunk(const VCodes &cd, const char *slot, 
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
     half8 y0, y1;
-    if (kFull) {
+    if constexpr (kBits != 4) {
+      uint32_t win[2];
+      cut_align<cut_window_words(kBits)>(cd.va[ct], lc.vsa, win);
+      y0 = __builtin_bit_cast(half8, operand_bytes(cut_bytes<kBits>(win, 0), lc.lbv, lut));
+      y1 = __builtin_bit_cast(half8, operand_bytes(cut_bytes<kBits>(win, 4), lc.lbv, lut));
+    } else if (kFull) {
       uint32_t e, o;
       code_bytes(cd.va[ct], cd.vr[ct], e, o);
       y0 = __builtin_bit_cast(half8, operand_full<0>(e, o, lc.lbv, lut));
@@ -1283,7 +1336,7 @@ __device__ __forceinline__ void value_chunk(const VCodes &cd, const char *slot, 
   }
 }
 
-template <bool kFull>
+template <bool kFull, int kBits>
 __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     const uint16_t *__restrict__ q, PlanesArg kp, PlanesArg vp,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -1317,11 +1370,13 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
   lc.voff = static_cast<uint32_t>(lc.n * 16 + lc.r * 4);
   lc.soff = static_cast<uint32_t>(lc.lane * 8);
   lc.keep_mask = lc.lo ? 0xFFFFE000u : 0u;
-  lc.lbk = kFull ? static_cast<uint32_t>((lc.lane & 31) * 4) : static_cast<uint32_t>((lc.lane & 15) * 8);
+  constexpr bool kWordTable = kFull || kBits != 4;
+  lc.lbk = kWordTable ? static_cast<uint32_t>((lc.lane & 31) * 4) : static_cast<uint32_t>((lc.lane & 15) * 8);
   lc.lbv = lc.lbk | static_cast<uint32_t>(kValueHalf);
   lc.lvl[0] = lc.lo ? 0x02030C0Cu : 0x030C0C0Cu;
   lc.lvl[1] = lc.lo ? 0x00010203u : 0x0102030Cu;
   lc.lvl[2] = lc.lo ? 0x0C0C0001u : 0x0C000102u;
+  if constexpr (kBits != 4) cut_lane_offsets<kBits>(lc);
   lc.sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
 
   // ---- this pair's run of chunks (as the waves of attn_mfma_kernel) ----
@@ -1369,14 +1424,23 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     const int trow = (tid >> 1) & 255;
     const bool tval = tid >= 512;
     uint32_t tw0, tw1;  // this thread's table words
-    if (kFull) {
+    if constexpr (kBits != 4) {
+      // row f: the draft of anchor field f (sign-extended), the code
+      // a * 2^(8-b) + 2^(7-b) - 1
+      constexpr int RB = 8 - kBits;
+      const int f = trow & ((1 << kBits) - 1);
+      const int a = f >= (1 << (kBits - 1)) ? f - (1 << kBits) : f;
+      const int code = (a * (1 << RB) + (1 << (RB - 1)) - 1) & 255;
+      tw0 = tval ? tab.full[code] : tab.kfull[code];
+      tw1 = tw0;
+    } else if (kFull) {
       tw0 = tval ? tab.full[trow] : tab.kfull[trow];
       tw1 = tw0;
     } else {
       tw0 = tval ? tab.draft[trow & 15] : tab.kdraft[trow & 15];
       tw1 = tval ? tab.draft[trow >> 4] : tab.kdraft[trow >> 4];
     }
-    const u32x4 v = kFull ? u32x4{tw0, tw0, tw0, tw0} : u32x4{tw0, tw1, tw0, tw1};
+    const u32x4 v = kWordTable ? u32x4{tw0, tw0, tw0, tw0} : u32x4{tw0, tw1, tw0, tw1};
     u32x4 *dst = reinterpret_cast<u32x4 *>(lut + trow * 256 + (tval ? kValueHalf : 0) + (tid & 1) * 64);
 #pragma unroll
     for (int k = 0; k < 4; ++k) dst[k] = v;
@@ -1429,12 +1493,12 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     // bytes before it requests the next chunk's codes into the same
     // registers, and stages the next chunk's constants before it requests
     // the scales of the chunk after that.
-    KCodes kc;
+    KCodes<kBits> kc;
     KScales ks;
     long long pg_c = page_in_run(cb);      // page of the chunk whose codes kc holds
     long long pg_s = page_in_run(cb + 1);  // page of the chunk whose scales ks holds next
     load_kscales(ks, kp, tile_of(pg_c), chunk_of(pg_c, cb), lc.soff);
-    load_kcodes<kFull>(kc, kp, tile_of(pg_c), chunk_of(pg_c, cb), lc.koff);
+    load_kcodes<kFull, kBits>(kc, kp, tile_of(pg_c), chunk_of(pg_c, cb), lc);
     const float qmax = setup_query();
     __syncthreads();  // tables and q
     double inv = stage_kslot(ks, kslot, lc.lane, qmax, q64);
@@ -1448,11 +1512,11 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
       const int c = cb + si;
       const long long cur = pg_c;
       uint32_t e[2][4], o[2][4];
-      key_bytes<kFull>(kc, e, o);
+      key_bytes<kFull, kBits>(kc, e, o);
       pg_c = pg_s;
-      load_kcodes<kFull>(kc, kp, tile_of(pg_c), chunk_of(pg_c, c + 1), lc.koff);
+      load_kcodes<kFull, kBits>(kc, kp, tile_of(pg_c), chunk_of(pg_c, c + 1), lc);
       if (cur >= 0)
-        score_chunk<kFull>(e, o, kslot, inv, bias, lc, lut, m_run, l_run,
+        score_chunk<kFull, kBits>(e, o, kslot, inv, bias, lc, lut, m_run, l_run,
                            srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr,
                            hand0 + (si & 1) * kHandBytes);
       wave_lds_sync();
@@ -1468,13 +1532,13 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     char *vslot = smem + kPVSlotOff + pr * kVSlotBytes;
     // codes of chunk c in buffer (c - cb) % 2; one scale buffer, refilled
     // after the next chunk's constants are staged
-    VCodes vc[2];
+    VCodes<kBits> vc[2];
     VScales vs;
     long long pg[2];
     pg[0] = page_in_run(cb);
     pg[1] = page_in_run(cb + 1);
     load_vscales(vs, vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc.soff);
-    load_vcodes<kFull>(vc[0], vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc.voff);
+    load_vcodes<kFull, kBits>(vc[0], vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc);
     setup_tables();
     __syncthreads();  // tables and q
     stage_vslot(vs, vslot, lc.lane);
@@ -1488,9 +1552,9 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
       if (si - 1 < nrun) {
         const long long cur = pg[J];
         pg[J] = page_in_run(c + 2);
-        load_vcodes<kFull>(vc[J ^ 1], vp, tile_of(pg[J ^ 1]), chunk_of(pg[J ^ 1], c + 1), lc.voff);
+        load_vcodes<kFull, kBits>(vc[J ^ 1], vp, tile_of(pg[J ^ 1]), chunk_of(pg[J ^ 1], c + 1), lc);
         if (cur >= 0)
-          value_chunk<kFull>(vc[J], vslot, lc, lut, acc, hand0 + ((si - 1) & 1) * kHandBytes);
+          value_chunk<kFull, kBits>(vc[J], vslot, lc, lut, acc, hand0 + ((si - 1) & 1) * kHandBytes);
         wave_lds_sync();
         stage_vslot(vs, vslot, lc.lane);  // constants of chunk c + 1
         load_vscales(vs, vp, tile_of(pg[J]), chunk_of(pg[J], c + 2), lc.soff);
@@ -1712,8 +1776,10 @@ void launch_mfma_kernel(dim3 grid, hipStream_t stream, const uint16_t *q, const 
                         const PlanesArg &v, const int32_t *block_table, const int32_t *seq_lens,
                         const AttnShape &s, float sm_scale, float *out, float *scores,
                         void *workspace, const MfmaTables &tables) {
-  if constexpr (kBits == 4)
-    hipLaunchKernelGGL((attn_pair_kernel<kFull>), grid, dim3(kPThreads), 0, stream, q, k, v,
+  // the 4 + 4 planes and the drafts of the other cuts run on the K/V wave
+  // pairs; the full code of a cut keeps the single-wave kernel
+  if constexpr (kBits == 4 || !kFull)
+    hipLaunchKernelGGL((attn_pair_kernel<kFull, kBits>), grid, dim3(kPThreads), 0, stream, q, k, v,
                        block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<kFull, kBits>), grid, dim3(kThreads), 0, stream, q, k, v,
