@@ -471,6 +471,25 @@ def test_ragged_lengths_group_sizes_and_skipped_pages(lynx):
             check_attention(got, ref, "ragged H=%d Hq=%d full=%s" % (H, Hq, full))
 
 
+@pytest.mark.parametrize("Hq", [8, 4])
+def test_most_splits_per_head(lynx, Hq):
+    """One request and one KV head over 256 pages: one page per block, so the
+    split combine merges 256 parts per head (the most attention_shape makes),
+    past the parts a combine thread preloads, for GQA groups 8 and 4."""
+    H, P = 1, 256
+    x_k = synth.laplace_pages(P, H, 128, seed=81, scale_channels=((0, 3, 90.0),))
+    x_v = synth.laplace_pages(P, H, 128, seed=82, scale_channels=((0, 77, 50.0),))
+    pk, ek, _, _ = check_encode(lynx, x_k, 0)
+    pv, ev, _, _ = check_encode(lynx, x_v, 1)
+    rng = np.random.default_rng(83)
+    q = synth.float_to_bf16_bits(rng.laplace(0, 1, (1, Hq, 128)).astype(np.float32))
+    for full in (False, True):
+        print("most splits Hq=%d full=%s" % (Hq, full), flush=True)
+        ref = oracle_attention_for(ek, ev, q, [list(range(P))], full)
+        got = run_gpu_attention(lynx, q, pk, pv, P, full)
+        check_attention(got, ref, "256 splits Hq=%d full=%s" % (Hq, full))
+
+
 def test_uneven_runs_across_the_pairs_of_a_block(lynx):
     """Runs of 3 pages per block, so each of a block's 8 K/V wave pairs takes
     3 chunks; the last block of request 1 (2 pages left by its length) gives
