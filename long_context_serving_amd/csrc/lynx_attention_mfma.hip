@@ -41,19 +41,18 @@
 // whose probabilities lane (n, r) provides: tokens 4r..4r+3 (step 0) and
 // 16+4r..16+4r+3 (step 1).
 //
-// Work split: one workgroup of 8 waves (one per CU: the registers of a
-// chunk in flight allow 2 waves per SIMD) per (request, KV head, run of
-// pages); each wave streams a contiguous run of chunks with the next
-// chunk's codes and scales in flight while the current one is computed.
-// Between chunks a wave stages the next chunk's constants in LDS, the W
-// words of all its (channel, head) pairs among them, so that a score step
-// only reads its four W words.  The block merges its waves
-// through LDS and writes the output itself when one run covers the request;
-// otherwise it writes a partial (base-2 max m, sum l, unnormalised o) and a
-// second, small kernel merges the runs exactly.
+// Work split: one workgroup of 16 waves (8 K/V wave pairs, one workgroup per
+// CU) per (request, KV head, run of pages); each pair streams a contiguous
+// part of the run, the K wave scoring chunk c while the V wave sums the
+// values of chunk c - 1, each with its next chunk's codes and scales in
+// flight.  Between chunks the K wave stages the next chunk's W words and
+// c0 in LDS, so that a score step only reads its four W words.  The block
+// merges its pairs through LDS and writes the output itself when one run
+// covers the request; otherwise it writes a partial (base-2 max m, sum l,
+// unnormalised o) and a second, small kernel merges the runs exactly.
 //
 // Other cuts of the code (page "Lynx: the KV cache does not have to arrive
-// whole", section 7 names 6 + 2, 2 + 6 and 5 + 3): the same kernel reads a
+// whole", section 7 names 6 + 2, 2 + 6 and 5 + 3): the kernel reads a
 // b-bit anchor stream (and an (8 - b)-bit residual stream), where a unit of
 // 32 elements -- the 16 bytes of a 4-bit plane -- is b words with the
 // fields least significant first.  A key lane reads its whole unit; a value
@@ -74,8 +73,6 @@ namespace {
 
 using namespace lanes;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kHeads = 8;  // MFMA columns per part
 constexpr float kSlack = 8.0f;  // log2 of the largest probability before rescaling
 
@@ -92,30 +89,19 @@ constexpr float kSlack = 8.0f;  // log2 of the largest probability before rescal
 // 128-byte offset.
 constexpr int kValueHalf = 128;
 constexpr int kTableBytes = 256 * 256;
-// Per wave, one slot of the chunk constants (the next chunk's are staged
-// after the current chunk's products have read it): the W words of the
-// score products, [8 heads][32 units of 4 channels + 1 pad unit] x 16 B
-// (the pad turns each head's row by 4 banks, so the 8 heads of one read
-// pass meet different banks), then c0k f64[128] | c1v f32[128] | c0v f32[128].
+// The W words of a chunk's score products: [8 heads][32 units of 4
+// channels + 1 pad unit] x 16 B (the pad turns each head's row by 4 banks,
+// so the 8 heads of one read pass meet different banks).
 constexpr int kWRowBytes = 33 * 16;
 constexpr int kWBytes = kHeads * kWRowBytes;
-constexpr int kSlotBytes = kWBytes + 1024 + 512 + 512;
-constexpr int kScaleOff = kTableBytes;
 // q as f64 [8 heads][130]: rows padded by 16 bytes, which turns each head's
 // row by 4 banks, so the lanes of one LDS pass, which read the same
 // channels of different heads, meet different banks
 constexpr int kQStride = kDim + 2;
-constexpr int kQOff = kScaleOff + kWaves * kSlotBytes;
-constexpr int kLdsBytes = kQOff + kHeads * kQStride * 8;
-// after the chunk loop the table and slot space holds the block merge: o of
-// every wave [wave][16 col][128 ch] f32, then m, l of every wave's 8 heads
 // Merge staging of the waves' value sums: rows of 128 floats padded to 132,
 // so that the 8 lanes of each 128-byte pass of a 16-byte store (8 rows, one
 // per lane) fall on 8 different 4-bank groups.
 constexpr int kORow = kDim + 4;
-constexpr int kMlOff = kWaves * 16 * kORow * 4;
-static_assert(kMlOff + kWaves * 2 * kHeads * 4 <= kQOff, "merge area must fit the table and slot space");
-static_assert(kSlotBytes % 16 == 0 && kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 
 struct MfmaTables {
   uint32_t full[256];   // code byte (a << 4 | r) -> fp16 hi | fp16 lo << 16 of yhat
@@ -219,70 +205,11 @@ __device__ __forceinline__ u32x4 operand_bytes(uint32_t x, uint32_t lb, const ch
 }
 
 // ---- streamed chunk data ----------------------------------------------------
-struct Codes {
-  u32x4 ka[2], kr[2];  // K tile t: anchor / residual of channels 32r.. of token 16t + n
-  uint32_t va[8], vr[8];  // V: word r of channel 16ct + n
-};
-// Codes of a chunk in b + (8 - b) streams: K tile t (token 16t + n,
-// channels 32r ..) is a whole unit; V channel 16ct + n holds the lane's
-// fields in its window words.
-template <int B>
-struct CutCodes {
-  static constexpr int RB = 8 - B;
-  static constexpr int VA = cut_window_words(B), VR = cut_window_words(RB);
-  uint32_t ka[2][B], kr[2][RB];
-  uint32_t va[8][VA], vr[8][VR];
-};
-struct Scales {
-  float2 mnk, rgk, muk, sk, mnv, rgv, muv, sv;  // channels 2l, 2l+1
-};
-
 __device__ __forceinline__ u32x4 load_nt(const u32x4 *p) {
   return __builtin_nontemporal_load(p);
 }
 __device__ __forceinline__ uint32_t load_nt(const uint32_t *p) {
   return __builtin_nontemporal_load(p);
-}
-
-// The tile and chunk are wave-uniform: the chunk's base address is scalar
-// and each lane adds a 32-bit offset (kept in one VGPR).
-template <bool kFull>
-__device__ __forceinline__ void load_codes(Codes &cd, const PlanesArg &kp, const PlanesArg &vp,
-                                           size_t tile, int c, uint32_t koff, uint32_t voff) {
-  const size_t cbytes = tile * kPlaneTileBytes + static_cast<size_t>(c) * (kChunk * kDim / 2);
-  const char *ka = reinterpret_cast<const char *>(kp.anchor) + cbytes;
-  cd.ka[0] = load_nt(reinterpret_cast<const u32x4 *>(ka + koff));
-  cd.ka[1] = load_nt(reinterpret_cast<const u32x4 *>(ka + koff + 1024));
-  if (kFull) {
-    const char *kr = reinterpret_cast<const char *>(kp.residual) + cbytes;
-    cd.kr[0] = load_nt(reinterpret_cast<const u32x4 *>(kr + koff));
-    cd.kr[1] = load_nt(reinterpret_cast<const u32x4 *>(kr + koff + 1024));
-  }
-  const char *va = reinterpret_cast<const char *>(vp.anchor) + cbytes;
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) cd.va[ct] = load_nt(reinterpret_cast<const uint32_t *>(va + voff + ct * 256));
-  if (kFull) {
-    const char *vr = reinterpret_cast<const char *>(vp.residual) + cbytes;
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) cd.vr[ct] = load_nt(reinterpret_cast<const uint32_t *>(vr + voff + ct * 256));
-  }
-}
-
-__device__ __forceinline__ void load_scales(Scales &sc, const PlanesArg &kp, const PlanesArg &vp,
-                                            size_t tile, int c, uint32_t soff) {
-  const size_t pb = tile * kDim * 4;
-  const size_t cb = (tile * kChunks + c) * kDim * 4;
-  auto f2 = [soff](const float *base, size_t off) {
-    return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(base) + off + soff);
-  };
-  sc.muk = f2(kp.chunk_mean, cb);
-  sc.sk = f2(kp.chunk_maxabs, cb);
-  sc.muv = f2(vp.chunk_mean, cb);
-  sc.sv = f2(vp.chunk_maxabs, cb);
-  sc.mnk = f2(kp.page_min, pb);
-  sc.rgk = f2(kp.page_range, pb);
-  sc.mnv = f2(vp.page_min, pb);
-  sc.rgv = f2(vp.page_range, pb);
 }
 
 // W word of one (channel, head) for the level products: the floor of
@@ -295,62 +222,11 @@ __device__ __forceinline__ uint32_t w_bytes(double q, double c1s) {
   return static_cast<uint32_t>(__builtin_fma(q, c1s, kBias)) ^ 0x80808080u;
 }
 
-// Chunk constants into an LDS slot.  c1k = rg * s is formed in fp64
-// (exact) and scaled by 2^S, S = 29 - e with e the exponent of qmax *
-// max c1k (qmax = largest |q| of the group), so every |q * c1k * 2^S| stays
-// below 2^30 (the fp32 maximum can undercut the fp64 one by an ulp, which
-// still leaves it below 2^31 - 2^24, the range of a 4-byte signed split).
-// Lane l forms the W words of channels 2l, 2l + 1 for the 8 heads (q from
-// the block's f64 copy) and c0k, c1v, c0v of its two channels; returns
-// 2^-(S + 22), the weight of the level sum assembled in compute_chunk.
-__device__ __forceinline__ double scale_stage(const Scales &sc, char *slot, int lane, float qmax,
-                                              const double *q64) {
-  const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // bound only
-  const float bound = qmax * wave_max(fmaxf(c1a, c1b));
-  int S = 0;
-  const uint32_t eb = (__float_as_uint(bound) >> 23) & 0xFFu;
-  if (bound > 0.0f && eb != 0xFFu) {
-    // exponent of a normal or subnormal positive float
-    const int e = eb != 0u ? static_cast<int>(eb) - 127
-                           : -127 - __builtin_clz(__float_as_uint(bound)) + 9;
-    S = 29 - e;
-  }
-  const double ks = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + S) << 52);
-  const double inv = __builtin_bit_cast(double, static_cast<uint64_t>(1023 - S - 22) << 52);
-  const double c1x = static_cast<double>(sc.rgk.x) * sc.sk.x * ks;
-  const double c1y = static_cast<double>(sc.rgk.y) * sc.sk.y * ks;
-  // W of channels 2l, 2l + 1 sit in unit l / 2 of each head's row
-  char *wdst = slot + (lane >> 1) * 16 + (lane & 1) * 8;
-  const double *qsrc = q64 + 2 * lane;
-#pragma unroll
-  for (int hh = 0; hh < kHeads; ++hh) {
-    const double2 qq = *reinterpret_cast<const double2 *>(qsrc + hh * kQStride);
-    *reinterpret_cast<uint2 *>(wdst + hh * kWRowBytes) = make_uint2(w_bytes(qq.x, c1x), w_bytes(qq.y, c1y));
-  }
-  double *c0k = reinterpret_cast<double *>(slot + kWBytes);
-  float *c1v = reinterpret_cast<float *>(c0k + kDim);
-  float *c0v = c1v + kDim;
-  reinterpret_cast<double2 *>(c0k)[lane] =
-      make_double2(static_cast<double>(sc.mnk.x) + static_cast<double>(sc.rgk.x) * sc.muk.x,
-                   static_cast<double>(sc.mnk.y) + static_cast<double>(sc.rgk.y) * sc.muk.y);
-  reinterpret_cast<float2 *>(c1v)[lane] = make_float2(sc.rgv.x * sc.sv.x, sc.rgv.y * sc.sv.y);
-  reinterpret_cast<float2 *>(c0v)[lane] =
-      make_float2(__builtin_fmaf(sc.rgv.x, sc.muv.x, sc.mnv.x), __builtin_fmaf(sc.rgv.y, sc.muv.y, sc.mnv.y));
-  return inv;
-}
-
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-
-// Running state of one wave: per lane, head n & 7, column n of the value sum.
-struct RunState {
-  float m;          // running max of the base-2 scores
-  float l;          // running sum of exp2(score - m)
-  floatx4 acc[8];   // O^T rows 16ct + 4r + i, column n
-};
 
 struct LaneConst {
   int n, r, lane;
@@ -385,578 +261,16 @@ __device__ __forceinline__ void cut_lane_offsets(LaneConst &lc) {
   lc.vsr = static_cast<uint32_t>((lc.r * RB) & 3);
 }
 
-// Codes of chunk c of a tile from b + (8 - b) streams: a tile is 1024
-// units, a chunk 128 (4 * B bytes per unit of the anchor stream).
-template <bool kFull, int B>
-__device__ __forceinline__ void load_codes_cut(CutCodes<B> &cd, const PlanesArg &kp,
-                                               const PlanesArg &vp, size_t tile, int c,
-                                               const LaneConst &lc) {
-  using C = CutCodes<B>;
-  constexpr int RB = C::RB;
-  const size_t unit0 = tile * 1024 + static_cast<size_t>(c) * 128;
-  const char *ka = reinterpret_cast<const char *>(kp.anchor) + unit0 * (4 * B);
-  const char *va = reinterpret_cast<const char *>(vp.anchor) + unit0 * (4 * B);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < B; ++i)
-      cd.ka[t][i] = load_nt(reinterpret_cast<const uint32_t *>(ka + lc.kca + t * 256 * B + 4 * i));
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-    for (int j = 0; j < C::VA; ++j)
-      cd.va[ct][j] = load_nt(reinterpret_cast<const uint32_t *>(va + ct * 64 * B + lc.vwa[j]));
-  if (kFull) {
-    const char *kr = reinterpret_cast<const char *>(kp.residual) + unit0 * (4 * RB);
-    const char *vr = reinterpret_cast<const char *>(vp.residual) + unit0 * (4 * RB);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < RB; ++i)
-        cd.kr[t][i] = load_nt(reinterpret_cast<const uint32_t *>(kr + lc.kcr + t * 256 * RB + 4 * i));
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int j = 0; j < C::VR; ++j)
-        cd.vr[ct][j] = load_nt(reinterpret_cast<const uint32_t *>(vr + ct * 64 * RB + lc.vwr[j]));
-  }
-}
-
-// Table index bytes of a K unit: x[w][h] holds elements 8w + 4h .. + 3.
-template <bool kFull, int B>
-__device__ __forceinline__ void cut_key_bytes(const uint32_t (&a)[B], const uint32_t (&r)[8 - B],
-                                              uint32_t (&x)[4][2]) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      x[w][h] = cut_bytes<B>(a, 8 * w + 4 * h);
-      if (kFull) x[w][h] = (x[w][h] << (8 - B)) | cut_bytes<8 - B>(r, 8 * w + 4 * h);
-    }
-}
-
-// One chunk: scores, online softmax (base 2), value sum.  kBits = 4 reads
-// the 4-bit planes, other values b + (8 - b) streams.
-template <bool kFull, int kBits, class CodesT>
-__device__ __forceinline__ void compute_chunk(const CodesT &cd, const char *slot, double inv_s,
-                                              const double *q64, const LaneConst &lc,
-                                              const char *lut, RunState &st, float *srow) {
-  const int n = lc.n, r = lc.r;
-  const double *c0k = reinterpret_cast<const double *>(slot + kWBytes);
-  const float *c1v = reinterpret_cast<const float *>(c0k + kDim);
-  const float *c0v = c1v + kDim;
-
-  // ---- chunk bias sum_d q_d c0k_d in fp64: lane takes channels 32r + 16*lo .. +15 ----
-  double bias;
-  {
-    const int d0 = 32 * r + (lc.lo ? 16 : 0);
-    const double *qh = q64 + (n & 7) * kQStride + d0;
-    double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-    for (int k = 0; k < 16; k += 2) {
-      const double2 qq = *reinterpret_cast<const double2 *>(qh + k);
-      const double2 cc = *reinterpret_cast<const double2 *>(c0k + d0 + k);
-      a0 = fma(qq.x, cc.x, a0);
-      a1 = fma(qq.y, cc.y, a1);
-    }
-    bias = a0 + a1;
-    bias += ror8(bias);
-    bias = xrows_sum(bias);
-  }
-
-  // ---- scores: S^T = Yk * W, three level products per tile (exact int32) ----
-  i32x4 sa0 = {0, 0, 0, 0}, sb0 = {0, 0, 0, 0}, sc0 = {0, 0, 0, 0};
-  i32x4 sa1 = {0, 0, 0, 0}, sb1 = {0, 0, 0, 0}, sc1 = {0, 0, 0, 0};
-  {
-    // 4 + 4: code bytes of even / odd elements (full) or the anchor words
-    // (draft); cuts: table index bytes of elements 8w + 4h ..
-    uint32_t e0[4], o0[4], e1[4], o1[4];
-    uint32_t x0[4][2], x1[4][2];
-    if constexpr (kBits == 4) {
-      const uint32_t ka0[4] = {cd.ka[0][0], cd.ka[0][1], cd.ka[0][2], cd.ka[0][3]};
-      const uint32_t ka1[4] = {cd.ka[1][0], cd.ka[1][1], cd.ka[1][2], cd.ka[1][3]};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if (kFull) {
-          code_bytes(ka0[w], cd.kr[0][w], e0[w], o0[w]);
-          code_bytes(ka1[w], cd.kr[1][w], e1[w], o1[w]);
-        } else {
-          e0[w] = ka0[w];
-          e1[w] = ka1[w];
-        }
-      }
-    } else {
-      cut_key_bytes<kFull, kBits>(cd.ka[0], cd.kr[0], x0);
-      cut_key_bytes<kFull, kBits>(cd.ka[1], cd.kr[1], x1);
-    }
-    // W words of channels 32r + 4 stp .. + 3 of the lane's head (lanes n
-    // and n + 8 read the same unit)
-    const char *wrow = slot + (n & 7) * kWRowBytes + r * 128;
-#pragma unroll
-    for (int stp = 0; stp < 8; ++stp) {
-      const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + stp * 16);
-      i32x4 ba, bb, bc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ba[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[0]));
-        bb[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[1]));
-        bc[i] = static_cast<int>(__builtin_amdgcn_perm(wv[i], wv[i], lc.lvl[2]));
-      }
-      u32x4 a0, a1;
-      const int w = stp >> 1;
-      if constexpr (kBits != 4) {
-        a0 = operand_bytes(x0[w][stp & 1], lc.lbk, lut);
-        a1 = operand_bytes(x1[w][stp & 1], lc.lbk, lut);
-      } else if (kFull) {
-        if (stp & 1) {
-          a0 = operand_full<1>(e0[w], o0[w], lc.lbk, lut);
-          a1 = operand_full<1>(e1[w], o1[w], lc.lbk, lut);
-        } else {
-          a0 = operand_full<0>(e0[w], o0[w], lc.lbk, lut);
-          a1 = operand_full<0>(e1[w], o1[w], lc.lbk, lut);
-        }
-      } else {
-        if (stp & 1) {
-          a0 = operand_draft<1>(e0[w], lc.lbk, lut);
-          a1 = operand_draft<1>(e1[w], lc.lbk, lut);
-        } else {
-          a0 = operand_draft<0>(e0[w], lc.lbk, lut);
-          a1 = operand_draft<0>(e1[w], lc.lbk, lut);
-        }
-      }
-      const i32x4 y0 = __builtin_bit_cast(i32x4, a0), y1 = __builtin_bit_cast(i32x4, a1);
-      sa0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, ba, sa0, 0, 0, 0);
-      sa1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, ba, sa1, 0, 0, 0);
-      sb0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, bb, sb0, 0, 0, 0);
-      sb1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, bb, sb1, 0, 0, 0);
-      sc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y0, bc, sc0, 0, 0, 0);
-      sc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(y1, bc, sc1, 0, 0, 0);
-    }
-  }
-
-  // ---- assemble: lanes n < 8 take tile 0, lanes n >= 8 tile 1 (tokens 16t + 4r + i) ----
-  // Levels 6, 4, 2 sit in columns n < 8, levels 5, 3, 1 in columns n >= 8:
-  // the high levels are this lane's own tile 0 (n < 8) or lane n - 8's tile
-  // 1, the low levels lane n + 8's tile 0 (n < 8) or this lane's tile 1.
-  const double scale2 = lc.sm2 * inv_s;
-  const double bias2 = bias * lc.sm2;
-  double sc2[4];
-  float cmax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    auto hi = [](int t0, int t1) {
-      return __builtin_bit_cast(int, ror8_to_hi(__builtin_bit_cast(float, t0), __builtin_bit_cast(float, t1)));
-    };
-    auto lo = [](int t1, int t0) {
-      return __builtin_bit_cast(int, ror8_to_lo(__builtin_bit_cast(float, t1), __builtin_bit_cast(float, t0)));
-    };
-    const int l6 = hi(sa0[i], sa1[i]), l5 = lo(sa1[i], sa0[i]);
-    const int l4 = hi(sb0[i], sb1[i]), l3 = lo(sb1[i], sb0[i]);
-    const int l2 = hi(sc0[i], sc1[i]), l1 = lo(sc1[i], sc0[i]);
-    // sum_L C_L 2^(8L) / 2^8.  C_L sums at most 128 * min(L + 1, 7 - L) byte
-    // products of magnitude <= 2^14, so C_6 * 2^8 + C_5, C_4 * 2^8 + C_3 and
-    // C_2 * 2^8 + C_1 stay inside int32, and the rest is fp64.
-    const int a = l6 * 256 + l5, b2 = l4 * 256 + l3, c2 = l2 * 256 + l1;
-    const double t = fma(fma(static_cast<double>(a), 65536.0, static_cast<double>(b2)), 65536.0,
-                         static_cast<double>(c2));
-    sc2[i] = fma(t, scale2, bias2);
-    cmax = fmaxf(cmax, static_cast<float>(sc2[i]));
-  }
-  cmax = fmaxf(cmax, ror8(cmax));
-  cmax = xrows(cmax, MaxOp());
-  // The reference maximum moves only when a score exceeds it by more than
-  // 2^8 (base 2), so probabilities stay below 256 and most chunks need no
-  // rescaling of the running sums.
-  const bool rescale = __builtin_amdgcn_ballot_w64(cmax > st.m + kSlack) != 0;
-  float alpha = 1.0f;
-  if (rescale) {
-    const float m_new = fmaxf(st.m, cmax);
-    alpha = st.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
-    st.m = m_new;
-  }
-  float p[4];
-  float psum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(static_cast<float>(sc2[i] - static_cast<double>(st.m)));
-    psum += p[i];
-  }
-  psum += ror8(psum);
-  psum = xrows(psum, SumOp());
-  st.l = st.l * alpha + psum;
-  if (srow != nullptr) {
-    // natural-log logits of tokens (16 * lo + 4r .. +3) of this chunk
-    constexpr double kLn2 = 0.69314718055994530942;
-    *reinterpret_cast<float4 *>(srow + (lc.lo ? 16 : 0) + 4 * r) =
-        make_float4(static_cast<float>(sc2[0] * kLn2), static_cast<float>(sc2[1] * kLn2),
-                    static_cast<float>(sc2[2] * kLn2), static_cast<float>(sc2[3] * kLn2));
-  }
-
-  // ---- P operands: step h holds tokens 16h + 4r + i of column n ----
-  half8 pa0, pa1;
-  {
-    u32x4 w0, w1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float t0 = ror8_to_hi(p[i], p[i]);  // tile 0: own (n < 8) or from n - 8
-      const float t1 = ror8_to_lo(p[i], p[i]);  // tile 1: from n + 8 (n < 8) or own
-      w0[i] = split_dup(t0, lc.keep_mask);
-      w1[i] = split_dup(t1, lc.keep_mask);
-    }
-    pa0 = __builtin_bit_cast(half8, w0);
-    pa1 = __builtin_bit_cast(half8, w1);
-  }
-
-  // ---- values: O^T += Yv^T * P, then the chunk's affine map ----
-  if (rescale) {
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alpha;
-  }
-  const float pc0 = lc.lo ? 0.0f : psum;  // the c0v term once per head (high half)
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    half8 y0, y1;
-    if constexpr (kBits != 4) {
-      uint32_t win[2];
-      cut_align<CodesT::VA>(cd.va[ct], lc.vsa, win);
-      uint32_t xa = cut_bytes<kBits>(win, 0), xb = cut_bytes<kBits>(win, 4);
-      if (kFull) {
-        uint32_t wr[2];
-        cut_align<CodesT::VR>(cd.vr[ct], lc.vsr, wr);
-        xa = (xa << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 0);
-        xb = (xb << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 4);
-      }
-      y0 = __builtin_bit_cast(half8, operand_bytes(xa, lc.lbv, lut));
-      y1 = __builtin_bit_cast(half8, operand_bytes(xb, lc.lbv, lut));
-    } else if (kFull) {
-      uint32_t e, o;
-      code_bytes(cd.va[ct], cd.vr[ct], e, o);
-      y0 = __builtin_bit_cast(half8, operand_full<0>(e, o, lc.lbv, lut));
-      y1 = __builtin_bit_cast(half8, operand_full<1>(e, o, lc.lbv, lut));
-    } else {
-      y0 = __builtin_bit_cast(half8, operand_draft<0>(cd.va[ct], lc.lbv, lut));
-      y1 = __builtin_bit_cast(half8, operand_draft<1>(cd.va[ct], lc.lbv, lut));
-    }
-    floatx4 ov = {0.0f, 0.0f, 0.0f, 0.0f};
-    ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pa0, ov, 0, 0, 0);
-    ov = __builtin_amdgcn_mfma_f32_16x16x32_f16(y1, pa1, ov, 0, 0, 0);
-    const float4 a1 = *reinterpret_cast<const float4 *>(c1v + 16 * ct + 4 * r);
-    const float4 a0 = *reinterpret_cast<const float4 *>(c0v + 16 * ct + 4 * r);
-    st.acc[ct][0] = __builtin_fmaf(a1.x, ov[0], __builtin_fmaf(a0.x, pc0, st.acc[ct][0]));
-    st.acc[ct][1] = __builtin_fmaf(a1.y, ov[1], __builtin_fmaf(a0.y, pc0, st.acc[ct][1]));
-    st.acc[ct][2] = __builtin_fmaf(a1.z, ov[2], __builtin_fmaf(a0.z, pc0, st.acc[ct][2]));
-    st.acc[ct][3] = __builtin_fmaf(a1.w, ov[3], __builtin_fmaf(a0.w, pc0, st.acc[ct][3]));
-  }
-}
-
-template <bool kFull, int kBits>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(
-    const uint16_t *__restrict__ q, PlanesArg kp, PlanesArg vp,
-    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
-    AttnShape s, float sm_scale, float *__restrict__ out, float *__restrict__ scores, void *ws,
-    MfmaTables tab) {
-  __shared__ __align__(16) char smem[kLdsBytes];
-  char *lut = smem;
-  double *q64 = reinterpret_cast<double *>(smem + kQOff);
-  float *s_ml = reinterpret_cast<float *>(smem + kMlOff);
-
-  // blocks of one (request, KV head) are consecutive logical blocks; spread
-  // over the 8 XCDs in contiguous groups so that they share one L2
-  const unsigned nblk = gridDim.x;
-  unsigned lb_idx = blockIdx.x;
-  if ((nblk & 7u) == 0u) lb_idx = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int split = static_cast<int>(lb_idx % static_cast<unsigned>(s.splits));
-  const int bh = static_cast<int>(lb_idx / static_cast<unsigned>(s.splits));
-  const int h = bh % s.heads;
-  const int b = bh / s.heads;  // query row
-  const int req = b / s.tq;     // its request
-  const int g = s.group;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
-
-  LaneConst lc;
-  lc.lane = tid & 63;
-  lc.n = lc.lane & 15;
-  lc.r = lc.lane >> 4;
-  lc.lo = lc.n >= 8;
-  lc.koff = static_cast<uint32_t>(lc.n * 64 + lc.r * 16);
-  lc.voff = static_cast<uint32_t>(lc.n * 16 + lc.r * 4);
-  lc.soff = static_cast<uint32_t>(lc.lane * 8);
-  lc.keep_mask = lc.lo ? 0xFFFFE000u : 0u;
-  // word copies for the full code and for every cut's index bytes, pair
-  // copies for the 4 + 4 draft; the value table sits 64 KiB up
-  constexpr bool kWordTable = kFull || kBits != 4;
-  lc.lbk = kWordTable ? static_cast<uint32_t>((lc.lane & 31) * 4) : static_cast<uint32_t>((lc.lane & 15) * 8);
-  lc.lbv = lc.lbk | static_cast<uint32_t>(kValueHalf);
-  // W bytes of this column's levels: 6, 4, 2 (n < 8) or 5, 3, 1 (n >= 8)
-  lc.lvl[0] = lc.lo ? 0x02030C0Cu : 0x030C0C0Cu;
-  lc.lvl[1] = lc.lo ? 0x00010203u : 0x0102030Cu;
-  lc.lvl[2] = lc.lo ? 0x0C0C0001u : 0x0C000102u;
-  if constexpr (kBits != 4) cut_lane_offsets<kBits>(lc);
-  lc.sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
-
-  // ---- this wave's run of chunks ----
-  // request metadata is read-only for the launch: read it through the
-  // constant address space so the wave-uniform reads become scalar loads
-  // (counted apart from the streaming vector loads)
-  const __attribute__((address_space(4))) int32_t *bt_c =
-      (const __attribute__((address_space(4))) int32_t *)block_table;
-  const __attribute__((address_space(4))) int32_t *sl_c =
-      (const __attribute__((address_space(4))) int32_t *)seq_lens;
-  int npages = s.max_pages;
-  if (seq_lens) {
-    npages = sl_c[req] / kPage;
-    npages = npages < 0 ? 0 : (npages > s.max_pages ? s.max_pages : npages);
-  }
-  const int pps = s.pages_per_split;
-  const int p0 = split * pps;
-  int p1 = p0 + pps;
-  p1 = p1 > npages ? npages : p1;
-  int cb = p0 * kChunks + w * pps;
-  int ce = cb + pps;
-  if (ce > p1 * kChunks) ce = p1 * kChunks;
-  if (cb > ce) cb = ce;
-
-  char *slot = smem + kScaleOff + w * kSlotBytes;
-  // page of chunk ci, or -1 when the block table marks it absent
-  auto page_of = [&](int ci) -> long long {
-    const int lp = ci >> 3;
-    const long long pg = block_table ? bt_c[static_cast<size_t>(req) * s.max_pages + lp]
-                                     : static_cast<long long>(req) * s.max_pages + lp;
-    return (pg < 0 || pg >= s.pool_pages) ? -1 : pg;
-  };
-
-  // Codes of NB chunks are held per wave: the chunk being computed and the
-  // next D = NB - 1 in flight (the 4 + 4 draft's chunks are smaller, so it
-  // looks further ahead; the cuts' unpacking leaves no registers for a
-  // third chunk).  Scales run one chunk further ahead than codes: the step
-  // of chunk c requests the scales of chunk c + D + 1 and then the codes of
-  // chunk c + D, so the scales staged at the end of a step were requested
-  // before the codes that step waited for.  A wave whose run is short thus
-  // pays one memory round trip in its prologue and not one per chunk.
-  // Every step issues its loads unconditionally -- a chunk past the run or
-  // on an absent page reads chunk 0 of pool page 0 instead, and is not
-  // computed -- so the wait counts the compiler derives are exact and never
-  // wait for loads that are still ahead in the pipeline.
-  constexpr int NB = (kFull || kBits != 4) ? 2 : 3;
-  constexpr int D = NB - 1;
-  using CodesT = std::conditional_t<kBits == 4, Codes, CutCodes<kBits>>;
-  CodesT cds[NB];   // codes of chunk c in buffer (c - cb) % NB
-  Scales scs[NB];   // scales of chunk c in buffer (c - cb) % NB
-  long long pgs[NB];  // page of chunk c, and after its step of chunk c + NB
-  auto tile_of = [&](long long pg) { return pg >= 0 ? static_cast<size_t>(pg) * s.heads + h : 0; };
-  auto chunk_of = [&](long long pg, int c) { return pg >= 0 ? (c & 7) : 0; };
-  auto page_in_run = [&](int c) -> long long { return c < ce ? page_of(c) : -1; };
-  auto load_chunk = [&](CodesT &cd, long long pg, int c) {
-    if constexpr (kBits == 4)
-      load_codes<kFull>(cd, kp, vp, tile_of(pg), chunk_of(pg, c), lc.koff, lc.voff);
-    else
-      load_codes_cut<kFull, kBits>(cd, kp, vp, tile_of(pg), chunk_of(pg, c), lc);
-  };
-  // ---- set-up loads: this thread's table words and its lane's query
-  // values, issued ahead of the chunk loads so that waiting for them never
-  // waits for chunk data ----
-  uint32_t tw0, tw1, kw0, kw1;  // value and key table words of this thread's row
-  {
-    const int e = tid & 255;
-    if constexpr (kBits != 4 && !kFull) {
-      // row f: the draft of anchor field f (sign-extended), the code
-      // a * 2^(8-b) + 2^(7-b) - 1
-      constexpr int RB = 8 - kBits;
-      const int f = e & ((1 << kBits) - 1);
-      const int a = f >= (1 << (kBits - 1)) ? f - (1 << kBits) : f;
-      const int c = (a * (1 << RB) + (1 << (RB - 1)) - 1) & 255;
-      tw0 = tab.full[c];
-      kw0 = tab.kfull[c];
-      tw1 = tw0;
-      kw1 = kw0;
-    } else if (kFull) {
-      tw0 = tab.full[e];
-      kw0 = tab.kfull[e];
-      tw1 = tw0;
-      kw1 = kw0;
-    } else {
-      tw0 = tab.draft[e & 15];
-      tw1 = tab.draft[e >> 4];
-      kw0 = tab.kdraft[e & 15];
-      kw1 = tab.kdraft[e >> 4];
-    }
-  }
-  const uint16_t *qg = q + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g) * kDim;
-  const int jq = lc.n & 7;  // this lane's query head
-  const bool qvalid = jq < g;
-  uint4 qraw[4];  // channels 32r .. 32r+31 of head jq (row 0 stands in when jq >= g)
-  {
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(qg + (qvalid ? jq : 0) * kDim + 32 * lc.r);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) qraw[k] = qrow[k];
-  }
-
-  // The first chunks' codes and scales are requested before the rest of the
-  // set-up, in the order the steps before chunk cb would have left them
-  // (scales of cb, then scales of cb + 1 + d and codes of cb + d for each
-  // d < D), so that the wait counts derived for the loop hold on entry.
-  // They are requested even by a wave with an empty run (page 0 stands in;
-  // the launcher guarantees the pool is not empty): a load on one path only
-  // would make every wait after the join count from the other path.
-#pragma unroll
-  for (int d = 0; d < NB; ++d) pgs[d] = page_in_run(cb + d);
-  load_scales(scs[0], kp, vp, tile_of(pgs[0]), chunk_of(pgs[0], cb), lc.soff);
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    load_scales(scs[d + 1], kp, vp, tile_of(pgs[d + 1]), chunk_of(pgs[d + 1], cb + d + 1), lc.soff);
-    load_chunk(cds[d], pgs[d], cb + d);
-  }
-
-  // ---- tables (replicated words): thread t fills the key half (t < 256)
-  // or the value half of row t % 256 ----
-  {
-    const bool val = tid >= 256;
-    const uint32_t w0 = val ? tw0 : kw0, w1 = val ? tw1 : kw1;
-    const u32x4 v = kWordTable ? u32x4{w0, w0, w0, w0} : u32x4{w0, w1, w0, w1};
-    u32x4 *dst = reinterpret_cast<u32x4 *>(lut + (val ? kValueHalf : 0) + (tid & 255) * 256);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k] = v;
-  }
-  // ---- q of this lane's head, channels 32r .. 32r+31 (exact bf16 values) ----
-  float qv[32];
-  float qmax = 0.0f;
-  {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t u[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[8 * k + 2 * e] = qvalid ? __uint_as_float(u[e] << 16) : 0.0f;
-        qv[8 * k + 2 * e + 1] = qvalid ? __uint_as_float(u[e] & 0xFFFF0000u) : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 32; ++k) qmax = fmaxf(qmax, fabsf(qv[k]));
-    qmax = wave_max(qmax);
-  }
-  // the query group in LDS as f64 (zero rows for heads >= g): wave w
-  // writes head w's row from the lanes n = w (first 16 of their 32
-  // channels) and n = w + 8 (last 16)
-  if (jq == w) {
-    const bool second = lc.n >= 8;
-    const int d0 = 32 * lc.r + (second ? 16 : 0);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float x = second ? qv[16 + k] : qv[k];
-      q64[w * kQStride + d0 + k] = static_cast<double>(x);
-    }
-  }
-  __syncthreads();
-
-  const size_t T = static_cast<size_t>(s.max_pages) * kPage;
-  float *srow_base = nullptr;
-  if (scores != nullptr && (lc.n & 7) < g)
-    srow_base = scores + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + (lc.n & 7)) * T;
-
-  RunState st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) st.acc[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  if (cb < ce) {
-    // the chunk's score weight 2^-(S + 22); the slot holds chunk c's
-    // constants during its step and chunk c + 1's after it (the products
-    // of chunk c have read the slot by then: a wave's LDS accesses complete
-    // in order)
-    double ks = scale_stage(scs[0], slot, lc.lane, qmax, q64);
-    // one chunk c held in buffers J = (c - cb) % NB
-    auto step = [&](auto jc, int c) {
-      constexpr int J = decltype(jc)::value;
-      constexpr int J1 = (J + 1) % NB, JD = (J + D) % NB;
-      const long long cur = pgs[J];
-      pgs[J] = page_in_run(c + D + 1);  // buffer J next holds chunk c + NB = c + D + 1
-      load_scales(scs[J], kp, vp, tile_of(pgs[J]), chunk_of(pgs[J], c + D + 1), lc.soff);
-      load_chunk(cds[JD], pgs[JD], c + D);
-      if (cur >= 0) {
-        wave_lds_sync();
-        compute_chunk<kFull, kBits>(cds[J], slot, ks, q64, lc, lut, st,
-                                    srow_base ? srow_base + static_cast<size_t>(c) * kChunk : nullptr);
-      }
-      wave_lds_sync();
-      ks = scale_stage(scs[J1], slot, lc.lane, qmax, q64);
-    };
-    for (int c = cb; c < ce; c += NB) {
-      step(std::integral_constant<int, 0>(), c);
-      if (c + 1 >= ce) break;
-      step(std::integral_constant<int, 1 % NB>(), c + 1);
-      if (NB > 2) {
-        if (c + 2 >= ce) break;
-        step(std::integral_constant<int, 2 % NB>(), c + 2);
-      }
-    }
-  }
-
-  // ---- merge the 8 waves of the block ----
-  __syncthreads();  // every wave is done with the table: reuse its space
-  float *s_o = reinterpret_cast<float *>(lut);  // [wave][16 col][128 ch, padded to kORow]
-  if (lc.r == 0 && lc.n < 8) {
-    s_ml[(w * 2 + 0) * kHeads + lc.n] = st.m;
-    s_ml[(w * 2 + 1) * kHeads + lc.n] = st.l;
-  }
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
-    *reinterpret_cast<float4 *>(s_o + (w * 16 + lc.n) * kORow + 16 * ct + 4 * lc.r) =
-        make_float4(st.acc[ct][0], st.acc[ct][1], st.acc[ct][2], st.acc[ct][3]);
-  __syncthreads();
-
-  // thread -> (head j, channels 4c .. 4c+3); the high and low column halves
-  // of a head are summed here
-  if (tid < g * (kDim / 4)) {
-    const int j = tid >> 5, c = tid & 31;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_ml[(ww * 2) * kHeads + j]);
-    float L = 0.0f;
-    float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float mw = s_ml[(ww * 2) * kHeads + j];
-      const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-      L += f * s_ml[(ww * 2 + 1) * kHeads + j];
-      const float4 hi = reinterpret_cast<const float4 *>(s_o + (ww * 16 + j) * kORow)[c];
-      const float4 lo = reinterpret_cast<const float4 *>(s_o + (ww * 16 + 8 + j) * kORow)[c];
-      O.x += f * (hi.x + lo.x);
-      O.y += f * (hi.y + lo.y);
-      O.z += f * (hi.z + lo.z);
-      O.w += f * (hi.w + lo.w);
-    }
-    if (s.parts == 1) {
-      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      reinterpret_cast<float4 *>(
-          out + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + j) * kDim)[c] =
-          make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
-    } else {
-      Partials pt = partials_of(ws, s);
-      const size_t row = (static_cast<size_t>(bh) * s.parts + split) * g + j;
-      reinterpret_cast<float4 *>(pt.o + row * kDim)[c] = O;
-      if (c == 0) {
-        pt.m[row] = static_cast<double>(M);
-        pt.l[row] = L;
-      }
-    }
-  }
-}
-
-// ---- K/V wave pairs (4 + 4 planes, drafts of the other cuts) -----------------
-// The 4 + 4 planes (draft and full) and the drafts of the other cuts take a
-// second form of the kernel with the roles of a chunk split between two
-// waves, so that each holds half the registers and a CU runs 16 waves (4 per
-// SIMD) instead of 8.  Wave p < 8 (the K wave of pair
-// p) streams the key codes and scales of its run of chunks and computes each
-// chunk's scores, running maximum and probabilities; wave p + 8 (the V wave)
-// streams the value codes and scales of the same run and accumulates the
-// value sums one chunk behind.  The K wave hands each chunk's probabilities,
-// rescale factor and probability sum to its V wave through LDS (two buffers
-// per pair); the block steps in lockstep, one barrier per chunk step.  The
-// arithmetic of every score, probability and value product is that of
-// attn_mfma_kernel, so the outputs are the same.
+// ---- K/V wave pairs -----------------------------------------------------------
+// The roles of a chunk are split between two waves, so that each holds half
+// the registers of the whole chunk and a CU runs 16 waves (4 per SIMD).
+// Wave p < 8 (the K wave of pair p) streams the key codes and scales of its
+// run of chunks and computes each chunk's scores, running maximum and
+// probabilities; wave p + 8 (the V wave) streams the value codes and scales
+// of the same run and accumulates the value sums one chunk behind.  The K
+// wave hands each chunk's probabilities, rescale factor and probability sum
+// to its V wave through LDS (two buffers per pair); the block steps in
+// lockstep, one barrier per chunk step.
 constexpr int kPairs = 8;
 constexpr int kPThreads = 128 * kPairs;
 constexpr int kKSlotBytes = kWBytes + 1024;  // W words | c0k f64[128]
@@ -978,12 +292,13 @@ static_assert(kKSlotBytes % 16 == 0 && kHandBytes % 16 == 0 && kPLdsBytes <= 160
               "LDS budget of one workgroup");
 
 // Codes of a chunk.  4 + 4 planes: K tile t, anchor / residual of channels
-// 32r .. of token 16t + n; V word r of channel 16ct + n.  Drafts from a
-// b-bit anchor stream (b != 4): the lane's K unit words of each tile, and
-// the window words of its V fields in channel 16ct + n.
+// 32r .. of token 16t + n; V word r of channel 16ct + n.  b + (8 - b)
+// streams (b != 4): the lane's K unit words of each tile, and the window
+// words of its V fields in channel 16ct + n (residual words for the full
+// code only).
 template <int kBits>
 struct KCodes {
-  uint32_t ka[2][kBits];
+  uint32_t ka[2][kBits], kr[2][8 - kBits];
 };
 template <>
 struct KCodes<4> {
@@ -991,7 +306,7 @@ struct KCodes<4> {
 };
 template <int kBits>
 struct VCodes {
-  uint32_t va[8][cut_window_words(kBits)];
+  uint32_t va[8][cut_window_words(kBits)], vr[8][cut_window_words(8 - kBits)];
 };
 template <>
 struct VCodes<4> {
@@ -1016,6 +331,15 @@ __device__ __forceinline__ void load_kcodes(KCodes<kBits> &cd, const PlanesArg &
 #pragma unroll
       for (int i = 0; i < kBits; ++i)
         cd.ka[t][i] = load_nt(reinterpret_cast<const uint32_t *>(ka + lc.kca + t * 256 * kBits + 4 * i));
+    if (kFull) {
+      constexpr int RB = 8 - kBits;
+      const char *kr = reinterpret_cast<const char *>(kp.residual) + unit0 * (4 * RB);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+          cd.kr[t][i] = load_nt(reinterpret_cast<const uint32_t *>(kr + lc.kcr + t * 256 * RB + 4 * i));
+    }
     return;
   } else {
   const uint32_t koff = lc.koff;
@@ -1042,6 +366,15 @@ __device__ __forceinline__ void load_vcodes(VCodes<kBits> &cd, const PlanesArg &
 #pragma unroll
       for (int j = 0; j < cut_window_words(kBits); ++j)
         cd.va[ct][j] = load_nt(reinterpret_cast<const uint32_t *>(va + ct * 64 * kBits + lc.vwa[j]));
+    if (kFull) {
+      constexpr int RB = 8 - kBits;
+      const char *vr = reinterpret_cast<const char *>(vp.residual) + unit0 * (4 * RB);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int j = 0; j < cut_window_words(RB); ++j)
+          cd.vr[ct][j] = load_nt(reinterpret_cast<const uint32_t *>(vr + ct * 64 * RB + lc.vwr[j]));
+    }
     return;
   } else {
   const uint32_t voff = lc.voff;
@@ -1081,8 +414,15 @@ __device__ __forceinline__ void load_vscales(VScales &sc, const PlanesArg &vp, s
   sc.rgv = scale_pair(vp.page_range, pb, soff);
 }
 
-// The key half of scale_stage: W words and c0k of the K wave's next chunk;
-// returns 2^-(S + 22).
+// Chunk constants of the K wave's next chunk into its LDS slot: the W words
+// and c0k.  c1k = rg * s is formed in fp64 (exact) and scaled by 2^S,
+// S = 29 - e with e the exponent of qmax * max c1k (qmax = largest |q| of
+// the group), so every |q * c1k * 2^S| stays below 2^30 (the fp32 maximum
+// can undercut the fp64 one by an ulp, which still leaves it below
+// 2^31 - 2^24, the range of a 4-byte signed split).  Lane l forms the W
+// words of channels 2l, 2l + 1 for the 8 heads (q from the block's f64
+// copy) and c0k of its two channels; returns 2^-(S + 22), the weight of the
+// level sums assembled in score_chunk.
 __device__ __forceinline__ double stage_kslot(const KScales &sc, char *slot, int lane, float qmax,
                                               const double *q64) {
   const float c1a = sc.rgk.x * sc.sk.x, c1b = sc.rgk.y * sc.sk.y;  // bound only
@@ -1145,6 +485,10 @@ __device__ __forceinline__ void key_bytes(const KCodes<kBits> &cd, uint32_t (&e)
       if constexpr (kBits != 4) {
         e[t][w] = cut_bytes<kBits>(cd.ka[t], 8 * w);
         o[t][w] = cut_bytes<kBits>(cd.ka[t], 8 * w + 4);
+        if (kFull) {
+          e[t][w] = (e[t][w] << (8 - kBits)) | cut_bytes<8 - kBits>(cd.kr[t], 8 * w);
+          o[t][w] = (o[t][w] << (8 - kBits)) | cut_bytes<8 - kBits>(cd.kr[t], 8 * w + 4);
+        }
       } else if (kFull) {
         code_bytes(cd.ka[t][w], cd.kr[t][w], e[t][w], o[t][w]);
       } else {
@@ -1154,7 +498,7 @@ __device__ __forceinline__ void key_bytes(const KCodes<kBits> &cd, uint32_t (&e)
     }
 }
 
-// The value half of scale_stage: c1v and c0v of the V wave's next chunk.
+// Chunk constants of the V wave's next chunk: c1v and c0v.
 __device__ __forceinline__ void stage_vslot(const VScales &sc, char *slot, int lane) {
   float *c1v = reinterpret_cast<float *>(slot);
   float *c0v = c1v + kDim;
@@ -1313,8 +657,15 @@ __device__ __forceinline__ void value_chunk(const VCodes<kBits> &cd, const char 
     if constexpr (kBits != 4) {
       uint32_t win[2];
       cut_align<cut_window_words(kBits)>(cd.va[ct], lc.vsa, win);
-      y0 = __builtin_bit_cast(half8, operand_bytes(cut_bytes<kBits>(win, 0), lc.lbv, lut));
-      y1 = __builtin_bit_cast(half8, operand_bytes(cut_bytes<kBits>(win, 4), lc.lbv, lut));
+      uint32_t xa = cut_bytes<kBits>(win, 0), xb = cut_bytes<kBits>(win, 4);
+      if (kFull) {
+        uint32_t wr[2];
+        cut_align<cut_window_words(8 - kBits)>(cd.vr[ct], lc.vsr, wr);
+        xa = (xa << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 0);
+        xb = (xb << (8 - kBits)) | cut_bytes<8 - kBits>(wr, 4);
+      }
+      y0 = __builtin_bit_cast(half8, operand_bytes(xa, lc.lbv, lut));
+      y1 = __builtin_bit_cast(half8, operand_bytes(xb, lc.lbv, lut));
     } else if (kFull) {
       uint32_t e, o;
       code_bytes(cd.va[ct], cd.vr[ct], e, o);
@@ -1379,7 +730,7 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
   if constexpr (kBits != 4) cut_lane_offsets<kBits>(lc);
   lc.sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
 
-  // ---- this pair's run of chunks (as the waves of attn_mfma_kernel) ----
+  // ---- this pair's run of chunks ----
   const __attribute__((address_space(4))) int32_t *bt_c =
       (const __attribute__((address_space(4))) int32_t *)block_table;
   const __attribute__((address_space(4))) int32_t *sl_c =
@@ -1424,7 +775,11 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     const int trow = (tid >> 1) & 255;
     const bool tval = tid >= 512;
     uint32_t tw0, tw1;  // this thread's table words
-    if constexpr (kBits != 4) {
+    if constexpr (kFull) {
+      // row = the 8-bit code, for the planes and every cut
+      tw0 = tval ? tab.full[trow] : tab.kfull[trow];
+      tw1 = tw0;
+    } else if constexpr (kBits != 4) {
       // row f: the draft of anchor field f (sign-extended), the code
       // a * 2^(8-b) + 2^(7-b) - 1
       constexpr int RB = 8 - kBits;
@@ -1432,9 +787,6 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
       const int a = f >= (1 << (kBits - 1)) ? f - (1 << kBits) : f;
       const int code = (a * (1 << RB) + (1 << (RB - 1)) - 1) & 255;
       tw0 = tval ? tab.full[code] : tab.kfull[code];
-      tw1 = tw0;
-    } else if (kFull) {
-      tw0 = tval ? tab.full[trow] : tab.kfull[trow];
       tw1 = tw0;
     } else {
       tw0 = tval ? tab.draft[trow & 15] : tab.kdraft[trow & 15];
@@ -1532,7 +884,10 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     char *vslot = smem + kPVSlotOff + pr * kVSlotBytes;
     // codes of chunk c in buffer (c - cb) % 2; one scale buffer, refilled
     // after the next chunk's constants are staged
-    VCodes<kBits> vc[2];
+    // the full code of a cut holds up to twice the code words of the
+    // planes: one buffer, refilled after its chunk's products
+    constexpr int kVBuf = (kFull && kBits != 4) ? 1 : 2;
+    VCodes<kBits> vc[kVBuf];
     VScales vs;
     long long pg[2];
     pg[0] = page_in_run(cb);
@@ -1552,9 +907,15 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
       if (si - 1 < nrun) {
         const long long cur = pg[J];
         pg[J] = page_in_run(c + 2);
-        load_vcodes<kFull, kBits>(vc[J ^ 1], vp, tile_of(pg[J ^ 1]), chunk_of(pg[J ^ 1], c + 1), lc);
-        if (cur >= 0)
-          value_chunk<kFull, kBits>(vc[J], vslot, lc, lut, acc, hand0 + ((si - 1) & 1) * kHandBytes);
+        if constexpr (kVBuf == 2) {
+          load_vcodes<kFull, kBits>(vc[J ^ 1], vp, tile_of(pg[J ^ 1]), chunk_of(pg[J ^ 1], c + 1), lc);
+          if (cur >= 0)
+            value_chunk<kFull, kBits>(vc[J], vslot, lc, lut, acc, hand0 + ((si - 1) & 1) * kHandBytes);
+        } else {
+          if (cur >= 0)
+            value_chunk<kFull, kBits>(vc[0], vslot, lc, lut, acc, hand0 + ((si - 1) & 1) * kHandBytes);
+          load_vcodes<kFull, kBits>(vc[0], vp, tile_of(pg[J ^ 1]), chunk_of(pg[J ^ 1], c + 1), lc);
+        }
         wave_lds_sync();
         stage_vslot(vs, vslot, lc.lane);  // constants of chunk c + 1
         load_vscales(vs, vp, tile_of(pg[J]), chunk_of(pg[J], c + 2), lc.soff);
@@ -1776,14 +1137,8 @@ void launch_mfma_kernel(dim3 grid, hipStream_t stream, const uint16_t *q, const 
                         const PlanesArg &v, const int32_t *block_table, const int32_t *seq_lens,
                         const AttnShape &s, float sm_scale, float *out, float *scores,
                         void *workspace, const MfmaTables &tables) {
-  // the 4 + 4 planes and the drafts of the other cuts run on the K/V wave
-  // pairs; the full code of a cut keeps the single-wave kernel
-  if constexpr (kBits == 4 || !kFull)
-    hipLaunchKernelGGL((attn_pair_kernel<kFull, kBits>), grid, dim3(kPThreads), 0, stream, q, k, v,
-                       block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
-  else
-    hipLaunchKernelGGL((attn_mfma_kernel<kFull, kBits>), grid, dim3(kThreads), 0, stream, q, k, v,
-                       block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
+  hipLaunchKernelGGL((attn_pair_kernel<kFull, kBits>), grid, dim3(kPThreads), 0, stream, q, k, v,
+                     block_table, seq_lens, s, sm_scale, out, scores, workspace, tables);
 }
 
 template <int kBits>
