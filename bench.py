@@ -533,8 +533,9 @@ def progressive_main(args):
 def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
     """The b + (8 - b) cuts after the timed region: encoding one tensor
     straight into the two streams, re-cutting its 4 + 4 planes into them,
-    the draft reconstruction from the anchor stream, and the fused draft
-    decode attention over the K and V anchor streams, each cycled over the
+    the draft reconstruction from the anchor stream, the fused draft
+    decode attention over the K and V anchor streams and the fused full
+    decode attention over both streams, each cycled over the
     buffer sets (cache-cold)."""
     import torch
     from long_context_serving_amd import lynx
@@ -557,8 +558,11 @@ def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
         attn_calls = [lambda ck=ck, cv=cv: lynx.decode_attention_split(
             q, ck, cv, b, w.pages, full=False, sm_scale=sm, out=out_attn, workspace=ws)
             for ck, cv in zip(cut_k, cut_v)]
+        full_calls = [lambda ck=ck, cv=cv: lynx.decode_attention_split(
+            q, ck, cv, b, w.pages, full=True, sm_scale=sm, out=out_attn, workspace=ws)
+            for ck, cv in zip(cut_k, cut_v)]
         times = []
-        for calls in (split_calls, draft_calls, attn_calls, enc_calls):
+        for calls in (split_calls, draft_calls, attn_calls, enc_calls, full_calls):
             for c in calls:
                 c()
             torch.cuda.synchronize()
@@ -580,11 +584,14 @@ def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
         split_bytes = elems * 2.0                    # 4 + 4 planes in, both streams out
         draft_bytes = elems * (b / 8.0 + scale_bytes + 4.0)
         attn_bytes = 2 * elems * (b / 8.0 + scale_bytes)  # K and V anchor streams and scales
+        full_bytes = 2 * elems * (1.0 + scale_bytes)      # both streams of K and V and scales
         res["%d+%d" % (b, 8 - b)] = {
             "encode_direct_us": times[3] * 1e3,
             "encode_direct_GBps": elems * 3.28125 / (times[3] * 1e-3) / 1e9,
             "draft_attention_us": times[2] * 1e3,
             "draft_attention_GBps": attn_bytes / (times[2] * 1e-3) / 1e9,
+            "full_attention_us": times[4] * 1e3,
+            "full_attention_GBps": full_bytes / (times[4] * 1e-3) / 1e9,
             "split_us": times[0] * 1e3, "split_GBps": split_bytes / (times[0] * 1e-3) / 1e9,
             "draft_dequant_us": times[1] * 1e3,
             "draft_dequant_GBps": draft_bytes / (times[1] * 1e-3) / 1e9,
