@@ -530,6 +530,46 @@ def progressive_main(args):
     print(json.dumps(result), flush=True)
 
 
+def dequant_leg(w, sets, stream):
+    """The standalone 4 + 4 dequantizers after the timed region: draft
+    (anchor plane) and full (both planes) reconstruction of K and of V into
+    fp32, one call per buffer set in turn (cache-cold), graph replays."""
+    import torch
+    from long_context_serving_amd import lynx
+    elems = w.batch * w.tokens * w.kv_heads * w.head_dim
+    out = torch.empty((w.pages * w.batch, 256, w.kv_heads, w.head_dim), dtype=torch.float32,
+                      device=sets[0]["pk"].anchor.device)
+    res = {}
+    for tensor, key in (("K", "pk"), ("V", "pv")):
+        for full in (False, True):
+            calls = [lambda e=e: lynx.dequantize(e[key], full=full, out=out) for e in sets]
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for c in calls:
+                    c()
+            with torch.cuda.stream(stream):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                for _ in range(4):
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / (4 * len(sets))
+            nbytes = elems * ((1.28125 if full else 0.78125) + 4.0)  # planes and scales in, fp32 out
+            res["%s_%s" % (tensor, "full" if full else "draft")] = {
+                "us_per_call": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                "pct_of_hbm_peak": 100.0 * nbytes / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}
+    return {"tensor": "one tensor of one buffer set per call, all %d sets in turn" % len(sets),
+            "timing": "events around 4 replays of a HIP graph of one call per set, after the timed region",
+            "by_call": res}
+
+
 def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
     """The b + (8 - b) cuts after the timed region: encoding one tensor
     straight into the two streams, re-cutting its 4 + 4 planes into them,
@@ -673,7 +713,7 @@ def main():
     ap.add_argument("--no-verify", dest="verify", action="store_false",
                     help="skip the verify-pass measurement (64 speculative tokens over the planes)")
     ap.add_argument("--no-cuts", dest="cuts", action="store_false",
-                    help="skip the measurement of the other code cuts")
+                    help="skip the measurement of the other code cuts and of the standalone dequantizers")
     ap.add_argument("--verify-only", action="store_true",
                     help="encode the buffer sets, then time the verify pass alone")
     ap.add_argument("--verify-tq", type=int, default=64)
@@ -820,6 +860,7 @@ def main():
 
     verify = verify_leg(args, w, sets, dev, sm, stream) if args.verify else None
     cuts = cuts_leg(args, w, sets, stream, q, out, ws, sm) if args.cuts else None
+    dequant = dequant_leg(w, sets, stream) if args.cuts else None
 
     if args.copy_probe:
         a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
@@ -878,6 +919,8 @@ def main():
         result["verify"] = verify
     if cuts is not None:
         result["cuts"] = cuts
+    if dequant is not None:
+        result["dequant"] = dequant
     if args.configs:
         del sets, enc_calls, anc_calls, full_calls, phases, tail_phases, plan
         torch.cuda.empty_cache()
