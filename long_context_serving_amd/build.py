@@ -16,7 +16,7 @@ OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "liblynx.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["lynx_tables.cpp", "lynx_api.cpp", "lynx_encode.hip", "lynx_dequant.hip",
+SOURCES = ["lynx_tables.cpp", "lynx_api.cpp", "lynx_encode.hip",
            "lynx_attention.hip", "lynx_attention_mfma.hip", "lynx_tail.hip",
            "lynx_split.hip", "lynx_verify.hip", "lynx_scratch.hip"]
 

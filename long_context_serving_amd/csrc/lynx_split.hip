@@ -1,9 +1,12 @@
 // Other cuts of the 8-bit code: a b + (8 - b) split into an anchor stream of
-// b bits and a residual stream of 8 - b bits per element.
+// b bits and a residual stream of 8 - b bits per element; and the
+// dequantizers of every cut, the 4 + 4 planes included.
 //
 // Page "Lynx: the KV cache does not have to arrive whole", section 3 cuts
 // the code 4 + 4 (the anchor names a geometric interval, the residual a
-// position in it); section 7 names 6 + 2, 2 + 6 and 5 + 3 as untried.  A
+// position in it), section 4 decodes a draft from the anchor alone and the
+// refined cache from both, and section 7 names 6 + 2, 2 + 6 and 5 + 3 as
+// untried.  A
 // cut keeps the top b bits of the code as the anchor and the low 8 - b bits
 // as the residual; the draft code of anchor a is a * 2^(8-b) + 2^(7-b) - 1,
 // the round-half-down centre of the anchor's codes.
@@ -14,7 +17,7 @@
 // stream (b * 4096 bytes) and bits k*(8-b) .. of its residual stream.  A
 // unit of 32 elements (16 bytes of each 4-bit plane) is exactly b words of
 // the anchor stream and 8 - b words of the residual stream, so every
-// thread here reads and writes whole words of its own unit.
+// thread here reads and writes whole words of its own units.
 #include "lynx_cut.h"
 #include "lynx_internal.h"
 
@@ -61,15 +64,20 @@ __global__ __launch_bounds__(kSplitThreads) void split_planes_kernel(
   for (int i = 0; i < RB; ++i) __builtin_nontemporal_store(wr[i], rout + u * RB + i);
 }
 
-// xhat = mn + rg * (mu + s * yhat(code)), the arithmetic of the 4 + 4
-// dequantizers (so a full reconstruction is bit-identical to theirs).  A
-// block takes 256 units of one tile.  Values: a unit is the 32 tokens of
-// one channel of a chunk, and consecutive lanes hold consecutive channels,
-// so each lane keeps its channel's four scales and every store instruction
-// is contiguous.  Keys: a unit is 32 channels of one token; the block's 256
-// units are 64 whole tokens, so each lane first unpacks its unit's codes
-// into an LDS tile of 64 tokens x 128 channels, then takes one channel of
-// one chunk (32 tokens) as for the values.
+// xhat = mn + rg * (mu + s * yhat(code)) in fp32, written in the encoder's
+// input layout [P][256][H][128].  The full code is the same 8-bit code at
+// every cut, so a full reconstruction does not depend on b.  Every 16-byte
+// store holds 4 channels of one token, and every store instruction of a
+// wave writes two whole 512-byte token rows (splitting a row between store
+// instructions, or writing half rows, measured a quarter to a third slower).
+//
+// A block takes one (page, head) tile.  Keys (a unit is 32 channels of one
+// token): lane t unpacks the 4 units of token t into an LDS tile of 256
+// tokens x 128 table indices; then lane l of wave v stores channels
+// 4q .. 4q+3 (q = l % 32) of tokens 64v + 2m + g (g = l / 32, m < 32), one
+// LDS word per token.  Values (a unit is the 32 tokens of one channel of a
+// chunk): lane l of wave v loads the 4 adjacent units of channels 4q .. 4q+3
+// of chunk 2v + g and stores its 32 tokens.
 template <int B, int kRole, bool kFull>
 __global__ __launch_bounds__(kSplitThreads) void dequant_split_kernel(
     const uint32_t *__restrict__ astream, const uint32_t *__restrict__ rstream, PlanesArg sc,
@@ -77,65 +85,120 @@ __global__ __launch_bounds__(kSplitThreads) void dequant_split_kernel(
   constexpr int RB = 8 - B;
   constexpr int kMid = RB > 0 ? (1 << (RB - 1)) - 1 : 0;
   __shared__ float s_y[256];
-  __shared__ uint32_t s_code[kRole == LYNX_ROLE_KEY ? 64 * kDim / 4 : 1];  // [token][128 codes]
   s_y[threadIdx.x] = tab.y[threadIdx.x];
-  // the launch covers whole tiles: kUnitsPerTile is a multiple of the block
-  const size_t u = static_cast<size_t>(blockIdx.x) * kSplitThreads + threadIdx.x;
-  uint32_t wa[B], wr[RB > 0 ? RB : 1];
-#pragma unroll
-  for (int i = 0; i < B; ++i) wa[i] = astream[u * B + i];
-  if (kFull) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i) wr[i] = rstream[u * RB + i];
-  }
-  // table index (code + 128) of field k of this lane's unit
-  auto index = [&](int k) {
-    const int a = field<B, true>(wa, k);
-    const int r = kFull ? field<RB, false>(wr, k) : kMid;
-    return static_cast<uint32_t>(a * (1 << RB) + r + 128);
+  const int q = threadIdx.x & 31;
+  const int g = (threadIdx.x >> 5) & 1;
+  const int v = threadIdx.x >> 6;
+  const size_t row = static_cast<size_t>(heads) * kDim;
+  float mn[4], rg[4], mu[4], s[4];
+  auto load4 = [](float (&x)[4], const float *src) {
+    const float4 f = *reinterpret_cast<const float4 *>(src);
+    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
   };
-  const size_t tile = u / kUnitsPerTile;
+  const size_t tile = blockIdx.x;
   const size_t p = tile / static_cast<size_t>(heads);
   const int h = static_cast<int>(tile % static_cast<size_t>(heads));
-  const size_t row = static_cast<size_t>(heads) * kDim;
-  const int ub = static_cast<int>((static_cast<size_t>(blockIdx.x) * kSplitThreads) % kUnitsPerTile);
-  int d, c, t0;  // this lane's channel, chunk and first token in the tile
-  uint32_t idx[32];
-  if (kRole == LYNX_ROLE_KEY) {
-    // unit ub + i: token (ub + i) / 4, channels ((ub + i) % 4) * 32 ..
+  if constexpr (kRole == LYNX_ROLE_KEY) {
+    // [token][128 table indices]; the 16-byte group j of token t's row sits
+    // at group j ^ ((t >> 1) & 7), so that 16 lanes writing groups of 16
+    // rows hit 64 distinct banks.
+    __shared__ u32x4 s_code[kPage * kDim / 16];
+    const int t = threadIdx.x;
+    // the 4 units of token t (128 channels), B or 8 - B words each, are
+    // contiguous and 16-byte aligned
+    const size_t unit0 = tile * kUnitsPerTile + 4 * static_cast<size_t>(t);
+    uint32_t wa[4 * B], wr[RB > 0 ? 4 * RB : 1];
 #pragma unroll
-    for (int w4 = 0; w4 < 8; ++w4)
-      s_code[threadIdx.x * 8 + w4] = index(4 * w4) | (index(4 * w4 + 1) << 8) |
-                                      (index(4 * w4 + 2) << 16) | (index(4 * w4 + 3) << 24);
+    for (int i = 0; i < B; ++i) {
+      const u32x4 x = reinterpret_cast<const u32x4 *>(astream + unit0 * B)[i];
+      wa[4 * i] = x[0]; wa[4 * i + 1] = x[1]; wa[4 * i + 2] = x[2]; wa[4 * i + 3] = x[3];
+    }
+    if (kFull) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const u32x4 x = reinterpret_cast<const u32x4 *>(rstream + unit0 * RB)[i];
+        wr[4 * i] = x[0]; wr[4 * i + 1] = x[1]; wr[4 * i + 2] = x[2]; wr[4 * i + 3] = x[3];
+      }
+    }
+    // lane (q, g) of wave v: tokens 64v + 2m + g, chunk 2v (m < 16) or 2v + 1
+    const int c0 = 2 * v;
+    float mu1[4], s1[4];
+    load4(mn, sc.page_min + tile * kDim + 4 * q);
+    load4(rg, sc.page_range + tile * kDim + 4 * q);
+    load4(mu, sc.chunk_mean + (tile * kChunks + c0) * kDim + 4 * q);
+    load4(s, sc.chunk_maxabs + (tile * kChunks + c0) * kDim + 4 * q);
+    load4(mu1, sc.chunk_mean + (tile * kChunks + c0 + 1) * kDim + 4 * q);
+    load4(s1, sc.chunk_maxabs + (tile * kChunks + c0 + 1) * kDim + 4 * q);
+#pragma unroll
+    for (int j = 0; j < kDim / 16; ++j) {  // 16 channels: half of unit j / 2
+      u32x4 x;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 16 * (j & 1) + 4 * w4 + e;  // field of unit j / 2
+          const int a = field<B, true>(wa + (j >> 1) * B, k);
+          const int r = kFull ? field<RB, false>(wr + (j >> 1) * RB, k) : kMid;
+          word |= static_cast<uint32_t>(a * (1 << RB) + r + 128) << (8 * e);
+        }
+        x[w4] = word;
+      }
+      s_code[t * (kDim / 16) + (j ^ ((t >> 1) & 7))] = x;
+    }
     __syncthreads();
-    d = threadIdx.x & 127;
-    const int half = threadIdx.x >> 7;  // tokens 32 half .. of the block's 64
-    t0 = ub / 4 + 32 * half;
-    c = t0 / kChunk;
-    const uint8_t *codes = reinterpret_cast<const uint8_t *>(s_code);
+    const uint32_t *codes = reinterpret_cast<const uint32_t *>(s_code);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) idx[k] = codes[(32 * half + k) * kDim + d];
+    for (int m = 0; m < 32; ++m) {
+      const int tk = 64 * v + 2 * m + g;
+      const uint32_t w = codes[tk * (kDim / 4) + 4 * ((q >> 2) ^ ((tk >> 1) & 7)) + (q & 3)];
+      const float *cm = m < 16 ? mu : mu1;
+      const float *cs = m < 16 ? s : s1;
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = __builtin_fmaf(rg[i], __builtin_fmaf(cs[i], s_y[(w >> (8 * i)) & 255u], cm[i]), mn[i]);
+      float *dst = out + (p * kPage + static_cast<size_t>(tk)) * row + static_cast<size_t>(h) * kDim;
+      reinterpret_cast<float4 *>(dst)[q] = make_float4(o[0], o[1], o[2], o[3]);
+    }
   } else {
-    const int uu = ub + static_cast<int>(threadIdx.x);
-    c = uu >> 7;
-    d = uu & 127;
-    t0 = c * kChunk;
+    const int c = 2 * v + g;
+    const size_t unit0 = tile * kUnitsPerTile + static_cast<size_t>(c) * kDim + 4 * q;
+    // the 4 units' words are contiguous and 16-byte aligned (unit0 % 4 == 0)
+    uint32_t wa[4 * B], wr[RB > 0 ? 4 * RB : 1];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) idx[k] = index(k);
+    for (int i = 0; i < B; ++i) {
+      const u32x4 x = reinterpret_cast<const u32x4 *>(astream + unit0 * B)[i];
+      wa[4 * i] = x[0]; wa[4 * i + 1] = x[1]; wa[4 * i + 2] = x[2]; wa[4 * i + 3] = x[3];
+    }
+    if (kFull) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const u32x4 x = reinterpret_cast<const u32x4 *>(rstream + unit0 * RB)[i];
+        wr[4 * i] = x[0]; wr[4 * i + 1] = x[1]; wr[4 * i + 2] = x[2]; wr[4 * i + 3] = x[3];
+      }
+    }
+    load4(mn, sc.page_min + tile * kDim + 4 * q);
+    load4(rg, sc.page_range + tile * kDim + 4 * q);
+    load4(mu, sc.chunk_mean + (tile * kChunks + c) * kDim + 4 * q);
+    load4(s, sc.chunk_maxabs + (tile * kChunks + c) * kDim + 4 * q);
     __syncthreads();  // the table
-  }
-  const float mn = sc.page_min[tile * kDim + d];
-  const float rg = sc.page_range[tile * kDim + d];
-  const float mu = sc.chunk_mean[(tile * kChunks + c) * kDim + d];
-  const float s = sc.chunk_maxabs[(tile * kChunks + c) * kDim + d];
-  float *dst = out + (p * kPage + static_cast<size_t>(t0)) * row + static_cast<size_t>(h) * kDim + d;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    // keys: token k of the lane's 32; values: field k is token 4w + i
-    // (i < 4) or 16 + 4w + i - 4 of the chunk, w = k / 8, i = k % 8
-    const int w = k >> 3, i = k & 7;
-    const int t = kRole == LYNX_ROLE_KEY ? k : (i < 4 ? 4 * w + i : 16 + 4 * w + (i - 4));
-    dst[static_cast<size_t>(t) * row] = __builtin_fmaf(rg, __builtin_fmaf(s, s_y[idx[k]], mu), mn);
+    for (int k = 0; k < 32; ++k) {
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = field<B, true>(wa + i * B, k);
+        const int r = kFull ? field<RB, false>(wr + i * RB, k) : kMid;
+        o[i] = __builtin_fmaf(rg[i], __builtin_fmaf(s[i], s_y[a * (1 << RB) + r + 128], mu[i]), mn[i]);
+      }
+      // field k is token 4w + i (i < 4) or 16 + 4w + i - 4 of the chunk,
+      // w = k / 8, i = k % 8
+      const int w = k >> 3, i = k & 7;
+      const int t = c * kChunk + (i < 4 ? 4 * w + i : 16 + 4 * w + (i - 4));
+      float *dst = out + (p * kPage + static_cast<size_t>(t)) * row + static_cast<size_t>(h) * kDim;
+      reinterpret_cast<float4 *>(dst)[q] = make_float4(o[0], o[1], o[2], o[3]);
+    }
   }
 }
 
@@ -156,8 +219,9 @@ hipError_t launch_dq_split(const uint8_t *a, const uint8_t *r, const PlanesArg &
   YTable tab;
   const DecodeTable &dt = decode_table();
   for (int i = 0; i < 256; ++i) tab.y[i] = dt.y[i];
-  static_assert(kUnitsPerTile % kSplitThreads == 0, "blocks cover whole tiles");
-  const dim3 grid(static_cast<unsigned>(units / kSplitThreads));
+  static_assert(kSplitThreads == kPage && kChunks == 2 * kSplitThreads / 64,
+                "a block's lanes cover a tile's tokens, its waves the tile's chunks");
+  const dim3 grid(static_cast<unsigned>(units / kUnitsPerTile));  // one tile per block
   hipLaunchKernelGGL((dequant_split_kernel<B, kRole, kFull>), grid, dim3(kSplitThreads), 0, stream,
                      reinterpret_cast<const uint32_t *>(a), reinterpret_cast<const uint32_t *>(r), sc,
                      heads, out, tab);
@@ -207,6 +271,15 @@ hipError_t launch_dequant_split(const uint8_t *anchor, const uint8_t *residual, 
     case 7: return launch_dq_b<7>(anchor, residual, scales, heads, role, units, out, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The 4 + 4 planes are the b = 4 streams (element k of a tile is nibble k of
+// its planes) and 16a + 7 is the b = 4 round-half-down centre, so the 4 + 4
+// dequantizers are the b = 4 kernel.
+hipError_t launch_dequant(const PlanesArg &in, int64_t num_pages, int heads, int role, bool full,
+                          float *out, hipStream_t stream) {
+  return launch_dequant_split(in.anchor, full ? in.residual : nullptr, 4, in, num_pages, heads,
+                              role, out, stream);
 }
 
 }  // namespace lynx
