@@ -5,7 +5,7 @@
 // drafted tokens are verified in one pass over the refined cache; section 3
 // gives the reconstruction x = mn + rg * (mu + s * yhat).  The decode
 // kernel serves one query token per row and rebuilds every chunk's operands
-// per row; here up to 16 query rows of one request and KV head share a
+// per row; here up to 32 query rows of one request and KV head share a
 // block, and each chunk's operands are built once per block in LDS:
 //
 //   K' = c1 * yhat (c1 = rg * s, times a power of two ks), so the score of
@@ -17,14 +17,18 @@
 //        the output only through the softmax weights (a convex combination).
 //
 // K' and V are stored as fp16 (hi, lo) pairs (hi = the value truncated to
-// 11 significant bits, lo = the rounded remainder), in consecutive k slots;
-// the other operand repeats its value in both slots.  The probabilities are
-// split into hi and lo column halves as in the decode kernel.  Scores are
-// assembled in fp64 (MFMA sum times 1/ks, plus the fp64 bias), the running
-// maximum is base 2 and moves only when exceeded by 2^8, and each wave
-// keeps its two rows' accumulators in the matrix-core C operand for the
-// whole run.  A block covers one run of pages; the runs' partials (m, l, o)
-// are merged with the bf16 tail's by the split combine kernel.
+// 11 significant bits, lo = the rounded remainder), each pair in two
+// consecutive k slots.  In the score product q repeats its value in both
+// slots; in the value product every 16 tokens take two products into the
+// same accumulator, one with the probabilities' hi parts repeated in both
+// slots and one with their lo parts, so that a lane's value columns are its
+// own score columns (row, head).  Scores are assembled in fp64 (MFMA sum
+// times 1/ks, plus the fp64 bias), the running maximum is base 2 and moves
+// only when exceeded by 2^8, and each wave keeps its 4 rows' accumulators
+// (two column groups of 2 rows x 8 heads) in the matrix-core C operand for
+// the whole run, so a block's 32 rows share each chunk's build.  A block
+// covers one run of pages; the runs' partials (m, l, o) are merged with the
+// bf16 tail's by the split combine kernel.
 #include <math.h>
 
 #include "lynx_internal.h"
@@ -37,7 +41,8 @@ using namespace lanes;
 
 constexpr int kVW = 8;                      // waves per block
 constexpr int kVT = 64 * kVW;
-constexpr int kVRows = 2 * kVW;             // query rows per block
+constexpr int kGroups = 2;                  // column groups of 2 query rows x 8 heads per wave
+constexpr int kVRows = 2 * kGroups * kVW;   // query rows per block
 constexpr int kG = 8;                       // query heads per KV head
 constexpr float kVSlack = 8.0f;             // log2 of the largest probability before rescaling
 constexpr int kKRowB = kDim * 4 + 16;       // one token of K': 128 (hi, lo) words + 16 B pad
@@ -220,11 +225,11 @@ __device__ __forceinline__ void build_chunk(const BuildIn &in, const char *slot,
 }
 
 // Running state of a wave: lane (n, r) follows column n = (row n / 8,
-// head n % 8) for the softmax and holds rows 16ct + 4r + i of the value
-// columns (head n % 8, half n / 8) of both rows.
+// head n % 8) for the softmax and holds channels 16ct + 4r + i of that
+// column's value sums.
 struct VState {
   float m, l;
-  floatx4 acc_a[8], acc_b[8];
+  floatx4 acc[8];
 };
 
 template <bool kFull>
@@ -237,7 +242,6 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int n = lane & 15, r = lane >> 4;
-  const bool lo = n >= 8;
   const uint32_t lb = static_cast<uint32_t>(lane * 4);
 
   // blocks of one (request, KV head, run) are consecutive logical blocks
@@ -253,16 +257,21 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
   const int h = bh % s.heads;
   const int req = bh / s.heads;
 
-  // ---- this wave's rows and its lane's query values ----
-  const int row_a = rb * kVRows + 2 * w;      // rows of the request: row_a, row_a + 1
-  const int my_row = row_a + (n >> 3);        // row of this lane's score column
-  const bool row_ok = my_row < s.tq;
-  const size_t qrow = static_cast<size_t>(req) * s.tq + (row_ok ? my_row : s.tq - 1);
-  const uint16_t *qg = q + (qrow * s.q_heads + static_cast<size_t>(h) * kG + (n & 7)) * kDim;
-  uint2 qraw[8];  // channels 16st + 4r .. + 3
+  // ---- this wave's rows and its lanes' query values: in column group g,
+  // lane (n, r) follows row row_a + 2g + n / 8, head n % 8 ----
+  const int row_a = rb * kVRows + 2 * kGroups * w;
+  bool row_ok[kGroups];
+  uint2 qraw[kGroups][8];  // channels 16st + 4r .. + 3
 #pragma unroll
-  for (int st = 0; st < 8; ++st)
-    qraw[st] = *reinterpret_cast<const uint2 *>(qg + 16 * st + 4 * r);
+  for (int g = 0; g < kGroups; ++g) {
+    const int my_row = row_a + 2 * g + (n >> 3);
+    row_ok[g] = my_row < s.tq;
+    const size_t qrow = static_cast<size_t>(req) * s.tq + (row_ok[g] ? my_row : s.tq - 1);
+    const uint16_t *qg = q + (qrow * s.q_heads + static_cast<size_t>(h) * kG + (n & 7)) * kDim;
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      qraw[g][st] = *reinterpret_cast<const uint2 *>(qg + 16 * st + 4 * r);
+  }
 
   // ---- this block's run of chunks ----
   const __attribute__((address_space(4))) int32_t *bt_c =
@@ -309,22 +318,21 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
     for (int k = 0; k < 8; ++k) dst[k] = u32x4{yb, yb, yb, yb};
   }
 
-  // ---- q (exact bf16 values) for the bias, and the block-wide power of
-  // two qs that brings max |q| into [2^14, 2^15) for the fp16 operand ----
-  float q32[32];
+  // ---- the block-wide power of two qs that brings max |q| into
+  // [2^14, 2^15): q * qs is then an exact fp16 value (bf16 has 8 significant
+  // bits), which both the score product and the fp64 chunk bias use ----
+  auto q_at = [&](int g, int st, int i) {  // bf16 q of channel 16st + 4r + i, 0 past the rows
+    const uint32_t u = (i >> 1) ? qraw[g][st].y : qraw[g][st].x;
+    const uint32_t bits = (i & 1) ? (u & 0xFFFF0000u) : (u << 16);
+    return row_ok[g] ? __uint_as_float(bits) : 0.0f;
+  };
   float qmax = 0.0f;
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const uint32_t u[2] = {qraw[st].x, qraw[st].y};
+  for (int g = 0; g < kGroups; ++g)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float a = row_ok ? __uint_as_float(u[e] << 16) : 0.0f;
-      const float b = row_ok ? __uint_as_float(u[e] & 0xFFFF0000u) : 0.0f;
-      q32[4 * st + 2 * e] = a;
-      q32[4 * st + 2 * e + 1] = b;
-      qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(b)));
-    }
-  }
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qmax = fmaxf(qmax, fabsf(q_at(g, st, i)));
   qmax = wave_max(qmax);
   float *s_qm = reinterpret_cast<float *>(smem + kQmOff);
   if (lane == 0) s_qm[w] = qmax;
@@ -343,31 +351,40 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
       inv_qs = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + 127 - ex) << 52);
     }
   }
-  half8 qb[8];  // B operand of step st: q * qs of channels 16st + 4r + i, in both slots
+  // q * qs of channels 16st + 4r + 2e, + 1 as an fp16 pair (word e of qh);
+  // the score product's B operand repeats each value in both k slots
+  uint2 qh[kGroups][8];
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    u32x4 v;
+  for (int g = 0; g < kGroups; ++g)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = q32[4 * st + i] * qs;
-      v[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, x));
+    for (int st = 0; st < 8; ++st) {
+      uint32_t v[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        v[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(q_at(g, st, 2 * e) * qs,
+                                                                       q_at(g, st, 2 * e + 1) * qs));
+      qh[g][st] = make_uint2(v[0], v[1]);
     }
-    qb[st] = __builtin_bit_cast(half8, v);
-  }
+  auto qb = [&](int g, int st) {
+    const uint2 x = qh[g][st];
+    const u32x4 v = {__builtin_amdgcn_perm(x.x, x.x, 0x01000100u), __builtin_amdgcn_perm(x.x, x.x, 0x03020302u),
+                     __builtin_amdgcn_perm(x.y, x.y, 0x01000100u), __builtin_amdgcn_perm(x.y, x.y, 0x03020302u)};
+    return __builtin_bit_cast(half8, v);
+  };
 
   char *ktiles = smem + kKOff;
   char *vtiles = smem + kVOff;
   char *slots = smem + kSOff;
   const double sm2 = static_cast<double>(sm_scale) * 1.4426950408889634074;
-  const uint32_t keep_mask = lo ? 0xFFFFE000u : 0u;
+  const double bias_scale = sm2 * inv_qs;
 
-  VState st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
+  VState st[kGroups];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    st.acc_a[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    st.acc_b[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g = 0; g < kGroups; ++g) {
+    st[g].m = -INFINITY;
+    st[g].l = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) st[g].acc[ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   if (cb < ce) {
@@ -390,97 +407,123 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
         load_kscale(ring, kp, tile_of(g2), chunk_of(g2, c + 2), lane);
       }
       if (page_of(c) >= 0) {
+        // (the packed q pairs are redefined here so that their expansion into
+        // operands stays inside the step instead of occupying 64 registers)
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int s8 = 0; s8 < 8; ++s8) asm volatile("" : "+v"(qh[g][s8].x), "+v"(qh[g][s8].y));
         const char *kt = ktiles + tb * kKTileB;
         const char *vt = vtiles + tb * kVTileB;
         const char *slot = slots + (j % 3) * kSlotB;
-        // chunk bias sum_d q_d c0k_d (fp64) of column n over channels 16st + 4r + i
-        double bias;
+        // chunk bias sum_d (q_d qs) c0k_d (fp64) of each group's column n over
+        // channels 16st + 4r + i; times sm2 / qs below
+        double bias[kGroups];
         {
           const double *c0k = reinterpret_cast<const double *>(slot + kDim * 4);
-          double a0 = 0.0, a1 = 0.0;
+          double a0[kGroups], a1[kGroups];
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) a0[g] = a1[g] = 0.0;
 #pragma unroll
           for (int s8 = 0; s8 < 8; ++s8) {
             const double2 x0 = *reinterpret_cast<const double2 *>(c0k + 16 * s8 + 4 * r);
             const double2 x1 = *reinterpret_cast<const double2 *>(c0k + 16 * s8 + 4 * r + 2);
-            a0 = fma(static_cast<double>(q32[4 * s8]), x0.x, a0);
-            a1 = fma(static_cast<double>(q32[4 * s8 + 1]), x0.y, a1);
-            a0 = fma(static_cast<double>(q32[4 * s8 + 2]), x1.x, a0);
-            a1 = fma(static_cast<double>(q32[4 * s8 + 3]), x1.y, a1);
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+              const uint2 qw = qh[g][s8];
+              auto qv = [](uint32_t word, int hi) {
+                return static_cast<double>(static_cast<float>(
+                    __builtin_bit_cast(_Float16, static_cast<uint16_t>(hi ? word >> 16 : word))));
+              };
+              a0[g] = fma(qv(qw.x, 0), x0.x, a0[g]);
+              a1[g] = fma(qv(qw.x, 1), x0.y, a1[g]);
+              a0[g] = fma(qv(qw.y, 0), x1.x, a0[g]);
+              a1[g] = fma(qv(qw.y, 1), x1.y, a1[g]);
+            }
           }
-          bias = xrows_sum(a0 + a1);
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) bias[g] = xrows_sum(a0[g] + a1[g]);
         }
-        // scores S^T[16 tok][16 col] for tiles 0, 1
-        floatx4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        // scores S^T[16 tok][16 col] of both groups for tiles 0, 1 (each K'
+        // operand read serves both groups)
+        floatx4 s0[kGroups], s1[kGroups];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) s0[g] = s1[g] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
           const half8 a0 = *reinterpret_cast<const half8 *>(kt + n * kKRowB + (16 * s8 + 4 * r) * 4);
           const half8 a1 =
               *reinterpret_cast<const half8 *>(kt + (16 + n) * kKRowB + (16 * s8 + 4 * r) * 4);
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[s8], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[s8], s1, 0, 0, 0);
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) {
+            const half8 b = qb(g, s8);
+            s0[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b, s0[g], 0, 0, 0);
+            s1[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b, s1[g], 0, 0, 0);
+          }
           // keep the operand reads of at most two steps in flight
           if (s8 & 1) __builtin_amdgcn_sched_barrier(0);
         }
         const double scale2 = sm2 * *reinterpret_cast<const double *>(slot + kDim * 12);
-        const double bias2 = bias * sm2;
-        double sc[8];
-        float cmax = -INFINITY;
+        // online softmax per group; P operands: the lane's own column n,
+        // tokens 16tt + 4r + i (p[4tt + i]), each in the two k slots of its
+        // V (hi, lo) pair: once the P hi part in both, once the P lo part
+        half8 pk[kGroups][4];  // [2tt]: hi parts of tile tt, [2tt + 1]: lo parts
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[i] = fma(static_cast<double>(s0[i]), scale2, bias2);
-          sc[4 + i] = fma(static_cast<double>(s1[i]), scale2, bias2);
-          cmax = fmaxf(cmax, fmaxf(static_cast<float>(sc[i]), static_cast<float>(sc[4 + i])));
-        }
-        cmax = xrows(cmax, MaxOp());
-        const bool rescale = __builtin_amdgcn_ballot_w64(cmax > st.m + kVSlack) != 0;
-        float alpha = 1.0f;
-        if (rescale) {
-          const float m_new = fmaxf(st.m, cmax);
-          alpha = st.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
-          st.m = m_new;
-          const float x = ror8(alpha);
-          const float al_a = lo ? x : alpha, al_b = lo ? alpha : x;
-#pragma unroll
-          for (int ct = 0; ct < 8; ++ct) {
-            st.acc_a[ct] *= al_a;
-            st.acc_b[ct] *= al_b;
-          }
-        }
-        float p[8];
-        float psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(static_cast<float>(sc[i] - static_cast<double>(st.m)));
-          psum += p[i];
-        }
-        psum = xrows(psum, SumOp());
-        st.l = st.l * alpha + psum;
-        // P operands of each row: column (head n % 8, half n / 8) takes the
-        // probabilities of lane n (row a, n < 8) or n ^ 8
-        half8 pa[2], pb[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          u32x4 wa, wb;
+        for (int g = 0; g < kGroups; ++g) {
+          const double bias2 = bias[g] * bias_scale;
+          double sc[8];
+          float cmax = -INFINITY;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float own = p[4 * tt + i];
-            const float x = ror8(own);
-            wa[i] = split_dup(lo ? x : own, keep_mask);
-            wb[i] = split_dup(lo ? own : x, keep_mask);
+            sc[i] = fma(static_cast<double>(s0[g][i]), scale2, bias2);
+            sc[4 + i] = fma(static_cast<double>(s1[g][i]), scale2, bias2);
+            cmax = fmaxf(cmax, fmaxf(static_cast<float>(sc[i]), static_cast<float>(sc[4 + i])));
           }
-          pa[tt] = __builtin_bit_cast(half8, wa);
-          pb[tt] = __builtin_bit_cast(half8, wb);
+          cmax = xrows(cmax, MaxOp());
+          const bool rescale = __builtin_amdgcn_ballot_w64(cmax > st[g].m + kVSlack) != 0;
+          float alpha = 1.0f;
+          if (rescale) {
+            const float m_new = fmaxf(st[g].m, cmax);
+            alpha = st[g].m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st[g].m - m_new);
+            st[g].m = m_new;
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) st[g].acc[ct] *= alpha;
+          }
+          float p[8];
+          float psum = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(static_cast<float>(sc[i] - static_cast<double>(st[g].m)));
+            psum += p[i];
+          }
+          psum = xrows(psum, SumOp());
+          st[g].l = st[g].l * alpha + psum;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            u32x4 vh, vl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              vh[i] = split_dup(p[4 * tt + i], 0u);
+              vl[i] = split_dup(p[4 * tt + i], 0xFFFFE000u);
+            }
+            pk[g][2 * tt] = __builtin_bit_cast(half8, vh);
+            pk[g][2 * tt + 1] = __builtin_bit_cast(half8, vl);
+          }
         }
         // values: O^T[16 ch][16 col] += V^T[16 ch][32 k] * P[32 k][16 col]
+        // (each V operand read serves both groups)
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
           const char *vrow = vt + (16 * ct + n) * kVRowB;
-          const half8 y0 = *reinterpret_cast<const half8 *>(vrow + (4 * r) * 4);
-          const half8 y1 = *reinterpret_cast<const half8 *>(vrow + (16 + 4 * r) * 4);
-          st.acc_a[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pa[0], st.acc_a[ct], 0, 0, 0);
-          st.acc_a[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y1, pa[1], st.acc_a[ct], 0, 0, 0);
-          st.acc_b[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y0, pb[0], st.acc_b[ct], 0, 0, 0);
-          st.acc_b[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y1, pb[1], st.acc_b[ct], 0, 0, 0);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const half8 y = *reinterpret_cast<const half8 *>(vrow + (16 * tt + 4 * r) * 4);
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+              st[g].acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y, pk[g][2 * tt], st[g].acc[ct], 0, 0, 0);
+              st[g].acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(y, pk[g][2 * tt + 1], st[g].acc[ct], 0, 0, 0);
+            }
+          }
           if (ct & 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -492,34 +535,22 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
     }
   }
 
-  // ---- partials of both rows: lanes n < 8 write head n ----
+  // ---- partials: lane (n, r) writes column n of each group ----
   {
     AttnPartials pt = attn_partials(ws, s);
-    const float m_other = ror8(st.m), l_other = ror8(st.l);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int row = row_a + k;
-      const float mk = k == 0 ? st.m : m_other;  // lanes n < 8: row a is their own column
-      const float lk = k == 0 ? st.l : l_other;
-      floatx4 o[8];
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const floatx4 a = k == 0 ? st.acc_a[ct] : st.acc_b[ct];
-        floatx4 x;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = a[i] + ror8(a[i]);
-        o[ct] = x;
-      }
-      if (!lo && row < s.tq) {
+    for (int g = 0; g < kGroups; ++g) {
+      const int row = row_a + 2 * g + (n >> 3);
+      if (row < s.tq) {
         const size_t grow = static_cast<size_t>(req) * s.tq + row;
-        const size_t prow = ((grow * s.heads + h) * s.parts + split) * kG + n;
+        const size_t prow = ((grow * s.heads + h) * s.parts + split) * kG + (n & 7);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
           *reinterpret_cast<float4 *>(pt.o + prow * kDim + 16 * ct + 4 * r) =
-              make_float4(o[ct][0], o[ct][1], o[ct][2], o[ct][3]);
+              make_float4(st[g].acc[ct][0], st[g].acc[ct][1], st[g].acc[ct][2], st[g].acc[ct][3]);
         if (r == 0) {
-          pt.m[prow] = static_cast<double>(mk);
-          pt.l[prow] = lk;
+          pt.m[prow] = static_cast<double>(st[g].m);
+          pt.l[prow] = st[g].l;
         }
       }
     }
