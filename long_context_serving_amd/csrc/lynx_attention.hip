@@ -378,7 +378,7 @@ AttnShape attention_shape_tail(int requests, int tq, int heads, int q_heads, int
   AttnShape s = attention_shape(requests * tq, heads, q_heads, max_pages);
   s.tq = tq;
   if (verify_mfma_used(s.group, tq) && max_pages > 0) {
-    // the verify kernel's blocks: (request, KV head, run, group of 16 rows)
+    // the verify kernel's blocks: (request, KV head, run, group of 16 or 32 rows)
     const long long units = static_cast<long long>(requests) * heads * verify_row_blocks(tq);
     const long long target = attention_mfma_target_blocks();
     long long pps = units > 0 ? (units * max_pages + target - 1) / target : 1;

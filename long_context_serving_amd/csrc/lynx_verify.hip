@@ -26,7 +26,8 @@
 // times 1/ks, plus the fp64 bias), the running maximum is base 2 and moves
 // only when exceeded by 2^8, and each wave keeps its 4 rows' accumulators
 // (two column groups of 2 rows x 8 heads) in the matrix-core C operand for
-// the whole run, so a block's 32 rows share each chunk's build.  A block
+// the whole run, so a block's 32 rows share each chunk's build (one group
+// of 2 rows, 16 per block, when the request has no more rows).  A block
 // covers one run of pages; the runs' partials (m, l, o) are merged with the
 // bf16 tail's by the split combine kernel.
 #include <math.h>
@@ -41,8 +42,7 @@ using namespace lanes;
 
 constexpr int kVW = 8;                      // waves per block
 constexpr int kVT = 64 * kVW;
-constexpr int kGroups = 2;                  // column groups of 2 query rows x 8 heads per wave
-constexpr int kVRows = 2 * kGroups * kVW;   // query rows per block
+constexpr int kGroupRows = 2 * kVW;         // query rows per block and column group
 constexpr int kG = 8;                       // query heads per KV head
 constexpr float kVSlack = 8.0f;             // log2 of the largest probability before rescaling
 constexpr int kKRowB = kDim * 4 + 16;       // one token of K': 128 (hi, lo) words + 16 B pad
@@ -232,7 +232,9 @@ struct VState {
   floatx4 acc[8];
 };
 
-template <bool kFull>
+// kGroups column groups of 2 query rows x 8 heads per wave (1 or 2): a
+// block serves 16 kGroups rows.
+template <bool kFull, int kGroups>
 __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
     const uint16_t *__restrict__ q, PlanesArg kp, PlanesArg vp,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ page_tokens,
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
 
   // ---- this wave's rows and its lanes' query values: in column group g,
   // lane (n, r) follows row row_a + 2g + n / 8, head n % 8 ----
-  const int row_a = rb * kVRows + 2 * kGroups * w;
+  const int row_a = rb * kGroupRows * kGroups + 2 * kGroups * w;
   bool row_ok[kGroups];
   uint2 qraw[kGroups][8];  // channels 16st + 4r .. + 3
 #pragma unroll
@@ -576,7 +578,15 @@ constexpr int kVerifyMinTokens = 5;
 
 bool verify_mfma_used(int group, int tq) { return group == kG && tq >= kVerifyMinTokens; }
 
-int verify_row_blocks(int tq) { return (tq + kVRows - 1) / kVRows; }
+// Two column groups per wave (32 rows per block) share each chunk's build
+// over twice the rows, at twice a block's per-chunk products; one group is
+// cheaper while all rows fit in 16.
+int verify_groups(int tq) { return tq > kGroupRows ? 2 : 1; }
+
+int verify_row_blocks(int tq) {
+  const int rows = kGroupRows * verify_groups(tq);
+  return (tq + rows - 1) / rows;
+}
 
 hipError_t launch_verify_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
                               const int32_t *block_table, const int32_t *page_tokens,
@@ -587,11 +597,18 @@ hipError_t launch_verify_mfma(const uint16_t *q, const PlanesArg &k, const Plane
   const int requests = s.batch / s.tq;
   const int rbs = verify_row_blocks(s.tq);
   const dim3 grid(static_cast<unsigned>(static_cast<long long>(requests) * s.heads * s.splits * rbs));
-  if (full)
-    hipLaunchKernelGGL(verify_mfma_kernel<true>, grid, dim3(kVT), 0, stream, q, k, v, block_table,
+  const bool two = verify_groups(s.tq) == 2;
+  if (full && two)
+    hipLaunchKernelGGL((verify_mfma_kernel<true, 2>), grid, dim3(kVT), 0, stream, q, k, v, block_table,
+                       page_tokens, s, rbs, sm_scale, workspace, table);
+  else if (full)
+    hipLaunchKernelGGL((verify_mfma_kernel<true, 1>), grid, dim3(kVT), 0, stream, q, k, v, block_table,
+                       page_tokens, s, rbs, sm_scale, workspace, table);
+  else if (two)
+    hipLaunchKernelGGL((verify_mfma_kernel<false, 2>), grid, dim3(kVT), 0, stream, q, k, v, block_table,
                        page_tokens, s, rbs, sm_scale, workspace, table);
   else
-    hipLaunchKernelGGL(verify_mfma_kernel<false>, grid, dim3(kVT), 0, stream, q, k, v, block_table,
+    hipLaunchKernelGGL((verify_mfma_kernel<false, 1>), grid, dim3(kVT), 0, stream, q, k, v, block_table,
                        page_tokens, s, rbs, sm_scale, workspace, table);
   return hipGetLastError();
 }

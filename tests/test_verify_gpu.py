@@ -107,14 +107,18 @@ def run_case(lynx, H, Hq, tq, page_lists, tail_len, P_pool, seed, full, max_page
 @pytest.mark.parametrize("full", [True, False])
 def test_verify_group8_ragged_pages_and_tails(lynx, full):
     # matrix-core page kernel (group 8); a request with no full page
-    for tq, tail_len in ((1, [1, 200, 320]), (5, [5, 64, 319]), (64, [64, 300, 320])):
+    # tq 5: one column group per wave (16 rows per block); 37 and 64: two
+    # (32 rows per block), 37 leaving the second block one row in wave 1
+    for tq, tail_len in ((1, [1, 200, 320]), (5, [5, 64, 319]), (37, [37, 100, 320]),
+                         (64, [64, 300, 320])):
         run_case(lynx, 2, 16, tq, [[4, 1, 6], [], [0, 2, 5, 3]], tail_len, 7, 101 + tq, full)
 
 
 @pytest.mark.parametrize("full", [True, False])
 def test_verify_group8_absent_pages_and_a_partial_row_group(lynx, full):
-    # 20 tokens: a second group of 16 rows with 4 of them; entries 9 and -4
-    # lie outside the pool of 7 pages and are skipped
+    # 20 tokens: one block of 32 rows with 20 of them (waves 5-7 without a
+    # row, wave 4 with 4); entries 9 and -4 lie outside the pool of 7 pages
+    # and are skipped
     run_case(lynx, 2, 16, 20, [[4, 9, 1], [2, -4, 6, 0]], [20, 150], 7, 211, full)
 
 
