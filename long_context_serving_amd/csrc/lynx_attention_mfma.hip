@@ -1097,6 +1097,82 @@ __global__ __launch_bounds__(kCombThreads) void attn_mfma_combine_kernel(AttnSha
   }
 }
 
+// The same merge with one block per (query row, KV head), for launches with
+// many of them (the verify pass's rows): the block computes the part
+// weights once for all 128 channels and reads every partial row whole;
+// thread t takes head j = t / 32 and channels 4(t % 32) .. + 3.  The o rows
+// of the first kRowCombPre parts are requested before the weights.
+constexpr int kRowCombPre = 16;
+constexpr int kRowCombMinPairs = 128;  // (row, KV head) pairs from which this kernel runs
+
+__global__ __launch_bounds__(kCombThreads) void attn_mfma_combine_rows_kernel(AttnShape s, const void *ws,
+                                                                              float *__restrict__ out) {
+  const int bh = blockIdx.x;
+  const int b = bh / s.heads, h = bh % s.heads;
+  const int g = s.group;
+  const int ns = s.parts;
+  const int tid = threadIdx.x, j = tid >> 5, i = tid & 31;
+  const bool valid = j < g;
+  Partials pt = partials_of(const_cast<void *>(ws), s);
+  const size_t first = static_cast<size_t>(bh) * ns * g;  // rows of part 0
+  __shared__ float c_w[kCombMaxSplits * kHeads];           // [part][head] weights
+  auto orow = [&](int sp) {
+    return reinterpret_cast<const float4 *>(pt.o + (first + static_cast<size_t>(sp) * g + j) * kDim) + i;
+  };
+  float4 v[kRowCombPre];
+#pragma unroll
+  for (int u = 0; u < kRowCombPre; ++u)
+    v[u] = valid && u < ns ? *orow(u) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  // part weights of head j: its 32 lanes over the parts
+  float L;
+  {
+    float mloc[kCombMaxSplits / 32], lloc[kCombMaxSplits / 32];
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kCombMaxSplits / 32; ++k) {
+      const int sp = i + 32 * k;
+      const bool ok = valid && sp < ns;
+      mloc[k] = ok ? static_cast<float>(pt.m[first + static_cast<size_t>(sp) * g + j]) : -INFINITY;
+      lloc[k] = ok ? pt.l[first + static_cast<size_t>(sp) * g + j] : 0.0f;
+      M = fmaxf(M, mloc[k]);
+    }
+    M = half_wave_reduce(M, MaxOp());
+    L = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCombMaxSplits / 32; ++k) {
+      const int sp = i + 32 * k;
+      const float wgt = mloc[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mloc[k] - M);
+      L += wgt * lloc[k];
+      if (valid && sp < ns) c_w[sp * kHeads + j] = wgt;
+    }
+    L = half_wave_reduce(L, SumOp());
+  }
+  __syncthreads();
+  if (!valid) return;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  auto add = [&](float wgt, const float4 &x) {
+    acc.x += wgt * x.x;
+    acc.y += wgt * x.y;
+    acc.z += wgt * x.z;
+    acc.w += wgt * x.w;
+  };
+#pragma unroll
+  for (int u = 0; u < kRowCombPre; ++u)
+    if (u < ns) add(c_w[u * kHeads + j], v[u]);
+  int sp = kRowCombPre;
+  for (; sp + 4 <= ns; sp += 4) {
+    float4 x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = *orow(sp + k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) add(c_w[(sp + k) * kHeads + j], x[k]);
+  }
+  for (; sp < ns; ++sp) add(c_w[sp * kHeads + j], *orow(sp));
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  reinterpret_cast<float4 *>(out + (static_cast<size_t>(b) * s.q_heads + static_cast<size_t>(h) * g + j) *
+                                       kDim)[i] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
 // Output of requests whose every page is skipped (an empty pool): zeros.
 __global__ __launch_bounds__(256) void attn_zero_kernel(float *__restrict__ out, size_t n) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -1197,8 +1273,13 @@ hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const Pl
 hipError_t launch_attention_mfma_combine(const AttnShape &s, const void *workspace, float *out,
                                          hipStream_t stream) {
   if (s.parts > kCombMaxSplits) return hipErrorInvalidValue;
-  const dim3 cgrid(static_cast<unsigned>(static_cast<long long>(s.batch) * s.heads *
-                                         (kDim / kCombChannels)));
+  const long long pairs = static_cast<long long>(s.batch) * s.heads;
+  if (pairs >= kRowCombMinPairs) {
+    hipLaunchKernelGGL(attn_mfma_combine_rows_kernel, dim3(static_cast<unsigned>(pairs)),
+                       dim3(kCombThreads), 0, stream, s, workspace, out);
+    return hipGetLastError();
+  }
+  const dim3 cgrid(static_cast<unsigned>(pairs * (kDim / kCombChannels)));
   hipLaunchKernelGGL(attn_mfma_combine_kernel, cgrid, dim3(kCombThreads), 0, stream, s, workspace,
                      out);
   return hipGetLastError();

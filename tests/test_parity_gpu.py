@@ -518,6 +518,28 @@ def test_uneven_runs_across_the_pairs_of_a_block(lynx):
             assert np.abs(sc[b, :, :256 * n] - lg).max() <= 1e-4 * max(1.0, np.abs(lg).max())
 
 
+def test_merge_of_many_rows_one_block_per_row_and_head(lynx):
+    """16 requests x 8 KV heads = 128 (row, KV head) pairs of up to 4 pages,
+    so each run splits in two and the split merge takes one block per pair;
+    ragged lengths leave some requests one part (no block table: request b
+    owns pool pages 4b .. 4b + 3)."""
+    H, Hq, max_pages, B = 8, 64, 4, 16
+    x_k = synth.laplace_pages(B * max_pages, H, 128, seed=81, scale_channels=((2, 7, 50.0),))
+    x_v = synth.laplace_pages(B * max_pages, H, 128, seed=82, scale_channels=((1, 3, 40.0),))
+    pk, ek, _, _ = check_encode(lynx, x_k, 0)
+    pv, ev, _, _ = check_encode(lynx, x_v, 1)
+    rng = np.random.default_rng(83)
+    lengths = [int(n) for n in rng.integers(1, max_pages + 1, B)]
+    lengths[0] = max_pages
+    pages = [list(range(b * max_pages, b * max_pages + n)) for b, n in enumerate(lengths)]
+    q = synth.float_to_bf16_bits(rng.laplace(0, 1, (B, Hq, 128)).astype(np.float32))
+    for full in (False, True):
+        print("many-row merge full=%s lengths=%s" % (full, lengths), flush=True)
+        ref = oracle_attention_for(ek, ev, q, pages, full)
+        got = run_gpu_attention(lynx, q, pk, pv, max_pages, full, seq_lens=[256 * n for n in lengths])
+        check_attention(got, ref, "many-row merge full=%s" % full)
+
+
 @pytest.mark.parametrize("P,H", [(1, 1), (3, 5), (128, 8)])
 def test_kv_encode_in_one_launch_equals_one_launch_per_tensor(lynx, P, H):
     # lynx_quantize_kv_pages: every byte of both tensors' planes as written by
