@@ -171,8 +171,9 @@ hipError_t launch_attention_mfma_combine(const AttnShape &s, const void *workspa
 
 // Verify-pass page kernel (GQA group 8, 5 or more query tokens per
 // request; fewer run on the decode kernels): up to 16 query rows of one
-// request and KV head per block, one block per (request, KV head, run of
-// pages, group of 16 rows); writes the split partials of its rows.
+// request and KV head per block when tq <= 16, else up to 32; one block per
+// (request, KV head, run of pages, group of rows); writes the split
+// partials of its rows.
 bool verify_mfma_used(int group, int tq);
 int verify_row_blocks(int tq);
 hipError_t launch_verify_mfma(const uint16_t *q, const PlanesArg &k, const PlanesArg &v,
