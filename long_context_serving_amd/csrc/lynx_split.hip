@@ -45,13 +45,20 @@ __device__ __forceinline__ int field(const uint32_t *w, int k) {
                  : static_cast<int>(__builtin_amdgcn_ubfe(x, 0, B));
 }
 
+// Thread t of a block packs unit u0 + t.  The block's 256 units are b KiB
+// of the anchor stream and 8 - b KiB of the residual stream, each
+// contiguous, so the words are staged in LDS and written as 512 pieces of
+// 16 B (pieces p < 64b the anchor stream's): every store instruction of a
+// wave writes 1 KiB contiguous.  The launch covers whole tiles, a multiple
+// of the block.
 template <int B>
 __global__ __launch_bounds__(kSplitThreads) void split_planes_kernel(
     const u32x4 *__restrict__ a4, const u32x4 *__restrict__ r4, uint32_t *__restrict__ aout,
-    uint32_t *__restrict__ rout, size_t units) {
+    uint32_t *__restrict__ rout) {
   constexpr int RB = 8 - B;
-  const size_t u = static_cast<size_t>(blockIdx.x) * kSplitThreads + threadIdx.x;
-  if (u >= units) return;
+  __shared__ __align__(16) uint32_t s_w[kSplitThreads * 8];  // anchor words, then residual words
+  const size_t u0 = static_cast<size_t>(blockIdx.x) * kSplitThreads;
+  const size_t u = u0 + threadIdx.x;
   const u32x4 av = __builtin_nontemporal_load(a4 + u);
   const u32x4 rv = __builtin_nontemporal_load(r4 + u);
   const uint32_t aw[4] = {av[0], av[1], av[2], av[3]};
@@ -59,9 +66,18 @@ __global__ __launch_bounds__(kSplitThreads) void split_planes_kernel(
   uint32_t wa[B], wr[RB];
   cut::unit<B>(aw, rw, wa, wr);
 #pragma unroll
-  for (int i = 0; i < B; ++i) __builtin_nontemporal_store(wa[i], aout + u * B + i);
+  for (int i = 0; i < B; ++i) s_w[threadIdx.x * B + i] = wa[i];
 #pragma unroll
-  for (int i = 0; i < RB; ++i) __builtin_nontemporal_store(wr[i], rout + u * RB + i);
+  for (int i = 0; i < RB; ++i) s_w[kSplitThreads * B + threadIdx.x * RB + i] = wr[i];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int p = static_cast<int>(threadIdx.x) + k * kSplitThreads;
+    const u32x4 x = reinterpret_cast<const u32x4 *>(s_w)[p];
+    u32x4 *dst = p < 64 * B ? reinterpret_cast<u32x4 *>(aout + u0 * B) + p
+                            : reinterpret_cast<u32x4 *>(rout + u0 * RB) + (p - 64 * B);
+    __builtin_nontemporal_store(x, dst);
+  }
 }
 
 // xhat = mn + rg * (mu + s * yhat(code)) in fp32, written in the encoder's
@@ -205,11 +221,12 @@ __global__ __launch_bounds__(kSplitThreads) void dequant_split_kernel(
 template <int B>
 hipError_t launch_split_b(const PlanesArg &in, size_t units, uint8_t *aout, uint8_t *rout,
                           hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((units + kSplitThreads - 1) / kSplitThreads));
+  static_assert(kUnitsPerTile % kSplitThreads == 0, "blocks cover whole tiles");
+  const dim3 grid(static_cast<unsigned>(units / kSplitThreads));
   hipLaunchKernelGGL(split_planes_kernel<B>, grid, dim3(kSplitThreads), 0, stream,
                      reinterpret_cast<const u32x4 *>(in.anchor),
                      reinterpret_cast<const u32x4 *>(in.residual), reinterpret_cast<uint32_t *>(aout),
-                     reinterpret_cast<uint32_t *>(rout), units);
+                     reinterpret_cast<uint32_t *>(rout));
   return hipGetLastError();
 }
 
