@@ -10,9 +10,11 @@
 // partials of the quantized pages; query token i of a request sees tail
 // tokens 0 .. tail_len - tq + i (itself and everything before it).
 //
-// Products of bf16 values are exact in fp64 and the sums run in fp64, so
-// the only roundings are those of the fp64 sums and exponentials, of the
-// rescaling between slabs of 64 tokens, and of storing l and o as fp32.
+// Products of bf16 values are exact in fp64 and the score sums run in fp64,
+// as does the running maximum.  The exponentials (of fp64 differences
+// rounded to fp32), the probability sums and the value sums run in fp32:
+// their rounding reaches the output only through the softmax weights, a
+// convex combination (the page kernels' value operands keep 22 bits).
 #include <math.h>
 
 #include "lynx_internal.h"
@@ -45,19 +47,12 @@ constexpr int kSlab = 64;
 constexpr int kKRow = kDim + 8;
 constexpr int kWaves = kTailThreads / 64;
 
-// value of x in lane t (t uniform over the wave)
-__device__ __forceinline__ double lane_value(double x, int t) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), t));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), t));
-  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
-}
 __device__ __forceinline__ double wave_max_d(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
   return v;
 }
-__device__ __forceinline__ double wave_sum_d(double v) {
+__device__ __forceinline__ float wave_sum_f(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
@@ -131,12 +126,13 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
   int vis = n - s.tq + i + 1;  // tail tokens this query token sees
   vis = vis < 0 ? 0 : (vis > n ? n : vis);
 
-  double m_run[kHpw], l_run[kHpw], o[kHpw][2];
+  double m_run[kHpw];
+  float l_run[kHpw], o[kHpw][2];
 #pragma unroll
   for (int hh = 0; hh < kHpw; ++hh) {
     m_run[hh] = -INFINITY;
-    l_run[hh] = 0.0;
-    o[hh][0] = o[hh][1] = 0.0;
+    l_run[hh] = 0.0f;
+    o[hh][0] = o[hh][1] = 0.0f;
   }
 
   for (int t0 = 0; t0 < vis; t0 += kSlab) {
@@ -192,28 +188,32 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
     }
 
     // ---- online softmax over the slab, then the value sums ----
-    double p[kHpw];
+    // exponent in base 2: fp64 difference (times log2 e for natural-base
+    // scores) rounded to fp32
+    constexpr double kLog2e = 1.4426950408889634074;
+    auto exp_of = [&](double d) {
+      return __builtin_amdgcn_exp2f(static_cast<float>(base2 ? d : d * kLog2e));
+    };
+    float p[kHpw];
 #pragma unroll
     for (int hh = 0; hh < kHpw; ++hh) {
       const double x = lane < cnt ? (acc[hh][0] + acc[hh][1]) * score_scale : -INFINITY;
       const double m_new = fmax(m_run[hh], wave_max_d(x));  // finite: cnt >= 1
-      const double dm = m_run[hh] - m_new;
-      const double alpha = base2 ? exp2(dm) : exp(dm);  // 0 on the first slab
-      const double xm = x - m_new;
-      p[hh] = lane < cnt ? (base2 ? exp2(xm) : exp(xm)) : 0.0;
-      l_run[hh] = l_run[hh] * alpha + wave_sum_d(p[hh]);
+      const float alpha = exp_of(m_run[hh] - m_new);          // 0 on the first slab
+      p[hh] = lane < cnt ? exp_of(x - m_new) : 0.0f;
+      l_run[hh] = l_run[hh] * alpha + wave_sum_f(p[hh]);
       m_run[hh] = m_new;
       o[hh][0] *= alpha;
       o[hh][1] *= alpha;
     }
     for (int t = 0; t < cnt; ++t) {
       const uint32_t v2 = *reinterpret_cast<const uint32_t *>(s_v + t * kDim + 2 * lane);
-      const double v0 = bf16_to_double(v2 & 0xFFFFu), v1 = bf16_to_double(v2 >> 16);
+      const float v0 = __uint_as_float(v2 << 16), v1 = __uint_as_float(v2 & 0xFFFF0000u);
 #pragma unroll
       for (int hh = 0; hh < kHpw; ++hh) {
-        const double pt = lane_value(p[hh], t);
-        o[hh][0] = fma(pt, v0, o[hh][0]);
-        o[hh][1] = fma(pt, v1, o[hh][1]);
+        const float pt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[hh]), t));
+        o[hh][0] = __builtin_fmaf(pt, v0, o[hh][0]);
+        o[hh][1] = __builtin_fmaf(pt, v1, o[hh][1]);
       }
     }
   }
@@ -224,11 +224,10 @@ __global__ __launch_bounds__(kTailThreads) void attn_tail_kernel(
   for (int hh = 0; hh < kHpw; ++hh) {
     const int j = wave + kWaves * hh;
     if (j < g) {
-      reinterpret_cast<float2 *>(pt.o + (row0 + j) * kDim)[lane] =
-          make_float2(static_cast<float>(o[hh][0]), static_cast<float>(o[hh][1]));
+      reinterpret_cast<float2 *>(pt.o + (row0 + j) * kDim)[lane] = make_float2(o[hh][0], o[hh][1]);
       if (lane == 0) {
         pt.m[row0 + j] = m_run[hh];  // -inf when the token sees no tail token
-        pt.l[row0 + j] = static_cast<float>(l_run[hh]);
+        pt.l[row0 + j] = l_run[hh];
       }
     }
   }
