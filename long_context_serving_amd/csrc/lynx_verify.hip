@@ -353,26 +353,17 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
       inv_qs = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + 127 - ex) << 52);
     }
   }
-  // q * qs of channels 16st + 4r + 2e, + 1 as an fp16 pair (word e of qh);
-  // the score product's B operand repeats each value in both k slots
-  uint2 qh[kGroups][8];
+  // B operand of step st: q * qs of channels 16st + 4r + i, in both k slots
+  u32x4 qb[kGroups][8];
 #pragma unroll
   for (int g = 0; g < kGroups; ++g)
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      uint32_t v[2];
+    for (int st = 0; st < 8; ++st)
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        v[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(q_at(g, st, 2 * e) * qs,
-                                                                       q_at(g, st, 2 * e + 1) * qs));
-      qh[g][st] = make_uint2(v[0], v[1]);
-    }
-  auto qb = [&](int g, int st) {
-    const uint2 x = qh[g][st];
-    const u32x4 v = {__builtin_amdgcn_perm(x.x, x.x, 0x01000100u), __builtin_amdgcn_perm(x.x, x.x, 0x03020302u),
-                     __builtin_amdgcn_perm(x.y, x.y, 0x01000100u), __builtin_amdgcn_perm(x.y, x.y, 0x03020302u)};
-    return __builtin_bit_cast(half8, v);
-  };
+      for (int i = 0; i < 4; ++i) {
+        const float x = q_at(g, st, i) * qs;
+        qb[g][st][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, x));
+      }
 
   char *ktiles = smem + kKOff;
   char *vtiles = smem + kVOff;
@@ -409,12 +400,14 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
         load_kscale(ring, kp, tile_of(g2), chunk_of(g2, c + 2), lane);
       }
       if (page_of(c) >= 0) {
-        // (the packed q pairs are redefined here so that their expansion into
-        // operands stays inside the step instead of occupying 64 registers)
+        // (the q operands are redefined here so that the bias's conversions
+        // of them stay inside the step: hoisted out of the loop, the fp64
+        // values would take 128 registers)
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
 #pragma unroll
-          for (int s8 = 0; s8 < 8; ++s8) asm volatile("" : "+v"(qh[g][s8].x), "+v"(qh[g][s8].y));
+          for (int s8 = 0; s8 < 8; ++s8)
+            asm volatile("" : "+v"(qb[g][s8][0]), "+v"(qb[g][s8][1]), "+v"(qb[g][s8][2]), "+v"(qb[g][s8][3]));
         const char *kt = ktiles + tb * kKTileB;
         const char *vt = vtiles + tb * kVTileB;
         const char *slot = slots + (j % 3) * kSlotB;
@@ -432,15 +425,14 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
             const double2 x1 = *reinterpret_cast<const double2 *>(c0k + 16 * s8 + 4 * r + 2);
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
-              const uint2 qw = qh[g][s8];
-              auto qv = [](uint32_t word, int hi) {
-                return static_cast<double>(static_cast<float>(
-                    __builtin_bit_cast(_Float16, static_cast<uint16_t>(hi ? word >> 16 : word))));
+              auto qv = [&](int i) {
+                return static_cast<double>(
+                    static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(qb[g][s8][i]))));
               };
-              a0[g] = fma(qv(qw.x, 0), x0.x, a0[g]);
-              a1[g] = fma(qv(qw.x, 1), x0.y, a1[g]);
-              a0[g] = fma(qv(qw.y, 0), x1.x, a0[g]);
-              a1[g] = fma(qv(qw.y, 1), x1.y, a1[g]);
+              a0[g] = fma(qv(0), x0.x, a0[g]);
+              a1[g] = fma(qv(1), x0.y, a1[g]);
+              a0[g] = fma(qv(2), x1.x, a0[g]);
+              a1[g] = fma(qv(3), x1.y, a1[g]);
             }
           }
 #pragma unroll
@@ -458,7 +450,7 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
               *reinterpret_cast<const half8 *>(kt + (16 + n) * kKRowB + (16 * s8 + 4 * r) * 4);
 #pragma unroll
           for (int g = 0; g < kGroups; ++g) {
-            const half8 b = qb(g, s8);
+            const half8 b = __builtin_bit_cast(half8, qb[g][s8]);
             s0[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b, s0[g], 0, 0, 0);
             s1[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b, s1[g], 0, 0, 0);
           }
