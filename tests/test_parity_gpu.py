@@ -518,12 +518,14 @@ def test_uneven_runs_across_the_pairs_of_a_block(lynx):
             assert np.abs(sc[b, :, :256 * n] - lg).max() <= 1e-4 * max(1.0, np.abs(lg).max())
 
 
-def test_merge_of_many_rows_one_block_per_row_and_head(lynx):
-    """16 requests x 8 KV heads = 128 (row, KV head) pairs of up to 4 pages,
-    so each run splits in two and the split merge takes one block per pair;
-    ragged lengths leave some requests one part (no block table: request b
-    owns pool pages 4b .. 4b + 3)."""
-    H, Hq, max_pages, B = 8, 64, 4, 16
+@pytest.mark.parametrize("H,Hq,B", [(8, 64, 16), (16, 32, 8)])
+def test_merge_of_many_rows_one_block_per_row_and_head(lynx, H, Hq, B):
+    """B requests x H KV heads = 128 (row, KV head) pairs of up to 4 pages,
+    so each run splits in two and the split merge takes one block per pair
+    (GQA groups 8 and 2: threads past the group idle); ragged lengths leave
+    some requests one part (no block table: request b owns pool pages
+    4b .. 4b + 3)."""
+    max_pages = 4
     x_k = synth.laplace_pages(B * max_pages, H, 128, seed=81, scale_channels=((2, 7, 50.0),))
     x_v = synth.laplace_pages(B * max_pages, H, 128, seed=82, scale_channels=((1, 3, 40.0),))
     pk, ek, _, _ = check_encode(lynx, x_k, 0)
@@ -534,10 +536,10 @@ def test_merge_of_many_rows_one_block_per_row_and_head(lynx):
     pages = [list(range(b * max_pages, b * max_pages + n)) for b, n in enumerate(lengths)]
     q = synth.float_to_bf16_bits(rng.laplace(0, 1, (B, Hq, 128)).astype(np.float32))
     for full in (False, True):
-        print("many-row merge full=%s lengths=%s" % (full, lengths), flush=True)
+        print("many-row merge H=%d Hq=%d full=%s lengths=%s" % (H, Hq, full, lengths), flush=True)
         ref = oracle_attention_for(ek, ev, q, pages, full)
         got = run_gpu_attention(lynx, q, pk, pv, max_pages, full, seq_lens=[256 * n for n in lengths])
-        check_attention(got, ref, "many-row merge full=%s" % full)
+        check_attention(got, ref, "many-row merge H=%d Hq=%d full=%s" % (H, Hq, full))
 
 
 @pytest.mark.parametrize("P,H", [(1, 1), (3, 5), (128, 8)])
