@@ -107,10 +107,11 @@ def run_case(lynx, H, Hq, tq, page_lists, tail_len, P_pool, seed, full, max_page
 @pytest.mark.parametrize("full", [True, False])
 def test_verify_group8_ragged_pages_and_tails(lynx, full):
     # matrix-core page kernel (group 8); a request with no full page
-    # tq 5: one column group per wave (16 rows per block); 37 and 64: two
-    # (32 rows per block), 37 leaving the second block one row in wave 1
-    for tq, tail_len in ((1, [1, 200, 320]), (5, [5, 64, 319]), (37, [37, 100, 320]),
-                         (64, [64, 300, 320])):
+    # tq 5 and 16: one column group per wave (16 rows per block); 17, 37 and
+    # 64: two (32 rows per block), 17 leaving row 16 alone in wave 4 and 37
+    # the second block one row in wave 1
+    for tq, tail_len in ((1, [1, 200, 320]), (5, [5, 64, 319]), (16, [16, 17, 272]),
+                         (17, [17, 260, 300]), (37, [37, 100, 320]), (64, [64, 300, 320])):
         run_case(lynx, 2, 16, tq, [[4, 1, 6], [], [0, 2, 5, 3]], tail_len, 7, 101 + tq, full)
 
 
