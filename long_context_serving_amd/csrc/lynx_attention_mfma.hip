@@ -892,10 +892,13 @@ __global__ __launch_bounds__(kPThreads) void attn_pair_kernel(
     long long pg[2];
     pg[0] = page_in_run(cb);
     pg[1] = page_in_run(cb + 1);
+    // the first codes are needed one step later than the scales: requested
+    // after the table fill, they leave the K waves' first requests less
+    // traffic to queue behind
     load_vscales(vs, vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc.soff);
-    load_vcodes<kFull, kBits>(vc[0], vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc);
     setup_tables();
     __syncthreads();  // tables and q
+    load_vcodes<kFull, kBits>(vc[0], vp, tile_of(pg[0]), chunk_of(pg[0], cb), lc);
     stage_vslot(vs, vslot, lc.lane);
     load_vscales(vs, vp, tile_of(pg[1]), chunk_of(pg[1], cb + 1), lc.soff);
     __syncthreads();  // step 0: the K waves score the first chunks
