@@ -208,10 +208,10 @@ __global__ __launch_bounds__(kSplitThreads) void dequant_split_kernel(
         const int r = kFull ? field<RB, false>(wr + i * RB, k) : kMid;
         o[i] = __builtin_fmaf(rg[i], __builtin_fmaf(s[i], s_y[a * (1 << RB) + r + 128], mu[i]), mn[i]);
       }
-      // field k is token 4w + i (i < 4) or 16 + 4w + i - 4 of the chunk,
-      // w = k / 8, i = k % 8
-      const int w = k >> 3, i = k & 7;
-      const int t = c * kChunk + (i < 4 ? 4 * w + i : 16 + 4 * w + (i - 4));
+      // field k is token 4 fw + fj (fj < 4) or 16 + 4 fw + fj - 4 of the
+      // chunk, fw = k / 8, fj = k % 8
+      const int fw = k >> 3, fj = k & 7;
+      const int t = c * kChunk + (fj < 4 ? 4 * fw + fj : 16 + 4 * fw + (fj - 4));
       float *dst = out + (p * kPage + static_cast<size_t>(t)) * row + static_cast<size_t>(h) * kDim;
       reinterpret_cast<float4 *>(dst)[q] = make_float4(o[0], o[1], o[2], o[3]);
     }
