@@ -123,6 +123,15 @@ def test_verify_group8_absent_pages_and_a_partial_row_group(lynx, full):
     run_case(lynx, 2, 16, 20, [[4, 9, 1], [2, -4, 6, 0]], [20, 150], 7, 211, full)
 
 
+def test_verify_merge_of_many_parts_per_row(lynx):
+    # one request of 32 pages in a reversed block table, 2 KV heads, 64
+    # speculative tokens: 128 (row, KV head) pairs whose runs split into 32
+    # parts plus the tail's, so the per-row merge reads 16 parts ahead of
+    # the weights, 16 in groups of four and the last one alone
+    pages = list(range(31, -1, -1))
+    run_case(lynx, 2, 16, 64, [pages], [90], 32, 808, True, max_pages=32)
+
+
 @pytest.mark.parametrize("full", [True, False])
 def test_verify_group16_valu_path(lynx, full):
     run_case(lynx, 2, 32, 7, [[3, 5], [1], [6, 0, 2]], [7, 100, 256], 7, 303, full)
