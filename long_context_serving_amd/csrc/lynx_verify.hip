@@ -262,6 +262,9 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
   // ---- this wave's rows and its lanes' query values: in column group g,
   // lane (n, r) follows row row_a + 2g + n / 8, head n % 8 ----
   const int row_a = rb * kGroupRows * kGroups + 2 * kGroups * w;
+  // a wave whose rows all lie past the request's tq builds and stages its
+  // share of every chunk but computes nothing (wave-uniform)
+  const bool wave_rows = row_a < s.tq;
   bool row_ok[kGroups];
   uint2 qraw[kGroups][8];  // channels 16st + 4r .. + 3
 #pragma unroll
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
         load_build<kFull>(bin, kp, vp, tile_of(g1), chunk_of(g1, c + 1), t);
         load_kscale(ring, kp, tile_of(g2), chunk_of(g2, c + 2), lane);
       }
-      if (page_of(c) >= 0) {
+      if (wave_rows && page_of(c) >= 0) {
         // (the q operands are redefined here so that the bias's conversions
         // of them stay inside the step: hoisted out of the loop, the fp64
         // values would take 128 registers)
