@@ -353,6 +353,17 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnShape
 
 }  // namespace
 
+// Pages per run: `units` work items (row and KV head, or row group) each
+// split into runs so that at most `target` blocks cover the call whenever
+// units <= target (a block per CU is one round: more blocks than that would
+// start a second round for a few of them), and one run per unit beyond.
+static long long run_pages(long long units, int max_pages, long long target) {
+  if (max_pages < 1 || units < 1) return 1;
+  const long long runs = units >= target ? 1 : target / units;  // >= 1
+  long long pps = (max_pages + runs - 1) / runs;
+  return pps < 1 ? 1 : (pps > max_pages ? max_pages : pps);
+}
+
 AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
   AttnShape s;
   s.batch = batch;
@@ -365,9 +376,7 @@ AttnShape attention_shape(int batch, int heads, int q_heads, int max_pages) {
   const long long units = static_cast<long long>(batch) * heads;
   const long long target =
       attention_mfma_supported(s.group) ? attention_mfma_target_blocks() : kTargetBlocks;
-  long long pps = units > 0 ? (units * max_pages + target - 1) / target : 1;
-  if (pps < 1) pps = 1;
-  if (pps > max_pages) pps = max_pages > 0 ? max_pages : 1;
+  const long long pps = run_pages(units, max_pages, target);
   s.pages_per_split = static_cast<int>(pps);
   s.splits = max_pages > 0 ? static_cast<int>((max_pages + pps - 1) / pps) : 1;
   s.parts = s.splits;
@@ -380,10 +389,7 @@ AttnShape attention_shape_tail(int requests, int tq, int heads, int q_heads, int
   if (verify_mfma_used(s.group, tq) && max_pages > 0) {
     // the verify kernel's blocks: (request, KV head, run, group of 16 or 32 rows)
     const long long units = static_cast<long long>(requests) * heads * verify_row_blocks(tq);
-    const long long target = attention_mfma_target_blocks();
-    long long pps = units > 0 ? (units * max_pages + target - 1) / target : 1;
-    if (pps < 1) pps = 1;
-    if (pps > max_pages) pps = max_pages;
+    const long long pps = run_pages(units, max_pages, attention_mfma_target_blocks());
     s.pages_per_split = static_cast<int>(pps);
     s.splits = static_cast<int>((max_pages + pps - 1) / pps);
   }

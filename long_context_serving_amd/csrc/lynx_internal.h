@@ -169,7 +169,7 @@ hipError_t launch_attention_mfma(const uint16_t *q, const PlanesArg &k, const Pl
 hipError_t launch_attention_mfma_combine(const AttnShape &s, const void *workspace, float *out,
                                          hipStream_t stream);
 
-// Verify-pass page kernel (GQA group 8, 5 or more query tokens per
+// Verify-pass page kernel (GQA group 8, 3 or more query tokens per
 // request; fewer run on the decode kernels): up to 16 query rows of one
 // request and KV head per block when tq <= 16, else up to 32; one block per
 // (request, KV head, run of pages, group of rows); writes the split

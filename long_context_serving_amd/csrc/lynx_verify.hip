@@ -569,7 +569,7 @@ VerifyTable build_verify_table() {
 // A block's cost per chunk does not depend on how many of its rows are
 // used, so few query tokens per request are cheaper on the decode kernels
 // (one row per query token); the crossover is measured.
-constexpr int kVerifyMinTokens = 5;
+constexpr int kVerifyMinTokens = 3;
 
 bool verify_mfma_used(int group, int tq) { return group == kG && tq >= kVerifyMinTokens; }
 

@@ -164,23 +164,24 @@ def test_argument_errors_are_reported_before_any_launch(lib):
 def test_verify_workspace_follows_the_split_rule(lib):
     """The verify workspace holds one (m, l, o) partial per (query row, KV
     head, part, query head): parts = the page runs plus the bf16 tail's.
-    Runs are sized so that about 256 blocks cover the call (2048 for the
-    VALU kernel of groups above 8): with GQA group 8 and 5 or more query
-    tokens a block takes 16 rows (tq <= 16) or 32 of a request and a KV
-    head, otherwise the decode kernels take one row per block.  m is fp64,
-    l fp32, o 128 fp32."""
+    Runs are sized so that at most 256 blocks cover the call (2048 for the
+    VALU kernel of groups above 8) when the work items fit in that many,
+    one run per item beyond: with GQA group 8 and 3 or more query tokens an
+    item (a block's rows) is 16 rows (tq <= 16) or 32 of a request and a KV
+    head, otherwise one row.  m is fp64, l fp32, o 128 fp32."""
     lib.lynx_verify_attention_workspace_size.restype = ctypes.c_size_t
     lib.lynx_verify_attention_workspace_size.argtypes = [ctypes.c_int32] * 6
 
     def expected(requests, tq, H, Hq, max_pages):
         g = Hq // H
-        if g == 8 and tq >= 5:
+        if g == 8 and tq >= 3:
             rows_per_block = 16 if tq <= 16 else 32
             units = requests * H * -(-tq // rows_per_block)
         else:
             units = requests * tq * H
         target = 256 if g <= 8 else 2048
-        pps = min(max(-(-units * max_pages // target), 1), max_pages)
+        runs = 1 if units >= target else target // units
+        pps = min(max(-(-max_pages // runs), 1), max_pages)
         parts = -(-max_pages // pps) + 1
         n = requests * tq * H * parts * g
         return ((n + 1) & ~1) * 8 + ((n + 3) & ~3) * 4 + n * 128 * 4
@@ -188,6 +189,7 @@ def test_verify_workspace_follows_the_split_rule(lib):
     for requests, tq, H, Hq, max_pages in ((1, 64, 8, 64, 128), (1, 33, 8, 64, 128),
                                            (1, 17, 8, 64, 128), (1, 16, 8, 64, 128),
                                            (1, 5, 8, 64, 128), (1, 4, 8, 64, 128),
+                                           (1, 2, 8, 64, 128), (3, 1, 8, 64, 128),
                                            (3, 37, 2, 16, 4), (2, 7, 2, 32, 3),
                                            (1, 64, 2, 16, 32), (4, 1, 8, 64, 2),
                                            (2, 3, 4, 64, 64)):
