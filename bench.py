@@ -642,13 +642,12 @@ def cuts_leg(args, w, sets, stream, q, out_attn, ws, sm):
             "by_cut": res}
 
 
-def verify_leg(args, w, sets, dev, sm, stream):
+def verify_leg(args, w, sets, dev, sm, stream, tq):
     """Verify pass after the timed region: the newest tq tokens of the
     request (its speculative tokens) attend to the full planes of every
     buffer set in turn (cache-cold) plus a bf16 tail of tq + 36 tokens."""
     import torch
     from long_context_serving_amd import lynx, synth
-    tq = args.verify_tq
     tail_len = tq + 36
     rng = np.random.default_rng(4242)
     tail = lambda: torch.from_numpy(synth.float_to_bf16_bits(
@@ -711,12 +710,15 @@ def main():
     ap.add_argument("--link-gbps", default="10,25,50",
                     help="emulated link rates for the progressive timeline (empty: none)")
     ap.add_argument("--no-verify", dest="verify", action="store_false",
-                    help="skip the verify-pass measurement (64 speculative tokens over the planes)")
+                    help="skip the verify-pass measurements (speculative tokens over the planes)")
     ap.add_argument("--no-cuts", dest="cuts", action="store_false",
                     help="skip the measurement of the other code cuts and of the standalone dequantizers")
     ap.add_argument("--verify-only", action="store_true",
                     help="encode the buffer sets, then time the verify pass alone")
-    ap.add_argument("--verify-tq", type=int, default=64)
+    ap.add_argument("--verify-tq", type=int, default=64,
+                    help="speculative tokens of the main verify measurement")
+    ap.add_argument("--verify-short-tq", type=int, default=5,
+                    help="speculative tokens of the short verify measurement (0: skip it)")
     ap.add_argument("--verify-reps", type=int, default=4)
     ap.add_argument("--config-only", choices=("tiny", "qwen3_235b_128k", "batched64x16k",
                                               "progressive32x64k"),
@@ -810,7 +812,8 @@ def main():
         for call in enc_calls:
             call()
         torch.cuda.synchronize()
-        print(json.dumps({"workload": w.name, "verify": verify_leg(args, w, sets, dev, sm, stream)}),
+        print(json.dumps({"workload": w.name,
+                          "verify": verify_leg(args, w, sets, dev, sm, stream, args.verify_tq)}),
               flush=True)
         return
     for call in enc_calls + anc_calls + full_calls:  # eager pass
@@ -858,7 +861,9 @@ def main():
     per_call_ms = {"encode": phase_ms[0] / K, "decode_anchor": phase_ms[1] / K,
                    "decode_full": phase_ms[2] / K}
 
-    verify = verify_leg(args, w, sets, dev, sm, stream) if args.verify else None
+    verify = verify_leg(args, w, sets, dev, sm, stream, args.verify_tq) if args.verify else None
+    verify_short = (verify_leg(args, w, sets, dev, sm, stream, args.verify_short_tq)
+                    if args.verify and args.verify_short_tq > 0 else None)
     cuts = cuts_leg(args, w, sets, stream, q, out, ws, sm) if args.cuts else None
     dequant = dequant_leg(w, sets, stream) if args.cuts else None
 
@@ -917,6 +922,8 @@ def main():
     }
     if verify is not None:
         result["verify"] = verify
+    if verify_short is not None:
+        result["verify_short"] = verify_short
     if cuts is not None:
         result["cuts"] = cuts
     if dequant is not None:
