@@ -8,11 +8,13 @@
 // per row; here up to 32 query rows of one request and KV head share a
 // block, and each chunk's operands are built once per block in LDS:
 //
-//   K' = c1 * yhat (c1 = rg * s, times a power of two ks), so the score of
-//        a token is q . K' / ks + q . c0 (c0 = mn + rg * mu, the chunk bias,
-//        summed in fp64); q enters the product unsplit (a bf16 value is an
-//        fp16 value after a power-of-two scale), so one 16 x 16 x 32 product
-//        covers 16 tokens x (2 query rows x 8 heads) x 16 channels;
+//   K' = rg * mu + c1 * yhat = x - mn (c1 = rg * s), times a power of two
+//        ks, so the score of a token is q . K' / ks + q . mn, the page bias
+//        q . mn summed in fp64 once per page (the page minimum holds a
+//        channel's offset, which may dwarf its range); q enters the product
+//        unsplit (a bf16 value is an fp16 value after a power-of-two scale),
+//        so one 16 x 16 x 32 product covers 16 tokens x (2 query rows x 8
+//        heads) x 16 channels;
 //   V  = the reconstructed values themselves, whose rounding error reaches
 //        the output only through the softmax weights (a convex combination).
 //
@@ -23,7 +25,7 @@
 // same accumulator, one with the probabilities' hi parts repeated in both
 // slots and one with their lo parts, so that a lane's value columns are its
 // own score columns (row, head).  Scores are assembled in fp64 (MFMA sum
-// times 1/ks, plus the fp64 bias), the running maximum is base 2 and moves
+// times 1/ks, plus the fp64 page bias), the running maximum is base 2 and moves
 // only when exceeded by 2^8, and each wave keeps its 4 rows' accumulators
 // (two column groups of 2 rows x 8 heads) in the matrix-core C operand for
 // the whole run, so a block's 32 rows share each chunk's build (one group
@@ -49,7 +51,8 @@ constexpr int kKRowB = kDim * 4 + 16;       // one token of K': 128 (hi, lo) wor
 constexpr int kKTileB = kChunk * kKRowB;
 constexpr int kVRowB = kChunk * 4 + 16;     // one channel of V: 32 (hi, lo) words + 16 B pad
 constexpr int kVTileB = kDim * kVRowB;
-constexpr int kSlotB = kDim * 4 + kDim * 8 + 16;  // c1k * ks f32[128] | c0k f64[128] | 1/(ks qs) f64
+// c1 * ks f32[128] | rg * mu * ks f32[128] | mn f64[128] | 1/(ks qs) f64
+constexpr int kSlotB = kDim * 16 + 16;
 // LDS map: yhat table (256 codes x 64 copies, lane l reads copy l), two K'
 // tiles, two V tiles, three scale slots, and the block's |q| maxima.
 constexpr int kYOff = 0;
@@ -157,13 +160,15 @@ __device__ __forceinline__ void load_kscale(KScale &ks, const PlanesArg &kp, siz
   ks.sk = *reinterpret_cast<const float2 *>(kp.chunk_maxabs + cidx);
 }
 
-// Scale slot of a chunk: c1k * ks and c0k for every channel (wave w writes
-// channels 16w .. 16w + 15), and 1 / (ks * qs) (wave 0).  ks = 2^(14 - e),
-// e the exponent of the largest c1k, keeps every K' below 2^15.
+// Scale slot of a chunk: c1 * ks, rg * mu * ks and mn for every channel
+// (wave w writes channels 16w .. 16w + 15), and 1 / (ks * qs) (wave 0).
+// ks = 2^(14 - e), e the exponent of the largest rg * (mu + s) (|yhat| <= 1),
+// keeps every K' below 2^15.
 __device__ __forceinline__ void stage_slot(const KScale &k, char *slot, int w, int lane,
                                            double inv_qs) {
   const float c1a = k.rgk.x * k.sk.x, c1b = k.rgk.y * k.sk.y;  // fp32
-  const float top = wave_max(fmaxf(c1a, c1b));
+  const float c0a = k.rgk.x * k.muk.x, c0b = k.rgk.y * k.muk.y;
+  const float top = wave_max(fmaxf(fabsf(c1a) + fabsf(c0a), fabsf(c1b) + fabsf(c0b)));
   float ks = 1.0f;
   double inv_ks = 1.0;
   const uint32_t eb = (__float_as_uint(top) >> 23) & 0xFFu;
@@ -175,11 +180,11 @@ __device__ __forceinline__ void stage_slot(const KScale &k, char *slot, int w, i
   }
   if ((lane >> 3) == w) {
     reinterpret_cast<float2 *>(slot)[lane] = make_float2(c1a * ks, c1b * ks);
-    reinterpret_cast<double2 *>(slot + kDim * 4)[lane] =
-        make_double2(static_cast<double>(k.mnk.x) + static_cast<double>(k.rgk.x) * k.muk.x,
-                     static_cast<double>(k.mnk.y) + static_cast<double>(k.rgk.y) * k.muk.y);
+    reinterpret_cast<float2 *>(slot + kDim * 4)[lane] = make_float2(c0a * ks, c0b * ks);
+    reinterpret_cast<double2 *>(slot + kDim * 8)[lane] =
+        make_double2(static_cast<double>(k.mnk.x), static_cast<double>(k.mnk.y));
   }
-  if (w == 0 && lane == 0) *reinterpret_cast<double *>(slot + kDim * 12) = inv_ks * inv_qs;
+  if (w == 0 && lane == 0) *reinterpret_cast<double *>(slot + kDim * 16) = inv_ks * inv_qs;
 }
 
 // Build the K' and V tiles of one chunk from thread t's inputs.
@@ -191,17 +196,19 @@ __device__ __forceinline__ void build_chunk(const BuildIn &in, const char *slot,
     float y[8];
     yhat8<kFull>(in.ka, in.kr, lb, ytab, y);
     const int ch0 = (t & 15) * 8;
-    const float4 c0 = *reinterpret_cast<const float4 *>(slot + ch0 * 4);
-    const float4 c1 = *reinterpret_cast<const float4 *>(slot + ch0 * 4 + 16);
+    const float4 ca = *reinterpret_cast<const float4 *>(slot + ch0 * 4);  // c1 * ks
+    const float4 cb = *reinterpret_cast<const float4 *>(slot + ch0 * 4 + 16);
+    const float4 da = *reinterpret_cast<const float4 *>(slot + kDim * 4 + ch0 * 4);  // rg * mu * ks
+    const float4 db = *reinterpret_cast<const float4 *>(slot + kDim * 4 + ch0 * 4 + 16);
     u32x4 w0, w1;
-    w0[0] = pair16(y[0] * c0.x);
-    w0[1] = pair16(y[1] * c0.y);
-    w0[2] = pair16(y[2] * c0.z);
-    w0[3] = pair16(y[3] * c0.w);
-    w1[0] = pair16(y[4] * c1.x);
-    w1[1] = pair16(y[5] * c1.y);
-    w1[2] = pair16(y[6] * c1.z);
-    w1[3] = pair16(y[7] * c1.w);
+    w0[0] = pair16(__builtin_fmaf(y[0], ca.x, da.x));
+    w0[1] = pair16(__builtin_fmaf(y[1], ca.y, da.y));
+    w0[2] = pair16(__builtin_fmaf(y[2], ca.z, da.z));
+    w0[3] = pair16(__builtin_fmaf(y[3], ca.w, da.w));
+    w1[0] = pair16(__builtin_fmaf(y[4], cb.x, db.x));
+    w1[1] = pair16(__builtin_fmaf(y[5], cb.y, db.y));
+    w1[2] = pair16(__builtin_fmaf(y[6], cb.z, db.z));
+    w1[3] = pair16(__builtin_fmaf(y[7], cb.w, db.w));
     char *dst = ktile + (t >> 4) * kKRowB + ch0 * 4;
     *reinterpret_cast<u32x4 *>(dst) = w0;
     *reinterpret_cast<u32x4 *>(dst + 16) = w1;
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
 
   // ---- the block-wide power of two qs that brings max |q| into
   // [2^14, 2^15): q * qs is then an exact fp16 value (bf16 has 8 significant
-  // bits), which both the score product and the fp64 chunk bias use ----
+  // bits), which both the score product and the fp64 page bias use ----
   auto q_at = [&](int g, int st, int i) {  // bf16 q of channel 16st + 4r + i, 0 past the rows
     const uint32_t u = (i >> 1) ? qraw[g][st].y : qraw[g][st].x;
     const uint32_t bits = (i & 1) ? (u & 0xFFFF0000u) : (u << 16);
@@ -375,8 +382,10 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
   const double bias_scale = sm2 * inv_qs;
 
   VState st[kGroups];
+  double bias2[kGroups];  // the current page's bias, times sm2 / qs
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
+    bias2[g] = 0.0;
     st[g].m = -INFINITY;
     st[g].l = 0.0f;
 #pragma unroll
@@ -414,18 +423,17 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
         const char *kt = ktiles + tb * kKTileB;
         const char *vt = vtiles + tb * kVTileB;
         const char *slot = slots + (j % 3) * kSlotB;
-        // chunk bias sum_d (q_d qs) c0k_d (fp64) of each group's column n over
-        // channels 16st + 4r + i; times sm2 / qs below
-        double bias[kGroups];
-        {
-          const double *c0k = reinterpret_cast<const double *>(slot + kDim * 4);
+        // page bias sum_d (q_d qs) mn_d (fp64) of each group's column n over
+        // channels 16st + 4r + i, times sm2 / qs, at the first chunk of a page
+        if (j == 0 || (c & (kChunks - 1)) == 0) {
+          const double *mnp = reinterpret_cast<const double *>(slot + kDim * 8);
           double a0[kGroups], a1[kGroups];
 #pragma unroll
           for (int g = 0; g < kGroups; ++g) a0[g] = a1[g] = 0.0;
 #pragma unroll
           for (int s8 = 0; s8 < 8; ++s8) {
-            const double2 x0 = *reinterpret_cast<const double2 *>(c0k + 16 * s8 + 4 * r);
-            const double2 x1 = *reinterpret_cast<const double2 *>(c0k + 16 * s8 + 4 * r + 2);
+            const double2 x0 = *reinterpret_cast<const double2 *>(mnp + 16 * s8 + 4 * r);
+            const double2 x1 = *reinterpret_cast<const double2 *>(mnp + 16 * s8 + 4 * r + 2);
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
               auto qv = [&](int i) {
@@ -439,7 +447,7 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
             }
           }
 #pragma unroll
-          for (int g = 0; g < kGroups; ++g) bias[g] = xrows_sum(a0[g] + a1[g]);
+          for (int g = 0; g < kGroups; ++g) bias2[g] = xrows_sum(a0[g] + a1[g]) * bias_scale;
         }
         // scores S^T[16 tok][16 col] of both groups for tiles 0, 1 (each K'
         // operand read serves both groups)
@@ -460,20 +468,19 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
           // keep the operand reads of at most two steps in flight
           if (s8 & 1) __builtin_amdgcn_sched_barrier(0);
         }
-        const double scale2 = sm2 * *reinterpret_cast<const double *>(slot + kDim * 12);
+        const double scale2 = sm2 * *reinterpret_cast<const double *>(slot + kDim * 16);
         // online softmax per group; P operands: the lane's own column n,
         // tokens 16tt + 4r + i (p[4tt + i]), each in the two k slots of its
         // V (hi, lo) pair: once the P hi part in both, once the P lo part
         half8 pk[kGroups][4];  // [2tt]: hi parts of tile tt, [2tt + 1]: lo parts
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-          const double bias2 = bias[g] * bias_scale;
           double sc[8];
           float cmax = -INFINITY;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            sc[i] = fma(static_cast<double>(s0[g][i]), scale2, bias2);
-            sc[4 + i] = fma(static_cast<double>(s1[g][i]), scale2, bias2);
+            sc[i] = fma(static_cast<double>(s0[g][i]), scale2, bias2[g]);
+            sc[4 + i] = fma(static_cast<double>(s1[g][i]), scale2, bias2[g]);
             cmax = fmaxf(cmax, fmaxf(static_cast<float>(sc[i]), static_cast<float>(sc[4 + i])));
           }
           cmax = xrows(cmax, MaxOp());
