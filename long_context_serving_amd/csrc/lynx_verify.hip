@@ -161,11 +161,12 @@ __device__ __forceinline__ void load_kscale(KScale &ks, const PlanesArg &kp, siz
 }
 
 // Scale slot of a chunk: c1 * ks, rg * mu * ks and mn for every channel
-// (wave w writes channels 16w .. 16w + 15), and 1 / (ks * qs) (wave 0).
+// (lane l writes channels 2l, 2l + 1), and 1 / (ks * qs) (lane 0).
 // ks = 2^(14 - e), e the exponent of the largest rg * (mu + s) (|yhat| <= 1),
-// keeps every K' below 2^15.
-__device__ __forceinline__ void stage_slot(const KScale &k, char *slot, int w, int lane,
-                                           double inv_qs) {
+// keeps every K' below 2^15.  One wave (kStager) loads the K scales and
+// stages every slot; the last wave has the fewest query rows.
+constexpr int kStager = kVW - 1;
+__device__ __forceinline__ void stage_slot(const KScale &k, char *slot, int lane, double inv_qs) {
   const float c1a = k.rgk.x * k.sk.x, c1b = k.rgk.y * k.sk.y;  // fp32
   const float c0a = k.rgk.x * k.muk.x, c0b = k.rgk.y * k.muk.y;
   const float top = wave_max(fmaxf(fabsf(c1a) + fabsf(c0a), fabsf(c1b) + fabsf(c0b)));
@@ -178,13 +179,11 @@ __device__ __forceinline__ void stage_slot(const KScale &k, char *slot, int w, i
     ks = __uint_as_float(static_cast<uint32_t>(ex) << 23);
     inv_ks = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + 127 - ex) << 52);
   }
-  if ((lane >> 3) == w) {
-    reinterpret_cast<float2 *>(slot)[lane] = make_float2(c1a * ks, c1b * ks);
-    reinterpret_cast<float2 *>(slot + kDim * 4)[lane] = make_float2(c0a * ks, c0b * ks);
-    reinterpret_cast<double2 *>(slot + kDim * 8)[lane] =
-        make_double2(static_cast<double>(k.mnk.x), static_cast<double>(k.mnk.y));
-  }
-  if (w == 0 && lane == 0) *reinterpret_cast<double *>(slot + kDim * 16) = inv_ks * inv_qs;
+  reinterpret_cast<float2 *>(slot)[lane] = make_float2(c1a * ks, c1b * ks);
+  reinterpret_cast<float2 *>(slot + kDim * 4)[lane] = make_float2(c0a * ks, c0b * ks);
+  reinterpret_cast<double2 *>(slot + kDim * 8)[lane] =
+      make_double2(static_cast<double>(k.mnk.x), static_cast<double>(k.mnk.y));
+  if (lane == 0) *reinterpret_cast<double *>(slot + kDim * 16) = inv_ks * inv_qs;
 }
 
 // Build the K' and V tiles of one chunk from thread t's inputs.
@@ -315,8 +314,10 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
   KScale ksa, ring;
   {
     const long long g0 = page_of(cb), g1 = page_of(cb + 1);
-    load_kscale(ksa, kp, tile_of(g0), chunk_of(g0, cb), lane);
-    load_kscale(ring, kp, tile_of(g1), chunk_of(g1, cb + 1), lane);
+    if (w == kStager) {
+      load_kscale(ksa, kp, tile_of(g0), chunk_of(g0, cb), lane);
+      load_kscale(ring, kp, tile_of(g1), chunk_of(g1, cb + 1), lane);
+    }
     load_build<kFull>(bin, kp, vp, tile_of(g0), chunk_of(g0, cb), t);
   }
 
@@ -393,8 +394,10 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
   }
 
   if (cb < ce) {
-    stage_slot(ksa, slots, w, lane, inv_qs);
-    stage_slot(ring, slots + kSlotB, w, lane, inv_qs);
+    if (w == kStager) {
+      stage_slot(ksa, slots, lane, inv_qs);
+      stage_slot(ring, slots + kSlotB, lane, inv_qs);
+    }
     __syncthreads();
     build_chunk<kFull>(bin, slots, ktiles, vtiles, ytab, t, lb);
     __syncthreads();
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
       {
         const long long g1 = page_of(c + 1), g2 = page_of(c + 2);
         load_build<kFull>(bin, kp, vp, tile_of(g1), chunk_of(g1, c + 1), t);
-        load_kscale(ring, kp, tile_of(g2), chunk_of(g2, c + 2), lane);
+        if (w == kStager) load_kscale(ring, kp, tile_of(g2), chunk_of(g2, c + 2), lane);
       }
       if (wave_rows && page_of(c) >= 0) {
         // (the q operands are redefined here so that the bias's conversions
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(kVT) void verify_mfma_kernel(
       if (c + 1 < ce)
         build_chunk<kFull>(bin, slots + ((j + 1) % 3) * kSlotB, ktiles + (tb ^ 1) * kKTileB,
                            vtiles + (tb ^ 1) * kVTileB, ytab, t, lb);
-      stage_slot(ring, slots + ((j + 2) % 3) * kSlotB, w, lane, inv_qs);
+      if (w == kStager) stage_slot(ring, slots + ((j + 2) % 3) * kSlotB, lane, inv_qs);
       __syncthreads();
     }
   }
