@@ -42,12 +42,14 @@ def check(got, ref, label):
     assert (err <= bound).all(), label
 
 
-def pool_and_oracle(lynx, P, H, seed):
+def pool_and_oracle(lynx, P, H, seed, k_shift=None):
     """Encoded K and V pools on the GPU and the oracle's dequantized pages
     (full and draft) of the same inputs; the GPU codes must equal the oracle's
     outside the flagged near-boundary elements, which are checked elsewhere --
     here the oracle dequantizes its own codes and the GPU reads its own."""
     xk = synth.laplace_pages(P, H, 128, seed=seed, scale_channels=((0, 3, 90.0),))
+    if k_shift is not None:  # applied to the float values, then rounded to bf16 again
+        xk = synth.float_to_bf16_bits(k_shift((xk.astype(np.uint32) << 16).view(np.float32)))
     xv = synth.laplace_pages(P, H, 128, seed=seed + 1, scale_channels=((H - 1, 77, 60.0),))
     pk = lynx.quantize_pages(to_dev(xk), lynx.ROLE_KEY)
     pv = lynx.quantize_pages(to_dev(xv), lynx.ROLE_VALUE)
@@ -66,14 +68,15 @@ def tails(B, H, seed):
 
 
 def run_case(lynx, H, Hq, tq, page_lists, tail_len, P_pool, seed, full, max_pages=4,
-             contiguous=False):
+             contiguous=False, k_shift=None):
     """contiguous: no block table; request b reads pool pages
     b * max_pages .. b * max_pages + len(page_lists[b]) - 1."""
     B = len(page_lists)
     if contiguous:
         assert all(pl == list(range(b * max_pages, b * max_pages + len(pl)))
                    for b, pl in enumerate(page_lists))
-    pk, pv, deq = pool_and_oracle(lynx, P_pool, H, seed) if P_pool else (None, None, None)
+    pk, pv, deq = (pool_and_oracle(lynx, P_pool, H, seed, k_shift) if P_pool
+                   else (None, None, None))
     if P_pool == 0:
         pk = lynx.alloc_planes(1, H, lynx.ROLE_KEY)
         pv = lynx.alloc_planes(1, H, lynx.ROLE_VALUE)
@@ -130,6 +133,27 @@ def test_verify_merge_of_many_parts_per_row(lynx):
     # the weights, 16 in groups of four and the last one alone
     pages = list(range(31, -1, -1))
     run_case(lynx, 2, 16, 64, [pages], [90], 32, 808, True, max_pages=32)
+
+
+def _offset_keys(x):
+    """Key channel (head 0, channel 7) on a DC offset of 300 (the page
+    minimum then dwarfs the range) and channel (1, 20) raised by 40 in every
+    other 32-token chunk (the chunk means then dwarf the chunk deviations)."""
+    x = x.copy()
+    x[:, :, 0, 7] += 300.0
+    t = np.arange(x.shape[1])
+    x[:, ((t // 32) % 2) == 1, 1, 20] += 40.0
+    return x
+
+
+@pytest.mark.parametrize("full", [True, False])
+def test_verify_keys_with_offset_and_shifted_chunks(lynx, full):
+    # the page minimum enters the scores through the fp64 page bias, the
+    # chunk offset rg * mu through the fp32 key operand: both stay inside
+    # the bar for one column group per wave (tq 5) and two (tq 64)
+    for tq, tail_len in ((5, [5, 200]), (64, [64, 320])):
+        run_case(lynx, 2, 16, tq, [[3, 0, 5], [1, 4, 2, 6]], tail_len, 7, 303 + tq, full,
+                 k_shift=_offset_keys)
 
 
 @pytest.mark.parametrize("full", [True, False])
