@@ -471,6 +471,33 @@ def test_ragged_lengths_group_sizes_and_skipped_pages(lynx):
             check_attention(got, ref, "ragged H=%d Hq=%d full=%s" % (H, Hq, full))
 
 
+@pytest.mark.parametrize("H,Hq", [(2, 16), (1, 16)])
+def test_keys_with_offset_and_shifted_chunks(lynx, H, Hq):
+    """Key channel (head 0, channel 7) on a DC offset of 300, so the page
+    minimum dwarfs the range, and channel (H - 1, 20) raised by 40 in every
+    other 32-token chunk, so the chunk means dwarf the chunk deviations:
+    encode parity and decode attention within the bar, for the matrix-core
+    kernel (group 8) and the other one (group 16)."""
+    rng = np.random.default_rng(29)
+    P_pool = 6
+    x = synth.laplace_pages(P_pool, H, 128, seed=H * 10 + 3, scale_channels=((0, 3, 90.0),))
+    xf = (x.astype(np.uint32) << 16).view(np.float32).copy()
+    xf[:, :, 0, 7] += 300.0
+    t = np.arange(xf.shape[1])
+    xf[:, ((t // 32) % 2) == 1, H - 1, 20] += 40.0
+    x_k = synth.float_to_bf16_bits(xf)
+    x_v = synth.laplace_pages(P_pool, H, 128, seed=H * 10 + 4, scale_channels=((0, 9, 60.0),))
+    pk, ek, _, _ = check_encode(lynx, x_k, 0)
+    pv, ev, _, _ = check_encode(lynx, x_v, 1)
+    pages = [[4, 0, 2], [5, 1, 3]]
+    bt = np.array(pages, np.int32)
+    q = synth.float_to_bf16_bits(rng.laplace(0, 1, (2, Hq, 128)).astype(np.float32))
+    for full in (False, True):
+        ref = oracle_attention_for(ek, ev, q, pages, full)
+        got = run_gpu_attention(lynx, q, pk, pv, 3, full, block_table=bt)
+        check_attention(got, ref, "offset keys H=%d Hq=%d full=%s" % (H, Hq, full))
+
+
 @pytest.mark.parametrize("Hq", [8, 4])
 def test_most_splits_per_head(lynx, Hq):
     """One request and one KV head over 256 pages: one page per block, so the
