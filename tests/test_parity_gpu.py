@@ -476,8 +476,9 @@ def test_keys_with_offset_and_shifted_chunks(lynx, H, Hq):
     """Key channel (head 0, channel 7) on a DC offset of 300, so the page
     minimum dwarfs the range, and channel (H - 1, 20) raised by 40 in every
     other 32-token chunk, so the chunk means dwarf the chunk deviations:
-    encode parity and decode attention within the bar, for the matrix-core
-    kernel (group 8) and the other one (group 16)."""
+    encode parity (both roles), both dequantizers, and decode attention
+    within the bar for the matrix-core kernel (group 8) and the other one
+    (group 16)."""
     rng = np.random.default_rng(29)
     P_pool = 6
     x = synth.laplace_pages(P_pool, H, 128, seed=H * 10 + 3, scale_channels=((0, 3, 90.0),))
@@ -487,8 +488,14 @@ def test_keys_with_offset_and_shifted_chunks(lynx, H, Hq):
     xf[:, ((t // 32) % 2) == 1, H - 1, 20] += 40.0
     x_k = synth.float_to_bf16_bits(xf)
     x_v = synth.laplace_pages(P_pool, H, 128, seed=H * 10 + 4, scale_channels=((0, 9, 60.0),))
-    pk, ek, _, _ = check_encode(lynx, x_k, 0)
+    pk, ek, kcodes, _ = check_encode(lynx, x_k, 0)
     pv, ev, _, _ = check_encode(lynx, x_v, 1)
+    for full in (True, False):
+        check_dequant(lynx, pk, ek, kcodes[2], full)
+    # the same keys under the value role, dequantized
+    pkv, ekv, kvcodes, _ = check_encode(lynx, x_k, 1)
+    for full in (True, False):
+        check_dequant(lynx, pkv, ekv, kvcodes[2], full)
     pages = [[4, 0, 2], [5, 1, 3]]
     bt = np.array(pages, np.int32)
     q = synth.float_to_bf16_bits(rng.laplace(0, 1, (2, Hq, 128)).astype(np.float32))
