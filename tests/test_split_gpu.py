@@ -222,3 +222,34 @@ def test_cut_attention_ragged_groups_and_skipped_pages(lynx):
             torch.cuda.synchronize()
             check_attention(got, cut_oracle_attention(ek, ev, q, pages, b, full),
                             "ragged H=%d Hq=%d b=%d full=%s" % (H, Hq, b, full))
+
+
+@pytest.mark.parametrize("b", [2, 6])
+def test_cut_attention_keys_with_offset_and_shifted_chunks(lynx, b):
+    """Keys with one channel on a DC offset of 300 (the page minimum dwarfs
+    the range) and one raised by 40 in every other 32-token chunk (the chunk
+    means dwarf the chunk deviations), read through a b + (8 - b) cut:
+    draft and full attention within the bar (group 8)."""
+    rng = np.random.default_rng(31 + b)
+    H, Hq, P_pool = 2, 16, 6
+    xk = synth.laplace_pages(P_pool, H, 128, seed=b * 10 + 5, scale_channels=((0, 3, 90.0),))
+    xf = oracle.bf16_bits_to_float(xk).copy()
+    xf[:, :, 0, 7] += 300.0
+    t = np.arange(xf.shape[1])
+    xf[:, ((t // 32) % 2) == 1, 1, 20] += 40.0
+    xk = synth.float_to_bf16_bits(xf)
+    xv = synth.laplace_pages(P_pool, H, 128, seed=b * 10 + 6, scale_channels=((1, 9, 60.0),))
+    pk = lynx.quantize_pages(to_dev(xk), lynx.ROLE_KEY)
+    pv = lynx.quantize_pages(to_dev(xv), lynx.ROLE_VALUE)
+    ek, ev = oracle.encode(xk), oracle.encode(xv)
+    ck, cv = lynx.cut_planes(pk, b), lynx.cut_planes(pv, b)
+    pages = [[4, 0, 2], [5, 1, 3]]
+    btd = torch.from_numpy(np.asarray(pages, np.int32)).cuda()
+    q = synth.float_to_bf16_bits(rng.laplace(0, 1, (2, Hq, 128)).astype(np.float32))
+    print("cut attention offset keys b=%d" % b, flush=True)
+    for full in (False, True):
+        got = lynx.decode_attention_split(to_dev(q), ck, cv, b, 3, full=full, block_table=btd,
+                                          sm_scale=SM)
+        torch.cuda.synchronize()
+        check_attention(got, cut_oracle_attention(ek, ev, q, pages, b, full),
+                        "offset keys b=%d full=%s" % (b, full))
